@@ -1,0 +1,171 @@
+"""CPU fp64 oracle of the gated delta rule -- TEST INFRASTRUCTURE.
+
+Only `tests/`, `__graft_entry__.smoke()` and the CPU-baseline leg of
+`bench.py` may import this package.  It shares no code with the HIP path
+(`gated_delta_rule_24_amd`), and neither imports the other.
+
+Functions:
+  recurrent(...)      the definition, token by token (C, fp64, OpenMP over
+                      independent (sequence, head) chains)   -- THE oracle
+  naive_product(...)  explicit dk x dk transition matrices (C, fp64), for
+                      brute force on tiny inputs
+  chunked(...)        the chunkwise WY/UT form in numpy fp64, exposing the
+                      per-chunk intermediates (see oracle/chunked.py)
+  step_strict(...)    one token with the input checks of the tutorial's
+                      reference step function (shape, finiteness, gates in
+                      [0, 1], unit key)
+
+Parity pins (all in tests/test_oracle_pins.py): the tutorial's worked
+two-cell example (tests/golden/), the delta-vs-additive 1-D example, the
+unit-key interpolation identity, untouched orthogonal directions, beta = 0
+pure decay, alpha -> 0 memory clearing, the SSD decay-mask closed form with
+orthonormal keys, brute force against naive_product, chunk-size invariance of
+chunked(), save-then-resume, packed-vs-separate, linearity in (S0, v) and the
+contraction bound.  No function here is "parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+import numpy as np
+
+from . import chunked as _chunked_mod
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(HERE, "liboracle.so")
+_lib = None
+
+
+def load(path: Optional[str] = None):
+    """Load (building first if absent) the oracle library."""
+    global _lib
+    if path is None and _lib is not None:
+        return _lib
+    p = path or _LIB_PATH
+    if not os.path.exists(p):
+        from . import build as _b
+        _b.build(p)
+    lib = ctypes.CDLL(p)
+    dp = ctypes.POINTER(ctypes.c_double)
+    lp = ctypes.POINTER(ctypes.c_int64)
+    i64 = ctypes.c_int64
+    lib.oracle_gdn_recurrent.argtypes = [i64, lp, i64, i64, i64, dp, dp, dp, dp, dp, dp, dp, dp,
+                                         ctypes.c_int]
+    lib.oracle_gdn_recurrent.restype = ctypes.c_int
+    lib.oracle_gdn_naive_product.argtypes = [i64, lp, i64, i64, i64, dp, dp, dp, dp, dp, dp, dp,
+                                             dp]
+    lib.oracle_gdn_naive_product.restype = ctypes.c_int
+    lib.oracle_num_threads.argtypes = []
+    lib.oracle_num_threads.restype = ctypes.c_int
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _f64(x):
+    return np.ascontiguousarray(x, dtype=np.float64)
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    return x.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def _flatten(q, k, v, log_alpha, beta, cu_seqlens):
+    """[B,T,H,d] (or [T,H,d]) inputs -> packed [B*T,H,d] plus cu offsets."""
+    q = np.asarray(q)
+    if q.ndim == 3:
+        q, k, v = q[None], np.asarray(k)[None], np.asarray(v)[None]
+        log_alpha, beta = np.asarray(log_alpha)[None], np.asarray(beta)[None]
+    B, T, H, dk = q.shape
+    dv = np.asarray(v).shape[-1]
+    if cu_seqlens is None:
+        cu = np.arange(B + 1, dtype=np.int64) * T
+    else:
+        if B != 1:
+            raise ValueError("cu_seqlens requires a packed batch (B == 1)")
+        cu = np.asarray(cu_seqlens, dtype=np.int64)
+    return (B, T, H, dk, dv, cu, _f64(q).reshape(B * T, H, dk), _f64(k).reshape(B * T, H, dk),
+            _f64(v).reshape(B * T, H, dv), _f64(log_alpha).reshape(B * T, H),
+            _f64(beta).reshape(B * T, H))
+
+
+def recurrent(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, threads=0,
+              lib=None):
+    """Token-by-token recurrence in fp64.
+
+    q, k: [B,T,H,dk]; v: [B,T,H,dv]; log_alpha, beta: [B,T,H] (any float
+    dtype; widened to fp64).  With cu_seqlens (int [N+1]) the batch is packed
+    (B == 1) and sequence n covers tokens cu[n]..cu[n+1]-1.
+    Returns (o [B,T,H,dv] fp64, final_state [N,H,dv,dk] fp64).
+    """
+    B, T, H, dk, dv, cu, qf, kf, vf, laf, bf = _flatten(q, k, v, log_alpha, beta, cu_seqlens)
+    N = len(cu) - 1
+    o = np.zeros((B * T, H, dv), dtype=np.float64)
+    fin = np.zeros((N, H, dv, dk), dtype=np.float64)
+    init = None if init_state is None else _f64(init_state).reshape(N, H, dv, dk)
+    lib = lib or load()
+    rc = lib.oracle_gdn_recurrent(N, cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), H, dk,
+                                  dv, _ptr(qf), _ptr(kf), _ptr(vf), _ptr(laf), _ptr(bf),
+                                  _ptr(init), _ptr(o), _ptr(fin), int(threads))
+    if rc != 0:
+        raise ValueError(f"oracle_gdn_recurrent failed with code {rc}")
+    return o.reshape(B, T, H, dv), fin
+
+
+def naive_product(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, lib=None):
+    """Brute-force form with explicit transition matrices (tiny inputs only)."""
+    B, T, H, dk, dv, cu, qf, kf, vf, laf, bf = _flatten(q, k, v, log_alpha, beta, cu_seqlens)
+    N = len(cu) - 1
+    o = np.zeros((B * T, H, dv), dtype=np.float64)
+    fin = np.zeros((N, H, dv, dk), dtype=np.float64)
+    init = None if init_state is None else _f64(init_state).reshape(N, H, dv, dk)
+    lib = lib or load()
+    rc = lib.oracle_gdn_naive_product(N, cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), H,
+                                      dk, dv, _ptr(qf), _ptr(kf), _ptr(vf), _ptr(laf), _ptr(bf),
+                                      _ptr(init), _ptr(o), _ptr(fin))
+    if rc != 0:
+        raise ValueError(f"oracle_gdn_naive_product failed with code {rc}")
+    return o.reshape(B, T, H, dv), fin
+
+
+def num_threads(lib=None):
+    return (lib or load()).oracle_num_threads()
+
+
+chunked = _chunked_mod.chunked
+chunked_single = _chunked_mod.chunked_single
+
+
+def step_strict(state, key, value, decay, write):
+    """One gated-delta step on plain nested lists, with the input checks the
+    tutorial's reference step function applies (it raises ValueError on an
+    empty or mismatched shape, non-finite entries, gates outside [0, 1] and a
+    key that is not unit length within 1e-9).  Returns the new state (lists).
+
+    The arithmetic goes through the C recurrence (one token, fp64); only the
+    checks are done here.
+    """
+    if not key or not state or len(state) != len(value):
+        raise ValueError("invalid state, key or value shape")
+    if any(len(row) != len(key) for row in state):
+        raise ValueError("state rows must match the key dimension")
+    scalars = [decay, write, *key, *value, *(x for row in state for x in row)]
+    if any(not math.isfinite(float(x)) for x in scalars):
+        raise ValueError("inputs must be finite")
+    if not (0.0 <= decay <= 1.0 and 0.0 <= write <= 1.0):
+        raise ValueError("gates must lie in [0, 1]")
+    if not math.isclose(sum(float(x) * float(x) for x in key), 1.0, abs_tol=1e-9):
+        raise ValueError("key must be unit length")
+    dv, dk = len(state), len(key)
+    S0 = np.asarray(state, dtype=np.float64).reshape(1, 1, dv, dk)
+    kk = np.asarray(key, dtype=np.float64).reshape(1, 1, 1, dk)
+    vv = np.asarray(value, dtype=np.float64).reshape(1, 1, 1, dv)
+    la = np.full((1, 1, 1), -np.inf if decay == 0.0 else math.log(decay))
+    bb = np.full((1, 1, 1), float(write))
+    _, fin = recurrent(np.zeros_like(kk), kk, vv, la, bb, init_state=S0)
+    return fin[0, 0].tolist()
