@@ -1,0 +1,212 @@
+"""Benchmark of the gated delta rule core on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+
+A step is one chunked prefill over the prefill workload (B=4, H=16, L=4096,
+dk=dv=128, C=64, bf16 q/k/v, fp32 gates, fp32 o and states), inputs resident
+in HBM.  `value` is prefill tokens/s.  The same run times 1000 in-place decode
+steps of the decode workload (256 sequences x 16 heads, 128x128 fp32 states)
+and reports steps/s under "decode".  Each kernel's average duration comes from
+HIP events the library records around its launches on the launch stream; the
+roofline objects use the algorithmic bytes and flops of the method (counted
+below) over that duration.  The CPU baseline is the fp64 oracle on a bounded
+sample of the prefill workload, on all host cores.
+
+Prints ONE JSON line.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "prefill tokens/s (H=16,dk=dv=128,C=64) + decode steps/s; % MFMA/HBM roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak, TFLOP/s
+C = 64
+
+
+def chunk_flops_per_token_head(dk, dv, c=C):
+    # W S^T, Q S^T and V'^T K (6 dk dv); K K^T, Q K^T, W, U and P V' (2C(3dk + 2dv)); the
+    # triangular inverse (C^2/3).  Counted dense, as the chunked algorithm computes them.
+    return 6 * dk * dv + 2 * c * (3 * dk + 2 * dv) + c * c / 3
+
+
+def chunk_min_bytes(B, T, H, dk, dv, N, in_bytes, out_bytes, has_init, has_final):
+    th = B * T * H
+    b = th * (2 * dk + dv) * in_bytes + th * 2 * 4 + th * dv * out_bytes
+    st = N * H * dv * dk * 4
+    return b + (st if has_init else 0) + (st if has_final else 0)
+
+
+def decode_min_bytes(N, H, dk, dv, in_bytes, out_bytes):
+    nh = N * H
+    return nh * dv * dk * 4 * 2 + nh * (2 * dk + dv) * in_bytes + nh * 2 * 4 + nh * dv * out_bytes
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the path has no multi-GPU mode; "
+              "(sequence, head) pairs are independent and would be sharded with no communication.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gated_delta_rule_24_amd as gdn
+    import workloads as W
+
+    if not os.path.exists(gdn.lib_path()):
+        from gated_delta_rule_24_amd import build as gbuild
+        gbuild.build()
+    gdn.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def to(x, dt=torch.float32):
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dev, dt)
+
+    # ---------------- prefill ----------------
+    inp = W.prefill()
+    B, T, H, dk, dv = inp.B, inp.T, inp.H, inp.dk, inp.dv
+    q, k, v = to(inp.q, torch.bfloat16), to(inp.k, torch.bfloat16), to(inp.v, torch.bfloat16)
+    la, be = to(inp.log_alpha), to(inp.beta)
+    o = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
+    fin = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
+    ws = torch.empty(gdn.chunk_fwd_workspace_size(B, T, H, dk, dv, B), dtype=torch.uint8, device=dev)
+
+    def step():
+        gdn.chunk_fwd(q, k, v, la, be, o=o, final_state=fin, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(args.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    tokens_per_s = B * T / (ms_per_step * 1e-3)
+
+    # per-kernel durations (events recorded by the library around each launch)
+    with gdn.profile() as prof:
+        for _ in range(args.steps):
+            step()
+    torch.cuda.synchronize()
+    kernels = {name: {"launches": n, "avg_us": 1e3 * ms / n} for name, (n, ms) in prof.results.items()}
+
+    flops = chunk_flops_per_token_head(dk, dv) * B * T * H
+    min_bytes = chunk_min_bytes(B, T, H, dk, dv, B, 2, 4, False, True)
+    dom = max(kernels, key=lambda n: kernels[n]["avg_us"] * kernels[n]["launches"])
+    dom_s = kernels[dom]["avg_us"] * 1e-6
+    path_s = ms_per_step * 1e-3
+    roofline = {
+        "kernel": dom,
+        "bound": "hbm",
+        "achieved": min_bytes / dom_s / 1e9,
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": min_bytes / dom_s / 1e9 / HBM_PEAK_GBS,
+        "traffic": None,
+        "algorithmic_bytes": min_bytes,
+        "mfma_tflops": flops / dom_s / 1e12,
+        "mfma_frac": flops / dom_s / 1e12 / MFMA_F16_PEAK_TFLOPS,
+        "path_hbm_frac": min_bytes / path_s / 1e9 / HBM_PEAK_GBS,
+        "path_mfma_frac": flops / path_s / 1e12 / MFMA_F16_PEAK_TFLOPS,
+    }
+    del q, k, v, la, be, o, fin, ws
+    torch.cuda.empty_cache()
+
+    # ---------------- decode ----------------
+    d = W.decode()
+    Nd, Hd = d.state.shape[:2]
+    state = to(d.state)
+    pool = [(to(d.q[p], torch.bfloat16), to(d.k[p], torch.bfloat16), to(d.v[p], torch.bfloat16), to(d.log_alpha[p]),
+             to(d.beta[p])) for p in range(d.pool)]
+    od = torch.empty((Nd, Hd, d.v.shape[-1]), dtype=torch.float32, device=dev)
+    for s in range(10):
+        gdn.decode_step(state, *pool[s % d.pool], o=od)
+    torch.cuda.synchronize()
+    ev0.record()
+    for s in range(args.decode_steps):
+        gdn.decode_step(state, *pool[s % d.pool], o=od)
+    ev1.record()
+    torch.cuda.synchronize()
+    dec_ms = ev0.elapsed_time(ev1) / args.decode_steps
+    with gdn.profile() as dprof:
+        for s in range(100):
+            gdn.decode_step(state, *pool[s % d.pool], o=od)
+    n_l, ms_l = dprof.results["gdn_decode_step"]
+    dec_kernel_s = ms_l / n_l * 1e-3
+    dbytes = decode_min_bytes(Nd, Hd, 128, 128, 2, 4)
+    decode = {
+        "value": 1e3 / dec_ms, "unit": "steps/s", "ms_per_step": dec_ms, "steps": args.decode_steps,
+        "config": {"workload": "decode", "N": int(Nd), "H": int(Hd), "dk": 128, "dv": 128, "in_dtype": "bf16",
+                   "state": "fp32 in place"},
+        "roofline": {"kernel": "gdn_decode_step", "bound": "hbm", "achieved": dbytes / dec_kernel_s / 1e9,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dbytes / dec_kernel_s / 1e9 / HBM_PEAK_GBS,
+                     "traffic": None, "algorithmic_bytes": dbytes, "avg_us": dec_kernel_s * 1e6},
+    }
+    del state, pool, od
+    torch.cuda.empty_cache()
+
+    # ---------------- CPU baseline (fp64 oracle) ----------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        threads = oracle.num_threads()
+        sl = 64
+        while True:
+            t0 = time.perf_counter()
+            oracle.recurrent(inp.q[:, :sl], inp.k[:, :sl], inp.v[:, :sl], inp.log_alpha[:, :sl], inp.beta[:, :sl],
+                             threads=threads)
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds or sl >= T:
+                break
+            sl = min(T, max(sl * 2, int(sl * args.cpu_seconds / max(el, 1e-3) * 1.1)))
+        cpu = {"value": B * sl / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+               "sample": f"prefill workload, first {sl} tokens of each of the {B} sequences, all {H} heads "
+                         f"(fp64 token recurrence, {el:.1f} s)"}
+
+    out = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "compute": "bf16 inputs; fp16 matrix-core operands, fp32 accumulation and fp32 state",
+        "data": "synthetic (seeded; q,k L2-normalised, log_alpha~U(-0.1,-0.001), beta=sigmoid(N(0,1)))",
+        "config": {"workload": "prefill", "B": B, "L": T, "H": H, "dk": dk, "dv": dv, "chunk": C,
+                   "in_dtype": "bf16", "out_dtype": "fp32", "init_state": None, "final_state": "fp32"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "decode": decode,
+        "kernels": kernels,
+        "device": torch.cuda.get_device_name(0),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,653 @@
+// Chunkwise-parallel forward pass of the gated delta rule on gfx950.
+//
+// Per (sequence, head) the tokens are cut into chunks of C = 64 rows
+// (row-stacked blocks Q, K in R^{C x dk}, V in R^{C x dv}).  With the state S
+// (dv x dk) at the chunk start, the chunk algorithm of the Gated Delta
+// Networks paper (section 3.3; paper-notes blog, "Hardware-Efficient
+// Chunkwise Training", summary (4), which derives the decay mask in the
+// output term) is
+//
+//   g_r      = sum_{i <= r} log alpha_i            (gamma^r = exp g_r)
+//   Gamma_ri = exp(g_r - g_i) for i <= r, else 0   (masked before exp)
+//   A        = strictLower(diag(beta) (Gamma o K K^T))
+//   T        = (I + A)^{-1}                       (UT transform)
+//   W        = T diag(beta) diag(gamma) K,   U = T diag(beta) V
+//   V'       = U - W S^T
+//   O        = diag(gamma) Q S^T + (Q K^T o Gamma) V'
+//   S_next   = gamma^C S + V'^T diag(exp(g_C - g_r)) K
+//
+// The kernels use the same algebra with one regrouping:
+//   V' = (T diag(beta)) (V - diag(gamma) (K S^T)),
+// i.e. W S^T is formed as (T diag(beta)) (diag(gamma) K S^T) instead of
+// materialising W, which saves a C x C x dk product per chunk and keeps the
+// per-chunk matrices handed from G1 to G2 at C x C size.
+//
+// Kernels (all launched on the caller's stream):
+//   G0 chunk_table_kernel  one block: validates cu_seqlens and lays out the
+//                          (sequence, chunk) rows.
+//   G1 chunk_prep_kernel   one block per (chunk row, head), fully parallel:
+//                          cumulative log-decay g, the decay-masked Q K^T
+//                          block P, A, T = (I + A)^{-1} by blocked forward
+//                          substitution in LDS (fp32), and M = T diag(beta).
+//                          Writes g, M, P to the workspace.
+//   G2 chunk_state_kernel  one block per (sequence, head, value tile), serial
+//                          over the sequence's chunks.  Each wave owns 16
+//                          value columns and keeps its slice of S^T in
+//                          registers (fp32 MFMA accumulators) for the whole
+//                          sequence.  Per chunk:  X = [Q; K] S^T,
+//                          Y = V - diag(gamma) X_K,  V' = M Y,
+//                          O = diag(gamma) X_Q + P V',
+//                          S^T <- gamma^C S^T + K^T (diag(exp(g_C - g)) V').
+//                          Accumulator tiles feed the next product as B
+//                          operands directly (see gdn_device.h), so only the
+//                          shared Q, K, K^T, M, P blocks go through LDS.
+#include "gdn_device.h"
+#include "gdn_launch.h"
+
+#include <stdlib.h>
+
+namespace gdn {
+
+constexpr int C = kChunk;
+
+__host__ __device__ constexpr int tri_index(int a, int b) { return a * (a + 1) / 2 + b; }
+__device__ __forceinline__ void tri_decode(int t, int &a, int &b) {
+    a = t < 1 ? 0 : (t < 3 ? 1 : (t < 6 ? 2 : 3));
+    b = t - a * (a + 1) / 2;
+}
+
+__device__ __forceinline__ void store_out(void *o, int64_t idx, int odt, float val) {
+    if (odt == DT_FP32)
+        static_cast<float *>(o)[idx] = val;
+    else if (odt == DT_BF16)
+        static_cast<bf16_t *>(o)[idx] = from_f32<bf16_t>(val);
+    else
+        static_cast<_Float16 *>(o)[idx] = (_Float16)val;
+}
+
+// Store 8 fp32 values as operands (two 4-element LDS writes).
+template <typename OP>
+__device__ __forceinline__ void lds_store8(OP *p, const float (&x)[8]) {
+    using M = Mma<OP>;
+    *reinterpret_cast<typename M::frag *>(p) = M::cvt(float4_t{x[0], x[1], x[2], x[3]});
+    *reinterpret_cast<typename M::frag *>(p + 4) = M::cvt(float4_t{x[4], x[5], x[6], x[7]});
+}
+
+// ============================================================================
+// G0: chunk table.
+//   meta[0] = number of rows, meta[1] = cu_seqlens error code (0 = valid)
+//   cu_ws[N+1] = token offsets, row0[N] = first row of each sequence,
+//   row_tok / row_len = token start and length of each row.
+// ============================================================================
+__global__ __launch_bounds__(256) void chunk_table_kernel(int N, int T, int packed,
+                                                          const int32_t *__restrict__ cu_in,
+                                                          int32_t *__restrict__ meta,
+                                                          int32_t *__restrict__ cu_ws,
+                                                          int32_t *__restrict__ row0,
+                                                          int32_t *__restrict__ row_tok,
+                                                          int32_t *__restrict__ row_len) {
+    __shared__ int s_code;
+    __shared__ int s_scan[256];
+    __shared__ int s_offset;
+    const int tid = threadIdx.x;
+    if (tid == 0) {
+        s_code = 0;
+        s_offset = 0;
+    }
+    __syncthreads();
+    for (int n = tid; n <= N; n += 256) {
+        const int val = packed ? cu_in[n] : n * T;
+        cu_ws[n] = val;
+        if (packed) {
+            if (n == 0 && val != 0) atomicOr(&s_code, 1);
+            if (n > 0 && cu_in[n - 1] > val) atomicOr(&s_code, 2);
+            if (n == N && val != T) atomicOr(&s_code, 4);
+        }
+    }
+    __syncthreads();
+    const int code = s_code;
+    if (code) {
+        if (tid == 0) {
+            meta[0] = 0;
+            meta[1] = (code & 1) ? 1 : ((code & 2) ? 2 : 3);
+        }
+        return;
+    }
+    for (int base = 0; base < N; base += 256) {
+        const int n = base + tid;
+        int cnt = 0;
+        if (n < N) {
+            const int s0 = packed ? cu_in[n] : n * T;
+            const int s1 = packed ? cu_in[n + 1] : (n + 1) * T;
+            cnt = (s1 - s0 + C - 1) / C;
+        }
+        s_scan[tid] = cnt;
+        __syncthreads();
+        for (int off = 1; off < 256; off <<= 1) {
+            const int x = tid >= off ? s_scan[tid - off] : 0;
+            __syncthreads();
+            s_scan[tid] += x;
+            __syncthreads();
+        }
+        if (n < N) row0[n] = s_offset + s_scan[tid] - cnt;
+        __syncthreads();
+        if (tid == 0) s_offset += s_scan[255];
+        __syncthreads();
+    }
+    if (tid == 0) {
+        meta[0] = s_offset;
+        meta[1] = 0;
+    }
+    for (int n = tid; n < N; n += 256) {
+        const int s0 = packed ? cu_in[n] : n * T;
+        const int s1 = packed ? cu_in[n + 1] : (n + 1) * T;
+        const int r = row0[n];
+        for (int j = 0; j * C < s1 - s0; ++j) {
+            row_tok[r + j] = s0 + j * C;
+            row_len[r + j] = min(C, s1 - s0 - j * C);
+        }
+    }
+}
+
+// ============================================================================
+// G1: per (chunk row, head): g, P = (Q K^T) o Gamma, A, T = (I + A)^{-1},
+// M = T diag(beta).  256 threads.
+// ============================================================================
+template <typename OP, int DK>
+struct PrepSmem {
+    static constexpr int PQ = DK + 4;   // operand row pitch (elements), keeps 8/16-byte alignment
+    static constexpr int PA = C + 4;    // fp32 pitch of A and T
+    static constexpr size_t q_off = 0;
+    static constexpr size_t k_off = q_off + sizeof(OP) * C * PQ;
+    static constexpr size_t a_off = k_off + sizeof(OP) * C * PQ;
+    static constexpr size_t t_off = a_off + sizeof(float) * C * PA;
+    static constexpr size_t g_off = t_off + sizeof(float) * C * PA;
+    static constexpr size_t b_off = g_off + sizeof(float) * C;
+    static constexpr size_t bytes = b_off + sizeof(float) * C;
+};
+
+template <typename in_t, typename OP, int DK>
+__global__ __launch_bounds__(256) void chunk_prep_kernel(int H, const int32_t *__restrict__ meta,
+                                                         const int32_t *__restrict__ row_tok,
+                                                         const int32_t *__restrict__ row_len,
+                                                         const in_t *__restrict__ q,
+                                                         const in_t *__restrict__ k,
+                                                         const float *__restrict__ log_alpha,
+                                                         const float *__restrict__ beta,
+                                                         float *__restrict__ ws_g,
+                                                         OP *__restrict__ ws_m,
+                                                         OP *__restrict__ ws_p) {
+    using M = Mma<OP>;
+    using frag = typename M::frag;
+    using L = PrepSmem<OP, DK>;
+    constexpr int PQ = L::PQ, PA = L::PA;
+    extern __shared__ __align__(16) unsigned char smem[];
+    OP *Qs = reinterpret_cast<OP *>(smem + L::q_off);
+    OP *Ks = reinterpret_cast<OP *>(smem + L::k_off);
+    float *As = reinterpret_cast<float *>(smem + L::a_off);
+    float *Ts = reinterpret_cast<float *>(smem + L::t_off);
+    float *gs = reinterpret_cast<float *>(smem + L::g_off);
+    float *bs = reinterpret_cast<float *>(smem + L::b_off);
+
+    const int row = blockIdx.x, h = blockIdx.y;
+    if (row >= meta[0]) return;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, nn = l & 15, jj = l >> 4;
+    const int tok0 = row_tok[row], len = row_len[row];
+    const int64_t rh = (int64_t)row * H + h;
+
+    // Stage the chunk's Q and K (rows past the end of the sequence are zero).
+    for (int idx = tid; idx < C * DK / 8; idx += 256) {
+        const int r = idx / (DK / 8), c8 = (idx % (DK / 8)) * 8;
+        float xq[8], xk[8];
+        if (r < len) {
+            const int64_t off = ((int64_t)(tok0 + r) * H + h) * DK + c8;
+            load8_f32(q + off, xq);
+            load8_f32(k + off, xk);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) xq[e] = xk[e] = 0.f;
+        }
+        lds_store8(Qs + r * PQ + c8, xq);
+        lds_store8(Ks + r * PQ + c8, xk);
+    }
+    // Gates; padded rows get log alpha = 0 and beta = 0, which leaves g flat
+    // and makes those rows inert in every later product.
+    if (w == 0) {
+        float la = 0.f, b = 0.f;
+        if (l < len) {
+            la = log_alpha[(int64_t)(tok0 + l) * H + h];
+            b = beta[(int64_t)(tok0 + l) * H + h];
+        }
+        const float g = wave_inclusive_scan(la);
+        gs[l] = g;
+        bs[l] = b;
+        ws_g[rh * C + l] = g;
+    }
+    __syncthreads();
+
+    // Lower-triangular 16x16 tiles of Q K^T (10) and K K^T (10).
+    for (int t = w; t < 2 * kTriTiles; t += 4) {
+        const bool isq = t < kTriTiles;
+        const int tl = isq ? t : t - kTriTiles;
+        int a, b;
+        tri_decode(tl, a, b);
+        const OP *asrc = (isq ? Qs : Ks) + (16 * a + nn) * PQ + 4 * jj;
+        const OP *bsrc = Ks + (16 * b + nn) * PQ + 4 * jj;
+        float4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kt = 0; kt < DK / 16; kt += M::KT_PER_ISSUE) {
+            const frag a0 = lds_frag(asrc + 16 * kt), b0 = lds_frag(bsrc + 16 * kt);
+            const frag a1 = M::KT_PER_ISSUE == 2 ? lds_frag(asrc + 16 * kt + 16) : a0;
+            const frag b1 = M::KT_PER_ISSUE == 2 ? lds_frag(bsrc + 16 * kt + 16) : b0;
+            M::issue(acc, a0, a1, b0, b1);
+        }
+        const int c = 16 * b + nn;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 16 * a + 4 * jj + i;
+            const float gam = (c <= r) ? expf(gs[r] - gs[c]) : 0.f;
+            if (isq)
+                ws_p[(rh * kTriTiles + tl) * kTileElems + (4 * jj + i) * 16 + nn] = from_f32<OP>(gam * acc[i]);
+            else
+                As[r * PA + c] = (c < r) ? bs[r] * gam * acc[i] : 0.f;
+        }
+    }
+    __syncthreads();
+
+    // T = (I + A)^{-1}.  Diagonal 16x16 blocks by forward substitution, one
+    // column per lane (wave 0: lane group jj = block, nn = column).
+    if (w == 0) {
+        const int blk = jj, col = nn;
+        float x[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float acc = (r == col) ? 1.f : 0.f;
+#pragma unroll
+            for (int i = 0; i < r; ++i) acc -= As[(16 * blk + r) * PA + 16 * blk + i] * x[i];
+            x[r] = acc;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) Ts[(16 * blk + r) * PA + 16 * blk + col] = x[r];
+    }
+    __syncthreads();
+    // Off-diagonal blocks, by distance d below the diagonal:
+    //   T_ab = -T_aa * sum_{b <= m < a} A_am T_mb     (fp32 matrix cores)
+    for (int d = 1; d < 4; ++d) {
+        if (w < 4 - d) {
+            const int b = w, a = w + d;
+            float4_t X = {0.f, 0.f, 0.f, 0.f};
+            for (int m = b; m < a; ++m) {
+                const float4_t af = *reinterpret_cast<const float4_t *>(As + (16 * a + nn) * PA + 16 * m + 4 * jj);
+                float4_t bf;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) bf[i] = Ts[(16 * m + 4 * jj + i) * PA + 16 * b + nn];
+                Mma<float>::issue(X, af, af, bf, bf);
+            }
+            const float4_t tf = *reinterpret_cast<const float4_t *>(Ts + (16 * a + nn) * PA + 16 * a + 4 * jj);
+            float4_t Y = {0.f, 0.f, 0.f, 0.f};
+            Mma<float>::issue(Y, tf, tf, X, X);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Ts[(16 * a + 4 * jj + i) * PA + 16 * b + nn] = -Y[i];
+        }
+        __syncthreads();
+    }
+
+    // M = T diag(beta), lower tiles packed.
+    for (int e = tid; e < kTriTiles * kTileElems; e += 256) {
+        const int tl = e >> 8, rr = (e >> 4) & 15, cc = e & 15;
+        int a, b;
+        tri_decode(tl, a, b);
+        const int r = 16 * a + rr, c = 16 * b + cc;
+        const float val = (c <= r) ? Ts[r * PA + c] * bs[c] : 0.f;
+        ws_m[rh * kTriTiles * kTileElems + e] = from_f32<OP>(val);
+    }
+}
+
+// ============================================================================
+// G2: serial state pass.  Block = NW waves = 16*NW value columns of one
+// (sequence, head).  Blocks of one (sequence, head) are placed on the same
+// XCD (workgroups are dispatched to the 8 XCDs round-robin by block id) so
+// the Q, K, M, P blocks they all read are shared through that XCD's L2.
+// ============================================================================
+template <typename OP, int DK>
+struct StateSmem {
+    static constexpr int PQ = DK + 4;       // Q, K row pitch
+    static constexpr int PT = C + 4;        // K^T row pitch
+    static constexpr int PM = 16 + 4;       // packed tile row pitch (M, P)
+    static constexpr size_t q_off = 0;
+    static constexpr size_t k_off = q_off + sizeof(OP) * C * PQ;
+    static constexpr size_t kt_off = k_off + sizeof(OP) * C * PQ;
+    static constexpr size_t m_off = kt_off + sizeof(OP) * DK * PT;
+    static constexpr size_t p_off = m_off + sizeof(OP) * kTriTiles * 16 * PM;
+    static constexpr size_t g_off = p_off + sizeof(OP) * kTriTiles * 16 * PM;
+    static constexpr size_t bytes = g_off + sizeof(float) * C;
+};
+
+template <typename in_t, typename OP, int DK, int NW>
+__global__ __launch_bounds__(64 * NW) void chunk_state_kernel(
+    int NH, int H, int DV, int nvt, int odt, const int32_t *__restrict__ meta,
+    const int32_t *__restrict__ cu_ws, const int32_t *__restrict__ row0,
+    const in_t *__restrict__ q, const in_t *__restrict__ k, const in_t *__restrict__ v,
+    const float *__restrict__ ws_g, const OP *__restrict__ ws_m, const OP *__restrict__ ws_p,
+    const float *init_state, float *final_state, void *__restrict__ o) {
+    using M = Mma<OP>;
+    using frag = typename M::frag;
+    using L = StateSmem<OP, DK>;
+    constexpr int PQ = L::PQ, PT = L::PT, PM = L::PM;
+    constexpr int NT = 64 * NW;       // threads
+    constexpr int KT = DK / 16;       // k-tiles along dk
+    constexpr int VEC = 16 / sizeof(OP);
+    extern __shared__ __align__(16) unsigned char smem[];
+    OP *Qs = reinterpret_cast<OP *>(smem + L::q_off);
+    OP *Ks = reinterpret_cast<OP *>(smem + L::k_off);
+    OP *KTs = reinterpret_cast<OP *>(smem + L::kt_off);
+    OP *Ms = reinterpret_cast<OP *>(smem + L::m_off);
+    OP *Ps = reinterpret_cast<OP *>(smem + L::p_off);
+    float *gs = reinterpret_cast<float *>(smem + L::g_off);
+
+    if (meta[1] != 0) return;
+    const int bid = blockIdx.x, xcd = bid & 7, slot = bid >> 3;
+    const int chain = (slot / nvt) * 8 + xcd, vt = slot % nvt;
+    if (chain >= NH) return;
+    const int n = chain / H, h = chain % H;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, nn = l & 15, jj = l >> 4;
+    const int v0 = (vt * NW + w) * 16;
+    const bool active = v0 < DV;
+    const int tok0 = cu_ws[n];
+    const int len_seq = cu_ws[n + 1] - tok0;
+    const int r0 = row0[n];
+    const int nchunks = (len_seq + C - 1) / C;
+
+    // S^T tiles: sT[mt][i] = S[v0 + nn][16 mt + 4 jj + i].
+    float4_t sT[KT];
+    const int64_t st_base = ((int64_t)chain * DV + v0 + nn) * DK + 4 * jj;
+#pragma unroll
+    for (int mt = 0; mt < KT; ++mt) {
+        if (active && init_state)
+            sT[mt] = *reinterpret_cast<const float4_t *>(init_state + st_base + 16 * mt);
+        else
+            sT[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
+    }
+
+    for (int ci = 0; ci < nchunks; ++ci) {
+        const int64_t rh = (int64_t)(r0 + ci) * H + h;
+        const int t0 = tok0 + ci * C;
+        const int len = min(C, len_seq - ci * C);
+        __syncthreads();
+        // ---- stage the chunk's shared operands ----
+        for (int idx = tid; idx < C * DK / 8; idx += NT) {
+            const int r = idx / (DK / 8), c8 = (idx % (DK / 8)) * 8;
+            float xq[8], xk[8];
+            if (r < len) {
+                const int64_t off = ((int64_t)(t0 + r) * H + h) * DK + c8;
+                load8_f32(q + off, xq);
+                load8_f32(k + off, xk);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) xq[e] = xk[e] = 0.f;
+            }
+            lds_store8(Qs + r * PQ + c8, xq);
+            lds_store8(Ks + r * PQ + c8, xk);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) KTs[(c8 + e) * PT + r] = from_f32<OP>(xk[e]);
+        }
+        for (int idx = tid; idx < kTriTiles * kTileElems / VEC; idx += NT) {
+            const int e = idx * VEC, tl = e >> 8, rr = (e >> 4) & 15, cc = e & 15;
+            const int4 mv = *reinterpret_cast<const int4 *>(ws_m + rh * kTriTiles * kTileElems + e);
+            const int4 pv = *reinterpret_cast<const int4 *>(ws_p + rh * kTriTiles * kTileElems + e);
+            // 16-byte vector split in two 8-byte LDS writes (tile rows are 8-byte aligned).
+            int2 *md = reinterpret_cast<int2 *>(Ms + (tl * 16 + rr) * PM + cc);
+            int2 *pd = reinterpret_cast<int2 *>(Ps + (tl * 16 + rr) * PM + cc);
+            md[0] = int2{mv.x, mv.y};
+            md[1] = int2{mv.z, mv.w};
+            pd[0] = int2{pv.x, pv.y};
+            pd[1] = int2{pv.z, pv.w};
+        }
+        if (tid < C) gs[tid] = ws_g[rh * C + tid];
+        __syncthreads();
+        if (!active) continue;
+
+        // ---- per-wave work on 16 value columns ----
+        float eg[4][4];   // exp(g_r) for the rows this lane holds in accumulator tiles
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) eg[mt][i] = expf(gs[16 * mt + 4 * jj + i]);
+        const float g_last = gs[C - 1];
+
+        // S^T as B operand (fp16 or fp32), reused by all 8 row tiles.
+        frag sB[KT];
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) sB[kt] = M::cvt(sT[kt]);
+
+        // X = [Q; K] S^T  (8 row tiles of 16 rows)
+        float4_t X[8];
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) {
+            X[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
+            const OP *asrc = (mt < 4 ? Qs : Ks) + (16 * (mt & 3) + nn) * PQ + 4 * jj;
+#pragma unroll
+            for (int kt = 0; kt < KT; kt += M::KT_PER_ISSUE) {
+                const frag a0 = lds_frag(asrc + 16 * kt);
+                const frag a1 = M::KT_PER_ISSUE == 2 ? lds_frag(asrc + 16 * kt + 16) : a0;
+                const frag b1 = M::KT_PER_ISSUE == 2 ? sB[kt + 1 < KT ? kt + 1 : kt] : sB[kt];
+                M::issue(X[mt], a0, a1, sB[kt], b1);
+            }
+        }
+
+        // Y = V - diag(gamma) X_K, as B operand.
+        frag yB[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            float4_t y;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * mt + 4 * jj + i;
+                const float vv = (r < len) ? to_f32(v[((int64_t)(t0 + r) * H + h) * DV + v0 + nn]) : 0.f;
+                y[i] = vv - eg[mt][i] * X[4 + mt][i];
+            }
+            yB[mt] = M::cvt(y);
+        }
+
+        // V' = M Y  (M lower triangular: k-tiles 0..mt)
+        float4_t Vp[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            Vp[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kt = 0; kt <= mt; kt += M::KT_PER_ISSUE) {
+                const frag a0 = lds_frag(Ms + (tri_index(mt, kt) * 16 + nn) * PM + 4 * jj);
+                frag a1 = M::zero(), b1 = M::zero();
+                if (M::KT_PER_ISSUE == 2 && kt + 1 <= mt) {
+                    a1 = lds_frag(Ms + (tri_index(mt, kt + 1) * 16 + nn) * PM + 4 * jj);
+                    b1 = yB[kt + 1];
+                }
+                M::issue(Vp[mt], a0, a1, yB[kt], b1);
+            }
+        }
+
+        // O = diag(gamma) X_Q + P V'
+        frag vB[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) vB[mt] = M::cvt(Vp[mt]);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            float4_t acc;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] = eg[mt][i] * X[mt][i];
+#pragma unroll
+            for (int kt = 0; kt <= mt; kt += M::KT_PER_ISSUE) {
+                const frag a0 = lds_frag(Ps + (tri_index(mt, kt) * 16 + nn) * PM + 4 * jj);
+                frag a1 = M::zero(), b1 = M::zero();
+                if (M::KT_PER_ISSUE == 2 && kt + 1 <= mt) {
+                    a1 = lds_frag(Ps + (tri_index(mt, kt + 1) * 16 + nn) * PM + 4 * jj);
+                    b1 = vB[kt + 1];
+                }
+                M::issue(acc, a0, a1, vB[kt], b1);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * mt + 4 * jj + i;
+                if (r < len) store_out(o, ((int64_t)(t0 + r) * H + h) * DV + v0 + nn, odt, acc[i]);
+            }
+        }
+
+        // S^T <- gamma^C S^T + K^T (diag(exp(g_C - g_r)) V')
+        frag dB[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            float4_t x;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[i] = Vp[mt][i] * expf(g_last - gs[16 * mt + 4 * jj + i]);
+            dB[mt] = M::cvt(x);
+        }
+        const float gC = expf(g_last);
+#pragma unroll
+        for (int mt = 0; mt < KT; ++mt) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sT[mt][i] *= gC;
+            const OP *asrc = KTs + (16 * mt + nn) * PT + 4 * jj;
+#pragma unroll
+            for (int kt = 0; kt < 4; kt += M::KT_PER_ISSUE) {
+                const frag a0 = lds_frag(asrc + 16 * kt);
+                const frag a1 = M::KT_PER_ISSUE == 2 ? lds_frag(asrc + 16 * kt + 16) : a0;
+                const frag b1 = M::KT_PER_ISSUE == 2 ? dB[kt + 1 < 4 ? kt + 1 : kt] : dB[kt];
+                M::issue(sT[mt], a0, a1, dB[kt], b1);
+            }
+        }
+    }
+
+    if (active && final_state) {
+#pragma unroll
+        for (int mt = 0; mt < KT; ++mt)
+            *reinterpret_cast<float4_t *>(final_state + st_base + 16 * mt) = sT[mt];
+    }
+}
+
+// ============================================================================
+// Host side: workspace layout and launches.
+// ============================================================================
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+ChunkWorkspace chunk_workspace_layout(int32_t B, int32_t T, int32_t N, bool packed, int32_t H,
+                                      int32_t in_dtype) {
+    ChunkWorkspace w{};
+    const int64_t per_row = (T + C - 1) / C;
+    w.max_rows = packed ? per_row + N : (int64_t)B * per_row;
+    const size_t op = in_dtype == DT_FP32 ? 4 : 2;
+    size_t off = 0;
+    w.off_meta = off;   off = align256(off + 8 * sizeof(int32_t));
+    w.off_cu = off;     off = align256(off + sizeof(int32_t) * (size_t)(N + 1));
+    w.off_row0 = off;   off = align256(off + sizeof(int32_t) * (size_t)N);
+    w.off_rowtok = off; off = align256(off + sizeof(int32_t) * (size_t)w.max_rows);
+    w.off_rowlen = off; off = align256(off + sizeof(int32_t) * (size_t)w.max_rows);
+    w.off_g = off;      off = align256(off + sizeof(float) * (size_t)w.max_rows * H * C);
+    w.off_m = off;      off = align256(off + op * (size_t)w.max_rows * H * kTriTiles * kTileElems);
+    w.off_p = off;      off = align256(off + op * (size_t)w.max_rows * H * kTriTiles * kTileElems);
+    w.total = off;
+    return w;
+}
+
+static int state_waves_per_block(int64_t NH, int DV) {
+    const char *env = getenv("GDN_STATE_WAVES");
+    if (env) {
+        const int x = atoi(env);
+        if (x == 1 || x == 2 || x == 4) return x;
+    }
+    const int tiles = (DV + 15) / 16;
+    for (int nw : {4, 2}) {
+        const int64_t blocks = NH * ((tiles + nw - 1) / nw);
+        if (blocks >= 256) return nw;
+    }
+    return 1;
+}
+
+template <typename K>
+static hipError_t allow_smem(K kernel, size_t bytes) {
+    if (bytes <= 64 * 1024) return hipSuccess;
+    return hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+template <typename in_t, typename OP, int DK, int NW>
+static hipError_t launch_state(const ChunkArgs &a, const ChunkWorkspace &w, hipStream_t st) {
+    using L = StateSmem<OP, DK>;
+    auto kern = chunk_state_kernel<in_t, OP, DK, NW>;
+    hipError_t e = allow_smem(kern, L::bytes);
+    if (e != hipSuccess) return e;
+    char *ws = static_cast<char *>(a.workspace);
+    const int64_t NH = (int64_t)a.N * a.H;
+    const int nvt = ((a.dv + 15) / 16 + NW - 1) / NW;
+    const int64_t blocks = ((NH + 7) / 8) * 8 * nvt;
+    ProfScope prof("gdn_chunk_state", st);
+    kern<<<dim3((unsigned)blocks), dim3(64 * NW), L::bytes, st>>>(
+        (int)NH, a.H, a.dv, nvt, a.out_dtype, reinterpret_cast<const int32_t *>(ws + w.off_meta),
+        reinterpret_cast<const int32_t *>(ws + w.off_cu), reinterpret_cast<const int32_t *>(ws + w.off_row0),
+        static_cast<const in_t *>(a.q), static_cast<const in_t *>(a.k), static_cast<const in_t *>(a.v),
+        reinterpret_cast<const float *>(ws + w.off_g), reinterpret_cast<const OP *>(ws + w.off_m),
+        reinterpret_cast<const OP *>(ws + w.off_p), a.init_state, a.final_state, a.o);
+    return hipGetLastError();
+}
+
+template <typename in_t, typename OP, int DK>
+static hipError_t launch_dk(const ChunkArgs &a, const ChunkWorkspace &w, hipStream_t st) {
+    char *ws = static_cast<char *>(a.workspace);
+    if (w.max_rows > 0) {   // no tokens at all: only the state pass runs (final = initial)
+        using L = PrepSmem<OP, DK>;
+        auto kern = chunk_prep_kernel<in_t, OP, DK>;
+        hipError_t e = allow_smem(kern, L::bytes);
+        if (e != hipSuccess) return e;
+        ProfScope prof("gdn_chunk_prep", st);
+        kern<<<dim3((unsigned)w.max_rows, (unsigned)a.H), dim3(256), L::bytes, st>>>(
+            a.H, reinterpret_cast<const int32_t *>(ws + w.off_meta),
+            reinterpret_cast<const int32_t *>(ws + w.off_rowtok),
+            reinterpret_cast<const int32_t *>(ws + w.off_rowlen), static_cast<const in_t *>(a.q),
+            static_cast<const in_t *>(a.k), a.log_alpha, a.beta, reinterpret_cast<float *>(ws + w.off_g),
+            reinterpret_cast<OP *>(ws + w.off_m), reinterpret_cast<OP *>(ws + w.off_p));
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    switch (state_waves_per_block((int64_t)a.N * a.H, a.dv)) {
+    case 4: return launch_state<in_t, OP, DK, 4>(a, w, st);
+    case 2: return launch_state<in_t, OP, DK, 2>(a, w, st);
+    default: return launch_state<in_t, OP, DK, 1>(a, w, st);
+    }
+}
+
+template <typename in_t, typename OP>
+static hipError_t launch_typed(const ChunkArgs &a, const ChunkWorkspace &w, hipStream_t st) {
+    switch (a.dk) {
+    case 32: return launch_dk<in_t, OP, 32>(a, w, st);
+    case 64: return launch_dk<in_t, OP, 64>(a, w, st);
+    case 128: return launch_dk<in_t, OP, 128>(a, w, st);
+    case 256:
+        if constexpr (sizeof(OP) == 2) return launch_dk<in_t, OP, 256>(a, w, st);
+        return hipErrorInvalidValue;
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_chunk_fwd(const ChunkArgs &a, hipStream_t st) {
+    const bool packed = a.cu_seqlens != nullptr;
+    const ChunkWorkspace w = chunk_workspace_layout(a.B, a.T, a.N, packed, a.H, a.in_dtype);
+    char *ws = static_cast<char *>(a.workspace);
+    {
+        ProfScope prof("gdn_chunk_table", st);
+        chunk_table_kernel<<<1, 256, 0, st>>>(a.N, a.T, packed ? 1 : 0, a.cu_seqlens,
+                                             reinterpret_cast<int32_t *>(ws + w.off_meta),
+                                             reinterpret_cast<int32_t *>(ws + w.off_cu),
+                                             reinterpret_cast<int32_t *>(ws + w.off_row0),
+                                             reinterpret_cast<int32_t *>(ws + w.off_rowtok),
+                                             reinterpret_cast<int32_t *>(ws + w.off_rowlen));
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    switch (a.in_dtype) {
+    case DT_FP32: return launch_typed<float, float>(a, w, st);
+    case DT_BF16: return launch_typed<bf16_t, _Float16>(a, w, st);
+    case DT_FP16: return launch_typed<_Float16, _Float16>(a, w, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace gdn

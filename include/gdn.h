@@ -1,0 +1,225 @@
+/*
+ * gdn.h -- C ABI of the gated delta rule layer core for MI355X (gfx950).
+ *
+ * The operation (Gated Delta Networks paper, section 3.1, eq. (10)):
+ *
+ *     S_t = S_{t-1} ( alpha_t (I - beta_t k_t k_t^T) ) + beta_t v_t k_t^T
+ *     o_t = S_t q_t                      S_t in R^{dv x dk},  alpha_t = exp(log_alpha_t)
+ *
+ * evaluated two ways:
+ *   gdn_chunk_fwd    -- chunkwise-parallel prefill over whole sequences
+ *                       (paper section 3.3, the WY/UT chunk algorithm with the
+ *                       decay mask; paper-notes blog, "Hardware-Efficient
+ *                       Chunkwise Training", summary (4)), optionally packed
+ *                       with cu_seqlens, from an initial state, returning the
+ *                       final state.
+ *   gdn_decode_step  -- one token of the recurrence for a batch of resident
+ *                       states, updated in place (tutorial page, decode
+ *                       recursion S_t = S_{t-1} A_t + B_t).
+ *
+ * Both return the same numbers as the recurrence up to floating-point
+ * rounding.  Chunked, single-step and save-then-resume evaluations agree
+ * (tutorial: the three paths must line up; independent samples reset the
+ * state, a continued request does not).
+ *
+ * CONVENTIONS (all calls)
+ *   - Every pointer argument except `stream` is a DEVICE pointer (HBM) unless
+ *     stated otherwise.  Tensors are dense, row-major, last index fastest.
+ *   - The caller owns every buffer.  The library keeps no pointer after the
+ *     call returns and allocates no device memory on these paths.
+ *   - Work is enqueued on `stream` (NULL = the default stream) and the call
+ *     returns without waiting.  Buffers must stay valid until the stream
+ *     reaches that point.  A kernel fault shows up at the caller's next
+ *     synchronisation, as for any HIP launch.
+ *   - All argument checks run before anything is enqueued: a call that
+ *     returns an error status has launched nothing and written nothing.
+ *     gdn_last_error_message() then describes the failure (thread-local).
+ *   - Device pointers must be 16-byte aligned (GDN_ERR_ALIGN otherwise).
+ *   - Calls are reentrant and may run concurrently on different streams with
+ *     disjoint buffers.
+ *   - Preconditions that are documented but NOT checked on the device:
+ *     finite inputs; log_alpha <= 0; beta in [0, 1] (any finite beta is
+ *     computed as given); q and k normalised upstream (the paper normalises
+ *     them in the token-mixing block, section 3.4).  With 16-bit inputs the
+ *     matrix-core operands are fp16, so |q|, |k|, |v| and the state entries
+ *     must stay below 65504.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_ABI_VERSION 1
+
+typedef enum {
+    GDN_OK = 0,
+    GDN_ERR_NULL = 1,         /* a required pointer is NULL                       */
+    GDN_ERR_SHAPE = 2,        /* sizes negative, zero where not allowed, or
+                                 inconsistent                                     */
+    GDN_ERR_DTYPE = 3,        /* unknown dtype code                               */
+    GDN_ERR_ALIGN = 4,        /* a device pointer is not 16-byte aligned          */
+    GDN_ERR_UNSUPPORTED = 5,  /* well-formed but not built (head dims, chunk size,
+                                 dtype combination)                               */
+    GDN_ERR_WORKSPACE = 6,    /* workspace NULL or smaller than required          */
+    GDN_ERR_HIP = 7,          /* a HIP runtime call or launch failed              */
+    GDN_ERR_ALIAS = 8,        /* an output overlaps an input it may not overlap   */
+    GDN_ERR_DEVICE_INPUT = 9  /* device-side validation failed (gdn_chunk_fwd_check) */
+} gdn_status;
+
+typedef enum {
+    GDN_FP32 = 0,
+    GDN_BF16 = 1,
+    GDN_FP16 = 2
+} gdn_dtype;
+
+/*
+ * Shape of one gdn_chunk_fwd call.
+ *   batch     B  >= 1: batch rows.  Must be 1 when cu_seqlens is given.
+ *   seqlen    T  >= 0: tokens per batch row (packed batch: total tokens).
+ *   heads     H  >= 1.
+ *   dk           key/query head dim: 32, 64, 128 or 256 (fp32 inputs: <= 128).
+ *   dv           value head dim: a multiple of 16, 16..1024.
+ *   num_seqs  N: number of sequences.  Without cu_seqlens it must equal B
+ *                (row b is sequence b); with cu_seqlens, N >= 1 and the
+ *                cu_seqlens array holds N+1 offsets.
+ *   chunk     C: chunk length; 64 is the supported value.
+ *   in_dtype     dtype of q, k, v (FP32, BF16 or FP16).  BF16/FP16 inputs run
+ *                the matrix products on fp16 operands with fp32 accumulation
+ *                and an fp32 state; FP32 inputs run them on fp32 operands.
+ *   out_dtype    dtype of o (FP32, BF16 or FP16).
+ */
+typedef struct {
+    int32_t batch;
+    int32_t seqlen;
+    int32_t heads;
+    int32_t dk;
+    int32_t dv;
+    int32_t num_seqs;
+    int32_t chunk;
+    int32_t in_dtype;   /* gdn_dtype */
+    int32_t out_dtype;  /* gdn_dtype */
+} gdn_chunk_desc;
+
+/* ABI version of the loaded library (GDN_ABI_VERSION at build time). */
+int gdn_abi_version(void);
+
+/* Static, human-readable name of a status code. */
+const char *gdn_status_string(gdn_status status);
+
+/* Detail of the last failed call on this thread ("" if none).  The pointer is
+ * valid until the next gdn_* call on the same thread. */
+const char *gdn_last_error_message(void);
+
+/*
+ * Workspace for gdn_chunk_fwd, in bytes, written to *bytes (host pointer).
+ * Depends only on the descriptor.  The workspace holds the chunk table built
+ * from cu_seqlens and, per (chunk, head), the UT-transform matrix
+ * T diag(beta), the decay-masked Q K^T block and the chunk's cumulative
+ * log-decay.  It need not be initialised and may be reused by later calls
+ * that are ordered after this one on the stream.
+ * Errors: GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_DTYPE, GDN_ERR_UNSUPPORTED.
+ */
+gdn_status gdn_chunk_fwd_workspace_size(const gdn_chunk_desc *desc, size_t *bytes);
+
+/*
+ * Chunkwise-parallel forward pass (prefill).
+ *
+ *   q           [B, T, H, dk]  in_dtype
+ *   k           [B, T, H, dk]  in_dtype
+ *   v           [B, T, H, dv]  in_dtype
+ *   log_alpha   [B, T, H]      fp32, log of the forget gate alpha_t
+ *   beta        [B, T, H]      fp32, write strength beta_t
+ *   init_state  [N, H, dv, dk] fp32 or NULL (zeros).  S[n,h] maps keys to
+ *                              values, row index = value dim (paper 2.1).
+ *   cu_seqlens  int32 [N+1] or NULL.  Packed batch (B == 1): sequence n is
+ *               tokens cu[n] .. cu[n+1]-1 of the T axis; cu[0] = 0,
+ *               non-decreasing, cu[N] = T.  Empty sequences are allowed
+ *               (their final state equals their initial state).  The state
+ *               restarts from init_state[n] at every sequence start, and
+ *               chunks restart there too (the last chunk of a sequence may
+ *               be partial).  The array is checked on the device; a
+ *               malformed one makes the kernels write nothing and is
+ *               reported by gdn_chunk_fwd_check.
+ *   o           [B, T, H, dv]  out_dtype (written)
+ *   final_state [N, H, dv, dk] fp32 or NULL (not returned).  May be the
+ *               same pointer as init_state (in-place continuation): each
+ *               state tile is read before it is written and tiles are
+ *               disjoint.  Partial overlap with init_state is not allowed.
+ *   workspace   device buffer of at least gdn_chunk_fwd_workspace_size bytes
+ *   stream      HIP stream the three kernels are launched on
+ *
+ * o must not overlap any input or the state buffers (GDN_ERR_ALIAS).
+ * Errors: GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_DTYPE, GDN_ERR_ALIGN,
+ * GDN_ERR_UNSUPPORTED, GDN_ERR_WORKSPACE, GDN_ERR_ALIAS, GDN_ERR_HIP.
+ */
+gdn_status gdn_chunk_fwd(const gdn_chunk_desc *desc,
+                         const void *q, const void *k, const void *v,
+                         const float *log_alpha, const float *beta,
+                         const float *init_state, const int32_t *cu_seqlens,
+                         void *o, float *final_state,
+                         void *workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
+/*
+ * Result of the device-side cu_seqlens check of the last gdn_chunk_fwd that
+ * used `workspace`.  Synchronises `stream`, then writes 0 (valid) or a
+ * non-zero code (1: cu[0] != 0, 2: decreasing offsets, 3: cu[N] != T) to
+ * *code (host pointer).  Returns GDN_ERR_DEVICE_INPUT when the code is
+ * non-zero, GDN_OK otherwise.
+ */
+gdn_status gdn_chunk_fwd_check(const void *workspace, hipStream_t stream, int32_t *code);
+
+/*
+ * One decode step for N resident states, in place.
+ *
+ *   state      [N, H, dv, dk] fp32, read and overwritten with S_t
+ *   q, k       [N, H, dk]     in_dtype
+ *   v          [N, H, dv]     in_dtype
+ *   log_alpha  [N, H]         fp32
+ *   beta       [N, H]         fp32
+ *   o          [N, H, dv]     out_dtype, o = S_t q (read after the update)
+ *
+ * Per (n, h) it computes, reading each state row once and writing it once:
+ *   Sbar = alpha S;  u = beta (v - Sbar k);  S_t = Sbar + u k^T;
+ *   o = alpha (S q) + u (k . q)
+ * (tutorial page: forget first, then correct the error of the decayed
+ * memory).  dk: a multiple of 8, 8..256.  dv: 1..4096.
+ * o must not overlap state.
+ * Errors: GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_DTYPE, GDN_ERR_ALIGN,
+ * GDN_ERR_UNSUPPORTED, GDN_ERR_ALIAS, GDN_ERR_HIP.
+ */
+gdn_status gdn_decode_step(int32_t N, int32_t H, int32_t dk, int32_t dv,
+                           int32_t in_dtype, int32_t out_dtype,
+                           float *state,
+                           const void *q, const void *k, const void *v,
+                           const float *log_alpha, const float *beta,
+                           void *o, hipStream_t stream);
+
+/*
+ * Per-kernel timing for measurement harnesses (host-side bookkeeping only;
+ * kernels are unchanged).  While enabled, every launch made by this library
+ * is bracketed by a pair of HIP events recorded on the launch stream.
+ *   gdn_profile_enable(1) clears previous records and starts recording;
+ *   gdn_profile_enable(0) stops recording.
+ *   gdn_profile_read synchronises the recorded events and reports, for the
+ *   i-th distinct kernel name (0 <= i < count), its name (static string),
+ *   the number of recorded launches and their summed duration in ms.
+ * gdn_profile_read(i, ...) with i >= count returns GDN_ERR_SHAPE.
+ */
+gdn_status gdn_profile_enable(int32_t on);
+gdn_status gdn_profile_count(int32_t *count);
+gdn_status gdn_profile_read(int32_t index, const char **name, int64_t *launches,
+                            double *total_ms);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */
