@@ -1,6 +1,7 @@
 """Benchmark of the gated delta rule core on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+                    [--only prefill|decode]
 
 A step is one chunked prefill over the prefill workload (B=4, H=16, L=4096,
 dk=dv=128, C=64, bf16 q/k/v, fp32 gates, fp32 o and states), inputs resident
@@ -12,7 +13,8 @@ roofline objects use the algorithmic bytes and flops of the method (counted
 below) over that duration.  The CPU baseline is the fp64 oracle on a bounded
 sample of the prefill workload, on all host cores.
 
-Prints ONE JSON line.
+Prints ONE JSON line.  --only runs a single leg (for profiler runs) and
+prints that leg's part of the line.
 """
 import argparse
 import json
@@ -36,6 +38,7 @@ def chunk_flops_per_token_head(dk, dv, c=C):
 
 
 def chunk_min_bytes(B, T, H, dk, dv, N, in_bytes, out_bytes, has_init, has_final):
+    # q, k, v in; log_alpha and beta in; o out; initial and final states
     th = B * T * H
     b = th * (2 * dk + dv) * in_bytes + th * 2 * 4 + th * dv * out_bytes
     st = N * H * dv * dk * 4
@@ -43,46 +46,23 @@ def chunk_min_bytes(B, T, H, dk, dv, N, in_bytes, out_bytes, has_init, has_final
 
 
 def decode_min_bytes(N, H, dk, dv, in_bytes, out_bytes):
+    # the fp32 state read and written once, q, k, v and gates in, o out
     nh = N * H
     return nh * dv * dk * 4 * 2 + nh * (2 * dk + dv) * in_bytes + nh * 2 * 4 + nh * dv * out_bytes
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--decode-steps", type=int, default=1000)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the path has no multi-GPU mode; "
-              "(sequence, head) pairs are independent and would be sharded with no communication.",
-              file=sys.stderr)
-        sys.exit(2)
-
+def _to(x, dev, dt):
     import numpy as np
     import torch
+    return torch.from_numpy(np.ascontiguousarray(x)).to(dev, dt)
 
-    import gated_delta_rule_24_amd as gdn
-    import workloads as W
 
-    if not os.path.exists(gdn.lib_path()):
-        from gated_delta_rule_24_amd import build as gbuild
-        gbuild.build()
-    gdn.load()
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-
-    def to(x, dt=torch.float32):
-        return torch.from_numpy(np.ascontiguousarray(x)).to(dev, dt)
-
-    # ---------------- prefill ----------------
+def run_prefill(args, gdn, W, dev):
+    import torch
     inp = W.prefill()
     B, T, H, dk, dv = inp.B, inp.T, inp.H, inp.dk, inp.dv
-    q, k, v = to(inp.q, torch.bfloat16), to(inp.k, torch.bfloat16), to(inp.v, torch.bfloat16)
-    la, be = to(inp.log_alpha), to(inp.beta)
+    q, k, v = (_to(x, dev, torch.bfloat16) for x in (inp.q, inp.k, inp.v))
+    la, be = _to(inp.log_alpha, dev, torch.float32), _to(inp.beta, dev, torch.float32)
     o = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
     fin = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
     ws = torch.empty(gdn.chunk_fwd_workspace_size(B, T, H, dk, dv, B), dtype=torch.uint8, device=dev)
@@ -92,7 +72,6 @@ def main():
 
     for _ in range(args.warmup):
         step()
-    torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     ev0.record()
@@ -101,7 +80,6 @@ def main():
     ev1.record()
     torch.cuda.synchronize()
     ms_per_step = ev0.elapsed_time(ev1) / args.steps
-    tokens_per_s = B * T / (ms_per_step * 1e-3)
 
     # per-kernel durations (events recorded by the library around each launch)
     with gdn.profile() as prof:
@@ -129,18 +107,26 @@ def main():
         "path_hbm_frac": min_bytes / path_s / 1e9 / HBM_PEAK_GBS,
         "path_mfma_frac": flops / path_s / 1e12 / MFMA_F16_PEAK_TFLOPS,
     }
+    res = {"value": B * T / path_s, "ms_per_step": ms_per_step, "roofline": roofline, "kernels": kernels,
+           "config": {"workload": "prefill", "B": B, "L": T, "H": H, "dk": dk, "dv": dv, "chunk": C,
+                      "in_dtype": "bf16", "out_dtype": "fp32", "init_state": None, "final_state": "fp32"}}
     del q, k, v, la, be, o, fin, ws
     torch.cuda.empty_cache()
+    return res, inp
 
-    # ---------------- decode ----------------
+
+def run_decode(args, gdn, W, dev):
+    import torch
     d = W.decode()
-    Nd, Hd = d.state.shape[:2]
-    state = to(d.state)
-    pool = [(to(d.q[p], torch.bfloat16), to(d.k[p], torch.bfloat16), to(d.v[p], torch.bfloat16), to(d.log_alpha[p]),
-             to(d.beta[p])) for p in range(d.pool)]
-    od = torch.empty((Nd, Hd, d.v.shape[-1]), dtype=torch.float32, device=dev)
+    Nd, Hd, dv, dk = d.state.shape
+    state = _to(d.state, dev, torch.float32)
+    pool = [tuple(_to(x, dev, torch.bfloat16) for x in (d.q[p], d.k[p], d.v[p]))
+            + (_to(d.log_alpha[p], dev, torch.float32), _to(d.beta[p], dev, torch.float32))
+            for p in range(d.pool)]
+    od = torch.empty((Nd, Hd, dv), dtype=torch.float32, device=dev)
     for s in range(10):
         gdn.decode_step(state, *pool[s % d.pool], o=od)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     ev0.record()
     for s in range(args.decode_steps):
@@ -153,56 +139,95 @@ def main():
             gdn.decode_step(state, *pool[s % d.pool], o=od)
     n_l, ms_l = dprof.results["gdn_decode_step"]
     dec_kernel_s = ms_l / n_l * 1e-3
-    dbytes = decode_min_bytes(Nd, Hd, 128, 128, 2, 4)
-    decode = {
+    dbytes = decode_min_bytes(Nd, Hd, dk, dv, 2, 4)
+    res = {
         "value": 1e3 / dec_ms, "unit": "steps/s", "ms_per_step": dec_ms, "steps": args.decode_steps,
-        "config": {"workload": "decode", "N": int(Nd), "H": int(Hd), "dk": 128, "dv": 128, "in_dtype": "bf16",
-                   "state": "fp32 in place"},
+        "config": {"workload": "decode", "N": int(Nd), "H": int(Hd), "dk": int(dk), "dv": int(dv),
+                   "in_dtype": "bf16", "state": "fp32 in place"},
         "roofline": {"kernel": "gdn_decode_step", "bound": "hbm", "achieved": dbytes / dec_kernel_s / 1e9,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dbytes / dec_kernel_s / 1e9 / HBM_PEAK_GBS,
                      "traffic": None, "algorithmic_bytes": dbytes, "avg_us": dec_kernel_s * 1e6},
     }
     del state, pool, od
     torch.cuda.empty_cache()
+    return res
 
-    # ---------------- CPU baseline (fp64 oracle) ----------------
-    cpu = None
-    if not args.no_cpu_baseline:
-        import oracle
-        threads = oracle.num_threads()
-        sl = 64
-        while True:
-            t0 = time.perf_counter()
-            oracle.recurrent(inp.q[:, :sl], inp.k[:, :sl], inp.v[:, :sl], inp.log_alpha[:, :sl], inp.beta[:, :sl],
-                             threads=threads)
-            el = time.perf_counter() - t0
-            if el >= args.cpu_seconds or sl >= T:
-                break
-            sl = min(T, max(sl * 2, int(sl * args.cpu_seconds / max(el, 1e-3) * 1.1)))
-        cpu = {"value": B * sl / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-               "sample": f"prefill workload, first {sl} tokens of each of the {B} sequences, all {H} heads "
-                         f"(fp64 token recurrence, {el:.1f} s)"}
 
+def run_cpu_baseline(args, inp):
+    import oracle
+    threads = oracle.num_threads()
+    B, T, H = inp.B, inp.T, inp.H
+    sl = 64
+    while True:
+        t0 = time.perf_counter()
+        oracle.recurrent(inp.q[:, :sl], inp.k[:, :sl], inp.v[:, :sl], inp.log_alpha[:, :sl], inp.beta[:, :sl],
+                         threads=threads)
+        el = time.perf_counter() - t0
+        if el >= args.cpu_seconds or sl >= T:
+            break
+        sl = min(T, max(sl * 2, int(sl * args.cpu_seconds / max(el, 1e-3) * 1.1)))
+    return {"value": B * sl / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"prefill workload, first {sl} tokens of each of the {B} sequences, all {H} heads "
+                      f"(fp64 token recurrence, {el:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--only", choices=["prefill", "decode"], default=None,
+                    help="run one leg only (for profiler runs) and print its part of the line")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the path has no multi-GPU mode; "
+              "(sequence, head) pairs are independent and would be sharded with no communication.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import gated_delta_rule_24_amd as gdn
+    import workloads as W
+
+    if not os.path.exists(gdn.lib_path()):
+        from gated_delta_rule_24_amd import build as gbuild
+        gbuild.build()
+    gdn.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.only == "decode":
+        print(json.dumps({"decode": run_decode(args, gdn, W, dev)}), flush=True)
+        return
+    pre, inp = run_prefill(args, gdn, W, dev)
+    if args.only == "prefill":
+        print(json.dumps({"prefill": pre}), flush=True)
+        return
+    decode = run_decode(args, gdn, W, dev)
+    cpu = None if args.no_cpu_baseline else run_cpu_baseline(args, inp)
     out = {
         "metric": METRIC,
-        "value": tokens_per_s,
+        "value": pre["value"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": pre["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "compute": "bf16 inputs; fp16 matrix-core operands, fp32 accumulation and fp32 state",
         "data": "synthetic (seeded; q,k L2-normalised, log_alpha~U(-0.1,-0.001), beta=sigmoid(N(0,1)))",
-        "config": {"workload": "prefill", "B": B, "L": T, "H": H, "dk": dk, "dv": dv, "chunk": C,
-                   "in_dtype": "bf16", "out_dtype": "fp32", "init_state": None, "final_state": "fp32"},
-        "roofline": roofline,
+        "config": pre["config"],
+        "roofline": pre["roofline"],
         "cpu_baseline": cpu,
         "decode": decode,
-        "kernels": kernels,
+        "kernels": pre["kernels"],
         "device": torch.cuda.get_device_name(0),
     }
     print(json.dumps(out), flush=True)

@@ -160,8 +160,11 @@ struct PrepSmem {
     static constexpr size_t q_off = 0;
     static constexpr size_t k_off = q_off + sizeof(OP) * C * PQ;
     static constexpr size_t a_off = k_off + sizeof(OP) * C * PQ;
-    static constexpr size_t t_off = a_off + sizeof(float) * C * PA;
-    static constexpr size_t g_off = t_off + sizeof(float) * C * PA;
+    static constexpr size_t mat_bytes = sizeof(float) * C * PA;
+    // T reuses the Q/K region once the Gram tiles are done, when it fits.
+    static constexpr bool t_aliases = mat_bytes <= a_off;
+    static constexpr size_t t_off = t_aliases ? 0 : a_off + mat_bytes;
+    static constexpr size_t g_off = t_aliases ? a_off + mat_bytes : t_off + mat_bytes;
     static constexpr size_t b_off = g_off + sizeof(float) * C;
     static constexpr size_t bytes = b_off + sizeof(float) * C;
 };
@@ -181,6 +184,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(int H, const int32_t *_
     using frag = typename M::frag;
     using L = PrepSmem<OP, DK>;
     constexpr int PQ = L::PQ, PA = L::PA;
+    constexpr int QK_IT = C * DK / 8 / 256;
     extern __shared__ __align__(16) unsigned char smem[];
     OP *Qs = reinterpret_cast<OP *>(smem + L::q_off);
     OP *Ks = reinterpret_cast<OP *>(smem + L::k_off);
@@ -195,33 +199,46 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(int H, const int32_t *_
     const int tok0 = row_tok[row], len = row_len[row];
     const int64_t rh = (int64_t)row * H + h;
 
-    // Stage the chunk's Q and K (rows past the end of the sequence are zero).
-    for (int idx = tid; idx < C * DK / 8; idx += 256) {
+    // Issue every global load of the chunk first, then convert into LDS.
+    // Rows past the end of the sequence are zero; their gates get
+    // log alpha = 0 and beta = 0, which leaves g flat and makes those rows
+    // inert in every later product.
+    Raw8<in_t> rq[QK_IT], rk[QK_IT];
+#pragma unroll
+    for (int it = 0; it < QK_IT; ++it) {
+        const int idx = tid + it * 256;
         const int r = idx / (DK / 8), c8 = (idx % (DK / 8)) * 8;
-        float xq[8], xk[8];
         if (r < len) {
             const int64_t off = ((int64_t)(tok0 + r) * H + h) * DK + c8;
-            load8_f32(q + off, xq);
-            load8_f32(k + off, xk);
+            rq[it].load(q + off);
+            rk[it].load(k + off);
         } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) xq[e] = xk[e] = 0.f;
+            rq[it].zero();
+            rk[it].zero();
         }
-        lds_store8(Qs + r * PQ + c8, xq);
-        lds_store8(Ks + r * PQ + c8, xk);
     }
-    // Gates; padded rows get log alpha = 0 and beta = 0, which leaves g flat
-    // and makes those rows inert in every later product.
+    float la = 0.f, bt = 0.f;
+    if (w == 0 && l < len) {
+        la = log_alpha[(int64_t)(tok0 + l) * H + h];
+        bt = beta[(int64_t)(tok0 + l) * H + h];
+    }
+#pragma unroll
+    for (int it = 0; it < QK_IT; ++it) {
+        const int idx = tid + it * 256;
+        const int r = idx / (DK / 8), c8 = (idx % (DK / 8)) * 8;
+        float x[8];
+        rq[it].to_f32(x);
+        lds_store8(Qs + r * PQ + c8, x);
+        rk[it].to_f32(x);
+        lds_store8(Ks + r * PQ + c8, x);
+    }
     if (w == 0) {
-        float la = 0.f, b = 0.f;
-        if (l < len) {
-            la = log_alpha[(int64_t)(tok0 + l) * H + h];
-            b = beta[(int64_t)(tok0 + l) * H + h];
-        }
         const float g = wave_inclusive_scan(la);
+        const float g_last = __shfl(g, C - 1, 64);
         gs[l] = g;
-        bs[l] = b;
-        ws_g[rh * C + l] = g;
+        bs[l] = bt;
+        ws_g[rh * 2 * C + l] = expf(g);               // gamma_r: decay from the chunk start
+        ws_g[rh * 2 * C + C + l] = expf(g_last - g);  // kappa_r: decay from row r to the chunk end
     }
     __syncthreads();
 
@@ -292,14 +309,16 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(int H, const int32_t *_
         __syncthreads();
     }
 
-    // M = T diag(beta), lower tiles packed.
-    for (int e = tid; e < kTriTiles * kTileElems; e += 256) {
-        const int tl = e >> 8, rr = (e >> 4) & 15, cc = e & 15;
+    // M = T diag(beta), lower tiles packed, 4 consecutive elements per store.
+    for (int e4 = tid; e4 < kTriTiles * kTileElems / 4; e4 += 256) {
+        const int e = e4 * 4, tl = e >> 8, rr = (e >> 4) & 15, cc = e & 15;
         int a, b;
         tri_decode(tl, a, b);
         const int r = 16 * a + rr, c = 16 * b + cc;
-        const float val = (c <= r) ? Ts[r * PA + c] * bs[c] : 0.f;
-        ws_m[rh * kTriTiles * kTileElems + e] = from_f32<OP>(val);
+        float4_t val;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) val[i] = (c + i <= r) ? Ts[r * PA + c + i] * bs[c + i] : 0.f;
+        *reinterpret_cast<typename M::frag *>(ws_m + rh * kTriTiles * kTileElems + e) = M::cvt(val);
     }
 }
 
@@ -308,20 +327,94 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(int H, const int32_t *_
 // (sequence, head).  Blocks of one (sequence, head) are placed on the same
 // XCD (workgroups are dispatched to the 8 XCDs round-robin by block id) so
 // the Q, K, M, P blocks they all read are shared through that XCD's L2.
+// The global loads of chunk ci+1 are issued into registers before chunk ci
+// is computed, so their latency overlaps the matrix-core work.
+//
+// Products per chunk and wave (16 value columns v, S^T slice in sT):
+//   X_K = K S^T                          (C x 16)   A: K rows,         B: sT
+//   Y   = V - diag(gamma) X_K                       V read transposed
+//   V'  = M Y                            (C x 16)   A: M,              B: Y
+//   O^T = (S Q^T) diag(gamma) + V'^T P^T (16 x C)   A: sT / V',        B: Q, P rows
+//   S^T = gamma_C S^T + K^T (kappa o V') (dk x 16)  A: K read transposed, B: kappa o V'
+// Everything staged in LDS is row-major; the two transposed operands (K^T
+// and V in accumulator layout) use the 16-bit transposed LDS read.  O is
+// produced transposed so each lane holds four consecutive value columns of
+// one token row and writes them with one vector store.
 // ============================================================================
-template <typename OP, int DK>
+template <typename in_t, typename OP, int DK, int NW>
 struct StateSmem {
-    static constexpr int PQ = DK + 4;       // Q, K row pitch
-    static constexpr int PT = C + 4;        // K^T row pitch
-    static constexpr int PM = 16 + 4;       // packed tile row pitch (M, P)
+    // Pitches chosen so the 64 lanes of each operand read (and of the
+    // transposed reads) spread evenly over the 32 LDS banks.
+    static constexpr int PQ = DK + 8 / (int)sizeof(OP);      // Q, K row pitch (elements)
+    static constexpr int BV = 16 * NW;
+    static constexpr int PV = BV + 16 / (int)sizeof(in_t);   // V row pitch, 16-byte rows
+    static constexpr int PM = 16 + 4;                        // packed tile row pitch (M, P)
     static constexpr size_t q_off = 0;
     static constexpr size_t k_off = q_off + sizeof(OP) * C * PQ;
-    static constexpr size_t kt_off = k_off + sizeof(OP) * C * PQ;
-    static constexpr size_t m_off = kt_off + sizeof(OP) * DK * PT;
+    static constexpr size_t v_off = k_off + sizeof(OP) * C * PQ;
+    static constexpr size_t m_off = v_off + sizeof(in_t) * C * PV;
     static constexpr size_t p_off = m_off + sizeof(OP) * kTriTiles * 16 * PM;
     static constexpr size_t g_off = p_off + sizeof(OP) * kTriTiles * 16 * PM;
-    static constexpr size_t bytes = g_off + sizeof(float) * C;
+    static constexpr size_t bytes = g_off + sizeof(float) * 2 * C;
 };
+
+// Four fp32 values to an output row (one 8- or 16-byte store).
+__device__ __forceinline__ void store_out4(void *o, int64_t idx, int odt, float4_t v) {
+    if (odt == DT_FP32) {
+        *reinterpret_cast<float4_t *>(static_cast<float *>(o) + idx) = v;
+    } else if (odt == DT_BF16) {
+        const uint32_t a = from_f32<bf16_t>(v[0]).bits | ((uint32_t)from_f32<bf16_t>(v[1]).bits << 16);
+        const uint32_t b = from_f32<bf16_t>(v[2]).bits | ((uint32_t)from_f32<bf16_t>(v[3]).bits << 16);
+        *reinterpret_cast<uint2 *>(static_cast<bf16_t *>(o) + idx) = uint2{a, b};
+    } else {
+        *reinterpret_cast<half4_t *>(static_cast<_Float16 *>(o) + idx) =
+            half4_t{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+    }
+}
+
+// Column fragment of a row-major matrix in LDS: rows R..R+3 of column c
+// for lane (c = c0 + nn, R = row0 + 4 jj), i.e. an operand tile element
+// set {X[row0 + 4 jj + i][c0 + nn], i < 4}.  `lane_off` is the per-lane
+// offset ((4 jj + nn/4) * pitch + 4 (nn % 4)) used by the transposed read;
+// the fp32 path reads the four rows directly.
+template <typename T>
+struct ColFrag;
+template <>
+struct ColFrag<_Float16> {
+    __device__ __forceinline__ static float4_t read_f32(const _Float16 *base, int lane_off, int, int) {
+        const half4_t h = __builtin_bit_cast(half4_t, lds_read_tr16(base + lane_off));
+        return float4_t{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+    }
+};
+template <>
+struct ColFrag<bf16_t> {
+    __device__ __forceinline__ static float4_t read_f32(const bf16_t *base, int lane_off, int, int) {
+        const uint2 r = lds_read_tr16(base + lane_off);
+        return float4_t{__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xffff0000u),
+                        __uint_as_float(r.y << 16), __uint_as_float(r.y & 0xffff0000u)};
+    }
+};
+template <>
+struct ColFrag<float> {
+    // plain_off = (4 jj) * pitch + nn; rows are `pitch` apart
+    __device__ __forceinline__ static float4_t read_f32(const float *base, int, int plain_off, int pitch) {
+        const float *p = base + plain_off;
+        return float4_t{p[0], p[pitch], p[2 * pitch], p[3 * pitch]};
+    }
+};
+
+// Column fragment of K (fp16 or fp32 operand copy in LDS) for the K^T operand.
+template <typename OP>
+__device__ __forceinline__ typename Mma<OP>::frag kt_frag(const OP *base, int tr_lane, int plain_lane, int pitch);
+template <>
+__device__ __forceinline__ half4_t kt_frag<_Float16>(const _Float16 *base, int tr_lane, int, int) {
+    return __builtin_bit_cast(half4_t, lds_read_tr16(base + tr_lane));
+}
+template <>
+__device__ __forceinline__ float4_t kt_frag<float>(const float *base, int, int plain_lane, int pitch) {
+    const float *p = base + plain_lane;
+    return float4_t{p[0], p[pitch], p[2 * pitch], p[3 * pitch]};
+}
 
 template <typename in_t, typename OP, int DK, int NW>
 __global__ __launch_bounds__(64 * NW) void chunk_state_kernel(
@@ -332,18 +425,26 @@ __global__ __launch_bounds__(64 * NW) void chunk_state_kernel(
     const float *init_state, float *final_state, void *__restrict__ o) {
     using M = Mma<OP>;
     using frag = typename M::frag;
-    using L = StateSmem<OP, DK>;
-    constexpr int PQ = L::PQ, PT = L::PT, PM = L::PM;
-    constexpr int NT = 64 * NW;       // threads
-    constexpr int KT = DK / 16;       // k-tiles along dk
-    constexpr int VEC = 16 / sizeof(OP);
+    using L = StateSmem<in_t, OP, DK, NW>;
+    constexpr int PQ = L::PQ, PV = L::PV, PM = L::PM, BV = L::BV;
+    constexpr int NT = 64 * NW;                              // threads
+    constexpr int KT = DK / 16;                              // k-tiles along dk
+    constexpr int QK_UNITS = C * (DK / 8);                   // 8-element pieces of Q (and K)
+    constexpr int QK_IT = (QK_UNITS + NT - 1) / NT;
+    constexpr int V_UNITS = C * (BV / 8);
+    constexpr int V_IT = (V_UNITS + NT - 1) / NT;
+    constexpr int MP_VEC = 16 / sizeof(OP);                  // M/P elements per 16-byte load
+    constexpr int MP_N = kTriTiles * kTileElems / MP_VEC;
+    constexpr int MP_IT = (MP_N + NT - 1) / NT;
+    constexpr int G_IT = (2 * C + NT - 1) / NT;
     extern __shared__ __align__(16) unsigned char smem[];
     OP *Qs = reinterpret_cast<OP *>(smem + L::q_off);
     OP *Ks = reinterpret_cast<OP *>(smem + L::k_off);
-    OP *KTs = reinterpret_cast<OP *>(smem + L::kt_off);
+    in_t *Vs = reinterpret_cast<in_t *>(smem + L::v_off);
     OP *Ms = reinterpret_cast<OP *>(smem + L::m_off);
     OP *Ps = reinterpret_cast<OP *>(smem + L::p_off);
-    float *gs = reinterpret_cast<float *>(smem + L::g_off);
+    float *gam_s = reinterpret_cast<float *>(smem + L::g_off);   // gamma_r, then kappa_r
+    float *kap_s = gam_s + C;
 
     if (meta[1] != 0) return;
     const int bid = blockIdx.x, xcd = bid & 7, slot = bid >> 3;
@@ -351,12 +452,21 @@ __global__ __launch_bounds__(64 * NW) void chunk_state_kernel(
     if (chain >= NH) return;
     const int n = chain / H, h = chain % H;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, nn = l & 15, jj = l >> 4;
-    const int v0 = (vt * NW + w) * 16;
+    const int vb = vt * BV;                 // first value column of the block
+    const int v0 = vb + w * 16;             // first value column of this wave
     const bool active = v0 < DV;
     const int tok0 = cu_ws[n];
     const int len_seq = cu_ws[n + 1] - tok0;
     const int r0 = row0[n];
     const int nchunks = (len_seq + C - 1) / C;
+
+    // Per-lane LDS offsets (elements) of the operand reads.
+    const int row_lane = nn * PQ + 4 * jj;                        // row-fragment reads of Q, K
+    const int trk_lane = (4 * jj + (nn >> 2)) * PQ + 4 * (nn & 3);  // transposed K reads
+    const int plk_lane = 4 * jj * PQ + nn;                          // fp32 direct column reads of K
+    const int trv_lane = (4 * jj + (nn >> 2)) * PV + 4 * (nn & 3) + 16 * w;
+    const int plv_lane = 4 * jj * PV + nn + 16 * w;
+    const int tile_lane = nn * PM + 4 * jj;                       // packed M / P tiles
 
     // S^T tiles: sT[mt][i] = S[v0 + nn][16 mt + 4 jj + i].
     float4_t sT[KT];
@@ -369,84 +479,176 @@ __global__ __launch_bounds__(64 * NW) void chunk_state_kernel(
             sT[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
     }
 
-    for (int ci = 0; ci < nchunks; ++ci) {
+    // ---- register prefetch of one chunk's inputs ----
+    // Loads use the chunk's first row as a uniform base plus 32-bit per-lane
+    // offsets, and are unconditional: in a partial chunk the rows past the end
+    // re-read the last valid row and are zeroed when committed to LDS.  The
+    // prefetched registers are not touched until the commit after the next
+    // barrier, so the loads stay in flight during the chunk's compute.
+    Raw8<in_t> pq[QK_IT], pk[QK_IT], pv[V_IT];
+    int4 pm[MP_IT], pp[MP_IT];
+    float pg[G_IT];
+    const int rowq = H * DK, rowv = H * DV;   // element stride between tokens
+    // Loop-invariant per-thread element offsets inside a chunk (row r, 8 columns).
+    int offq[QK_IT], offv[V_IT];
+#pragma unroll
+    for (int it = 0; it < QK_IT; ++it) {
+        const int u = (tid + it * NT) % QK_UNITS;
+        offq[it] = (u / (DK / 8)) * rowq + (u % (DK / 8)) * 8;
+    }
+#pragma unroll
+    for (int it = 0; it < V_IT; ++it) {
+        const int u = (tid + it * NT) % V_UNITS;
+        offv[it] = (u / (BV / 8)) * rowv + (u % (BV / 8)) * 8;
+    }
+    const bool v_cols_ok = vb + ((tid % (BV / 8)) * 8) < DV;   // same for every it (NT % (BV/8) == 0)
+    auto prefetch = [&](int ci) {
         const int64_t rh = (int64_t)(r0 + ci) * H + h;
+        const int64_t tb = (int64_t)(tok0 + ci * C) * H + h;
+        const int last = min(C, len_seq - ci * C) - 1;
+        const in_t *qc = q + tb * DK;
+        const in_t *kc = k + tb * DK;
+        const in_t *vc = v + tb * DV + vb;
+        if (last == C - 1) {
+#pragma unroll
+            for (int it = 0; it < QK_IT; ++it) {
+                pq[it].load(qc + offq[it]);
+                pk[it].load(kc + offq[it]);
+            }
+            if (v_cols_ok) {
+#pragma unroll
+                for (int it = 0; it < V_IT; ++it) pv[it].load(vc + offv[it]);
+            }
+        } else {
+            // partial chunk: rows past the end re-read the last valid row
+#pragma unroll
+            for (int it = 0; it < QK_IT; ++it) {
+                const int u = (tid + it * NT) % QK_UNITS;
+                const int off = min(u / (DK / 8), last) * rowq + (u % (DK / 8)) * 8;
+                pq[it].load(qc + off);
+                pk[it].load(kc + off);
+            }
+            if (v_cols_ok) {
+#pragma unroll
+                for (int it = 0; it < V_IT; ++it) {
+                    const int u = (tid + it * NT) % V_UNITS;
+                    pv[it].load(vc + min(u / (BV / 8), last) * rowv + (u % (BV / 8)) * 8);
+                }
+            }
+        }
+        const OP *mc = ws_m + rh * kTriTiles * kTileElems;
+        const OP *pc = ws_p + rh * kTriTiles * kTileElems;
+#pragma unroll
+        for (int it = 0; it < MP_IT; ++it) {
+            const int idx = min(tid + it * NT, MP_N - 1);
+            pm[it] = *reinterpret_cast<const int4 *>(mc + idx * MP_VEC);
+            pp[it] = *reinterpret_cast<const int4 *>(pc + idx * MP_VEC);
+        }
+#pragma unroll
+        for (int it = 0; it < G_IT; ++it) pg[it] = ws_g[rh * 2 * C + min(tid + it * NT, 2 * C - 1)];
+    };
+    auto commit = [&](int len) {
+        const bool full = len == C;
+#pragma unroll
+        for (int it = 0; it < QK_IT; ++it) {
+            const int u = tid + it * NT;
+            if (u >= QK_UNITS) continue;
+            const int r = u / (DK / 8), c8 = (u % (DK / 8)) * 8;
+            if (!full && r >= len) {
+                pq[it].zero();
+                pk[it].zero();
+            }
+            frag lo, hi;
+            to_op(pq[it], lo, hi);
+            *reinterpret_cast<frag *>(Qs + r * PQ + c8) = lo;
+            *reinterpret_cast<frag *>(Qs + r * PQ + c8 + 4) = hi;
+            to_op(pk[it], lo, hi);
+            *reinterpret_cast<frag *>(Ks + r * PQ + c8) = lo;
+            *reinterpret_cast<frag *>(Ks + r * PQ + c8 + 4) = hi;
+        }
+        if (v_cols_ok) {
+#pragma unroll
+            for (int it = 0; it < V_IT; ++it) {
+                const int u = tid + it * NT;
+                if (u >= V_UNITS) continue;
+                const int r = u / (BV / 8), c8 = (u % (BV / 8)) * 8;
+                if (!full && r >= len) pv[it].zero();
+                pv[it].store_lds(Vs + r * PV + c8);
+            }
+        }
+#pragma unroll
+        for (int it = 0; it < MP_IT; ++it) {
+            const int idx = tid + it * NT;
+            if (idx < MP_N) {
+                const int e = idx * MP_VEC, tl = e >> 8, rr = (e >> 4) & 15, cc = e & 15;
+                int2 *md = reinterpret_cast<int2 *>(Ms + (tl * 16 + rr) * PM + cc);
+                int2 *pd = reinterpret_cast<int2 *>(Ps + (tl * 16 + rr) * PM + cc);
+                md[0] = int2{pm[it].x, pm[it].y};
+                md[1] = int2{pm[it].z, pm[it].w};
+                pd[0] = int2{pp[it].x, pp[it].y};
+                pd[1] = int2{pp[it].z, pp[it].w};
+            }
+        }
+#pragma unroll
+        for (int it = 0; it < G_IT; ++it) {
+            const int idx = tid + it * NT;
+            if (idx < 2 * C) gam_s[idx] = pg[it];
+        }
+    };
+
+    // Finish the initial-state loads before the first prefetch so no load of
+    // the loop is ever waited on together with them.
+    {
+        float acc = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < KT; ++mt) acc += sT[mt][0];
+        __builtin_amdgcn_s_waitcnt(0);
+        asm volatile("" ::"v"(acc));
+    }
+
+    if (nchunks > 0) prefetch(0);
+    for (int ci = 0; ci < nchunks; ++ci) {
         const int t0 = tok0 + ci * C;
         const int len = min(C, len_seq - ci * C);
+        __syncthreads();             // previous chunk's LDS reads are done
+        commit(len);
         __syncthreads();
-        // ---- stage the chunk's shared operands ----
-        for (int idx = tid; idx < C * DK / 8; idx += NT) {
-            const int r = idx / (DK / 8), c8 = (idx % (DK / 8)) * 8;
-            float xq[8], xk[8];
-            if (r < len) {
-                const int64_t off = ((int64_t)(t0 + r) * H + h) * DK + c8;
-                load8_f32(q + off, xq);
-                load8_f32(k + off, xk);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) xq[e] = xk[e] = 0.f;
-            }
-            lds_store8(Qs + r * PQ + c8, xq);
-            lds_store8(Ks + r * PQ + c8, xk);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) KTs[(c8 + e) * PT + r] = from_f32<OP>(xk[e]);
-        }
-        for (int idx = tid; idx < kTriTiles * kTileElems / VEC; idx += NT) {
-            const int e = idx * VEC, tl = e >> 8, rr = (e >> 4) & 15, cc = e & 15;
-            const int4 mv = *reinterpret_cast<const int4 *>(ws_m + rh * kTriTiles * kTileElems + e);
-            const int4 pv = *reinterpret_cast<const int4 *>(ws_p + rh * kTriTiles * kTileElems + e);
-            // 16-byte vector split in two 8-byte LDS writes (tile rows are 8-byte aligned).
-            int2 *md = reinterpret_cast<int2 *>(Ms + (tl * 16 + rr) * PM + cc);
-            int2 *pd = reinterpret_cast<int2 *>(Ps + (tl * 16 + rr) * PM + cc);
-            md[0] = int2{mv.x, mv.y};
-            md[1] = int2{mv.z, mv.w};
-            pd[0] = int2{pv.x, pv.y};
-            pd[1] = int2{pv.z, pv.w};
-        }
-        if (tid < C) gs[tid] = ws_g[rh * C + tid];
-        __syncthreads();
+        if (ci + 1 < nchunks) prefetch(ci + 1);
         if (!active) continue;
 
-        // ---- per-wave work on 16 value columns ----
-        float eg[4][4];   // exp(g_r) for the rows this lane holds in accumulator tiles
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) eg[mt][i] = expf(gs[16 * mt + 4 * jj + i]);
-        const float g_last = gs[C - 1];
-
-        // S^T as B operand (fp16 or fp32), reused by all 8 row tiles.
+        // S as an operand: B of K S^T and A of S Q^T use the same fragment.
         frag sB[KT];
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt) sB[kt] = M::cvt(sT[kt]);
 
-        // X = [Q; K] S^T  (8 row tiles of 16 rows)
-        float4_t X[8];
+        // X_K = K S^T and (S Q^T) for the output: both need only S, so their
+        // matrix-core work is issued together.
+        float4_t x[4], oq[4];
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt) {
-            X[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
-            const OP *asrc = (mt < 4 ? Qs : Ks) + (16 * (mt & 3) + nn) * PQ + 4 * jj;
+        for (int mt = 0; mt < 4; ++mt) {
+            x[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
+            oq[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
+            const OP *asrc = Ks + 16 * mt * PQ + row_lane;
+            const OP *bsrc = Qs + 16 * mt * PQ + row_lane;
 #pragma unroll
             for (int kt = 0; kt < KT; kt += M::KT_PER_ISSUE) {
                 const frag a0 = lds_frag(asrc + 16 * kt);
                 const frag a1 = M::KT_PER_ISSUE == 2 ? lds_frag(asrc + 16 * kt + 16) : a0;
-                const frag b1 = M::KT_PER_ISSUE == 2 ? sB[kt + 1 < KT ? kt + 1 : kt] : sB[kt];
-                M::issue(X[mt], a0, a1, sB[kt], b1);
+                const frag s1 = M::KT_PER_ISSUE == 2 ? sB[kt + 1 < KT ? kt + 1 : kt] : sB[kt];
+                M::issue(x[mt], a0, a1, sB[kt], s1);
+                const frag b0 = lds_frag(bsrc + 16 * kt);
+                const frag b1 = M::KT_PER_ISSUE == 2 ? lds_frag(bsrc + 16 * kt + 16) : b0;
+                M::issue(oq[mt], sB[kt], s1, b0, b1);
             }
         }
 
-        // Y = V - diag(gamma) X_K, as B operand.
+        // Y = V - diag(gamma) X_K as B operand.
         frag yB[4];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
-            float4_t y;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 16 * mt + 4 * jj + i;
-                const float vv = (r < len) ? to_f32(v[((int64_t)(t0 + r) * H + h) * DV + v0 + nn]) : 0.f;
-                y[i] = vv - eg[mt][i] * X[4 + mt][i];
-            }
-            yB[mt] = M::cvt(y);
+            const float4_t vv = ColFrag<in_t>::read_f32(Vs + 16 * mt * PV, trv_lane, plv_lane, PV);
+            const float4_t gm = *reinterpret_cast<const float4_t *>(gam_s + 16 * mt + 4 * jj);
+            yB[mt] = M::cvt(vv - gm * x[mt]);
         }
 
         // V' = M Y  (M lower triangular: k-tiles 0..mt)
@@ -456,61 +658,60 @@ __global__ __launch_bounds__(64 * NW) void chunk_state_kernel(
             Vp[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kt = 0; kt <= mt; kt += M::KT_PER_ISSUE) {
-                const frag a0 = lds_frag(Ms + (tri_index(mt, kt) * 16 + nn) * PM + 4 * jj);
+                const frag a0 = lds_frag(Ms + tri_index(mt, kt) * 16 * PM + tile_lane);
                 frag a1 = M::zero(), b1 = M::zero();
                 if (M::KT_PER_ISSUE == 2 && kt + 1 <= mt) {
-                    a1 = lds_frag(Ms + (tri_index(mt, kt + 1) * 16 + nn) * PM + 4 * jj);
+                    a1 = lds_frag(Ms + tri_index(mt, kt + 1) * 16 * PM + tile_lane);
                     b1 = yB[kt + 1];
                 }
                 M::issue(Vp[mt], a0, a1, yB[kt], b1);
             }
         }
-
-        // O = diag(gamma) X_Q + P V'
-        frag vB[4];
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) vB[mt] = M::cvt(Vp[mt]);
+        frag vB[4], dB[4];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
-            float4_t acc;
+            vB[mt] = M::cvt(Vp[mt]);
+            const float4_t kp = *reinterpret_cast<const float4_t *>(kap_s + 16 * mt + 4 * jj);
+            dB[mt] = M::cvt(kp * Vp[mt]);
+        }
+
+        // O^T = (S Q^T) diag(gamma) + V'^T P^T, one 16-row block of tokens at a time.
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] = eg[mt][i] * X[mt][i];
+        for (int rt = 0; rt < 4; ++rt) {
+            oq[rt] *= gam_s[16 * rt + nn];
 #pragma unroll
-            for (int kt = 0; kt <= mt; kt += M::KT_PER_ISSUE) {
-                const frag a0 = lds_frag(Ps + (tri_index(mt, kt) * 16 + nn) * PM + 4 * jj);
-                frag a1 = M::zero(), b1 = M::zero();
-                if (M::KT_PER_ISSUE == 2 && kt + 1 <= mt) {
-                    a1 = lds_frag(Ps + (tri_index(mt, kt + 1) * 16 + nn) * PM + 4 * jj);
-                    b1 = vB[kt + 1];
+            for (int kt = 0; kt <= rt; kt += M::KT_PER_ISSUE) {
+                const frag b0 = lds_frag(Ps + tri_index(rt, kt) * 16 * PM + tile_lane);
+                frag b1 = M::zero(), a1 = M::zero();
+                if (M::KT_PER_ISSUE == 2 && kt + 1 <= rt) {
+                    b1 = lds_frag(Ps + tri_index(rt, kt + 1) * 16 * PM + tile_lane);
+                    a1 = vB[kt + 1];
                 }
-                M::issue(acc, a0, a1, vB[kt], b1);
+                M::issue(oq[rt], vB[kt], a1, b0, b1);
             }
+        }
+        {
+            const int64_t obase = ((int64_t)t0 * H + h) * DV + v0 + 4 * jj + (int64_t)nn * H * DV;
+            const int64_t ostep = (int64_t)16 * H * DV;
+            if (len == C) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 16 * mt + 4 * jj + i;
-                if (r < len) store_out(o, ((int64_t)(t0 + r) * H + h) * DV + v0 + nn, odt, acc[i]);
+                for (int rt = 0; rt < 4; ++rt) store_out4(o, obase + rt * ostep, odt, oq[rt]);
+            } else {
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt)
+                    if (16 * rt + nn < len) store_out4(o, obase + rt * ostep, odt, oq[rt]);
             }
         }
 
-        // S^T <- gamma^C S^T + K^T (diag(exp(g_C - g_r)) V')
-        frag dB[4];
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-            float4_t x;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) x[i] = Vp[mt][i] * expf(g_last - gs[16 * mt + 4 * jj + i]);
-            dB[mt] = M::cvt(x);
-        }
-        const float gC = expf(g_last);
+        // S^T <- gamma_C S^T + K^T (kappa o V'); K^T fragments by transposed reads.
+        const float gC = gam_s[C - 1];
 #pragma unroll
         for (int mt = 0; mt < KT; ++mt) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sT[mt][i] *= gC;
-            const OP *asrc = KTs + (16 * mt + nn) * PT + 4 * jj;
+            sT[mt] *= gC;
 #pragma unroll
             for (int kt = 0; kt < 4; kt += M::KT_PER_ISSUE) {
-                const frag a0 = lds_frag(asrc + 16 * kt);
-                const frag a1 = M::KT_PER_ISSUE == 2 ? lds_frag(asrc + 16 * kt + 16) : a0;
+                const frag a0 = kt_frag<OP>(Ks + 16 * kt * PQ + 16 * mt, trk_lane, plk_lane, PQ);
+                const frag a1 = M::KT_PER_ISSUE == 2 ? kt_frag<OP>(Ks + 16 * (kt + 1) * PQ + 16 * mt, trk_lane, plk_lane, PQ) : a0;
                 const frag b1 = M::KT_PER_ISSUE == 2 ? dB[kt + 1 < 4 ? kt + 1 : kt] : dB[kt];
                 M::issue(sT[mt], a0, a1, dB[kt], b1);
             }
@@ -541,25 +742,21 @@ ChunkWorkspace chunk_workspace_layout(int32_t B, int32_t T, int32_t N, bool pack
     w.off_row0 = off;   off = align256(off + sizeof(int32_t) * (size_t)N);
     w.off_rowtok = off; off = align256(off + sizeof(int32_t) * (size_t)w.max_rows);
     w.off_rowlen = off; off = align256(off + sizeof(int32_t) * (size_t)w.max_rows);
-    w.off_g = off;      off = align256(off + sizeof(float) * (size_t)w.max_rows * H * C);
+    w.off_g = off;      off = align256(off + sizeof(float) * (size_t)w.max_rows * H * 2 * C);
     w.off_m = off;      off = align256(off + op * (size_t)w.max_rows * H * kTriTiles * kTileElems);
     w.off_p = off;      off = align256(off + op * (size_t)w.max_rows * H * kTriTiles * kTileElems);
     w.total = off;
     return w;
 }
 
-static int state_waves_per_block(int64_t NH, int DV) {
+static int state_waves_per_block(int DV) {
     const char *env = getenv("GDN_STATE_WAVES");
     if (env) {
         const int x = atoi(env);
         if (x == 1 || x == 2 || x == 4) return x;
     }
     const int tiles = (DV + 15) / 16;
-    for (int nw : {4, 2}) {
-        const int64_t blocks = NH * ((tiles + nw - 1) / nw);
-        if (blocks >= 256) return nw;
-    }
-    return 1;
+    return tiles >= 4 ? 4 : (tiles >= 2 ? 2 : 1);
 }
 
 template <typename K>
@@ -571,7 +768,7 @@ static hipError_t allow_smem(K kernel, size_t bytes) {
 
 template <typename in_t, typename OP, int DK, int NW>
 static hipError_t launch_state(const ChunkArgs &a, const ChunkWorkspace &w, hipStream_t st) {
-    using L = StateSmem<OP, DK>;
+    using L = StateSmem<in_t, OP, DK, NW>;
     auto kern = chunk_state_kernel<in_t, OP, DK, NW>;
     hipError_t e = allow_smem(kern, L::bytes);
     if (e != hipSuccess) return e;
@@ -607,7 +804,7 @@ static hipError_t launch_dk(const ChunkArgs &a, const ChunkWorkspace &w, hipStre
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    switch (state_waves_per_block((int64_t)a.N * a.H, a.dv)) {
+    switch (state_waves_per_block(a.dv)) {
     case 4: return launch_state<in_t, OP, DK, 4>(a, w, st);
     case 2: return launch_state<in_t, OP, DK, 2>(a, w, st);
     default: return launch_state<in_t, OP, DK, 1>(a, w, st);

@@ -71,6 +71,13 @@ struct Mma<_Float16> {
     __device__ __forceinline__ static frag cvt(float4_t x) {
         return frag{(_Float16)x[0], (_Float16)x[1], (_Float16)x[2], (_Float16)x[3]};
     }
+    __device__ __forceinline__ static half8_t cvt8(float4_t x, float4_t y) {
+        return half8_t{(_Float16)x[0], (_Float16)x[1], (_Float16)x[2], (_Float16)x[3],
+                       (_Float16)y[0], (_Float16)y[1], (_Float16)y[2], (_Float16)y[3]};
+    }
+    __device__ __forceinline__ static void issue8(float4_t &acc, half8_t a, half8_t b) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc, 0, 0, 0);
+    }
     // acc += A(k-tiles a0,a1) * B(k-tiles b0,b1)
     __device__ __forceinline__ static void issue(float4_t &acc, frag a0, frag a1, frag b0, frag b1) {
         half8_t a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -92,6 +99,21 @@ struct Mma<float> {
         acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], acc, 0, 0, 0);
     }
 };
+
+// 16-bit transposed LDS read (gfx950 ds_read_b64_tr_b16).  Within each group
+// of 16 lanes, lane j receives as element e the (j mod 4)-th 16-bit value of
+// the 8 bytes read by lane 4e + j/4 of its group.  So if lane s of the group
+// points at row (R + s/4), columns (c0 + 4 (s mod 4)) .. +3 of a row-major
+// 16-bit matrix, lane j receives rows R..R+3 of column c0 + j: a column
+// fragment, i.e. a read of the transposed matrix.
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4_t lds_short4_t;
+__device__ __forceinline__ uint2 lds_read_tr16(const void *p) {
+    // generic -> LDS address: the low 32 bits of a shared-memory pointer
+    const uint32_t a = (uint32_t)(uintptr_t)p;
+    const short4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t *)(uintptr_t)a);
+    return __builtin_bit_cast(uint2, v);
+}
 
 // Four consecutive operand values from LDS (8-byte or 16-byte aligned read).
 template <typename OP>
@@ -116,6 +138,112 @@ __device__ __forceinline__ void load8_f32(const bf16_t *p, float (&o)[8]) {
     ushort8_t a = *reinterpret_cast<const ushort8_t *>(p);
 #pragma unroll
     for (int i = 0; i < 8; ++i) o[i] = __uint_as_float(((uint32_t)a[i]) << 16);
+}
+
+// ---- 8 consecutive input elements held as raw bits (for register prefetch) -------
+
+template <typename in_t>
+struct Raw8;
+
+template <>
+struct Raw8<bf16_t> {
+    uint4 x;
+    __device__ __forceinline__ void load(const bf16_t *p) { x = *reinterpret_cast<const uint4 *>(p); }
+    __device__ __forceinline__ void zero() { x = make_uint4(0u, 0u, 0u, 0u); }
+    __device__ __forceinline__ void store_lds(bf16_t *p) const { *reinterpret_cast<uint4 *>(p) = x; }
+    __device__ __forceinline__ static void store_zero_lds(bf16_t *p) { *reinterpret_cast<uint4 *>(p) = make_uint4(0u, 0u, 0u, 0u); }
+    __device__ __forceinline__ void to_f32(float (&o)[8]) const {
+        const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            o[2 * e] = __uint_as_float(w[e] << 16);
+            o[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+        }
+    }    // Element e of this vector and of `next` (the following row), packed as
+    // one 32-bit LDS write; rows flagged false are written as zero.
+    __device__ __forceinline__ void store_pair(const Raw8 &next, int e, bool k0, bool k1, bf16_t *dst) const {
+        const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+        const uint32_t n[4] = {next.x.x, next.x.y, next.x.z, next.x.w};
+        uint32_t a = k0 ? w[e >> 1] : 0u, b = k1 ? n[e >> 1] : 0u;
+        *reinterpret_cast<uint32_t *>(dst) = __builtin_amdgcn_perm(b, a, (e & 1) ? 0x07060302u : 0x05040100u);
+    }
+};
+
+template <>
+struct Raw8<_Float16> {
+    uint4 x;
+    __device__ __forceinline__ void load(const _Float16 *p) { x = *reinterpret_cast<const uint4 *>(p); }
+    __device__ __forceinline__ void zero() { x = make_uint4(0u, 0u, 0u, 0u); }
+    __device__ __forceinline__ void store_lds(_Float16 *p) const { *reinterpret_cast<uint4 *>(p) = x; }
+    __device__ __forceinline__ static void store_zero_lds(_Float16 *p) { *reinterpret_cast<uint4 *>(p) = make_uint4(0u, 0u, 0u, 0u); }
+    __device__ __forceinline__ void to_f32(float (&o)[8]) const {
+        const half8_t h = __builtin_bit_cast(half8_t, x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = (float)h[e];
+    }    __device__ __forceinline__ void store_pair(const Raw8 &next, int e, bool k0, bool k1, _Float16 *dst) const {
+        const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+        const uint32_t n[4] = {next.x.x, next.x.y, next.x.z, next.x.w};
+        uint32_t a = k0 ? w[e >> 1] : 0u, b = k1 ? n[e >> 1] : 0u;
+        *reinterpret_cast<uint32_t *>(dst) = __builtin_amdgcn_perm(b, a, (e & 1) ? 0x07060302u : 0x05040100u);
+    }
+};
+
+template <>
+struct Raw8<float> {
+    uint4 x[2];
+    __device__ __forceinline__ void load(const float *p) {
+        x[0] = *reinterpret_cast<const uint4 *>(p);
+        x[1] = *reinterpret_cast<const uint4 *>(p + 4);
+    }
+    __device__ __forceinline__ void zero() { x[0] = x[1] = make_uint4(0u, 0u, 0u, 0u); }
+    __device__ __forceinline__ void store_lds(float *p) const {
+        reinterpret_cast<uint4 *>(p)[0] = x[0];
+        reinterpret_cast<uint4 *>(p)[1] = x[1];
+    }
+    __device__ __forceinline__ static void store_zero_lds(float *p) {
+        reinterpret_cast<uint4 *>(p)[0] = make_uint4(0u, 0u, 0u, 0u);
+        reinterpret_cast<uint4 *>(p)[1] = make_uint4(0u, 0u, 0u, 0u);
+    }
+    __device__ __forceinline__ void to_f32(float (&o)[8]) const {
+        o[0] = __uint_as_float(x[0].x); o[1] = __uint_as_float(x[0].y);
+        o[2] = __uint_as_float(x[0].z); o[3] = __uint_as_float(x[0].w);
+        o[4] = __uint_as_float(x[1].x); o[5] = __uint_as_float(x[1].y);
+        o[6] = __uint_as_float(x[1].z); o[7] = __uint_as_float(x[1].w);
+    }
+    __device__ __forceinline__ void store_pair(const Raw8 &next, int e, bool k0, bool k1, float *dst) const {
+        const uint32_t w[8] = {x[0].x, x[0].y, x[0].z, x[0].w, x[1].x, x[1].y, x[1].z, x[1].w};
+        const uint32_t n[8] = {next.x[0].x, next.x[0].y, next.x[0].z, next.x[0].w,
+                               next.x[1].x, next.x[1].y, next.x[1].z, next.x[1].w};
+        *reinterpret_cast<uint2 *>(dst) = uint2{k0 ? w[e] : 0u, k1 ? n[e] : 0u};
+    }
+};
+
+template <typename in_t>
+__device__ __forceinline__ in_t zero_elem() { return in_t{}; }
+
+// Eight input values as two 4-element matrix-core operand fragments.  16-bit
+// inputs become fp16 operands: fp16 inputs are copied bit for bit, bf16
+// inputs are widened to fp32 and packed with one conversion per pair (the
+// conversion rounds toward zero, which is exact for every bf16 value inside
+// the fp16 normal range, the documented operand-range precondition).
+__device__ __forceinline__ void to_op(const Raw8<bf16_t> &r, half4_t &lo, half4_t &hi) {
+    const uint32_t w[4] = {r.x.x, r.x.y, r.x.z, r.x.w};
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    h2 p[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        p[e] = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(w[e] << 16),
+                                                                  __uint_as_float(w[e] & 0xffff0000u)));
+    lo = half4_t{p[0][0], p[0][1], p[1][0], p[1][1]};
+    hi = half4_t{p[2][0], p[2][1], p[3][0], p[3][1]};
+}
+__device__ __forceinline__ void to_op(const Raw8<_Float16> &r, half4_t &lo, half4_t &hi) {
+    lo = __builtin_bit_cast(half4_t, uint2{r.x.x, r.x.y});
+    hi = __builtin_bit_cast(half4_t, uint2{r.x.z, r.x.w});
+}
+__device__ __forceinline__ void to_op(const Raw8<float> &r, float4_t &lo, float4_t &hi) {
+    lo = __builtin_bit_cast(float4_t, r.x[0]);
+    hi = __builtin_bit_cast(float4_t, r.x[1]);
 }
 
 // ---- wave-level helpers ---------------------------------------------------------
