@@ -616,78 +616,122 @@ __global__ __launch_bounds__(64 * NW) void chunk_state_kernel(
         if (ci + 1 < nchunks) prefetch(ci + 1);
         if (!active) continue;
 
+        using F2 = Frag2<OP>;
+        constexpr int KP = KT / 2;                       // k-tile pairs along dk
         // S as an operand: B of K S^T and A of S Q^T use the same fragment.
-        frag sB[KT];
+        F2 sB[KP];
 #pragma unroll
-        for (int kt = 0; kt < KT; ++kt) sB[kt] = M::cvt(sT[kt]);
+        for (int p = 0; p < KP; ++p) sB[p] = F2::cvt(sT[2 * p], sT[2 * p + 1]);
 
-        // X_K = K S^T and (S Q^T) for the output: both need only S, so their
-        // matrix-core work is issued together.
+        // X_K = K S^T and (S Q^T) for the output: both need only S.  The K and
+        // Q fragments of row tile mt+1 are read while tile mt's products run.
         float4_t x[4], oq[4];
+        F2 kf[2][KP], qf[2][KP];
+        auto load_kq = [&](F2 (&kd)[KP], F2 (&qd)[KP], int mt) {
+            const OP *ks = Ks + 16 * mt * PQ + row_lane;
+            const OP *qs = Qs + 16 * mt * PQ + row_lane;
+#pragma unroll
+            for (int p = 0; p < KP; ++p) {
+                kd[p] = F2::make(lds_frag(ks + 32 * p), lds_frag(ks + 32 * p + 16));
+                qd[p] = F2::make(lds_frag(qs + 32 * p), lds_frag(qs + 32 * p + 16));
+            }
+        };
+        load_kq(kf[0], qf[0], 0);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
+            if (mt < 3) load_kq(kf[(mt + 1) & 1], qf[(mt + 1) & 1], mt + 1);
             x[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
             oq[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
-            const OP *asrc = Ks + 16 * mt * PQ + row_lane;
-            const OP *bsrc = Qs + 16 * mt * PQ + row_lane;
 #pragma unroll
-            for (int kt = 0; kt < KT; kt += M::KT_PER_ISSUE) {
-                const frag a0 = lds_frag(asrc + 16 * kt);
-                const frag a1 = M::KT_PER_ISSUE == 2 ? lds_frag(asrc + 16 * kt + 16) : a0;
-                const frag s1 = M::KT_PER_ISSUE == 2 ? sB[kt + 1 < KT ? kt + 1 : kt] : sB[kt];
-                M::issue(x[mt], a0, a1, sB[kt], s1);
-                const frag b0 = lds_frag(bsrc + 16 * kt);
-                const frag b1 = M::KT_PER_ISSUE == 2 ? lds_frag(bsrc + 16 * kt + 16) : b0;
-                M::issue(oq[mt], sB[kt], s1, b0, b1);
+            for (int p = 0; p < KP; ++p) {
+                mma2(x[mt], kf[mt & 1][p], sB[p]);
+                mma2(oq[mt], sB[p], qf[mt & 1][p]);
             }
         }
 
-        // Y = V - diag(gamma) X_K as B operand.
-        frag yB[4];
+        // Y = V - diag(gamma) X_K as B operand (pairs of row tiles).
+        F2 yB[2];
+        {
+            float4_t y[4];
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-            const float4_t vv = ColFrag<in_t>::read_f32(Vs + 16 * mt * PV, trv_lane, plv_lane, PV);
-            const float4_t gm = *reinterpret_cast<const float4_t *>(gam_s + 16 * mt + 4 * jj);
-            yB[mt] = M::cvt(vv - gm * x[mt]);
+            for (int mt = 0; mt < 4; ++mt) {
+                const float4_t vv = ColFrag<in_t>::read_f32(Vs + 16 * mt * PV, trv_lane, plv_lane, PV);
+                const float4_t gm = *reinterpret_cast<const float4_t *>(gam_s + 16 * mt + 4 * jj);
+                y[mt] = vv - gm * x[mt];
+            }
+            yB[0] = F2::cvt(y[0], y[1]);
+            yB[1] = F2::cvt(y[2], y[3]);
         }
 
-        // V' = M Y  (M lower triangular: k-tiles 0..mt)
+        // V' = M Y  (M lower triangular).  Row tile mt uses k-tiles 0..mt:
+        // pair 0 = tiles (0,1), pair 1 = tiles (2,3); missing tiles are zero.
+        auto tri_pair = [&](const OP *T, int mt, int p) {
+            const int k0 = 2 * p, k1 = 2 * p + 1;
+            const typename M::frag lo = k0 <= mt ? lds_frag(T + tri_index(mt, k0) * 16 * PM + tile_lane) : M::zero();
+            const typename M::frag hi = k1 <= mt ? lds_frag(T + tri_index(mt, k1) * 16 * PM + tile_lane) : M::zero();
+            return F2::make(lo, hi);
+        };
         float4_t Vp[4];
+        {
+            F2 mf[4][2];
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-            Vp[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
+            for (int mt = 0; mt < 4; ++mt) {
+                mf[mt][0] = tri_pair(Ms, mt, 0);
+                if (mt >= 2) mf[mt][1] = tri_pair(Ms, mt, 1);
+            }
 #pragma unroll
-            for (int kt = 0; kt <= mt; kt += M::KT_PER_ISSUE) {
-                const frag a0 = lds_frag(Ms + tri_index(mt, kt) * 16 * PM + tile_lane);
-                frag a1 = M::zero(), b1 = M::zero();
-                if (M::KT_PER_ISSUE == 2 && kt + 1 <= mt) {
-                    a1 = lds_frag(Ms + tri_index(mt, kt + 1) * 16 * PM + tile_lane);
-                    b1 = yB[kt + 1];
-                }
-                M::issue(Vp[mt], a0, a1, yB[kt], b1);
+            for (int mt = 0; mt < 4; ++mt) {
+                Vp[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
+                mma2(Vp[mt], mf[mt][0], yB[0]);
+                if (mt >= 2) mma2(Vp[mt], mf[mt][1], yB[1]);
             }
         }
-        frag vB[4], dB[4];
+        F2 vB[2], dB[2];
+        {
+            float4_t d[4];
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-            vB[mt] = M::cvt(Vp[mt]);
-            const float4_t kp = *reinterpret_cast<const float4_t *>(kap_s + 16 * mt + 4 * jj);
-            dB[mt] = M::cvt(kp * Vp[mt]);
+            for (int mt = 0; mt < 4; ++mt) {
+                const float4_t kp = *reinterpret_cast<const float4_t *>(kap_s + 16 * mt + 4 * jj);
+                d[mt] = kp * Vp[mt];
+            }
+            vB[0] = F2::cvt(Vp[0], Vp[1]);
+            vB[1] = F2::cvt(Vp[2], Vp[3]);
+            dB[0] = F2::cvt(d[0], d[1]);
+            dB[1] = F2::cvt(d[2], d[3]);
         }
 
-        // O^T = (S Q^T) diag(gamma) + V'^T P^T, one 16-row block of tokens at a time.
+        // O^T = (S Q^T) diag(gamma) + V'^T P^T, interleaved with the state
+        // update S^T <- gamma_C S^T + K^T (kappa o V') (independent work);
+        // K^T fragments come from transposed reads of K.
+        F2 pf[4][2];
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
-            oq[rt] *= gam_s[16 * rt + nn];
+            pf[rt][0] = tri_pair(Ps, rt, 0);
+            if (rt >= 2) pf[rt][1] = tri_pair(Ps, rt, 1);
+        }
+        auto load_kt = [&](F2 (&kd)[2], int mt) {
 #pragma unroll
-            for (int kt = 0; kt <= rt; kt += M::KT_PER_ISSUE) {
-                const frag b0 = lds_frag(Ps + tri_index(rt, kt) * 16 * PM + tile_lane);
-                frag b1 = M::zero(), a1 = M::zero();
-                if (M::KT_PER_ISSUE == 2 && kt + 1 <= rt) {
-                    b1 = lds_frag(Ps + tri_index(rt, kt + 1) * 16 * PM + tile_lane);
-                    a1 = vB[kt + 1];
-                }
-                M::issue(oq[rt], vB[kt], a1, b0, b1);
+            for (int p = 0; p < 2; ++p)
+                kd[p] = F2::make(kt_frag<OP>(Ks + 32 * p * PQ + 16 * mt, trk_lane, plk_lane, PQ),
+                                 kt_frag<OP>(Ks + (32 * p + 16) * PQ + 16 * mt, trk_lane, plk_lane, PQ));
+        };
+        const float gC = gam_s[C - 1];
+        F2 ktf[2][2];
+        load_kt(ktf[0], 0);
+        constexpr int NSTEP = KT > 4 ? KT : 4;           // dk row tiles and output row tiles
+#pragma unroll
+        for (int mt = 0; mt < NSTEP; ++mt) {
+            if (mt < KT) {
+                if (mt + 1 < KT) load_kt(ktf[(mt + 1) & 1], mt + 1);
+                sT[mt] *= gC;
+                mma2(sT[mt], ktf[mt & 1][0], dB[0]);
+                mma2(sT[mt], ktf[mt & 1][1], dB[1]);
+            }
+            if (mt < 4) {
+                const int rt = mt;
+                oq[rt] *= gam_s[16 * rt + nn];
+                mma2(oq[rt], vB[0], pf[rt][0]);
+                if (rt >= 2) mma2(oq[rt], vB[1], pf[rt][1]);
             }
         }
         {
@@ -700,20 +744,6 @@ __global__ __launch_bounds__(64 * NW) void chunk_state_kernel(
 #pragma unroll
                 for (int rt = 0; rt < 4; ++rt)
                     if (16 * rt + nn < len) store_out4(o, obase + rt * ostep, odt, oq[rt]);
-            }
-        }
-
-        // S^T <- gamma_C S^T + K^T (kappa o V'); K^T fragments by transposed reads.
-        const float gC = gam_s[C - 1];
-#pragma unroll
-        for (int mt = 0; mt < KT; ++mt) {
-            sT[mt] *= gC;
-#pragma unroll
-            for (int kt = 0; kt < 4; kt += M::KT_PER_ISSUE) {
-                const frag a0 = kt_frag<OP>(Ks + 16 * kt * PQ + 16 * mt, trk_lane, plk_lane, PQ);
-                const frag a1 = M::KT_PER_ISSUE == 2 ? kt_frag<OP>(Ks + 16 * (kt + 1) * PQ + 16 * mt, trk_lane, plk_lane, PQ) : a0;
-                const frag b1 = M::KT_PER_ISSUE == 2 ? dB[kt + 1 < 4 ? kt + 1 : kt] : dB[kt];
-                M::issue(sT[mt], a0, a1, dB[kt], b1);
             }
         }
     }

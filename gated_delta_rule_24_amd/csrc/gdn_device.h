@@ -115,6 +115,42 @@ __device__ __forceinline__ uint2 lds_read_tr16(const void *p) {
     return __builtin_bit_cast(uint2, v);
 }
 
+// Operand fragment of a pair of k-tiles (32 consecutive k indices in the
+// permuted order described at the top of this file): what one fp16 matrix
+// instruction consumes per lane, or eight fp32 instructions.
+template <typename OP>
+struct Frag2;
+template <>
+struct Frag2<_Float16> {
+    half8_t v;
+    __device__ __forceinline__ static Frag2 make(half4_t lo, half4_t hi) {
+        return Frag2{__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7)};
+    }
+    __device__ __forceinline__ static Frag2 zero() { return Frag2{half8_t{0, 0, 0, 0, 0, 0, 0, 0}}; }
+    __device__ __forceinline__ static Frag2 cvt(float4_t lo, float4_t hi) {
+        return Frag2{half8_t{(_Float16)lo[0], (_Float16)lo[1], (_Float16)lo[2], (_Float16)lo[3],
+                             (_Float16)hi[0], (_Float16)hi[1], (_Float16)hi[2], (_Float16)hi[3]}};
+    }
+};
+template <>
+struct Frag2<float> {
+    float4_t lo, hi;
+    __device__ __forceinline__ static Frag2 make(float4_t a, float4_t b) { return Frag2{a, b}; }
+    __device__ __forceinline__ static Frag2 zero() { return Frag2{float4_t{0.f, 0.f, 0.f, 0.f}, float4_t{0.f, 0.f, 0.f, 0.f}}; }
+    __device__ __forceinline__ static Frag2 cvt(float4_t a, float4_t b) { return Frag2{a, b}; }
+};
+
+// acc += A * B over one pair of k-tiles.
+__device__ __forceinline__ void mma2(float4_t &acc, const Frag2<_Float16> &a, const Frag2<_Float16> &b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a.v, b.v, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma2(float4_t &acc, const Frag2<float> &a, const Frag2<float> &b) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo[i], b.lo[i], acc, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[i], b.hi[i], acc, 0, 0, 0);
+}
+
 // Four consecutive operand values from LDS (8-byte or 16-byte aligned read).
 template <typename OP>
 __device__ __forceinline__ typename Mma<OP>::frag lds_frag(const OP *p) {
