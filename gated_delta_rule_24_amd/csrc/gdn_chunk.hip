@@ -150,13 +150,21 @@ __global__ __launch_bounds__(256) void chunk_table_kernel(int N, int T, int pack
 }
 
 // ============================================================================
-// G1: per (chunk row, head): g, P = (Q K^T) o Gamma, A, T = (I + A)^{-1},
-// M = T diag(beta).  256 threads.
+// G1: per (chunk row, head): gamma, kappa, P = (Q K^T) o Gamma, A,
+// T = (I + A)^{-1}, M = T diag(beta).  Persistent blocks of 256 threads loop
+// over (row, head) items and load the next item while computing the current.
+//
+// P and M are written as lower-triangular 16x16 tiles in "fragment order":
+// tile t occupies 256 consecutive elements and lane l (n = l % 16, j = l / 16)
+// owns elements [4l, 4l+4) = X[16a + n][16b + 4j .. 16b + 4j + 3] of tile
+// (a, b), i.e. exactly the operand fragment G2 reads for it.  G1 produces
+// them transposed (P^T = K Q^T), so each lane's accumulator already holds
+// its fragment.
 // ============================================================================
 template <typename OP, int DK>
 struct PrepSmem {
-    static constexpr int PQ = DK + 4;   // operand row pitch (elements), keeps 8/16-byte alignment
-    static constexpr int PA = C + 4;    // fp32 pitch of A and T
+    static constexpr int PQ = DK + 8 / (int)sizeof(OP);  // operand row pitch (elements)
+    static constexpr int PA = C + 4;                     // fp32 pitch of A and T
     static constexpr size_t q_off = 0;
     static constexpr size_t k_off = q_off + sizeof(OP) * C * PQ;
     static constexpr size_t a_off = k_off + sizeof(OP) * C * PQ;
@@ -168,6 +176,10 @@ struct PrepSmem {
     static constexpr size_t b_off = g_off + sizeof(float) * C;
     static constexpr size_t bytes = b_off + sizeof(float) * C;
 };
+
+// exp(x) for x <= 0 with the hardware base-2 exponential (about 1 ulp;
+// large negative arguments flush to 0, never NaN).
+__device__ __forceinline__ float exp_neg(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
 
 template <typename in_t, typename OP, int DK>
 __global__ __launch_bounds__(256) void chunk_prep_kernel(int H, const int32_t *__restrict__ meta,
@@ -181,10 +193,11 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(int H, const int32_t *_
                                                          OP *__restrict__ ws_m,
                                                          OP *__restrict__ ws_p) {
     using M = Mma<OP>;
-    using frag = typename M::frag;
+    using F2 = Frag2<OP>;
     using L = PrepSmem<OP, DK>;
     constexpr int PQ = L::PQ, PA = L::PA;
     constexpr int QK_IT = C * DK / 8 / 256;
+    constexpr int KP = DK / 32;                          // k-tile pairs along dk
     extern __shared__ __align__(16) unsigned char smem[];
     OP *Qs = reinterpret_cast<OP *>(smem + L::q_off);
     OP *Ks = reinterpret_cast<OP *>(smem + L::k_off);
@@ -193,132 +206,154 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(int H, const int32_t *_
     float *gs = reinterpret_cast<float *>(smem + L::g_off);
     float *bs = reinterpret_cast<float *>(smem + L::b_off);
 
-    const int row = blockIdx.x, h = blockIdx.y;
-    if (row >= meta[0]) return;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, nn = l & 15, jj = l >> 4;
-    const int tok0 = row_tok[row], len = row_len[row];
-    const int64_t rh = (int64_t)row * H + h;
+    const int items = meta[0] * H;
 
-    // Issue every global load of the chunk first, then convert into LDS.
-    // Rows past the end of the sequence are zero; their gates get
-    // log alpha = 0 and beta = 0, which leaves g flat and makes those rows
-    // inert in every later product.
     Raw8<in_t> rq[QK_IT], rk[QK_IT];
+    float la = 0.f, bt = 0.f;
+    auto load = [&](int item) {
+        const int row = item / H, h = item % H;
+        const int tok0 = row_tok[row], len = row_len[row];
 #pragma unroll
-    for (int it = 0; it < QK_IT; ++it) {
-        const int idx = tid + it * 256;
-        const int r = idx / (DK / 8), c8 = (idx % (DK / 8)) * 8;
-        if (r < len) {
+        for (int it = 0; it < QK_IT; ++it) {
+            const int idx = tid + it * 256;
+            const int r = min(idx / (DK / 8), len - 1), c8 = (idx % (DK / 8)) * 8;
             const int64_t off = ((int64_t)(tok0 + r) * H + h) * DK + c8;
             rq[it].load(q + off);
             rk[it].load(k + off);
-        } else {
-            rq[it].zero();
-            rk[it].zero();
         }
-    }
-    float la = 0.f, bt = 0.f;
-    if (w == 0 && l < len) {
-        la = log_alpha[(int64_t)(tok0 + l) * H + h];
-        bt = beta[(int64_t)(tok0 + l) * H + h];
-    }
-#pragma unroll
-    for (int it = 0; it < QK_IT; ++it) {
-        const int idx = tid + it * 256;
-        const int r = idx / (DK / 8), c8 = (idx % (DK / 8)) * 8;
-        float x[8];
-        rq[it].to_f32(x);
-        lds_store8(Qs + r * PQ + c8, x);
-        rk[it].to_f32(x);
-        lds_store8(Ks + r * PQ + c8, x);
-    }
-    if (w == 0) {
-        const float g = wave_inclusive_scan(la);
-        const float g_last = __shfl(g, C - 1, 64);
-        gs[l] = g;
-        bs[l] = bt;
-        ws_g[rh * 2 * C + l] = expf(g);               // gamma_r: decay from the chunk start
-        ws_g[rh * 2 * C + C + l] = expf(g_last - g);  // kappa_r: decay from row r to the chunk end
-    }
-    __syncthreads();
+        if (w == 0) {
+            const int r = min(l, len - 1);
+            la = log_alpha[(int64_t)(tok0 + r) * H + h];
+            bt = beta[(int64_t)(tok0 + r) * H + h];
+        }
+    };
 
-    // Lower-triangular 16x16 tiles of Q K^T (10) and K K^T (10).
-    for (int t = w; t < 2 * kTriTiles; t += 4) {
-        const bool isq = t < kTriTiles;
-        const int tl = isq ? t : t - kTriTiles;
-        int a, b;
-        tri_decode(tl, a, b);
-        const OP *asrc = (isq ? Qs : Ks) + (16 * a + nn) * PQ + 4 * jj;
-        const OP *bsrc = Ks + (16 * b + nn) * PQ + 4 * jj;
-        float4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kt = 0; kt < DK / 16; kt += M::KT_PER_ISSUE) {
-            const frag a0 = lds_frag(asrc + 16 * kt), b0 = lds_frag(bsrc + 16 * kt);
-            const frag a1 = M::KT_PER_ISSUE == 2 ? lds_frag(asrc + 16 * kt + 16) : a0;
-            const frag b1 = M::KT_PER_ISSUE == 2 ? lds_frag(bsrc + 16 * kt + 16) : b0;
-            M::issue(acc, a0, a1, b0, b1);
-        }
-        const int c = 16 * b + nn;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = 16 * a + 4 * jj + i;
-            const float gam = (c <= r) ? expf(gs[r] - gs[c]) : 0.f;
-            if (isq)
-                ws_p[(rh * kTriTiles + tl) * kTileElems + (4 * jj + i) * 16 + nn] = from_f32<OP>(gam * acc[i]);
-            else
-                As[r * PA + c] = (c < r) ? bs[r] * gam * acc[i] : 0.f;
-        }
-    }
-    __syncthreads();
+    int item = blockIdx.x;
+    if (item < items) load(item);
+    for (; item < items; item += gridDim.x) {
+        const int row = item / H;
+        const int len = row_len[row];
+        const int64_t rh = item;   // == row * H + h
 
-    // T = (I + A)^{-1}.  Diagonal 16x16 blocks by forward substitution, one
-    // column per lane (wave 0: lane group jj = block, nn = column).
-    if (w == 0) {
-        const int blk = jj, col = nn;
-        float x[16];
+        // Commit the prefetched chunk.  Rows past the end of the sequence are
+        // zero, with log alpha = 0 and beta = 0: g stays flat and those rows
+        // are inert in every later product.
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float acc = (r == col) ? 1.f : 0.f;
-#pragma unroll
-            for (int i = 0; i < r; ++i) acc -= As[(16 * blk + r) * PA + 16 * blk + i] * x[i];
-            x[r] = acc;
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) Ts[(16 * blk + r) * PA + 16 * blk + col] = x[r];
-    }
-    __syncthreads();
-    // Off-diagonal blocks, by distance d below the diagonal:
-    //   T_ab = -T_aa * sum_{b <= m < a} A_am T_mb     (fp32 matrix cores)
-    for (int d = 1; d < 4; ++d) {
-        if (w < 4 - d) {
-            const int b = w, a = w + d;
-            float4_t X = {0.f, 0.f, 0.f, 0.f};
-            for (int m = b; m < a; ++m) {
-                const float4_t af = *reinterpret_cast<const float4_t *>(As + (16 * a + nn) * PA + 16 * m + 4 * jj);
-                float4_t bf;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) bf[i] = Ts[(16 * m + 4 * jj + i) * PA + 16 * b + nn];
-                Mma<float>::issue(X, af, af, bf, bf);
+        for (int it = 0; it < QK_IT; ++it) {
+            const int idx = tid + it * 256;
+            const int r = idx / (DK / 8), c8 = (idx % (DK / 8)) * 8;
+            if (r >= len) {
+                rq[it].zero();
+                rk[it].zero();
             }
-            const float4_t tf = *reinterpret_cast<const float4_t *>(Ts + (16 * a + nn) * PA + 16 * a + 4 * jj);
-            float4_t Y = {0.f, 0.f, 0.f, 0.f};
-            Mma<float>::issue(Y, tf, tf, X, X);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) Ts[(16 * a + 4 * jj + i) * PA + 16 * b + nn] = -Y[i];
+            typename M::frag lo, hi;
+            to_op(rq[it], lo, hi);
+            *reinterpret_cast<typename M::frag *>(Qs + r * PQ + c8) = lo;
+            *reinterpret_cast<typename M::frag *>(Qs + r * PQ + c8 + 4) = hi;
+            to_op(rk[it], lo, hi);
+            *reinterpret_cast<typename M::frag *>(Ks + r * PQ + c8) = lo;
+            *reinterpret_cast<typename M::frag *>(Ks + r * PQ + c8 + 4) = hi;
+        }
+        if (w == 0) {
+            if (l >= len) la = bt = 0.f;
+            const float g = wave_inclusive_scan(la);
+            const float g_last = __shfl(g, C - 1, 64);
+            gs[l] = g;
+            bs[l] = bt;
+            ws_g[rh * 2 * C + l] = expf(g);               // gamma_r: decay from the chunk start
+            ws_g[rh * 2 * C + C + l] = expf(g_last - g);  // kappa_r: decay from row r to the chunk end
         }
         __syncthreads();
-    }
+        if (item + gridDim.x < items) load(item + gridDim.x);   // next item, in flight during compute
 
-    // M = T diag(beta), lower tiles packed, 4 consecutive elements per store.
-    for (int e4 = tid; e4 < kTriTiles * kTileElems / 4; e4 += 256) {
-        const int e = e4 * 4, tl = e >> 8, rr = (e >> 4) & 15, cc = e & 15;
-        int a, b;
-        tri_decode(tl, a, b);
-        const int r = 16 * a + rr, c = 16 * b + cc;
-        float4_t val;
+        // Lower-triangular 16x16 tiles (a, b), b <= a, of P^T = K Q^T (10) and
+        // of (K K^T)^T (10).  Lane (n, j) gets row r = 16a + n and columns
+        // c = 16b + 4j + i of P (resp. K K^T).
+        for (int t = w; t < 2 * kTriTiles; t += 4) {
+            const bool isq = t < kTriTiles;
+            const int tl = isq ? t : t - kTriTiles;
+            int a, b;
+            tri_decode(tl, a, b);
+            const OP *asrc = Ks + (16 * b + nn) * PQ + 4 * jj;
+            const OP *bsrc = (isq ? Qs : Ks) + (16 * a + nn) * PQ + 4 * jj;
+            float4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) val[i] = (c + i <= r) ? Ts[r * PA + c + i] * bs[c + i] : 0.f;
-        *reinterpret_cast<typename M::frag *>(ws_m + rh * kTriTiles * kTileElems + e) = M::cvt(val);
+            for (int p = 0; p < KP; ++p)
+                mma2(acc, F2::make(lds_frag(asrc + 32 * p), lds_frag(asrc + 32 * p + 16)),
+                     F2::make(lds_frag(bsrc + 32 * p), lds_frag(bsrc + 32 * p + 16)));
+            const int r = 16 * a + nn, c0 = 16 * b + 4 * jj;
+            const float gr = gs[r];
+            const float4_t gc = *reinterpret_cast<const float4_t *>(gs + c0);
+            float4_t val;
+            if (isq) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) val[i] = (c0 + i <= r) ? exp_neg(gr - gc[i]) * acc[i] : 0.f;
+                *reinterpret_cast<typename M::frag *>(ws_p + (rh * kTriTiles + tl) * kTileElems + 4 * l) = M::cvt(val);
+            } else {
+                const float br = bs[r];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) val[i] = (c0 + i < r) ? br * exp_neg(gr - gc[i]) * acc[i] : 0.f;
+                *reinterpret_cast<float4_t *>(As + r * PA + c0) = val;
+            }
+        }
+        __syncthreads();
+
+        // T = (I + A)^{-1}.  Diagonal 16x16 blocks by forward substitution,
+        // wave w takes block w, one column per lane.
+        {
+            const int blk = w, col = nn;
+            const float *arow = As + 16 * blk * PA + 16 * blk;
+            float x[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float acc = (r == col) ? 1.f : 0.f;
+#pragma unroll
+                for (int i = 0; i < r; ++i) acc -= arow[r * PA + i] * x[i];
+                x[r] = acc;
+            }
+            if (jj == 0) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) Ts[(16 * blk + r) * PA + 16 * blk + col] = x[r];
+            }
+        }
+        __syncthreads();
+        // Off-diagonal blocks, by distance d below the diagonal:
+        //   T_ab = -T_aa * sum_{b <= m < a} A_am T_mb     (fp32 matrix cores)
+        for (int d = 1; d < 4; ++d) {
+            if (w < 4 - d) {
+                const int b = w, a = w + d;
+                float4_t X = {0.f, 0.f, 0.f, 0.f};
+                for (int m = b; m < a; ++m) {
+                    const float4_t af = *reinterpret_cast<const float4_t *>(As + (16 * a + nn) * PA + 16 * m + 4 * jj);
+                    float4_t bf;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) bf[i] = Ts[(16 * m + 4 * jj + i) * PA + 16 * b + nn];
+                    Mma<float>::issue(X, af, af, bf, bf);
+                }
+                const float4_t tf = *reinterpret_cast<const float4_t *>(Ts + (16 * a + nn) * PA + 16 * a + 4 * jj);
+                float4_t Y = {0.f, 0.f, 0.f, 0.f};
+                Mma<float>::issue(Y, tf, tf, X, X);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) Ts[(16 * a + 4 * jj + i) * PA + 16 * b + nn] = -Y[i];
+            }
+            __syncthreads();
+        }
+
+        // M = T diag(beta) in fragment order: lane l of tile (a, b) writes
+        // M[16a + n][16b + 4j .. +3].
+        for (int tl = w; tl < kTriTiles; tl += 4) {
+            int a, b;
+            tri_decode(tl, a, b);
+            const int r = 16 * a + nn, c0 = 16 * b + 4 * jj;
+            const float4_t tv = *reinterpret_cast<const float4_t *>(Ts + r * PA + c0);
+            const float4_t bv = *reinterpret_cast<const float4_t *>(bs + c0);
+            float4_t val;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) val[i] = (c0 + i <= r) ? tv[i] * bv[i] : 0.f;
+            *reinterpret_cast<typename M::frag *>(ws_m + (rh * kTriTiles + tl) * kTileElems + 4 * l) = M::cvt(val);
+        }
+        __syncthreads();   // LDS is reused by the next item
     }
 }
 
@@ -348,13 +383,12 @@ struct StateSmem {
     static constexpr int PQ = DK + 8 / (int)sizeof(OP);      // Q, K row pitch (elements)
     static constexpr int BV = 16 * NW;
     static constexpr int PV = BV + 16 / (int)sizeof(in_t);   // V row pitch, 16-byte rows
-    static constexpr int PM = 16 + 4;                        // packed tile row pitch (M, P)
     static constexpr size_t q_off = 0;
     static constexpr size_t k_off = q_off + sizeof(OP) * C * PQ;
     static constexpr size_t v_off = k_off + sizeof(OP) * C * PQ;
     static constexpr size_t m_off = v_off + sizeof(in_t) * C * PV;
-    static constexpr size_t p_off = m_off + sizeof(OP) * kTriTiles * 16 * PM;
-    static constexpr size_t g_off = p_off + sizeof(OP) * kTriTiles * 16 * PM;
+    static constexpr size_t p_off = m_off + sizeof(OP) * kTriTiles * kTileElems;   // fragment order
+    static constexpr size_t g_off = p_off + sizeof(OP) * kTriTiles * kTileElems;
     static constexpr size_t bytes = g_off + sizeof(float) * 2 * C;
 };
 
@@ -426,7 +460,7 @@ __global__ __launch_bounds__(64 * NW) void chunk_state_kernel(
     using M = Mma<OP>;
     using frag = typename M::frag;
     using L = StateSmem<in_t, OP, DK, NW>;
-    constexpr int PQ = L::PQ, PV = L::PV, PM = L::PM, BV = L::BV;
+    constexpr int PQ = L::PQ, PV = L::PV, BV = L::BV;
     constexpr int NT = 64 * NW;                              // threads
     constexpr int KT = DK / 16;                              // k-tiles along dk
     constexpr int QK_UNITS = C * (DK / 8);                   // 8-element pieces of Q (and K)
@@ -466,7 +500,7 @@ __global__ __launch_bounds__(64 * NW) void chunk_state_kernel(
     const int plk_lane = 4 * jj * PQ + nn;                          // fp32 direct column reads of K
     const int trv_lane = (4 * jj + (nn >> 2)) * PV + 4 * (nn & 3) + 16 * w;
     const int plv_lane = 4 * jj * PV + nn + 16 * w;
-    const int tile_lane = nn * PM + 4 * jj;                       // packed M / P tiles
+    const int tile_lane = 4 * l;                                  // M / P tiles in fragment order
 
     // S^T tiles: sT[mt][i] = S[v0 + nn][16 mt + 4 jj + i].
     float4_t sT[KT];
@@ -486,7 +520,7 @@ __global__ __launch_bounds__(64 * NW) void chunk_state_kernel(
     // prefetched registers are not touched until the commit after the next
     // barrier, so the loads stay in flight during the chunk's compute.
     Raw8<in_t> pq[QK_IT], pk[QK_IT], pv[V_IT];
-    int4 pm[MP_IT], pp[MP_IT];
+    u32x4_t pm[MP_IT], pp[MP_IT];
     float pg[G_IT];
     const int rowq = H * DK, rowv = H * DV;   // element stride between tokens
     // Loop-invariant per-thread element offsets inside a chunk (row r, 8 columns).
@@ -541,8 +575,8 @@ __global__ __launch_bounds__(64 * NW) void chunk_state_kernel(
 #pragma unroll
         for (int it = 0; it < MP_IT; ++it) {
             const int idx = min(tid + it * NT, MP_N - 1);
-            pm[it] = *reinterpret_cast<const int4 *>(mc + idx * MP_VEC);
-            pp[it] = *reinterpret_cast<const int4 *>(pc + idx * MP_VEC);
+            pm[it] = *reinterpret_cast<const u32x4_t *>(mc + idx * MP_VEC);
+            pp[it] = *reinterpret_cast<const u32x4_t *>(pc + idx * MP_VEC);
         }
 #pragma unroll
         for (int it = 0; it < G_IT; ++it) pg[it] = ws_g[rh * 2 * C + min(tid + it * NT, 2 * C - 1)];
@@ -580,13 +614,8 @@ __global__ __launch_bounds__(64 * NW) void chunk_state_kernel(
         for (int it = 0; it < MP_IT; ++it) {
             const int idx = tid + it * NT;
             if (idx < MP_N) {
-                const int e = idx * MP_VEC, tl = e >> 8, rr = (e >> 4) & 15, cc = e & 15;
-                int2 *md = reinterpret_cast<int2 *>(Ms + (tl * 16 + rr) * PM + cc);
-                int2 *pd = reinterpret_cast<int2 *>(Ps + (tl * 16 + rr) * PM + cc);
-                md[0] = int2{pm[it].x, pm[it].y};
-                md[1] = int2{pm[it].z, pm[it].w};
-                pd[0] = int2{pp[it].x, pp[it].y};
-                pd[1] = int2{pp[it].z, pp[it].w};
+                *reinterpret_cast<u32x4_t *>(Ms + idx * MP_VEC) = pm[it];
+                *reinterpret_cast<u32x4_t *>(Ps + idx * MP_VEC) = pp[it];
             }
         }
 #pragma unroll
@@ -623,29 +652,23 @@ __global__ __launch_bounds__(64 * NW) void chunk_state_kernel(
 #pragma unroll
         for (int p = 0; p < KP; ++p) sB[p] = F2::cvt(sT[2 * p], sT[2 * p + 1]);
 
-        // X_K = K S^T and (S Q^T) for the output: both need only S.  The K and
-        // Q fragments of row tile mt+1 are read while tile mt's products run.
-        float4_t x[4], oq[4];
-        F2 kf[2][KP], qf[2][KP];
-        auto load_kq = [&](F2 (&kd)[KP], F2 (&qd)[KP], int mt) {
-            const OP *ks = Ks + 16 * mt * PQ + row_lane;
-            const OP *qs = Qs + 16 * mt * PQ + row_lane;
+        // X_K = K S^T; the K fragments of row tile mt+1 are read while tile
+        // mt's products run.
+        float4_t x[4];
+        {
+            F2 kf[2][KP];
+            auto load_k = [&](F2 (&kd)[KP], int mt) {
+                const OP *ks = Ks + 16 * mt * PQ + row_lane;
 #pragma unroll
-            for (int p = 0; p < KP; ++p) {
-                kd[p] = F2::make(lds_frag(ks + 32 * p), lds_frag(ks + 32 * p + 16));
-                qd[p] = F2::make(lds_frag(qs + 32 * p), lds_frag(qs + 32 * p + 16));
-            }
-        };
-        load_kq(kf[0], qf[0], 0);
+                for (int p = 0; p < KP; ++p) kd[p] = F2::make(lds_frag(ks + 32 * p), lds_frag(ks + 32 * p + 16));
+            };
+            load_k(kf[0], 0);
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-            if (mt < 3) load_kq(kf[(mt + 1) & 1], qf[(mt + 1) & 1], mt + 1);
-            x[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
-            oq[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
+            for (int mt = 0; mt < 4; ++mt) {
+                if (mt < 3) load_k(kf[(mt + 1) & 1], mt + 1);
+                x[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int p = 0; p < KP; ++p) {
-                mma2(x[mt], kf[mt & 1][p], sB[p]);
-                mma2(oq[mt], sB[p], qf[mt & 1][p]);
+                for (int p = 0; p < KP; ++p) mma2(x[mt], kf[mt & 1][p], sB[p]);
             }
         }
 
@@ -667,8 +690,8 @@ __global__ __launch_bounds__(64 * NW) void chunk_state_kernel(
         // pair 0 = tiles (0,1), pair 1 = tiles (2,3); missing tiles are zero.
         auto tri_pair = [&](const OP *T, int mt, int p) {
             const int k0 = 2 * p, k1 = 2 * p + 1;
-            const typename M::frag lo = k0 <= mt ? lds_frag(T + tri_index(mt, k0) * 16 * PM + tile_lane) : M::zero();
-            const typename M::frag hi = k1 <= mt ? lds_frag(T + tri_index(mt, k1) * 16 * PM + tile_lane) : M::zero();
+            const typename M::frag lo = k0 <= mt ? lds_frag(T + tri_index(mt, k0) * kTileElems + tile_lane) : M::zero();
+            const typename M::frag hi = k1 <= mt ? lds_frag(T + tri_index(mt, k1) * kTileElems + tile_lane) : M::zero();
             return F2::make(lo, hi);
         };
         float4_t Vp[4];
@@ -700,15 +723,10 @@ __global__ __launch_bounds__(64 * NW) void chunk_state_kernel(
             dB[1] = F2::cvt(d[2], d[3]);
         }
 
-        // O^T = (S Q^T) diag(gamma) + V'^T P^T, interleaved with the state
-        // update S^T <- gamma_C S^T + K^T (kappa o V') (independent work);
-        // K^T fragments come from transposed reads of K.
-        F2 pf[4][2];
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-            pf[rt][0] = tri_pair(Ps, rt, 0);
-            if (rt >= 2) pf[rt][1] = tri_pair(Ps, rt, 1);
-        }
+        // State update S^T <- gamma_C S^T + K^T (kappa o V') (K^T fragments by
+        // transposed reads), interleaved with the output tiles
+        // O^T = (S Q^T) diag(gamma) + V'^T P^T, which only need the S
+        // fragments taken before the update.
         auto load_kt = [&](F2 (&kd)[2], int mt) {
 #pragma unroll
             for (int p = 0; p < 2; ++p)
@@ -716,6 +734,7 @@ __global__ __launch_bounds__(64 * NW) void chunk_state_kernel(
                                  kt_frag<OP>(Ks + (32 * p + 16) * PQ + 16 * mt, trk_lane, plk_lane, PQ));
         };
         const float gC = gam_s[C - 1];
+        float4_t oq[4];
         F2 ktf[2][2];
         load_kt(ktf[0], 0);
         constexpr int NSTEP = KT > 4 ? KT : 4;           // dk row tiles and output row tiles
@@ -729,9 +748,14 @@ __global__ __launch_bounds__(64 * NW) void chunk_state_kernel(
             }
             if (mt < 4) {
                 const int rt = mt;
+                const OP *qs = Qs + 16 * rt * PQ + row_lane;
+                oq[rt] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int p = 0; p < KP; ++p)
+                    mma2(oq[rt], sB[p], F2::make(lds_frag(qs + 32 * p), lds_frag(qs + 32 * p + 16)));
                 oq[rt] *= gam_s[16 * rt + nn];
-                mma2(oq[rt], vB[0], pf[rt][0]);
-                if (rt >= 2) mma2(oq[rt], vB[1], pf[rt][1]);
+                mma2(oq[rt], vB[0], tri_pair(Ps, rt, 0));
+                if (rt >= 2) mma2(oq[rt], vB[1], tri_pair(Ps, rt, 1));
             }
         }
         {
@@ -825,7 +849,9 @@ static hipError_t launch_dk(const ChunkArgs &a, const ChunkWorkspace &w, hipStre
         hipError_t e = allow_smem(kern, L::bytes);
         if (e != hipSuccess) return e;
         ProfScope prof("gdn_chunk_prep", st);
-        kern<<<dim3((unsigned)w.max_rows, (unsigned)a.H), dim3(256), L::bytes, st>>>(
+        const int64_t items = w.max_rows * a.H;
+        const int64_t grid = items < 768 ? items : 768;   // about three resident blocks per CU
+        kern<<<dim3((unsigned)grid), dim3(256), L::bytes, st>>>(
             a.H, reinterpret_cast<const int32_t *>(ws + w.off_meta),
             reinterpret_cast<const int32_t *>(ws + w.off_rowtok),
             reinterpret_cast<const int32_t *>(ws + w.off_rowlen), static_cast<const in_t *>(a.q),

@@ -27,6 +27,7 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef uint16_t ushort4_t __attribute__((ext_vector_type(4)));
 typedef uint16_t ushort8_t __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));   // raw 16 bytes, a native vector
 
 struct bf16_t {
     uint16_t bits;
