@@ -35,6 +35,7 @@ gdn_status ok() {
 bool valid_dtype(int32_t d) { return d == GDN_FP32 || d == GDN_BF16 || d == GDN_FP16; }
 size_t dtype_size(int32_t d) { return d == GDN_FP32 ? 4 : 2; }
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 struct Range {
     const char *name;
@@ -169,10 +170,14 @@ gdn_status gdn_chunk_fwd(const gdn_chunk_desc *desc, const void *q, const void *
     const auto w = gdn::chunk_workspace_layout(d.batch, d.seqlen, d.num_seqs, packed, d.heads, d.in_dtype);
     if (workspace_bytes < w.total)
         return fail(GDN_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, w.total);
-    const void *ptrs[] = {q, k, v, log_alpha, beta, init_state, cu_seqlens, o, final_state, workspace};
-    const char *names[] = {"q", "k", "v", "log_alpha", "beta", "init_state", "cu_seqlens", "o", "final_state", "workspace"};
-    for (int i = 0; i < 10; ++i)
+    const void *ptrs[] = {q, k, v, init_state, o, final_state, workspace};
+    const char *names[] = {"q", "k", "v", "init_state", "o", "final_state", "workspace"};
+    for (int i = 0; i < 7; ++i)
         if (ptrs[i] && !aligned16(ptrs[i])) return fail(GDN_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
+    const void *sptrs[] = {log_alpha, beta, cu_seqlens};
+    const char *snames[] = {"log_alpha", "beta", "cu_seqlens"};
+    for (int i = 0; i < 3; ++i)
+        if (sptrs[i] && !aligned4(sptrs[i])) return fail(GDN_ERR_ALIGN, "%s is not 4-byte aligned", snames[i]);
 
     const size_t isz = dtype_size(d.in_dtype), osz = dtype_size(d.out_dtype);
     const size_t th = (size_t)toks * d.heads;
@@ -224,10 +229,11 @@ gdn_status gdn_decode_step(int32_t N, int32_t H, int32_t dk, int32_t dv, int32_t
     if ((int64_t)N * H == 0) return ok();
     if (!state || !q || !k || !v || !log_alpha || !beta || !o)
         return fail(GDN_ERR_NULL, "state, q, k, v, log_alpha, beta and o are required");
-    const void *ptrs[] = {state, q, k, v, log_alpha, beta, o};
-    const char *names[] = {"state", "q", "k", "v", "log_alpha", "beta", "o"};
-    for (int i = 0; i < 7; ++i)
+    const void *ptrs[] = {state, q, k, v, o};
+    const char *names[] = {"state", "q", "k", "v", "o"};
+    for (int i = 0; i < 5; ++i)
         if (!aligned16(ptrs[i])) return fail(GDN_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
+    if (!aligned4(log_alpha) || !aligned4(beta)) return fail(GDN_ERR_ALIGN, "log_alpha and beta must be 4-byte aligned");
     const size_t nh = (size_t)N * H;
     const Range r_o = rng("o", o, nh * dv * dtype_size(out_dtype));
     const Range others[] = {rng("state", state, nh * dv * dk * sizeof(float)), rng("q", q, nh * dk * dtype_size(in_dtype)),

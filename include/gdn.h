@@ -34,7 +34,9 @@
  *   - All argument checks run before anything is enqueued: a call that
  *     returns an error status has launched nothing and written nothing.
  *     gdn_last_error_message() then describes the failure (thread-local).
- *   - Device pointers must be 16-byte aligned (GDN_ERR_ALIGN otherwise).
+ *   - q, k, v, o, the state buffers and the workspace must be 16-byte
+ *     aligned; log_alpha, beta and cu_seqlens 4-byte aligned
+ *     (GDN_ERR_ALIGN otherwise).
  *   - Calls are reentrant and may run concurrently on different streams with
  *     disjoint buffers.
  *   - Preconditions that are documented but NOT checked on the device:
@@ -64,7 +66,7 @@ typedef enum {
     GDN_ERR_SHAPE = 2,        /* sizes negative, zero where not allowed, or
                                  inconsistent                                     */
     GDN_ERR_DTYPE = 3,        /* unknown dtype code                               */
-    GDN_ERR_ALIGN = 4,        /* a device pointer is not 16-byte aligned          */
+    GDN_ERR_ALIGN = 4,        /* a device pointer is misaligned (see CONVENTIONS) */
     GDN_ERR_UNSUPPORTED = 5,  /* well-formed but not built (head dims, chunk size,
                                  dtype combination)                               */
     GDN_ERR_WORKSPACE = 6,    /* workspace NULL or smaller than required          */
@@ -121,8 +123,9 @@ const char *gdn_last_error_message(void);
  * Workspace for gdn_chunk_fwd, in bytes, written to *bytes (host pointer).
  * Depends only on the descriptor.  The workspace holds the chunk table built
  * from cu_seqlens and, per (chunk, head), the UT-transform matrix
- * T diag(beta), the decay-masked Q K^T block and the chunk's cumulative
- * log-decay.  It need not be initialised and may be reused by later calls
+ * T diag(beta), the decay-masked Q K^T block and the chunk's decay factors
+ * (exp of the cumulative log-decay from the chunk start, and to the chunk
+ * end).  It need not be initialised and may be reused by later calls
  * that are ordered after this one on the stream.
  * Errors: GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_DTYPE, GDN_ERR_UNSUPPORTED.
  */

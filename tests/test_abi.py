@@ -89,6 +89,7 @@ def test_chunk_argument_errors(lib):
     assert call_chunk(lib, d, ws=None) == 6                             # no workspace
     assert call_chunk(lib, d, ws_bytes=16) == 6                         # workspace too small
     assert call_chunk(lib, d, k=FAKE + 8) == 4                          # misaligned
+    assert call_chunk(lib, d, la=FAKE + 2) == 4                         # gates: 4-byte alignment
     assert call_chunk(lib, d, cu=FAKE) == 2                             # cu with batch != 1
     assert call_chunk(lib, desc(num_seqs=3)) == 2                       # N != B without cu
     assert call_chunk(lib, d, o=FAKE) == 8                              # o aliases q
@@ -108,6 +109,8 @@ def test_decode_argument_errors(lib):
     assert call(dv=5000) == 5
     assert call(q=None) == 1
     assert call(v=FAKE + 2) == 4
+    assert call(la=FAKE + 2) == 4                   # gates need 4-byte alignment
+    assert call(la=FAKE + 4, b=FAKE + 8) != 4        # ... and no more
     assert call(o=FAKE2 + 64) == 8                  # o inside the state
     assert call(N=0, state=None, q=None) == 0       # nothing to do
 
