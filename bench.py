@@ -51,6 +51,36 @@ def decode_min_bytes(N, H, dk, dv, in_bytes, out_bytes):
     return nh * dv * dk * 4 * 2 + nh * (2 * dk + dv) * in_bytes + nh * 2 * 4 + nh * dv * out_bytes
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+CSRC = os.path.join(ROOT, "gated_delta_rule_24_amd", "csrc")
+
+
+def kernel_sources_digest(files):
+    """sha256 over the sources a kernel is built from, to tie counter readings to a kernel version."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed FETCH_SIZE / WRITE_SIZE readings, each scaled
+    by what the same counter reads for a copy of known size; None when the kernel's sources have changed
+    since the counters were taken (or none were taken)."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)
+    except OSError:
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    if not k or kernel_sources_digest(k["sources"]) != k["sources_sha256"]:
+        return None
+    cal = rec["copy_calibration"]
+    return 1024.0 * (k["fetch_kib"] * cal["fetch_scale"] + k["write_kib"] * cal["write_scale"])
+
+
 def _to(x, dev, dt):
     import numpy as np
     import torch
@@ -100,7 +130,7 @@ def run_prefill(args, gdn, W, dev):
         "peak": HBM_PEAK_GBS,
         "unit": "GB/s",
         "frac": min_bytes / dom_s / 1e9 / HBM_PEAK_GBS,
-        "traffic": None,
+        "traffic": measured_traffic(dom),
         "algorithmic_bytes": min_bytes,
         "mfma_tflops": flops / dom_s / 1e12,
         "mfma_frac": flops / dom_s / 1e12 / MFMA_F16_PEAK_TFLOPS,
@@ -146,7 +176,7 @@ def run_decode(args, gdn, W, dev):
                    "in_dtype": "bf16", "state": "fp32 in place"},
         "roofline": {"kernel": "gdn_decode_step", "bound": "hbm", "achieved": dbytes / dec_kernel_s / 1e9,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dbytes / dec_kernel_s / 1e9 / HBM_PEAK_GBS,
-                     "traffic": None, "algorithmic_bytes": dbytes, "avg_us": dec_kernel_s * 1e6},
+                     "traffic": measured_traffic("gdn_decode_step"), "algorithmic_bytes": dbytes, "avg_us": dec_kernel_s * 1e6},
     }
     del state, pool, od
     torch.cuda.empty_cache()
@@ -154,21 +184,32 @@ def run_decode(args, gdn, W, dev):
 
 
 def run_cpu_baseline(args, inp):
+    """The fp64 oracle on the prefill workload's inputs: a prefix of every sequence, grown until one
+    pass takes about --cpu-seconds; once the prefix is the whole workload, whole passes are repeated
+    until the total reaches --cpu-seconds."""
     import oracle
     threads = oracle.num_threads()
     B, T, H = inp.B, inp.T, inp.H
-    sl = 64
-    while True:
+
+    def one(sl):
         t0 = time.perf_counter()
         oracle.recurrent(inp.q[:, :sl], inp.k[:, :sl], inp.v[:, :sl], inp.log_alpha[:, :sl], inp.beta[:, :sl],
                          threads=threads)
-        el = time.perf_counter() - t0
+        return time.perf_counter() - t0
+
+    sl = 64
+    while True:
+        el = one(sl)
         if el >= args.cpu_seconds or sl >= T:
             break
         sl = min(T, max(sl * 2, int(sl * args.cpu_seconds / max(el, 1e-3) * 1.1)))
-    return {"value": B * sl / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"prefill workload, first {sl} tokens of each of the {B} sequences, all {H} heads "
-                      f"(fp64 token recurrence, {el:.1f} s)"}
+    passes = 1
+    while el < args.cpu_seconds:
+        el += one(sl)
+        passes += 1
+    return {"value": passes * B * sl / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"prefill workload, first {sl} of {T} tokens of each of the {B} sequences, all {H} heads, "
+                      f"{passes} pass(es) (fp64 token recurrence, {el:.1f} s)"}
 
 
 def main():
@@ -179,8 +220,10 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--only", choices=["prefill", "decode"], default=None,
-                    help="run one leg only (for profiler runs) and print its part of the line")
+    ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None,
+                    help="run one leg only (for profiler runs) and print its part of the line; "
+                         "'copy' runs a plain 256 MiB read + 256 MiB write elementwise kernel used to "
+                         "calibrate the FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the path has no multi-GPU mode; "
@@ -202,6 +245,16 @@ def main():
 
     if args.only == "decode":
         print(json.dumps({"decode": run_decode(args, gdn, W, dev)}), flush=True)
+        return
+    if args.only == "copy":
+        n = 64 * 1024 * 1024                      # 256 MiB of fp32
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(max(1, args.steps)):
+            torch.mul(a, 1.0, out=b)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy": {"bytes_read": 4 * n, "bytes_written": 4 * n, "launches": max(1, args.steps)}}),
+              flush=True)
         return
     pre, inp = run_prefill(args, gdn, W, dev)
     if args.only == "prefill":
