@@ -19,8 +19,11 @@ ARCH = os.environ.get("GDN_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # -packed-fp32-ops off: the compiler must not form packed fp32 VALU ops.
+# -amdgpu-mfma-vgpr-form: matrix-core results go to ordinary VGPRs, so the
+# fp32 state and accumulators are not shuttled between AGPRs and VGPRs.
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-mllvm", "-amdgpu-mfma-vgpr-form",
           "-Wall", "-Wno-unused-function", "-I", os.path.join(HERE, "..", "include")]
 
 

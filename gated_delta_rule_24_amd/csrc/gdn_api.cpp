@@ -1,7 +1,7 @@
 // C ABI of the gated delta rule core: argument validation, workspace sizing,
 // launch timing, error reporting.  Declarations and the full contract are in
 // include/gdn.h.  Every check runs before anything is enqueued.
-#include "../../include/gdn.h"
+#include "gdn.h"
 #include "gdn_launch.h"
 
 #include <hip/hip_runtime.h>

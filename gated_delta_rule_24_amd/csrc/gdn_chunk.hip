@@ -362,8 +362,6 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(int H, const int32_t *_
 // (sequence, head).  Blocks of one (sequence, head) are placed on the same
 // XCD (workgroups are dispatched to the 8 XCDs round-robin by block id) so
 // the Q, K, M, P blocks they all read are shared through that XCD's L2.
-// The global loads of chunk ci+1 are issued into registers before chunk ci
-// is computed, so their latency overlaps the matrix-core work.
 //
 // Products per chunk and wave (16 value columns v, S^T slice in sT):
 //   X_K = K S^T                          (C x 16)   A: K rows,         B: sT
@@ -371,25 +369,46 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(int H, const int32_t *_
 //   V'  = M Y                            (C x 16)   A: M,              B: Y
 //   O^T = (S Q^T) diag(gamma) + V'^T P^T (16 x C)   A: sT / V',        B: Q, P rows
 //   S^T = gamma_C S^T + K^T (kappa o V') (dk x 16)  A: K read transposed, B: kappa o V'
-// Everything staged in LDS is row-major; the two transposed operands (K^T
-// and V in accumulator layout) use the 16-bit transposed LDS read.  O is
-// produced transposed so each lane holds four consecutive value columns of
-// one token row and writes them with one vector store.
+// O is produced transposed so each lane holds four consecutive value columns
+// of one token row and writes them with one vector store.
+//
+// Order of dk inside the state registers: tile 2p + h, lane (n, j), element
+// i holds S^T[32p + 8j + 4h + i][n].  Read as a k-tile pair, lane j then
+// covers dk 32p + 8j .. 32p + 8j + 7, eight consecutive values, so every
+// Q or K operand fragment is one 16-byte LDS read of a row.
+//
+// Staging.  Q and K are loaded into registers one chunk ahead, converted to
+// operand precision and written to LDS; V, M, P and the decay factors are
+// copied global -> LDS by direct loads (16 bytes per lane, lane order) into
+// the buffer of the next chunk while the current chunk is computed.  V rows
+// have no padding; their 16-byte units are XOR-swizzled by row so the
+// transposed reads do not collide in the LDS banks.  Q and K rows are padded
+// by 32 bytes, which makes both the 16-byte row reads and the transposed
+// reads conflict-free.  Q and K are double-buffered when LDS allows, so a
+// chunk needs one barrier; otherwise a second barrier separates their
+// commit from the reads.
 // ============================================================================
 template <typename in_t, typename OP, int DK, int NW>
 struct StateSmem {
-    // Pitches chosen so the 64 lanes of each operand read (and of the
-    // transposed reads) spread evenly over the 32 LDS banks.
-    static constexpr int PQ = DK + 8 / (int)sizeof(OP);      // Q, K row pitch (elements)
-    static constexpr int BV = 16 * NW;
-    static constexpr int PV = BV + 16 / (int)sizeof(in_t);   // V row pitch, 16-byte rows
-    static constexpr size_t q_off = 0;
-    static constexpr size_t k_off = q_off + sizeof(OP) * C * PQ;
-    static constexpr size_t v_off = k_off + sizeof(OP) * C * PQ;
-    static constexpr size_t m_off = v_off + sizeof(in_t) * C * PV;
-    static constexpr size_t p_off = m_off + sizeof(OP) * kTriTiles * kTileElems;   // fragment order
-    static constexpr size_t g_off = p_off + sizeof(OP) * kTriTiles * kTileElems;
-    static constexpr size_t bytes = g_off + sizeof(float) * 2 * C;
+    static constexpr int BV = 16 * NW;                                  // value columns per block
+    static constexpr int QROW = DK * (int)sizeof(OP) + 32;              // bytes per Q / K row
+    static constexpr int VROW = BV * (int)sizeof(in_t);                 // bytes per V row
+    static constexpr int VUNITS = VROW / 16;                            // 16-byte units per V row
+    static constexpr int VSWZ = VUNITS >= 8 ? 7 : VUNITS - 1;           // unit XOR mask (row bits)
+    static constexpr size_t QK = (size_t)C * QROW;                      // one Q or K block
+    static constexpr size_t VB = (size_t)C * VROW;
+    static constexpr size_t MP = sizeof(OP) * kTriTiles * kTileElems;   // one M or P block
+    static constexpr size_t GB = 1024;                                  // gamma, kappa, spare half
+    static constexpr size_t DMA = VB + 2 * MP + GB;                     // directly loaded inputs
+    static constexpr int QKB = (4 * QK + 2 * DMA <= 160 * 1024) ? 2 : 1;   // Q/K buffers
+    static constexpr size_t qk_off(int b) { return (size_t)b * 2 * QK; }   // Q, then K
+    static constexpr size_t dma_off(int b) { return (size_t)QKB * 2 * QK + (size_t)b * DMA; }
+    static constexpr size_t m_rel = VB, p_rel = VB + MP, g_rel = VB + 2 * MP;
+    static constexpr size_t bytes = (size_t)QKB * 2 * QK + 2 * DMA;
+    static constexpr int NV = (int)(VB / 1024), NM = (int)(MP / 1024);
+    static constexpr int NDMA = NV + 2 * NM + 1;                         // 1 KiB wave copies per chunk
+    static_assert(VB % 1024 == 0 && MP % 1024 == 0, "direct loads move whole 1 KiB wave blocks");
+    static_assert(QROW % 16 == 0 && VROW % 16 == 0, "16-byte rows");
 };
 
 // Four fp32 values to an output row (one 8- or 16-byte store).
@@ -406,52 +425,70 @@ __device__ __forceinline__ void store_out4(void *o, int64_t idx, int odt, float4
     }
 }
 
-// Column fragment of a row-major matrix in LDS: rows R..R+3 of column c
-// for lane (c = c0 + nn, R = row0 + 4 jj), i.e. an operand tile element
-// set {X[row0 + 4 jj + i][c0 + nn], i < 4}.  `lane_off` is the per-lane
-// offset ((4 jj + nn/4) * pitch + 4 (nn % 4)) used by the transposed read;
-// the fp32 path reads the four rows directly.
+// Eight consecutive operand values of one LDS row: a k-tile pair fragment.
+__device__ __forceinline__ Frag2<_Float16> row_frag2(const _Float16 *p) {
+    return Frag2<_Float16>{*reinterpret_cast<const half8_t *>(p)};
+}
+__device__ __forceinline__ Frag2<float> row_frag2(const float *p) {
+    return Frag2<float>{*reinterpret_cast<const float4_t *>(p), *reinterpret_cast<const float4_t *>(p + 4)};
+}
+// Eight values as the 16-byte LDS store of a row segment.
+__device__ __forceinline__ void store_row8(_Float16 *p, half4_t lo, half4_t hi) {
+    *reinterpret_cast<half8_t *>(p) = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ void store_row8(float *p, float4_t lo, float4_t hi) {
+    reinterpret_cast<float4_t *>(p)[0] = lo;
+    reinterpret_cast<float4_t *>(p)[1] = hi;
+}
+
+// V in accumulator layout: V[R + i][c] for lane (c = c0 + n, R = row0 + 4 j),
+// i < 4, as fp32.  16-bit V uses one transposed read at the lane's address
+// `a`; fp32 V reads the four rows at the four lane addresses a[0..3].
 template <typename T>
-struct ColFrag;
+struct VFrag;
 template <>
-struct ColFrag<_Float16> {
-    __device__ __forceinline__ static float4_t read_f32(const _Float16 *base, int lane_off, int, int) {
-        const half4_t h = __builtin_bit_cast(half4_t, lds_read_tr16(base + lane_off));
-        return float4_t{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
-    }
-};
-template <>
-struct ColFrag<bf16_t> {
-    __device__ __forceinline__ static float4_t read_f32(const bf16_t *base, int lane_off, int, int) {
-        const uint2 r = lds_read_tr16(base + lane_off);
+struct VFrag<bf16_t> {
+    __device__ __forceinline__ static float4_t read(const unsigned char *base, const int (&a)[4]) {
+        const uint2 r = lds_read_tr16(base + a[0]);
         return float4_t{__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xffff0000u),
                         __uint_as_float(r.y << 16), __uint_as_float(r.y & 0xffff0000u)};
     }
 };
 template <>
-struct ColFrag<float> {
-    // plain_off = (4 jj) * pitch + nn; rows are `pitch` apart
-    __device__ __forceinline__ static float4_t read_f32(const float *base, int, int plain_off, int pitch) {
-        const float *p = base + plain_off;
-        return float4_t{p[0], p[pitch], p[2 * pitch], p[3 * pitch]};
+struct VFrag<_Float16> {
+    __device__ __forceinline__ static float4_t read(const unsigned char *base, const int (&a)[4]) {
+        const half4_t h = __builtin_bit_cast(half4_t, lds_read_tr16(base + a[0]));
+        return float4_t{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+    }
+};
+template <>
+struct VFrag<float> {
+    __device__ __forceinline__ static float4_t read(const unsigned char *base, const int (&a)[4]) {
+        return float4_t{*reinterpret_cast<const float *>(base + a[0]), *reinterpret_cast<const float *>(base + a[1]),
+                        *reinterpret_cast<const float *>(base + a[2]), *reinterpret_cast<const float *>(base + a[3])};
     }
 };
 
-// Column fragment of K (fp16 or fp32 operand copy in LDS) for the K^T operand.
-template <typename OP>
-__device__ __forceinline__ typename Mma<OP>::frag kt_frag(const OP *base, int tr_lane, int plain_lane, int pitch);
-template <>
-__device__ __forceinline__ half4_t kt_frag<_Float16>(const _Float16 *base, int tr_lane, int, int) {
-    return __builtin_bit_cast(half4_t, lds_read_tr16(base + tr_lane));
+// K^T operand fragment (rows = dk, k = tokens) of one k-tile: lane (n, j)
+// gets K[R + i][d(n)], i < 4.  fp16: one transposed read at `a` (bytes from
+// the K block); fp32: four reads, rows QROW apart.
+__device__ __forceinline__ half4_t kt_frag(const unsigned char *p, int, _Float16 *) {
+    return __builtin_bit_cast(half4_t, lds_read_tr16(p));
 }
-template <>
-__device__ __forceinline__ float4_t kt_frag<float>(const float *base, int, int plain_lane, int pitch) {
-    const float *p = base + plain_lane;
-    return float4_t{p[0], p[pitch], p[2 * pitch], p[3 * pitch]};
+__device__ __forceinline__ float4_t kt_frag(const unsigned char *p, int qrow, float *) {
+    return float4_t{*reinterpret_cast<const float *>(p), *reinterpret_cast<const float *>(p + qrow),
+                    *reinterpret_cast<const float *>(p + 2 * qrow), *reinterpret_cast<const float *>(p + 3 * qrow)};
+}
+
+// One 1 KiB wave copy global -> LDS: lane l's 16 bytes at g land at lds + 16 l
+// (gfx950 direct load to LDS; the LDS base is wave-uniform).
+__device__ __forceinline__ void dma16(const void *g, uint32_t lds) {
+    __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void *)(uintptr_t)g,
+                                     (__attribute__((address_space(3))) void *)(uintptr_t)lds, 16, 0, 0);
 }
 
 template <typename in_t, typename OP, int DK, int NW>
-__global__ __launch_bounds__(64 * NW) void chunk_state_kernel(
+__global__ __launch_bounds__(128 * NW) void chunk_state_kernel(
     int NH, int H, int DV, int nvt, int odt, const int32_t *__restrict__ meta,
     const int32_t *__restrict__ cu_ws, const int32_t *__restrict__ row0,
     const in_t *__restrict__ q, const in_t *__restrict__ k, const in_t *__restrict__ v,
@@ -459,26 +496,17 @@ __global__ __launch_bounds__(64 * NW) void chunk_state_kernel(
     const float *init_state, float *final_state, void *__restrict__ o) {
     using M = Mma<OP>;
     using frag = typename M::frag;
+    using F2 = Frag2<OP>;
     using L = StateSmem<in_t, OP, DK, NW>;
-    constexpr int PQ = L::PQ, PV = L::PV, BV = L::BV;
-    constexpr int NT = 64 * NW;                              // threads
-    constexpr int KT = DK / 16;                              // k-tiles along dk
+    constexpr int QROW = L::QROW, VROW = L::VROW, BV = L::BV, QKB = L::QKB;
+    constexpr int NT = 64 * NW;                              // threads per role
+    constexpr int KT = DK / 16;                              // state tiles along dk
+    constexpr int KP = DK / 32;                              // k-tile pairs along dk
     constexpr int QK_UNITS = C * (DK / 8);                   // 8-element pieces of Q (and K)
     constexpr int QK_IT = (QK_UNITS + NT - 1) / NT;
-    constexpr int V_UNITS = C * (BV / 8);
-    constexpr int V_IT = (V_UNITS + NT - 1) / NT;
-    constexpr int MP_VEC = 16 / sizeof(OP);                  // M/P elements per 16-byte load
-    constexpr int MP_N = kTriTiles * kTileElems / MP_VEC;
-    constexpr int MP_IT = (MP_N + NT - 1) / NT;
-    constexpr int G_IT = (2 * C + NT - 1) / NT;
+    constexpr int OPB = (int)sizeof(OP);
     extern __shared__ __align__(16) unsigned char smem[];
-    OP *Qs = reinterpret_cast<OP *>(smem + L::q_off);
-    OP *Ks = reinterpret_cast<OP *>(smem + L::k_off);
-    in_t *Vs = reinterpret_cast<in_t *>(smem + L::v_off);
-    OP *Ms = reinterpret_cast<OP *>(smem + L::m_off);
-    OP *Ps = reinterpret_cast<OP *>(smem + L::p_off);
-    float *gam_s = reinterpret_cast<float *>(smem + L::g_off);   // gamma_r, then kappa_r
-    float *kap_s = gam_s + C;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)smem;       // LDS address of smem
 
     if (meta[1] != 0) return;
     const int bid = blockIdx.x, xcd = bid & 7, slot = bid >> 3;
@@ -486,142 +514,155 @@ __global__ __launch_bounds__(64 * NW) void chunk_state_kernel(
     if (chain >= NH) return;
     const int n = chain / H, h = chain % H;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, nn = l & 15, jj = l >> 4;
+    // Waves 0..NW-1 compute (16 value columns each); waves NW..2NW-1 stage the
+    // next chunk's inputs into LDS.  The hardware places one wave of each
+    // role on every SIMD.
+    const bool stager = w >= NW;
+    const int sw = w - NW, stid = tid - NT;  // stager wave / thread index
     const int vb = vt * BV;                 // first value column of the block
-    const int v0 = vb + w * 16;             // first value column of this wave
-    const bool active = v0 < DV;
+    const int v0 = vb + w * 16;             // first value column of a compute wave
+    const bool active = !stager && v0 < DV;
     const int tok0 = cu_ws[n];
     const int len_seq = cu_ws[n + 1] - tok0;
     const int r0 = row0[n];
     const int nchunks = (len_seq + C - 1) / C;
 
-    // Per-lane LDS offsets (elements) of the operand reads.
-    const int row_lane = nn * PQ + 4 * jj;                        // row-fragment reads of Q, K
-    const int trk_lane = (4 * jj + (nn >> 2)) * PQ + 4 * (nn & 3);  // transposed K reads
-    const int plk_lane = 4 * jj * PQ + nn;                          // fp32 direct column reads of K
-    const int trv_lane = (4 * jj + (nn >> 2)) * PV + 4 * (nn & 3) + 16 * w;
-    const int plv_lane = 4 * jj * PV + nn + 16 * w;
-    const int tile_lane = 4 * l;                                  // M / P tiles in fragment order
-
-    // S^T tiles: sT[mt][i] = S[v0 + nn][16 mt + 4 jj + i].
-    float4_t sT[KT];
-    const int64_t st_base = ((int64_t)chain * DV + v0 + nn) * DK + 4 * jj;
+    // ---- per-lane LDS byte offsets ----
+    const int frag_lane = nn * QROW + 8 * jj * OPB;                 // Q / K row fragments
+    int kt_lane;                                                    // K^T fragments
+    if constexpr (OPB == 2)
+        kt_lane = (4 * jj + (nn >> 2)) * QROW + 16 * (nn & 3);
+    else
+        kt_lane = 4 * jj * QROW + 4 * (8 * (nn >> 2) + (nn & 3));
+    int v_lane[4];                                                  // V in accumulator layout
+    if constexpr (sizeof(in_t) == 2) {
+        const int row = 4 * jj + (nn >> 2), unit = 2 * w + ((nn & 3) >> 1);
+        v_lane[0] = row * VROW + 16 * (unit ^ (row & L::VSWZ)) + 8 * (nn & 1);
+        v_lane[1] = v_lane[2] = v_lane[3] = v_lane[0];
+    } else {
+        const int unit = 4 * w + (nn >> 2);
 #pragma unroll
-    for (int mt = 0; mt < KT; ++mt) {
+        for (int i = 0; i < 4; ++i) {
+            const int row = 4 * jj + i;
+            v_lane[i] = row * VROW + 16 * (unit ^ (row & L::VSWZ)) + 4 * (nn & 3);
+        }
+    }
+    const int tile_lane = 4 * l;                                    // M / P tiles (elements)
+
+    // S^T tiles in the dk order described above.
+    float4_t sT[KT];
+    const int64_t st_base = ((int64_t)chain * DV + v0 + nn) * DK + 8 * jj;
+#pragma unroll
+    for (int t = 0; t < KT; ++t) {
+        const int off = 32 * (t >> 1) + 4 * (t & 1);
         if (active && init_state)
-            sT[mt] = *reinterpret_cast<const float4_t *>(init_state + st_base + 16 * mt);
+            sT[t] = *reinterpret_cast<const float4_t *>(init_state + st_base + off);
         else
-            sT[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
+            sT[t] = float4_t{0.f, 0.f, 0.f, 0.f};
     }
 
-    // ---- register prefetch of one chunk's inputs ----
+    // ---- Q / K register prefetch (one chunk ahead) ----
     // Loads use the chunk's first row as a uniform base plus 32-bit per-lane
-    // offsets, and are unconditional: in a partial chunk the rows past the end
-    // re-read the last valid row and are zeroed when committed to LDS.  The
-    // prefetched registers are not touched until the commit after the next
-    // barrier, so the loads stay in flight during the chunk's compute.
-    Raw8<in_t> pq[QK_IT], pk[QK_IT], pv[V_IT];
-    u32x4_t pm[MP_IT], pp[MP_IT];
-    float pg[G_IT];
-    const int rowq = H * DK, rowv = H * DV;   // element stride between tokens
-    // Loop-invariant per-thread element offsets inside a chunk (row r, 8 columns).
-    int offq[QK_IT], offv[V_IT];
+    // offsets; in a partial chunk the rows past the end re-read the last
+    // valid row and are zeroed when committed to LDS.
+    Raw8<in_t> pq[QK_IT], pk[QK_IT];
+    const int rowq = H * DK;   // element stride between tokens
+    int offq[QK_IT];
 #pragma unroll
     for (int it = 0; it < QK_IT; ++it) {
-        const int u = (tid + it * NT) % QK_UNITS;
+        const int u = (stid + it * NT) % QK_UNITS;
         offq[it] = (u / (DK / 8)) * rowq + (u % (DK / 8)) * 8;
     }
-#pragma unroll
-    for (int it = 0; it < V_IT; ++it) {
-        const int u = (tid + it * NT) % V_UNITS;
-        offv[it] = (u / (BV / 8)) * rowv + (u % (BV / 8)) * 8;
-    }
-    const bool v_cols_ok = vb + ((tid % (BV / 8)) * 8) < DV;   // same for every it (NT % (BV/8) == 0)
-    auto prefetch = [&](int ci) {
-        const int64_t rh = (int64_t)(r0 + ci) * H + h;
+    auto prefetch_qk = [&](int ci) {
         const int64_t tb = (int64_t)(tok0 + ci * C) * H + h;
         const int last = min(C, len_seq - ci * C) - 1;
         const in_t *qc = q + tb * DK;
         const in_t *kc = k + tb * DK;
-        const in_t *vc = v + tb * DV + vb;
         if (last == C - 1) {
 #pragma unroll
             for (int it = 0; it < QK_IT; ++it) {
                 pq[it].load(qc + offq[it]);
                 pk[it].load(kc + offq[it]);
             }
-            if (v_cols_ok) {
-#pragma unroll
-                for (int it = 0; it < V_IT; ++it) pv[it].load(vc + offv[it]);
-            }
         } else {
-            // partial chunk: rows past the end re-read the last valid row
 #pragma unroll
             for (int it = 0; it < QK_IT; ++it) {
-                const int u = (tid + it * NT) % QK_UNITS;
+                const int u = (stid + it * NT) % QK_UNITS;
                 const int off = min(u / (DK / 8), last) * rowq + (u % (DK / 8)) * 8;
                 pq[it].load(qc + off);
                 pk[it].load(kc + off);
             }
-            if (v_cols_ok) {
-#pragma unroll
-                for (int it = 0; it < V_IT; ++it) {
-                    const int u = (tid + it * NT) % V_UNITS;
-                    pv[it].load(vc + min(u / (BV / 8), last) * rowv + (u % (BV / 8)) * 8);
-                }
-            }
         }
-        const OP *mc = ws_m + rh * kTriTiles * kTileElems;
-        const OP *pc = ws_p + rh * kTriTiles * kTileElems;
-#pragma unroll
-        for (int it = 0; it < MP_IT; ++it) {
-            const int idx = min(tid + it * NT, MP_N - 1);
-            pm[it] = *reinterpret_cast<const u32x4_t *>(mc + idx * MP_VEC);
-            pp[it] = *reinterpret_cast<const u32x4_t *>(pc + idx * MP_VEC);
-        }
-#pragma unroll
-        for (int it = 0; it < G_IT; ++it) pg[it] = ws_g[rh * 2 * C + min(tid + it * NT, 2 * C - 1)];
     };
-    auto commit = [&](int len) {
-        const bool full = len == C;
+    auto commit_qk = [&](int b, int len) {
+        OP *Qb = reinterpret_cast<OP *>(smem + L::qk_off(b));
+        OP *Kb = reinterpret_cast<OP *>(smem + L::qk_off(b) + L::QK);
 #pragma unroll
         for (int it = 0; it < QK_IT; ++it) {
-            const int u = tid + it * NT;
+            const int u = stid + it * NT;
             if (u >= QK_UNITS) continue;
             const int r = u / (DK / 8), c8 = (u % (DK / 8)) * 8;
-            if (!full && r >= len) {
+            if (len < C && r >= len) {
                 pq[it].zero();
                 pk[it].zero();
             }
             frag lo, hi;
             to_op(pq[it], lo, hi);
-            *reinterpret_cast<frag *>(Qs + r * PQ + c8) = lo;
-            *reinterpret_cast<frag *>(Qs + r * PQ + c8 + 4) = hi;
+            store_row8(Qb + r * (QROW / OPB) + c8, lo, hi);
             to_op(pk[it], lo, hi);
-            *reinterpret_cast<frag *>(Ks + r * PQ + c8) = lo;
-            *reinterpret_cast<frag *>(Ks + r * PQ + c8 + 4) = hi;
+            store_row8(Kb + r * (QROW / OPB) + c8, lo, hi);
         }
-        if (v_cols_ok) {
+    };
+    // ---- direct global -> LDS copies of V, M, P and the decay factors ----
+    // Copy ii of a chunk (stager wave sw issues ii = sw, sw + NW, ...) fills LDS bytes
+    // [1024 ii, 1024 ii + 1024) of the chunk's buffer: V blocks first, then
+    // M, P and the 2C decay factors.  Per-lane source offsets do not depend
+    // on the chunk and are computed once.  Rows past the end of a partial
+    // chunk re-read the last valid row: M and P are exactly zero in those
+    // rows and columns, so they stay inert.
+    constexpr int KD = (L::NDMA + NW - 1) / NW;
+    int dsrc[KD];   // V: elements from the chunk's first row; M, P, g: bytes
 #pragma unroll
-            for (int it = 0; it < V_IT; ++it) {
-                const int u = tid + it * NT;
-                if (u >= V_UNITS) continue;
-                const int r = u / (BV / 8), c8 = (u % (BV / 8)) * 8;
-                if (!full && r >= len) pv[it].zero();
-                pv[it].store_lds(Vs + r * PV + c8);
+    for (int kx = 0; kx < KD; ++kx) {
+        const int ii = sw + NW * kx;
+        if (ii < L::NV) {
+            const int byte = ii * 1024 + 16 * l;
+            const int row = byte / VROW, unit = (byte % VROW) / 16;
+            int col = vb + (unit ^ (row & L::VSWZ)) * (16 / (int)sizeof(in_t));
+            if (col >= DV) col = vb;                     // columns of inactive waves
+            dsrc[kx] = row * H * DV + col;
+        } else if (ii < L::NV + 2 * L::NM) {
+            dsrc[kx] = ((ii - L::NV) % L::NM) * 1024 + 16 * l;
+        } else {
+            dsrc[kx] = 16 * min(l, 2 * C / 4 - 1);
+        }
+    }
+    auto dma = [&](int ci, int b) {
+        const int64_t rh = (int64_t)(r0 + ci) * H + h;
+        const int len = min(C, len_seq - ci * C);
+        const uint32_t base = lds0 + (uint32_t)L::dma_off(b);
+        const in_t *vc = v + ((int64_t)(tok0 + ci * C) * H + h) * DV;
+        const unsigned char *mc = reinterpret_cast<const unsigned char *>(ws_m + rh * kTriTiles * kTileElems);
+        const unsigned char *pc = reinterpret_cast<const unsigned char *>(ws_p + rh * kTriTiles * kTileElems);
+        const unsigned char *gc = reinterpret_cast<const unsigned char *>(ws_g + rh * 2 * C);
+#pragma unroll
+        for (int kx = 0; kx < KD; ++kx) {
+            const int ii = sw + NW * kx;
+            if (ii >= L::NDMA) break;
+            if (ii < L::NV) {
+                int off = dsrc[kx];
+                if (len < C) {
+                    const int row = (ii * 1024 + 16 * l) / VROW;
+                    if (row >= len) off -= (row - (len - 1)) * H * DV;
+                }
+                dma16(vc + off, base + (uint32_t)(ii * 1024));
+            } else if (ii < L::NV + L::NM) {
+                dma16(mc + dsrc[kx], base + (uint32_t)(L::m_rel + (ii - L::NV) * 1024));
+            } else if (ii < L::NV + 2 * L::NM) {
+                dma16(pc + dsrc[kx], base + (uint32_t)(L::p_rel + (ii - L::NV - L::NM) * 1024));
+            } else {
+                dma16(gc + dsrc[kx], base + (uint32_t)L::g_rel);
             }
-        }
-#pragma unroll
-        for (int it = 0; it < MP_IT; ++it) {
-            const int idx = tid + it * NT;
-            if (idx < MP_N) {
-                *reinterpret_cast<u32x4_t *>(Ms + idx * MP_VEC) = pm[it];
-                *reinterpret_cast<u32x4_t *>(Ps + idx * MP_VEC) = pp[it];
-            }
-        }
-#pragma unroll
-        for (int it = 0; it < G_IT; ++it) {
-            const int idx = tid + it * NT;
-            if (idx < 2 * C) gam_s[idx] = pg[it];
         }
     };
 
@@ -630,46 +671,87 @@ __global__ __launch_bounds__(64 * NW) void chunk_state_kernel(
     {
         float acc = 0.f;
 #pragma unroll
-        for (int mt = 0; mt < KT; ++mt) acc += sT[mt][0];
+        for (int t = 0; t < KT; ++t) acc += sT[t][0];
         __builtin_amdgcn_s_waitcnt(0);
         asm volatile("" ::"v"(acc));
     }
 
-    if (nchunks > 0) prefetch(0);
+    // Outputs of a chunk are stored at the start of the next one, after the
+    // barrier, so the wait before that barrier (which also covers stores)
+    // never waits on stores issued just before it.
+    float4_t oq[4];
+    int pend_t0 = -1, pend_len = 0;
+    auto store_o = [&]() {
+        const int64_t obase = ((int64_t)pend_t0 * H + h) * DV + v0 + 4 * jj + (int64_t)nn * H * DV;
+        const int64_t ostep = (int64_t)16 * H * DV;
+        if (pend_len == C) {
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) store_out4(o, obase + rt * ostep, odt, oq[rt]);
+        } else {
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+                if (16 * rt + nn < pend_len) store_out4(o, obase + rt * ostep, odt, oq[rt]);
+        }
+    };
+
+    if (stager && nchunks > 0) {
+        prefetch_qk(0);
+        dma(0, 0);
+        commit_qk(0, min(C, len_seq));
+        if (QKB == 2 && nchunks > 1) prefetch_qk(1);
+    }
     for (int ci = 0; ci < nchunks; ++ci) {
         const int t0 = tok0 + ci * C;
         const int len = min(C, len_seq - ci * C);
-        __syncthreads();             // previous chunk's LDS reads are done
-        commit(len);
+        const int b = ci & 1;
+        // Everything a wave issued for this chunk has landed (direct loads,
+        // Q/K registers, the previous outputs); after the barrier the
+        // staged chunk is visible and every wave is done with chunk ci-1's
+        // buffers.
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        if (ci + 1 < nchunks) prefetch(ci + 1);
+        if constexpr (QKB == 1) {
+            // single Q/K buffer: chunk ci's Q/K is committed here, after the
+            // compute waves finished reading chunk ci-1's.
+            if (stager && ci > 0) commit_qk(0, len);
+            __syncthreads();
+        }
+        if (stager) {
+            if (ci + 1 < nchunks) {
+                dma(ci + 1, b ^ 1);
+                if constexpr (QKB == 2) {
+                    commit_qk(b ^ 1, min(C, len_seq - (ci + 1) * C));
+                    if (ci + 2 < nchunks) prefetch_qk(ci + 2);
+                } else {
+                    prefetch_qk(ci + 1);
+                }
+            }
+            continue;
+        }
+        if (active && pend_t0 >= 0) store_o();
         if (!active) continue;
 
-        using F2 = Frag2<OP>;
-        constexpr int KP = KT / 2;                       // k-tile pairs along dk
+        const unsigned char *Qb = smem + L::qk_off(QKB == 2 ? b : 0);
+        const unsigned char *Kb = Qb + L::QK;
+        const unsigned char *Db = smem + L::dma_off(b);
+        const OP *Ms = reinterpret_cast<const OP *>(Db + L::m_rel);
+        const OP *Ps = reinterpret_cast<const OP *>(Db + L::p_rel);
+        const float *gam_s = reinterpret_cast<const float *>(Db + L::g_rel);   // gamma_r, then kappa_r
+        const float *kap_s = gam_s + C;
+
         // S as an operand: B of K S^T and A of S Q^T use the same fragment.
         F2 sB[KP];
 #pragma unroll
         for (int p = 0; p < KP; ++p) sB[p] = F2::cvt(sT[2 * p], sT[2 * p + 1]);
 
-        // X_K = K S^T; the K fragments of row tile mt+1 are read while tile
-        // mt's products run.
+        // X_K = K S^T
         float4_t x[4];
-        {
-            F2 kf[2][KP];
-            auto load_k = [&](F2 (&kd)[KP], int mt) {
-                const OP *ks = Ks + 16 * mt * PQ + row_lane;
 #pragma unroll
-                for (int p = 0; p < KP; ++p) kd[p] = F2::make(lds_frag(ks + 32 * p), lds_frag(ks + 32 * p + 16));
-            };
-            load_k(kf[0], 0);
+        for (int mt = 0; mt < 4; ++mt) {
+            x[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
+            const OP *kr = reinterpret_cast<const OP *>(Kb + 16 * mt * QROW + frag_lane);
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                if (mt < 3) load_k(kf[(mt + 1) & 1], mt + 1);
-                x[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int p = 0; p < KP; ++p) mma2(x[mt], kf[mt & 1][p], sB[p]);
-            }
+            for (int p = 0; p < KP; ++p) mma2(x[mt], row_frag2(kr + 32 * p), sB[p]);
         }
 
         // Y = V - diag(gamma) X_K as B operand (pairs of row tiles).
@@ -678,7 +760,7 @@ __global__ __launch_bounds__(64 * NW) void chunk_state_kernel(
             float4_t y[4];
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
-                const float4_t vv = ColFrag<in_t>::read_f32(Vs + 16 * mt * PV, trv_lane, plv_lane, PV);
+                const float4_t vv = VFrag<in_t>::read(Db + 16 * mt * VROW, v_lane);
                 const float4_t gm = *reinterpret_cast<const float4_t *>(gam_s + 16 * mt + 4 * jj);
                 y[mt] = vv - gm * x[mt];
             }
@@ -690,24 +772,16 @@ __global__ __launch_bounds__(64 * NW) void chunk_state_kernel(
         // pair 0 = tiles (0,1), pair 1 = tiles (2,3); missing tiles are zero.
         auto tri_pair = [&](const OP *T, int mt, int p) {
             const int k0 = 2 * p, k1 = 2 * p + 1;
-            const typename M::frag lo = k0 <= mt ? lds_frag(T + tri_index(mt, k0) * kTileElems + tile_lane) : M::zero();
-            const typename M::frag hi = k1 <= mt ? lds_frag(T + tri_index(mt, k1) * kTileElems + tile_lane) : M::zero();
+            const frag lo = k0 <= mt ? lds_frag(T + tri_index(mt, k0) * kTileElems + tile_lane) : M::zero();
+            const frag hi = k1 <= mt ? lds_frag(T + tri_index(mt, k1) * kTileElems + tile_lane) : M::zero();
             return F2::make(lo, hi);
         };
         float4_t Vp[4];
-        {
-            F2 mf[4][2];
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                mf[mt][0] = tri_pair(Ms, mt, 0);
-                if (mt >= 2) mf[mt][1] = tri_pair(Ms, mt, 1);
-            }
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                Vp[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
-                mma2(Vp[mt], mf[mt][0], yB[0]);
-                if (mt >= 2) mma2(Vp[mt], mf[mt][1], yB[1]);
-            }
+        for (int mt = 0; mt < 4; ++mt) {
+            Vp[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
+            mma2(Vp[mt], tri_pair(Ms, mt, 0), yB[0]);
+            if (mt >= 2) mma2(Vp[mt], tri_pair(Ms, mt, 1), yB[1]);
         }
         F2 vB[2], dB[2];
         {
@@ -723,59 +797,45 @@ __global__ __launch_bounds__(64 * NW) void chunk_state_kernel(
             dB[1] = F2::cvt(d[2], d[3]);
         }
 
-        // State update S^T <- gamma_C S^T + K^T (kappa o V') (K^T fragments by
-        // transposed reads), interleaved with the output tiles
-        // O^T = (S Q^T) diag(gamma) + V'^T P^T, which only need the S
-        // fragments taken before the update.
-        auto load_kt = [&](F2 (&kd)[2], int mt) {
-#pragma unroll
-            for (int p = 0; p < 2; ++p)
-                kd[p] = F2::make(kt_frag<OP>(Ks + 32 * p * PQ + 16 * mt, trk_lane, plk_lane, PQ),
-                                 kt_frag<OP>(Ks + (32 * p + 16) * PQ + 16 * mt, trk_lane, plk_lane, PQ));
-        };
+        // State update S^T <- gamma_C S^T + K^T (kappa o V'), interleaved with
+        // the output tiles O^T = (S Q^T) diag(gamma) + V'^T P^T, which use the
+        // S fragments taken before the update.  State tile t = 2p + hs covers
+        // dk 32p + 8j + 4hs + i; its K^T rows come from K columns
+        // 32p + 8 (n/4) + 4hs + n%4.
         const float gC = gam_s[C - 1];
-        float4_t oq[4];
-        F2 ktf[2][2];
-        load_kt(ktf[0], 0);
-        constexpr int NSTEP = KT > 4 ? KT : 4;           // dk row tiles and output row tiles
+        constexpr int NSTEP = KT > 4 ? KT : 4;           // state tiles and output row tiles
 #pragma unroll
-        for (int mt = 0; mt < NSTEP; ++mt) {
-            if (mt < KT) {
-                if (mt + 1 < KT) load_kt(ktf[(mt + 1) & 1], mt + 1);
-                sT[mt] *= gC;
-                mma2(sT[mt], ktf[mt & 1][0], dB[0]);
-                mma2(sT[mt], ktf[mt & 1][1], dB[1]);
+        for (int st = 0; st < NSTEP; ++st) {
+            if (st < KT) {
+                const int p = st >> 1, hs = st & 1;
+                const unsigned char *kt = Kb + kt_lane + (OPB == 2 ? 2 * (32 * p + 4 * hs) : 4 * (32 * p + 4 * hs));
+                F2 a0 = F2::make(kt_frag(kt, QROW, (OP *)nullptr), kt_frag(kt + 16 * QROW, QROW, (OP *)nullptr));
+                F2 a1 = F2::make(kt_frag(kt + 32 * QROW, QROW, (OP *)nullptr),
+                                 kt_frag(kt + 48 * QROW, QROW, (OP *)nullptr));
+                sT[st] *= gC;
+                mma2(sT[st], a0, dB[0]);
+                mma2(sT[st], a1, dB[1]);
             }
-            if (mt < 4) {
-                const int rt = mt;
-                const OP *qs = Qs + 16 * rt * PQ + row_lane;
+            if (st < 4) {
+                const int rt = st;
+                const OP *qr = reinterpret_cast<const OP *>(Qb + 16 * rt * QROW + frag_lane);
                 oq[rt] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int p = 0; p < KP; ++p)
-                    mma2(oq[rt], sB[p], F2::make(lds_frag(qs + 32 * p), lds_frag(qs + 32 * p + 16)));
+                for (int p = 0; p < KP; ++p) mma2(oq[rt], sB[p], row_frag2(qr + 32 * p));
                 oq[rt] *= gam_s[16 * rt + nn];
                 mma2(oq[rt], vB[0], tri_pair(Ps, rt, 0));
                 if (rt >= 2) mma2(oq[rt], vB[1], tri_pair(Ps, rt, 1));
             }
         }
-        {
-            const int64_t obase = ((int64_t)t0 * H + h) * DV + v0 + 4 * jj + (int64_t)nn * H * DV;
-            const int64_t ostep = (int64_t)16 * H * DV;
-            if (len == C) {
-#pragma unroll
-                for (int rt = 0; rt < 4; ++rt) store_out4(o, obase + rt * ostep, odt, oq[rt]);
-            } else {
-#pragma unroll
-                for (int rt = 0; rt < 4; ++rt)
-                    if (16 * rt + nn < len) store_out4(o, obase + rt * ostep, odt, oq[rt]);
-            }
-        }
+        pend_t0 = t0;
+        pend_len = len;
     }
+    if (active && pend_t0 >= 0) store_o();
 
     if (active && final_state) {
 #pragma unroll
-        for (int mt = 0; mt < KT; ++mt)
-            *reinterpret_cast<float4_t *>(final_state + st_base + 16 * mt) = sT[mt];
+        for (int t = 0; t < KT; ++t)
+            *reinterpret_cast<float4_t *>(final_state + st_base + 32 * (t >> 1) + 4 * (t & 1)) = sT[t];
     }
 }
 
@@ -803,14 +863,20 @@ ChunkWorkspace chunk_workspace_layout(int32_t B, int32_t T, int32_t N, bool pack
     return w;
 }
 
-static int state_waves_per_block(int DV) {
+// Compute waves per state-pass block (the block has as many staging waves).
+// With 4 + 4 waves two waves share each SIMD, which leaves 256 registers per
+// lane; the largest heads (dk = 256, or fp32 dk = 128) need more and use
+// 2 + 2.  GDN_STATE_WAVES (1, 2 or 4) lowers the count for experiments.
+static int state_waves_per_block(int DV, int DK, int in_dtype) {
+    const int cap = (DK >= 256 || (in_dtype == DT_FP32 && DK >= 128)) ? 2 : 4;
+    const int tiles = (DV + 15) / 16;
+    int nw = tiles >= 4 ? 4 : (tiles >= 2 ? 2 : 1);
     const char *env = getenv("GDN_STATE_WAVES");
     if (env) {
         const int x = atoi(env);
-        if (x == 1 || x == 2 || x == 4) return x;
+        if (x == 1 || x == 2 || x == 4) nw = x;
     }
-    const int tiles = (DV + 15) / 16;
-    return tiles >= 4 ? 4 : (tiles >= 2 ? 2 : 1);
+    return nw < cap ? nw : cap;
 }
 
 template <typename K>
@@ -831,7 +897,7 @@ static hipError_t launch_state(const ChunkArgs &a, const ChunkWorkspace &w, hipS
     const int nvt = ((a.dv + 15) / 16 + NW - 1) / NW;
     const int64_t blocks = ((NH + 7) / 8) * 8 * nvt;
     ProfScope prof("gdn_chunk_state", st);
-    kern<<<dim3((unsigned)blocks), dim3(64 * NW), L::bytes, st>>>(
+    kern<<<dim3((unsigned)blocks), dim3(128 * NW), L::bytes, st>>>(
         (int)NH, a.H, a.dv, nvt, a.out_dtype, reinterpret_cast<const int32_t *>(ws + w.off_meta),
         reinterpret_cast<const int32_t *>(ws + w.off_cu), reinterpret_cast<const int32_t *>(ws + w.off_row0),
         static_cast<const in_t *>(a.q), static_cast<const in_t *>(a.k), static_cast<const in_t *>(a.v),
@@ -860,7 +926,7 @@ static hipError_t launch_dk(const ChunkArgs &a, const ChunkWorkspace &w, hipStre
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    switch (state_waves_per_block(a.dv)) {
+    switch (state_waves_per_block(a.dv, DK, a.in_dtype)) {
     case 4: return launch_state<in_t, OP, DK, 4>(a, w, st);
     case 2: return launch_state<in_t, OP, DK, 2>(a, w, st);
     default: return launch_state<in_t, OP, DK, 1>(a, w, st);
