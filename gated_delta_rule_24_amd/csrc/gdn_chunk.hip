@@ -388,6 +388,9 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(int H, const int32_t *_
 // chunk needs one barrier; otherwise a second barrier separates their
 // commit from the reads.
 // ============================================================================
+// Waves of a state-pass block that stage inputs (the others compute).
+constexpr int kStagers = 4;
+
 template <typename in_t, typename OP, int DK, int NW>
 struct StateSmem {
     static constexpr int BV = 16 * NW;                                  // value columns per block
@@ -488,7 +491,7 @@ __device__ __forceinline__ void dma16(const void *g, uint32_t lds) {
 }
 
 template <typename in_t, typename OP, int DK, int NW>
-__global__ __launch_bounds__(128 * NW) void chunk_state_kernel(
+__global__ __launch_bounds__(64 * (NW + kStagers)) void chunk_state_kernel(
     int NH, int H, int DV, int nvt, int odt, const int32_t *__restrict__ meta,
     const int32_t *__restrict__ cu_ws, const int32_t *__restrict__ row0,
     const in_t *__restrict__ q, const in_t *__restrict__ k, const in_t *__restrict__ v,
@@ -499,7 +502,7 @@ __global__ __launch_bounds__(128 * NW) void chunk_state_kernel(
     using F2 = Frag2<OP>;
     using L = StateSmem<in_t, OP, DK, NW>;
     constexpr int QROW = L::QROW, VROW = L::VROW, BV = L::BV, QKB = L::QKB;
-    constexpr int NT = 64 * NW;                              // threads per role
+    constexpr int NT = 64 * kStagers;                        // staging threads
     constexpr int KT = DK / 16;                              // state tiles along dk
     constexpr int KP = DK / 32;                              // k-tile pairs along dk
     constexpr int QK_UNITS = C * (DK / 8);                   // 8-element pieces of Q (and K)
@@ -514,11 +517,10 @@ __global__ __launch_bounds__(128 * NW) void chunk_state_kernel(
     if (chain >= NH) return;
     const int n = chain / H, h = chain % H;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, nn = l & 15, jj = l >> 4;
-    // Waves 0..NW-1 compute (16 value columns each); waves NW..2NW-1 stage the
-    // next chunk's inputs into LDS.  The hardware places one wave of each
-    // role on every SIMD.
+    // Waves 0..NW-1 compute (16 value columns each); the kStagers waves after
+    // them stage the next chunk's inputs into LDS.
     const bool stager = w >= NW;
-    const int sw = w - NW, stid = tid - NT;  // stager wave / thread index
+    const int sw = w - NW, stid = tid - 64 * NW;  // stager wave / thread index
     const int vb = vt * BV;                 // first value column of the block
     const int v0 = vb + w * 16;             // first value column of a compute wave
     const bool active = !stager && v0 < DV;
@@ -561,11 +563,16 @@ __global__ __launch_bounds__(128 * NW) void chunk_state_kernel(
             sT[t] = float4_t{0.f, 0.f, 0.f, 0.f};
     }
 
-    // ---- Q / K register prefetch (one chunk ahead) ----
+    // ---- Q / K register prefetch ----
+    // Two register sets: the loads for one chunk are issued before the other
+    // set is converted and committed, so they have a whole chunk to land.
     // Loads use the chunk's first row as a uniform base plus 32-bit per-lane
     // offsets; in a partial chunk the rows past the end re-read the last
     // valid row and are zeroed when committed to LDS.
-    Raw8<in_t> pq[QK_IT], pk[QK_IT];
+    struct QKRegs {
+        Raw8<in_t> q[QK_IT], k[QK_IT];
+    };
+    QKRegs RA, RB;
     const int rowq = H * DK;   // element stride between tokens
     int offq[QK_IT];
 #pragma unroll
@@ -573,7 +580,7 @@ __global__ __launch_bounds__(128 * NW) void chunk_state_kernel(
         const int u = (stid + it * NT) % QK_UNITS;
         offq[it] = (u / (DK / 8)) * rowq + (u % (DK / 8)) * 8;
     }
-    auto prefetch_qk = [&](int ci) {
+    auto prefetch_qk = [&](int ci, QKRegs &R) {
         const int64_t tb = (int64_t)(tok0 + ci * C) * H + h;
         const int last = min(C, len_seq - ci * C) - 1;
         const in_t *qc = q + tb * DK;
@@ -581,20 +588,20 @@ __global__ __launch_bounds__(128 * NW) void chunk_state_kernel(
         if (last == C - 1) {
 #pragma unroll
             for (int it = 0; it < QK_IT; ++it) {
-                pq[it].load(qc + offq[it]);
-                pk[it].load(kc + offq[it]);
+                R.q[it].load(qc + offq[it]);
+                R.k[it].load(kc + offq[it]);
             }
         } else {
 #pragma unroll
             for (int it = 0; it < QK_IT; ++it) {
                 const int u = (stid + it * NT) % QK_UNITS;
                 const int off = min(u / (DK / 8), last) * rowq + (u % (DK / 8)) * 8;
-                pq[it].load(qc + off);
-                pk[it].load(kc + off);
+                R.q[it].load(qc + off);
+                R.k[it].load(kc + off);
             }
         }
     };
-    auto commit_qk = [&](int b, int len) {
+    auto commit_qk = [&](int b, int len, QKRegs &R) {
         OP *Qb = reinterpret_cast<OP *>(smem + L::qk_off(b));
         OP *Kb = reinterpret_cast<OP *>(smem + L::qk_off(b) + L::QK);
 #pragma unroll
@@ -603,28 +610,28 @@ __global__ __launch_bounds__(128 * NW) void chunk_state_kernel(
             if (u >= QK_UNITS) continue;
             const int r = u / (DK / 8), c8 = (u % (DK / 8)) * 8;
             if (len < C && r >= len) {
-                pq[it].zero();
-                pk[it].zero();
+                R.q[it].zero();
+                R.k[it].zero();
             }
             frag lo, hi;
-            to_op(pq[it], lo, hi);
+            to_op(R.q[it], lo, hi);
             store_row8(Qb + r * (QROW / OPB) + c8, lo, hi);
-            to_op(pk[it], lo, hi);
+            to_op(R.k[it], lo, hi);
             store_row8(Kb + r * (QROW / OPB) + c8, lo, hi);
         }
     };
     // ---- direct global -> LDS copies of V, M, P and the decay factors ----
-    // Copy ii of a chunk (stager wave sw issues ii = sw, sw + NW, ...) fills LDS bytes
+    // Copy ii of a chunk (stager wave sw issues ii = sw, sw + kStagers, ...) fills LDS bytes
     // [1024 ii, 1024 ii + 1024) of the chunk's buffer: V blocks first, then
     // M, P and the 2C decay factors.  Per-lane source offsets do not depend
     // on the chunk and are computed once.  Rows past the end of a partial
     // chunk re-read the last valid row: M and P are exactly zero in those
     // rows and columns, so they stay inert.
-    constexpr int KD = (L::NDMA + NW - 1) / NW;
+    constexpr int KD = (L::NDMA + kStagers - 1) / kStagers;
     int dsrc[KD];   // V: elements from the chunk's first row; M, P, g: bytes
 #pragma unroll
     for (int kx = 0; kx < KD; ++kx) {
-        const int ii = sw + NW * kx;
+        const int ii = sw + kStagers * kx;
         if (ii < L::NV) {
             const int byte = ii * 1024 + 16 * l;
             const int row = byte / VROW, unit = (byte % VROW) / 16;
@@ -647,7 +654,7 @@ __global__ __launch_bounds__(128 * NW) void chunk_state_kernel(
         const unsigned char *gc = reinterpret_cast<const unsigned char *>(ws_g + rh * 2 * C);
 #pragma unroll
         for (int kx = 0; kx < KD; ++kx) {
-            const int ii = sw + NW * kx;
+            const int ii = sw + kStagers * kx;
             if (ii >= L::NDMA) break;
             if (ii < L::NV) {
                 int off = dsrc[kx];
@@ -694,42 +701,46 @@ __global__ __launch_bounds__(128 * NW) void chunk_state_kernel(
         }
     };
 
-    if (stager && nchunks > 0) {
-        prefetch_qk(0);
-        dma(0, 0);
-        commit_qk(0, min(C, len_seq));
-        if (QKB == 2 && nchunks > 1) prefetch_qk(1);
-    }
-    for (int ci = 0; ci < nchunks; ++ci) {
-        const int t0 = tok0 + ci * C;
-        const int len = min(C, len_seq - ci * C);
+    // The two roles run separate loops with the same barriers: one per chunk
+    // (two with a single Q/K buffer).  Before each barrier a wave waits for
+    // everything it issued for that chunk (direct loads, Q/K registers,
+    // outputs); after it the staged chunk is visible and every wave is done
+    // with chunk ci-1's buffers.
+    //
+    // Stager step ci (QKB == 2): with chunk ci+1 held in `cur`, load chunk
+    // ci+2 into `nxt`, copy chunk ci+1's V, M, P and decay factors, then
+    // commit chunk ci+1's Q and K.  With a single Q/K buffer (QKB == 1)
+    // chunk ci is committed between the two barriers instead.
+    auto stage = [&](int ci, QKRegs &cur, QKRegs &nxt) {
         const int b = ci & 1;
-        // Everything a wave issued for this chunk has landed (direct loads,
-        // Q/K registers, the previous outputs); after the barrier the
-        // staged chunk is visible and every wave is done with chunk ci-1's
-        // buffers.
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         if constexpr (QKB == 1) {
-            // single Q/K buffer: chunk ci's Q/K is committed here, after the
-            // compute waves finished reading chunk ci-1's.
-            if (stager && ci > 0) commit_qk(0, len);
+            if (ci > 0) commit_qk(0, min(C, len_seq - ci * C), cur);
             __syncthreads();
         }
-        if (stager) {
+        if constexpr (QKB == 2) {
+            if (ci + 2 < nchunks) prefetch_qk(ci + 2, nxt);
             if (ci + 1 < nchunks) {
                 dma(ci + 1, b ^ 1);
-                if constexpr (QKB == 2) {
-                    commit_qk(b ^ 1, min(C, len_seq - (ci + 1) * C));
-                    if (ci + 2 < nchunks) prefetch_qk(ci + 2);
-                } else {
-                    prefetch_qk(ci + 1);
-                }
+                commit_qk(b ^ 1, min(C, len_seq - (ci + 1) * C), cur);
             }
-            continue;
+        } else {
+            if (ci + 1 < nchunks) {
+                prefetch_qk(ci + 1, nxt);
+                dma(ci + 1, b ^ 1);
+            }
         }
-        if (active && pend_t0 >= 0) store_o();
-        if (!active) continue;
+    };
+    // Compute step ci.
+    auto compute = [&](int ci) {
+        const int t0 = tok0 + ci * C;
+        const int len = min(C, len_seq - ci * C);
+        const int b = ci & 1;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if constexpr (QKB == 1) __syncthreads();
+        if (!active) return;
 
         const unsigned char *Qb = smem + L::qk_off(QKB == 2 ? b : 0);
         const unsigned char *Kb = Qb + L::QK;
@@ -753,6 +764,8 @@ __global__ __launch_bounds__(128 * NW) void chunk_state_kernel(
 #pragma unroll
             for (int p = 0; p < KP; ++p) mma2(x[mt], row_frag2(kr + 32 * p), sB[p]);
         }
+        // The previous chunk's outputs leave while these products run.
+        if (pend_t0 >= 0) store_o();
 
         // Y = V - diag(gamma) X_K as B operand (pairs of row tiles).
         F2 yB[2];
@@ -829,7 +842,29 @@ __global__ __launch_bounds__(128 * NW) void chunk_state_kernel(
         }
         pend_t0 = t0;
         pend_len = len;
+    };
+
+    if (stager) {
+        if (nchunks > 0) {
+            prefetch_qk(0, RA);
+            dma(0, 0);
+            commit_qk(0, min(C, len_seq), RA);
+            if (QKB == 2 && nchunks > 1) prefetch_qk(1, RB);
+        }
+        // Register sets alternate: with QKB == 2, chunk ci+1 sits in RB for
+        // even ci and in RA for odd ci; with QKB == 1, chunk ci does.
+        for (int ci = 0; ci < nchunks; ci += 2) {
+            if constexpr (QKB == 2) {
+                stage(ci, RB, RA);
+                if (ci + 1 < nchunks) stage(ci + 1, RA, RB);
+            } else {
+                stage(ci, RA, RB);
+                if (ci + 1 < nchunks) stage(ci + 1, RB, RA);
+            }
+        }
+        return;
     }
+    for (int ci = 0; ci < nchunks; ++ci) compute(ci);
     if (active && pend_t0 >= 0) store_o();
 
     if (active && final_state) {
@@ -863,20 +898,18 @@ ChunkWorkspace chunk_workspace_layout(int32_t B, int32_t T, int32_t N, bool pack
     return w;
 }
 
-// Compute waves per state-pass block (the block has as many staging waves).
-// With 4 + 4 waves two waves share each SIMD, which leaves 256 registers per
-// lane; the largest heads (dk = 256, or fp32 dk = 128) need more and use
-// 2 + 2.  GDN_STATE_WAVES (1, 2 or 4) lowers the count for experiments.
-static int state_waves_per_block(int DV, int DK, int in_dtype) {
-    const int cap = (DK >= 256 || (in_dtype == DT_FP32 && DK >= 128)) ? 2 : 4;
+// Compute waves per state-pass block (16 value columns each; the block also
+// has kStagers staging waves).  GDN_STATE_WAVES (1, 2 or 4) lowers the count
+// for experiments.
+static int state_waves_per_block(int DV) {
     const int tiles = (DV + 15) / 16;
     int nw = tiles >= 4 ? 4 : (tiles >= 2 ? 2 : 1);
     const char *env = getenv("GDN_STATE_WAVES");
     if (env) {
         const int x = atoi(env);
-        if (x == 1 || x == 2 || x == 4) nw = x;
+        if ((x == 1 || x == 2 || x == 4) && x < nw) nw = x;
     }
-    return nw < cap ? nw : cap;
+    return nw;
 }
 
 template <typename K>
@@ -897,7 +930,7 @@ static hipError_t launch_state(const ChunkArgs &a, const ChunkWorkspace &w, hipS
     const int nvt = ((a.dv + 15) / 16 + NW - 1) / NW;
     const int64_t blocks = ((NH + 7) / 8) * 8 * nvt;
     ProfScope prof("gdn_chunk_state", st);
-    kern<<<dim3((unsigned)blocks), dim3(128 * NW), L::bytes, st>>>(
+    kern<<<dim3((unsigned)blocks), dim3(64 * (NW + kStagers)), L::bytes, st>>>(
         (int)NH, a.H, a.dv, nvt, a.out_dtype, reinterpret_cast<const int32_t *>(ws + w.off_meta),
         reinterpret_cast<const int32_t *>(ws + w.off_cu), reinterpret_cast<const int32_t *>(ws + w.off_row0),
         static_cast<const in_t *>(a.q), static_cast<const in_t *>(a.k), static_cast<const in_t *>(a.v),
@@ -926,7 +959,7 @@ static hipError_t launch_dk(const ChunkArgs &a, const ChunkWorkspace &w, hipStre
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    switch (state_waves_per_block(a.dv, DK, a.in_dtype)) {
+    switch (state_waves_per_block(a.dv)) {
     case 4: return launch_state<in_t, OP, DK, 4>(a, w, st);
     case 2: return launch_state<in_t, OP, DK, 2>(a, w, st);
     default: return launch_state<in_t, OP, DK, 1>(a, w, st);
