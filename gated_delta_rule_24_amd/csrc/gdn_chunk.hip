@@ -683,48 +683,45 @@ __global__ __launch_bounds__(64 * (NW + kStagers)) void chunk_state_kernel(
         asm volatile("" ::"v"(acc));
     }
 
-    // Outputs of a chunk are stored at the start of the next one, after the
-    // barrier, so the wait before that barrier (which also covers stores)
-    // never waits on stores issued just before it.
     float4_t oq[4];
-    int pend_t0 = -1, pend_len = 0;
-    auto store_o = [&]() {
-        const int64_t obase = ((int64_t)pend_t0 * H + h) * DV + v0 + 4 * jj + (int64_t)nn * H * DV;
+    auto store_o = [&](int t0, int len) {
+        const int64_t obase = ((int64_t)t0 * H + h) * DV + v0 + 4 * jj + (int64_t)nn * H * DV;
         const int64_t ostep = (int64_t)16 * H * DV;
-        if (pend_len == C) {
+        if (len == C) {
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) store_out4(o, obase + rt * ostep, odt, oq[rt]);
         } else {
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt)
-                if (16 * rt + nn < pend_len) store_out4(o, obase + rt * ostep, odt, oq[rt]);
+                if (16 * rt + nn < len) store_out4(o, obase + rt * ostep, odt, oq[rt]);
         }
     };
 
     // The two roles run separate loops with the same barriers: one per chunk
-    // (two with a single Q/K buffer).  Before each barrier a wave waits for
-    // everything it issued for that chunk (direct loads, Q/K registers,
-    // outputs); after it the staged chunk is visible and every wave is done
-    // with chunk ci-1's buffers.
+    // (two with a single Q/K buffer).  Before a barrier a stager waits for
+    // its direct loads, Q/K register loads and LDS writes; a compute wave
+    // waits only for its LDS reads, never for its output stores, which drain
+    // in the background.  After the barrier the staged chunk is visible and
+    // every wave is done with chunk ci-1's buffers.  The barriers are written
+    // out (rather than __syncthreads) so that no wait for outstanding global
+    // stores is attached to them.
     //
-    // Stager step ci (QKB == 2): with chunk ci+1 held in `cur`, load chunk
-    // ci+2 into `nxt`, copy chunk ci+1's V, M, P and decay factors, then
-    // commit chunk ci+1's Q and K.  With a single Q/K buffer (QKB == 1)
-    // chunk ci is committed between the two barriers instead.
+    // Stager step ci (QKB == 2): commit chunk ci+1's Q and K (held in `cur`)
+    // first, then load chunk ci+2 into `nxt` and copy chunk ci+1's V, M, P
+    // and decay factors.  Committing first means no wait on the loads just
+    // issued; they have the rest of the chunk to land.  With a single Q/K
+    // buffer (QKB == 1) chunk ci is committed between the two barriers.
     auto stage = [&](int ci, QKRegs &cur, QKRegs &nxt) {
         const int b = ci & 1;
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
         if constexpr (QKB == 1) {
             if (ci > 0) commit_qk(0, min(C, len_seq - ci * C), cur);
-            __syncthreads();
+            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
         }
         if constexpr (QKB == 2) {
+            if (ci + 1 < nchunks) commit_qk(b ^ 1, min(C, len_seq - (ci + 1) * C), cur);
             if (ci + 2 < nchunks) prefetch_qk(ci + 2, nxt);
-            if (ci + 1 < nchunks) {
-                dma(ci + 1, b ^ 1);
-                commit_qk(b ^ 1, min(C, len_seq - (ci + 1) * C), cur);
-            }
+            if (ci + 1 < nchunks) dma(ci + 1, b ^ 1);
         } else {
             if (ci + 1 < nchunks) {
                 prefetch_qk(ci + 1, nxt);
@@ -737,9 +734,8 @@ __global__ __launch_bounds__(64 * (NW + kStagers)) void chunk_state_kernel(
         const int t0 = tok0 + ci * C;
         const int len = min(C, len_seq - ci * C);
         const int b = ci & 1;
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        if constexpr (QKB == 1) __syncthreads();
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        if constexpr (QKB == 1) asm volatile("s_barrier" ::: "memory");
         if (!active) return;
 
         const unsigned char *Qb = smem + L::qk_off(QKB == 2 ? b : 0);
@@ -754,6 +750,10 @@ __global__ __launch_bounds__(64 * (NW + kStagers)) void chunk_state_kernel(
         F2 sB[KP];
 #pragma unroll
         for (int p = 0; p < KP; ++p) sB[p] = F2::cvt(sT[2 * p], sT[2 * p + 1]);
+        // The decay of the carried state; the update adds K^T (kappa o V') later.
+        const float gC = gam_s[C - 1];
+#pragma unroll
+        for (int t = 0; t < KT; ++t) sT[t] *= gC;
 
         // X_K = K S^T
         float4_t x[4];
@@ -764,9 +764,6 @@ __global__ __launch_bounds__(64 * (NW + kStagers)) void chunk_state_kernel(
 #pragma unroll
             for (int p = 0; p < KP; ++p) mma2(x[mt], row_frag2(kr + 32 * p), sB[p]);
         }
-        // The previous chunk's outputs leave while these products run.
-        if (pend_t0 >= 0) store_o();
-
         // Y = V - diag(gamma) X_K as B operand (pairs of row tiles).
         F2 yB[2];
         {
@@ -815,7 +812,6 @@ __global__ __launch_bounds__(64 * (NW + kStagers)) void chunk_state_kernel(
         // S fragments taken before the update.  State tile t = 2p + hs covers
         // dk 32p + 8j + 4hs + i; its K^T rows come from K columns
         // 32p + 8 (n/4) + 4hs + n%4.
-        const float gC = gam_s[C - 1];
         constexpr int NSTEP = KT > 4 ? KT : 4;           // state tiles and output row tiles
 #pragma unroll
         for (int st = 0; st < NSTEP; ++st) {
@@ -825,7 +821,6 @@ __global__ __launch_bounds__(64 * (NW + kStagers)) void chunk_state_kernel(
                 F2 a0 = F2::make(kt_frag(kt, QROW, (OP *)nullptr), kt_frag(kt + 16 * QROW, QROW, (OP *)nullptr));
                 F2 a1 = F2::make(kt_frag(kt + 32 * QROW, QROW, (OP *)nullptr),
                                  kt_frag(kt + 48 * QROW, QROW, (OP *)nullptr));
-                sT[st] *= gC;
                 mma2(sT[st], a0, dB[0]);
                 mma2(sT[st], a1, dB[1]);
             }
@@ -840,8 +835,7 @@ __global__ __launch_bounds__(64 * (NW + kStagers)) void chunk_state_kernel(
                 if (rt >= 2) mma2(oq[rt], vB[1], tri_pair(Ps, rt, 1));
             }
         }
-        pend_t0 = t0;
-        pend_len = len;
+        store_o(t0, len);
     };
 
     if (stager) {
@@ -865,7 +859,6 @@ __global__ __launch_bounds__(64 * (NW + kStagers)) void chunk_state_kernel(
         return;
     }
     for (int ci = 0; ci < nchunks; ++ci) compute(ci);
-    if (active && pend_t0 >= 0) store_o();
 
     if (active && final_state) {
 #pragma unroll
