@@ -710,11 +710,12 @@ __global__ __launch_bounds__(64 * (NW + kStagers)) void chunk_state_kernel(
     // out (rather than __syncthreads) so that no wait for outstanding global
     // stores is attached to them.
     //
-    // Stager step ci (QKB == 2): commit chunk ci+1's Q and K (held in `cur`)
-    // first, then load chunk ci+2 into `nxt` and copy chunk ci+1's V, M, P
-    // and decay factors.  Committing first means no wait on the loads just
-    // issued; they have the rest of the chunk to land.  With a single Q/K
-    // buffer (QKB == 1) chunk ci is committed between the two barriers.
+    // Stager step ci (QKB == 2): load chunk ci+2's Q and K into `nxt` and
+    // copy chunk ci+1's V, M, P and decay factors first, so the loads have
+    // the whole chunk to land, then commit chunk ci+1's Q and K from `cur`
+    // (complete since the barrier's wait; `touch` keeps the compiler from
+    // waiting again behind the new loads).  With a single Q/K buffer
+    // (QKB == 1) chunk ci is committed between the two barriers.
     auto stage = [&](int ci, QKRegs &cur, QKRegs &nxt) {
         const int b = ci & 1;
         asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -723,14 +724,26 @@ __global__ __launch_bounds__(64 * (NW + kStagers)) void chunk_state_kernel(
             asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
         }
         if constexpr (QKB == 2) {
-            if (ci + 1 < nchunks) commit_qk(b ^ 1, min(C, len_seq - (ci + 1) * C), cur);
-            if (ci + 2 < nchunks) prefetch_qk(ci + 2, nxt);
-            if (ci + 1 < nchunks) dma(ci + 1, b ^ 1);
-        } else {
-            if (ci + 1 < nchunks) {
-                prefetch_qk(ci + 1, nxt);
-                dma(ci + 1, b ^ 1);
+#pragma unroll
+            for (int it = 0; it < QK_IT; ++it) {
+                cur.q[it].touch();
+                cur.k[it].touch();
             }
+            // (near the end the last chunk is loaded again: the register
+            // sets are then written on every path, which keeps them in place)
+            prefetch_qk(min(ci + 2, nchunks - 1), nxt);
+            if (ci + 1 < nchunks) {
+                dma(ci + 1, b ^ 1);
+                commit_qk(b ^ 1, min(C, len_seq - (ci + 1) * C), cur);
+            }
+        } else {
+#pragma unroll
+            for (int it = 0; it < QK_IT; ++it) {
+                cur.q[it].touch();
+                cur.k[it].touch();
+            }
+            prefetch_qk(min(ci + 1, nchunks - 1), nxt);
+            if (ci + 1 < nchunks) dma(ci + 1, b ^ 1);
         }
     };
     // Compute step ci.
@@ -750,95 +763,160 @@ __global__ __launch_bounds__(64 * (NW + kStagers)) void chunk_state_kernel(
         const float *gam_s = reinterpret_cast<const float *>(Db + L::g_rel);   // gamma_r, then kappa_r
         const float *kap_s = gam_s + C;
 
-        // S as an operand: B of K S^T and A of S Q^T use the same fragment.
-        F2 sB[KP];
-#pragma unroll
-        for (int p = 0; p < KP; ++p) sB[p] = F2::cvt(sT[2 * p], sT[2 * p + 1]);
-        // The decay of the carried state; the update adds K^T (kappa o V') later.
-        const float gC = gam_s[C - 1];
-#pragma unroll
-        for (int t = 0; t < KT; ++t) sT[t] *= gC;
-
-        // X_K = K S^T
-        float4_t x[4];
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-            x[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
-            const OP *kr = reinterpret_cast<const OP *>(Kb + 16 * mt * QROW + frag_lane);
-#pragma unroll
-            for (int p = 0; p < KP; ++p) mma2(x[mt], row_frag2(kr + 32 * p), sB[p]);
-        }
-        // Y = V - diag(gamma) X_K as B operand (pairs of row tiles).
-        F2 yB[2];
-        {
-            float4_t y[4];
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                const float4_t vv = VFrag<in_t>::read(Db + 16 * mt * VROW, v_lane);
-                const float4_t gm = *reinterpret_cast<const float4_t *>(gam_s + 16 * mt + 4 * jj);
-                y[mt] = vv - gm * x[mt];
-            }
-            yB[0] = F2::cvt(y[0], y[1]);
-            yB[1] = F2::cvt(y[2], y[3]);
-        }
-
-        // V' = M Y  (M lower triangular).  Row tile mt uses k-tiles 0..mt:
-        // pair 0 = tiles (0,1), pair 1 = tiles (2,3); missing tiles are zero.
+        // The chunk is software-pipelined: each phase issues the LDS reads of
+        // a later phase before its own products, and the phases are pinned
+        // in order (scheduling barriers), so read latency hides behind
+        // matrix-core and vector work.  Row-fragment item i of K or Q is
+        // (k-tile pair i / 4, row tile i % 4); consecutive products of a phase
+        // go to different accumulators.
+        constexpr int NX = 4 * KP;                      // K (and Q) row fragments
+        constexpr int FR = 4 * OPB / 2;                 // registers per fragment pair
+        constexpr int RB = KT > 8 ? 32 : 64;            // registers for read-ahead fragments
+        constexpr int WX = NX < RB / FR ? NX : RB / FR; // K fragments held at once
+        constexpr int WQ = NX / 2 < RB / 2 / FR ? NX / 2 : RB / 2 / FR;   // Q fragments held at once
+        auto rd_row = [&](const unsigned char *blk, int i) {
+            return row_frag2(reinterpret_cast<const OP *>(blk + 16 * (i % 4) * QROW + frag_lane) + 32 * (i / 4));
+        };
+        // V' = M Y and V'^T P^T use the lower-triangular tiles of M and P as
+        // k-tile pairs: row tile mt takes pair 0 (tiles (mt,0),(mt,1)) and,
+        // for mt >= 2, pair 1 (tiles (mt,2),(mt,3)); absent tiles are zero.
         auto tri_pair = [&](const OP *T, int mt, int p) {
             const int k0 = 2 * p, k1 = 2 * p + 1;
             const frag lo = k0 <= mt ? lds_frag(T + tri_index(mt, k0) * kTileElems + tile_lane) : M::zero();
             const frag hi = k1 <= mt ? lds_frag(T + tri_index(mt, k1) * kTileElems + tile_lane) : M::zero();
             return F2::make(lo, hi);
         };
-        float4_t Vp[4];
+        // pair j of the six: (mt, p) = (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
+        constexpr int PMT[6] = {0, 1, 2, 2, 3, 3}, PP[6] = {0, 0, 0, 1, 0, 1};
+        // K^T fragments of state tile t = 2p + hs (dk 32p + 8j + 4hs + i) for
+        // token pair tp: K columns 32p + 8 (n/4) + 4hs + n%4.
+        auto rd_kt = [&](int t, int tp) {
+            const int p = t >> 1, hs = t & 1;
+            const unsigned char *kt = Kb + kt_lane + OPB * (32 * p + 4 * hs) + 32 * tp * QROW;
+            return F2::make(kt_frag(kt, QROW, (OP *)nullptr), kt_frag(kt + 16 * QROW, QROW, (OP *)nullptr));
+        };
+
+        // -- phase 0: K fragments, V, gamma; S as an operand; decay of S --
+        F2 kf[WX];
+#pragma unroll
+        for (int i = 0; i < WX; ++i) kf[i] = rd_row(Kb, i);
+        float4_t vv[4], gm[4];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
-            Vp[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
-            mma2(Vp[mt], tri_pair(Ms, mt, 0), yB[0]);
-            if (mt >= 2) mma2(Vp[mt], tri_pair(Ms, mt, 1), yB[1]);
+            vv[mt] = VFrag<in_t>::read(Db + 16 * mt * VROW, v_lane);
+            gm[mt] = *reinterpret_cast<const float4_t *>(gam_s + 16 * mt + 4 * jj);
         }
+        const float gC = gam_s[C - 1];
+        F2 sB[KP];            // B of K S^T and A of S Q^T
+#pragma unroll
+        for (int p = 0; p < KP; ++p) sB[p] = F2::cvt(sT[2 * p], sT[2 * p + 1]);
+#pragma unroll
+        for (int t = 0; t < KT; ++t) sT[t] *= gC;   // the update adds K^T (kappa o V') later
+        __builtin_amdgcn_sched_barrier(0);
+
+        // -- phase 1: X_K = K S^T; reads of M and the first Q fragments --
+        float4_t x[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) x[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < NX; ++i) {
+            mma2(x[i % 4], kf[i % WX], sB[i / 4]);
+            if (i + WX < NX) kf[i % WX] = rd_row(Kb, i + WX);
+        }
+        F2 mpair[6];
+#pragma unroll
+        for (int jx = 0; jx < 6; ++jx) mpair[jx] = tri_pair(Ms, PMT[jx], PP[jx]);
+        constexpr int NQ1 = NX / 2;                     // Q S^T items before the update
+        F2 qf[WQ];
+#pragma unroll
+        for (int i = 0; i < WQ; ++i) qf[i] = rd_row(Qb, i);
+        __builtin_amdgcn_sched_barrier(0);
+
+        // -- phase 2: Y = V - diag(gamma) X_K as B operand --
+        F2 yB[2];
+        {
+            float4_t y[4];
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) y[mt] = vv[mt] - gm[mt] * x[mt];
+            yB[0] = F2::cvt(y[0], y[1]);
+            yB[1] = F2::cvt(y[2], y[3]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+
+        // -- phase 3: V' = M Y; reads of kappa and the first K^T fragments --
+        float4_t Vp[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) Vp[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int jx = 0; jx < 6; ++jx) mma2(Vp[PMT[jx]], mpair[jx], yB[PP[jx]]);
+        float4_t kp4[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) kp4[mt] = *reinterpret_cast<const float4_t *>(kap_s + 16 * mt + 4 * jj);
+        constexpr int NT1 = KT < RB / 4 / FR ? KT : RB / 4 / FR;   // K^T tiles read ahead
+        F2 ka[KT][2];
+#pragma unroll
+        for (int t = 0; t < NT1; ++t) {
+            ka[t][0] = rd_kt(t, 0);
+            ka[t][1] = rd_kt(t, 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+
+        // -- phase 4: the first half of Q S^T (independent of the chain) --
+        float4_t qs[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) qs[rt] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < NQ1; ++i) {
+            mma2(qs[i % 4], sB[i / 4], qf[i % WQ]);
+            if (i + WQ < NX) qf[i % WQ] = rd_row(Qb, i + WQ);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+
+        // -- phase 5: kappa o V' and the operand forms of V' --
         F2 vB[2], dB[2];
         {
             float4_t d[4];
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                const float4_t kp = *reinterpret_cast<const float4_t *>(kap_s + 16 * mt + 4 * jj);
-                d[mt] = kp * Vp[mt];
-            }
+            for (int mt = 0; mt < 4; ++mt) d[mt] = kp4[mt] * Vp[mt];
             vB[0] = F2::cvt(Vp[0], Vp[1]);
             vB[1] = F2::cvt(Vp[2], Vp[3]);
             dB[0] = F2::cvt(d[0], d[1]);
             dB[1] = F2::cvt(d[2], d[3]);
         }
+        __builtin_amdgcn_sched_barrier(0);
 
-        // State update S^T <- gamma_C S^T + K^T (kappa o V'), interleaved with
-        // the output tiles O^T = (S Q^T) diag(gamma) + V'^T P^T, which use the
-        // S fragments taken before the update.  State tile t = 2p + hs covers
-        // dk 32p + 8j + 4hs + i; its K^T rows come from K columns
-        // 32p + 8 (n/4) + 4hs + n%4.
-        constexpr int NSTEP = KT > 4 ? KT : 4;           // state tiles and output row tiles
+        // -- phase 6: state update, K^T fragments read NT1 tiles ahead --
 #pragma unroll
-        for (int st = 0; st < NSTEP; ++st) {
-            if (st < KT) {
-                const int p = st >> 1, hs = st & 1;
-                const unsigned char *kt = Kb + kt_lane + (OPB == 2 ? 2 * (32 * p + 4 * hs) : 4 * (32 * p + 4 * hs));
-                F2 a0 = F2::make(kt_frag(kt, QROW, (OP *)nullptr), kt_frag(kt + 16 * QROW, QROW, (OP *)nullptr));
-                F2 a1 = F2::make(kt_frag(kt + 32 * QROW, QROW, (OP *)nullptr),
-                                 kt_frag(kt + 48 * QROW, QROW, (OP *)nullptr));
-                mma2(sT[st], a0, dB[0]);
-                mma2(sT[st], a1, dB[1]);
+        for (int t = 0; t < KT; ++t) {
+            if (t + NT1 < KT) {
+                ka[t + NT1][0] = rd_kt(t + NT1, 0);
+                ka[t + NT1][1] = rd_kt(t + NT1, 1);
             }
-            if (st < 4) {
-                const int rt = st;
-                const OP *qr = reinterpret_cast<const OP *>(Qb + 16 * rt * QROW + frag_lane);
-                oq[rt] = float4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int p = 0; p < KP; ++p) mma2(oq[rt], sB[p], row_frag2(qr + 32 * p));
-                oq[rt] *= gam_s[16 * rt + nn];
-                mma2(oq[rt], vB[0], tri_pair(Ps, rt, 0));
-                if (rt >= 2) mma2(oq[rt], vB[1], tri_pair(Ps, rt, 1));
-            }
+            mma2(sT[t], ka[t][0], dB[0]);
+            mma2(sT[t], ka[t][1], dB[1]);
         }
+        F2 ppair[6];
+#pragma unroll
+        for (int jx = 0; jx < 6; ++jx) ppair[jx] = tri_pair(Ps, PMT[jx], PP[jx]);
+        float g1[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) g1[rt] = gam_s[16 * rt + nn];
+        __builtin_amdgcn_sched_barrier(0);
+
+        // -- phase 7: rest of Q S^T, then V'^T P^T into a separate sum --
+#pragma unroll
+        for (int i = NQ1; i < NX; ++i) {
+            mma2(qs[i % 4], sB[i / 4], qf[i % WQ]);
+            if (i + WQ < NX) qf[i % WQ] = rd_row(Qb, i + WQ);
+        }
+        float4_t pv[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) pv[rt] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int jx = 0; jx < 6; ++jx) mma2(pv[PMT[jx]], vB[PP[jx]], ppair[jx]);
+        // O^T = (S Q^T) diag(gamma) + V'^T P^T
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) oq[rt] = qs[rt] * g1[rt] + pv[rt];
         store_o(t0, len);
     };
 
@@ -850,15 +928,23 @@ __global__ __launch_bounds__(64 * (NW + kStagers)) void chunk_state_kernel(
             if (QKB == 2 && nchunks > 1) prefetch_qk(1, RB);
         }
         // Register sets alternate: with QKB == 2, chunk ci+1 sits in RB for
-        // even ci and in RA for odd ci; with QKB == 1, chunk ci does.
-        for (int ci = 0; ci < nchunks; ci += 2) {
+        // even ci and in RA for odd ci; with QKB == 1, chunk ci does.  Steps
+        // run in pairs so both sets are written on every path.
+        int ci = 0;
+        for (; ci + 1 < nchunks; ci += 2) {
             if constexpr (QKB == 2) {
                 stage(ci, RB, RA);
-                if (ci + 1 < nchunks) stage(ci + 1, RA, RB);
+                stage(ci + 1, RA, RB);
             } else {
                 stage(ci, RA, RB);
-                if (ci + 1 < nchunks) stage(ci + 1, RB, RA);
+                stage(ci + 1, RB, RA);
             }
+        }
+        if (ci < nchunks) {
+            if constexpr (QKB == 2)
+                stage(ci, RB, RA);
+            else
+                stage(ci, RA, RB);
         }
         return;
     }

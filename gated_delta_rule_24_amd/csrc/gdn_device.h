@@ -178,6 +178,11 @@ __device__ __forceinline__ void load8_f32(const bf16_t *p, float (&o)[8]) {
 }
 
 // ---- 8 consecutive input elements held as raw bits (for register prefetch) -------
+// touch(): an empty asm that takes the registers as input and output.  Called
+// right after a point where the loads filling them are known to be complete
+// (an explicit wait for all vector memory), it makes the compiler treat the
+// value as produced there, so it does not wait again, behind loads issued
+// later, before the registers' first use.
 
 template <typename in_t>
 struct Raw8;
@@ -186,6 +191,8 @@ template <>
 struct Raw8<bf16_t> {
     uint4 x;
     __device__ __forceinline__ void load(const bf16_t *p) { x = *reinterpret_cast<const uint4 *>(p); }
+    // Re-issues the value as produced here (see Raw8 notes).
+    __device__ __forceinline__ void touch() { asm volatile("" : "+v"(x.x), "+v"(x.y), "+v"(x.z), "+v"(x.w)); }
     __device__ __forceinline__ void zero() { x = make_uint4(0u, 0u, 0u, 0u); }
     __device__ __forceinline__ void store_lds(bf16_t *p) const { *reinterpret_cast<uint4 *>(p) = x; }
     __device__ __forceinline__ static void store_zero_lds(bf16_t *p) { *reinterpret_cast<uint4 *>(p) = make_uint4(0u, 0u, 0u, 0u); }
@@ -210,6 +217,7 @@ template <>
 struct Raw8<_Float16> {
     uint4 x;
     __device__ __forceinline__ void load(const _Float16 *p) { x = *reinterpret_cast<const uint4 *>(p); }
+    __device__ __forceinline__ void touch() { asm volatile("" : "+v"(x.x), "+v"(x.y), "+v"(x.z), "+v"(x.w)); }
     __device__ __forceinline__ void zero() { x = make_uint4(0u, 0u, 0u, 0u); }
     __device__ __forceinline__ void store_lds(_Float16 *p) const { *reinterpret_cast<uint4 *>(p) = x; }
     __device__ __forceinline__ static void store_zero_lds(_Float16 *p) { *reinterpret_cast<uint4 *>(p) = make_uint4(0u, 0u, 0u, 0u); }
@@ -233,6 +241,10 @@ struct Raw8<float> {
         x[1] = *reinterpret_cast<const uint4 *>(p + 4);
     }
     __device__ __forceinline__ void zero() { x[0] = x[1] = make_uint4(0u, 0u, 0u, 0u); }
+    __device__ __forceinline__ void touch() {
+        asm volatile("" : "+v"(x[0].x), "+v"(x[0].y), "+v"(x[0].z), "+v"(x[0].w));
+        asm volatile("" : "+v"(x[1].x), "+v"(x[1].y), "+v"(x[1].z), "+v"(x[1].w));
+    }
     __device__ __forceinline__ void store_lds(float *p) const {
         reinterpret_cast<uint4 *>(p)[0] = x[0];
         reinterpret_cast<uint4 *>(p)[1] = x[1];
