@@ -414,23 +414,6 @@ struct StateSmem {
     static_assert(QROW % 16 == 0 && VROW % 16 == 0, "16-byte rows");
 };
 
-// Four fp32 values to an output row (one 8- or 16-byte store).  Outputs are
-// written once and not read again here, so the stores are non-temporal:
-// they do not wait behind cache allocation (measured: about 20% of the state
-// pass at the prefill shape).
-__device__ __forceinline__ void store_out4(void *o, int64_t idx, int odt, float4_t v) {
-    if (odt == DT_FP32) {
-        __builtin_nontemporal_store(v, reinterpret_cast<float4_t *>(static_cast<float *>(o) + idx));
-    } else if (odt == DT_BF16) {
-        const uint32_t a = from_f32<bf16_t>(v[0]).bits | ((uint32_t)from_f32<bf16_t>(v[1]).bits << 16);
-        const uint32_t b = from_f32<bf16_t>(v[2]).bits | ((uint32_t)from_f32<bf16_t>(v[3]).bits << 16);
-        typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-        __builtin_nontemporal_store(u32x2_t{a, b}, reinterpret_cast<u32x2_t *>(static_cast<bf16_t *>(o) + idx));
-    } else {
-        __builtin_nontemporal_store(half4_t{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]},
-                                    reinterpret_cast<half4_t *>(static_cast<_Float16 *>(o) + idx));
-    }
-}
 
 // Eight consecutive operand values of one LDS row: a k-tile pair fragment.
 __device__ __forceinline__ Frag2<_Float16> row_frag2(const _Float16 *p) {
@@ -449,31 +432,42 @@ __device__ __forceinline__ void store_row8(float *p, float4_t lo, float4_t hi) {
 }
 
 // V in accumulator layout: V[R + i][c] for lane (c = c0 + n, R = row0 + 4 j),
-// i < 4, as fp32.  16-bit V uses one transposed read at the lane's address
-// `a`; fp32 V reads the four rows at the four lane addresses a[0..3].
+// i < 4.  16-bit V uses one transposed read at the lane's address `a`; fp32
+// V reads the four rows at the four lane addresses a[0..3].  read() returns
+// the raw bits, to_f32() converts them, so the conversion (which waits for
+// the read) can sit later than the read.
 template <typename T>
 struct VFrag;
 template <>
 struct VFrag<bf16_t> {
-    __device__ __forceinline__ static float4_t read(const unsigned char *base, const int (&a)[4]) {
-        const uint2 r = lds_read_tr16(base + a[0]);
+    using raw = uint2;
+    __device__ __forceinline__ static raw read(const unsigned char *base, const int (&a)[4]) {
+        return lds_read_tr16(base + a[0]);
+    }
+    __device__ __forceinline__ static float4_t to_f32(raw r) {
         return float4_t{__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xffff0000u),
                         __uint_as_float(r.y << 16), __uint_as_float(r.y & 0xffff0000u)};
     }
 };
 template <>
 struct VFrag<_Float16> {
-    __device__ __forceinline__ static float4_t read(const unsigned char *base, const int (&a)[4]) {
-        const half4_t h = __builtin_bit_cast(half4_t, lds_read_tr16(base + a[0]));
+    using raw = uint2;
+    __device__ __forceinline__ static raw read(const unsigned char *base, const int (&a)[4]) {
+        return lds_read_tr16(base + a[0]);
+    }
+    __device__ __forceinline__ static float4_t to_f32(raw r) {
+        const half4_t h = __builtin_bit_cast(half4_t, r);
         return float4_t{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
     }
 };
 template <>
 struct VFrag<float> {
-    __device__ __forceinline__ static float4_t read(const unsigned char *base, const int (&a)[4]) {
+    using raw = float4_t;
+    __device__ __forceinline__ static raw read(const unsigned char *base, const int (&a)[4]) {
         return float4_t{*reinterpret_cast<const float *>(base + a[0]), *reinterpret_cast<const float *>(base + a[1]),
                         *reinterpret_cast<const float *>(base + a[2]), *reinterpret_cast<const float *>(base + a[3])};
     }
+    __device__ __forceinline__ static float4_t to_f32(raw r) { return r; }
 };
 
 // K^T operand fragment (rows = dk, k = tokens) of one k-tile: lane (n, j)
@@ -488,10 +482,23 @@ __device__ __forceinline__ float4_t kt_frag(const unsigned char *p, int qrow, fl
 }
 
 // One 1 KiB wave copy global -> LDS: lane l's 16 bytes at g land at lds + 16 l
-// (gfx950 direct load to LDS; the LDS base is wave-uniform).
+// (gfx950 direct load to LDS; the LDS base is wave-uniform and goes in M0).
+// Written as inline assembly so the compiler does not treat every later LDS
+// read as possibly depending on the copy: completion is awaited explicitly
+// (s_waitcnt vmcnt before the barriers).  M0 is saved and restored around
+// it, and one wait state separates the M0 write from the load.
 __device__ __forceinline__ void dma16(const void *g, uint32_t lds) {
-    __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void *)(uintptr_t)g,
-                                     (__attribute__((address_space(3))) void *)(uintptr_t)lds, 16, 0, 0);
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_nop 0\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds))
+        : "memory");
 }
 
 template <typename in_t, typename OP, int DK, int NW>
@@ -677,27 +684,47 @@ __global__ __launch_bounds__(64 * (NW + kStagers)) void chunk_state_kernel(
         }
     };
 
-    // Finish the initial-state loads before the first prefetch so no load of
-    // the loop is ever waited on together with them.
-    {
-        float acc = 0.f;
+    // Finish the initial-state loads here, and re-issue the state registers
+    // as produced after that wait, so no wait inside the loop is attached to
+    // these loads.
+    __builtin_amdgcn_s_waitcnt(0);
 #pragma unroll
-        for (int t = 0; t < KT; ++t) acc += sT[t][0];
-        __builtin_amdgcn_s_waitcnt(0);
-        asm volatile("" ::"v"(acc));
-    }
+    for (int t = 0; t < KT; ++t) asm volatile("" : "+v"(sT[t]));
 
-    float4_t oq[4];
+    // Output stores of the last chunk.  Their data and address registers are
+    // left untouched until the next chunk rewrites them (phase 7): reusing
+    // them earlier would make the next chunk wait for those stores to finish.
+    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+    float4_t oq[4] = {};        // output tiles, fp32 (the data of fp32 stores)
+    u32x2_t oh[4] = {};         // the same rounded to 16 bits and packed
+    uint64_t oa[4] = {};        // store addresses
+    auto keep_stores = [&]() {
+        asm volatile("" ::"v"(oq[0]), "v"(oq[1]), "v"(oq[2]), "v"(oq[3]), "v"(oh[0]), "v"(oh[1]), "v"(oh[2]),
+                     "v"(oh[3]), "v"(oa[0]), "v"(oa[1]), "v"(oa[2]), "v"(oa[3]));
+    };
+    const int osize = odt == DT_FP32 ? 4 : 2;
     auto store_o = [&](int t0, int len) {
         const int64_t obase = ((int64_t)t0 * H + h) * DV + v0 + 4 * jj + (int64_t)nn * H * DV;
         const int64_t ostep = (int64_t)16 * H * DV;
-        if (len == C) {
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt) store_out4(o, obase + rt * ostep, odt, oq[rt]);
-        } else {
+        for (int rt = 0; rt < 4; ++rt) {
+            oa[rt] = reinterpret_cast<uint64_t>(o) + (uint64_t)((obase + rt * ostep) * osize);
+            if (odt == DT_BF16) {
+                oh[rt] = u32x2_t{from_f32<bf16_t>(oq[rt][0]).bits | ((uint32_t)from_f32<bf16_t>(oq[rt][1]).bits << 16),
+                                 from_f32<bf16_t>(oq[rt][2]).bits | ((uint32_t)from_f32<bf16_t>(oq[rt][3]).bits << 16)};
+            } else if (odt == DT_FP16) {
+                oh[rt] = __builtin_bit_cast(u32x2_t, half4_t{(_Float16)oq[rt][0], (_Float16)oq[rt][1],
+                                                             (_Float16)oq[rt][2], (_Float16)oq[rt][3]});
+            }
+        }
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt)
-                if (16 * rt + nn < len) store_out4(o, obase + rt * ostep, odt, oq[rt]);
+        for (int rt = 0; rt < 4; ++rt) {
+            if (len == C || 16 * rt + nn < len) {
+                if (odt == DT_FP32)
+                    __builtin_nontemporal_store(oq[rt], reinterpret_cast<__attribute__((address_space(1))) float4_t *>(oa[rt]));
+                else
+                    __builtin_nontemporal_store(oh[rt], reinterpret_cast<__attribute__((address_space(1))) u32x2_t *>(oa[rt]));
+            }
         }
     };
 
@@ -786,8 +813,9 @@ __global__ __launch_bounds__(64 * (NW + kStagers)) void chunk_state_kernel(
             const frag hi = k1 <= mt ? lds_frag(T + tri_index(mt, k1) * kTileElems + tile_lane) : M::zero();
             return F2::make(lo, hi);
         };
-        // pair j of the six: (mt, p) = (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
-        constexpr int PMT[6] = {0, 1, 2, 2, 3, 3}, PP[6] = {0, 0, 0, 1, 0, 1};
+        // pair j of the six: (mt, p) = (0,0) (1,0) (2,0) (3,0) (2,1) (3,1), so
+        // products into one accumulator are never back to back
+        constexpr int PMT[6] = {0, 1, 2, 3, 2, 3}, PP[6] = {0, 0, 0, 0, 1, 1};
         // K^T fragments of state tile t = 2p + hs (dk 32p + 8j + 4hs + i) for
         // token pair tp: K columns 32p + 8 (n/4) + 4hs + n%4.
         auto rd_kt = [&](int t, int tp) {
@@ -796,17 +824,20 @@ __global__ __launch_bounds__(64 * (NW + kStagers)) void chunk_state_kernel(
             return F2::make(kt_frag(kt, QROW, (OP *)nullptr), kt_frag(kt + 16 * QROW, QROW, (OP *)nullptr));
         };
 
-        // -- phase 0: K fragments, V, gamma; S as an operand; decay of S --
+        // -- phase 0: K fragments, V, gamma; S as an operand; decay of S.
+        // LDS reads complete in order, so gamma_C is read first: the decay
+        // waits for it alone, not for the fragments behind it. --
+        const float gC = gam_s[C - 1];
         F2 kf[WX];
 #pragma unroll
         for (int i = 0; i < WX; ++i) kf[i] = rd_row(Kb, i);
-        float4_t vv[4], gm[4];
+        typename VFrag<in_t>::raw vraw[4];
+        float4_t gm[4];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
-            vv[mt] = VFrag<in_t>::read(Db + 16 * mt * VROW, v_lane);
+            vraw[mt] = VFrag<in_t>::read(Db + 16 * mt * VROW, v_lane);
             gm[mt] = *reinterpret_cast<const float4_t *>(gam_s + 16 * mt + 4 * jj);
         }
-        const float gC = gam_s[C - 1];
         F2 sB[KP];            // B of K S^T and A of S Q^T
 #pragma unroll
         for (int p = 0; p < KP; ++p) sB[p] = F2::cvt(sT[2 * p], sT[2 * p + 1]);
@@ -837,7 +868,7 @@ __global__ __launch_bounds__(64 * (NW + kStagers)) void chunk_state_kernel(
         {
             float4_t y[4];
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) y[mt] = vv[mt] - gm[mt] * x[mt];
+            for (int mt = 0; mt < 4; ++mt) y[mt] = VFrag<in_t>::to_f32(vraw[mt]) - gm[mt] * x[mt];
             yB[0] = F2::cvt(y[0], y[1]);
             yB[1] = F2::cvt(y[2], y[3]);
         }
@@ -885,15 +916,18 @@ __global__ __launch_bounds__(64 * (NW + kStagers)) void chunk_state_kernel(
         }
         __builtin_amdgcn_sched_barrier(0);
 
-        // -- phase 6: state update, K^T fragments read NT1 tiles ahead --
+        // -- phase 6: state update, K^T fragments read NT1 tiles ahead; the
+        // two products of a tile are NT1 apart, not back to back --
 #pragma unroll
-        for (int t = 0; t < KT; ++t) {
-            if (t + NT1 < KT) {
-                ka[t + NT1][0] = rd_kt(t + NT1, 0);
-                ka[t + NT1][1] = rd_kt(t + NT1, 1);
+        for (int t = 0; t < KT + NT1; ++t) {
+            if (t < KT) {
+                if (t + NT1 < KT) {
+                    ka[t + NT1][0] = rd_kt(t + NT1, 0);
+                    ka[t + NT1][1] = rd_kt(t + NT1, 1);
+                }
+                mma2(sT[t], ka[t][0], dB[0]);
             }
-            mma2(sT[t], ka[t][0], dB[0]);
-            mma2(sT[t], ka[t][1], dB[1]);
+            if (t >= NT1) mma2(sT[t - NT1], ka[t - NT1][1], dB[1]);
         }
         F2 ppair[6];
 #pragma unroll
@@ -915,6 +949,7 @@ __global__ __launch_bounds__(64 * (NW + kStagers)) void chunk_state_kernel(
 #pragma unroll
         for (int jx = 0; jx < 6; ++jx) mma2(pv[PMT[jx]], vB[PP[jx]], ppair[jx]);
         // O^T = (S Q^T) diag(gamma) + V'^T P^T
+        keep_stores();
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) oq[rt] = qs[rt] * g1[rt] + pv[rt];
         store_o(t0, len);
