@@ -163,16 +163,19 @@ __global__ __launch_bounds__(256) void chunk_table_kernel(int N, int T, int pack
 // ============================================================================
 template <typename OP, int DK>
 struct PrepSmem {
-    static constexpr int PQ = DK + 8 / (int)sizeof(OP);  // operand row pitch (elements)
-    static constexpr int PA = C + 4;                     // fp32 pitch of A and T
+    // Q and K rows padded by 32 bytes (conflict-free 16-byte row reads).
+    static constexpr int PQ = DK + 32 / (int)sizeof(OP);  // operand row pitch (elements)
+    static constexpr int PA = C + 4;                      // fp32 pitch of A and T
     static constexpr size_t q_off = 0;
     static constexpr size_t k_off = q_off + sizeof(OP) * C * PQ;
-    static constexpr size_t a_off = k_off + sizeof(OP) * C * PQ;
+    static constexpr size_t qk_end = k_off + sizeof(OP) * C * PQ;
     static constexpr size_t mat_bytes = sizeof(float) * C * PA;
-    // T reuses the Q/K region once the Gram tiles are done, when it fits.
-    static constexpr bool t_aliases = mat_bytes <= a_off;
-    static constexpr size_t t_off = t_aliases ? 0 : a_off + mat_bytes;
-    static constexpr size_t g_off = t_aliases ? a_off + mat_bytes : t_off + mat_bytes;
+    // A and T reuse the Q/K region once the Gram products are done, when
+    // both fit there (a smaller block lets more blocks share a CU).
+    static constexpr bool mats_alias = 2 * mat_bytes <= qk_end;
+    static constexpr size_t a_off = mats_alias ? 0 : qk_end;
+    static constexpr size_t t_off = a_off + mat_bytes;
+    static constexpr size_t g_off = mats_alias ? qk_end : t_off + mat_bytes;
     static constexpr size_t b_off = g_off + sizeof(float) * C;
     static constexpr size_t bytes = b_off + sizeof(float) * C;
 };
@@ -249,11 +252,9 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(int H, const int32_t *_
             }
             typename M::frag lo, hi;
             to_op(rq[it], lo, hi);
-            *reinterpret_cast<typename M::frag *>(Qs + r * PQ + c8) = lo;
-            *reinterpret_cast<typename M::frag *>(Qs + r * PQ + c8 + 4) = hi;
+            store_row8(Qs + r * PQ + c8, lo, hi);
             to_op(rk[it], lo, hi);
-            *reinterpret_cast<typename M::frag *>(Ks + r * PQ + c8) = lo;
-            *reinterpret_cast<typename M::frag *>(Ks + r * PQ + c8 + 4) = hi;
+            store_row8(Ks + r * PQ + c8, lo, hi);
         }
         if (w == 0) {
             if (l >= len) la = bt = 0.f;
@@ -268,20 +269,37 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(int H, const int32_t *_
         if (item + gridDim.x < items) load(item + gridDim.x);   // next item, in flight during compute
 
         // Lower-triangular 16x16 tiles (a, b), b <= a, of P^T = K Q^T (10) and
-        // of (K K^T)^T (10).  Lane (n, j) gets row r = 16a + n and columns
-        // c = 16b + 4j + i of P (resp. K K^T).
-        for (int t = w; t < 2 * kTriTiles; t += 4) {
+        // of (K K^T)^T (10); wave w takes tiles w, w + 4, ...  Lane (n, j) gets
+        // row r = 16a + n and columns c = 16b + 4j + i of P (resp. K K^T).
+        // Both operands are rows of Q or K over dk, so the k order inside a
+        // tile pair is free: lane group j takes dk 32p + 8j .. +7, one 16-byte
+        // read per operand.  The products all finish before A and T, which
+        // may share the Q/K space, are written.
+        constexpr int NTW = (2 * kTriTiles + 3) / 4;   // tiles per wave
+        float4_t gacc[NTW];
+#pragma unroll
+        for (int u = 0; u < NTW; ++u) {
+            const int t = w + 4 * u;
+            gacc[u] = float4_t{0.f, 0.f, 0.f, 0.f};
+            if (t >= 2 * kTriTiles) continue;
+            const bool isq = t < kTriTiles;
+            int a, b;
+            tri_decode(isq ? t : t - kTriTiles, a, b);
+            const OP *asrc = Ks + (16 * b + nn) * PQ + 8 * jj;
+            const OP *bsrc = (isq ? Qs : Ks) + (16 * a + nn) * PQ + 8 * jj;
+#pragma unroll
+            for (int p = 0; p < KP; ++p) mma2(gacc[u], row_frag2(asrc + 32 * p), row_frag2(bsrc + 32 * p));
+        }
+        if constexpr (L::mats_alias) __syncthreads();
+#pragma unroll
+        for (int u = 0; u < NTW; ++u) {
+            const int t = w + 4 * u;
+            if (t >= 2 * kTriTiles) continue;
             const bool isq = t < kTriTiles;
             const int tl = isq ? t : t - kTriTiles;
             int a, b;
             tri_decode(tl, a, b);
-            const OP *asrc = Ks + (16 * b + nn) * PQ + 4 * jj;
-            const OP *bsrc = (isq ? Qs : Ks) + (16 * a + nn) * PQ + 4 * jj;
-            float4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int p = 0; p < KP; ++p)
-                mma2(acc, F2::make(lds_frag(asrc + 32 * p), lds_frag(asrc + 32 * p + 16)),
-                     F2::make(lds_frag(bsrc + 32 * p), lds_frag(bsrc + 32 * p + 16)));
+            const float4_t acc = gacc[u];
             const int r = 16 * a + nn, c0 = 16 * b + 4 * jj;
             const float gr = gs[r];
             const float4_t gc = *reinterpret_cast<const float4_t *>(gs + c0);
@@ -414,22 +432,6 @@ struct StateSmem {
     static_assert(QROW % 16 == 0 && VROW % 16 == 0, "16-byte rows");
 };
 
-
-// Eight consecutive operand values of one LDS row: a k-tile pair fragment.
-__device__ __forceinline__ Frag2<_Float16> row_frag2(const _Float16 *p) {
-    return Frag2<_Float16>{*reinterpret_cast<const half8_t *>(p)};
-}
-__device__ __forceinline__ Frag2<float> row_frag2(const float *p) {
-    return Frag2<float>{*reinterpret_cast<const float4_t *>(p), *reinterpret_cast<const float4_t *>(p + 4)};
-}
-// Eight values as the 16-byte LDS store of a row segment.
-__device__ __forceinline__ void store_row8(_Float16 *p, half4_t lo, half4_t hi) {
-    *reinterpret_cast<half8_t *>(p) = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-__device__ __forceinline__ void store_row8(float *p, float4_t lo, float4_t hi) {
-    reinterpret_cast<float4_t *>(p)[0] = lo;
-    reinterpret_cast<float4_t *>(p)[1] = hi;
-}
 
 // V in accumulator layout: V[R + i][c] for lane (c = c0 + n, R = row0 + 4 j),
 // i < 4.  16-bit V uses one transposed read at the lane's address `a`; fp32
@@ -1017,15 +1019,32 @@ ChunkWorkspace chunk_workspace_layout(int32_t B, int32_t T, int32_t N, bool pack
 }
 
 // Compute waves per state-pass block (16 value columns each; the block also
-// has kStagers staging waves).  GDN_STATE_WAVES (1, 2 or 4) lowers the count
-// for experiments.
-static int state_waves_per_block(int DV) {
+// has kStagers staging waves).  A chunk's latency does not shrink with more
+// compute waves per block, so the block count is what matters: the fewest
+// waves (at least 2) whose blocks still fit on the GPU in one round; 4 when
+// no choice does.  GDN_STATE_WAVES (1, 2 or 4) overrides, for experiments.
+static int state_waves_per_block(int DV, int64_t NH) {
+    static int cus = 0;
+    if (cus == 0) {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cus = n;
+    }
     const int tiles = (DV + 15) / 16;
-    int nw = tiles >= 4 ? 4 : (tiles >= 2 ? 2 : 1);
+    const int64_t slots = ((NH + 7) / 8) * 8;
+    int nw = 4;
+    for (int c = 2; c <= 4; c *= 2)
+        if (slots * ((tiles + c - 1) / c) <= cus) {
+            nw = c;
+            break;
+        }
+    if (tiles < nw) nw = tiles >= 2 ? 2 : 1;
     const char *env = getenv("GDN_STATE_WAVES");
     if (env) {
         const int x = atoi(env);
-        if ((x == 1 || x == 2 || x == 4) && x < nw) nw = x;
+        if (x == 1 || x == 2 || x == 4) nw = x;
     }
     return nw;
 }
@@ -1077,7 +1096,7 @@ static hipError_t launch_dk(const ChunkArgs &a, const ChunkWorkspace &w, hipStre
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    switch (state_waves_per_block(a.dv)) {
+    switch (state_waves_per_block(a.dv, (int64_t)a.N * a.H)) {
     case 4: return launch_state<in_t, OP, DK, 4>(a, w, st);
     case 2: return launch_state<in_t, OP, DK, 2>(a, w, st);
     default: return launch_state<in_t, OP, DK, 1>(a, w, st);

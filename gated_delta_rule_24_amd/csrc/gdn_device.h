@@ -152,6 +152,22 @@ __device__ __forceinline__ void mma2(float4_t &acc, const Frag2<float> &a, const
     for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[i], b.hi[i], acc, 0, 0, 0);
 }
 
+// Eight consecutive operand values of one LDS row: a k-tile pair fragment.
+__device__ __forceinline__ Frag2<_Float16> row_frag2(const _Float16 *p) {
+    return Frag2<_Float16>{*reinterpret_cast<const half8_t *>(p)};
+}
+__device__ __forceinline__ Frag2<float> row_frag2(const float *p) {
+    return Frag2<float>{*reinterpret_cast<const float4_t *>(p), *reinterpret_cast<const float4_t *>(p + 4)};
+}
+// Eight values as the 16-byte LDS store of a row segment.
+__device__ __forceinline__ void store_row8(_Float16 *p, half4_t lo, half4_t hi) {
+    *reinterpret_cast<half8_t *>(p) = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ void store_row8(float *p, float4_t lo, float4_t hi) {
+    reinterpret_cast<float4_t *>(p)[0] = lo;
+    reinterpret_cast<float4_t *>(p)[1] = hi;
+}
+
 // Four consecutive operand values from LDS (8-byte or 16-byte aligned read).
 template <typename OP>
 __device__ __forceinline__ typename Mma<OP>::frag lds_frag(const OP *p) {
