@@ -74,12 +74,14 @@ __device__ __forceinline__ void lds_store8(OP *p, const float (&x)[8]) {
 }
 
 // ============================================================================
-// G0: chunk table.
+// G0: chunk table of a packed batch (cu_seqlens given).
 //   meta[0] = number of rows, meta[1] = cu_seqlens error code (0 = valid)
 //   cu_ws[N+1] = token offsets, row0[N] = first row of each sequence,
 //   row_tok / row_len = token start and length of each row.
+// A batch of equal-length sequences needs no table: G1 and G2 derive a row's
+// span from its index (row_span below) and G0 is not launched.
 // ============================================================================
-__global__ __launch_bounds__(256) void chunk_table_kernel(int N, int T, int packed,
+__global__ __launch_bounds__(256) void chunk_table_kernel(int N, int T,
                                                           const int32_t *__restrict__ cu_in,
                                                           int32_t *__restrict__ meta,
                                                           int32_t *__restrict__ cu_ws,
@@ -96,13 +98,11 @@ __global__ __launch_bounds__(256) void chunk_table_kernel(int N, int T, int pack
     }
     __syncthreads();
     for (int n = tid; n <= N; n += 256) {
-        const int val = packed ? cu_in[n] : n * T;
+        const int val = cu_in[n];
         cu_ws[n] = val;
-        if (packed) {
-            if (n == 0 && val != 0) atomicOr(&s_code, 1);
-            if (n > 0 && cu_in[n - 1] > val) atomicOr(&s_code, 2);
-            if (n == N && val != T) atomicOr(&s_code, 4);
-        }
+        if (n == 0 && val != 0) atomicOr(&s_code, 1);
+        if (n > 0 && cu_in[n - 1] > val) atomicOr(&s_code, 2);
+        if (n == N && val != T) atomicOr(&s_code, 4);
     }
     __syncthreads();
     const int code = s_code;
@@ -117,9 +117,7 @@ __global__ __launch_bounds__(256) void chunk_table_kernel(int N, int T, int pack
         const int n = base + tid;
         int cnt = 0;
         if (n < N) {
-            const int s0 = packed ? cu_in[n] : n * T;
-            const int s1 = packed ? cu_in[n + 1] : (n + 1) * T;
-            cnt = (s1 - s0 + C - 1) / C;
+            cnt = (cu_in[n + 1] - cu_in[n] + C - 1) / C;
         }
         s_scan[tid] = cnt;
         __syncthreads();
@@ -139,13 +137,27 @@ __global__ __launch_bounds__(256) void chunk_table_kernel(int N, int T, int pack
         meta[1] = 0;
     }
     for (int n = tid; n < N; n += 256) {
-        const int s0 = packed ? cu_in[n] : n * T;
-        const int s1 = packed ? cu_in[n + 1] : (n + 1) * T;
+        const int s0 = cu_in[n], s1 = cu_in[n + 1];
         const int r = row0[n];
         for (int j = 0; j * C < s1 - s0; ++j) {
             row_tok[r + j] = s0 + j * C;
             row_len[r + j] = min(C, s1 - s0 - j * C);
         }
+    }
+}
+
+// Token start and length of chunk row `row`.  With cpr > 0 the batch is
+// B sequences of T tokens each, cpr = ceil(T / C) rows per sequence, and the
+// span follows from the index; cpr = 0 reads the packed table.
+__device__ __forceinline__ void row_span(int row, int T, int cpr, const int32_t *__restrict__ row_tok,
+                                         const int32_t *__restrict__ row_len, int &tok0, int &len) {
+    if (cpr) {
+        const int s = row / cpr, c = row - s * cpr;
+        tok0 = s * T + c * C;
+        len = min(C, T - c * C);
+    } else {
+        tok0 = row_tok[row];
+        len = row_len[row];
     }
 }
 
@@ -185,7 +197,8 @@ struct PrepSmem {
 __device__ __forceinline__ float exp_neg(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
 
 template <typename in_t, typename OP, int DK>
-__global__ __launch_bounds__(256) void chunk_prep_kernel(int H, const int32_t *__restrict__ meta,
+__global__ __launch_bounds__(256) void chunk_prep_kernel(int H, int T, int cpr, int urows,
+                                                         const int32_t *__restrict__ meta,
                                                          const int32_t *__restrict__ row_tok,
                                                          const int32_t *__restrict__ row_len,
                                                          const in_t *__restrict__ q,
@@ -210,13 +223,14 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(int H, const int32_t *_
     float *bs = reinterpret_cast<float *>(smem + L::b_off);
 
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, nn = l & 15, jj = l >> 4;
-    const int items = meta[0] * H;
+    const int items = (cpr ? urows : meta[0]) * H;
 
     Raw8<in_t> rq[QK_IT], rk[QK_IT];
     float la = 0.f, bt = 0.f;
     auto load = [&](int item) {
         const int row = item / H, h = item % H;
-        const int tok0 = row_tok[row], len = row_len[row];
+        int tok0, len;
+        row_span(row, T, cpr, row_tok, row_len, tok0, len);
 #pragma unroll
         for (int it = 0; it < QK_IT; ++it) {
             const int idx = tid + it * 256;
@@ -236,7 +250,8 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(int H, const int32_t *_
     if (item < items) load(item);
     for (; item < items; item += gridDim.x) {
         const int row = item / H;
-        const int len = row_len[row];
+        int tok_unused, len;
+        row_span(row, T, cpr, row_tok, row_len, tok_unused, len);
         const int64_t rh = item;   // == row * H + h
 
         // Commit the prefetched chunk.  Rows past the end of the sequence are
@@ -505,7 +520,7 @@ __device__ __forceinline__ void dma16(const void *g, uint32_t lds) {
 
 template <typename in_t, typename OP, int DK, int NW>
 __global__ __launch_bounds__(64 * (NW + kStagers)) void chunk_state_kernel(
-    int NH, int H, int DV, int nvt, int odt, const int32_t *__restrict__ meta,
+    int NH, int H, int DV, int nvt, int odt, int T, int cpr, int32_t *__restrict__ meta,
     const int32_t *__restrict__ cu_ws, const int32_t *__restrict__ row0,
     const in_t *__restrict__ q, const in_t *__restrict__ k, const in_t *__restrict__ v,
     const float *__restrict__ ws_g, const OP *__restrict__ ws_m, const OP *__restrict__ ws_p,
@@ -524,7 +539,16 @@ __global__ __launch_bounds__(64 * (NW + kStagers)) void chunk_state_kernel(
     extern __shared__ __align__(16) unsigned char smem[];
     const uint32_t lds0 = (uint32_t)(uintptr_t)smem;       // LDS address of smem
 
-    if (meta[1] != 0) return;
+    if (cpr) {
+        // Equal-length batch: no table pass ran, so report its row count and
+        // a clean status for the host-side check here.
+        if (blockIdx.x == 0 && threadIdx.x == 0) {
+            meta[0] = (NH / H) * ((T + C - 1) / C);
+            meta[1] = 0;
+        }
+    } else if (meta[1] != 0) {
+        return;
+    }
     const int bid = blockIdx.x, xcd = bid & 7, slot = bid >> 3;
     const int chain = (slot / nvt) * 8 + xcd, vt = slot % nvt;
     if (chain >= NH) return;
@@ -537,9 +561,9 @@ __global__ __launch_bounds__(64 * (NW + kStagers)) void chunk_state_kernel(
     const int vb = vt * BV;                 // first value column of the block
     const int v0 = vb + w * 16;             // first value column of a compute wave
     const bool active = !stager && v0 < DV;
-    const int tok0 = cu_ws[n];
-    const int len_seq = cu_ws[n + 1] - tok0;
-    const int r0 = row0[n];
+    const int tok0 = cpr ? n * T : cu_ws[n];
+    const int len_seq = cpr ? T : cu_ws[n + 1] - tok0;
+    const int r0 = cpr ? n * cpr : row0[n];
     const int nchunks = (len_seq + C - 1) / C;
 
     // ---- per-lane LDS byte offsets ----
@@ -1056,6 +1080,10 @@ static hipError_t allow_smem(K kernel, size_t bytes) {
                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
+// Chunk rows per sequence of an equal-length batch (at least 1, so that an
+// empty batch still reads as equal-length), 0 for a packed one.
+static int uniform_cpr(const ChunkArgs &a) { return a.cu_seqlens ? 0 : (a.T + C - 1) / C + (a.T == 0); }
+
 template <typename in_t, typename OP, int DK, int NW>
 static hipError_t launch_state(const ChunkArgs &a, const ChunkWorkspace &w, hipStream_t st) {
     using L = StateSmem<in_t, OP, DK, NW>;
@@ -1068,7 +1096,7 @@ static hipError_t launch_state(const ChunkArgs &a, const ChunkWorkspace &w, hipS
     const int64_t blocks = ((NH + 7) / 8) * 8 * nvt;
     ProfScope prof("gdn_chunk_state", st);
     kern<<<dim3((unsigned)blocks), dim3(64 * (NW + kStagers)), L::bytes, st>>>(
-        (int)NH, a.H, a.dv, nvt, a.out_dtype, reinterpret_cast<const int32_t *>(ws + w.off_meta),
+        (int)NH, a.H, a.dv, nvt, a.out_dtype, a.T, uniform_cpr(a), reinterpret_cast<int32_t *>(ws + w.off_meta),
         reinterpret_cast<const int32_t *>(ws + w.off_cu), reinterpret_cast<const int32_t *>(ws + w.off_row0),
         static_cast<const in_t *>(a.q), static_cast<const in_t *>(a.k), static_cast<const in_t *>(a.v),
         reinterpret_cast<const float *>(ws + w.off_g), reinterpret_cast<const OP *>(ws + w.off_m),
@@ -1088,7 +1116,8 @@ static hipError_t launch_dk(const ChunkArgs &a, const ChunkWorkspace &w, hipStre
         const int64_t items = w.max_rows * a.H;
         const int64_t grid = items < 768 ? items : 768;   // about three resident blocks per CU
         kern<<<dim3((unsigned)grid), dim3(256), L::bytes, st>>>(
-            a.H, reinterpret_cast<const int32_t *>(ws + w.off_meta),
+            a.H, a.T, uniform_cpr(a), (int)(uniform_cpr(a) ? w.max_rows : 0),
+            reinterpret_cast<const int32_t *>(ws + w.off_meta),
             reinterpret_cast<const int32_t *>(ws + w.off_rowtok),
             reinterpret_cast<const int32_t *>(ws + w.off_rowlen), static_cast<const in_t *>(a.q),
             static_cast<const in_t *>(a.k), a.log_alpha, a.beta, reinterpret_cast<float *>(ws + w.off_g),
@@ -1120,9 +1149,9 @@ hipError_t launch_chunk_fwd(const ChunkArgs &a, hipStream_t st) {
     const bool packed = a.cu_seqlens != nullptr;
     const ChunkWorkspace w = chunk_workspace_layout(a.B, a.T, a.N, packed, a.H, a.in_dtype);
     char *ws = static_cast<char *>(a.workspace);
-    {
+    if (packed) {
         ProfScope prof("gdn_chunk_table", st);
-        chunk_table_kernel<<<1, 256, 0, st>>>(a.N, a.T, packed ? 1 : 0, a.cu_seqlens,
+        chunk_table_kernel<<<1, 256, 0, st>>>(a.N, a.T, a.cu_seqlens,
                                              reinterpret_cast<int32_t *>(ws + w.off_meta),
                                              reinterpret_cast<int32_t *>(ws + w.off_cu),
                                              reinterpret_cast<int32_t *>(ws + w.off_row0),
