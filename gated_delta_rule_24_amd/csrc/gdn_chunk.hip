@@ -162,231 +162,285 @@ __device__ __forceinline__ void row_span(int row, int T, int cpr, const int32_t 
 }
 
 // ============================================================================
-// G1: per (chunk row, head): gamma, kappa, P = (Q K^T) o Gamma, A,
-// T = (I + A)^{-1}, M = T diag(beta).  Persistent blocks of 256 threads loop
-// over (row, head) items and load the next item while computing the current.
+// G1: one wave per (chunk row, head) item, no block barriers:
+//   g = inclusive scan of log alpha, gamma_r = e^{g_r}, kappa_r = e^{g_C - g_r},
+//   P = (Q K^T) o Gamma,  A = strictLower(diag(beta) (Gamma o K K^T)),
+//   T = (I + A)^{-1},  M = T diag(beta).
 //
-// P and M are written as lower-triangular 16x16 tiles in "fragment order":
-// tile t occupies 256 consecutive elements and lane l (n = l % 16, j = l / 16)
-// owns elements [4l, 4l+4) = X[16a + n][16b + 4j .. 16b + 4j + 3] of tile
-// (a, b), i.e. exactly the operand fragment G2 reads for it.  G1 produces
-// them transposed (P^T = K Q^T), so each lane's accumulator already holds
-// its fragment.
+// Q and K go from global memory straight into matrix-core operand registers:
+// for row block b (rows 16b .. 16b + 15) lane (n, j) (n = l % 16, j = l / 16)
+// holds dk indices 32p + 8j .. 32p + 8j + 7 of row 16b + n, for every k-tile
+// pair p.  The product of row blocks X (first operand) and Y (second) then
+// leaves lane (n, j) holding (Y X^T)[n][4j .. 4j + 3]: the "row layout" R of
+// that 16 x 16 tile.  R is also the order P and M are stored in (tile t of
+// a row = 256 consecutive elements, lane l owning elements 4l .. 4l + 3),
+// which is the operand fragment G2 reads for them.
+//
+// The 64 x 64 inverse works on 16 x 16 blocks:
+//   diagonal      T_aa = (I + A_aa)^{-1}: lane (n, j) solves row n of T_jj by
+//                 back substitution (x (I + N) = e_n, last column first),
+//                 reading N^T of its block from LDS;
+//   off-diagonal  T_ab = -T_aa U_ab,  U_ab = sum_{b <= m < a} A_am T_mb, by
+//                 distance a - b, on fp32 matrix cores.
+// Besides R(X), tiles appear transposed, C(X): lane (n, j) holds
+// X[4j .. 4j + 3][n].  One fp32 16 x 16 x 16 product turns (R(A), C(B)) into
+// C(AB), and equally (C(U), R(T)) into R(TU), so T_ab is produced in R layout
+// for M and, where a later U needs it, in C layout as well.
 // ============================================================================
-template <typename OP, int DK>
-struct PrepSmem {
-    // Q and K rows padded by 32 bytes (conflict-free 16-byte row reads).
-    static constexpr int PQ = DK + 32 / (int)sizeof(OP);  // operand row pitch (elements)
-    static constexpr int PA = C + 4;                      // fp32 pitch of A and T
-    static constexpr size_t q_off = 0;
-    static constexpr size_t k_off = q_off + sizeof(OP) * C * PQ;
-    static constexpr size_t qk_end = k_off + sizeof(OP) * C * PQ;
-    static constexpr size_t mat_bytes = sizeof(float) * C * PA;
-    // A and T reuse the Q/K region once the Gram products are done, when
-    // both fit there (a smaller block lets more blocks share a CU).
-    static constexpr bool mats_alias = 2 * mat_bytes <= qk_end;
-    static constexpr size_t a_off = mats_alias ? 0 : qk_end;
-    static constexpr size_t t_off = a_off + mat_bytes;
-    static constexpr size_t g_off = mats_alias ? qk_end : t_off + mat_bytes;
-    static constexpr size_t b_off = g_off + sizeof(float) * C;
-    static constexpr size_t bytes = b_off + sizeof(float) * C;
-};
 
 // exp(x) for x <= 0 with the hardware base-2 exponential (about 1 ulp;
 // large negative arguments flush to 0, never NaN).
 __device__ __forceinline__ float exp_neg(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
 
+// LDS of one G1 wave, in floats: g and beta of the 64 rows, then four 16 x 16
+// blocks (N^T of each diagonal block during the solve, T_aa after it).  Row
+// pitch 20 and block pitch 324 keep the 16-byte row reads, the column reads
+// and the four-block broadcast reads free of bank conflicts.
+constexpr int kPrepBP = 20;
+constexpr int kPrepBS = 16 * kPrepBP + 4;
+constexpr int kPrepLds = 2 * C + 4 * kPrepBS;
+
+// acc += (row block X) (row block Y)^T over one k-tile pair of raw inputs.
+// bf16 and fp16 rows use their own 16x16x32 instruction (exact products,
+// fp32 sums); fp32 rows take eight 16x16x4 fp32 instructions.
+__device__ __forceinline__ void gram_mma(float4_t &acc, const Raw8<bf16_t> &x, const Raw8<bf16_t> &y) {
+    typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, x.x),
+                                                 __builtin_bit_cast(bf16x8_t, y.x), acc, 0, 0, 0);
+}
+__device__ __forceinline__ void gram_mma(float4_t &acc, const Raw8<_Float16> &x, const Raw8<_Float16> &y) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, x.x),
+                                                __builtin_bit_cast(half8_t, y.x), acc, 0, 0, 0);
+}
+__device__ __forceinline__ void gram_mma(float4_t &acc, const Raw8<float> &x, const Raw8<float> &y) {
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+        const float4_t a = __builtin_bit_cast(float4_t, x.x[hh]), b = __builtin_bit_cast(float4_t, y.x[hh]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[i], acc, 0, 0, 0);
+    }
+}
+
+// One fp32 16 x 16 x 16 tile product: (R(A), C(B)) -> C(AB) + acc, or
+// equally (C(U), R(T)) -> R(TU) + acc.
+__device__ __forceinline__ float4_t mm16(const float4_t &x, const float4_t &y, float4_t acc) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x[s], y[s], acc, 0, 0, 0);
+    return acc;
+}
+
 template <typename in_t, typename OP, int DK>
-__global__ __launch_bounds__(256) void chunk_prep_kernel(int H, int T, int cpr, int urows,
-                                                         const int32_t *__restrict__ meta,
-                                                         const int32_t *__restrict__ row_tok,
-                                                         const int32_t *__restrict__ row_len,
-                                                         const in_t *__restrict__ q,
-                                                         const in_t *__restrict__ k,
-                                                         const float *__restrict__ log_alpha,
-                                                         const float *__restrict__ beta,
-                                                         float *__restrict__ ws_g,
-                                                         OP *__restrict__ ws_m,
-                                                         OP *__restrict__ ws_p) {
+__global__ __launch_bounds__(64) void chunk_prep_kernel(int H, int T, int cpr, int urows,
+                                                        const int32_t *__restrict__ meta,
+                                                        const int32_t *__restrict__ row_tok,
+                                                        const int32_t *__restrict__ row_len,
+                                                        const in_t *__restrict__ q,
+                                                        const in_t *__restrict__ k,
+                                                        const float *__restrict__ log_alpha,
+                                                        const float *__restrict__ beta,
+                                                        float *__restrict__ ws_g,
+                                                        OP *__restrict__ ws_m,
+                                                        OP *__restrict__ ws_p) {
     using M = Mma<OP>;
-    using F2 = Frag2<OP>;
-    using L = PrepSmem<OP, DK>;
-    constexpr int PQ = L::PQ, PA = L::PA;
-    constexpr int QK_IT = C * DK / 8 / 256;
-    constexpr int KP = DK / 32;                          // k-tile pairs along dk
-    extern __shared__ __align__(16) unsigned char smem[];
-    OP *Qs = reinterpret_cast<OP *>(smem + L::q_off);
-    OP *Ks = reinterpret_cast<OP *>(smem + L::k_off);
-    float *As = reinterpret_cast<float *>(smem + L::a_off);
-    float *Ts = reinterpret_cast<float *>(smem + L::t_off);
-    float *gs = reinterpret_cast<float *>(smem + L::g_off);
-    float *bs = reinterpret_cast<float *>(smem + L::b_off);
+    constexpr int KP = DK / 32;   // k-tile pairs along dk
+    // Q and K registers of one pass over dk: at most 128 per lane.
+    constexpr int REGS_PER_PAIR = 2 * 4 * (int)sizeof(Raw8<in_t>) / 4;
+    constexpr int NPASS = KP * REGS_PER_PAIR > 128 ? KP * REGS_PER_PAIR / 128 : 1;
+    constexpr int PP = KP / NPASS;   // k-tile pairs per pass
+    static_assert(PP * NPASS == KP, "dk must split evenly into passes");
+    constexpr int BP = kPrepBP, BS = kPrepBS;
+    __shared__ __align__(16) float lds[kPrepLds];
+    float *gs = lds, *bs = lds + C, *blk = lds + 2 * C;
 
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, nn = l & 15, jj = l >> 4;
+    const int l = threadIdx.x, nn = l & 15, jj = l >> 4;
     const int items = (cpr ? urows : meta[0]) * H;
+    const int64_t tok_stride = (int64_t)H * DK;
 
-    Raw8<in_t> rq[QK_IT], rk[QK_IT];
-    float la = 0.f, bt = 0.f;
-    auto load = [&](int item) {
+    for (int item = blockIdx.x; item < items; item += gridDim.x) {
         const int row = item / H, h = item % H;
         int tok0, len;
         row_span(row, T, cpr, row_tok, row_len, tok0, len);
-#pragma unroll
-        for (int it = 0; it < QK_IT; ++it) {
-            const int idx = tid + it * 256;
-            const int r = min(idx / (DK / 8), len - 1), c8 = (idx % (DK / 8)) * 8;
-            const int64_t off = ((int64_t)(tok0 + r) * H + h) * DK + c8;
-            rq[it].load(q + off);
-            rk[it].load(k + off);
-        }
-        if (w == 0) {
+        const int64_t rh = item;   // == row * H + h
+
+        // Decay inputs, lane l = chunk row l.  Rows past the end of the
+        // sequence get log alpha = 0 and beta = 0 and zero Q and K rows: g
+        // stays flat there and those rows are inert in every product.
+        float la, bt;
+        {
             const int r = min(l, len - 1);
             la = log_alpha[(int64_t)(tok0 + r) * H + h];
             bt = beta[(int64_t)(tok0 + r) * H + h];
         }
-    };
-
-    int item = blockIdx.x;
-    if (item < items) load(item);
-    for (; item < items; item += gridDim.x) {
-        const int row = item / H;
-        int tok_unused, len;
-        row_span(row, T, cpr, row_tok, row_len, tok_unused, len);
-        const int64_t rh = item;   // == row * H + h
-
-        // Commit the prefetched chunk.  Rows past the end of the sequence are
-        // zero, with log alpha = 0 and beta = 0: g stays flat and those rows
-        // are inert in every later product.
+        const in_t *qb = q + ((int64_t)tok0 * H + h) * DK + 8 * jj;
+        const in_t *kb = k + ((int64_t)tok0 * H + h) * DK + 8 * jj;
+        int64_t roff[4];   // offset of the lane's row in each row block (clamped)
 #pragma unroll
-        for (int it = 0; it < QK_IT; ++it) {
-            const int idx = tid + it * 256;
-            const int r = idx / (DK / 8), c8 = (idx % (DK / 8)) * 8;
-            if (r >= len) {
-                rq[it].zero();
-                rk[it].zero();
+        for (int b = 0; b < 4; ++b) roff[b] = (int64_t)min(16 * b + nn, len - 1) * tok_stride;
+
+        Raw8<in_t> kr[4][PP], qr[4][PP];
+        auto load_pass = [&](int s) {
+#pragma unroll
+            for (int p = 0; p < PP; ++p)
+#pragma unroll
+                for (int b = 0; b < 4; ++b) kr[b][p].load(kb + roff[b] + 32 * (s * PP + p));
+#pragma unroll
+            for (int p = 0; p < PP; ++p)
+#pragma unroll
+                for (int b = 0; b < 4; ++b) qr[b][p].load(qb + roff[b] + 32 * (s * PP + p));
+            if (len < C) {
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+                    if (16 * b + nn >= len)
+#pragma unroll
+                        for (int p = 0; p < PP; ++p) {
+                            kr[b][p].zero();
+                            qr[b][p].zero();
+                        }
             }
-            typename M::frag lo, hi;
-            to_op(rq[it], lo, hi);
-            store_row8(Qs + r * PQ + c8, lo, hi);
-            to_op(rk[it], lo, hi);
-            store_row8(Ks + r * PQ + c8, lo, hi);
-        }
-        if (w == 0) {
-            if (l >= len) la = bt = 0.f;
-            const float g = wave_inclusive_scan(la);
-            const float g_last = __shfl(g, C - 1, 64);
-            gs[l] = g;
-            bs[l] = bt;
-            ws_g[rh * 2 * C + l] = expf(g);               // gamma_r: decay from the chunk start
-            ws_g[rh * 2 * C + C + l] = expf(g_last - g);  // kappa_r: decay from row r to the chunk end
-        }
-        __syncthreads();
-        if (item + gridDim.x < items) load(item + gridDim.x);   // next item, in flight during compute
+        };
+        load_pass(0);
 
-        // Lower-triangular 16x16 tiles (a, b), b <= a, of P^T = K Q^T (10) and
-        // of (K K^T)^T (10); wave w takes tiles w, w + 4, ...  Lane (n, j) gets
-        // row r = 16a + n and columns c = 16b + 4j + i of P (resp. K K^T).
-        // Both operands are rows of Q or K over dk, so the k order inside a
-        // tile pair is free: lane group j takes dk 32p + 8j .. +7, one 16-byte
-        // read per operand.  The products all finish before A and T, which
-        // may share the Q/K space, are written.
-        constexpr int NTW = (2 * kTriTiles + 3) / 4;   // tiles per wave
-        float4_t gacc[NTW];
+        if (l >= len) la = bt = 0.f;
+        const float g = wave_inclusive_scan(la);
+        const float g_last = __shfl(g, C - 1, 64);
+        gs[l] = g;
+        bs[l] = bt;
+        ws_g[rh * 2 * C + l] = expf(g);               // gamma_r: decay from the chunk start
+        ws_g[rh * 2 * C + C + l] = expf(g_last - g);  // kappa_r: decay from row r to the chunk end
+
+        // Lower-triangular tiles (a, b), b <= a, of Q K^T and K K^T in R
+        // layout: first operand row block b of K, second row block a.
+        float4_t pacc[kTriTiles], gacc[kTriTiles];
 #pragma unroll
-        for (int u = 0; u < NTW; ++u) {
-            const int t = w + 4 * u;
-            gacc[u] = float4_t{0.f, 0.f, 0.f, 0.f};
-            if (t >= 2 * kTriTiles) continue;
-            const bool isq = t < kTriTiles;
-            int a, b;
-            tri_decode(isq ? t : t - kTriTiles, a, b);
-            const OP *asrc = Ks + (16 * b + nn) * PQ + 8 * jj;
-            const OP *bsrc = (isq ? Qs : Ks) + (16 * a + nn) * PQ + 8 * jj;
+        for (int t = 0; t < kTriTiles; ++t) pacc[t] = gacc[t] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int p = 0; p < KP; ++p) mma2(gacc[u], row_frag2(asrc + 32 * p), row_frag2(bsrc + 32 * p));
+        for (int s = 0; s < NPASS; ++s) {
+            if (s > 0) {
+                __builtin_amdgcn_sched_barrier(0);
+                load_pass(s);
+            }
+#pragma unroll
+            for (int t = 0; t < kTriTiles; ++t) {
+                int a, b;
+                tri_decode(t, a, b);
+#pragma unroll
+                for (int p = 0; p < PP; ++p) {
+                    gram_mma(gacc[t], kr[b][p], kr[a][p]);
+                    gram_mma(pacc[t], kr[b][p], qr[a][p]);
+                }
+            }
         }
-        if constexpr (L::mats_alias) __syncthreads();
+
+        // Decay masks.  Off-diagonal tiles: row r = 16a + n, columns
+        // c = 16b + 4j + i < r, one exponential shared by P and A.  Diagonal
+        // tiles: the lane's positions with c <= r belong to P; the others
+        // give N^T[n][c - 16a] = A[c][r] of the same block, whose decay is
+        // e^{g_c - g_r}, so again one exponential per position.
+        float gr[4], br[4];
 #pragma unroll
-        for (int u = 0; u < NTW; ++u) {
-            const int t = w + 4 * u;
-            if (t >= 2 * kTriTiles) continue;
-            const bool isq = t < kTriTiles;
-            const int tl = isq ? t : t - kTriTiles;
+        for (int a = 0; a < 4; ++a) {
+            gr[a] = gs[16 * a + nn];
+            br[a] = bs[16 * a + nn];
+        }
+        float4_t aR[kTriTiles];   // R(A_ab) for a > b
+#pragma unroll
+        for (int t = 0; t < kTriTiles; ++t) {
             int a, b;
-            tri_decode(tl, a, b);
-            const float4_t acc = gacc[u];
-            const int r = 16 * a + nn, c0 = 16 * b + 4 * jj;
-            const float gr = gs[r];
-            const float4_t gc = *reinterpret_cast<const float4_t *>(gs + c0);
-            float4_t val;
-            if (isq) {
+            tri_decode(t, a, b);
+            const float4_t gc = *reinterpret_cast<const float4_t *>(gs + 16 * b + 4 * jj);
+            float4_t pv, av;
+            if (a > b) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) val[i] = (c0 + i <= r) ? exp_neg(gr - gc[i]) * acc[i] : 0.f;
-                *reinterpret_cast<typename M::frag *>(ws_p + (rh * kTriTiles + tl) * kTileElems + 4 * l) = M::cvt(val);
+                for (int i = 0; i < 4; ++i) {
+                    const float e = exp_neg(gr[a] - gc[i]);
+                    pv[i] = e * pacc[t][i];
+                    av[i] = br[a] * e * gacc[t][i];
+                }
+                aR[t] = av;
             } else {
-                const float br = bs[r];
+                const float4_t bc = *reinterpret_cast<const float4_t *>(bs + 16 * a + 4 * jj);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) val[i] = (c0 + i < r) ? br * exp_neg(gr - gc[i]) * acc[i] : 0.f;
-                *reinterpret_cast<float4_t *>(As + r * PA + c0) = val;
+                for (int i = 0; i < 4; ++i) {
+                    const bool lower = 4 * jj + i <= nn;
+                    const float x = gr[a] - gc[i];
+                    const float e = exp_neg(lower ? x : -x);
+                    pv[i] = lower ? e * pacc[t][i] : 0.f;
+                    av[i] = lower ? 0.f : bc[i] * e * gacc[t][i];
+                }
+                *reinterpret_cast<float4_t *>(blk + a * BS + nn * BP + 4 * jj) = av;
+                aR[t] = float4_t{0.f, 0.f, 0.f, 0.f};
             }
+            *reinterpret_cast<typename M::frag *>(ws_p + (rh * kTriTiles + t) * kTileElems + 4 * l) = M::cvt(pv);
         }
-        __syncthreads();
+        asm volatile("" ::: "memory");
 
-        // T = (I + A)^{-1}.  Diagonal 16x16 blocks by forward substitution,
-        // wave w takes block w, one column per lane.
+        // Diagonal blocks: lane (n, j) computes row n of T_jj,
+        //   x[c] = [c == n] - sum_{i > c} x[i] N[i][c],  c = 15 .. 0,
+        // reading row c of N^T (broadcast to the 16 lanes of the block).
         {
-            const int blk = w, col = nn;
-            const float *arow = As + 16 * blk * PA + 16 * blk;
+            const float *nt = blk + jj * BS;
             float x[16];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float acc = (r == col) ? 1.f : 0.f;
+            for (int c = 15; c >= 0; --c) {
+                float acc = (c == nn) ? 1.f : 0.f;
 #pragma unroll
-                for (int i = 0; i < r; ++i) acc -= arow[r * PA + i] * x[i];
-                x[r] = acc;
-            }
-            if (jj == 0) {
+                for (int qd = (c + 1) / 4; qd < 4; ++qd) {
+                    const float4_t v = *reinterpret_cast<const float4_t *>(nt + c * BP + 4 * qd);
 #pragma unroll
-                for (int r = 0; r < 16; ++r) Ts[(16 * blk + r) * PA + 16 * blk + col] = x[r];
-            }
-        }
-        __syncthreads();
-        // Off-diagonal blocks, by distance d below the diagonal:
-        //   T_ab = -T_aa * sum_{b <= m < a} A_am T_mb     (fp32 matrix cores)
-        for (int d = 1; d < 4; ++d) {
-            if (w < 4 - d) {
-                const int b = w, a = w + d;
-                float4_t X = {0.f, 0.f, 0.f, 0.f};
-                for (int m = b; m < a; ++m) {
-                    const float4_t af = *reinterpret_cast<const float4_t *>(As + (16 * a + nn) * PA + 16 * m + 4 * jj);
-                    float4_t bf;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) bf[i] = Ts[(16 * m + 4 * jj + i) * PA + 16 * b + nn];
-                    Mma<float>::issue(X, af, af, bf, bf);
+                    for (int e = 0; e < 4; ++e)
+                        if (4 * qd + e > c) acc -= x[4 * qd + e] * v[e];
                 }
-                const float4_t tf = *reinterpret_cast<const float4_t *>(Ts + (16 * a + nn) * PA + 16 * a + 4 * jj);
-                float4_t Y = {0.f, 0.f, 0.f, 0.f};
-                Mma<float>::issue(Y, tf, tf, X, X);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) Ts[(16 * a + 4 * jj + i) * PA + 16 * b + nn] = -Y[i];
+                x[c] = acc;
             }
-            __syncthreads();
-        }
-
-        // M = T diag(beta) in fragment order: lane l of tile (a, b) writes
-        // M[16a + n][16b + 4j .. +3].
-        for (int tl = w; tl < kTriTiles; tl += 4) {
-            int a, b;
-            tri_decode(tl, a, b);
-            const int r = 16 * a + nn, c0 = 16 * b + 4 * jj;
-            const float4_t tv = *reinterpret_cast<const float4_t *>(Ts + r * PA + c0);
-            const float4_t bv = *reinterpret_cast<const float4_t *>(bs + c0);
-            float4_t val;
+            asm volatile("" ::: "memory");
 #pragma unroll
-            for (int i = 0; i < 4; ++i) val[i] = (c0 + i <= r) ? tv[i] * bv[i] : 0.f;
-            *reinterpret_cast<typename M::frag *>(ws_m + (rh * kTriTiles + tl) * kTileElems + 4 * l) = M::cvt(val);
+            for (int qd = 0; qd < 4; ++qd)
+                *reinterpret_cast<float4_t *>(blk + jj * BS + nn * BP + 4 * qd) =
+                    float4_t{x[4 * qd], x[4 * qd + 1], x[4 * qd + 2], x[4 * qd + 3]};
         }
-        __syncthreads();   // LDS is reused by the next item
+        asm volatile("" ::: "memory");
+        float4_t tR[4], tC[3];   // R(T_aa), C(T_bb)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) tR[a] = *reinterpret_cast<const float4_t *>(blk + a * BS + nn * BP + 4 * jj);
+#pragma unroll
+        for (int b = 0; b < 3; ++b)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) tC[b][i] = blk[b * BS + (4 * jj + i) * BP + nn];
+
+        // Off-diagonal blocks by distance from the diagonal.
+        const float4_t z = {0.f, 0.f, 0.f, 0.f};
+        float4_t TR[kTriTiles];   // R(T_ab)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) TR[tri_index(a, a)] = tR[a];
+        float4_t U, C10, C21, C20;
+        U = mm16(aR[tri_index(1, 0)], tC[0], z);
+        TR[tri_index(1, 0)] = -mm16(U, tR[1], z);
+        C10 = -mm16(tR[1], U, z);
+        U = mm16(aR[tri_index(2, 1)], tC[1], z);
+        TR[tri_index(2, 1)] = -mm16(U, tR[2], z);
+        C21 = -mm16(tR[2], U, z);
+        U = mm16(aR[tri_index(3, 2)], tC[2], z);
+        TR[tri_index(3, 2)] = -mm16(U, tR[3], z);
+        U = mm16(aR[tri_index(2, 1)], C10, mm16(aR[tri_index(2, 0)], tC[0], z));
+        TR[tri_index(2, 0)] = -mm16(U, tR[2], z);
+        C20 = -mm16(tR[2], U, z);
+        U = mm16(aR[tri_index(3, 2)], C21, mm16(aR[tri_index(3, 1)], tC[1], z));
+        TR[tri_index(3, 1)] = -mm16(U, tR[3], z);
+        U = mm16(aR[tri_index(3, 2)], C20, mm16(aR[tri_index(3, 1)], C10, mm16(aR[tri_index(3, 0)], tC[0], z)));
+        TR[tri_index(3, 0)] = -mm16(U, tR[3], z);
+
+        // M = T diag(beta), R layout = fragment order.
+#pragma unroll
+        for (int t = 0; t < kTriTiles; ++t) {
+            int a, b;
+            tri_decode(t, a, b);
+            const float4_t bc = *reinterpret_cast<const float4_t *>(bs + 16 * b + 4 * jj);
+            float4_t mv;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mv[i] = TR[t][i] * bc[i];
+            *reinterpret_cast<typename M::frag *>(ws_m + (rh * kTriTiles + t) * kTileElems + 4 * l) = M::cvt(mv);
+        }
+        asm volatile("" ::: "memory");   // LDS is reused by the wave's next item
     }
 }
 
@@ -1108,21 +1162,18 @@ template <typename in_t, typename OP, int DK>
 static hipError_t launch_dk(const ChunkArgs &a, const ChunkWorkspace &w, hipStream_t st) {
     char *ws = static_cast<char *>(a.workspace);
     if (w.max_rows > 0) {   // no tokens at all: only the state pass runs (final = initial)
-        using L = PrepSmem<OP, DK>;
-        auto kern = chunk_prep_kernel<in_t, OP, DK>;
-        hipError_t e = allow_smem(kern, L::bytes);
-        if (e != hipSuccess) return e;
         ProfScope prof("gdn_chunk_prep", st);
+        // One wave per (row, head) item; very large batches loop.
         const int64_t items = w.max_rows * a.H;
-        const int64_t grid = items < 768 ? items : 768;   // about three resident blocks per CU
-        kern<<<dim3((unsigned)grid), dim3(256), L::bytes, st>>>(
+        const int64_t grid = items < (1 << 22) ? items : (1 << 22);
+        chunk_prep_kernel<in_t, OP, DK><<<dim3((unsigned)grid), dim3(64), 0, st>>>(
             a.H, a.T, uniform_cpr(a), (int)(uniform_cpr(a) ? w.max_rows : 0),
             reinterpret_cast<const int32_t *>(ws + w.off_meta),
             reinterpret_cast<const int32_t *>(ws + w.off_rowtok),
             reinterpret_cast<const int32_t *>(ws + w.off_rowlen), static_cast<const in_t *>(a.q),
             static_cast<const in_t *>(a.k), a.log_alpha, a.beta, reinterpret_cast<float *>(ws + w.off_g),
             reinterpret_cast<OP *>(ws + w.off_m), reinterpret_cast<OP *>(ws + w.off_p));
-        e = hipGetLastError();
+        const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     switch (state_waves_per_block(a.dv, (int64_t)a.N * a.H)) {
