@@ -188,9 +188,11 @@ __device__ __forceinline__ void row_span(int row, int T, int cpr, const int32_t 
 // for M and, where a later U needs it, in C layout as well.
 // ============================================================================
 
-// exp(x) for x <= 0 with the hardware base-2 exponential (about 1 ulp;
-// large negative arguments flush to 0, never NaN).
-__device__ __forceinline__ float exp_neg(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+// 2^x for x <= 0 with the hardware base-2 exponential (about 1 ulp; large
+// negative arguments flush to 0, never NaN).  G1 keeps g in base-2 units
+// (g log2 e), so the decay masks need no extra multiply.
+constexpr float kLog2e = 1.4426950408889634f;
+__device__ __forceinline__ float exp2_neg(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // LDS of one G1 wave, in floats: g and beta of the 64 rows, then four 16 x 16
 // blocks (N^T of each diagonal block during the solve, T_aa after it).  Row
@@ -221,13 +223,47 @@ __device__ __forceinline__ void gram_mma(float4_t &acc, const Raw8<float> &x, co
     }
 }
 
-// One fp32 16 x 16 x 16 tile product: (R(A), C(B)) -> C(AB) + acc, or
-// equally (C(U), R(T)) -> R(TU) + acc.
-__device__ __forceinline__ float4_t mm16(const float4_t &x, const float4_t &y, float4_t acc) {
+// One 16 x 16 x 16 tile product of the inverse: (R(A), C(B)) -> C(AB) + acc,
+// or equally (C(U), R(T)) -> R(TU) + acc, fp32 sums.  When M is stored in
+// fp16 the operands are rounded to fp16 (one instruction; the rounding is
+// that of the stored M); fp32 M keeps fp32 operands (four instructions).
+template <typename OP>
+struct InvMma;
+template <>
+struct InvMma<_Float16> {
+    __device__ __forceinline__ static float4_t mm(const float4_t &x, const float4_t &y, float4_t acc) {
+        return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_convertvector(x, half4_t),
+                                                    __builtin_convertvector(y, half4_t), acc, 0, 0, 0);
+    }
+};
+template <>
+struct InvMma<float> {
+    __device__ __forceinline__ static float4_t mm(const float4_t &x, const float4_t &y, float4_t acc) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x[s], y[s], acc, 0, 0, 0);
-    return acc;
-}
+        for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x[s], y[s], acc, 0, 0, 0);
+        return acc;
+    }
+};
+
+// Register passes over dk in G1: the raw Q and K registers of one pass
+// stay within 128 per lane, so two waves fit on a SIMD and one computes
+// while the other waits for its loads.
+template <typename in_t, int DK>
+struct PrepShape {
+    static constexpr int KP = DK / 32;   // k-tile pairs along dk
+    static constexpr int REGS_PER_PAIR = 2 * 4 * (int)sizeof(Raw8<in_t>) / 4;
+    static constexpr int NPASS = KP * REGS_PER_PAIR > 128 ? KP * REGS_PER_PAIR / 128 : 1;
+    static constexpr int PP = KP / NPASS;   // k-tile pairs per pass
+    static_assert(PP * NPASS == KP, "dk must split evenly into passes");
+};
+
+// Raw Q and K operand registers of one item (one pass over dk) and its
+// decay inputs.
+template <typename in_t, int PP>
+struct PrepRegs {
+    Raw8<in_t> k[4][PP], q[4][PP];
+    float la, bt;
+};
 
 template <typename in_t, typename OP, int DK>
 __global__ __launch_bounds__(64) void chunk_prep_kernel(int H, int T, int cpr, int urows,
@@ -242,12 +278,9 @@ __global__ __launch_bounds__(64) void chunk_prep_kernel(int H, int T, int cpr, i
                                                         OP *__restrict__ ws_m,
                                                         OP *__restrict__ ws_p) {
     using M = Mma<OP>;
-    constexpr int KP = DK / 32;   // k-tile pairs along dk
-    // Q and K registers of one pass over dk: at most 128 per lane.
-    constexpr int REGS_PER_PAIR = 2 * 4 * (int)sizeof(Raw8<in_t>) / 4;
-    constexpr int NPASS = KP * REGS_PER_PAIR > 128 ? KP * REGS_PER_PAIR / 128 : 1;
-    constexpr int PP = KP / NPASS;   // k-tile pairs per pass
-    static_assert(PP * NPASS == KP, "dk must split evenly into passes");
+    using L = PrepShape<in_t, DK>;
+    using MI = InvMma<OP>;
+    constexpr int NPASS = L::NPASS, PP = L::PP;
     constexpr int BP = kPrepBP, BS = kPrepBS;
     __shared__ __align__(16) float lds[kPrepLds];
     float *gs = lds, *bs = lds + C, *blk = lds + 2 * C;
@@ -256,54 +289,59 @@ __global__ __launch_bounds__(64) void chunk_prep_kernel(int H, int T, int cpr, i
     const int items = (cpr ? urows : meta[0]) * H;
     const int64_t tok_stride = (int64_t)H * DK;
 
-    for (int item = blockIdx.x; item < items; item += gridDim.x) {
+    // Issue the loads of pass s of an item (no waits).  Row indices are
+    // clamped to the sequence; process() zeroes the rows past its end.
+    auto load = [&](int item, int s, PrepRegs<in_t, PP> &R) {
         const int row = item / H, h = item % H;
+        int tok0, len;
+        row_span(row, T, cpr, row_tok, row_len, tok0, len);
+        if (s == 0) {
+            const int r = min(l, len - 1);
+            R.la = log_alpha[(int64_t)(tok0 + r) * H + h];
+            R.bt = beta[(int64_t)(tok0 + r) * H + h];
+        }
+        const int64_t base = ((int64_t)tok0 * H + h) * DK + 8 * jj + 32 * s * PP;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int64_t off = base + (int64_t)min(16 * b + nn, len - 1) * tok_stride;
+#pragma unroll
+            for (int p = 0; p < PP; ++p) R.k[b][p].load(k + off + 32 * p);
+        }
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int64_t off = base + (int64_t)min(16 * b + nn, len - 1) * tok_stride;
+#pragma unroll
+            for (int p = 0; p < PP; ++p) R.q[b][p].load(q + off + 32 * p);
+        }
+    };
+
+    // Everything of one item once pass 0 of its loads has been issued into R.
+    auto process = [&](int item, PrepRegs<in_t, PP> &R) {
+        const int row = item / H;
         int tok0, len;
         row_span(row, T, cpr, row_tok, row_len, tok0, len);
         const int64_t rh = item;   // == row * H + h
 
-        // Decay inputs, lane l = chunk row l.  Rows past the end of the
-        // sequence get log alpha = 0 and beta = 0 and zero Q and K rows: g
-        // stays flat there and those rows are inert in every product.
-        float la, bt;
-        {
-            const int r = min(l, len - 1);
-            la = log_alpha[(int64_t)(tok0 + r) * H + h];
-            bt = beta[(int64_t)(tok0 + r) * H + h];
-        }
-        const in_t *qb = q + ((int64_t)tok0 * H + h) * DK + 8 * jj;
-        const in_t *kb = k + ((int64_t)tok0 * H + h) * DK + 8 * jj;
-        int64_t roff[4];   // offset of the lane's row in each row block (clamped)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) roff[b] = (int64_t)min(16 * b + nn, len - 1) * tok_stride;
-
-        Raw8<in_t> kr[4][PP], qr[4][PP];
-        auto load_pass = [&](int s) {
-#pragma unroll
-            for (int p = 0; p < PP; ++p)
-#pragma unroll
-                for (int b = 0; b < 4; ++b) kr[b][p].load(kb + roff[b] + 32 * (s * PP + p));
-#pragma unroll
-            for (int p = 0; p < PP; ++p)
-#pragma unroll
-                for (int b = 0; b < 4; ++b) qr[b][p].load(qb + roff[b] + 32 * (s * PP + p));
+        // Rows past the end of the sequence get log alpha = 0, beta = 0 and
+        // zero Q and K rows: g stays flat there and those rows are inert in
+        // every product.
+        auto mask_rows = [&]() {
             if (len < C) {
 #pragma unroll
                 for (int b = 0; b < 4; ++b)
                     if (16 * b + nn >= len)
 #pragma unroll
                         for (int p = 0; p < PP; ++p) {
-                            kr[b][p].zero();
-                            qr[b][p].zero();
+                            R.k[b][p].zero();
+                            R.q[b][p].zero();
                         }
             }
         };
-        load_pass(0);
-
+        float la = R.la, bt = R.bt;
         if (l >= len) la = bt = 0.f;
         const float g = wave_inclusive_scan(la);
         const float g_last = __shfl(g, C - 1, 64);
-        gs[l] = g;
+        gs[l] = g * kLog2e;   // base-2 units for the decay masks
         bs[l] = bt;
         ws_g[rh * 2 * C + l] = expf(g);               // gamma_r: decay from the chunk start
         ws_g[rh * 2 * C + C + l] = expf(g_last - g);  // kappa_r: decay from row r to the chunk end
@@ -317,21 +355,22 @@ __global__ __launch_bounds__(64) void chunk_prep_kernel(int H, int T, int cpr, i
         for (int s = 0; s < NPASS; ++s) {
             if (s > 0) {
                 __builtin_amdgcn_sched_barrier(0);
-                load_pass(s);
+                load(item, s, R);
             }
+            mask_rows();
 #pragma unroll
             for (int t = 0; t < kTriTiles; ++t) {
                 int a, b;
                 tri_decode(t, a, b);
 #pragma unroll
                 for (int p = 0; p < PP; ++p) {
-                    gram_mma(gacc[t], kr[b][p], kr[a][p]);
-                    gram_mma(pacc[t], kr[b][p], qr[a][p]);
+                    gram_mma(gacc[t], R.k[b][p], R.k[a][p]);
+                    gram_mma(pacc[t], R.k[b][p], R.q[a][p]);
                 }
             }
         }
 
-        // Decay masks.  Off-diagonal tiles: row r = 16a + n, columns
+        // Decay masks (g in base-2 units).  Off-diagonal tiles: row r = 16a + n, columns
         // c = 16b + 4j + i < r, one exponential shared by P and A.  Diagonal
         // tiles: the lane's positions with c <= r belong to P; the others
         // give N^T[n][c - 16a] = A[c][r] of the same block, whose decay is
@@ -342,7 +381,7 @@ __global__ __launch_bounds__(64) void chunk_prep_kernel(int H, int T, int cpr, i
             gr[a] = gs[16 * a + nn];
             br[a] = bs[16 * a + nn];
         }
-        float4_t aR[kTriTiles];   // R(A_ab) for a > b
+        float4_t aR[kTriTiles];   // R(-A_ab) for a > b
 #pragma unroll
         for (int t = 0; t < kTriTiles; ++t) {
             int a, b;
@@ -352,9 +391,9 @@ __global__ __launch_bounds__(64) void chunk_prep_kernel(int H, int T, int cpr, i
             if (a > b) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float e = exp_neg(gr[a] - gc[i]);
+                    const float e = exp2_neg(gr[a] - gc[i]);
                     pv[i] = e * pacc[t][i];
-                    av[i] = br[a] * e * gacc[t][i];
+                    av[i] = -br[a] * e * gacc[t][i];
                 }
                 aR[t] = av;
             } else {
@@ -363,7 +402,7 @@ __global__ __launch_bounds__(64) void chunk_prep_kernel(int H, int T, int cpr, i
                 for (int i = 0; i < 4; ++i) {
                     const bool lower = 4 * jj + i <= nn;
                     const float x = gr[a] - gc[i];
-                    const float e = exp_neg(lower ? x : -x);
+                    const float e = exp2_neg(lower ? x : -x);
                     pv[i] = lower ? e * pacc[t][i] : 0.f;
                     av[i] = lower ? 0.f : bc[i] * e * gacc[t][i];
                 }
@@ -412,22 +451,24 @@ __global__ __launch_bounds__(64) void chunk_prep_kernel(int H, int T, int cpr, i
         float4_t TR[kTriTiles];   // R(T_ab)
 #pragma unroll
         for (int a = 0; a < 4; ++a) TR[tri_index(a, a)] = tR[a];
-        float4_t U, C10, C21, C20;
-        U = mm16(aR[tri_index(1, 0)], tC[0], z);
-        TR[tri_index(1, 0)] = -mm16(U, tR[1], z);
-        C10 = -mm16(tR[1], U, z);
-        U = mm16(aR[tri_index(2, 1)], tC[1], z);
-        TR[tri_index(2, 1)] = -mm16(U, tR[2], z);
-        C21 = -mm16(tR[2], U, z);
-        U = mm16(aR[tri_index(3, 2)], tC[2], z);
-        TR[tri_index(3, 2)] = -mm16(U, tR[3], z);
-        U = mm16(aR[tri_index(2, 1)], C10, mm16(aR[tri_index(2, 0)], tC[0], z));
-        TR[tri_index(2, 0)] = -mm16(U, tR[2], z);
-        C20 = -mm16(tR[2], U, z);
-        U = mm16(aR[tri_index(3, 2)], C21, mm16(aR[tri_index(3, 1)], tC[1], z));
-        TR[tri_index(3, 1)] = -mm16(U, tR[3], z);
-        U = mm16(aR[tri_index(3, 2)], C20, mm16(aR[tri_index(3, 1)], C10, mm16(aR[tri_index(3, 0)], tC[0], z)));
-        TR[tri_index(3, 0)] = -mm16(U, tR[3], z);
+        // W = -U_ab (from the negated A tiles); T_ab = T_aa W in R layout, and
+        // in C layout where a later U needs it.
+        float4_t W, C10, C21, C20;
+        W = MI::mm(aR[tri_index(1, 0)], tC[0], z);
+        TR[tri_index(1, 0)] = MI::mm(W, tR[1], z);
+        C10 = MI::mm(tR[1], W, z);
+        W = MI::mm(aR[tri_index(2, 1)], tC[1], z);
+        TR[tri_index(2, 1)] = MI::mm(W, tR[2], z);
+        C21 = MI::mm(tR[2], W, z);
+        W = MI::mm(aR[tri_index(3, 2)], tC[2], z);
+        TR[tri_index(3, 2)] = MI::mm(W, tR[3], z);
+        W = MI::mm(aR[tri_index(2, 1)], C10, MI::mm(aR[tri_index(2, 0)], tC[0], z));
+        TR[tri_index(2, 0)] = MI::mm(W, tR[2], z);
+        C20 = MI::mm(tR[2], W, z);
+        W = MI::mm(aR[tri_index(3, 2)], C21, MI::mm(aR[tri_index(3, 1)], tC[1], z));
+        TR[tri_index(3, 1)] = MI::mm(W, tR[3], z);
+        W = MI::mm(aR[tri_index(3, 2)], C20, MI::mm(aR[tri_index(3, 1)], C10, MI::mm(aR[tri_index(3, 0)], tC[0], z)));
+        TR[tri_index(3, 0)] = MI::mm(W, tR[3], z);
 
         // M = T diag(beta), R layout = fragment order.
 #pragma unroll
@@ -441,6 +482,12 @@ __global__ __launch_bounds__(64) void chunk_prep_kernel(int H, int T, int cpr, i
             *reinterpret_cast<typename M::frag *>(ws_m + (rh * kTriTiles + t) * kTileElems + 4 * l) = M::cvt(mv);
         }
         asm volatile("" ::: "memory");   // LDS is reused by the wave's next item
+    };
+
+    PrepRegs<in_t, PP> R;
+    for (int item = blockIdx.x; item < items; item += gridDim.x) {
+        load(item, 0, R);
+        process(item, R);
     }
 }
 
@@ -1101,7 +1148,8 @@ ChunkWorkspace chunk_workspace_layout(int32_t B, int32_t T, int32_t N, bool pack
 // compute waves per block, so the block count is what matters: the fewest
 // waves (at least 2) whose blocks still fit on the GPU in one round; 4 when
 // no choice does.  GDN_STATE_WAVES (1, 2 or 4) overrides, for experiments.
-static int state_waves_per_block(int DV, int64_t NH) {
+// Compute units of the current device (cached after the first query).
+static int cu_count() {
     static int cus = 0;
     if (cus == 0) {
         int dev = 0, n = 0;
@@ -1110,6 +1158,11 @@ static int state_waves_per_block(int DV, int64_t NH) {
             n = 256;
         cus = n;
     }
+    return cus;
+}
+
+static int state_waves_per_block(int DV, int64_t NH) {
+    const int cus = cu_count();
     const int tiles = (DV + 15) / 16;
     const int64_t slots = ((NH + 7) / 8) * 8;
     int nw = 4;
