@@ -93,12 +93,13 @@ def run_prefill(args, gdn, W, dev):
     B, T, H, dk, dv = inp.B, inp.T, inp.H, inp.dk, inp.dv
     q, k, v = (_to(x, dev, torch.bfloat16) for x in (inp.q, inp.k, inp.v))
     la, be = _to(inp.log_alpha, dev, torch.float32), _to(inp.beta, dev, torch.float32)
-    o = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
+    odt = {"fp32": torch.float32, "bf16": torch.bfloat16}[args.out_dtype]
+    o = torch.empty((B, T, H, dv), dtype=odt, device=dev)
     fin = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
-    ws = torch.empty(gdn.chunk_fwd_workspace_size(B, T, H, dk, dv, B), dtype=torch.uint8, device=dev)
+    ws = torch.empty(gdn.chunk_fwd_workspace_size(B, T, H, dk, dv, B, out_dtype=odt), dtype=torch.uint8, device=dev)
 
     def step():
-        gdn.chunk_fwd(q, k, v, la, be, o=o, final_state=fin, workspace=ws)
+        gdn.chunk_fwd(q, k, v, la, be, o=o, final_state=fin, workspace=ws, out_dtype=odt)
 
     for _ in range(args.warmup):
         step()
@@ -119,7 +120,7 @@ def run_prefill(args, gdn, W, dev):
     kernels = {name: {"launches": n, "avg_us": 1e3 * ms / n} for name, (n, ms) in prof.results.items()}
 
     flops = chunk_flops_per_token_head(dk, dv) * B * T * H
-    min_bytes = chunk_min_bytes(B, T, H, dk, dv, B, 2, 4, False, True)
+    min_bytes = chunk_min_bytes(B, T, H, dk, dv, B, 2, o.element_size(), False, True)
     dom = max(kernels, key=lambda n: kernels[n]["avg_us"] * kernels[n]["launches"])
     dom_s = kernels[dom]["avg_us"] * 1e-6
     path_s = ms_per_step * 1e-3
@@ -139,7 +140,7 @@ def run_prefill(args, gdn, W, dev):
     }
     res = {"value": B * T / path_s, "ms_per_step": ms_per_step, "roofline": roofline, "kernels": kernels,
            "config": {"workload": "prefill", "B": B, "L": T, "H": H, "dk": dk, "dv": dv, "chunk": C,
-                      "in_dtype": "bf16", "out_dtype": "fp32", "init_state": None, "final_state": "fp32"}}
+                      "in_dtype": "bf16", "out_dtype": args.out_dtype, "init_state": None, "final_state": "fp32"}}
     del q, k, v, la, be, o, fin, ws
     torch.cuda.empty_cache()
     return res, inp
@@ -220,6 +221,8 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--out-dtype", choices=["fp32", "bf16"], default="fp32",
+                    help="prefill output dtype (the state is fp32 either way)")
     ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None,
                     help="run one leg only (for profiler runs) and print its part of the line; "
                          "'copy' runs a plain 256 MiB read + 256 MiB write elementwise kernel used to "
