@@ -23,13 +23,16 @@
 // per-chunk matrices handed from G1 to G2 at C x C size.
 //
 // Kernels (all launched on the caller's stream):
-//   G0 chunk_table_kernel  one block: validates cu_seqlens and lays out the
-//                          (sequence, chunk) rows.
-//   G1 chunk_prep_kernel   one block per (chunk row, head), fully parallel:
+//   G0 chunk_table_kernel  packed batches only, one block: validates
+//                          cu_seqlens and lays out the (sequence, chunk)
+//                          rows.  Equal-length batches derive a row's span
+//                          from its index.
+//   G1 chunk_prep_kernel   one wave per (chunk row, head), fully parallel:
 //                          cumulative log-decay g, the decay-masked Q K^T
-//                          block P, A, T = (I + A)^{-1} by blocked forward
-//                          substitution in LDS (fp32), and M = T diag(beta).
-//                          Writes g, M, P to the workspace.
+//                          block P, A, T = (I + A)^{-1} (diagonal 16x16
+//                          blocks by back substitution, the rest by blocked
+//                          products), and M = T diag(beta).  Writes the decay
+//                          factors, M and P to the workspace.
 //   G2 chunk_state_kernel  one block per (sequence, head, value tile), serial
 //                          over the sequence's chunks.  Each wave owns 16
 //                          value columns and keeps its slice of S^T in
