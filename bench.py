@@ -184,6 +184,56 @@ def run_decode(args, gdn, W, dev):
     return res
 
 
+def run_continuation(args, gdn, W, dev):
+    """256 resident (sequence, head) state sets take 2..16 tokens each in one packed chunked call,
+    final states written over the initial ones; repeated calls keep appending the same tokens."""
+    import torch
+    inp = W.continuation()
+    T, H, dk, dv, N = inp.T, inp.H, inp.dk, inp.dv, inp.num_seqs
+    q, k, v = (_to(x, dev, torch.bfloat16) for x in (inp.q, inp.k, inp.v))
+    la, be = _to(inp.log_alpha, dev, torch.float32), _to(inp.beta, dev, torch.float32)
+    cu = torch.from_numpy(inp.cu_seqlens).to(dev)
+    state = _to(inp.init_state, dev, torch.float32)
+    o = torch.empty((1, T, H, dv), dtype=torch.float32, device=dev)
+    ws = torch.empty(gdn.chunk_fwd_workspace_size(1, T, H, dk, dv, N), dtype=torch.uint8, device=dev)
+
+    def step():
+        gdn.chunk_fwd(q, k, v, la, be, init_state=state, cu_seqlens=cu, o=o, final_state=state, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(args.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    with gdn.profile() as prof:
+        for _ in range(args.steps):
+            step()
+    torch.cuda.synchronize()
+    kernels = {name: {"launches": n, "avg_us": 1e3 * t / n} for name, (n, t) in prof.results.items()}
+    nbytes = chunk_min_bytes(1, T, H, dk, dv, N, 2, 4, True, True)
+    dom = max(kernels, key=lambda n: kernels[n]["avg_us"] * kernels[n]["launches"])
+    dom_s = kernels[dom]["avg_us"] * 1e-6
+    lens = inp.cu_seqlens[1:] - inp.cu_seqlens[:-1]
+    res = {
+        "value": T / (ms * 1e-3), "unit": "tokens/s", "ms_per_call": ms, "calls": args.steps,
+        "config": {"workload": "continuation", "N": int(N), "H": int(H), "dk": int(dk), "dv": int(dv),
+                   "tokens": int(T), "lengths": f"{int(lens.min())}..{int(lens.max())}", "in_dtype": "bf16",
+                   "out_dtype": "fp32", "state": "fp32, initial and final aliased in place"},
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": nbytes / dom_s / 1e9, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": nbytes / dom_s / 1e9 / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes": nbytes, "path_hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        "kernels": kernels,
+    }
+    del q, k, v, la, be, cu, state, o, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def run_cpu_baseline(args, inp):
     """The fp64 oracle on the prefill workload's inputs: a prefix of every sequence, grown until one
     pass takes about --cpu-seconds; once the prefix is the whole workload, whole passes are repeated
@@ -223,7 +273,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--out-dtype", choices=["fp32", "bf16"], default="fp32",
                     help="prefill output dtype (the state is fp32 either way)")
-    ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "continuation", "copy"], default=None,
                     help="run one leg only (for profiler runs) and print its part of the line; "
                          "'copy' runs a plain 256 MiB read + 256 MiB write elementwise kernel used to "
                          "calibrate the FETCH_SIZE / WRITE_SIZE counters")
@@ -249,6 +299,9 @@ def main():
     if args.only == "decode":
         print(json.dumps({"decode": run_decode(args, gdn, W, dev)}), flush=True)
         return
+    if args.only == "continuation":
+        print(json.dumps({"continuation": run_continuation(args, gdn, W, dev)}), flush=True)
+        return
     if args.only == "copy":
         n = 64 * 1024 * 1024                      # 256 MiB of fp32
         a = torch.ones(n, dtype=torch.float32, device=dev)
@@ -264,6 +317,7 @@ def main():
         print(json.dumps({"prefill": pre}), flush=True)
         return
     decode = run_decode(args, gdn, W, dev)
+    cont = run_continuation(args, gdn, W, dev)
     cpu = None if args.no_cpu_baseline else run_cpu_baseline(args, inp)
     out = {
         "metric": METRIC,
@@ -283,6 +337,7 @@ def main():
         "roofline": pre["roofline"],
         "cpu_baseline": cpu,
         "decode": decode,
+        "continuation": cont,
         "kernels": pre["kernels"],
         "device": torch.cuda.get_device_name(0),
     }

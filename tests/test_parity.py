@@ -125,6 +125,23 @@ def test_workload_packed_sampled():
     check_parity(inp, o, S, heads=[5])
 
 
+def test_workload_continuation():
+    """Continuation at serving shape: 256 resident state sets x 16 heads take
+    2..16 tokens each in one packed call, final states written over the
+    initial ones; every fifth sequence (all heads) against the oracle."""
+    import gated_delta_rule_24_amd as gdn
+    inp = W.continuation()
+    lens = np.diff(inp.cu_seqlens)
+    log(f"[continuation] {len(lens)} sequences, {int(lens.sum())} tokens, lengths {lens.min()}..{lens.max()}")
+    q, k, v = (dev(x, torch.bfloat16) for x in (inp.q, inp.k, inp.v))
+    la, b = dev(inp.log_alpha), dev(inp.beta)
+    S = dev(inp.init_state)
+    o, S_out = gdn.chunk_fwd(q, k, v, la, b, init_state=S, cu_seqlens=dev(inp.cu_seqlens, torch.int32), final_state=S)
+    torch.cuda.synchronize()
+    assert S_out.data_ptr() == S.data_ptr()
+    check_parity(inp, o, S, seqs=range(0, len(lens), 5))
+
+
 def test_workload_decode_sampled():
     """The 256 x 16 decode workload: 1000 in-place steps on the GPU; the oracle
     follows a sample of (sequence, head) states and is compared at steps

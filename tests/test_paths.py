@@ -72,6 +72,29 @@ def test_decode_continues_chunked_state():
     assert max(e1, e2, e3) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("Ktok", [2, 16])
+def test_continuation_equals_decode_steps(Ktok):
+    """Serving shape (256 resident states x 16 heads): appending Ktok tokens to
+    every state with one packed chunked call, states updated in place, agrees
+    with Ktok single-token decode steps on a copy of the same states."""
+    N, H = 256, 16
+    inp = W.packed_inputs([Ktok] * N, H=H, dk=128, dv=128, in_dtype="bf16", seed=40 + Ktok)
+    q, k, v, la, b = _dev_inputs(inp)
+    cu = dev(inp.cu_seqlens, torch.int32)
+    S_chunk = dev(inp.init_state)
+    o_chunk, _ = gdn.chunk_fwd(q, k, v, la, b, init_state=S_chunk, cu_seqlens=cu, final_state=S_chunk)
+    state = dev(inp.init_state)
+    tok = lambda x, t: x[0].reshape(N, Ktok, *x.shape[2:])[:, t].contiguous()
+    outs = [gdn.decode_step(state, tok(q, t), tok(k, t), tok(v, t), tok(la, t), tok(b, t)) for t in range(Ktok)]
+    o_dec = torch.stack(outs, dim=1).reshape(1, N * Ktok, H, 128)
+    torch.cuda.synchronize()
+    rms = float(o_chunk.float().pow(2).mean().sqrt())
+    e_o = float((o_dec - o_chunk).abs().max()) / rms
+    e_s = float((state - S_chunk).abs().max()) / rms
+    log(f"[continuation K={Ktok}] chunk vs {Ktok} decode steps: o {e_o:.2e} S {e_s:.2e} (rms {rms:.3f})")
+    assert max(e_o, e_s) <= TOL["bf16"]
+
+
 def test_packed_equals_separate_bitwise():
     lens = [70, 1, 0, 129, 64, 33]
     inp = W.packed_inputs(lens, H=2, dk=128, dv=128, in_dtype="bf16", seed=33)

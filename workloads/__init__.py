@@ -196,6 +196,17 @@ def packed():
                         name="packed", rng=rng)
 
 
+def continuation():
+    """Serving-shape continuation: 256 resident (sequence, head) state sets each
+    take 2..16 new tokens in one packed chunked call, the final states written
+    over the initial ones.  The lengths are the first draws of the generator."""
+    rng = np.random.Generator(np.random.PCG64(6))
+    lengths = rng.integers(2, 16, size=256, endpoint=True)
+    return chunk_inputs(1, int(lengths.sum()), 16, 128, 128, "bf16", seed=6,
+                        lengths=[int(x) for x in lengths], init_std=INIT_STATE_STD,
+                        name="continuation", rng=rng)
+
+
 @dataclasses.dataclass
 class DecodeInputs:
     """Resident states plus a pool of single-token step inputs.
@@ -242,4 +253,5 @@ WORKLOADS = {
     "long": long_context,
     "packed": packed,
     "decode": decode,
+    "continuation": continuation,
 }
