@@ -25,6 +25,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CHUNK = 64
 
 GDN_FP32, GDN_BF16, GDN_FP16 = 0, 1, 2
+GDN_QK_L2NORM = 1
 _DT = {torch.float32: GDN_FP32, torch.bfloat16: GDN_BF16, torch.float16: GDN_FP16}
 _STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_DTYPE", 4: "GDN_ERR_ALIGN",
            5: "GDN_ERR_UNSUPPORTED", 6: "GDN_ERR_WORKSPACE", 7: "GDN_ERR_HIP", 8: "GDN_ERR_ALIAS",
@@ -41,7 +42,8 @@ class GdnError(RuntimeError):
 class ChunkDesc(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("seqlen", ctypes.c_int32), ("heads", ctypes.c_int32),
                 ("dk", ctypes.c_int32), ("dv", ctypes.c_int32), ("num_seqs", ctypes.c_int32),
-                ("chunk", ctypes.c_int32), ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32)]
+                ("chunk", ctypes.c_int32), ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+                ("flags", ctypes.c_int32)]
 
 
 def lib_path() -> str:
@@ -73,7 +75,7 @@ def load():
     lib.gdn_chunk_fwd_check.restype = ctypes.c_int
     lib.gdn_chunk_fwd_check.argtypes = [vp, vp, ctypes.POINTER(i32)]
     lib.gdn_decode_step.restype = ctypes.c_int
-    lib.gdn_decode_step.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.gdn_decode_step.argtypes = [i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.gdn_profile_enable.restype = ctypes.c_int
     lib.gdn_profile_enable.argtypes = [i32]
     lib.gdn_profile_count.restype = ctypes.c_int
@@ -81,7 +83,7 @@ def load():
     lib.gdn_profile_read.restype = ctypes.c_int
     lib.gdn_profile_read.argtypes = [i32, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_int64),
                                      ctypes.POINTER(ctypes.c_double)]
-    if lib.gdn_abi_version() != 1:
+    if lib.gdn_abi_version() != 2:
         raise RuntimeError(f"{p}: unexpected ABI version {lib.gdn_abi_version()}")
     _lib = lib
     return lib
@@ -113,8 +115,8 @@ def _need(t, name, dtypes, device, ndim):
         raise ValueError(f"{name} must be contiguous")
 
 
-def _desc(B, T, H, dk, dv, N, in_dt, out_dt, chunk=CHUNK):
-    return ChunkDesc(B, T, H, dk, dv, N, chunk, in_dt, out_dt)
+def _desc(B, T, H, dk, dv, N, in_dt, out_dt, chunk=CHUNK, flags=0):
+    return ChunkDesc(B, T, H, dk, dv, N, chunk, in_dt, out_dt, flags)
 
 
 def chunk_fwd_workspace_size(B, T, H, dk, dv, num_seqs, in_dtype=torch.bfloat16, out_dtype=torch.float32,
@@ -126,14 +128,15 @@ def chunk_fwd_workspace_size(B, T, H, dk, dv, num_seqs, in_dtype=torch.bfloat16,
 
 
 def chunk_fwd(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, *, out_dtype=torch.float32,
-              o=None, final_state=True, workspace=None, chunk=CHUNK):
+              o=None, final_state=True, workspace=None, chunk=CHUNK, qk_l2norm=False):
     """Chunkwise-parallel prefill.
 
     q, k [B,T,H,dk], v [B,T,H,dv] (fp32/bf16/fp16, same dtype);
     log_alpha, beta [B,T,H] fp32; init_state [N,H,dv,dk] fp32 or None;
     cu_seqlens int32 [N+1] (packed batch, B == 1) or None.
     final_state: True (allocate), False/None (not returned) or a tensor to
-    write (it may be init_state itself).  Returns (o, final_state or None).
+    write (it may be init_state itself).  qk_l2norm: normalise q and k per
+    (token, head) inside the kernels.  Returns (o, final_state or None).
     """
     lib = load()
     dev = q.device
@@ -172,7 +175,7 @@ def chunk_fwd(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, *, out
         _need(final_state, "final_state", (torch.float32,), dev, 4)
         if tuple(final_state.shape) != (N, H, dv, dk):
             raise ValueError("final_state has the wrong shape")
-    desc = _desc(B, T, H, dk, dv, N, _DT[q.dtype], _DT[o.dtype], chunk)
+    desc = _desc(B, T, H, dk, dv, N, _DT[q.dtype], _DT[o.dtype], chunk, GDN_QK_L2NORM if qk_l2norm else 0)
     need = ctypes.c_size_t(0)
     _check(lib.gdn_chunk_fwd_workspace_size(ctypes.byref(desc), ctypes.byref(need)))
     if workspace is None:
@@ -193,9 +196,10 @@ def chunk_fwd_check(workspace: torch.Tensor) -> int:
     return int(code.value)
 
 
-def decode_step(state, q, k, v, log_alpha, beta, *, out_dtype=torch.float32, o=None):
+def decode_step(state, q, k, v, log_alpha, beta, *, out_dtype=torch.float32, o=None, qk_l2norm=False):
     """One decode step, in place on `state` [N,H,dv,dk] fp32.
-    q, k [N,H,dk], v [N,H,dv]; log_alpha, beta [N,H] fp32.  Returns o [N,H,dv]."""
+    q, k [N,H,dk], v [N,H,dv]; log_alpha, beta [N,H] fp32.  qk_l2norm:
+    normalise q and k inside the kernel.  Returns o [N,H,dv]."""
     lib = load()
     dev = state.device
     _need(state, "state", (torch.float32,), dev, 4)
@@ -214,7 +218,8 @@ def decode_step(state, q, k, v, log_alpha, beta, *, out_dtype=torch.float32, o=N
         o = torch.empty((N, H, dv), dtype=out_dtype, device=dev)
     else:
         _need(o, "o", dts, dev, 3)
-    _check(lib.gdn_decode_step(N, H, dk, dv, _DT[q.dtype], _DT[o.dtype], _ptr(state), _ptr(q), _ptr(k), _ptr(v),
+    _check(lib.gdn_decode_step(N, H, dk, dv, _DT[q.dtype], _DT[o.dtype], GDN_QK_L2NORM if qk_l2norm else 0,
+                               _ptr(state), _ptr(q), _ptr(k), _ptr(v),
                                _ptr(log_alpha), _ptr(beta), _ptr(o), _stream(dev)))
     return o
 

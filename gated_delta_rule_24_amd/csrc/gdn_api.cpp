@@ -70,6 +70,8 @@ void prof_clear_locked() {
     g_prof_records.clear();
 }
 
+static_assert(gdn::kFlagQkL2Norm == GDN_QK_L2NORM, "flag values");
+
 gdn_status check_chunk_desc(const gdn_chunk_desc *d) {
     if (!d) return fail(GDN_ERR_NULL, "desc is NULL");
     if (!valid_dtype(d->in_dtype) || !valid_dtype(d->out_dtype))
@@ -86,6 +88,7 @@ gdn_status check_chunk_desc(const gdn_chunk_desc *d) {
     if (!dk_ok) return fail(GDN_ERR_UNSUPPORTED, "dk %d not built for this input dtype", d->dk);
     if (d->dv % 16 != 0 || d->dv > 1024)
         return fail(GDN_ERR_UNSUPPORTED, "dv %d not built (multiple of 16, at most 1024)", d->dv);
+    if (d->flags & ~GDN_QK_L2NORM) return fail(GDN_ERR_UNSUPPORTED, "unknown flags 0x%x", d->flags);
     return GDN_OK;
 }
 
@@ -197,7 +200,7 @@ gdn_status gdn_chunk_fwd(const gdn_chunk_desc *desc, const void *q, const void *
     for (int i = 0; i < 8; ++i)
         if (overlap(r_ws, ins[i])) return fail(GDN_ERR_ALIAS, "workspace overlaps %s", ins[i].name);
 
-    gdn::ChunkArgs a{d.batch, d.seqlen, d.heads, d.dk, d.dv, d.num_seqs, d.in_dtype, d.out_dtype,
+    gdn::ChunkArgs a{d.batch, d.seqlen, d.heads, d.dk, d.dv, d.num_seqs, d.in_dtype, d.out_dtype, d.flags,
                      q, k, v, log_alpha, beta, init_state, cu_seqlens, o, final_state, workspace};
     hipError_t e = gdn::launch_chunk_fwd(a, stream);
     if (e != hipSuccess) return hip_fail(e, "gdn_chunk_fwd launch");
@@ -217,7 +220,7 @@ gdn_status gdn_chunk_fwd_check(const void *workspace, hipStream_t stream, int32_
 }
 
 gdn_status gdn_decode_step(int32_t N, int32_t H, int32_t dk, int32_t dv, int32_t in_dtype, int32_t out_dtype,
-                           float *state, const void *q, const void *k, const void *v, const float *log_alpha,
+                           int32_t flags, float *state, const void *q, const void *k, const void *v, const float *log_alpha,
                            const float *beta, void *o, hipStream_t stream) {
     if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype))
         return fail(GDN_ERR_DTYPE, "unknown dtype code (in %d, out %d)", in_dtype, out_dtype);
@@ -225,6 +228,7 @@ gdn_status gdn_decode_step(int32_t N, int32_t H, int32_t dk, int32_t dv, int32_t
     if (dv > 4096) return fail(GDN_ERR_UNSUPPORTED, "dv %d not built (at most 4096)", dv);
     if (!(dk == 32 || dk == 64 || dk == 128 || dk == 256))
         return fail(GDN_ERR_UNSUPPORTED, "dk %d not built (32, 64, 128, 256)", dk);
+    if (flags & ~GDN_QK_L2NORM) return fail(GDN_ERR_UNSUPPORTED, "unknown flags 0x%x", flags);
     if ((int64_t)N * H > INT32_MAX) return fail(GDN_ERR_SHAPE, "N * H too large");
     if ((int64_t)N * H == 0) return ok();
     if (!state || !q || !k || !v || !log_alpha || !beta || !o)
@@ -243,7 +247,7 @@ gdn_status gdn_decode_step(int32_t N, int32_t H, int32_t dk, int32_t dv, int32_t
         if (overlap(r_o, r)) return fail(GDN_ERR_ALIAS, "o overlaps %s", r.name);
     for (int i = 1; i < 6; ++i)
         if (overlap(others[0], others[i])) return fail(GDN_ERR_ALIAS, "state overlaps %s", others[i].name);
-    gdn::DecodeArgs a{N, H, dk, dv, in_dtype, out_dtype, state, q, k, v, log_alpha, beta, o};
+    gdn::DecodeArgs a{N, H, dk, dv, in_dtype, out_dtype, flags, state, q, k, v, log_alpha, beta, o};
     hipError_t e = gdn::launch_decode_step(a, stream);
     if (e != hipSuccess) return hip_fail(e, "gdn_decode_step launch");
     return ok();

@@ -197,13 +197,14 @@ __device__ __forceinline__ void row_span(int row, int T, int cpr, const int32_t 
 constexpr float kLog2e = 1.4426950408889634f;
 __device__ __forceinline__ float exp2_neg(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// LDS of one G1 wave, in floats: g and beta of the 64 rows, then four 16 x 16
-// blocks (N^T of each diagonal block during the solve, T_aa after it).  Row
-// pitch 20 and block pitch 324 keep the 16-byte row reads, the column reads
-// and the four-block broadcast reads free of bank conflicts.
+// LDS of one G1 wave, in floats: g, beta and the reciprocal row norms of Q and
+// K for the 64 rows, then four 16 x 16 blocks (N^T of each diagonal block
+// during the solve, T_aa after it).  Row pitch 20 and block pitch 324 keep the
+// 16-byte row reads, the column reads and the four-block broadcast reads free
+// of bank conflicts.
 constexpr int kPrepBP = 20;
 constexpr int kPrepBS = 16 * kPrepBP + 4;
-constexpr int kPrepLds = 2 * C + 4 * kPrepBS;
+constexpr int kPrepLds = 4 * C + 4 * kPrepBS;
 
 // acc += (row block X) (row block Y)^T over one k-tile pair of raw inputs.
 // bf16 and fp16 rows use their own 16x16x32 instruction (exact products,
@@ -269,7 +270,7 @@ struct PrepRegs {
 };
 
 template <typename in_t, typename OP, int DK>
-__global__ __launch_bounds__(64) void chunk_prep_kernel(int H, int T, int cpr, int urows,
+__global__ __launch_bounds__(64) void chunk_prep_kernel(int H, int T, int cpr, int urows, int qk_norm,
                                                         const int32_t *__restrict__ meta,
                                                         const int32_t *__restrict__ row_tok,
                                                         const int32_t *__restrict__ row_len,
@@ -286,7 +287,7 @@ __global__ __launch_bounds__(64) void chunk_prep_kernel(int H, int T, int cpr, i
     constexpr int NPASS = L::NPASS, PP = L::PP;
     constexpr int BP = kPrepBP, BS = kPrepBS;
     __shared__ __align__(16) float lds[kPrepLds];
-    float *gs = lds, *bs = lds + C, *blk = lds + 2 * C;
+    float *gs = lds, *bs = lds + C, *qn = lds + 2 * C, *kn = lds + 3 * C, *blk = lds + 4 * C;
 
     const int l = threadIdx.x, nn = l & 15, jj = l >> 4;
     const int items = (cpr ? urows : meta[0]) * H;
@@ -346,14 +347,15 @@ __global__ __launch_bounds__(64) void chunk_prep_kernel(int H, int T, int cpr, i
         const float g_last = __shfl(g, C - 1, 64);
         gs[l] = g * kLog2e;   // base-2 units for the decay masks
         bs[l] = bt;
-        ws_g[rh * 2 * C + l] = expf(g);               // gamma_r: decay from the chunk start
-        ws_g[rh * 2 * C + C + l] = expf(g_last - g);  // kappa_r: decay from row r to the chunk end
+        const float gam = expf(g);             // gamma_r: decay from the chunk start
+        const float kap = expf(g_last - g);    // kappa_r: decay from row r to the chunk end
 
         // Lower-triangular tiles (a, b), b <= a, of Q K^T and K K^T in R
         // layout: first operand row block b of K, second row block a.
         float4_t pacc[kTriTiles], gacc[kTriTiles];
 #pragma unroll
         for (int t = 0; t < kTriTiles; ++t) pacc[t] = gacc[t] = float4_t{0.f, 0.f, 0.f, 0.f};
+        float ssk[4] = {0.f, 0.f, 0.f, 0.f}, ssq[4] = {0.f, 0.f, 0.f, 0.f};   // row sums of squares
 #pragma unroll
         for (int s = 0; s < NPASS; ++s) {
             if (s > 0) {
@@ -361,6 +363,20 @@ __global__ __launch_bounds__(64) void chunk_prep_kernel(int H, int T, int cpr, i
                 load(item, s, R);
             }
             mask_rows();
+            if (qk_norm) {
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+#pragma unroll
+                    for (int p = 0; p < PP; ++p) {
+                        float f[8];
+                        R.k[b][p].to_f32(f);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) ssk[b] += f[e] * f[e];
+                        R.q[b][p].to_f32(f);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) ssq[b] += f[e] * f[e];
+                    }
+            }
 #pragma unroll
             for (int t = 0; t < kTriTiles; ++t) {
                 int a, b;
@@ -373,16 +389,49 @@ __global__ __launch_bounds__(64) void chunk_prep_kernel(int H, int T, int cpr, i
             }
         }
 
+        // L2 normalisation of the Q and K rows (when asked for) is applied as
+        // row and column factors of the products: Qn Kn^T = D_q (Q K^T) D_k
+        // with D = diag(1 / ||row||).  Lane (n, j) has the partial sums of
+        // squares of rows 16b + n over its dk pieces; the four lanes of a row
+        // add theirs.  A zero row keeps a factor of 0 (it stays zero).  The
+        // factors are 1 without normalisation.  Lane l keeps row l's.
+        float rq = 1.f, rk = 1.f;
+        if (qk_norm) {
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                ssk[b] += __shfl_xor(ssk[b], 16, 64);
+                ssk[b] += __shfl_xor(ssk[b], 32, 64);
+                ssq[b] += __shfl_xor(ssq[b], 16, 64);
+                ssq[b] += __shfl_xor(ssq[b], 32, 64);
+            }
+            const float sk = jj == 0 ? ssk[0] : (jj == 1 ? ssk[1] : (jj == 2 ? ssk[2] : ssk[3]));
+            const float sq = jj == 0 ? ssq[0] : (jj == 1 ? ssq[1] : (jj == 2 ? ssq[2] : ssq[3]));
+            rk = sk > 0.f ? rsqrtf(sk) : 0.f;
+            rq = sq > 0.f ? rsqrtf(sq) : 0.f;
+        }
+        qn[l] = rq;
+        kn[l] = rk;
+        // Decay factors for the state pass, with the normalisation folded in:
+        // gamma / ||k|| (scales K S^T in Y), kappa / ||k|| (the update), gamma
+        // / ||q|| (the output), and gamma itself (the chunk's total decay).
+        ws_g[rh * 4 * C + l] = gam * rk;
+        ws_g[rh * 4 * C + C + l] = kap * rk;
+        ws_g[rh * 4 * C + 2 * C + l] = gam * rq;
+        ws_g[rh * 4 * C + 3 * C + l] = gam;
+        asm volatile("" ::: "memory");
+
         // Decay masks (g in base-2 units).  Off-diagonal tiles: row r = 16a + n, columns
         // c = 16b + 4j + i < r, one exponential shared by P and A.  Diagonal
         // tiles: the lane's positions with c <= r belong to P; the others
         // give N^T[n][c - 16a] = A[c][r] of the same block, whose decay is
         // e^{g_c - g_r}, so again one exponential per position.
-        float gr[4], br[4];
+        float gr[4], br[4], iqr[4], ikr[4];
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
             gr[a] = gs[16 * a + nn];
             br[a] = bs[16 * a + nn];
+            iqr[a] = qn[16 * a + nn];
+            ikr[a] = kn[16 * a + nn];
         }
         float4_t aR[kTriTiles];   // R(-A_ab) for a > b
 #pragma unroll
@@ -390,13 +439,14 @@ __global__ __launch_bounds__(64) void chunk_prep_kernel(int H, int T, int cpr, i
             int a, b;
             tri_decode(t, a, b);
             const float4_t gc = *reinterpret_cast<const float4_t *>(gs + 16 * b + 4 * jj);
+            const float4_t kc = *reinterpret_cast<const float4_t *>(kn + 16 * b + 4 * jj);   // column factors
             float4_t pv, av;
             if (a > b) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float e = exp2_neg(gr[a] - gc[i]);
-                    pv[i] = e * pacc[t][i];
-                    av[i] = -br[a] * e * gacc[t][i];
+                    const float e = exp2_neg(gr[a] - gc[i]) * kc[i];
+                    pv[i] = e * iqr[a] * pacc[t][i];
+                    av[i] = -br[a] * ikr[a] * e * gacc[t][i];
                 }
                 aR[t] = av;
             } else {
@@ -405,9 +455,9 @@ __global__ __launch_bounds__(64) void chunk_prep_kernel(int H, int T, int cpr, i
                 for (int i = 0; i < 4; ++i) {
                     const bool lower = 4 * jj + i <= nn;
                     const float x = gr[a] - gc[i];
-                    const float e = exp2_neg(lower ? x : -x);
-                    pv[i] = lower ? e * pacc[t][i] : 0.f;
-                    av[i] = lower ? 0.f : bc[i] * e * gacc[t][i];
+                    const float e = exp2_neg(lower ? x : -x) * kc[i];
+                    pv[i] = lower ? e * iqr[a] * pacc[t][i] : 0.f;
+                    av[i] = lower ? 0.f : bc[i] * ikr[a] * e * gacc[t][i];
                 }
                 *reinterpret_cast<float4_t *>(blk + a * BS + nn * BP + 4 * jj) = av;
                 aR[t] = float4_t{0.f, 0.f, 0.f, 0.f};
@@ -538,7 +588,7 @@ struct StateSmem {
     static constexpr size_t QK = (size_t)C * QROW;                      // one Q or K block
     static constexpr size_t VB = (size_t)C * VROW;
     static constexpr size_t MP = sizeof(OP) * kTriTiles * kTileElems;   // one M or P block
-    static constexpr size_t GB = 1024;                                  // gamma, kappa, spare half
+    static constexpr size_t GB = 1024;                                  // the four decay vectors
     static constexpr size_t DMA = VB + 2 * MP + GB;                     // directly loaded inputs
     static constexpr int QKB = (4 * QK + 2 * DMA <= 160 * 1024) ? 2 : 1;   // Q/K buffers
     static constexpr size_t qk_off(int b) { return (size_t)b * 2 * QK; }   // Q, then K
@@ -764,7 +814,7 @@ __global__ __launch_bounds__(64 * (NW + kStagers)) void chunk_state_kernel(
     // ---- direct global -> LDS copies of V, M, P and the decay factors ----
     // Copy ii of a chunk (stager wave sw issues ii = sw, sw + kStagers, ...) fills LDS bytes
     // [1024 ii, 1024 ii + 1024) of the chunk's buffer: V blocks first, then
-    // M, P and the 2C decay factors.  Per-lane source offsets do not depend
+    // M, P and the 4C decay factors.  Per-lane source offsets do not depend
     // on the chunk and are computed once.  Rows past the end of a partial
     // chunk re-read the last valid row: M and P are exactly zero in those
     // rows and columns, so they stay inert.
@@ -782,7 +832,7 @@ __global__ __launch_bounds__(64 * (NW + kStagers)) void chunk_state_kernel(
         } else if (ii < L::NV + 2 * L::NM) {
             dsrc[kx] = ((ii - L::NV) % L::NM) * 1024 + 16 * l;
         } else {
-            dsrc[kx] = 16 * min(l, 2 * C / 4 - 1);
+            dsrc[kx] = 16 * l;
         }
     }
     auto dma = [&](int ci, int b) {
@@ -792,7 +842,7 @@ __global__ __launch_bounds__(64 * (NW + kStagers)) void chunk_state_kernel(
         const in_t *vc = v + ((int64_t)(tok0 + ci * C) * H + h) * DV;
         const unsigned char *mc = reinterpret_cast<const unsigned char *>(ws_m + rh * kTriTiles * kTileElems);
         const unsigned char *pc = reinterpret_cast<const unsigned char *>(ws_p + rh * kTriTiles * kTileElems);
-        const unsigned char *gc = reinterpret_cast<const unsigned char *>(ws_g + rh * 2 * C);
+        const unsigned char *gc = reinterpret_cast<const unsigned char *>(ws_g + rh * 4 * C);
 #pragma unroll
         for (int kx = 0; kx < KD; ++kx) {
             const int ii = sw + kStagers * kx;
@@ -917,8 +967,10 @@ __global__ __launch_bounds__(64 * (NW + kStagers)) void chunk_state_kernel(
         const unsigned char *Db = smem + L::dma_off(b);
         const OP *Ms = reinterpret_cast<const OP *>(Db + L::m_rel);
         const OP *Ps = reinterpret_cast<const OP *>(Db + L::p_rel);
-        const float *gam_s = reinterpret_cast<const float *>(Db + L::g_rel);   // gamma_r, then kappa_r
+        // decay factors (G1): gamma / ||k||, kappa / ||k||, gamma / ||q||, gamma
+        const float *gam_s = reinterpret_cast<const float *>(Db + L::g_rel);
         const float *kap_s = gam_s + C;
+        const float *gao_s = gam_s + 2 * C;
 
         // The chunk is software-pipelined: each phase issues the LDS reads of
         // a later phase before its own products, and the phases are pinned
@@ -957,7 +1009,7 @@ __global__ __launch_bounds__(64 * (NW + kStagers)) void chunk_state_kernel(
         // -- phase 0: K fragments, V, gamma; S as an operand; decay of S.
         // LDS reads complete in order, so gamma_C is read first: the decay
         // waits for it alone, not for the fragments behind it. --
-        const float gC = gam_s[C - 1];
+        const float gC = gam_s[4 * C - 1];
         F2 kf[WX];
 #pragma unroll
         for (int i = 0; i < WX; ++i) kf[i] = rd_row(Kb, i);
@@ -1064,7 +1116,7 @@ __global__ __launch_bounds__(64 * (NW + kStagers)) void chunk_state_kernel(
         for (int jx = 0; jx < 6; ++jx) ppair[jx] = tri_pair(Ps, PMT[jx], PP[jx]);
         float g1[4];
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) g1[rt] = gam_s[16 * rt + nn];
+        for (int rt = 0; rt < 4; ++rt) g1[rt] = gao_s[16 * rt + nn];
         __builtin_amdgcn_sched_barrier(0);
 
         // -- phase 7: rest of Q S^T, then V'^T P^T into a separate sum --
@@ -1139,7 +1191,7 @@ ChunkWorkspace chunk_workspace_layout(int32_t B, int32_t T, int32_t N, bool pack
     w.off_row0 = off;   off = align256(off + sizeof(int32_t) * (size_t)N);
     w.off_rowtok = off; off = align256(off + sizeof(int32_t) * (size_t)w.max_rows);
     w.off_rowlen = off; off = align256(off + sizeof(int32_t) * (size_t)w.max_rows);
-    w.off_g = off;      off = align256(off + sizeof(float) * (size_t)w.max_rows * H * 2 * C);
+    w.off_g = off;      off = align256(off + sizeof(float) * (size_t)w.max_rows * H * 4 * C);
     w.off_m = off;      off = align256(off + op * (size_t)w.max_rows * H * kTriTiles * kTileElems);
     w.off_p = off;      off = align256(off + op * (size_t)w.max_rows * H * kTriTiles * kTileElems);
     w.total = off;
@@ -1223,7 +1275,7 @@ static hipError_t launch_dk(const ChunkArgs &a, const ChunkWorkspace &w, hipStre
         const int64_t items = w.max_rows * a.H;
         const int64_t grid = items < (1 << 22) ? items : (1 << 22);
         chunk_prep_kernel<in_t, OP, DK><<<dim3((unsigned)grid), dim3(64), 0, st>>>(
-            a.H, a.T, uniform_cpr(a), (int)(uniform_cpr(a) ? w.max_rows : 0),
+            a.H, a.T, uniform_cpr(a), (int)(uniform_cpr(a) ? w.max_rows : 0), (a.flags & kFlagQkL2Norm) ? 1 : 0,
             reinterpret_cast<const int32_t *>(ws + w.off_meta),
             reinterpret_cast<const int32_t *>(ws + w.off_rowtok),
             reinterpret_cast<const int32_t *>(ws + w.off_rowlen), static_cast<const in_t *>(a.q),

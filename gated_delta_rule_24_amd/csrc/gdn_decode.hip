@@ -30,7 +30,7 @@ __device__ __forceinline__ float group_sum(float x) {
 }
 
 template <typename in_t, typename out_t, int DK>
-__global__ __launch_bounds__(256) void decode_step_kernel(int H, int DV, float *__restrict__ state,
+__global__ __launch_bounds__(256) void decode_step_kernel(int H, int DV, int qk_norm, float *__restrict__ state,
                                                           const in_t *__restrict__ q,
                                                           const in_t *__restrict__ k,
                                                           const in_t *__restrict__ v,
@@ -48,6 +48,23 @@ __global__ __launch_bounds__(256) void decode_step_kernel(int H, int DV, float *
     float kk[8], qq[8];
     load8_f32(k + nh * DK + sub * 8, kk);
     load8_f32(q + nh * DK + sub * 8, qq);
+    if (qk_norm) {
+        // q / ||q||, k / ||k|| (an all-zero vector stays zero)
+        float sk = 0.f, sq = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            sk += kk[e] * kk[e];
+            sq += qq[e] * qq[e];
+        }
+        sk = group_sum<TPR>(sk);
+        sq = group_sum<TPR>(sq);
+        const float rk = sk > 0.f ? rsqrtf(sk) : 0.f, rq = sq > 0.f ? rsqrtf(sq) : 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            kk[e] *= rk;
+            qq[e] *= rq;
+        }
+    }
     const float a = expf(log_alpha[nh]);
     const float b = beta[nh];
     float kq = 0.f;
@@ -112,16 +129,16 @@ static hipError_t decode_dispatch_dk(const DecodeArgs &d, hipStream_t st) {
     ProfScope prof("gdn_decode_step", st);
     switch (d.dk) {
     case 32:
-        decode_step_kernel<in_t, out_t, 32><<<grid, block, 0, st>>>(d.H, d.dv, d.state, q, k, v, d.log_alpha, d.beta, o);
+        decode_step_kernel<in_t, out_t, 32><<<grid, block, 0, st>>>(d.H, d.dv, (d.flags & kFlagQkL2Norm) ? 1 : 0, d.state, q, k, v, d.log_alpha, d.beta, o);
         break;
     case 64:
-        decode_step_kernel<in_t, out_t, 64><<<grid, block, 0, st>>>(d.H, d.dv, d.state, q, k, v, d.log_alpha, d.beta, o);
+        decode_step_kernel<in_t, out_t, 64><<<grid, block, 0, st>>>(d.H, d.dv, (d.flags & kFlagQkL2Norm) ? 1 : 0, d.state, q, k, v, d.log_alpha, d.beta, o);
         break;
     case 128:
-        decode_step_kernel<in_t, out_t, 128><<<grid, block, 0, st>>>(d.H, d.dv, d.state, q, k, v, d.log_alpha, d.beta, o);
+        decode_step_kernel<in_t, out_t, 128><<<grid, block, 0, st>>>(d.H, d.dv, (d.flags & kFlagQkL2Norm) ? 1 : 0, d.state, q, k, v, d.log_alpha, d.beta, o);
         break;
     case 256:
-        decode_step_kernel<in_t, out_t, 256><<<grid, block, 0, st>>>(d.H, d.dv, d.state, q, k, v, d.log_alpha, d.beta, o);
+        decode_step_kernel<in_t, out_t, 256><<<grid, block, 0, st>>>(d.H, d.dv, (d.flags & kFlagQkL2Norm) ? 1 : 0, d.state, q, k, v, d.log_alpha, d.beta, o);
         break;
     default:
         return hipErrorInvalidValue;

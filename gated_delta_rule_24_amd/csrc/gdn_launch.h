@@ -11,11 +11,12 @@ namespace gdn {
 enum DType : int32_t { DT_FP32 = 0, DT_BF16 = 1, DT_FP16 = 2 };
 
 constexpr int kChunk = 64;                  // chunk length C
+constexpr int32_t kFlagQkL2Norm = 1;        // GDN_QK_L2NORM
 constexpr int kTriTiles = 10;               // 16x16 tiles in the lower triangle of a C x C block
 constexpr int kTileElems = 256;             // 16 x 16
 
 struct DecodeArgs {
-    int32_t N, H, dk, dv, in_dtype, out_dtype;
+    int32_t N, H, dk, dv, in_dtype, out_dtype, flags;
     float *state;
     const void *q, *k, *v;
     const float *log_alpha, *beta;
@@ -23,7 +24,7 @@ struct DecodeArgs {
 };
 
 struct ChunkArgs {
-    int32_t B, T, H, dk, dv, N, in_dtype, out_dtype;
+    int32_t B, T, H, dk, dv, N, in_dtype, out_dtype, flags;
     const void *q, *k, *v;
     const float *log_alpha, *beta, *init_state;
     const int32_t *cu_seqlens;

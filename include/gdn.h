@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 1
+#define GDN_ABI_VERSION 2
 
 typedef enum {
     GDN_OK = 0,
@@ -82,6 +82,19 @@ typedef enum {
 } gdn_dtype;
 
 /*
+ * Options of gdn_chunk_fwd (gdn_chunk_desc.flags) and gdn_decode_step.
+ *   GDN_QK_L2NORM  q and k are L2-normalised per (token, head) inside the
+ *                  kernels, q / ||q||_2 and k / ||k||_2, as the Gated
+ *                  DeltaNet paper's token-mixing block does before the delta
+ *                  rule (section 3.3, "Token mixer block"; the paper notes
+ *                  list it for training stability).  The input buffers are
+ *                  not modified.  An all-zero vector stays zero.
+ */
+typedef enum {
+    GDN_QK_L2NORM = 1
+} gdn_flags;
+
+/*
  * Shape of one gdn_chunk_fwd call.
  *   batch     B  >= 1: batch rows.  Must be 1 when cu_seqlens is given.
  *   seqlen    T  >= 0: tokens per batch row (packed batch: total tokens).
@@ -96,6 +109,7 @@ typedef enum {
  *                the matrix products on fp16 operands with fp32 accumulation
  *                and an fp32 state; FP32 inputs run them on fp32 operands.
  *   out_dtype    dtype of o (FP32, BF16 or FP16).
+ *   flags        bitwise OR of gdn_flags (0: none).
  */
 typedef struct {
     int32_t batch;
@@ -107,6 +121,7 @@ typedef struct {
     int32_t chunk;
     int32_t in_dtype;   /* gdn_dtype */
     int32_t out_dtype;  /* gdn_dtype */
+    int32_t flags;      /* gdn_flags */
 } gdn_chunk_desc;
 
 /* ABI version of the loaded library (GDN_ABI_VERSION at build time). */
@@ -193,13 +208,14 @@ gdn_status gdn_chunk_fwd_check(const void *workspace, hipStream_t stream, int32_
  *   Sbar = alpha S;  u = beta (v - Sbar k);  S_t = Sbar + u k^T;
  *   o = alpha (S q) + u (k . q)
  * (tutorial page: forget first, then correct the error of the decayed
- * memory).  dk: a multiple of 8, 8..256.  dv: 1..4096.
+ * memory).  flags: 0 or GDN_QK_L2NORM (q and k normalised first).
+ * dk: 32, 64, 128 or 256.  dv: 1..4096.
  * o must not overlap state.
  * Errors: GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_DTYPE, GDN_ERR_ALIGN,
  * GDN_ERR_UNSUPPORTED, GDN_ERR_ALIAS, GDN_ERR_HIP.
  */
 gdn_status gdn_decode_step(int32_t N, int32_t H, int32_t dk, int32_t dv,
-                           int32_t in_dtype, int32_t out_dtype,
+                           int32_t in_dtype, int32_t out_dtype, int32_t flags,
                            float *state,
                            const void *q, const void *k, const void *v,
                            const float *log_alpha, const float *beta,

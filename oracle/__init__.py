@@ -14,14 +14,19 @@ Functions:
   step_strict(...)    one token with the input checks of the tutorial's
                       reference step function (shape, finiteness, gates in
                       [0, 1], unit key)
+  l2_normalise(x)     x / ||x||_2 per vector (fp64), the q/k normalisation of
+                      the paper's token-mixer block; recurrent(...,
+                      qk_l2norm=True) applies it to q and k first
 
 Parity pins (all in tests/test_oracle_pins.py): the tutorial's worked
 two-cell example (tests/golden/), the delta-vs-additive 1-D example, the
 unit-key interpolation identity, untouched orthogonal directions, beta = 0
 pure decay, alpha -> 0 memory clearing, the SSD decay-mask closed form with
 orthonormal keys, brute force against naive_product, chunk-size invariance of
-chunked(), save-then-resume, packed-vs-separate, linearity in (S0, v) and the
-contraction bound.  No function here is "parity unpinned".
+chunked(), save-then-resume, packed-vs-separate, linearity in (S0, v), the
+contraction bound, and for the q/k normalisation unit norms, kept directions,
+invariance of the result under positive per-token scaling of q and k, and
+zero vectors staying zero.  No function here is "parity unpinned".
 """
 from __future__ import annotations
 
@@ -94,15 +99,28 @@ def _flatten(q, k, v, log_alpha, beta, cu_seqlens):
             _f64(beta).reshape(B * T, H))
 
 
+def l2_normalise(x):
+    """x / ||x||_2 over the last axis, in fp64.  The Gated DeltaNet paper
+    L2-normalises q and k before the gated delta rule (section 3.3, token
+    mixer block; the paper notes list it for training stability).  The pages
+    give no epsilon; an all-zero vector is left as zero."""
+    x = _f64(x)
+    n = np.sqrt((x * x).sum(axis=-1, keepdims=True))
+    return np.divide(x, n, out=np.zeros_like(x), where=n > 0)
+
+
 def recurrent(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, threads=0,
-              lib=None):
+              lib=None, qk_l2norm=False):
     """Token-by-token recurrence in fp64.
 
     q, k: [B,T,H,dk]; v: [B,T,H,dv]; log_alpha, beta: [B,T,H] (any float
     dtype; widened to fp64).  With cu_seqlens (int [N+1]) the batch is packed
-    (B == 1) and sequence n covers tokens cu[n]..cu[n+1]-1.
+    (B == 1) and sequence n covers tokens cu[n]..cu[n+1]-1.  qk_l2norm:
+    l2_normalise q and k first.
     Returns (o [B,T,H,dv] fp64, final_state [N,H,dv,dk] fp64).
     """
+    if qk_l2norm:
+        q, k = l2_normalise(q), l2_normalise(k)
     B, T, H, dk, dv, cu, qf, kf, vf, laf, bf = _flatten(q, k, v, log_alpha, beta, cu_seqlens)
     N = len(cu) - 1
     o = np.zeros((B * T, H, dv), dtype=np.float64)

@@ -39,7 +39,7 @@ def run_chunk(inp, out_dtype=torch.float32, init_override="default", final=True,
     return o, S
 
 
-def oracle_chunk(inp, heads=None, seqs=None, threads=0):
+def oracle_chunk(inp, heads=None, seqs=None, threads=0, qk_l2norm=False):
     """fp64 oracle on a subset of heads / sequences (all by default).
     Returns (o [B,T,Hs,dv], final [Ns,Hs,dv,dk], heads, seqs)."""
     H = inp.H
@@ -53,7 +53,7 @@ def oracle_chunk(inp, heads=None, seqs=None, threads=0):
         sl = (slice(b, b + 1), slice(s, e), heads)
         init = None if inp.init_state is None else inp.init_state[n:n + 1][:, heads]
         oo, ff = oracle.recurrent(inp.q[sl], inp.k[sl], inp.v[sl], inp.log_alpha[sl], inp.beta[sl],
-                                  init_state=init, threads=threads)
+                                  init_state=init, threads=threads, qk_l2norm=qk_l2norm)
         o[b, s:e] = oo[0]
         fin[si] = ff[0]
     return o, fin, heads, seqs
@@ -64,11 +64,11 @@ def rel_err(got, want, scale):
     return float(np.abs(got - want).max() / scale) if got.size else 0.0
 
 
-def check_parity(inp, o_gpu, S_gpu, heads=None, seqs=None, tol=None, label=""):
+def check_parity(inp, o_gpu, S_gpu, heads=None, seqs=None, tol=None, label="", qk_l2norm=False):
     """Compare the GPU outputs with the oracle on the chosen heads/sequences.
     Returns (err_o, err_S) as max|err| / RMS(o)."""
     tol = TOL[inp.in_dtype] if tol is None else tol
-    o_ref, S_ref, heads, seqs = oracle_chunk(inp, heads, seqs)
+    o_ref, S_ref, heads, seqs = oracle_chunk(inp, heads, seqs, qk_l2norm=qk_l2norm)
     bounds = inp.seq_bounds()
     mask = np.zeros(inp.q.shape[:2], dtype=bool)
     for n in seqs:

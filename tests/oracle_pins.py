@@ -283,8 +283,42 @@ def pin_contraction(lib):
         S = f
 
 
+def pin_l2_normalise(lib):
+    """q/k normalisation (paper 3.3, token mixer block): unit norms, the same
+    direction (x = ||x|| x_hat), and an all-zero vector stays zero."""
+    rng = np.random.default_rng(23)
+    x = rng.standard_normal((3, 7, 16)) * rng.uniform(0.1, 10.0, size=(3, 7, 1))
+    x[1, 2] = 0.0
+    y = oracle.l2_normalise(x)
+    n = np.linalg.norm(y, axis=-1)
+    n[1, 2] = 1.0
+    assert np.abs(n - 1.0).max() < 1e-14
+    assert np.abs(y[1, 2]).max() == 0.0
+    assert np.abs(np.linalg.norm(x, axis=-1, keepdims=True) * y - x).max() < 1e-12
+
+
+def pin_qk_l2norm_scale_invariance(lib):
+    """With q/k normalisation the result does not depend on the length of any
+    q_t or k_t: positive per-(token, head) scalings of q and k leave o and the
+    final state unchanged, and on unit q, k the option is the identity.  A
+    normalisation applied to only one of q, k, or not at all, fails this."""
+    rng = np.random.default_rng(24)
+    B, T, H, dk, dv = 2, 70, 2, 16, 8
+    q, k, v, la, b = _rand_inputs(rng, B, T, H, dk, dv)
+    S0 = 0.1 * rng.standard_normal((B, H, dv, dk))
+    o1, f1 = oracle.recurrent(q, k, v, la, b, init_state=S0, lib=lib)
+    o2, f2 = oracle.recurrent(q, k, v, la, b, init_state=S0, lib=lib, qk_l2norm=True)
+    assert max(np.abs(o1 - o2).max(), np.abs(f1 - f2).max()) < 1e-12
+    cq = rng.uniform(0.2, 5.0, size=(B, T, H, 1))
+    ck = rng.uniform(0.2, 5.0, size=(B, T, H, 1))
+    o3, f3 = oracle.recurrent(cq * q, ck * k, v, la, b, init_state=S0, lib=lib, qk_l2norm=True)
+    assert max(np.abs(o1 - o3).max(), np.abs(f1 - f3).max()) < 1e-12
+    o4, _ = oracle.recurrent(cq * q, ck * k, v, la, b, init_state=S0, lib=lib)
+    assert np.abs(o4 - o1).max() > 1e-3      # without the option the scalings matter
+
+
 ALL_PINS = [pin_worked_example, pin_delta_vs_additive, pin_interpolation,
             pin_orthogonal_untouched, pin_beta_zero_pure_decay, pin_alpha_to_zero,
             pin_ssd_closed_form, pin_naive_product, pin_composition_order,
             pin_chunked_matches_recurrent, pin_resume, pin_packed_vs_separate, pin_linearity,
-            pin_contraction]
+            pin_contraction, pin_l2_normalise, pin_qk_l2norm_scale_invariance]

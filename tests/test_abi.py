@@ -36,13 +36,13 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.gdn_abi_version() == 1
+    assert lib.gdn_abi_version() == 2
     for code, name in [(0, b"GDN_OK"), (2, b"GDN_ERR_SHAPE"), (9, b"GDN_ERR_DEVICE_INPUT")]:
         assert lib.gdn_status_string(code) == name
 
 
 def desc(**kw):
-    base = dict(batch=2, seqlen=100, heads=3, dk=128, dv=128, num_seqs=2, chunk=64, in_dtype=1, out_dtype=0)
+    base = dict(batch=2, seqlen=100, heads=3, dk=128, dv=128, num_seqs=2, chunk=64, in_dtype=1, out_dtype=0, flags=0)
     base.update(kw)
     return ChunkDesc(**base)
 
@@ -66,7 +66,7 @@ def test_workspace_size_host_only(lib):
 @pytest.mark.parametrize("kw,code", [
     (dict(in_dtype=7), 3), (dict(out_dtype=-1), 3), (dict(batch=0), 2), (dict(heads=0), 2),
     (dict(seqlen=-1), 2), (dict(chunk=32), 5), (dict(dk=96), 5), (dict(dv=24), 5), (dict(dv=2048), 5),
-    (dict(dk=256, in_dtype=0), 5), (dict(num_seqs=0), 2),
+    (dict(dk=256, in_dtype=0), 5), (dict(num_seqs=0), 2), (dict(flags=4), 5),
 ])
 def test_bad_descriptor(lib, kw, code):
     st, _ = ws_size(lib, desc(**kw))
@@ -100,10 +100,13 @@ def test_chunk_argument_errors(lib):
 def test_decode_argument_errors(lib):
     vp = ctypes.c_void_p
 
-    def call(N=4, H=2, dk=128, dv=128, idt=1, odt=0, state=FAKE2, q=FAKE, k=FAKE, v=FAKE, la=FAKE, b=FAKE, o=FAKE2 * 8):
-        return lib.gdn_decode_step(N, H, dk, dv, idt, odt, vp(state), vp(q), vp(k), vp(v), vp(la), vp(b), vp(o), None)
+    def call(N=4, H=2, dk=128, dv=128, idt=1, odt=0, flags=0, state=FAKE2, q=FAKE, k=FAKE, v=FAKE, la=FAKE, b=FAKE,
+             o=FAKE2 * 8):
+        return lib.gdn_decode_step(N, H, dk, dv, idt, odt, flags, vp(state), vp(q), vp(k), vp(v), vp(la), vp(b),
+                                   vp(o), None)
 
     assert call(idt=5) == 3
+    assert call(flags=2) == 5                       # unknown option
     assert call(H=0) == 2
     assert call(dk=48) == 5
     assert call(dv=5000) == 5
