@@ -1319,6 +1319,11 @@ hipError_t launch_chunk_fwd(const ChunkArgs &a, hipStream_t st) {
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
+    // Few tokens per sequence (e.g. appending to resident states): the
+    // token-serial kernel reads and writes each state once and skips the
+    // chunk intermediates.
+    if ((int64_t)a.B * a.T <= (int64_t)kShortAvg * a.N)
+        return launch_chunk_short(a, reinterpret_cast<int32_t *>(ws + w.off_meta), st);
     switch (a.in_dtype) {
     case DT_FP32: return launch_typed<float, float>(a, w, st);
     case DT_BF16: return launch_typed<bf16_t, _Float16>(a, w, st);

@@ -43,6 +43,11 @@ ChunkWorkspace chunk_workspace_layout(int32_t B, int32_t T, int32_t N, bool pack
 
 hipError_t launch_decode_step(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_chunk_fwd(const ChunkArgs &a, hipStream_t stream);
+// Token-serial chunk call for batches of short sequences (meta: the
+// workspace's status words; read when cu_seqlens is given, else written).
+hipError_t launch_chunk_short(const ChunkArgs &a, int32_t *meta, hipStream_t stream);
+// Average tokens per sequence up to which gdn_chunk_fwd runs token-serially.
+constexpr int kShortAvg = 16;
 
 // Host-side launch timing (see gdn_profile_* in gdn.h).  While profiling is
 // enabled the scope records a HIP event pair around the launches it covers.

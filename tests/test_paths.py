@@ -15,6 +15,7 @@ from .gpu_util import TOL, check_parity, dev, log, run_chunk
 
 pytestmark = pytest.mark.gpu
 BF = torch.bfloat16
+SHORT_AVG = 16   # gdn.h: a call averaging at most this many tokens per sequence runs token-serially
 
 
 def _dev_inputs(inp):
@@ -107,8 +108,16 @@ def test_packed_equals_separate_bitwise():
                                  la[:, s:e].contiguous(), b[:, s:e].contiguous(),
                                  init_state=dev(inp.init_state[n:n + 1]))
         torch.cuda.synchronize()
-        assert torch.equal(o_n, o_p[:, s:e]), f"sequence {n} output differs"
-        assert torch.equal(S_n[0], S_p[n]), f"sequence {n} final state differs"
+        if e - s > SHORT_AVG:
+            # both calls run the chunked kernels: the same arithmetic, bit for bit
+            assert torch.equal(o_n, o_p[:, s:e]), f"sequence {n} output differs"
+            assert torch.equal(S_n[0], S_p[n]), f"sequence {n} final state differs"
+        else:
+            # a lone short sequence runs token-serially: equal to the bound
+            rms = max(float(o_p.float().pow(2).mean().sqrt()), 1e-6)
+            err = max(float((o_n - o_p[:, s:e]).abs().max()) if e > s else 0.0,
+                      float((S_n[0] - S_p[n]).abs().max())) / rms
+            assert err <= TOL["bf16"], f"sequence {n}: {err:.3e}"
 
 
 def test_deterministic():
@@ -228,3 +237,63 @@ def test_beta_extended_range():
     rms = _rms(o_ref)
     assert float(np.abs(od.cpu().numpy() - o_ref[:, 0]).max()) / rms <= TOL["bf16"]
     assert float(np.abs(st.cpu().numpy() - S_ref).max()) / rms <= TOL["bf16"]
+
+
+# ---- token-serial path (calls averaging at most SHORT_AVG tokens per sequence) ----------
+
+SHORT_CASES = [
+    # lengths, H, dk, dv, dtype
+    ([1, 16, 5, 0, 9, 2, 3, 7], 2, 128, 128, "fp32"),
+    ([4, 4, 4, 4], 3, 32, 96, "fp32"),
+    ([40, 0, 0, 1], 2, 64, 48, "bf16"),       # one sequence spans three 16-token batches
+    ([3, 12, 1], 1, 256, 208, "fp16"),        # four row groups, the last one ragged
+    ([2, 2], 2, 128, 16, "bf16"),
+    ([16] * 5, 2, 256, 256, "bf16"),
+]
+
+
+@pytest.mark.parametrize("lens,H,dk,dv,dt", SHORT_CASES, ids=lambda x: str(x))
+def test_short_path_parity(lens, H, dk, dv, dt):
+    assert sum(lens) <= SHORT_AVG * len(lens)
+    inp = W.packed_inputs(lens, H=H, dk=dk, dv=dv, in_dtype=dt, seed=50 + dk + dv, init_std=0.1,
+                          name=f"short {lens} H{H} dk{dk} dv{dv} {dt}")
+    o, S = run_chunk(inp)
+    check_parity(inp, o, S)
+
+
+def test_short_path_batched():
+    """Equal-length batch (no cu_seqlens) of short sequences, with and without
+    an initial state."""
+    inp = W.chunk_inputs(6, 10, 2, 64, 64, "fp32", seed=57, init_std=0.1, name="short batched")
+    o, S = run_chunk(inp)
+    check_parity(inp, o, S)
+    o0, S0 = run_chunk(inp, init_override=None)
+    inp.init_state = None
+    check_parity(inp, o0, S0, label="short batched, zero initial state")
+
+
+@pytest.mark.parametrize("gate", ["-60", "-5", "0", "mixed", "beta2"])
+def test_short_path_gates(gate):
+    """Decay extremes on the token-serial path: log alpha = -60 or -5 drives
+    the running decay scale out of its range every token or every few tokens,
+    0 never decays; 'mixed' interleaves -60 with mild decay; 'beta2' takes
+    beta in (0, 2)."""
+    inp = W.packed_inputs([16, 9, 1, 14], H=2, dk=128, dv=128, in_dtype="fp32", seed=58, init_std=0.1,
+                          name=f"short gates {gate}")
+    if gate == "mixed":
+        inp.log_alpha[:] = -0.5
+        inp.log_alpha[:, ::3] = -60.0
+    elif gate == "beta2":
+        inp.beta[:] = np.random.default_rng(58).uniform(0.0, 2.0, size=inp.beta.shape).astype(np.float32)
+    else:
+        inp.log_alpha[:] = float(gate)
+    o, S = run_chunk(inp)
+    check_parity(inp, o, S)
+
+
+def test_short_path_qk_l2norm():
+    inp = W.packed_inputs([5, 11, 0, 16], H=2, dk=128, dv=64, in_dtype="bf16", seed=59, init_std=0.1,
+                          name="short l2norm")
+    inp.k[:, 3] = 0.0     # an all-zero key row stays zero after normalisation
+    o, S = run_chunk(inp, qk_l2norm=True)
+    check_parity(inp, o, S, qk_l2norm=True)
