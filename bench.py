@@ -225,7 +225,7 @@ def run_continuation(args, gdn, W, dev):
                    "tokens": int(T), "lengths": f"{int(lens.min())}..{int(lens.max())}", "in_dtype": "bf16",
                    "out_dtype": "fp32", "state": "fp32, initial and final aliased in place"},
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": nbytes / dom_s / 1e9, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": nbytes / dom_s / 1e9 / HBM_PEAK_GBS, "traffic": None,
+                     "unit": "GB/s", "frac": nbytes / dom_s / 1e9 / HBM_PEAK_GBS, "traffic": measured_traffic(dom),
                      "algorithmic_bytes": nbytes, "path_hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
         "kernels": kernels,
     }
