@@ -17,6 +17,10 @@ Functions:
   l2_normalise(x)     x / ||x||_2 per vector (fp64), the q/k normalisation of
                       the paper's token-mixer block; recurrent(...,
                       qk_l2norm=True) applies it to q and k first
+  recurrent_bwd(...)  gradients of recurrent() with respect to q, k, v,
+                      log alpha, beta and the initial state, given the
+                      gradients of o and of the final state (C, fp64, the
+                      chain rule through each token, newest first)
 
 Parity pins (all in tests/test_oracle_pins.py): the tutorial's worked
 two-cell example (tests/golden/), the delta-vs-additive 1-D example, the
@@ -26,7 +30,11 @@ orthonormal keys, brute force against naive_product, chunk-size invariance of
 chunked(), save-then-resume, packed-vs-separate, linearity in (S0, v), the
 contraction bound, and for the q/k normalisation unit norms, kept directions,
 invariance of the result under positive per-token scaling of q and k, and
-zero vectors staying zero.  No function here is "parity unpinned".
+zero vectors staying zero; for the gradients, central finite differences of
+recurrent() on every input element (packed sequences, initial and final
+state terms included), the closed form at alpha = 1, beta = 0 (a frozen
+state), and linearity in (d_o, d_final).  No function here is "parity
+unpinned".
 """
 from __future__ import annotations
 
@@ -63,6 +71,9 @@ def load(path: Optional[str] = None):
     lib.oracle_gdn_naive_product.argtypes = [i64, lp, i64, i64, i64, dp, dp, dp, dp, dp, dp, dp,
                                              dp]
     lib.oracle_gdn_naive_product.restype = ctypes.c_int
+    lib.oracle_gdn_recurrent_bwd.argtypes = [i64, lp, i64, i64, i64, dp, dp, dp, dp, dp, dp, dp, dp,
+                                             dp, dp, dp, dp, dp, dp, ctypes.c_int]
+    lib.oracle_gdn_recurrent_bwd.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     if path is None:
@@ -133,6 +144,40 @@ def recurrent(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, thread
     if rc != 0:
         raise ValueError(f"oracle_gdn_recurrent failed with code {rc}")
     return o.reshape(B, T, H, dv), fin
+
+
+def recurrent_bwd(q, k, v, log_alpha, beta, d_o, init_state=None, d_final=None, cu_seqlens=None,
+                  threads=0, lib=None):
+    """Gradients of recurrent(...) in fp64: the chain rule through each token
+    of the recurrence, newest first (see oracle_gdn_recurrent_bwd in
+    gdn_oracle.c for the step).  The pages give no gradient formulas.
+
+    d_o: [B,T,H,dv], the gradient of a loss with respect to o; d_final:
+    [N,H,dv,dk] or None (zeros), its gradient with respect to the final state.
+    Returns (dq, dk [B,T,H,dk], dv [B,T,H,dv], dlog_alpha, dbeta [B,T,H],
+    d_init [N,H,dv,dk]), all fp64.  Memory per (sequence, head) chain is
+    (L + 1) dv dk doubles for a sequence of L tokens.
+    """
+    B, T, H, dk, dv, cu, qf, kf, vf, laf, bf = _flatten(q, k, v, log_alpha, beta, cu_seqlens)
+    N = len(cu) - 1
+    dof = _f64(d_o).reshape(B * T, H, dv)
+    init = None if init_state is None else _f64(init_state).reshape(N, H, dv, dk)
+    dfin = None if d_final is None else _f64(d_final).reshape(N, H, dv, dk)
+    dq = np.zeros((B * T, H, dk))
+    dkk = np.zeros((B * T, H, dk))
+    dvv = np.zeros((B * T, H, dv))
+    dla = np.zeros((B * T, H))
+    db = np.zeros((B * T, H))
+    dinit = np.zeros((N, H, dv, dk))
+    lib = lib or load()
+    rc = lib.oracle_gdn_recurrent_bwd(N, cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), H, dk, dv,
+                                      _ptr(qf), _ptr(kf), _ptr(vf), _ptr(laf), _ptr(bf), _ptr(init),
+                                      _ptr(dof), _ptr(dfin), _ptr(dq), _ptr(dkk), _ptr(dvv), _ptr(dla),
+                                      _ptr(db), _ptr(dinit), int(threads))
+    if rc != 0:
+        raise ValueError(f"oracle_gdn_recurrent_bwd failed with code {rc}")
+    return (dq.reshape(B, T, H, dk), dkk.reshape(B, T, H, dk), dvv.reshape(B, T, H, dv),
+            dla.reshape(B, T, H), db.reshape(B, T, H), dinit)
 
 
 def naive_product(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, lib=None):

@@ -188,3 +188,125 @@ int oracle_num_threads(void)
     return 1;
 #endif
 }
+
+/*
+ * Reverse-mode gradient of oracle_gdn_recurrent.  The pages call the
+ * chunked algorithm a training method but print no gradient formulas, so
+ * this is the chain rule applied to the ordered step above, one token at a
+ * time, newest token first:
+ *
+ *   forward   Sbar = alpha S_{t-1};  e = beta (v - Sbar k);  S_t = Sbar + e k^T;  o_t = S_t q
+ *   reverse   G   += do_t q^T                       (G = dL/dS_t from here on)
+ *             dq   = S_t^T do_t
+ *             de   = G k,        dk  = G^T e        (through S_t = Sbar + e k^T)
+ *             dbeta = de . (v - Sbar k),  dv = beta de,
+ *             dSbar = G - beta de k^T,    dk -= beta Sbar^T de   (through e)
+ *             dalpha = <dSbar, S_{t-1}>,  dlog_alpha = alpha dalpha
+ *             G    = alpha dSbar                    (= dL/dS_{t-1})
+ *
+ * G starts from d_final (zeros when NULL); what is left after a sequence's
+ * first token is d_init.  The states S_0 .. S_L of a sequence are kept (the
+ * forward pass is replayed with gated_delta_token), so memory per chain is
+ * (L + 1) dv dk doubles.
+ *
+ * d_o  [T, H, dv];  d_final, d_init [N, H, dv, dk] (NULL: zeros / not
+ * returned);  dq, dk [T, H, dk];  dv [T, H, dv];  dlog_alpha, dbeta [T, H].
+ */
+int oracle_gdn_recurrent_bwd(int64_t n_seqs, const int64_t *cu, int64_t H, int64_t dk, int64_t dv,
+                             const double *q, const double *k, const double *v,
+                             const double *log_alpha, const double *beta,
+                             const double *init_state, const double *d_o, const double *d_final,
+                             double *dq, double *dkey, double *dval, double *dlog_alpha,
+                             double *dbeta, double *d_init, int n_threads)
+{
+    int rc = check_args(n_seqs, cu, H, dk, dv);
+    if (rc) return rc;
+    const int64_t jobs = n_seqs * H;
+    const int64_t sz = dv * dk;
+    int failed = 0;
+#ifdef _OPENMP
+    if (n_threads <= 0) n_threads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(n_threads) reduction(| : failed)
+#endif
+    for (int64_t job = 0; job < jobs; ++job) {
+        const int64_t n = job / H, h = job % H;
+        const int64_t t0 = cu[n], L = cu[n + 1] - cu[n];
+        double *states = (double *)malloc(sizeof(double) * (size_t)((L + 1) * sz));
+        double *G = (double *)malloc(sizeof(double) * (size_t)sz);
+        double *work = (double *)malloc(sizeof(double) * (size_t)(4 * dv));
+        if (!states || !G || !work) {
+            free(states);
+            free(G);
+            free(work);
+            failed = 1;
+            continue;
+        }
+        double *err = work, *pred = work + dv, *de = work + 2 * dv, *obuf = work + 3 * dv;
+        if (init_state)
+            memcpy(states, init_state + job * sz, sizeof(double) * (size_t)sz);
+        else
+            memset(states, 0, sizeof(double) * (size_t)sz);
+        for (int64_t t = 0; t < L; ++t) {
+            const int64_t th = (t0 + t) * H + h;
+            memcpy(states + (t + 1) * sz, states + t * sz, sizeof(double) * (size_t)sz);
+            gated_delta_token(states + (t + 1) * sz, err, dk, dv, q + th * dk, k + th * dk, v + th * dv,
+                              log_alpha[th], beta[th], obuf);
+        }
+        if (d_final)
+            memcpy(G, d_final + job * sz, sizeof(double) * (size_t)sz);
+        else
+            memset(G, 0, sizeof(double) * (size_t)sz);
+        for (int64_t t = L - 1; t >= 0; --t) {
+            const int64_t th = (t0 + t) * H + h;
+            const double *Sp = states + t * sz, *Sc = states + (t + 1) * sz;
+            const double *qt = q + th * dk, *kt = k + th * dk, *vt = v + th * dv, *dot = d_o + th * dv;
+            const double alpha = exp(log_alpha[th]), b = beta[th];
+            double *dqt = dq + th * dk, *dkt = dkey + th * dk, *dvt = dval + th * dv;
+            /* o_t = S_t q */
+            for (int64_t i = 0; i < dv; ++i)
+                for (int64_t j = 0; j < dk; ++j) G[i * dk + j] += dot[i] * qt[j];
+            for (int64_t j = 0; j < dk; ++j) {
+                double acc = 0.0;
+                for (int64_t i = 0; i < dv; ++i) acc += Sc[i * dk + j] * dot[i];
+                dqt[j] = acc;
+            }
+            /* e = beta (v - Sbar k), Sbar = alpha S_{t-1} */
+            for (int64_t i = 0; i < dv; ++i) {
+                double p = 0.0, g = 0.0;
+                for (int64_t j = 0; j < dk; ++j) {
+                    p += alpha * Sp[i * dk + j] * kt[j];
+                    g += G[i * dk + j] * kt[j];
+                }
+                pred[i] = p;
+                err[i] = b * (vt[i] - p);
+                de[i] = g;
+            }
+            double db = 0.0;
+            for (int64_t i = 0; i < dv; ++i) {
+                db += de[i] * (vt[i] - pred[i]);
+                dvt[i] = b * de[i];
+            }
+            dbeta[th] = db;
+            for (int64_t j = 0; j < dk; ++j) {
+                double acc = 0.0;
+                for (int64_t i = 0; i < dv; ++i)
+                    acc += G[i * dk + j] * err[i] - b * alpha * Sp[i * dk + j] * de[i];
+                dkt[j] = acc;
+            }
+            /* dSbar = G - beta de k^T; dalpha = <dSbar, S_{t-1}>; G = alpha dSbar */
+            double da = 0.0;
+            for (int64_t i = 0; i < dv; ++i)
+                for (int64_t j = 0; j < dk; ++j) {
+                    const double dsb = G[i * dk + j] - b * de[i] * kt[j];
+                    da += dsb * Sp[i * dk + j];
+                    G[i * dk + j] = alpha * dsb;
+                }
+            dlog_alpha[th] = alpha * da;
+        }
+        if (d_init) memcpy(d_init + job * sz, G, sizeof(double) * (size_t)sz);
+        free(states);
+        free(G);
+        free(work);
+    }
+    return failed ? -3 : 0;
+}

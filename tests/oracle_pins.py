@@ -317,8 +317,87 @@ def pin_qk_l2norm_scale_invariance(lib):
     assert np.abs(o4 - o1).max() > 1e-3      # without the option the scalings matter
 
 
+# -- gradients ------------------------------------------------------------------
+
+def _loss(lib, q, k, v, la, b, S0, cu, Wo, WS):
+    o, fin = oracle.recurrent(q, k, v, la, b, init_state=S0, cu_seqlens=cu, lib=lib)
+    return float((Wo * o).sum() + (WS * fin).sum())
+
+
+def pin_bwd_finite_difference(lib):
+    """Every gradient recurrent_bwd returns equals the central finite
+    difference of the loss sum(Wo * o) + sum(WS * S_final) computed with the
+    forward oracle, element by element, on a packed batch with an empty
+    sequence and initial states (q, k, v, log alpha, beta and S_0)."""
+    rng = np.random.default_rng(30)
+    lens = [3, 0, 5]
+    cu = np.cumsum([0] + lens)
+    T, H, dk, dv = int(cu[-1]), 2, 4, 3
+    q, k, v, la, b = _rand_inputs(rng, 1, T, H, dk, dv, la_range=(-0.7, -0.05))
+    b = rng.uniform(0.1, 1.9, size=b.shape)
+    S0 = rng.standard_normal((len(lens), H, dv, dk))
+    Wo = rng.standard_normal((1, T, H, dv))
+    WS = rng.standard_normal((len(lens), H, dv, dk))
+    grads = oracle.recurrent_bwd(q, k, v, la, b, Wo, init_state=S0, d_final=WS, cu_seqlens=cu, lib=lib)
+    args = [q, k, v, la, b, S0]
+    h = 1e-6
+    for idx, (x, g) in enumerate(zip(args, grads)):
+        assert g.shape == x.shape, (idx, g.shape, x.shape)
+        for pos in np.ndindex(*x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[pos] += h
+            xm[pos] -= h
+            ap, am = list(args), list(args)
+            ap[idx], am[idx] = xp, xm
+            fd = (_loss(lib, *ap, cu, Wo, WS) - _loss(lib, *am, cu, Wo, WS)) / (2 * h)
+            assert abs(fd - g[pos]) <= 1e-6 * (1.0 + abs(fd)), (idx, pos, fd, g[pos])
+
+
+def pin_bwd_frozen_state(lib):
+    """alpha = 1, beta = 0 freeze the state (S_t = S_0, o_t = S_0 q_t), so
+    with G_t = d_final + sum_{s >= t} do_s q_s^T the gradients are
+    dq_t = S_0^T do_t, dv = dk = 0, dbeta_t = (G_t k_t) . (v_t - S_0 k_t),
+    dlog_alpha_t = <G_t, S_0> and d_S0 = G_1."""
+    rng = np.random.default_rng(31)
+    T, dk, dv = 9, 5, 4
+    q, k, v, _, _ = _rand_inputs(rng, 1, T, 1, dk, dv)
+    la, b = np.zeros((1, T, 1)), np.zeros((1, T, 1))
+    S0 = rng.standard_normal((1, 1, dv, dk))
+    do = rng.standard_normal((1, T, 1, dv))
+    dfin = rng.standard_normal((1, 1, dv, dk))
+    dq, dkk, dvv, dla, db, dinit = oracle.recurrent_bwd(q, k, v, la, b, do, init_state=S0, d_final=dfin,
+                                                        lib=lib)
+    S = S0[0, 0]
+    G = dfin[0, 0].copy()
+    for t in range(T - 1, -1, -1):
+        G += np.outer(do[0, t, 0], q[0, t, 0])
+        assert np.abs(dq[0, t, 0] - S.T @ do[0, t, 0]).max() < 1e-12
+        assert abs(db[0, t, 0] - (G @ k[0, t, 0]) @ (v[0, t, 0] - S @ k[0, t, 0])) < 1e-12
+        assert abs(dla[0, t, 0] - (G * S).sum()) < 1e-12
+    assert np.abs(dvv).max() == 0.0 and np.abs(dkk).max() < 1e-12
+    assert np.abs(dinit[0, 0] - G).max() < 1e-12
+
+
+def pin_bwd_linearity(lib):
+    """The gradients are linear in the incoming gradients (d_o, d_final)."""
+    rng = np.random.default_rng(32)
+    B, T, H, dk, dv = 2, 11, 2, 6, 5
+    q, k, v, la, b = _rand_inputs(rng, B, T, H, dk, dv)
+    S0 = rng.standard_normal((B, H, dv, dk))
+    do1, do2 = rng.standard_normal((2, B, T, H, dv))
+    df1, df2 = rng.standard_normal((2, B, H, dv, dk))
+    a1, a2 = 0.6, -1.7
+    g1 = oracle.recurrent_bwd(q, k, v, la, b, do1, init_state=S0, d_final=df1, lib=lib)
+    g2 = oracle.recurrent_bwd(q, k, v, la, b, do2, init_state=S0, d_final=df2, lib=lib)
+    g3 = oracle.recurrent_bwd(q, k, v, la, b, a1 * do1 + a2 * do2, init_state=S0,
+                              d_final=a1 * df1 + a2 * df2, lib=lib)
+    for x1, x2, x3 in zip(g1, g2, g3):
+        assert np.abs(x3 - (a1 * x1 + a2 * x2)).max() < 1e-11
+
+
 ALL_PINS = [pin_worked_example, pin_delta_vs_additive, pin_interpolation,
             pin_orthogonal_untouched, pin_beta_zero_pure_decay, pin_alpha_to_zero,
             pin_ssd_closed_form, pin_naive_product, pin_composition_order,
             pin_chunked_matches_recurrent, pin_resume, pin_packed_vs_separate, pin_linearity,
-            pin_contraction, pin_l2_normalise, pin_qk_l2norm_scale_invariance]
+            pin_contraction, pin_l2_normalise, pin_qk_l2norm_scale_invariance,
+            pin_bwd_finite_difference, pin_bwd_frozen_state, pin_bwd_linearity]

@@ -94,6 +94,12 @@ C_MUTANTS = {
                      "        if (0 && init_state)\n            memcpy(S, init_state + (n * H + h) * dv * dk, sizeof(double) * (size_t)(dv * dk));\n        else"),
     "beta_wrong_head": ("log_alpha[th], beta[th], o + th * dv);",
                         "log_alpha[th], beta[t * H], o + th * dv);"),
+    "bwd_dq_from_previous_state": ("acc += Sc[i * dk + j] * dot[i];", "acc += Sp[i * dk + j] * dot[i];"),
+    "bwd_dk_without_beta": ("acc += G[i * dk + j] * err[i] - b * alpha * Sp[i * dk + j] * de[i];",
+                            "acc += G[i * dk + j] * err[i] - alpha * Sp[i * dk + j] * de[i];"),
+    "bwd_dlog_alpha_not_scaled": ("dlog_alpha[th] = alpha * da;", "dlog_alpha[th] = da;"),
+    "bwd_adjoint_not_decayed": ("G[i * dk + j] = alpha * dsb;", "G[i * dk + j] = dsb;"),
+    "bwd_output_term_dropped": ("G[i * dk + j] += dot[i] * qt[j];", "G[i * dk + j] += 0.0 * dot[i] * qt[j];"),
 }
 
 
