@@ -72,6 +72,10 @@ def load():
     lib.gdn_chunk_fwd_workspace_size.argtypes = [ctypes.POINTER(ChunkDesc), ctypes.POINTER(sz)]
     lib.gdn_chunk_fwd.restype = ctypes.c_int
     lib.gdn_chunk_fwd.argtypes = [ctypes.POINTER(ChunkDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.gdn_chunk_bwd_workspace_size.restype = ctypes.c_int
+    lib.gdn_chunk_bwd_workspace_size.argtypes = [ctypes.POINTER(ChunkDesc), ctypes.POINTER(sz)]
+    lib.gdn_chunk_bwd.restype = ctypes.c_int
+    lib.gdn_chunk_bwd.argtypes = [ctypes.POINTER(ChunkDesc)] + [vp] * 16 + [sz, vp]
     lib.gdn_chunk_fwd_check.restype = ctypes.c_int
     lib.gdn_chunk_fwd_check.argtypes = [vp, vp, ctypes.POINTER(i32)]
     lib.gdn_decode_step.restype = ctypes.c_int
@@ -83,7 +87,7 @@ def load():
     lib.gdn_profile_read.restype = ctypes.c_int
     lib.gdn_profile_read.argtypes = [i32, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_int64),
                                      ctypes.POINTER(ctypes.c_double)]
-    if lib.gdn_abi_version() != 2:
+    if lib.gdn_abi_version() != 3:
         raise RuntimeError(f"{p}: unexpected ABI version {lib.gdn_abi_version()}")
     _lib = lib
     return lib
@@ -184,6 +188,58 @@ def chunk_fwd(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, *, out
                              _ptr(init_state), _ptr(cu_seqlens), _ptr(o), _ptr(final_state), _ptr(workspace),
                              ctypes.c_size_t(workspace.numel() * workspace.element_size()), _stream(dev)))
     return o, final_state
+
+
+def chunk_bwd(q, k, v, log_alpha, beta, d_o, init_state=None, d_final=None, cu_seqlens=None, *,
+              d_init=True, workspace=None, chunk=CHUNK):
+    """Gradients of chunk_fwd's o and final state with respect to its inputs.
+
+    q, k, v, log_alpha, beta, init_state, cu_seqlens as for chunk_fwd;
+    d_o [B,T,H,dv] fp32; d_final [N,H,dv,dk] fp32 or None (zeros).
+    d_init: True (allocate and return dL/d init_state) or False.
+    Returns (dq, dk, dv, dlog_alpha, dbeta, d_init or None), all fp32.
+    """
+    lib = load()
+    dev = q.device
+    dts = (torch.float32, torch.bfloat16, torch.float16)
+    _need(q, "q", dts, dev, 4)
+    B, T, H, dk = q.shape
+    _need(k, "k", (q.dtype,), dev, 4)
+    _need(v, "v", (q.dtype,), dev, 4)
+    dv = v.shape[3]
+    if tuple(k.shape) != (B, T, H, dk) or tuple(v.shape[:3]) != (B, T, H):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    _need(log_alpha, "log_alpha", (torch.float32,), dev, 3)
+    _need(beta, "beta", (torch.float32,), dev, 3)
+    if tuple(log_alpha.shape) != (B, T, H) or tuple(beta.shape) != (B, T, H):
+        raise ValueError("log_alpha and beta must be [B, T, H]")
+    _need(d_o, "d_o", (torch.float32,), dev, 4)
+    if tuple(d_o.shape) != (B, T, H, dv):
+        raise ValueError(f"d_o must be {(B, T, H, dv)}, got {tuple(d_o.shape)}")
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", (torch.int32,), dev, 1)
+        N = cu_seqlens.shape[0] - 1
+    else:
+        N = B
+    for name, t in (("init_state", init_state), ("d_final", d_final)):
+        if t is not None:
+            _need(t, name, (torch.float32,), dev, 4)
+            if tuple(t.shape) != (N, H, dv, dk):
+                raise ValueError(f"{name} must be {(N, H, dv, dk)}, got {tuple(t.shape)}")
+    f32 = dict(dtype=torch.float32, device=dev)
+    dq, dk_, dv_ = torch.empty((B, T, H, dk), **f32), torch.empty((B, T, H, dk), **f32), torch.empty((B, T, H, dv), **f32)
+    dla, db = torch.empty((B, T, H), **f32), torch.empty((B, T, H), **f32)
+    di = torch.empty((N, H, dv, dk), **f32) if d_init else None
+    desc = _desc(B, T, H, dk, dv, N, _DT[q.dtype], _DT[torch.float32], chunk)
+    need = ctypes.c_size_t(0)
+    _check(lib.gdn_chunk_bwd_workspace_size(ctypes.byref(desc), ctypes.byref(need)))
+    if workspace is None:
+        workspace = torch.empty(int(need.value), dtype=torch.uint8, device=dev)
+    _check(lib.gdn_chunk_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                             _ptr(init_state), _ptr(cu_seqlens), _ptr(d_o), _ptr(d_final), _ptr(dq), _ptr(dk_),
+                             _ptr(dv_), _ptr(dla), _ptr(db), _ptr(di), _ptr(workspace),
+                             ctypes.c_size_t(workspace.numel() * workspace.element_size()), _stream(dev)))
+    return dq, dk_, dv_, dla, db, di
 
 
 def chunk_fwd_check(workspace: torch.Tensor) -> int:

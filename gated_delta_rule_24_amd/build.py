@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libgdn.so")
-SOURCES = ["gdn_api.cpp", "gdn_chunk.hip", "gdn_decode.hip"]
+SOURCES = ["gdn_api.cpp", "gdn_chunk.hip", "gdn_decode.hip", "gdn_bwd.hip"]
 ARCH = os.environ.get("GDN_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -207,6 +207,75 @@ gdn_status gdn_chunk_fwd(const gdn_chunk_desc *desc, const void *q, const void *
     return ok();
 }
 
+gdn_status gdn_chunk_bwd_workspace_size(const gdn_chunk_desc *desc, size_t *bytes) {
+    if (!bytes) return fail(GDN_ERR_NULL, "bytes is NULL");
+    gdn_status s = check_chunk_desc(desc);
+    if (s != GDN_OK) return s;
+    const auto a = gdn::chunk_bwd_workspace_layout(desc->batch, desc->seqlen, desc->num_seqs, true, desc->heads,
+                                                   desc->dk, desc->dv);
+    const auto b = gdn::chunk_bwd_workspace_layout(desc->batch, desc->seqlen, desc->num_seqs, false, desc->heads,
+                                                   desc->dk, desc->dv);
+    *bytes = a.total > b.total ? a.total : b.total;
+    return ok();
+}
+
+gdn_status gdn_chunk_bwd(const gdn_chunk_desc *desc, const void *q, const void *k, const void *v,
+                         const float *log_alpha, const float *beta, const float *init_state,
+                         const int32_t *cu_seqlens, const float *d_o, const float *d_final_state, float *dq,
+                         float *dk, float *dv, float *dlog_alpha, float *dbeta, float *d_init_state,
+                         void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    gdn_status s = check_chunk_desc(desc);
+    if (s != GDN_OK) return s;
+    const gdn_chunk_desc &d = *desc;
+    if (d.dk > 128) return fail(GDN_ERR_UNSUPPORTED, "dk %d not built for the backward pass (at most 128)", d.dk);
+    if (d.flags != 0) return fail(GDN_ERR_UNSUPPORTED, "flags 0x%x not supported by the backward pass", d.flags);
+    const bool packed = cu_seqlens != nullptr;
+    if (packed && d.batch != 1) return fail(GDN_ERR_SHAPE, "cu_seqlens requires batch == 1 (got %d)", d.batch);
+    if (!packed && d.num_seqs != d.batch)
+        return fail(GDN_ERR_SHAPE, "without cu_seqlens num_seqs must equal batch (%d != %d)", d.num_seqs, d.batch);
+    const int64_t toks = (int64_t)d.batch * d.seqlen;
+    if (toks > 0 && (!q || !k || !v || !log_alpha || !beta || !d_o || !dq || !dk || !dv || !dlog_alpha || !dbeta))
+        return fail(GDN_ERR_NULL, "q, k, v, log_alpha, beta, d_o, dq, dk, dv, dlog_alpha and dbeta are required");
+    if (!workspace) return fail(GDN_ERR_WORKSPACE, "workspace is NULL");
+    const auto w = gdn::chunk_bwd_workspace_layout(d.batch, d.seqlen, d.num_seqs, packed, d.heads, d.dk, d.dv);
+    if (workspace_bytes < w.total)
+        return fail(GDN_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, w.total);
+    const void *ptrs[] = {q, k, v, init_state, d_o, d_final_state, dq, dk, dv, d_init_state, workspace};
+    const char *names[] = {"q", "k", "v", "init_state", "d_o", "d_final_state", "dq", "dk", "dv", "d_init_state",
+                           "workspace"};
+    for (int i = 0; i < 11; ++i)
+        if (ptrs[i] && !aligned16(ptrs[i])) return fail(GDN_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
+    const void *sptrs[] = {log_alpha, beta, cu_seqlens, dlog_alpha, dbeta};
+    const char *snames[] = {"log_alpha", "beta", "cu_seqlens", "dlog_alpha", "dbeta"};
+    for (int i = 0; i < 5; ++i)
+        if (sptrs[i] && !aligned4(sptrs[i])) return fail(GDN_ERR_ALIGN, "%s is not 4-byte aligned", snames[i]);
+
+    const size_t isz = dtype_size(d.in_dtype);
+    const size_t th = (size_t)toks * d.heads;
+    const size_t state_bytes = sizeof(float) * (size_t)d.num_seqs * d.heads * d.dv * d.dk;
+    const Range ins[] = {rng("q", q, th * d.dk * isz), rng("k", k, th * d.dk * isz), rng("v", v, th * d.dv * isz),
+                         rng("log_alpha", log_alpha, th * 4), rng("beta", beta, th * 4),
+                         rng("init_state", init_state, state_bytes),
+                         rng("cu_seqlens", cu_seqlens, sizeof(int32_t) * (d.num_seqs + 1)),
+                         rng("d_o", d_o, th * d.dv * 4), rng("d_final_state", d_final_state, state_bytes)};
+    const Range outs[] = {rng("dq", dq, th * d.dk * 4), rng("dk", dk, th * d.dk * 4), rng("dv", dv, th * d.dv * 4),
+                          rng("dlog_alpha", dlog_alpha, th * 4), rng("dbeta", dbeta, th * 4),
+                          rng("d_init_state", d_init_state, state_bytes), rng("workspace", workspace, w.total)};
+    for (int i = 0; i < 7; ++i) {
+        for (const Range &r : ins)
+            if (overlap(outs[i], r)) return fail(GDN_ERR_ALIAS, "%s overlaps %s", outs[i].name, r.name);
+        for (int j = 0; j < i; ++j)
+            if (overlap(outs[i], outs[j])) return fail(GDN_ERR_ALIAS, "%s overlaps %s", outs[i].name, outs[j].name);
+    }
+
+    gdn::ChunkArgs a{d.batch, d.seqlen, d.heads, d.dk, d.dv, d.num_seqs, d.in_dtype, d.out_dtype, d.flags,
+                     q, k, v, log_alpha, beta, init_state, cu_seqlens, nullptr, nullptr, workspace};
+    gdn::BwdArgs g{d_o, d_final_state, dq, dk, dv, dlog_alpha, dbeta, d_init_state};
+    hipError_t e = gdn::launch_chunk_bwd(a, g, stream);
+    if (e != hipSuccess) return hip_fail(e, "gdn_chunk_bwd launch");
+    return ok();
+}
+
 gdn_status gdn_chunk_fwd_check(const void *workspace, hipStream_t stream, int32_t *code) {
     if (!workspace || !code) return fail(GDN_ERR_NULL, "workspace and code are required");
     hipError_t e = hipStreamSynchronize(stream);

@@ -1,0 +1,909 @@
+// Backward pass of the chunked gated delta rule: gradients of o and of the
+// final state flowing back to q, k, v, log alpha, beta and the initial state.
+//
+// The pages call the chunkwise algorithm a training method (Gated Delta
+// Networks paper, section 3.3, "Hardware-efficient chunkwise training") but
+// print no gradient formulas, so these follow from differentiating the chunk
+// equations the forward kernels evaluate.  Per chunk, with S the state at
+// the chunk start (dv x dk), g the in-chunk cumulative log decay, gamma = e^g,
+// kappa_r = e^{g_last - g_r}, Gamma_ri = e^{g_r - g_i} (i <= r):
+//
+//   forward   A = strictLower(diag(beta)(Gamma o K K^T)),  T = (I + A)^{-1},  M = T diag(beta)
+//             P = (Q K^T) o Gamma
+//             X = K S^T,  Y = V - diag(gamma) X,  V' = M Y
+//             O = diag(gamma) Q S^T + P V'
+//             S_next = gamma_last S + V'^T diag(kappa) K
+//
+//   reverse   (dO, dS_next given; dS flows to the previous chunk)
+//             dV' = P^T dO + diag(kappa) K dS_next^T
+//             dY  = M^T dV'                    = dV
+//             dS  = gamma_last dS_next + dO^T diag(gamma) Q - dY^T diag(gamma) K
+//             dP  = lower(dO V'^T),  dM = dV' Y^T,  dT = dM diag(beta),  dA = -T^T dT T^T
+//             dbeta_r = sum_x dM_xr T_xr + sum_{i<r} dA_ri Gamma_ri (K K^T)_ri
+//             dQ  = diag(gamma) dO S + (dP o Gamma) K
+//             dK  = -diag(gamma) dY S + diag(kappa) V' dS_next + (dP o Gamma)^T Q + (dK o + dK o^T) K,
+//                   dK o = strictLower(diag(beta) dA o Gamma)
+//             dlog alpha_i = sum_{r>=i} dg_r (g is the in-chunk cumulative sum), which
+//                   expands to sum_{r>=i} gamma_r dgamma_r + sum_{r<i} kappa_r dkappa_r
+//                   + gamma_last <dS_next, S> + sum_{r>=i, c<i} (dGamma o Gamma)_rc,
+//                   with dGamma = dP o Q K^T + diag(beta) dA o K K^T,
+//                   dgamma_r = dO_r . (Q S^T)_r - dY_r . X_r, dkappa_r = V'_r . (K dS_next^T)_r.
+//
+// Four kernels:
+//   B1 bwd_prep_kernel      per (chunk row, head): g, gamma, kappa, T, P (fp32, VALU).
+//   B2 bwd_fwd_pass_kernel  per (sequence, head, 16 value columns), chunks in order:
+//                           replays the state pass and stores the state at every
+//                           chunk start (the checkpoints).
+//   B3 bwd_rev_pass_kernel  the same, chunks in reverse: the gradient of the state
+//                           at every chunk end, and of the initial state.
+//   B4 bwd_grad_kernel      per (chunk row, head): every per-token gradient of the
+//                           chunk from its checkpoint and state gradient.
+// All arithmetic is fp32 (products on the fp32 matrix-core instruction), so the
+// gradients carry the same precision for every input dtype.  Matrix-core
+// tiles use the lane convention of gdn_device.h: lane l, n = l % 16,
+// j = l / 16; an accumulator holds X[4j + i][n]; on issue i of a k-tile kt
+// lane (n, j) supplies A[n][16 kt + 4j + i] and B[16 kt + 4j + i][n].
+#include "gdn_device.h"
+#include "gdn_launch.h"
+
+namespace gdn {
+
+namespace {
+
+constexpr int C = kChunk;
+
+__device__ __forceinline__ void mfma4(float4_t &acc, float a, float b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
+}
+
+// acc += A B over the k-tiles kt0 .. kt1 - 1; fa(r, k) returns A[r][k] for the
+// lane's row r = n, fb(k, c) returns B[k][c] for the lane's column c = n.
+template <typename FA, typename FB>
+__device__ __forceinline__ void tile_mm(float4_t &acc, int kt0, int kt1, FA fa, FB fb) {
+    const int l = threadIdx.x & 63, n = l & 15, j = l >> 4;
+    for (int kt = kt0; kt < kt1; ++kt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int k = 16 * kt + 4 * j + i;
+            mfma4(acc, fa(n, k), fb(k, n));
+        }
+    }
+}
+
+// Sum over the 16 lanes of a DPP row (lanes 16 j .. 16 j + 15); every lane
+// of the row gets the same bits.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_sum(float x) {
+    x += dpp_mov<0xB1>(x);    // quad_perm [1,0,3,2]
+    x += dpp_mov<0x4E>(x);    // quad_perm [2,3,0,1]
+    x += dpp_mov<0x141>(x);   // half-row mirror
+    x += dpp_mov<0x140>(x);   // row mirror
+    return x;
+}
+
+__device__ __forceinline__ float4_t zero4() { return float4_t{0.f, 0.f, 0.f, 0.f}; }
+
+// First chunk row, first token and token count of sequence n.
+__device__ __forceinline__ void seq_rows(int n, int T, int cpr, const int32_t *cu_ws, const int32_t *row0, int &r0,
+                                         int &nrows) {
+    if (cpr) {
+        r0 = n * cpr;
+        nrows = (T + C - 1) / C;
+    } else {
+        r0 = row0[n];
+        nrows = (cu_ws[n + 1] - cu_ws[n] + C - 1) / C;
+    }
+}
+
+// Per-(row, head) vectors written by B1, in floats from the item's base:
+//   [0, C) g,  [C, 2C) gamma,  [2C, 3C) kappa,  [3C, 4C) beta (0 past the row's end).
+constexpr int kVecFloats = 4 * C;
+
+}  // namespace
+
+// ============================================================================
+// B1: g, gamma, kappa, T = (I + A)^{-1} and P per (chunk row, head).
+// One 256-thread block per item; Q and K rows staged in LDS as fp32.
+// ============================================================================
+template <typename in_t, int DK>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(int H, int T, int cpr, int urows,
+                                                       const int32_t *__restrict__ meta,
+                                                       const int32_t *__restrict__ row_tok,
+                                                       const int32_t *__restrict__ row_len,
+                                                       const in_t *__restrict__ q, const in_t *__restrict__ k,
+                                                       const float *__restrict__ log_alpha,
+                                                       const float *__restrict__ beta, float *__restrict__ ws_t,
+                                                       float *__restrict__ ws_p, float *__restrict__ ws_vec) {
+    constexpr int KP = DK + 1;
+    extern __shared__ __align__(16) float smem[];
+    float *sq = smem;                 // [C][KP]
+    float *sk = sq + C * KP;          // [C][KP]
+    float *sa = sk + C * KP;          // [C][C + 1]  A, then scratch
+    float *st = sa + C * (C + 1);     // [C][C + 1]  T
+    float *sg = st + C * (C + 1);     // [C]
+    float *sb = sg + C;               // [C]
+    if (!cpr && meta[1] != 0) return;   // malformed cu_seqlens: nothing is written
+    const int nrows = cpr ? urows : meta[0];
+    const int item = blockIdx.x, row = item / H, h = item % H;
+    if (row >= nrows) return;
+    int tok0, len;
+    row_span(row, T, cpr, row_tok, row_len, tok0, len);
+    const int tid = threadIdx.x;
+
+    for (int idx = tid * 8; idx < C * DK; idx += 256 * 8) {
+        const int r = idx / DK, c = idx % DK;
+        float xq[8], xk[8];
+        if (r < len) {
+            const int64_t off = ((int64_t)(tok0 + r) * H + h) * DK + c;
+            load8_f32(q + off, xq);
+            load8_f32(k + off, xk);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) xq[e] = xk[e] = 0.f;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            sq[r * KP + c + e] = xq[e];
+            sk[r * KP + c + e] = xk[e];
+        }
+    }
+    if (tid < C) {
+        const bool in = tid < len;
+        const int64_t th = (int64_t)(tok0 + tid) * H + h;
+        sg[tid] = in ? log_alpha[th] : 0.f;
+        sb[tid] = in ? beta[th] : 0.f;
+    }
+    __syncthreads();
+    float *vec = ws_vec + (int64_t)item * kVecFloats;
+    if (tid == 0) {
+        float acc = 0.f;
+        for (int r = 0; r < C; ++r) {
+            acc += sg[r];
+            sg[r] = acc;
+        }
+    }
+    __syncthreads();
+    const float glast = len > 0 ? sg[len - 1] : 0.f;
+    if (tid < C) {
+        vec[tid] = sg[tid];
+        vec[C + tid] = expf(sg[tid]);
+        vec[2 * C + tid] = expf(glast - sg[tid]);
+        vec[3 * C + tid] = sb[tid];
+    }
+    // A (strictly lower) into sa, P (lower with the diagonal) straight to HBM.
+    float *P = ws_p + (int64_t)item * C * C;
+    for (int e = tid; e < C * C; e += 256) {
+        const int r = e / C, i = e % C;
+        float a = 0.f, p = 0.f;
+        if (i <= r) {
+            float kk = 0.f, qk = 0.f;
+            for (int c = 0; c < DK; ++c) {
+                kk += sk[r * KP + c] * sk[i * KP + c];
+                qk += sq[r * KP + c] * sk[i * KP + c];
+            }
+            const float gm = expf(sg[r] - sg[i]);
+            p = qk * gm;
+            if (i < r) a = sb[r] * gm * kk;
+        }
+        sa[r * (C + 1) + i] = a;
+        P[e] = p;
+    }
+    __syncthreads();
+    // T = (I + A)^{-1} by forward substitution, one row per step: thread c
+    // owns column c, T[r][c] = [r == c] - sum_{c <= i < r} A[r][i] T[i][c].
+    for (int r = 0; r < C; ++r) {
+        if (tid < C) {
+            const int c = tid;
+            float x = 0.f;
+            if (c <= r) {
+                x = (c == r) ? 1.f : 0.f;
+                for (int i = c; i < r; ++i) x -= sa[r * (C + 1) + i] * st[i * (C + 1) + c];
+            }
+            st[r * (C + 1) + c] = x;
+        }
+        __syncthreads();
+    }
+    float *Tm = ws_t + (int64_t)item * C * C;
+    for (int e = tid; e < C * C; e += 256) Tm[e] = st[(e / C) * (C + 1) + e % C];
+}
+
+// ============================================================================
+// B2: the state pass again, storing the state at every chunk start.
+// One wave per (sequence, head, 16 value columns); the wave holds S^T for its
+// columns (dk x 16) in DK / 16 accumulator tiles: tile a, element i of lane
+// (n, j) = S[v0 + n][16 a + 4 j + i].
+// ============================================================================
+template <typename in_t, int DK>
+__global__ __launch_bounds__(64) void bwd_fwd_pass_kernel(int H, int DV, int T, int cpr, int nvt,
+                                                          const int32_t *__restrict__ meta,
+                                                          const int32_t *__restrict__ cu_ws,
+                                                          const int32_t *__restrict__ row0,
+                                                          const int32_t *__restrict__ row_tok,
+                                                          const int32_t *__restrict__ row_len,
+                                                          const in_t *__restrict__ k, const in_t *__restrict__ v,
+                                                          const float *__restrict__ ws_t,
+                                                          const float *__restrict__ ws_vec,
+                                                          const float *__restrict__ init_state,
+                                                          float *__restrict__ ws_ck) {
+    constexpr int KP = DK + 4;
+    constexpr int NA = DK / 16;
+    extern __shared__ __align__(16) float smem[];
+    float *sk = smem;               // [C][KP]
+    float *sv = sk + C * KP;        // gamma, kappa, beta: [3][C]
+    if (!cpr && meta[1] != 0) return;
+    const int nh = blockIdx.x / nvt, vt = blockIdx.x % nvt;
+    const int n = nh / H, h = nh % H, v0 = vt * 16;
+    const int l = threadIdx.x, nn = l & 15, jj = l >> 4;
+    int r0, nrows;
+    seq_rows(n, T, cpr, cu_ws, row0, r0, nrows);
+
+    float4_t s[NA];
+#pragma unroll
+    for (int a = 0; a < NA; ++a)
+        s[a] = init_state ? *reinterpret_cast<const float4_t *>(init_state + ((int64_t)nh * DV + v0 + nn) * DK +
+                                                                16 * a + 4 * jj)
+                          : zero4();
+    for (int c = 0; c < nrows; ++c) {
+        const int row = r0 + c;
+        int tok0, len;
+        row_span(row, T, cpr, row_tok, row_len, tok0, len);
+        const int64_t item = (int64_t)row * H + h;
+        float *ck = ws_ck + (item * DV + v0 + nn) * DK + 4 * jj;
+#pragma unroll
+        for (int a = 0; a < NA; ++a) *reinterpret_cast<float4_t *>(ck + 16 * a) = s[a];
+        __syncthreads();   // the previous chunk's K is no longer read
+        for (int idx = l * 8; idx < C * DK; idx += 64 * 8) {
+            const int r = idx / DK, cc = idx % DK;
+            float x[8];
+            if (r < len) {
+                load8_f32(k + ((int64_t)(tok0 + r) * H + h) * DK + cc, x);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] = 0.f;
+            }
+            *reinterpret_cast<float4_t *>(sk + r * KP + cc) = float4_t{x[0], x[1], x[2], x[3]};
+            *reinterpret_cast<float4_t *>(sk + r * KP + cc + 4) = float4_t{x[4], x[5], x[6], x[7]};
+        }
+        const float *vec = ws_vec + item * kVecFloats;
+        sv[l] = vec[C + l];
+        sv[C + l] = vec[2 * C + l];
+        sv[2 * C + l] = vec[3 * C + l];
+        __syncthreads();
+        const float glast = len > 0 ? sv[len - 1] : 1.f;
+        const float *Tm = ws_t + item * C * C;
+        // X = K S^T and Y = V - diag(gamma) X, four 16-row blocks
+        float4_t y[4];
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+            float4_t x = zero4();
+#pragma unroll
+            for (int kt = 0; kt < NA; ++kt) {
+                const float4_t kr = *reinterpret_cast<const float4_t *>(sk + (16 * rb + nn) * KP + 16 * kt + 4 * jj);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) mfma4(x, kr[i], s[kt][i]);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * rb + 4 * jj + i;
+                const float vv = r < len ? to_f32(v[((int64_t)(tok0 + r) * H + h) * DV + v0 + nn]) : 0.f;
+                y[rb][i] = vv - sv[r] * x[i];
+            }
+        }
+        // V' = M Y with M = T diag(beta), lower block triangular
+        float4_t vp[4];
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+            vp[rb] = zero4();
+#pragma unroll
+            for (int kt = 0; kt <= rb; ++kt) {
+                const float4_t tr = *reinterpret_cast<const float4_t *>(Tm + (16 * rb + nn) * C + 16 * kt + 4 * jj);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) mfma4(vp[rb], tr[i] * sv[2 * C + 16 * kt + 4 * jj + i], y[kt][i]);
+            }
+        }
+        // S^T <- gamma_last S^T + K^T diag(kappa) V'
+#pragma unroll
+        for (int a = 0; a < NA; ++a) {
+            float4_t acc = glast * s[a];
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 16 * kt + 4 * jj + i;
+                    mfma4(acc, sk[r * KP + 16 * a + nn] * sv[C + r], vp[kt][i]);
+                }
+            }
+            s[a] = acc;
+        }
+    }
+}
+
+// ============================================================================
+// B3: the reverse state pass.  One wave per (sequence, head, 16 value
+// columns) holds dS^T for its columns in the layout of B2.  Chunks in
+// reverse: store dS (the gradient of the state at the chunk's end), then
+//   dV' = P^T dO + diag(kappa) K dS^T,  dY = M^T dV',
+//   dS  <- gamma_last dS + dO^T diag(gamma) Q - dY^T diag(gamma) K.
+// What is left after the first chunk is the initial state's gradient.
+// ============================================================================
+template <typename in_t, int DK>
+__global__ __launch_bounds__(64) void bwd_rev_pass_kernel(int H, int DV, int T, int cpr, int nvt,
+                                                          const int32_t *__restrict__ meta,
+                                                          const int32_t *__restrict__ cu_ws,
+                                                          const int32_t *__restrict__ row0,
+                                                          const int32_t *__restrict__ row_tok,
+                                                          const int32_t *__restrict__ row_len,
+                                                          const in_t *__restrict__ q, const in_t *__restrict__ k,
+                                                          const float *__restrict__ d_o,
+                                                          const float *__restrict__ ws_t,
+                                                          const float *__restrict__ ws_p,
+                                                          const float *__restrict__ ws_vec,
+                                                          const float *__restrict__ d_final,
+                                                          float *__restrict__ ws_ds, float *__restrict__ d_init) {
+    constexpr int KP = DK + 4;
+    constexpr int NA = DK / 16;
+    extern __shared__ __align__(16) float smem[];
+    float *sk = smem;               // [C][KP]
+    float *sq = sk + C * KP;        // [C][KP]
+    float *sv = sq + C * KP;        // gamma, kappa, beta: [3][C]
+    if (!cpr && meta[1] != 0) return;
+    const int nh = blockIdx.x / nvt, vt = blockIdx.x % nvt;
+    const int n = nh / H, h = nh % H, v0 = vt * 16;
+    const int l = threadIdx.x, nn = l & 15, jj = l >> 4;
+    int r0, nrows;
+    seq_rows(n, T, cpr, cu_ws, row0, r0, nrows);
+
+    float4_t s[NA];
+#pragma unroll
+    for (int a = 0; a < NA; ++a)
+        s[a] = d_final ? *reinterpret_cast<const float4_t *>(d_final + ((int64_t)nh * DV + v0 + nn) * DK + 16 * a +
+                                                             4 * jj)
+                       : zero4();
+    for (int c = nrows - 1; c >= 0; --c) {
+        const int row = r0 + c;
+        int tok0, len;
+        row_span(row, T, cpr, row_tok, row_len, tok0, len);
+        const int64_t item = (int64_t)row * H + h;
+        float *ds = ws_ds + (item * DV + v0 + nn) * DK + 4 * jj;
+#pragma unroll
+        for (int a = 0; a < NA; ++a) *reinterpret_cast<float4_t *>(ds + 16 * a) = s[a];
+        __syncthreads();
+        for (int idx = l * 8; idx < C * DK; idx += 64 * 8) {
+            const int r = idx / DK, cc = idx % DK;
+            float xk[8], xq[8];
+            if (r < len) {
+                const int64_t off = ((int64_t)(tok0 + r) * H + h) * DK + cc;
+                load8_f32(k + off, xk);
+                load8_f32(q + off, xq);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) xk[e] = xq[e] = 0.f;
+            }
+            *reinterpret_cast<float4_t *>(sk + r * KP + cc) = float4_t{xk[0], xk[1], xk[2], xk[3]};
+            *reinterpret_cast<float4_t *>(sk + r * KP + cc + 4) = float4_t{xk[4], xk[5], xk[6], xk[7]};
+            *reinterpret_cast<float4_t *>(sq + r * KP + cc) = float4_t{xq[0], xq[1], xq[2], xq[3]};
+            *reinterpret_cast<float4_t *>(sq + r * KP + cc + 4) = float4_t{xq[4], xq[5], xq[6], xq[7]};
+        }
+        const float *vec = ws_vec + item * kVecFloats;
+        sv[l] = vec[C + l];
+        sv[C + l] = vec[2 * C + l];
+        sv[2 * C + l] = vec[3 * C + l];
+        __syncthreads();
+        const float glast = len > 0 ? sv[len - 1] : 1.f;
+        const float *Tm = ws_t + item * C * C;
+        const float *Pm = ws_p + item * C * C;
+        // dO of the chunk as B operands: element i of k-tile kt = dO[16 kt + 4 j + i][v0 + n]
+        float4_t dof[4];
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * kt + 4 * jj + i;
+                dof[kt][i] = r < len ? d_o[((int64_t)(tok0 + r) * H + h) * DV + v0 + nn] : 0.f;
+            }
+        // dV' = P^T dO + diag(kappa) K dS^T
+        float4_t dvp[4];
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+            float4_t x = zero4();
+#pragma unroll
+            for (int kt = 0; kt < NA; ++kt) {
+                const float4_t kr = *reinterpret_cast<const float4_t *>(sk + (16 * rb + nn) * KP + 16 * kt + 4 * jj);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) mfma4(x, kr[i], s[kt][i]);
+            }
+            float4_t acc;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] = sv[C + 16 * rb + 4 * jj + i] * x[i];
+#pragma unroll
+            for (int kt = rb; kt < 4; ++kt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) mfma4(acc, Pm[(16 * kt + 4 * jj + i) * C + 16 * rb + nn], dof[kt][i]);
+            dvp[rb] = acc;
+        }
+        // dY = M^T dV', M^T[r][x] = T[x][r] beta[r]
+        float4_t dy[4];
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+            dy[rb] = zero4();
+            const float br = sv[2 * C + 16 * rb + nn];
+#pragma unroll
+            for (int kt = rb; kt < 4; ++kt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) mfma4(dy[rb], Tm[(16 * kt + 4 * jj + i) * C + 16 * rb + nn] * br, dvp[kt][i]);
+        }
+        // dS^T <- gamma_last dS^T + Q^T diag(gamma) dO - K^T diag(gamma) dY
+#pragma unroll
+        for (int a = 0; a < NA; ++a) {
+            float4_t acc = glast * s[a];
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 16 * kt + 4 * jj + i;
+                    const float gr = sv[r];
+                    mfma4(acc, sq[r * KP + 16 * a + nn] * gr, dof[kt][i]);
+                    mfma4(acc, -sk[r * KP + 16 * a + nn] * gr, dy[kt][i]);
+                }
+            }
+            s[a] = acc;
+        }
+    }
+    if (d_init) {
+        float *di = d_init + ((int64_t)nh * DV + v0 + nn) * DK + 4 * jj;
+#pragma unroll
+        for (int a = 0; a < NA; ++a) *reinterpret_cast<float4_t *>(di + 16 * a) = s[a];
+    }
+}
+
+// ============================================================================
+// B4: per (chunk row, head), every per-token gradient of the chunk.  Four
+// waves; wave w owns rows 16 w .. 16 w + 15 of the chunk.  The value
+// dimension is walked in blocks of 16 columns: the products that sum over it
+// (dP, dM, the S terms of dQ and dK, the decay sums) accumulate in registers.
+// ============================================================================
+template <int DK>
+struct GradSmem {
+    static constexpr int KP = DK + 4;       // Q, K, S and dS block rows
+    static constexpr int CP = C + 4;        // C x C matrices
+    static constexpr int BP = 16 + 1;       // C x 16 value blocks (scalar access only)
+    static constexpr int off_q = 0;
+    static constexpr int off_k = off_q + C * KP;
+    static constexpr int off_t = off_k + C * KP;
+    static constexpr int off_p = off_t + C * CP;          // P, later dP o Gamma
+    static constexpr int off_s = off_p + C * CP;          // S block [16][KP], later dT
+    static constexpr int off_ds = off_s + 16 * KP;        // dS block [16][KP]
+    static constexpr int off_o = off_ds + 16 * KP;        // dO block [C][BP]
+    static constexpr int off_y = off_o + C * BP;          // Y block
+    static constexpr int off_vp = off_y + C * BP;         // V' block
+    static constexpr int off_dvp = off_vp + C * BP;       // dV' block
+    static constexpr int off_dy = off_dvp + C * BP;       // dY block
+    static constexpr int off_w = off_dy + C * BP;         // W = T^T dT, later dK o (sym)
+    static constexpr int off_vec = off_w + C * CP;        // g, gamma, kappa, beta, dgamma, dkappa, dbeta
+    static constexpr int floats = off_vec + 7 * C + 4;
+    static constexpr size_t bytes = sizeof(float) * floats;
+    static_assert(off_s + 16 * KP + 16 * KP + 5 * C * BP >= off_s + C * CP, "dT fits the S/dS/value blocks");
+    static_assert(bytes <= 160 * 1024, "one block per CU: at most the 160 KiB of LDS");
+};
+
+template <typename in_t, int DK>
+__global__ __launch_bounds__(256) void bwd_grad_kernel(int H, int DV, int T, int cpr, int urows,
+                                                       const int32_t *__restrict__ meta,
+                                                       const int32_t *__restrict__ row_tok,
+                                                       const int32_t *__restrict__ row_len,
+                                                       const in_t *__restrict__ q, const in_t *__restrict__ k,
+                                                       const in_t *__restrict__ v, const float *__restrict__ d_o,
+                                                       const float *__restrict__ ws_t,
+                                                       const float *__restrict__ ws_p,
+                                                       const float *__restrict__ ws_vec,
+                                                       const float *__restrict__ ws_ck,
+                                                       const float *__restrict__ ws_ds, float *__restrict__ dq,
+                                                       float *__restrict__ dk, float *__restrict__ dv,
+                                                       float *__restrict__ dla, float *__restrict__ dbeta) {
+    using L = GradSmem<DK>;
+    constexpr int KP = L::KP, CP = L::CP, BP = L::BP, NA = DK / 16;
+    extern __shared__ __align__(16) float smem[];
+    float *sq = smem + L::off_q, *sk = smem + L::off_k, *st = smem + L::off_t, *sp = smem + L::off_p;
+    float *ss = smem + L::off_s, *sds = smem + L::off_ds, *so = smem + L::off_o, *sy = smem + L::off_y;
+    float *svp = smem + L::off_vp, *sdvp = smem + L::off_dvp, *sdy = smem + L::off_dy, *sw = smem + L::off_w;
+    float *vg = smem + L::off_vec, *vgam = vg + C, *vkap = vg + 2 * C, *vb = vg + 3 * C;
+    float *vdgam = vg + 4 * C, *vdkap = vg + 5 * C, *vdb = vg + 6 * C;
+    float *vgl = vg + 7 * C;   // [0] = <dS_next, S>
+    if (!cpr && meta[1] != 0) return;
+    const int nrows = cpr ? urows : meta[0];
+    const int item = blockIdx.x, row = item / H, h = item % H;
+    if (row >= nrows) return;
+    int tok0, len;
+    row_span(row, T, cpr, row_tok, row_len, tok0, len);
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, nn = l & 15, jj = l >> 4;
+    const int64_t it64 = (int64_t)item;
+
+    // ---- stage Q, K, T, P and the vectors ----
+    for (int idx = tid * 8; idx < C * DK; idx += 256 * 8) {
+        const int r = idx / DK, c = idx % DK;
+        float xq[8], xk[8];
+        if (r < len) {
+            const int64_t off = ((int64_t)(tok0 + r) * H + h) * DK + c;
+            load8_f32(q + off, xq);
+            load8_f32(k + off, xk);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) xq[e] = xk[e] = 0.f;
+        }
+        *reinterpret_cast<float4_t *>(sq + r * KP + c) = float4_t{xq[0], xq[1], xq[2], xq[3]};
+        *reinterpret_cast<float4_t *>(sq + r * KP + c + 4) = float4_t{xq[4], xq[5], xq[6], xq[7]};
+        *reinterpret_cast<float4_t *>(sk + r * KP + c) = float4_t{xk[0], xk[1], xk[2], xk[3]};
+        *reinterpret_cast<float4_t *>(sk + r * KP + c + 4) = float4_t{xk[4], xk[5], xk[6], xk[7]};
+    }
+    const float *Tg = ws_t + it64 * C * C, *Pg = ws_p + it64 * C * C;
+    for (int e = tid * 4; e < C * C; e += 256 * 4) {
+        const int r = e / C, c = e % C;
+        *reinterpret_cast<float4_t *>(st + r * CP + c) = *reinterpret_cast<const float4_t *>(Tg + e);
+        *reinterpret_cast<float4_t *>(sp + r * CP + c) = *reinterpret_cast<const float4_t *>(Pg + e);
+    }
+    if (tid < 4 * C) vg[tid] = ws_vec[it64 * kVecFloats + tid];
+    if (tid < 3 * C) vdgam[tid] = 0.f;   // dgamma, dkappa, dbeta
+    if (tid == 0) vgl[0] = 0.f;
+    __syncthreads();
+
+    const int rw = 16 * w;           // the wave's first chunk row
+    float4_t accq[NA], acck[NA];     // dQ, dK rows of the wave: tile a = columns 16 a ..
+#pragma unroll
+    for (int a = 0; a < NA; ++a) accq[a] = acck[a] = zero4();
+    float4_t dp[4], dm[4];           // dP, dM tiles (w, c) for c <= w
+#pragma unroll
+    for (int c = 0; c < 4; ++c) dp[c] = dm[c] = zero4();
+    float pgam[4] = {0.f, 0.f, 0.f, 0.f}, pkap[4] = {0.f, 0.f, 0.f, 0.f}, pgl = 0.f;
+
+    const float *ck = ws_ck + it64 * DV * DK, *dsn = ws_ds + it64 * DV * DK;
+    for (int vb0 = 0; vb0 < DV; vb0 += 16) {
+        // stage S and dS_next rows vb0 .. vb0 + 15, and dO columns vb0 .. vb0 + 15
+        for (int e = tid * 4; e < 16 * DK; e += 256 * 4) {
+            const int r = e / DK, c = e % DK;
+            const float4_t a4 = *reinterpret_cast<const float4_t *>(ck + (int64_t)(vb0 + r) * DK + c);
+            const float4_t b4 = *reinterpret_cast<const float4_t *>(dsn + (int64_t)(vb0 + r) * DK + c);
+            *reinterpret_cast<float4_t *>(ss + r * KP + c) = a4;
+            *reinterpret_cast<float4_t *>(sds + r * KP + c) = b4;
+            pgl += a4[0] * b4[0] + a4[1] * b4[1] + a4[2] * b4[2] + a4[3] * b4[3];
+        }
+        for (int e = tid; e < C * 16; e += 256) {
+            const int r = e / 16, c = e % 16;
+            so[r * BP + c] = r < len ? d_o[((int64_t)(tok0 + r) * H + h) * DV + vb0 + c] : 0.f;
+        }
+        __syncthreads();
+        // X = K S^T, QS = Q S^T, KdS = K dS^T for the wave's rows; Y = V - gamma X
+        float4_t x = zero4(), qs = zero4(), kds = zero4();
+#pragma unroll
+        for (int kt = 0; kt < NA; ++kt) {
+            const float4_t kr = *reinterpret_cast<const float4_t *>(sk + (rw + nn) * KP + 16 * kt + 4 * jj);
+            const float4_t qr = *reinterpret_cast<const float4_t *>(sq + (rw + nn) * KP + 16 * kt + 4 * jj);
+            const float4_t sr = *reinterpret_cast<const float4_t *>(ss + nn * KP + 16 * kt + 4 * jj);
+            const float4_t dr = *reinterpret_cast<const float4_t *>(sds + nn * KP + 16 * kt + 4 * jj);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                mfma4(x, kr[i], sr[i]);
+                mfma4(qs, qr[i], sr[i]);
+                mfma4(kds, kr[i], dr[i]);
+            }
+        }
+        float4_t y;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = rw + 4 * jj + i;
+            const float vv = r < len ? to_f32(v[((int64_t)(tok0 + r) * H + h) * DV + vb0 + nn]) : 0.f;
+            y[i] = vv - vgam[r] * x[i];
+            sy[r * BP + nn] = y[i];
+            pgam[i] += so[r * BP + nn] * qs[i];
+        }
+        __syncthreads();
+        // V' = M Y (M = T diag(beta));  dV' = P^T dO + diag(kappa) KdS
+        float4_t vp = zero4(), dvp;
+        tile_mm(vp, 0, w + 1, [&](int rr, int kk) { return st[(rw + rr) * CP + kk] * vb[kk]; },
+                [&](int kk, int cc) { return sy[kk * BP + cc]; });
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dvp[i] = vkap[rw + 4 * jj + i] * kds[i];
+        tile_mm(dvp, w, 4, [&](int rr, int kk) { return sp[kk * CP + rw + rr]; },
+                [&](int kk, int cc) { return so[kk * BP + cc]; });
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = rw + 4 * jj + i;
+            svp[r * BP + nn] = vp[i];
+            sdvp[r * BP + nn] = dvp[i];
+            pkap[i] += vp[i] * kds[i];
+        }
+        __syncthreads();
+        // dY = M^T dV'  (= dV)
+        float4_t dy = zero4();
+        tile_mm(dy, w, 4, [&](int rr, int kk) { return st[kk * CP + rw + rr] * vb[rw + rr]; },
+                [&](int kk, int cc) { return sdvp[kk * BP + cc]; });
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = rw + 4 * jj + i;
+            sdy[r * BP + nn] = dy[i];
+            pgam[i] -= dy[i] * x[i];
+            if (r < len) dv[((int64_t)(tok0 + r) * H + h) * DV + vb0 + nn] = dy[i];
+        }
+        __syncthreads();
+        // dP += dO V'^T and dM += dV' Y^T on tiles (w, c), c <= w (one k-tile: the 16 columns)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            if (c <= w) {
+                tile_mm(dp[c], 0, 1, [&](int rr, int kk) { return so[(rw + rr) * BP + kk]; },
+                        [&](int kk, int cc) { return svp[(16 * c + cc) * BP + kk]; });
+                tile_mm(dm[c], 0, 1, [&](int rr, int kk) { return sdvp[(rw + rr) * BP + kk]; },
+                        [&](int kk, int cc) { return sy[(16 * c + cc) * BP + kk]; });
+            }
+        }
+        // dQ += diag(gamma) dO S;  dK += -diag(gamma) dY S + diag(kappa) V' dS
+#pragma unroll
+        for (int a = 0; a < NA; ++a) {
+            tile_mm(accq[a], 0, 1, [&](int rr, int kk) { return vgam[rw + rr] * so[(rw + rr) * BP + kk]; },
+                    [&](int kk, int cc) { return ss[kk * KP + 16 * a + cc]; });
+            tile_mm(acck[a], 0, 1, [&](int rr, int kk) { return -vgam[rw + rr] * sdy[(rw + rr) * BP + kk]; },
+                    [&](int kk, int cc) { return ss[kk * KP + 16 * a + cc]; });
+            tile_mm(acck[a], 0, 1, [&](int rr, int kk) { return vkap[rw + rr] * svp[(rw + rr) * BP + kk]; },
+                    [&](int kk, int cc) { return sds[kk * KP + 16 * a + cc]; });
+        }
+        __syncthreads();   // the blocks are restaged next
+    }
+
+    // ---- decay sums of the value loop ----
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float g1 = row16_sum(pgam[i]), k1 = row16_sum(pkap[i]);
+        if (nn == 0) {
+            vdgam[rw + 4 * jj + i] = g1;
+            vdkap[rw + 4 * jj + i] = k1;
+        }
+    }
+    atomicAdd(vgl, pgl);
+    // dT = dM diag(beta) on the lower tiles (into the S-block area), dbeta's first part
+    float *sdt = ss;   // [C][CP]
+    for (int e = tid; e < C * CP; e += 256) sdt[e] = 0.f;
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        if (c <= w) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = rw + 4 * jj + i, cc = 16 * c + nn;
+                if (cc <= r) sdt[r * CP + cc] = dm[c][i] * vb[cc];
+                atomicAdd(&vdb[cc], cc <= r ? dm[c][i] * st[r * CP + cc] : 0.f);
+            }
+        }
+    }
+    __syncthreads();
+    // W = T^T dT (rows of the wave, all column blocks), to LDS
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        float4_t wt = zero4();
+        tile_mm(wt, 0, 4, [&](int rr, int kk) { return st[kk * CP + rw + rr]; },
+                [&](int kk, int cc) { return sdt[kk * CP + 16 * c + cc]; });
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sw[(rw + 4 * jj + i) * CP + 16 * c + nn] = wt[i];
+    }
+    __syncthreads();
+    // dA = -W T^T on tiles (w, c <= w); with K K^T, Q K^T and Gamma form
+    // dbeta's second part, dK o, dP o Gamma and the sums of dGamma o Gamma.
+    float4_t dkk[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        dkk[c] = zero4();
+        if (c > w) continue;
+        float4_t da = zero4(), kk = zero4(), qk = zero4();
+        tile_mm(da, 0, 4, [&](int rr, int kx) { return -sw[(rw + rr) * CP + kx]; },
+                [&](int kx, int cc) { return st[(16 * c + cc) * CP + kx]; });
+        tile_mm(kk, 0, NA, [&](int rr, int kx) { return sk[(rw + rr) * KP + kx]; },
+                [&](int kx, int cc) { return sk[(16 * c + cc) * KP + kx]; });
+        tile_mm(qk, 0, NA, [&](int rr, int kx) { return sq[(rw + rr) * KP + kx]; },
+                [&](int kx, int cc) { return sk[(16 * c + cc) * KP + kx]; });
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = rw + 4 * jj + i, cc = 16 * c + nn;
+            const float gm = cc <= r ? expf(vg[r] - vg[cc]) : 0.f;
+            const float dav = cc < r ? da[i] : 0.f;
+            const float db2 = dav * gm * kk[i];
+            const float dB = vb[r] * dav;
+            dkk[c][i] = dB * gm;
+            const float dpv = dp[c][i];
+            const float dG = (cc <= r ? dpv * qk[i] : 0.f) + dB * kk[i];
+            const float dgg = dG * gm;
+            sp[r * CP + cc] = cc <= r ? dpv * gm : 0.f;   // dP o Gamma (P is no longer needed)
+            const float rs = row16_sum(db2);
+            if (nn == 0) atomicAdd(&vdb[r], rs);
+            sdt[r * CP + cc] = cc < r ? dgg : 0.f;   // E = dGamma o Gamma, strictly lower
+        }
+    }
+    // the upper tiles of dP o Gamma and of E are zero
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+        if (c > w)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                sp[(rw + 4 * jj + i) * CP + 16 * c + nn] = 0.f;
+                sdt[(rw + 4 * jj + i) * CP + 16 * c + nn] = 0.f;
+            }
+    __syncthreads();
+    // dK o (strictly lower) into sw (W is no longer needed)
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sw[(rw + 4 * jj + i) * CP + 16 * c + nn] = dkk[c][i];
+    __syncthreads();
+    // dQ += (dP o Gamma) K;  dK += (dP o Gamma)^T Q + (dK o + dK o^T) K
+#pragma unroll
+    for (int a = 0; a < NA; ++a) {
+        tile_mm(accq[a], 0, 4, [&](int rr, int kx) { return sp[(rw + rr) * CP + kx]; },
+                [&](int kx, int cc) { return sk[kx * KP + 16 * a + cc]; });
+        tile_mm(acck[a], 0, 4, [&](int rr, int kx) { return sp[kx * CP + rw + rr]; },
+                [&](int kx, int cc) { return sq[kx * KP + 16 * a + cc]; });
+        tile_mm(acck[a], 0, 4, [&](int rr, int kx) { return sw[(rw + rr) * CP + kx] + sw[kx * CP + rw + rr]; },
+                [&](int kx, int cc) { return sk[kx * KP + 16 * a + cc]; });
+    }
+#pragma unroll
+    for (int a = 0; a < NA; ++a)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = rw + 4 * jj + i;
+            if (r < len) {
+                const int64_t off = ((int64_t)(tok0 + r) * H + h) * DK + 16 * a + nn;
+                dq[off] = accq[a][i];
+                dk[off] = acck[a][i];
+            }
+        }
+    // dlog alpha_i is the sum over r >= i of dg_r.  Written out term by term
+    // it is sum_{r>=i} gamma_r dgamma_r + sum_{r<i} kappa_r dkappa_r
+    // + gamma_last <dS_next, S> + sum_{r>=i, c<i} E_rc: every term already
+    // carries its decay factor, so a tiny gradient (strong decay) is not the
+    // difference of large partial sums.  E's exclusive row prefix sums first.
+    if (tid < C) {
+        float *er = sdt + tid * CP;
+        float acc = 0.f;
+        for (int c = 0; c < C; ++c) {
+            const float x = er[c];
+            er[c] = acc;
+            acc += x;
+        }
+    }
+    __syncthreads();
+    if (tid < len) {
+        const int i = tid;
+        float x = vgl[0] * vgam[len - 1];
+        for (int r = i; r < len; ++r) x += sdt[r * CP + i] + vdgam[r] * vgam[r];
+        for (int r = 0; r < i; ++r) x += vdkap[r] * vkap[r];
+        const int64_t th = (int64_t)(tok0 + i) * H + h;
+        dla[th] = x;
+        dbeta[th] = vdb[i];
+    }
+}
+
+// ============================================================================
+// Host side
+// ============================================================================
+namespace {
+
+template <typename K>
+hipError_t bwd_allow_smem(K kernel, size_t bytes) {
+    if (bytes <= 64 * 1024) return hipSuccess;
+    return hipFuncSetAttribute(reinterpret_cast<const void *>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)bytes);
+}
+
+int bwd_cpr(const ChunkArgs &a) { return a.cu_seqlens ? 0 : (a.T + C - 1) / C + (a.T == 0); }
+
+template <typename in_t, int DK>
+hipError_t launch_bwd_dk(const ChunkArgs &a, const BwdArgs &g, const BwdWorkspace &w, hipStream_t st) {
+    char *ws = static_cast<char *>(a.workspace);
+    const int32_t *meta = reinterpret_cast<const int32_t *>(ws + w.fwd.off_meta);
+    const int32_t *cu_ws = reinterpret_cast<const int32_t *>(ws + w.fwd.off_cu);
+    const int32_t *row0 = reinterpret_cast<const int32_t *>(ws + w.fwd.off_row0);
+    const int32_t *rtok = reinterpret_cast<const int32_t *>(ws + w.fwd.off_rowtok);
+    const int32_t *rlen = reinterpret_cast<const int32_t *>(ws + w.fwd.off_rowlen);
+    float *wt = reinterpret_cast<float *>(ws + w.off_t), *wp = reinterpret_cast<float *>(ws + w.off_p);
+    float *wv = reinterpret_cast<float *>(ws + w.off_vec), *wck = reinterpret_cast<float *>(ws + w.off_ck);
+    float *wds = reinterpret_cast<float *>(ws + w.off_ds);
+    auto *q = static_cast<const in_t *>(a.q);
+    auto *k = static_cast<const in_t *>(a.k);
+    auto *v = static_cast<const in_t *>(a.v);
+    const int cpr = bwd_cpr(a);
+    const int urows = cpr ? (int)w.fwd.max_rows : 0;
+    const int64_t items = w.fwd.max_rows * a.H;
+    const int nvt = a.dv / 16;
+    const int64_t chains = (int64_t)a.N * a.H * nvt;
+    hipError_t e;
+    if (items > 0) {
+        const size_t sb = sizeof(float) * (2 * C * (DK + 1) + 2 * C * (C + 1) + 2 * C);
+        auto kern = bwd_prep_kernel<in_t, DK>;
+        if ((e = bwd_allow_smem(kern, sb)) != hipSuccess) return e;
+        ProfScope prof("gdn_bwd_prep", st);
+        kern<<<dim3((unsigned)items), dim3(256), sb, st>>>(a.H, a.T, cpr, urows, meta, rtok, rlen, q, k,
+                                                           a.log_alpha, a.beta, wt, wp, wv);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    if (chains > 0) {
+        {
+            const size_t sb = sizeof(float) * (C * (DK + 4) + 3 * C);
+            auto kern = bwd_fwd_pass_kernel<in_t, DK>;
+            if ((e = bwd_allow_smem(kern, sb)) != hipSuccess) return e;
+            ProfScope prof("gdn_bwd_fwd_pass", st);
+            kern<<<dim3((unsigned)chains), dim3(64), sb, st>>>(a.H, a.dv, a.T, cpr, nvt, meta, cu_ws, row0, rtok,
+                                                               rlen, k, v, wt, wv, a.init_state, wck);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
+        {
+            const size_t sb = sizeof(float) * (2 * C * (DK + 4) + 3 * C);
+            auto kern = bwd_rev_pass_kernel<in_t, DK>;
+            if ((e = bwd_allow_smem(kern, sb)) != hipSuccess) return e;
+            ProfScope prof("gdn_bwd_rev_pass", st);
+            kern<<<dim3((unsigned)chains), dim3(64), sb, st>>>(a.H, a.dv, a.T, cpr, nvt, meta, cu_ws, row0, rtok,
+                                                               rlen, q, k, g.d_o, wt, wp, wv, g.d_final, wds,
+                                                               g.d_init);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
+    }
+    if (items > 0) {
+        using L = GradSmem<DK>;
+        auto kern = bwd_grad_kernel<in_t, DK>;
+        if ((e = bwd_allow_smem(kern, L::bytes)) != hipSuccess) return e;
+        ProfScope prof("gdn_bwd_grad", st);
+        kern<<<dim3((unsigned)items), dim3(256), L::bytes, st>>>(a.H, a.dv, a.T, cpr, urows, meta, rtok, rlen, q, k,
+                                                                 v, g.d_o, wt, wp, wv, wck, wds, g.dq, g.dk, g.dv,
+                                                                 g.dlog_alpha, g.dbeta);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+template <typename in_t>
+hipError_t launch_bwd_typed(const ChunkArgs &a, const BwdArgs &g, const BwdWorkspace &w, hipStream_t st) {
+    switch (a.dk) {
+    case 32: return launch_bwd_dk<in_t, 32>(a, g, w, st);
+    case 64: return launch_bwd_dk<in_t, 64>(a, g, w, st);
+    case 128: return launch_bwd_dk<in_t, 128>(a, g, w, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+static size_t bwd_align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+BwdWorkspace chunk_bwd_workspace_layout(int32_t B, int32_t T, int32_t N, bool packed, int32_t H, int32_t dk,
+                                        int32_t dv) {
+    BwdWorkspace w{};
+    w.fwd = chunk_workspace_layout(B, T, N, packed, H, DT_FP32);
+    const size_t items = (size_t)w.fwd.max_rows * H;
+    size_t off = bwd_align256(w.fwd.off_g);   // only the table part of the forward layout is used
+    w.off_t = off;   off = bwd_align256(off + sizeof(float) * items * C * C);
+    w.off_p = off;   off = bwd_align256(off + sizeof(float) * items * C * C);
+    w.off_vec = off; off = bwd_align256(off + sizeof(float) * items * kVecFloats);
+    w.off_ck = off;  off = bwd_align256(off + sizeof(float) * items * (size_t)dv * dk);
+    w.off_ds = off;  off = bwd_align256(off + sizeof(float) * items * (size_t)dv * dk);
+    w.total = off;
+    return w;
+}
+
+hipError_t launch_chunk_bwd(const ChunkArgs &a, const BwdArgs &g, hipStream_t st) {
+    const bool packed = a.cu_seqlens != nullptr;
+    const BwdWorkspace w = chunk_bwd_workspace_layout(a.B, a.T, a.N, packed, a.H, a.dk, a.dv);
+    char *ws = static_cast<char *>(a.workspace);
+    if (packed) {
+        hipError_t e = launch_chunk_table(a.N, a.T, a.cu_seqlens, reinterpret_cast<int32_t *>(ws + w.fwd.off_meta),
+                                          reinterpret_cast<int32_t *>(ws + w.fwd.off_cu),
+                                          reinterpret_cast<int32_t *>(ws + w.fwd.off_row0),
+                                          reinterpret_cast<int32_t *>(ws + w.fwd.off_rowtok),
+                                          reinterpret_cast<int32_t *>(ws + w.fwd.off_rowlen), st);
+        if (e != hipSuccess) return e;
+    }
+    switch (a.in_dtype) {
+    case DT_FP32: return launch_bwd_typed<float>(a, g, w, st);
+    case DT_BF16: return launch_bwd_typed<bf16_t>(a, g, w, st);
+    case DT_FP16: return launch_bwd_typed<_Float16>(a, g, w, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace gdn

@@ -82,7 +82,7 @@ __device__ __forceinline__ void lds_store8(OP *p, const float (&x)[8]) {
 //   cu_ws[N+1] = token offsets, row0[N] = first row of each sequence,
 //   row_tok / row_len = token start and length of each row.
 // A batch of equal-length sequences needs no table: G1 and G2 derive a row's
-// span from its index (row_span below) and G0 is not launched.
+// span from its index (row_span, gdn_launch.h) and G0 is not launched.
 // ============================================================================
 __global__ __launch_bounds__(256) void chunk_table_kernel(int N, int T,
                                                           const int32_t *__restrict__ cu_in,
@@ -146,21 +146,6 @@ __global__ __launch_bounds__(256) void chunk_table_kernel(int N, int T,
             row_tok[r + j] = s0 + j * C;
             row_len[r + j] = min(C, s1 - s0 - j * C);
         }
-    }
-}
-
-// Token start and length of chunk row `row`.  With cpr > 0 the batch is
-// B sequences of T tokens each, cpr = ceil(T / C) rows per sequence, and the
-// span follows from the index; cpr = 0 reads the packed table.
-__device__ __forceinline__ void row_span(int row, int T, int cpr, const int32_t *__restrict__ row_tok,
-                                         const int32_t *__restrict__ row_len, int &tok0, int &len) {
-    if (cpr) {
-        const int s = row / cpr, c = row - s * cpr;
-        tok0 = s * T + c * C;
-        len = min(C, T - c * C);
-    } else {
-        tok0 = row_tok[row];
-        len = row_len[row];
     }
 }
 
@@ -1304,19 +1289,23 @@ static hipError_t launch_typed(const ChunkArgs &a, const ChunkWorkspace &w, hipS
     return hipErrorInvalidValue;
 }
 
+hipError_t launch_chunk_table(int32_t N, int32_t T, const int32_t *cu_seqlens, int32_t *meta, int32_t *cu_ws,
+                              int32_t *row0, int32_t *row_tok, int32_t *row_len, hipStream_t st) {
+    ProfScope prof("gdn_chunk_table", st);
+    chunk_table_kernel<<<1, 256, 0, st>>>(N, T, cu_seqlens, meta, cu_ws, row0, row_tok, row_len);
+    return hipGetLastError();
+}
+
 hipError_t launch_chunk_fwd(const ChunkArgs &a, hipStream_t st) {
     const bool packed = a.cu_seqlens != nullptr;
     const ChunkWorkspace w = chunk_workspace_layout(a.B, a.T, a.N, packed, a.H, a.in_dtype);
     char *ws = static_cast<char *>(a.workspace);
     if (packed) {
-        ProfScope prof("gdn_chunk_table", st);
-        chunk_table_kernel<<<1, 256, 0, st>>>(a.N, a.T, a.cu_seqlens,
-                                             reinterpret_cast<int32_t *>(ws + w.off_meta),
-                                             reinterpret_cast<int32_t *>(ws + w.off_cu),
-                                             reinterpret_cast<int32_t *>(ws + w.off_row0),
-                                             reinterpret_cast<int32_t *>(ws + w.off_rowtok),
-                                             reinterpret_cast<int32_t *>(ws + w.off_rowlen));
-        hipError_t e = hipGetLastError();
+        hipError_t e = launch_chunk_table(a.N, a.T, a.cu_seqlens, reinterpret_cast<int32_t *>(ws + w.off_meta),
+                                          reinterpret_cast<int32_t *>(ws + w.off_cu),
+                                          reinterpret_cast<int32_t *>(ws + w.off_row0),
+                                          reinterpret_cast<int32_t *>(ws + w.off_rowtok),
+                                          reinterpret_cast<int32_t *>(ws + w.off_rowlen), st);
         if (e != hipSuccess) return e;
     }
     // Few tokens per sequence (e.g. appending to resident states): the

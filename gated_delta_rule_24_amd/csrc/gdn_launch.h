@@ -15,6 +15,21 @@ constexpr int32_t kFlagQkL2Norm = 1;        // GDN_QK_L2NORM
 constexpr int kTriTiles = 10;               // 16x16 tiles in the lower triangle of a C x C block
 constexpr int kTileElems = 256;             // 16 x 16
 
+// Token start and length of chunk row `row`.  With cpr > 0 the batch is
+// B sequences of T tokens each, cpr = ceil(T / C) rows per sequence, and the
+// span follows from the index; cpr = 0 reads the packed table.
+__device__ __forceinline__ void row_span(int row, int T, int cpr, const int32_t *__restrict__ row_tok,
+                                         const int32_t *__restrict__ row_len, int &tok0, int &len) {
+    if (cpr) {
+        const int s = row / cpr, c = row - s * cpr;
+        tok0 = s * T + c * kChunk;
+        len = min(kChunk, T - c * kChunk);
+    } else {
+        tok0 = row_tok[row];
+        len = row_len[row];
+    }
+}
+
 struct DecodeArgs {
     int32_t N, H, dk, dv, in_dtype, out_dtype, flags;
     float *state;
@@ -48,6 +63,26 @@ hipError_t launch_chunk_fwd(const ChunkArgs &a, hipStream_t stream);
 hipError_t launch_chunk_short(const ChunkArgs &a, int32_t *meta, hipStream_t stream);
 // Average tokens per sequence up to which gdn_chunk_fwd runs token-serially.
 constexpr int kShortAvg = 16;
+
+// Backward pass (gdn_chunk_bwd): the incoming gradients and the gradients it writes.
+struct BwdArgs {
+    const float *d_o, *d_final;
+    float *dq, *dk, *dv, *dlog_alpha, *dbeta, *d_init;
+};
+
+// Workspace carve-up for one gdn_chunk_bwd call: the chunk table of the
+// forward layout, then per (chunk row, head) T, P and the decay vectors, and
+// the state and state-gradient checkpoints.
+struct BwdWorkspace {
+    ChunkWorkspace fwd;
+    size_t off_t, off_p, off_vec, off_ck, off_ds, total;
+};
+BwdWorkspace chunk_bwd_workspace_layout(int32_t B, int32_t T, int32_t N, bool packed, int32_t H, int32_t dk,
+                                        int32_t dv);
+hipError_t launch_chunk_bwd(const ChunkArgs &a, const BwdArgs &g, hipStream_t stream);
+// G0 on its own (validates cu_seqlens and builds the chunk-row table).
+hipError_t launch_chunk_table(int32_t N, int32_t T, const int32_t *cu_seqlens, int32_t *meta, int32_t *cu_ws,
+                              int32_t *row0, int32_t *row_tok, int32_t *row_len, hipStream_t stream);
 
 // Host-side launch timing (see gdn_profile_* in gdn.h).  While profiling is
 // enabled the scope records a HIP event pair around the launches it covers.

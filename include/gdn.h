@@ -16,6 +16,9 @@
  *   gdn_decode_step  -- one token of the recurrence for a batch of resident
  *                       states, updated in place (tutorial page, decode
  *                       recursion S_t = S_{t-1} A_t + B_t).
+ * and differentiated:
+ *   gdn_chunk_bwd    -- gradients of gdn_chunk_fwd's outputs with respect to
+ *                       all of its inputs (for training).
  *
  * Both return the same numbers as the recurrence up to floating-point
  * rounding.  Chunked, single-step and save-then-resume evaluations agree
@@ -58,7 +61,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 2
+#define GDN_ABI_VERSION 3
 
 typedef enum {
     GDN_OK = 0,
@@ -194,8 +197,61 @@ gdn_status gdn_chunk_fwd(const gdn_chunk_desc *desc,
                          hipStream_t stream);
 
 /*
- * Result of the device-side cu_seqlens check of the last gdn_chunk_fwd that
- * used `workspace`.  Synchronises `stream`, then writes 0 (valid) or a
+ * Workspace for gdn_chunk_bwd, in bytes, written to *bytes (host pointer).
+ * Depends only on the descriptor.  Besides the chunk table it holds, per
+ * (chunk, head), the fp32 UT-transform matrix T = (I + A)^{-1}, the
+ * decay-masked Q K^T block and the decay vectors (33 KiB at C = 64), and
+ * the state and the state's gradient at every chunk boundary
+ * (2 * dv * dk * 4 bytes).  Prefill with B = 4, T = 4096, H = 16,
+ * dk = dv = 128 needs about 644 MiB.
+ * Errors: GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_DTYPE, GDN_ERR_UNSUPPORTED.
+ */
+gdn_status gdn_chunk_bwd_workspace_size(const gdn_chunk_desc *desc, size_t *bytes);
+
+/*
+ * Backward pass of gdn_chunk_fwd: given the gradients of a loss with respect
+ * to o and to the final state, the gradients with respect to every input.
+ * The pages call the chunkwise algorithm a training method (paper section
+ * 3.3) but give no gradient formulas; these follow from differentiating the
+ * recurrence of eq. (10), evaluated on the chunked form.  The forward pass
+ * is recomputed from the inputs (nothing from gdn_chunk_fwd is kept).
+ *
+ *   desc, q, k, v, log_alpha, beta, init_state, cu_seqlens
+ *               as for gdn_chunk_fwd (desc->out_dtype is not used)
+ *   d_o            [B, T, H, dv]  fp32, dL/do
+ *   d_final_state  [N, H, dv, dk] fp32 or NULL (zeros): dL/d final state
+ *   dq, dk         [B, T, H, dk]  fp32 (written)
+ *   dv             [B, T, H, dv]  fp32 (written)
+ *   dlog_alpha     [B, T, H]      fp32 (written), dL/d log_alpha
+ *   dbeta          [B, T, H]      fp32 (written)
+ *   d_init_state   [N, H, dv, dk] fp32 or NULL (not returned): dL/d init_state
+ *                  (with init_state NULL it is the gradient at a zero state)
+ *   workspace      at least gdn_chunk_bwd_workspace_size bytes
+ *
+ * Supported: dk 32, 64 or 128; dv a multiple of 16 up to 1024; flags 0
+ * (GDN_QK_L2NORM is not differentiated: GDN_ERR_UNSUPPORTED).  All
+ * gradient arithmetic is fp32 for every input dtype.  Tokens past a
+ * sequence's end are not written.  With cu_seqlens the array is checked on
+ * the device as in gdn_chunk_fwd; a malformed one makes the kernels write
+ * nothing and gdn_chunk_fwd_check(workspace, ...) reports it.
+ * The outputs must not overlap each other, any input or the workspace
+ * (GDN_ERR_ALIAS).
+ * Errors: GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_DTYPE, GDN_ERR_ALIGN,
+ * GDN_ERR_UNSUPPORTED, GDN_ERR_WORKSPACE, GDN_ERR_ALIAS, GDN_ERR_HIP.
+ */
+gdn_status gdn_chunk_bwd(const gdn_chunk_desc *desc,
+                         const void *q, const void *k, const void *v,
+                         const float *log_alpha, const float *beta,
+                         const float *init_state, const int32_t *cu_seqlens,
+                         const float *d_o, const float *d_final_state,
+                         float *dq, float *dk, float *dv,
+                         float *dlog_alpha, float *dbeta, float *d_init_state,
+                         void *workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
+/*
+ * Result of the device-side cu_seqlens check of the last gdn_chunk_fwd (or
+ * packed gdn_chunk_bwd) that used `workspace`.  Synchronises `stream`, then writes 0 (valid) or a
  * non-zero code (1: cu[0] != 0, 2: decreasing offsets, 3: cu[N] != T) to
  * *code (host pointer).  Returns GDN_ERR_DEVICE_INPUT when the code is
  * non-zero, GDN_OK otherwise.

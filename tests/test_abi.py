@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.gdn_abi_version() == 2
+    assert lib.gdn_abi_version() == 3
     for code, name in [(0, b"GDN_OK"), (2, b"GDN_ERR_SHAPE"), (9, b"GDN_ERR_DEVICE_INPUT")]:
         assert lib.gdn_status_string(code) == name
 
@@ -95,6 +95,42 @@ def test_chunk_argument_errors(lib):
     assert call_chunk(lib, d, o=FAKE) == 8                              # o aliases q
     assert call_chunk(lib, d, init=FAKE2 * 2, fin=FAKE2 * 2 + 256) == 8  # partial state overlap
     assert b"overlap" in lib.gdn_last_error_message()
+
+
+def call_bwd(lib, d, q=FAKE, k=FAKE, v=FAKE, la=FAKE, beta=FAKE, init=None, cu=None, do=FAKE * 2, dfin=None,
+             dq=FAKE2, dk=FAKE2 * 2, dv=FAKE2 * 3, dla=FAKE2 * 5, db=FAKE2 * 6, dinit=None, ws=FAKE2 * 8,
+             ws_bytes=None):
+    if ws_bytes is None:
+        n = ctypes.c_size_t(0)
+        assert lib.gdn_chunk_bwd_workspace_size(ctypes.byref(d), ctypes.byref(n)) == 0
+        ws_bytes = n.value
+    vp = ctypes.c_void_p
+    return lib.gdn_chunk_bwd(ctypes.byref(d), vp(q), vp(k), vp(v), vp(la), vp(beta), vp(init), vp(cu), vp(do),
+                             vp(dfin), vp(dq), vp(dk), vp(dv), vp(dla), vp(db), vp(dinit), vp(ws),
+                             ctypes.c_size_t(ws_bytes), None)
+
+
+def test_bwd_workspace_and_argument_errors(lib):
+    n = ctypes.c_size_t(0)
+    # prefill shape: T, P, decay vectors, two state checkpoints per (chunk, head)
+    d = desc(batch=4, seqlen=4096, heads=16, num_seqs=4)
+    assert lib.gdn_chunk_bwd_workspace_size(ctypes.byref(d), ctypes.byref(n)) == 0
+    rows = 4 * 64 * 16
+    assert n.value >= rows * (2 * 64 * 64 * 4 + 4 * 64 * 4 + 2 * 128 * 128 * 4)
+    d = desc()
+    assert call_bwd(lib, desc(dk=256)) == 5                            # dk 256 not differentiated
+    assert call_bwd(lib, desc(flags=1)) == 5                           # q/k normalisation not differentiated
+    assert call_bwd(lib, d, do=None) == 1
+    assert call_bwd(lib, d, dla=None) == 1
+    assert call_bwd(lib, d, ws=None) == 6
+    assert call_bwd(lib, d, ws_bytes=16) == 6
+    assert call_bwd(lib, d, dq=FAKE2 + 4) == 4                         # 16-byte alignment
+    assert call_bwd(lib, d, db=FAKE2 * 6 + 2) == 4                     # 4-byte alignment
+    assert call_bwd(lib, d, cu=FAKE) == 2                              # cu with batch != 1
+    assert call_bwd(lib, d, dk=FAKE) == 8                              # output over an input
+    assert call_bwd(lib, d, dv=FAKE2 + 256) == 8                       # two outputs overlap
+    assert call_bwd(lib, d, dinit=FAKE2 * 8 + 4096) == 8               # output inside the workspace
+    assert b"overlaps" in lib.gdn_last_error_message()
 
 
 def test_decode_argument_errors(lib):

@@ -1,0 +1,111 @@
+"""GPU parity of the backward pass (gdn_chunk_bwd through the C ABI) against
+the fp64 oracle's gradients (oracle.recurrent_bwd), element by element.
+
+Every gradient is computed in fp32 on the GPU for any input dtype, and the
+oracle gets the same input values, so the bound is the fp32 one for all
+cases: max |err| <= 1e-4 * RMS of the oracle's gradient, per gradient
+tensor."""
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_24_amd as gdn
+import oracle
+import workloads as W
+
+from .gpu_util import TORCH_DT, dev, log
+
+pytestmark = pytest.mark.gpu
+GRAD_TOL = 1e-4
+NAMES = ("dq", "dk", "dv", "dlog_alpha", "dbeta", "d_init")
+
+
+def _run(inp, d_o, d_final):
+    dt = TORCH_DT[inp.in_dtype]
+    q, k, v = dev(inp.q, dt), dev(inp.k, dt), dev(inp.v, dt)
+    la, b = dev(inp.log_alpha), dev(inp.beta)
+    S0 = None if inp.init_state is None else dev(inp.init_state)
+    cu = None if inp.cu_seqlens is None else dev(inp.cu_seqlens, torch.int32)
+    out = gdn.chunk_bwd(q, k, v, la, b, dev(d_o), init_state=S0, d_final=None if d_final is None else dev(d_final),
+                        cu_seqlens=cu)
+    torch.cuda.synchronize()
+    return [x.cpu().numpy() for x in out]
+
+
+def _check(inp, d_o, d_final, label, heads=None, tol=GRAD_TOL):
+    got = _run(inp, d_o, d_final)
+    H = inp.H
+    heads = list(range(H)) if heads is None else list(heads)
+    sl = (slice(None), slice(None), heads)
+    init = None if inp.init_state is None else inp.init_state[:, heads]
+    ref = oracle.recurrent_bwd(inp.q[sl], inp.k[sl], inp.v[sl], inp.log_alpha[sl], inp.beta[sl], d_o[sl],
+                               init_state=init, d_final=None if d_final is None else d_final[:, heads],
+                               cu_seqlens=inp.cu_seqlens)
+    errs = []
+    for name, g, r in zip(NAMES, got, ref):
+        g = g[:, heads] if name == "d_init" else g[:, :, heads]
+        rms = float(np.sqrt((r ** 2).mean())) if r.size else 1.0
+        rms = rms if rms > 0 else 1.0
+        assert np.isfinite(g).all(), f"{label}: {name} not finite"
+        e = float(np.abs(g - r).max()) / rms if r.size else 0.0
+        errs.append(e)
+    log(f"[bwd] {label}: " + " ".join(f"{n} {e:.2e}" for n, e in zip(NAMES, errs)) + f" (tol {tol:.0e})")
+    for n, e in zip(NAMES, errs):
+        assert e <= tol, f"{label}: {n} error {e:.3e} > {tol:.0e}"
+
+
+CASES = [
+    # B, T, H, dk, dv, dtype, init_std, d_final
+    (1, 130, 2, 64, 32, "fp32", 0.1, True),
+    (2, 64, 1, 32, 16, "bf16", None, False),
+    (1, 10, 2, 128, 128, "fp32", 0.1, True),
+    (2, 200, 2, 128, 128, "bf16", 0.1, True),
+    (1, 100, 1, 128, 256, "fp16", 0.1, True),
+    (1, 257, 3, 32, 48, "fp32", None, True),
+]
+
+
+@pytest.mark.parametrize("B,T,H,dk,dv,dt,init_std,dfin", CASES, ids=lambda x: str(x))
+def test_bwd_small(B, T, H, dk, dv, dt, init_std, dfin):
+    inp = W.chunk_inputs(B, T, H, dk, dv, dt, seed=60 + T + dk, init_std=init_std)
+    d_o, d_final = W.incoming_grads(inp, seed=61 + T, final=dfin)
+    _check(inp, d_o, d_final, f"B{B} T{T} H{H} dk{dk} dv{dv} {dt}")
+
+
+def test_bwd_packed():
+    inp = W.packed_inputs([5, 0, 64, 1, 130, 63, 65], H=2, dk=128, dv=128, in_dtype="bf16", seed=62)
+    d_o, d_final = W.incoming_grads(inp, seed=63)
+    _check(inp, d_o, d_final, "packed [5,0,64,1,130,63,65]")
+
+
+@pytest.mark.parametrize("gate", ["-60", "0", "beta2"])
+def test_bwd_gates(gate):
+    inp = W.chunk_inputs(1, 150, 2, 64, 64, "fp32", seed=64, init_std=0.1)
+    if gate == "beta2":
+        inp.beta[:] = np.random.default_rng(64).uniform(0.0, 2.0, size=inp.beta.shape).astype(np.float32)
+    else:
+        inp.log_alpha[:] = float(gate)
+    d_o, d_final = W.incoming_grads(inp, seed=65)
+    _check(inp, d_o, d_final, f"gates {gate}")
+
+
+def test_bwd_prefill_shape_sampled():
+    """H=16, dk=dv=128, bf16, 1024 tokens per sequence (16 chunks), two
+    heads checked against the oracle."""
+    inp = W.chunk_inputs(2, 1024, 16, 128, 128, "bf16", seed=66)
+    d_o, d_final = W.incoming_grads(inp, seed=67)
+    _check(inp, d_o, d_final, "B2 T1024 H16 d128 bf16", heads=[0, 11])
+
+
+def test_bwd_malformed_cu_reported():
+    inp = W.packed_inputs([10, 20], H=1, dk=64, dv=32, in_dtype="fp32", seed=68)
+    d_o, _ = W.incoming_grads(inp, seed=69, final=False)
+    q, k, v = dev(inp.q), dev(inp.k), dev(inp.v)
+    la, b = dev(inp.log_alpha), dev(inp.beta)
+    cu = torch.tensor([0, 25, 30], dtype=torch.int32, device="cuda")
+    bad = torch.tensor([0, 31, 30], dtype=torch.int32, device="cuda")
+    ws = torch.empty(1 << 24, dtype=torch.uint8, device="cuda")
+    gdn.chunk_bwd(q, k, v, la, b, dev(d_o), cu_seqlens=cu, workspace=ws)
+    assert gdn.chunk_fwd_check(ws) == 0
+    dq, *_ = gdn.chunk_bwd(q, k, v, la, b, dev(d_o), cu_seqlens=bad, workspace=ws)
+    assert gdn.chunk_fwd_check(ws) == 2

@@ -161,6 +161,19 @@ def chunk_inputs(B, T, H, dk, dv, in_dtype="bf16", seed=0, *, lengths=None,
                        cu_seqlens=cu, seed=seed)
 
 
+def incoming_grads(inp: ChunkInputs, seed: int, final: bool = True):
+    """Seeded gradients of a loss with respect to o ([B,T,H,dv]) and to the
+    final state ([N,H,dv,dk], or None), standard normal fp32, for the
+    backward pass."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    B, T, H, _ = inp.q.shape
+    dv, dk = inp.v.shape[-1], inp.q.shape[-1]
+    d_o = rng.standard_normal((B, T, H, dv), dtype=np.float32)
+    N = B if inp.cu_seqlens is None else len(inp.cu_seqlens) - 1
+    d_final = rng.standard_normal((N, H, dv, dk), dtype=np.float32) if final else None
+    return d_o, d_final
+
+
 def packed_lengths(n, lo, hi, seed):
     rng = np.random.Generator(np.random.PCG64(seed))
     return rng.integers(lo, hi, size=n, endpoint=True).astype(np.int64)
