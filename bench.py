@@ -7,7 +7,9 @@ A step is one chunked prefill over the prefill workload (B=4, H=16, L=4096,
 dk=dv=128, C=64, bf16 q/k/v, fp32 gates, fp32 o and states), inputs resident
 in HBM.  `value` is prefill tokens/s.  The same run times 1000 in-place decode
 steps of the decode workload (256 sequences x 16 heads, 128x128 fp32 states)
-and reports steps/s under "decode".  Each kernel's average duration comes from
+and reports steps/s under "decode", the continuation call (256 resident states
+take 2..16 tokens each) under "continuation" and the backward pass over the
+prefill workload under "backward".  Each kernel's average duration comes from
 HIP events the library records around its launches on the launch stream; the
 roofline objects use the algorithmic bytes and flops of the method (counted
 below) over that duration.  The CPU baseline is the fp64 oracle on a bounded
@@ -43,6 +45,18 @@ def chunk_min_bytes(B, T, H, dk, dv, N, in_bytes, out_bytes, has_init, has_final
     b = th * (2 * dk + dv) * in_bytes + th * 2 * 4 + th * dv * out_bytes
     st = N * H * dv * dk * 4
     return b + (st if has_init else 0) + (st if has_final else 0)
+
+
+MFMA_F32_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix peak, TFLOP/s
+
+
+def bwd_grad_flops_per_chunk_head(dk, dv, c=C):
+    # The gradient kernel's products, triangular ones at their triangular size (t = c(c+1)/2):
+    # K S^T, Q S^T, K dS^T (6 c dk dv); M Y, P^T dO, M^T dV', dO V'^T, dV' Y^T (5 * 2 t dv);
+    # dO S, dY S, V' dS (6 c dv dk); T^T dT and W T^T (about 2 * c^3 / 3); K K^T, Q K^T (2 * 2 t dk);
+    # (dP o Gamma) K, (dP o Gamma)^T Q (2 * 2 t dk) and (dK + dK^T) K (2 c^2 dk).
+    t = c * (c + 1) / 2
+    return 12 * c * dk * dv + 10 * t * dv + 2 * c ** 3 / 3 + 8 * t * dk + 2 * c * c * dk
 
 
 def decode_min_bytes(N, H, dk, dv, in_bytes, out_bytes):
@@ -234,6 +248,58 @@ def run_continuation(args, gdn, W, dev):
     return res
 
 
+def run_backward(args, gdn, W, dev):
+    """gdn_chunk_bwd on the prefill workload: gradients of o (fp32, standard normal) and of the final
+    state flow back to q, k, v, log alpha, beta and the (zero) initial state."""
+    import torch
+    inp = W.prefill()
+    B, T, H, dk, dv = inp.B, inp.T, inp.H, inp.dk, inp.dv
+    q, k, v = (_to(x, dev, torch.bfloat16) for x in (inp.q, inp.k, inp.v))
+    la, be = _to(inp.log_alpha, dev, torch.float32), _to(inp.beta, dev, torch.float32)
+    d_o_np, d_fin_np = W.incoming_grads(inp, seed=12)
+    d_o, d_fin = _to(d_o_np, dev, torch.float32), _to(d_fin_np, dev, torch.float32)
+    del d_o_np, d_fin_np
+    ws = torch.empty(gdn.chunk_bwd_workspace_size(B, T, H, dk, dv, B), dtype=torch.uint8, device=dev)
+
+    def step():
+        gdn.chunk_bwd(q, k, v, la, be, d_o, d_final=d_fin, workspace=ws)
+
+    steps = max(1, args.steps // 2)
+    for _ in range(max(1, args.warmup // 2)):
+        step()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / steps
+    with gdn.profile() as prof:
+        for _ in range(steps):
+            step()
+    torch.cuda.synchronize()
+    kernels = {name: {"launches": n_, "avg_us": 1e3 * t / n_} for name, (n_, t) in prof.results.items()}
+    dom = max(kernels, key=lambda x: kernels[x]["avg_us"] * kernels[x]["launches"])
+    items = B * ((T + C - 1) // C) * H
+    gflops = bwd_grad_flops_per_chunk_head(dk, dv) * items
+    g_s = kernels["gdn_bwd_grad"]["avg_us"] * 1e-6
+    res = {
+        "value": B * T / (ms * 1e-3), "unit": "tokens/s", "ms_per_call": ms, "calls": steps,
+        "config": {"workload": "backward", "B": B, "L": T, "H": H, "dk": dk, "dv": dv, "chunk": C,
+                   "in_dtype": "bf16", "grads": "fp32", "d_final": "fp32"},
+        "roofline": {"kernel": "gdn_bwd_grad", "bound": "mfma", "achieved": gflops / g_s / 1e12,
+                     "peak": MFMA_F32_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": gflops / g_s / 1e12 / MFMA_F32_PEAK_TFLOPS,
+                     "traffic": measured_traffic("gdn_bwd_grad"), "algorithmic_flops": gflops,
+                     "dominant_kernel": dom},
+        "kernels": kernels,
+    }
+    del q, k, v, la, be, d_o, d_fin, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def run_cpu_baseline(args, inp):
     """The fp64 oracle on the prefill workload's inputs: a prefix of every sequence, grown until one
     pass takes about --cpu-seconds; once the prefix is the whole workload, whole passes are repeated
@@ -273,7 +339,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--out-dtype", choices=["fp32", "bf16"], default="fp32",
                     help="prefill output dtype (the state is fp32 either way)")
-    ap.add_argument("--only", choices=["prefill", "decode", "continuation", "copy"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "continuation", "backward", "copy"], default=None,
                     help="run one leg only (for profiler runs) and print its part of the line; "
                          "'copy' runs a plain 256 MiB read + 256 MiB write elementwise kernel used to "
                          "calibrate the FETCH_SIZE / WRITE_SIZE counters")
@@ -302,6 +368,9 @@ def main():
     if args.only == "continuation":
         print(json.dumps({"continuation": run_continuation(args, gdn, W, dev)}), flush=True)
         return
+    if args.only == "backward":
+        print(json.dumps({"backward": run_backward(args, gdn, W, dev)}), flush=True)
+        return
     if args.only == "copy":
         n = 64 * 1024 * 1024                      # 256 MiB of fp32
         a = torch.ones(n, dtype=torch.float32, device=dev)
@@ -318,6 +387,7 @@ def main():
         return
     decode = run_decode(args, gdn, W, dev)
     cont = run_continuation(args, gdn, W, dev)
+    bwd = run_backward(args, gdn, W, dev)
     cpu = None if args.no_cpu_baseline else run_cpu_baseline(args, inp)
     out = {
         "metric": METRIC,
@@ -338,6 +408,7 @@ def main():
         "cpu_baseline": cpu,
         "decode": decode,
         "continuation": cont,
+        "backward": bwd,
         "kernels": pre["kernels"],
         "device": torch.cuda.get_device_name(0),
     }

@@ -190,6 +190,13 @@ def chunk_fwd(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, *, out
     return o, final_state
 
 
+def chunk_bwd_workspace_size(B, T, H, dk, dv, num_seqs, in_dtype=torch.bfloat16, chunk=CHUNK) -> int:
+    d = _desc(B, T, H, dk, dv, num_seqs, _DT[in_dtype], GDN_FP32, chunk)
+    n = ctypes.c_size_t(0)
+    _check(load().gdn_chunk_bwd_workspace_size(ctypes.byref(d), ctypes.byref(n)))
+    return int(n.value)
+
+
 def chunk_bwd(q, k, v, log_alpha, beta, d_o, init_state=None, d_final=None, cu_seqlens=None, *,
               d_init=True, workspace=None, chunk=CHUNK):
     """Gradients of chunk_fwd's o and final state with respect to its inputs.

@@ -31,7 +31,7 @@
 //
 // Four kernels:
 //   B1 bwd_prep_kernel      per (chunk row, head): g, gamma, kappa, T, P (fp32, VALU).
-//   B2 bwd_fwd_pass_kernel  per (sequence, head, 16 value columns), chunks in order:
+//   B2 bwd_fwd_pass_kernel  per (sequence, head, 16 value columns), four waves, chunks in order:
 //                           replays the state pass and stores the state at every
 //                           chunk start (the checkpoints).
 //   B3 bwd_rev_pass_kernel  the same, chunks in reverse: the gradient of the state
@@ -106,8 +106,16 @@ constexpr int kVecFloats = 4 * C;
 
 // ============================================================================
 // B1: g, gamma, kappa, T = (I + A)^{-1} and P per (chunk row, head).
-// One 256-thread block per item; Q and K rows staged in LDS as fp32.
+// One 256-thread block per item; Q and K rows staged in LDS as fp32.  The
+// 10 lower 16 x 16 tiles of K K^T and Q K^T come from the matrix cores
+// (waves take tiles w, w + 4, w + 8); T by forward substitution, column c of
+// T solving (I + A) t = e_c on its own (columns need no exchange).
 // ============================================================================
+__device__ __forceinline__ void tri_tile(int t, int &a, int &b) {
+    a = t < 1 ? 0 : (t < 3 ? 1 : (t < 6 ? 2 : 3));
+    b = t - a * (a + 1) / 2;
+}
+
 template <typename in_t, int DK>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(int H, int T, int cpr, int urows,
                                                        const int32_t *__restrict__ meta,
@@ -117,13 +125,13 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(int H, int T, int cpr, in
                                                        const float *__restrict__ log_alpha,
                                                        const float *__restrict__ beta, float *__restrict__ ws_t,
                                                        float *__restrict__ ws_p, float *__restrict__ ws_vec) {
-    constexpr int KP = DK + 1;
+    constexpr int KP = DK + 4, NA = DK / 16, AP = C + 1;
     extern __shared__ __align__(16) float smem[];
     float *sq = smem;                 // [C][KP]
     float *sk = sq + C * KP;          // [C][KP]
-    float *sa = sk + C * KP;          // [C][C + 1]  A, then scratch
-    float *st = sa + C * (C + 1);     // [C][C + 1]  T
-    float *sg = st + C * (C + 1);     // [C]
+    float *sa = sk + C * KP;          // [C][AP]  A (strictly lower)
+    float *st = sa + C * AP;          // [C][AP]  T transposed
+    float *sg = st + C * AP;          // [C]
     float *sb = sg + C;               // [C]
     if (!cpr && meta[1] != 0) return;   // malformed cu_seqlens: nothing is written
     const int nrows = cpr ? urows : meta[0];
@@ -131,7 +139,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(int H, int T, int cpr, in
     if (row >= nrows) return;
     int tok0, len;
     row_span(row, T, cpr, row_tok, row_len, tok0, len);
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, nn = l & 15, jj = l >> 4;
 
     for (int idx = tid * 8; idx < C * DK; idx += 256 * 8) {
         const int r = idx / DK, c = idx % DK;
@@ -144,11 +152,10 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(int H, int T, int cpr, in
 #pragma unroll
             for (int e = 0; e < 8; ++e) xq[e] = xk[e] = 0.f;
         }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            sq[r * KP + c + e] = xq[e];
-            sk[r * KP + c + e] = xk[e];
-        }
+        *reinterpret_cast<float4_t *>(sq + r * KP + c) = float4_t{xq[0], xq[1], xq[2], xq[3]};
+        *reinterpret_cast<float4_t *>(sq + r * KP + c + 4) = float4_t{xq[4], xq[5], xq[6], xq[7]};
+        *reinterpret_cast<float4_t *>(sk + r * KP + c) = float4_t{xk[0], xk[1], xk[2], xk[3]};
+        *reinterpret_cast<float4_t *>(sk + r * KP + c + 4) = float4_t{xk[4], xk[5], xk[6], xk[7]};
     }
     if (tid < C) {
         const bool in = tid < len;
@@ -173,89 +180,129 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(int H, int T, int cpr, in
         vec[2 * C + tid] = expf(glast - sg[tid]);
         vec[3 * C + tid] = sb[tid];
     }
-    // A (strictly lower) into sa, P (lower with the diagonal) straight to HBM.
+    // K K^T and Q K^T tiles; A (strictly lower) to LDS, P (lower with the diagonal) to HBM.
     float *P = ws_p + (int64_t)item * C * C;
-    for (int e = tid; e < C * C; e += 256) {
-        const int r = e / C, i = e % C;
-        float a = 0.f, p = 0.f;
-        if (i <= r) {
-            float kk = 0.f, qk = 0.f;
-            for (int c = 0; c < DK; ++c) {
-                kk += sk[r * KP + c] * sk[i * KP + c];
-                qk += sq[r * KP + c] * sk[i * KP + c];
-            }
-            const float gm = expf(sg[r] - sg[i]);
-            p = qk * gm;
-            if (i < r) a = sb[r] * gm * kk;
+    for (int t = w; t < 16; t += 4) {
+        if (t >= 10) {   // upper tiles of P are zero
+            const int a = (t - 10) / 3 < 1 ? 0 : ((t - 10) < 5 ? 1 : 2);
+            const int b = a == 0 ? 1 + (t - 10) : (a == 1 ? (t - 10) - 1 : 3);
+            // (0,1) (0,2) (0,3) (1,2) (1,3) (2,3)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) P[(16 * a + 4 * jj + i) * C + 16 * b + nn] = 0.f;
+            continue;
         }
-        sa[r * (C + 1) + i] = a;
-        P[e] = p;
+        int a, b;
+        tri_tile(t, a, b);
+        float4_t kk = zero4(), qk = zero4();
+        tile_mm(kk, 0, NA, [&](int rr, int kx) { return sk[(16 * a + rr) * KP + kx]; },
+                [&](int kx, int cc) { return sk[(16 * b + cc) * KP + kx]; });
+        tile_mm(qk, 0, NA, [&](int rr, int kx) { return sq[(16 * a + rr) * KP + kx]; },
+                [&](int kx, int cc) { return sk[(16 * b + cc) * KP + kx]; });
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 16 * a + 4 * jj + i, c = 16 * b + nn;
+            const float gm = c <= r ? expf(sg[r] - sg[c]) : 0.f;
+            P[r * C + c] = qk[i] * gm;
+            sa[r * AP + c] = c < r ? sb[r] * gm * kk[i] : 0.f;
+        }
     }
     __syncthreads();
-    // T = (I + A)^{-1} by forward substitution, one row per step: thread c
-    // owns column c, T[r][c] = [r == c] - sum_{c <= i < r} A[r][i] T[i][c].
-    for (int r = 0; r < C; ++r) {
-        if (tid < C) {
-            const int c = tid;
-            float x = 0.f;
-            if (c <= r) {
-                x = (c == r) ? 1.f : 0.f;
-                for (int i = c; i < r; ++i) x -= sa[r * (C + 1) + i] * st[i * (C + 1) + c];
-            }
-            st[r * (C + 1) + c] = x;
+    // Column c of T belongs to the four lanes 4c .. 4c + 3 (lane q sums the
+    // terms i = q mod 4; two DPP steps add the quad).  T is kept transposed,
+    // st[c][i] = T[i][c], and each lane stores exactly the entries it reads
+    // later, so the solve needs no barrier.
+    {
+        const int c = tid >> 2, qd = tid & 3;
+        for (int r = 0; r < C; ++r) {
+            float acc = 0.f;
+#pragma unroll 4
+            for (int i = qd; i < r; i += 4) acc += sa[r * AP + i] * st[c * AP + i];
+            acc += dpp_mov<0xB1>(acc);
+            acc += dpp_mov<0x4E>(acc);
+            const float x = r < c ? 0.f : (r == c ? 1.f : -acc);
+            if ((r & 3) == qd) st[c * AP + r] = x;
         }
-        __syncthreads();
     }
+    __syncthreads();
     float *Tm = ws_t + (int64_t)item * C * C;
-    for (int e = tid; e < C * C; e += 256) Tm[e] = st[(e / C) * (C + 1) + e % C];
+    for (int e = tid; e < C * C; e += 256) Tm[e] = st[(e % C) * AP + e / C];
 }
 
 // ============================================================================
 // B2: the state pass again, storing the state at every chunk start.
-// One wave per (sequence, head, 16 value columns); the wave holds S^T for its
-// columns (dk x 16) in DK / 16 accumulator tiles: tile a, element i of lane
-// (n, j) = S[v0 + n][16 a + 4 j + i].
+// One 256-thread block per (sequence, head, 16 value columns).  S^T for the
+// columns (dk x 16) lives in DK / 16 accumulator tiles spread over the four
+// waves (wave w holds tiles w, w + 4, ...): tile a, element i of lane (n, j)
+// = S[v0 + n][16 a + 4 j + i].  Per chunk wave w forms rows 16 w .. 16 w + 15
+// of X = K S^T, Y and V' = M Y; the tiles, Y and V' pass through LDS.
 // ============================================================================
+template <int DK>
+struct PassSmem {
+    static constexpr int KP = DK + 4;   // K and Q rows
+    static constexpr int SP = 16 + 1;   // S^T / dS^T [dk][16], value blocks [C][16]
+    static constexpr int off_k = 0;
+    static constexpr int off_s = off_k + C * KP;
+    static constexpr int off_a = off_s + DK * SP;      // Y (forward) or dO (reverse)
+    static constexpr int off_b = off_a + C * SP;       // V' (forward) or dV' (reverse)
+    static constexpr int off_c = off_b + C * SP;       // dY (reverse)
+    static constexpr int MP = C + 1;    // M = T diag(beta) and P
+    static constexpr int off_m = off_c + C * SP;
+    static constexpr int off_v = off_m + C * MP;       // gamma, kappa, beta
+    static constexpr int off_p = off_v + 3 * C;        // P (reverse pass only)
+    static constexpr int off_q = off_p + C * MP;       // Q (reverse pass only)
+    static constexpr size_t bytes_fwd = sizeof(float) * off_p;
+    static constexpr size_t bytes_rev = sizeof(float) * (off_q + C * KP);
+};
+
 template <typename in_t, int DK>
-__global__ __launch_bounds__(64) void bwd_fwd_pass_kernel(int H, int DV, int T, int cpr, int nvt,
-                                                          const int32_t *__restrict__ meta,
-                                                          const int32_t *__restrict__ cu_ws,
-                                                          const int32_t *__restrict__ row0,
-                                                          const int32_t *__restrict__ row_tok,
-                                                          const int32_t *__restrict__ row_len,
-                                                          const in_t *__restrict__ k, const in_t *__restrict__ v,
-                                                          const float *__restrict__ ws_t,
-                                                          const float *__restrict__ ws_vec,
-                                                          const float *__restrict__ init_state,
-                                                          float *__restrict__ ws_ck) {
-    constexpr int KP = DK + 4;
-    constexpr int NA = DK / 16;
+__global__ __launch_bounds__(256) void bwd_fwd_pass_kernel(int H, int DV, int T, int cpr, int nvt,
+                                                           const int32_t *__restrict__ meta,
+                                                           const int32_t *__restrict__ cu_ws,
+                                                           const int32_t *__restrict__ row0,
+                                                           const int32_t *__restrict__ row_tok,
+                                                           const int32_t *__restrict__ row_len,
+                                                           const in_t *__restrict__ k, const in_t *__restrict__ v,
+                                                           const float *__restrict__ ws_t,
+                                                           const float *__restrict__ ws_vec,
+                                                           const float *__restrict__ init_state,
+                                                           float *__restrict__ ws_ck) {
+    using L = PassSmem<DK>;
+    constexpr int KP = L::KP, SP = L::SP, MP = L::MP, NA = DK / 16, NT = (NA + 3) / 4;
     extern __shared__ __align__(16) float smem[];
-    float *sk = smem;               // [C][KP]
-    float *sv = sk + C * KP;        // gamma, kappa, beta: [3][C]
+    float *sk = smem + L::off_k, *ss = smem + L::off_s, *sy = smem + L::off_a, *svp = smem + L::off_b;
+    float *sm = smem + L::off_m;
+    float *sv = smem + L::off_v;   // gamma [C], kappa [C], beta [C]
     if (!cpr && meta[1] != 0) return;
     const int nh = blockIdx.x / nvt, vt = blockIdx.x % nvt;
     const int n = nh / H, h = nh % H, v0 = vt * 16;
-    const int l = threadIdx.x, nn = l & 15, jj = l >> 4;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, nn = l & 15, jj = l >> 4;
     int r0, nrows;
     seq_rows(n, T, cpr, cu_ws, row0, r0, nrows);
 
-    float4_t s[NA];
+    float4_t s[NT];   // tiles a = w + 4 t
 #pragma unroll
-    for (int a = 0; a < NA; ++a)
-        s[a] = init_state ? *reinterpret_cast<const float4_t *>(init_state + ((int64_t)nh * DV + v0 + nn) * DK +
-                                                                16 * a + 4 * jj)
-                          : zero4();
+    for (int t = 0; t < NT; ++t) {
+        const int a = w + 4 * t;
+        s[t] = (init_state && a < NA)
+                   ? *reinterpret_cast<const float4_t *>(init_state + ((int64_t)nh * DV + v0 + nn) * DK + 16 * a + 4 * jj)
+                   : zero4();
+    }
     for (int c = 0; c < nrows; ++c) {
         const int row = r0 + c;
         int tok0, len;
         row_span(row, T, cpr, row_tok, row_len, tok0, len);
         const int64_t item = (int64_t)row * H + h;
-        float *ck = ws_ck + (item * DV + v0 + nn) * DK + 4 * jj;
+        __syncthreads();   // the previous chunk's LDS contents are no longer read
 #pragma unroll
-        for (int a = 0; a < NA; ++a) *reinterpret_cast<float4_t *>(ck + 16 * a) = s[a];
-        __syncthreads();   // the previous chunk's K is no longer read
-        for (int idx = l * 8; idx < C * DK; idx += 64 * 8) {
+        for (int t = 0; t < NT; ++t) {
+            const int a = w + 4 * t;
+            if (a < NA) {
+                *reinterpret_cast<float4_t *>(ws_ck + (item * DV + v0 + nn) * DK + 16 * a + 4 * jj) = s[t];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ss[(16 * a + 4 * jj + i) * SP + nn] = s[t][i];
+            }
+        }
+        for (int idx = tid * 8; idx < C * DK; idx += 256 * 8) {
             const int r = idx / DK, cc = idx % DK;
             float x[8];
             if (r < len) {
@@ -268,110 +315,111 @@ __global__ __launch_bounds__(64) void bwd_fwd_pass_kernel(int H, int DV, int T, 
             *reinterpret_cast<float4_t *>(sk + r * KP + cc + 4) = float4_t{x[4], x[5], x[6], x[7]};
         }
         const float *vec = ws_vec + item * kVecFloats;
-        sv[l] = vec[C + l];
-        sv[C + l] = vec[2 * C + l];
-        sv[2 * C + l] = vec[3 * C + l];
+        if (tid < 3 * C) sv[tid] = vec[C + tid];
+        const float *Tm = ws_t + item * C * C;
+        {
+            const float4_t b4 = *reinterpret_cast<const float4_t *>(vec + 3 * C + (tid * 4) % C);
+            for (int e = tid * 4; e < C * C; e += 256 * 4) {
+                const float4_t t4 = *reinterpret_cast<const float4_t *>(Tm + e);
+                const int r = e / C, cc = e % C;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sm[r * MP + cc + i] = t4[i] * b4[i];
+            }
+        }
         __syncthreads();
         const float glast = len > 0 ? sv[len - 1] : 1.f;
-        const float *Tm = ws_t + item * C * C;
-        // X = K S^T and Y = V - diag(gamma) X, four 16-row blocks
-        float4_t y[4];
+        const int rw = 16 * w;
+        // rows of the wave: X = K S^T, Y = V - diag(gamma) X
+        float4_t x = zero4();
+        tile_mm(x, 0, NA, [&](int rr, int kx) { return sk[(rw + rr) * KP + kx]; },
+                [&](int kx, int cc) { return ss[kx * SP + cc]; });
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-            float4_t x = zero4();
-#pragma unroll
-            for (int kt = 0; kt < NA; ++kt) {
-                const float4_t kr = *reinterpret_cast<const float4_t *>(sk + (16 * rb + nn) * KP + 16 * kt + 4 * jj);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) mfma4(x, kr[i], s[kt][i]);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 16 * rb + 4 * jj + i;
-                const float vv = r < len ? to_f32(v[((int64_t)(tok0 + r) * H + h) * DV + v0 + nn]) : 0.f;
-                y[rb][i] = vv - sv[r] * x[i];
-            }
+        for (int i = 0; i < 4; ++i) {
+            const int r = rw + 4 * jj + i;
+            const float vv = r < len ? to_f32(v[((int64_t)(tok0 + r) * H + h) * DV + v0 + nn]) : 0.f;
+            sy[r * SP + nn] = vv - sv[r] * x[i];
         }
-        // V' = M Y with M = T diag(beta), lower block triangular
-        float4_t vp[4];
+        __syncthreads();
+        // V' = M Y, M = T diag(beta) lower block triangular
+        float4_t vp = zero4();
+        tile_mm(vp, 0, w + 1, [&](int rr, int kx) { return sm[(rw + rr) * MP + kx]; },
+                [&](int kx, int cc) { return sy[kx * SP + cc]; });
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-            vp[rb] = zero4();
+        for (int i = 0; i < 4; ++i) svp[(rw + 4 * jj + i) * SP + nn] = vp[i];
+        __syncthreads();
+        // S^T <- gamma_last S^T + K^T diag(kappa) V' on the wave's tiles
 #pragma unroll
-            for (int kt = 0; kt <= rb; ++kt) {
-                const float4_t tr = *reinterpret_cast<const float4_t *>(Tm + (16 * rb + nn) * C + 16 * kt + 4 * jj);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) mfma4(vp[rb], tr[i] * sv[2 * C + 16 * kt + 4 * jj + i], y[kt][i]);
+        for (int t = 0; t < NT; ++t) {
+            const int a = w + 4 * t;
+            if (a < NA) {
+                float4_t acc = glast * s[t];
+                tile_mm(acc, 0, 4, [&](int rr, int kx) { return sk[kx * KP + 16 * a + rr] * sv[C + kx]; },
+                        [&](int kx, int cc) { return svp[kx * SP + cc]; });
+                s[t] = acc;
             }
-        }
-        // S^T <- gamma_last S^T + K^T diag(kappa) V'
-#pragma unroll
-        for (int a = 0; a < NA; ++a) {
-            float4_t acc = glast * s[a];
-#pragma unroll
-            for (int kt = 0; kt < 4; ++kt) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = 16 * kt + 4 * jj + i;
-                    mfma4(acc, sk[r * KP + 16 * a + nn] * sv[C + r], vp[kt][i]);
-                }
-            }
-            s[a] = acc;
         }
     }
 }
 
 // ============================================================================
-// B3: the reverse state pass.  One wave per (sequence, head, 16 value
-// columns) holds dS^T for its columns in the layout of B2.  Chunks in
-// reverse: store dS (the gradient of the state at the chunk's end), then
+// B3: the reverse state pass, in the layout of B2 with dS^T in the tiles.
+// Chunks in reverse: store dS (the gradient of the state at the chunk's
+// end), then
 //   dV' = P^T dO + diag(kappa) K dS^T,  dY = M^T dV',
 //   dS  <- gamma_last dS + dO^T diag(gamma) Q - dY^T diag(gamma) K.
 // What is left after the first chunk is the initial state's gradient.
 // ============================================================================
 template <typename in_t, int DK>
-__global__ __launch_bounds__(64) void bwd_rev_pass_kernel(int H, int DV, int T, int cpr, int nvt,
-                                                          const int32_t *__restrict__ meta,
-                                                          const int32_t *__restrict__ cu_ws,
-                                                          const int32_t *__restrict__ row0,
-                                                          const int32_t *__restrict__ row_tok,
-                                                          const int32_t *__restrict__ row_len,
-                                                          const in_t *__restrict__ q, const in_t *__restrict__ k,
-                                                          const float *__restrict__ d_o,
-                                                          const float *__restrict__ ws_t,
-                                                          const float *__restrict__ ws_p,
-                                                          const float *__restrict__ ws_vec,
-                                                          const float *__restrict__ d_final,
-                                                          float *__restrict__ ws_ds, float *__restrict__ d_init) {
-    constexpr int KP = DK + 4;
-    constexpr int NA = DK / 16;
+__global__ __launch_bounds__(256) void bwd_rev_pass_kernel(int H, int DV, int T, int cpr, int nvt,
+                                                           const int32_t *__restrict__ meta,
+                                                           const int32_t *__restrict__ cu_ws,
+                                                           const int32_t *__restrict__ row0,
+                                                           const int32_t *__restrict__ row_tok,
+                                                           const int32_t *__restrict__ row_len,
+                                                           const in_t *__restrict__ q, const in_t *__restrict__ k,
+                                                           const float *__restrict__ d_o,
+                                                           const float *__restrict__ ws_t,
+                                                           const float *__restrict__ ws_p,
+                                                           const float *__restrict__ ws_vec,
+                                                           const float *__restrict__ d_final,
+                                                           float *__restrict__ ws_ds, float *__restrict__ d_init) {
+    using L = PassSmem<DK>;
+    constexpr int KP = L::KP, SP = L::SP, MP = L::MP, NA = DK / 16, NT = (NA + 3) / 4;
     extern __shared__ __align__(16) float smem[];
-    float *sk = smem;               // [C][KP]
-    float *sq = sk + C * KP;        // [C][KP]
-    float *sv = sq + C * KP;        // gamma, kappa, beta: [3][C]
+    float *sk = smem + L::off_k, *ss = smem + L::off_s;
+    float *so = smem + L::off_a, *sdvp = smem + L::off_b, *sdy = smem + L::off_c, *sv = smem + L::off_v;
+    float *sm = smem + L::off_m, *sp = smem + L::off_p, *sq = smem + L::off_q;
     if (!cpr && meta[1] != 0) return;
     const int nh = blockIdx.x / nvt, vt = blockIdx.x % nvt;
     const int n = nh / H, h = nh % H, v0 = vt * 16;
-    const int l = threadIdx.x, nn = l & 15, jj = l >> 4;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, nn = l & 15, jj = l >> 4;
     int r0, nrows;
     seq_rows(n, T, cpr, cu_ws, row0, r0, nrows);
 
-    float4_t s[NA];
+    float4_t s[NT];
 #pragma unroll
-    for (int a = 0; a < NA; ++a)
-        s[a] = d_final ? *reinterpret_cast<const float4_t *>(d_final + ((int64_t)nh * DV + v0 + nn) * DK + 16 * a +
-                                                             4 * jj)
-                       : zero4();
+    for (int t = 0; t < NT; ++t) {
+        const int a = w + 4 * t;
+        s[t] = (d_final && a < NA)
+                   ? *reinterpret_cast<const float4_t *>(d_final + ((int64_t)nh * DV + v0 + nn) * DK + 16 * a + 4 * jj)
+                   : zero4();
+    }
     for (int c = nrows - 1; c >= 0; --c) {
         const int row = r0 + c;
         int tok0, len;
         row_span(row, T, cpr, row_tok, row_len, tok0, len);
         const int64_t item = (int64_t)row * H + h;
-        float *ds = ws_ds + (item * DV + v0 + nn) * DK + 4 * jj;
-#pragma unroll
-        for (int a = 0; a < NA; ++a) *reinterpret_cast<float4_t *>(ds + 16 * a) = s[a];
         __syncthreads();
-        for (int idx = l * 8; idx < C * DK; idx += 64 * 8) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const int a = w + 4 * t;
+            if (a < NA) {
+                *reinterpret_cast<float4_t *>(ws_ds + (item * DV + v0 + nn) * DK + 16 * a + 4 * jj) = s[t];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ss[(16 * a + 4 * jj + i) * SP + nn] = s[t][i];
+            }
+        }
+        for (int idx = tid * 8; idx < C * DK; idx += 256 * 8) {
             const int r = idx / DK, cc = idx % DK;
             float xk[8], xq[8];
             if (r < len) {
@@ -387,75 +435,71 @@ __global__ __launch_bounds__(64) void bwd_rev_pass_kernel(int H, int DV, int T, 
             *reinterpret_cast<float4_t *>(sq + r * KP + cc) = float4_t{xq[0], xq[1], xq[2], xq[3]};
             *reinterpret_cast<float4_t *>(sq + r * KP + cc + 4) = float4_t{xq[4], xq[5], xq[6], xq[7]};
         }
+        for (int e = tid; e < C * 16; e += 256) {
+            const int r = e / 16, cc = e % 16;
+            so[r * SP + cc] = r < len ? d_o[((int64_t)(tok0 + r) * H + h) * DV + v0 + cc] : 0.f;
+        }
         const float *vec = ws_vec + item * kVecFloats;
-        sv[l] = vec[C + l];
-        sv[C + l] = vec[2 * C + l];
-        sv[2 * C + l] = vec[3 * C + l];
-        __syncthreads();
-        const float glast = len > 0 ? sv[len - 1] : 1.f;
+        if (tid < 3 * C) sv[tid] = vec[C + tid];
         const float *Tm = ws_t + item * C * C;
         const float *Pm = ws_p + item * C * C;
-        // dO of the chunk as B operands: element i of k-tile kt = dO[16 kt + 4 j + i][v0 + n]
-        float4_t dof[4];
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 16 * kt + 4 * jj + i;
-                dof[kt][i] = r < len ? d_o[((int64_t)(tok0 + r) * H + h) * DV + v0 + nn] : 0.f;
-            }
-        // dV' = P^T dO + diag(kappa) K dS^T
-        float4_t dvp[4];
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-            float4_t x = zero4();
-#pragma unroll
-            for (int kt = 0; kt < NA; ++kt) {
-                const float4_t kr = *reinterpret_cast<const float4_t *>(sk + (16 * rb + nn) * KP + 16 * kt + 4 * jj);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) mfma4(x, kr[i], s[kt][i]);
-            }
-            float4_t acc;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] = sv[C + 16 * rb + 4 * jj + i] * x[i];
-#pragma unroll
-            for (int kt = rb; kt < 4; ++kt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) mfma4(acc, Pm[(16 * kt + 4 * jj + i) * C + 16 * rb + nn], dof[kt][i]);
-            dvp[rb] = acc;
-        }
-        // dY = M^T dV', M^T[r][x] = T[x][r] beta[r]
-        float4_t dy[4];
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-            dy[rb] = zero4();
-            const float br = sv[2 * C + 16 * rb + nn];
-#pragma unroll
-            for (int kt = rb; kt < 4; ++kt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) mfma4(dy[rb], Tm[(16 * kt + 4 * jj + i) * C + 16 * rb + nn] * br, dvp[kt][i]);
-        }
-        // dS^T <- gamma_last dS^T + Q^T diag(gamma) dO - K^T diag(gamma) dY
-#pragma unroll
-        for (int a = 0; a < NA; ++a) {
-            float4_t acc = glast * s[a];
-#pragma unroll
-            for (int kt = 0; kt < 4; ++kt) {
+        {
+            // M = T diag(beta): a thread's four columns are the same in every row it stages
+            const float4_t b4 = *reinterpret_cast<const float4_t *>(vec + 3 * C + (tid * 4) % C);
+            for (int e = tid * 4; e < C * C; e += 256 * 4) {
+                const float4_t t4 = *reinterpret_cast<const float4_t *>(Tm + e);
+                const float4_t p4 = *reinterpret_cast<const float4_t *>(Pm + e);
+                const int r = e / C, cc = e % C;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int r = 16 * kt + 4 * jj + i;
-                    const float gr = sv[r];
-                    mfma4(acc, sq[r * KP + 16 * a + nn] * gr, dof[kt][i]);
-                    mfma4(acc, -sk[r * KP + 16 * a + nn] * gr, dy[kt][i]);
+                    sm[r * MP + cc + i] = t4[i] * b4[i];
+                    sp[r * MP + cc + i] = p4[i];
                 }
             }
-            s[a] = acc;
+        }
+        __syncthreads();
+        const float glast = len > 0 ? sv[len - 1] : 1.f;
+        const int rw = 16 * w;
+        // dV' = P^T dO + diag(kappa) K dS^T on the wave's rows
+        float4_t x = zero4();
+        tile_mm(x, 0, NA, [&](int rr, int kx) { return sk[(rw + rr) * KP + kx]; },
+                [&](int kx, int cc) { return ss[kx * SP + cc]; });
+        float4_t dvp;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dvp[i] = sv[C + rw + 4 * jj + i] * x[i];
+        tile_mm(dvp, w, 4, [&](int rr, int kx) { return sp[kx * MP + rw + rr]; },
+                [&](int kx, int cc) { return so[kx * SP + cc]; });
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sdvp[(rw + 4 * jj + i) * SP + nn] = dvp[i];
+        __syncthreads();
+        // dY = M^T dV', M^T[r][x] = T[x][r] beta[r]
+        float4_t dy = zero4();
+        tile_mm(dy, w, 4, [&](int rr, int kx) { return sm[kx * MP + rw + rr]; },
+                [&](int kx, int cc) { return sdvp[kx * SP + cc]; });
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sdy[(rw + 4 * jj + i) * SP + nn] = dy[i];
+        __syncthreads();
+        // dS^T <- gamma_last dS^T + Q^T diag(gamma) dO - K^T diag(gamma) dY on the wave's tiles
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const int a = w + 4 * t;
+            if (a < NA) {
+                float4_t acc = glast * s[t];
+                tile_mm(acc, 0, 4, [&](int rr, int kx) { return sq[kx * KP + 16 * a + rr] * sv[kx]; },
+                        [&](int kx, int cc) { return so[kx * SP + cc]; });
+                tile_mm(acc, 0, 4, [&](int rr, int kx) { return -sk[kx * KP + 16 * a + rr] * sv[kx]; },
+                        [&](int kx, int cc) { return sdy[kx * SP + cc]; });
+                s[t] = acc;
+            }
         }
     }
     if (d_init) {
-        float *di = d_init + ((int64_t)nh * DV + v0 + nn) * DK + 4 * jj;
 #pragma unroll
-        for (int a = 0; a < NA; ++a) *reinterpret_cast<float4_t *>(di + 16 * a) = s[a];
+        for (int t = 0; t < NT; ++t) {
+            const int a = w + 4 * t;
+            if (a < NA)
+                *reinterpret_cast<float4_t *>(d_init + ((int64_t)nh * DV + v0 + nn) * DK + 16 * a + 4 * jj) = s[t];
+        }
     }
 }
 
@@ -815,7 +859,7 @@ hipError_t launch_bwd_dk(const ChunkArgs &a, const BwdArgs &g, const BwdWorkspac
     const int64_t chains = (int64_t)a.N * a.H * nvt;
     hipError_t e;
     if (items > 0) {
-        const size_t sb = sizeof(float) * (2 * C * (DK + 1) + 2 * C * (C + 1) + 2 * C);
+        const size_t sb = sizeof(float) * (2 * C * (DK + 4) + 2 * C * (C + 1) + 2 * C);
         auto kern = bwd_prep_kernel<in_t, DK>;
         if ((e = bwd_allow_smem(kern, sb)) != hipSuccess) return e;
         ProfScope prof("gdn_bwd_prep", st);
@@ -825,22 +869,22 @@ hipError_t launch_bwd_dk(const ChunkArgs &a, const BwdArgs &g, const BwdWorkspac
     }
     if (chains > 0) {
         {
-            const size_t sb = sizeof(float) * (C * (DK + 4) + 3 * C);
+            const size_t sb = PassSmem<DK>::bytes_fwd;
             auto kern = bwd_fwd_pass_kernel<in_t, DK>;
             if ((e = bwd_allow_smem(kern, sb)) != hipSuccess) return e;
             ProfScope prof("gdn_bwd_fwd_pass", st);
-            kern<<<dim3((unsigned)chains), dim3(64), sb, st>>>(a.H, a.dv, a.T, cpr, nvt, meta, cu_ws, row0, rtok,
-                                                               rlen, k, v, wt, wv, a.init_state, wck);
+            kern<<<dim3((unsigned)chains), dim3(256), sb, st>>>(a.H, a.dv, a.T, cpr, nvt, meta, cu_ws, row0, rtok,
+                                                                rlen, k, v, wt, wv, a.init_state, wck);
             if ((e = hipGetLastError()) != hipSuccess) return e;
         }
         {
-            const size_t sb = sizeof(float) * (2 * C * (DK + 4) + 3 * C);
+            const size_t sb = PassSmem<DK>::bytes_rev;
             auto kern = bwd_rev_pass_kernel<in_t, DK>;
             if ((e = bwd_allow_smem(kern, sb)) != hipSuccess) return e;
             ProfScope prof("gdn_bwd_rev_pass", st);
-            kern<<<dim3((unsigned)chains), dim3(64), sb, st>>>(a.H, a.dv, a.T, cpr, nvt, meta, cu_ws, row0, rtok,
-                                                               rlen, q, k, g.d_o, wt, wp, wv, g.d_final, wds,
-                                                               g.d_init);
+            kern<<<dim3((unsigned)chains), dim3(256), sb, st>>>(a.H, a.dv, a.T, cpr, nvt, meta, cu_ws, row0, rtok,
+                                                                rlen, q, k, g.d_o, wt, wp, wv, g.d_final, wds,
+                                                                g.d_init);
             if ((e = hipGetLastError()) != hipSuccess) return e;
         }
     }
