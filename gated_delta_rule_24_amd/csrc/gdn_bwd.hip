@@ -38,6 +38,8 @@
 //                           at every chunk end, and of the initial state.
 //   B4 bwd_grad_kernel      per (chunk row, head): every per-token gradient of the
 //                           chunk from its checkpoint and state gradient.
+// B2 also stores each chunk's Y and V', B3 its dV' and dY (= dV, written to
+// the output), so B4 recomputes none of the state products.
 // All arithmetic is fp32 (products on the fp32 matrix-core instruction), so the
 // gradients carry the same precision for every input dtype.  Matrix-core
 // tiles use the lane convention of gdn_device.h: lane l, n = l % 16,
@@ -254,6 +256,104 @@ struct PassSmem {
     static constexpr size_t bytes_rev = sizeof(float) * (off_q + C * KP);
 };
 
+// One chunk's operands of a serial pass, loaded into registers while the
+// previous chunk computes (thread tid covers K / Q elements tid * 8 + 2048 m,
+// T / P elements tid * 4 + 1024 m, dO element tid + 256 m of the value block,
+// and vector element tid).
+template <typename in_t, int DK, bool REV>
+struct PassStage {
+    static constexpr int MK = C * DK / 2048;
+    int tok0, len;
+    int64_t item;
+    Raw8<in_t> kr[MK], qr[REV ? MK : 1];
+    float4_t t4[4], p4[REV ? 4 : 1], b4;
+    float dov[REV ? 4 : 1], vv[REV ? 1 : 4];
+    float vec;
+};
+
+template <typename in_t, int DK, bool REV>
+__device__ __forceinline__ void pass_load(PassStage<in_t, DK, REV> &S, int row, int H, int h, int DV, int v0, int T,
+                                          int cpr, const int32_t *row_tok, const int32_t *row_len, const in_t *q,
+                                          const in_t *k, const in_t *v, const float *d_o, const float *ws_t,
+                                          const float *ws_p, const float *ws_vec) {
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, nn = l & 15, jj = l >> 4;
+    row_span(row, T, cpr, row_tok, row_len, S.tok0, S.len);
+    S.item = (int64_t)row * H + h;
+#pragma unroll
+    for (int m = 0; m < PassStage<in_t, DK, REV>::MK; ++m) {
+        const int idx = tid * 8 + 2048 * m, r = idx / DK, cc = idx % DK;
+        const int64_t off = ((int64_t)(S.tok0 + r) * H + h) * DK + cc;
+        if (r < S.len) {
+            S.kr[m].load(k + off);
+            if constexpr (REV) S.qr[m].load(q + off);
+        } else {
+            S.kr[m].zero();
+            if constexpr (REV) S.qr[m].zero();
+        }
+    }
+    const float *Tm = ws_t + S.item * C * C, *Pm = ws_p + S.item * C * C, *vec = ws_vec + S.item * kVecFloats;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        S.t4[m] = *reinterpret_cast<const float4_t *>(Tm + tid * 4 + 1024 * m);
+        if constexpr (REV) S.p4[m] = *reinterpret_cast<const float4_t *>(Pm + tid * 4 + 1024 * m);
+    }
+    S.b4 = *reinterpret_cast<const float4_t *>(vec + 3 * C + (tid * 4) % C);
+    S.vec = tid < 3 * C ? vec[C + tid] : 0.f;
+    if constexpr (REV) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int e = tid + 256 * m, r = e / 16, cc = e % 16;
+            S.dov[m] = r < S.len ? d_o[((int64_t)(S.tok0 + r) * H + h) * DV + v0 + cc] : 0.f;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 16 * w + 4 * jj + i;
+            S.vv[i] = r < S.len ? to_f32(v[((int64_t)(S.tok0 + r) * H + h) * DV + v0 + nn]) : 0.f;
+        }
+    }
+}
+
+// Writes a staged chunk into LDS: K (and Q) as fp32 rows of pitch KP,
+// M = T diag(beta) (and P) with pitch MP, dO block with pitch SP, gamma,
+// kappa, beta.
+template <typename in_t, int DK, bool REV>
+__device__ __forceinline__ void pass_store(const PassStage<in_t, DK, REV> &S, float *sk, float *sq, float *sm, float *sp,
+                                           float *so, float *sv) {
+    constexpr int KP = DK + 4, MP = C + 1, SP = 16 + 1;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int m = 0; m < PassStage<in_t, DK, REV>::MK; ++m) {
+        const int idx = tid * 8 + 2048 * m, r = idx / DK, cc = idx % DK;
+        float x[8];
+        S.kr[m].to_f32(x);
+        *reinterpret_cast<float4_t *>(sk + r * KP + cc) = float4_t{x[0], x[1], x[2], x[3]};
+        *reinterpret_cast<float4_t *>(sk + r * KP + cc + 4) = float4_t{x[4], x[5], x[6], x[7]};
+        if constexpr (REV) {
+            S.qr[m].to_f32(x);
+            *reinterpret_cast<float4_t *>(sq + r * KP + cc) = float4_t{x[0], x[1], x[2], x[3]};
+            *reinterpret_cast<float4_t *>(sq + r * KP + cc + 4) = float4_t{x[4], x[5], x[6], x[7]};
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const int e = tid * 4 + 1024 * m, r = e / C, cc = e % C;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            sm[r * MP + cc + i] = S.t4[m][i] * S.b4[i];
+            if constexpr (REV) sp[r * MP + cc + i] = S.p4[m][i];
+        }
+    }
+    if (tid < 3 * C) sv[tid] = S.vec;
+    if constexpr (REV) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int e = tid + 256 * m;
+            so[(e / 16) * SP + e % 16] = S.dov[m];
+        }
+    }
+}
+
 template <typename in_t, int DK>
 __global__ __launch_bounds__(256) void bwd_fwd_pass_kernel(int H, int DV, int T, int cpr, int nvt,
                                                            const int32_t *__restrict__ meta,
@@ -265,7 +365,8 @@ __global__ __launch_bounds__(256) void bwd_fwd_pass_kernel(int H, int DV, int T,
                                                            const float *__restrict__ ws_t,
                                                            const float *__restrict__ ws_vec,
                                                            const float *__restrict__ init_state,
-                                                           float *__restrict__ ws_ck) {
+                                                           float *__restrict__ ws_ck, float *__restrict__ ws_y,
+                                                           float *__restrict__ ws_vp) {
     using L = PassSmem<DK>;
     constexpr int KP = L::KP, SP = L::SP, MP = L::MP, NA = DK / 16, NT = (NA + 3) / 4;
     extern __shared__ __align__(16) float smem[];
@@ -287,11 +388,16 @@ __global__ __launch_bounds__(256) void bwd_fwd_pass_kernel(int H, int DV, int T,
                    ? *reinterpret_cast<const float4_t *>(init_state + ((int64_t)nh * DV + v0 + nn) * DK + 16 * a + 4 * jj)
                    : zero4();
     }
+    PassStage<in_t, DK, false> S;
+    if (nrows > 0)
+        pass_load(S, r0, H, h, DV, v0, T, cpr, row_tok, row_len, (const in_t *)nullptr, k, v, (const float *)nullptr,
+                  ws_t, (const float *)nullptr, ws_vec);
     for (int c = 0; c < nrows; ++c) {
-        const int row = r0 + c;
-        int tok0, len;
-        row_span(row, T, cpr, row_tok, row_len, tok0, len);
-        const int64_t item = (int64_t)row * H + h;
+        const int tok0 = S.tok0, len = S.len;
+        const int64_t item = S.item;
+        float vv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) vv[i] = S.vv[i];
         __syncthreads();   // the previous chunk's LDS contents are no longer read
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
@@ -302,33 +408,14 @@ __global__ __launch_bounds__(256) void bwd_fwd_pass_kernel(int H, int DV, int T,
                 for (int i = 0; i < 4; ++i) ss[(16 * a + 4 * jj + i) * SP + nn] = s[t][i];
             }
         }
-        for (int idx = tid * 8; idx < C * DK; idx += 256 * 8) {
-            const int r = idx / DK, cc = idx % DK;
-            float x[8];
-            if (r < len) {
-                load8_f32(k + ((int64_t)(tok0 + r) * H + h) * DK + cc, x);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) x[e] = 0.f;
-            }
-            *reinterpret_cast<float4_t *>(sk + r * KP + cc) = float4_t{x[0], x[1], x[2], x[3]};
-            *reinterpret_cast<float4_t *>(sk + r * KP + cc + 4) = float4_t{x[4], x[5], x[6], x[7]};
-        }
-        const float *vec = ws_vec + item * kVecFloats;
-        if (tid < 3 * C) sv[tid] = vec[C + tid];
-        const float *Tm = ws_t + item * C * C;
-        {
-            const float4_t b4 = *reinterpret_cast<const float4_t *>(vec + 3 * C + (tid * 4) % C);
-            for (int e = tid * 4; e < C * C; e += 256 * 4) {
-                const float4_t t4 = *reinterpret_cast<const float4_t *>(Tm + e);
-                const int r = e / C, cc = e % C;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) sm[r * MP + cc + i] = t4[i] * b4[i];
-            }
-        }
+        pass_store(S, sk, (float *)nullptr, sm, (float *)nullptr, (float *)nullptr, sv);
+        if (c + 1 < nrows)   // the next chunk's operands load while this one computes
+            pass_load(S, r0 + c + 1, H, h, DV, v0, T, cpr, row_tok, row_len, (const in_t *)nullptr, k, v,
+                      (const float *)nullptr, ws_t, (const float *)nullptr, ws_vec);
         __syncthreads();
         const float glast = len > 0 ? sv[len - 1] : 1.f;
         const int rw = 16 * w;
+        (void)tok0;
         // rows of the wave: X = K S^T, Y = V - diag(gamma) X
         float4_t x = zero4();
         tile_mm(x, 0, NA, [&](int rr, int kx) { return sk[(rw + rr) * KP + kx]; },
@@ -336,8 +423,9 @@ __global__ __launch_bounds__(256) void bwd_fwd_pass_kernel(int H, int DV, int T,
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = rw + 4 * jj + i;
-            const float vv = r < len ? to_f32(v[((int64_t)(tok0 + r) * H + h) * DV + v0 + nn]) : 0.f;
-            sy[r * SP + nn] = vv - sv[r] * x[i];
+            const float yv = vv[i] - sv[r] * x[i];
+            sy[r * SP + nn] = yv;
+            ws_y[(item * C + r) * DV + v0 + nn] = yv;
         }
         __syncthreads();
         // V' = M Y, M = T diag(beta) lower block triangular
@@ -345,7 +433,11 @@ __global__ __launch_bounds__(256) void bwd_fwd_pass_kernel(int H, int DV, int T,
         tile_mm(vp, 0, w + 1, [&](int rr, int kx) { return sm[(rw + rr) * MP + kx]; },
                 [&](int kx, int cc) { return sy[kx * SP + cc]; });
 #pragma unroll
-        for (int i = 0; i < 4; ++i) svp[(rw + 4 * jj + i) * SP + nn] = vp[i];
+        for (int i = 0; i < 4; ++i) {
+            const int r = rw + 4 * jj + i;
+            svp[r * SP + nn] = vp[i];
+            ws_vp[(item * C + r) * DV + v0 + nn] = vp[i];
+        }
         __syncthreads();
         // S^T <- gamma_last S^T + K^T diag(kappa) V' on the wave's tiles
 #pragma unroll
@@ -382,7 +474,8 @@ __global__ __launch_bounds__(256) void bwd_rev_pass_kernel(int H, int DV, int T,
                                                            const float *__restrict__ ws_p,
                                                            const float *__restrict__ ws_vec,
                                                            const float *__restrict__ d_final,
-                                                           float *__restrict__ ws_ds, float *__restrict__ d_init) {
+                                                           float *__restrict__ ws_ds, float *__restrict__ ws_dvp,
+                                                           float *__restrict__ dv, float *__restrict__ d_init) {
     using L = PassSmem<DK>;
     constexpr int KP = L::KP, SP = L::SP, MP = L::MP, NA = DK / 16, NT = (NA + 3) / 4;
     extern __shared__ __align__(16) float smem[];
@@ -404,11 +497,13 @@ __global__ __launch_bounds__(256) void bwd_rev_pass_kernel(int H, int DV, int T,
                    ? *reinterpret_cast<const float4_t *>(d_final + ((int64_t)nh * DV + v0 + nn) * DK + 16 * a + 4 * jj)
                    : zero4();
     }
+    PassStage<in_t, DK, true> S;
+    if (nrows > 0)
+        pass_load(S, r0 + nrows - 1, H, h, DV, v0, T, cpr, row_tok, row_len, q, k, (const in_t *)nullptr, d_o, ws_t,
+                  ws_p, ws_vec);
     for (int c = nrows - 1; c >= 0; --c) {
-        const int row = r0 + c;
-        int tok0, len;
-        row_span(row, T, cpr, row_tok, row_len, tok0, len);
-        const int64_t item = (int64_t)row * H + h;
+        const int tok0 = S.tok0, len = S.len;
+        const int64_t item = S.item;
         __syncthreads();
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
@@ -419,44 +514,10 @@ __global__ __launch_bounds__(256) void bwd_rev_pass_kernel(int H, int DV, int T,
                 for (int i = 0; i < 4; ++i) ss[(16 * a + 4 * jj + i) * SP + nn] = s[t][i];
             }
         }
-        for (int idx = tid * 8; idx < C * DK; idx += 256 * 8) {
-            const int r = idx / DK, cc = idx % DK;
-            float xk[8], xq[8];
-            if (r < len) {
-                const int64_t off = ((int64_t)(tok0 + r) * H + h) * DK + cc;
-                load8_f32(k + off, xk);
-                load8_f32(q + off, xq);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) xk[e] = xq[e] = 0.f;
-            }
-            *reinterpret_cast<float4_t *>(sk + r * KP + cc) = float4_t{xk[0], xk[1], xk[2], xk[3]};
-            *reinterpret_cast<float4_t *>(sk + r * KP + cc + 4) = float4_t{xk[4], xk[5], xk[6], xk[7]};
-            *reinterpret_cast<float4_t *>(sq + r * KP + cc) = float4_t{xq[0], xq[1], xq[2], xq[3]};
-            *reinterpret_cast<float4_t *>(sq + r * KP + cc + 4) = float4_t{xq[4], xq[5], xq[6], xq[7]};
-        }
-        for (int e = tid; e < C * 16; e += 256) {
-            const int r = e / 16, cc = e % 16;
-            so[r * SP + cc] = r < len ? d_o[((int64_t)(tok0 + r) * H + h) * DV + v0 + cc] : 0.f;
-        }
-        const float *vec = ws_vec + item * kVecFloats;
-        if (tid < 3 * C) sv[tid] = vec[C + tid];
-        const float *Tm = ws_t + item * C * C;
-        const float *Pm = ws_p + item * C * C;
-        {
-            // M = T diag(beta): a thread's four columns are the same in every row it stages
-            const float4_t b4 = *reinterpret_cast<const float4_t *>(vec + 3 * C + (tid * 4) % C);
-            for (int e = tid * 4; e < C * C; e += 256 * 4) {
-                const float4_t t4 = *reinterpret_cast<const float4_t *>(Tm + e);
-                const float4_t p4 = *reinterpret_cast<const float4_t *>(Pm + e);
-                const int r = e / C, cc = e % C;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    sm[r * MP + cc + i] = t4[i] * b4[i];
-                    sp[r * MP + cc + i] = p4[i];
-                }
-            }
-        }
+        pass_store(S, sk, sq, sm, sp, so, sv);
+        if (c > 0)   // the next chunk's operands load while this one computes
+            pass_load(S, r0 + c - 1, H, h, DV, v0, T, cpr, row_tok, row_len, q, k, (const in_t *)nullptr, d_o, ws_t,
+                      ws_p, ws_vec);
         __syncthreads();
         const float glast = len > 0 ? sv[len - 1] : 1.f;
         const int rw = 16 * w;
@@ -470,14 +531,22 @@ __global__ __launch_bounds__(256) void bwd_rev_pass_kernel(int H, int DV, int T,
         tile_mm(dvp, w, 4, [&](int rr, int kx) { return sp[kx * MP + rw + rr]; },
                 [&](int kx, int cc) { return so[kx * SP + cc]; });
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sdvp[(rw + 4 * jj + i) * SP + nn] = dvp[i];
+        for (int i = 0; i < 4; ++i) {
+            const int r = rw + 4 * jj + i;
+            sdvp[r * SP + nn] = dvp[i];
+            ws_dvp[(item * C + r) * DV + v0 + nn] = dvp[i];
+        }
         __syncthreads();
         // dY = M^T dV', M^T[r][x] = T[x][r] beta[r]
         float4_t dy = zero4();
         tile_mm(dy, w, 4, [&](int rr, int kx) { return sm[kx * MP + rw + rr]; },
                 [&](int kx, int cc) { return sdvp[kx * SP + cc]; });
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sdy[(rw + 4 * jj + i) * SP + nn] = dy[i];
+        for (int i = 0; i < 4; ++i) {
+            const int r = rw + 4 * jj + i;
+            sdy[r * SP + nn] = dy[i];
+            if (r < len) dv[((int64_t)(tok0 + r) * H + h) * DV + v0 + nn] = dy[i];
+        }
         __syncthreads();
         // dS^T <- gamma_last dS^T + Q^T diag(gamma) dO - K^T diag(gamma) dY on the wave's tiles
 #pragma unroll
@@ -507,7 +576,9 @@ __global__ __launch_bounds__(256) void bwd_rev_pass_kernel(int H, int DV, int T,
 // B4: per (chunk row, head), every per-token gradient of the chunk.  Four
 // waves; wave w owns rows 16 w .. 16 w + 15 of the chunk.  The value
 // dimension is walked in blocks of 16 columns: the products that sum over it
-// (dP, dM, the S terms of dQ and dK, the decay sums) accumulate in registers.
+// (dP, dM, U = dO S, Z = dY S, W2 = V' dS_next) accumulate in registers.
+// The decay sums follow from them: dO_r . (Q S^T)_r = q_r . U_r,
+// dY_r . X_r = k_r . Z_r and V'_r . (K dS_next^T)_r = k_r . W2_r.
 // ============================================================================
 template <int DK>
 struct GradSmem {
@@ -539,13 +610,16 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(int H, int DV, int T, int
                                                        const int32_t *__restrict__ row_tok,
                                                        const int32_t *__restrict__ row_len,
                                                        const in_t *__restrict__ q, const in_t *__restrict__ k,
-                                                       const in_t *__restrict__ v, const float *__restrict__ d_o,
+                                                       const float *__restrict__ d_o,
                                                        const float *__restrict__ ws_t,
                                                        const float *__restrict__ ws_p,
                                                        const float *__restrict__ ws_vec,
                                                        const float *__restrict__ ws_ck,
-                                                       const float *__restrict__ ws_ds, float *__restrict__ dq,
-                                                       float *__restrict__ dk, float *__restrict__ dv,
+                                                       const float *__restrict__ ws_ds,
+                                                       const float *__restrict__ ws_y,
+                                                       const float *__restrict__ ws_vp,
+                                                       const float *__restrict__ ws_dvp, float *__restrict__ dq,
+                                                       float *__restrict__ dk, const float *__restrict__ dv,
                                                        float *__restrict__ dla, float *__restrict__ dbeta) {
     using L = GradSmem<DK>;
     constexpr int KP = L::KP, CP = L::CP, BP = L::BP, NA = DK / 16;
@@ -589,22 +663,26 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(int H, int DV, int T, int
         *reinterpret_cast<float4_t *>(sp + r * CP + c) = *reinterpret_cast<const float4_t *>(Pg + e);
     }
     if (tid < 4 * C) vg[tid] = ws_vec[it64 * kVecFloats + tid];
-    if (tid < 3 * C) vdgam[tid] = 0.f;   // dgamma, dkappa, dbeta
+    if (tid < C) vdb[tid] = 0.f;
     if (tid == 0) vgl[0] = 0.f;
     __syncthreads();
 
     const int rw = 16 * w;           // the wave's first chunk row
-    float4_t accq[NA], acck[NA];     // dQ, dK rows of the wave: tile a = columns 16 a ..
+    // Sums over the value dimension, rows of the wave, tile a = key columns 16 a ..:
+    //   U = dO S,  Z = dY S,  W2 = V' dS_next;  dP, dM tiles (w, c) for c <= w.
+    float4_t au[NA], az[NA], aw[NA];
 #pragma unroll
-    for (int a = 0; a < NA; ++a) accq[a] = acck[a] = zero4();
-    float4_t dp[4], dm[4];           // dP, dM tiles (w, c) for c <= w
+    for (int a = 0; a < NA; ++a) au[a] = az[a] = aw[a] = zero4();
+    float4_t dp[4], dm[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) dp[c] = dm[c] = zero4();
-    float pgam[4] = {0.f, 0.f, 0.f, 0.f}, pkap[4] = {0.f, 0.f, 0.f, 0.f}, pgl = 0.f;
+    float pgl = 0.f;
 
     const float *ck = ws_ck + it64 * DV * DK, *dsn = ws_ds + it64 * DV * DK;
+    const float *gy = ws_y + it64 * C * DV, *gvp = ws_vp + it64 * C * DV, *gdvp = ws_dvp + it64 * C * DV;
     for (int vb0 = 0; vb0 < DV; vb0 += 16) {
-        // stage S and dS_next rows vb0 .. vb0 + 15, and dO columns vb0 .. vb0 + 15
+        __syncthreads();   // the previous blocks are no longer read
+        // S and dS_next rows vb0 .. vb0 + 15; dO, Y, V', dV', dY columns vb0 .. vb0 + 15
         for (int e = tid * 4; e < 16 * DK; e += 256 * 4) {
             const int r = e / DK, c = e % DK;
             const float4_t a4 = *reinterpret_cast<const float4_t *>(ck + (int64_t)(vb0 + r) * DK + c);
@@ -615,60 +693,14 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(int H, int DV, int T, int
         }
         for (int e = tid; e < C * 16; e += 256) {
             const int r = e / 16, c = e % 16;
-            so[r * BP + c] = r < len ? d_o[((int64_t)(tok0 + r) * H + h) * DV + vb0 + c] : 0.f;
-        }
-        __syncthreads();
-        // X = K S^T, QS = Q S^T, KdS = K dS^T for the wave's rows; Y = V - gamma X
-        float4_t x = zero4(), qs = zero4(), kds = zero4();
-#pragma unroll
-        for (int kt = 0; kt < NA; ++kt) {
-            const float4_t kr = *reinterpret_cast<const float4_t *>(sk + (rw + nn) * KP + 16 * kt + 4 * jj);
-            const float4_t qr = *reinterpret_cast<const float4_t *>(sq + (rw + nn) * KP + 16 * kt + 4 * jj);
-            const float4_t sr = *reinterpret_cast<const float4_t *>(ss + nn * KP + 16 * kt + 4 * jj);
-            const float4_t dr = *reinterpret_cast<const float4_t *>(sds + nn * KP + 16 * kt + 4 * jj);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                mfma4(x, kr[i], sr[i]);
-                mfma4(qs, qr[i], sr[i]);
-                mfma4(kds, kr[i], dr[i]);
-            }
-        }
-        float4_t y;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = rw + 4 * jj + i;
-            const float vv = r < len ? to_f32(v[((int64_t)(tok0 + r) * H + h) * DV + vb0 + nn]) : 0.f;
-            y[i] = vv - vgam[r] * x[i];
-            sy[r * BP + nn] = y[i];
-            pgam[i] += so[r * BP + nn] * qs[i];
-        }
-        __syncthreads();
-        // V' = M Y (M = T diag(beta));  dV' = P^T dO + diag(kappa) KdS
-        float4_t vp = zero4(), dvp;
-        tile_mm(vp, 0, w + 1, [&](int rr, int kk) { return st[(rw + rr) * CP + kk] * vb[kk]; },
-                [&](int kk, int cc) { return sy[kk * BP + cc]; });
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dvp[i] = vkap[rw + 4 * jj + i] * kds[i];
-        tile_mm(dvp, w, 4, [&](int rr, int kk) { return sp[kk * CP + rw + rr]; },
-                [&](int kk, int cc) { return so[kk * BP + cc]; });
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = rw + 4 * jj + i;
-            svp[r * BP + nn] = vp[i];
-            sdvp[r * BP + nn] = dvp[i];
-            pkap[i] += vp[i] * kds[i];
-        }
-        __syncthreads();
-        // dY = M^T dV'  (= dV)
-        float4_t dy = zero4();
-        tile_mm(dy, w, 4, [&](int rr, int kk) { return st[kk * CP + rw + rr] * vb[rw + rr]; },
-                [&](int kk, int cc) { return sdvp[kk * BP + cc]; });
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = rw + 4 * jj + i;
-            sdy[r * BP + nn] = dy[i];
-            pgam[i] -= dy[i] * x[i];
-            if (r < len) dv[((int64_t)(tok0 + r) * H + h) * DV + vb0 + nn] = dy[i];
+            const bool in = r < len;
+            const int64_t tv = ((int64_t)(tok0 + r) * H + h) * DV + vb0 + c;
+            const int64_t wv = (int64_t)r * DV + vb0 + c;
+            so[r * BP + c] = in ? d_o[tv] : 0.f;
+            sdy[r * BP + c] = in ? dv[tv] : 0.f;
+            sy[r * BP + c] = gy[wv];
+            svp[r * BP + c] = gvp[wv];
+            sdvp[r * BP + c] = gdvp[wv];
         }
         __syncthreads();
         // dP += dO V'^T and dM += dV' Y^T on tiles (w, c), c <= w (one k-tile: the 16 columns)
@@ -681,29 +713,54 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(int H, int DV, int T, int
                         [&](int kk, int cc) { return sy[(16 * c + cc) * BP + kk]; });
             }
         }
-        // dQ += diag(gamma) dO S;  dK += -diag(gamma) dY S + diag(kappa) V' dS
+        // U += dO S,  Z += dY S,  W2 += V' dS_next
 #pragma unroll
-        for (int a = 0; a < NA; ++a) {
-            tile_mm(accq[a], 0, 1, [&](int rr, int kk) { return vgam[rw + rr] * so[(rw + rr) * BP + kk]; },
-                    [&](int kk, int cc) { return ss[kk * KP + 16 * a + cc]; });
-            tile_mm(acck[a], 0, 1, [&](int rr, int kk) { return -vgam[rw + rr] * sdy[(rw + rr) * BP + kk]; },
-                    [&](int kk, int cc) { return ss[kk * KP + 16 * a + cc]; });
-            tile_mm(acck[a], 0, 1, [&](int rr, int kk) { return vkap[rw + rr] * svp[(rw + rr) * BP + kk]; },
-                    [&](int kk, int cc) { return sds[kk * KP + 16 * a + cc]; });
+        for (int i = 0; i < 4; ++i) {
+            const int kk = 4 * jj + i;
+            const float ao = so[(rw + nn) * BP + kk], ay = sdy[(rw + nn) * BP + kk], av = svp[(rw + nn) * BP + kk];
+#pragma unroll
+            for (int a = 0; a < NA; ++a) {
+                const float bs = ss[kk * KP + 16 * a + nn], bd = sds[kk * KP + 16 * a + nn];
+                mfma4(au[a], ao, bs);
+                mfma4(az[a], ay, bs);
+                mfma4(aw[a], av, bd);
+            }
         }
-        __syncthreads();   // the blocks are restaged next
     }
 
-    // ---- decay sums of the value loop ----
+    // ---- decay sums: dgamma_r = q_r . U_r - k_r . Z_r,  dkappa_r = k_r . W2_r ----
+    {
+        float pg[4] = {0.f, 0.f, 0.f, 0.f}, pk[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const float g1 = row16_sum(pgam[i]), k1 = row16_sum(pkap[i]);
-        if (nn == 0) {
-            vdgam[rw + 4 * jj + i] = g1;
-            vdkap[rw + 4 * jj + i] = k1;
+        for (int a = 0; a < NA; ++a)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = rw + 4 * jj + i, c = 16 * a + nn;
+                const float qv = sq[r * KP + c], kv = sk[r * KP + c];
+                pg[i] += qv * au[a][i] - kv * az[a][i];
+                pk[i] += kv * aw[a][i];
+            }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float g1 = row16_sum(pg[i]), k1 = row16_sum(pk[i]);
+            if (nn == 0) {
+                vdgam[rw + 4 * jj + i] = g1;
+                vdkap[rw + 4 * jj + i] = k1;
+            }
         }
     }
+    // dQ and dK rows of the wave so far: diag(gamma) U and -diag(gamma) Z + diag(kappa) W2
+    float4_t accq[NA], acck[NA];
+#pragma unroll
+    for (int a = 0; a < NA; ++a)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = rw + 4 * jj + i;
+            accq[a][i] = vgam[r] * au[a][i];
+            acck[a][i] = vkap[r] * aw[a][i] - vgam[r] * az[a][i];
+        }
     atomicAdd(vgl, pgl);
+    __syncthreads();
     // dT = dM diag(beta) on the lower tiles (into the S-block area), dbeta's first part
     float *sdt = ss;   // [C][CP]
     for (int e = tid; e < C * CP; e += 256) sdt[e] = 0.f;
@@ -849,6 +906,8 @@ hipError_t launch_bwd_dk(const ChunkArgs &a, const BwdArgs &g, const BwdWorkspac
     float *wt = reinterpret_cast<float *>(ws + w.off_t), *wp = reinterpret_cast<float *>(ws + w.off_p);
     float *wv = reinterpret_cast<float *>(ws + w.off_vec), *wck = reinterpret_cast<float *>(ws + w.off_ck);
     float *wds = reinterpret_cast<float *>(ws + w.off_ds);
+    float *wy = reinterpret_cast<float *>(ws + w.off_y), *wvp = reinterpret_cast<float *>(ws + w.off_vp);
+    float *wdvp = reinterpret_cast<float *>(ws + w.off_dvp);
     auto *q = static_cast<const in_t *>(a.q);
     auto *k = static_cast<const in_t *>(a.k);
     auto *v = static_cast<const in_t *>(a.v);
@@ -874,7 +933,7 @@ hipError_t launch_bwd_dk(const ChunkArgs &a, const BwdArgs &g, const BwdWorkspac
             if ((e = bwd_allow_smem(kern, sb)) != hipSuccess) return e;
             ProfScope prof("gdn_bwd_fwd_pass", st);
             kern<<<dim3((unsigned)chains), dim3(256), sb, st>>>(a.H, a.dv, a.T, cpr, nvt, meta, cu_ws, row0, rtok,
-                                                                rlen, k, v, wt, wv, a.init_state, wck);
+                                                                rlen, k, v, wt, wv, a.init_state, wck, wy, wvp);
             if ((e = hipGetLastError()) != hipSuccess) return e;
         }
         {
@@ -884,7 +943,7 @@ hipError_t launch_bwd_dk(const ChunkArgs &a, const BwdArgs &g, const BwdWorkspac
             ProfScope prof("gdn_bwd_rev_pass", st);
             kern<<<dim3((unsigned)chains), dim3(256), sb, st>>>(a.H, a.dv, a.T, cpr, nvt, meta, cu_ws, row0, rtok,
                                                                 rlen, q, k, g.d_o, wt, wp, wv, g.d_final, wds,
-                                                                g.d_init);
+                                                                wdvp, g.dv, g.d_init);
             if ((e = hipGetLastError()) != hipSuccess) return e;
         }
     }
@@ -894,8 +953,8 @@ hipError_t launch_bwd_dk(const ChunkArgs &a, const BwdArgs &g, const BwdWorkspac
         if ((e = bwd_allow_smem(kern, L::bytes)) != hipSuccess) return e;
         ProfScope prof("gdn_bwd_grad", st);
         kern<<<dim3((unsigned)items), dim3(256), L::bytes, st>>>(a.H, a.dv, a.T, cpr, urows, meta, rtok, rlen, q, k,
-                                                                 v, g.d_o, wt, wp, wv, wck, wds, g.dq, g.dk, g.dv,
-                                                                 g.dlog_alpha, g.dbeta);
+                                                                 g.d_o, wt, wp, wv, wck, wds, wy, wvp, wdvp, g.dq,
+                                                                 g.dk, g.dv, g.dlog_alpha, g.dbeta);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     return hipSuccess;
@@ -926,6 +985,9 @@ BwdWorkspace chunk_bwd_workspace_layout(int32_t B, int32_t T, int32_t N, bool pa
     w.off_vec = off; off = bwd_align256(off + sizeof(float) * items * kVecFloats);
     w.off_ck = off;  off = bwd_align256(off + sizeof(float) * items * (size_t)dv * dk);
     w.off_ds = off;  off = bwd_align256(off + sizeof(float) * items * (size_t)dv * dk);
+    w.off_y = off;   off = bwd_align256(off + sizeof(float) * items * C * (size_t)dv);
+    w.off_vp = off;  off = bwd_align256(off + sizeof(float) * items * C * (size_t)dv);
+    w.off_dvp = off; off = bwd_align256(off + sizeof(float) * items * C * (size_t)dv);
     w.total = off;
     return w;
 }

@@ -200,10 +200,10 @@ gdn_status gdn_chunk_fwd(const gdn_chunk_desc *desc,
  * Workspace for gdn_chunk_bwd, in bytes, written to *bytes (host pointer).
  * Depends only on the descriptor.  Besides the chunk table it holds, per
  * (chunk, head), the fp32 UT-transform matrix T = (I + A)^{-1}, the
- * decay-masked Q K^T block and the decay vectors (33 KiB at C = 64), and
- * the state and the state's gradient at every chunk boundary
- * (2 * dv * dk * 4 bytes).  Prefill with B = 4, T = 4096, H = 16,
- * dk = dv = 128 needs about 644 MiB.
+ * decay-masked Q K^T block and the decay vectors (33 KiB at C = 64), the
+ * state and the state's gradient at every chunk boundary (2 * dv * dk * 4
+ * bytes) and three C x dv fp32 chunk intermediates.  Prefill with B = 4,
+ * T = 4096, H = 16, dk = dv = 128 needs about 1 GiB.
  * Errors: GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_DTYPE, GDN_ERR_UNSUPPORTED.
  */
 gdn_status gdn_chunk_bwd_workspace_size(const gdn_chunk_desc *desc, size_t *bytes);
