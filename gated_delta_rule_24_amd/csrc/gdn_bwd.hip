@@ -110,8 +110,8 @@ constexpr int kVecFloats = 4 * C;
 // B1: g, gamma, kappa, T = (I + A)^{-1} and P per (chunk row, head).
 // One 256-thread block per item; Q and K rows staged in LDS as fp32.  The
 // 10 lower 16 x 16 tiles of K K^T and Q K^T come from the matrix cores
-// (waves take tiles w, w + 4, w + 8); T by forward substitution, column c of
-// T solving (I + A) t = e_c on its own (columns need no exchange).
+// (waves take tiles w, w + 4, w + 8); T blockwise: the 16 x 16 diagonal
+// blocks by substitution, the others from matrix-core products.
 // ============================================================================
 __device__ __forceinline__ void tri_tile(int t, int &a, int &b) {
     a = t < 1 ? 0 : (t < 3 ? 1 : (t < 6 ? 2 : 3));
@@ -132,7 +132,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(int H, int T, int cpr, in
     float *sq = smem;                 // [C][KP]
     float *sk = sq + C * KP;          // [C][KP]
     float *sa = sk + C * KP;          // [C][AP]  A (strictly lower)
-    float *st = sa + C * AP;          // [C][AP]  T transposed
+    float *st = sa + C * AP;          // [C][AP]  T
     float *sg = st + C * AP;          // [C]
     float *sb = sg + C;               // [C]
     if (!cpr && meta[1] != 0) return;   // malformed cu_seqlens: nothing is written
@@ -208,26 +208,42 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(int H, int T, int cpr, in
             sa[r * AP + c] = c < r ? sb[r] * gm * kk[i] : 0.f;
         }
     }
+    // T = (I + A)^{-1} on 16 x 16 blocks.  Diagonal blocks: lane n of wave w
+    // solves column n of T_ww by substitution in registers.  Off-diagonal,
+    // by distance d = a - b: T_ab = -T_aa sum_{b <= m < a} A_am T_mb on the
+    // matrix cores, wave a taking block (a, a - d).
+    for (int e = tid; e < C * AP; e += 256) st[e] = 0.f;
     __syncthreads();
-    // Column c of T belongs to the four lanes 4c .. 4c + 3 (lane q sums the
-    // terms i = q mod 4; two DPP steps add the quad).  T is kept transposed,
-    // st[c][i] = T[i][c], and each lane stores exactly the entries it reads
-    // later, so the solve needs no barrier.
-    {
-        const int c = tid >> 2, qd = tid & 3;
-        for (int r = 0; r < C; ++r) {
-            float acc = 0.f;
-#pragma unroll 4
-            for (int i = qd; i < r; i += 4) acc += sa[r * AP + i] * st[c * AP + i];
-            acc += dpp_mov<0xB1>(acc);
-            acc += dpp_mov<0x4E>(acc);
-            const float x = r < c ? 0.f : (r == c ? 1.f : -acc);
-            if ((r & 3) == qd) st[c * AP + r] = x;
+    if (l < 16) {
+        const int a = w, c = l;
+        float tc[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float x = r == c ? 1.f : 0.f;
+#pragma unroll
+            for (int i = 0; i < r; ++i) x -= sa[(16 * a + r) * AP + 16 * a + i] * tc[i];
+            tc[r] = r < c ? 0.f : x;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) st[(16 * a + r) * AP + 16 * a + c] = tc[r];
+    }
+    for (int d = 1; d < 4; ++d) {
+        __syncthreads();
+        if (w >= d) {
+            const int a = w, b = w - d;
+            float4_t u = zero4();
+            tile_mm(u, b, a, [&](int rr, int kx) { return sa[(16 * a + rr) * AP + kx]; },
+                    [&](int kx, int cc) { return st[kx * AP + 16 * b + cc]; });
+            float4_t t = zero4();
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mfma4(t, -st[(16 * a + nn) * AP + 16 * a + 4 * jj + i], u[i]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) st[(16 * a + 4 * jj + i) * AP + 16 * b + nn] = t[i];
         }
     }
     __syncthreads();
     float *Tm = ws_t + (int64_t)item * C * C;
-    for (int e = tid; e < C * C; e += 256) Tm[e] = st[(e % C) * AP + e / C];
+    for (int e = tid; e < C * C; e += 256) Tm[e] = st[(e / C) * AP + e % C];
 }
 
 // ============================================================================
@@ -680,28 +696,58 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(int H, int DV, int T, int
 
     const float *ck = ws_ck + it64 * DV * DK, *dsn = ws_ds + it64 * DV * DK;
     const float *gy = ws_y + it64 * C * DV, *gvp = ws_vp + it64 * C * DV, *gdvp = ws_dvp + it64 * C * DV;
+    // One value block's operands, loaded into registers while the previous
+    // block computes: S and dS_next rows (float4 e = tid * 4 + 1024 m) and the
+    // dO, dY, Y, V', dV' columns (element tid + 256 m of the C x 16 block).
+    constexpr int NS = (16 * DK + 1023) / 1024;
+    float4_t ga[NS], gb[NS];
+    float go[4], gdy[4], gyv[4], gvp4[4], gdvp4[4];
+    auto load_block = [&](int vb) {
+#pragma unroll
+        for (int m = 0; m < NS; ++m) {
+            const int e = tid * 4 + 1024 * m;
+            if (e < 16 * DK) {
+                const int r = e / DK, c = e % DK;
+                ga[m] = *reinterpret_cast<const float4_t *>(ck + (int64_t)(vb + r) * DK + c);
+                gb[m] = *reinterpret_cast<const float4_t *>(dsn + (int64_t)(vb + r) * DK + c);
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int e = tid + 256 * m, r = e / 16, c = e % 16;
+            const bool in = r < len;
+            const int64_t tv = ((int64_t)(tok0 + r) * H + h) * DV + vb + c;
+            const int64_t wv = (int64_t)r * DV + vb + c;
+            go[m] = in ? d_o[tv] : 0.f;
+            gdy[m] = in ? dv[tv] : 0.f;
+            gyv[m] = gy[wv];
+            gvp4[m] = gvp[wv];
+            gdvp4[m] = gdvp[wv];
+        }
+    };
+    load_block(0);
     for (int vb0 = 0; vb0 < DV; vb0 += 16) {
         __syncthreads();   // the previous blocks are no longer read
-        // S and dS_next rows vb0 .. vb0 + 15; dO, Y, V', dV', dY columns vb0 .. vb0 + 15
-        for (int e = tid * 4; e < 16 * DK; e += 256 * 4) {
-            const int r = e / DK, c = e % DK;
-            const float4_t a4 = *reinterpret_cast<const float4_t *>(ck + (int64_t)(vb0 + r) * DK + c);
-            const float4_t b4 = *reinterpret_cast<const float4_t *>(dsn + (int64_t)(vb0 + r) * DK + c);
-            *reinterpret_cast<float4_t *>(ss + r * KP + c) = a4;
-            *reinterpret_cast<float4_t *>(sds + r * KP + c) = b4;
-            pgl += a4[0] * b4[0] + a4[1] * b4[1] + a4[2] * b4[2] + a4[3] * b4[3];
+#pragma unroll
+        for (int m = 0; m < NS; ++m) {
+            const int e = tid * 4 + 1024 * m;
+            if (e < 16 * DK) {
+                const int r = e / DK, c = e % DK;
+                *reinterpret_cast<float4_t *>(ss + r * KP + c) = ga[m];
+                *reinterpret_cast<float4_t *>(sds + r * KP + c) = gb[m];
+                pgl += ga[m][0] * gb[m][0] + ga[m][1] * gb[m][1] + ga[m][2] * gb[m][2] + ga[m][3] * gb[m][3];
+            }
         }
-        for (int e = tid; e < C * 16; e += 256) {
-            const int r = e / 16, c = e % 16;
-            const bool in = r < len;
-            const int64_t tv = ((int64_t)(tok0 + r) * H + h) * DV + vb0 + c;
-            const int64_t wv = (int64_t)r * DV + vb0 + c;
-            so[r * BP + c] = in ? d_o[tv] : 0.f;
-            sdy[r * BP + c] = in ? dv[tv] : 0.f;
-            sy[r * BP + c] = gy[wv];
-            svp[r * BP + c] = gvp[wv];
-            sdvp[r * BP + c] = gdvp[wv];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int e = tid + 256 * m, r = e / 16, c = e % 16;
+            so[r * BP + c] = go[m];
+            sdy[r * BP + c] = gdy[m];
+            sy[r * BP + c] = gyv[m];
+            svp[r * BP + c] = gvp4[m];
+            sdvp[r * BP + c] = gdvp4[m];
         }
+        if (vb0 + 16 < DV) load_block(vb0 + 16);
         __syncthreads();
         // dP += dO V'^T and dM += dV' Y^T on tiles (w, c), c <= w (one k-tile: the 16 columns)
 #pragma unroll
