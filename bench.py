@@ -52,11 +52,11 @@ MFMA_F32_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix peak, TFLOP/s
 
 def bwd_grad_flops_per_chunk_head(dk, dv, c=C):
     # The gradient kernel's products, triangular ones at their triangular size (t = c(c+1)/2):
-    # K S^T, Q S^T, K dS^T (6 c dk dv); M Y, P^T dO, M^T dV', dO V'^T, dV' Y^T (5 * 2 t dv);
-    # dO S, dY S, V' dS (6 c dv dk); T^T dT and W T^T (about 2 * c^3 / 3); K K^T, Q K^T (2 * 2 t dk);
-    # (dP o Gamma) K, (dP o Gamma)^T Q (2 * 2 t dk) and (dK + dK^T) K (2 c^2 dk).
+    # U = dO S, Z = dY S, W2 = V' dS_next (6 c dk dv); dP = dO V'^T, dM = dV' Y^T (2 * 2 t dv);
+    # T^T dT and W T^T (about 2 c^3 / 3); K K^T, Q K^T (2 * 2 t dk); (dP o Gamma) K and
+    # (dP o Gamma)^T Q (2 * 2 t dk); (dK o + dK o^T) K (2 c^2 dk).
     t = c * (c + 1) / 2
-    return 12 * c * dk * dv + 10 * t * dv + 2 * c ** 3 / 3 + 8 * t * dk + 2 * c * c * dk
+    return 6 * c * dk * dv + 4 * t * dv + 2 * c ** 3 / 3 + 8 * t * dk + 2 * c * c * dk
 
 
 def decode_min_bytes(N, H, dk, dv, in_bytes, out_bytes):

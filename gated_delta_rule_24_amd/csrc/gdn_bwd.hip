@@ -256,20 +256,20 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(int H, int T, int cpr, in
 // ============================================================================
 template <int DK>
 struct PassSmem {
-    static constexpr int KP = DK + 4;   // K and Q rows
-    static constexpr int SP = 16 + 1;   // S^T / dS^T [dk][16], value blocks [C][16]
+    static constexpr int KP = DK + 4;   // rows of K; rows of the state tile (S or dS, 16 x DK)
+    static constexpr int TP = C + 4;    // transposed value blocks [16][C]; C x C matrices; K^T, Q^T [DK][C]
     static constexpr int off_k = 0;
     static constexpr int off_s = off_k + C * KP;
-    static constexpr int off_a = off_s + DK * SP;      // Y (forward) or dO (reverse)
-    static constexpr int off_b = off_a + C * SP;       // V' (forward) or dV' (reverse)
-    static constexpr int off_c = off_b + C * SP;       // dY (reverse)
-    static constexpr int MP = C + 1;    // M = T diag(beta) and P
-    static constexpr int off_m = off_c + C * SP;
-    static constexpr int off_v = off_m + C * MP;       // gamma, kappa, beta
-    static constexpr int off_p = off_v + 3 * C;        // P (reverse pass only)
-    static constexpr int off_q = off_p + C * MP;       // Q (reverse pass only)
+    static constexpr int off_a = off_s + 16 * KP;      // Y^T (forward) or dO^T (reverse)
+    static constexpr int off_b = off_a + 16 * TP;      // V'^T (forward) or dV'^T (reverse)
+    static constexpr int off_c = off_b + 16 * TP;      // dY^T (reverse)
+    static constexpr int off_m = off_c + 16 * TP;      // M (forward) or M^T (reverse), M = T diag(beta)
+    static constexpr int off_v = off_m + C * TP;       // gamma, kappa, beta
+    static constexpr int off_p = off_v + 3 * C;        // P^T (reverse only)
+    static constexpr int off_q = off_p + C * TP;       // Q rows (reverse only)
     static constexpr size_t bytes_fwd = sizeof(float) * off_p;
     static constexpr size_t bytes_rev = sizeof(float) * (off_q + C * KP);
+    static_assert(bytes_rev <= 160 * 1024, "reverse pass fits the 160 KiB of LDS");
 };
 
 // One chunk's operands of a serial pass, loaded into registers while the
@@ -330,13 +330,14 @@ __device__ __forceinline__ void pass_load(PassStage<in_t, DK, REV> &S, int row, 
     }
 }
 
-// Writes a staged chunk into LDS: K (and Q) as fp32 rows of pitch KP,
-// M = T diag(beta) (and P) with pitch MP, dO block with pitch SP, gamma,
-// kappa, beta.
+// Writes a staged chunk into LDS (layout of PassSmem): K rows (and Q rows
+// for the reverse pass); M (forward) or M^T and P^T (reverse); dO^T
+// (reverse); gamma, kappa, beta.
 template <typename in_t, int DK, bool REV>
-__device__ __forceinline__ void pass_store(const PassStage<in_t, DK, REV> &S, float *sk, float *sq, float *sm, float *sp,
-                                           float *so, float *sv) {
-    constexpr int KP = DK + 4, MP = C + 1, SP = 16 + 1;
+__device__ __forceinline__ void pass_store(const PassStage<in_t, DK, REV> &S, float *smem) {
+    using L = PassSmem<DK>;
+    constexpr int KP = L::KP, TP = L::TP;
+    float *sk = smem + L::off_k, *sm = smem + L::off_m, *sv = smem + L::off_v;
     const int tid = threadIdx.x;
 #pragma unroll
     for (int m = 0; m < PassStage<in_t, DK, REV>::MK; ++m) {
@@ -346,6 +347,7 @@ __device__ __forceinline__ void pass_store(const PassStage<in_t, DK, REV> &S, fl
         *reinterpret_cast<float4_t *>(sk + r * KP + cc) = float4_t{x[0], x[1], x[2], x[3]};
         *reinterpret_cast<float4_t *>(sk + r * KP + cc + 4) = float4_t{x[4], x[5], x[6], x[7]};
         if constexpr (REV) {
+            float *sq = smem + L::off_q;
             S.qr[m].to_f32(x);
             *reinterpret_cast<float4_t *>(sq + r * KP + cc) = float4_t{x[0], x[1], x[2], x[3]};
             *reinterpret_cast<float4_t *>(sq + r * KP + cc + 4) = float4_t{x[4], x[5], x[6], x[7]};
@@ -354,18 +356,24 @@ __device__ __forceinline__ void pass_store(const PassStage<in_t, DK, REV> &S, fl
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
         const int e = tid * 4 + 1024 * m, r = e / C, cc = e % C;
+        if constexpr (REV) {
+            float *spt = smem + L::off_p;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            sm[r * MP + cc + i] = S.t4[m][i] * S.b4[i];
-            if constexpr (REV) sp[r * MP + cc + i] = S.p4[m][i];
+            for (int i = 0; i < 4; ++i) {
+                sm[(cc + i) * TP + r] = S.t4[m][i] * S.b4[i];
+                spt[(cc + i) * TP + r] = S.p4[m][i];
+            }
+        } else {
+            *reinterpret_cast<float4_t *>(sm + r * TP + cc) = S.t4[m] * S.b4;
         }
     }
     if (tid < 3 * C) sv[tid] = S.vec;
     if constexpr (REV) {
+        float *sot = smem + L::off_a;
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const int e = tid + 256 * m;
-            so[(e / 16) * SP + e % 16] = S.dov[m];
+            sot[(e % 16) * TP + e / 16] = S.dov[m];
         }
     }
 }
@@ -384,11 +392,10 @@ __global__ __launch_bounds__(256) void bwd_fwd_pass_kernel(int H, int DV, int T,
                                                            float *__restrict__ ws_ck, float *__restrict__ ws_y,
                                                            float *__restrict__ ws_vp) {
     using L = PassSmem<DK>;
-    constexpr int KP = L::KP, SP = L::SP, MP = L::MP, NA = DK / 16, NT = (NA + 3) / 4;
+    constexpr int KP = L::KP, TP = L::TP, NA = DK / 16, NT = (NA + 3) / 4;
     extern __shared__ __align__(16) float smem[];
-    float *sk = smem + L::off_k, *ss = smem + L::off_s, *sy = smem + L::off_a, *svp = smem + L::off_b;
-    float *sm = smem + L::off_m;
-    float *sv = smem + L::off_v;   // gamma [C], kappa [C], beta [C]
+    float *sk = smem + L::off_k, *ss = smem + L::off_s, *syt = smem + L::off_a, *svpt = smem + L::off_b;
+    float *sm = smem + L::off_m, *sv = smem + L::off_v;   // sv: gamma [C], kappa [C], beta [C]
     if (!cpr && meta[1] != 0) return;
     const int nh = blockIdx.x / nvt, vt = blockIdx.x % nvt;
     const int n = nh / H, h = nh % H, v0 = vt * 16;
@@ -408,8 +415,9 @@ __global__ __launch_bounds__(256) void bwd_fwd_pass_kernel(int H, int DV, int T,
     if (nrows > 0)
         pass_load(S, r0, H, h, DV, v0, T, cpr, row_tok, row_len, (const in_t *)nullptr, k, v, (const float *)nullptr,
                   ws_t, (const float *)nullptr, ws_vec);
+    const int rw = 16 * w;
     for (int c = 0; c < nrows; ++c) {
-        const int tok0 = S.tok0, len = S.len;
+        const int len = S.len;
         const int64_t item = S.item;
         float vv[4];
 #pragma unroll
@@ -420,40 +428,47 @@ __global__ __launch_bounds__(256) void bwd_fwd_pass_kernel(int H, int DV, int T,
             const int a = w + 4 * t;
             if (a < NA) {
                 *reinterpret_cast<float4_t *>(ws_ck + (item * DV + v0 + nn) * DK + 16 * a + 4 * jj) = s[t];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) ss[(16 * a + 4 * jj + i) * SP + nn] = s[t][i];
+                *reinterpret_cast<float4_t *>(ss + nn * KP + 16 * a + 4 * jj) = s[t];   // row v0 + n of S
             }
         }
-        pass_store(S, sk, (float *)nullptr, sm, (float *)nullptr, (float *)nullptr, sv);
+        pass_store(S, smem);
         if (c + 1 < nrows)   // the next chunk's operands load while this one computes
             pass_load(S, r0 + c + 1, H, h, DV, v0, T, cpr, row_tok, row_len, (const in_t *)nullptr, k, v,
                       (const float *)nullptr, ws_t, (const float *)nullptr, ws_vec);
         __syncthreads();
         const float glast = len > 0 ? sv[len - 1] : 1.f;
-        const int rw = 16 * w;
-        (void)tok0;
         // rows of the wave: X = K S^T, Y = V - diag(gamma) X
         float4_t x = zero4();
-        tile_mm(x, 0, NA, [&](int rr, int kx) { return sk[(rw + rr) * KP + kx]; },
-                [&](int kx, int cc) { return ss[kx * SP + cc]; });
+#pragma unroll
+        for (int kt = 0; kt < NA; ++kt) {
+            const float4_t a4 = *reinterpret_cast<const float4_t *>(sk + (rw + nn) * KP + 16 * kt + 4 * jj);
+            const float4_t b4 = *reinterpret_cast<const float4_t *>(ss + nn * KP + 16 * kt + 4 * jj);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mfma4(x, a4[i], b4[i]);
+        }
+        float4_t y;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = rw + 4 * jj + i;
-            const float yv = vv[i] - sv[r] * x[i];
-            sy[r * SP + nn] = yv;
-            ws_y[(item * C + r) * DV + v0 + nn] = yv;
+            y[i] = vv[i] - sv[r] * x[i];
+            ws_y[(item * C + r) * DV + v0 + nn] = y[i];
         }
+        *reinterpret_cast<float4_t *>(syt + nn * TP + rw + 4 * jj) = y;
         __syncthreads();
-        // V' = M Y, M = T diag(beta) lower block triangular
+        // V' = M Y, M lower block triangular
         float4_t vp = zero4();
-        tile_mm(vp, 0, w + 1, [&](int rr, int kx) { return sm[(rw + rr) * MP + kx]; },
-                [&](int kx, int cc) { return sy[kx * SP + cc]; });
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = rw + 4 * jj + i;
-            svp[r * SP + nn] = vp[i];
-            ws_vp[(item * C + r) * DV + v0 + nn] = vp[i];
+        for (int kt = 0; kt < 4; ++kt) {
+            if (kt <= w) {
+                const float4_t a4 = *reinterpret_cast<const float4_t *>(sm + (rw + nn) * TP + 16 * kt + 4 * jj);
+                const float4_t b4 = *reinterpret_cast<const float4_t *>(syt + nn * TP + 16 * kt + 4 * jj);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) mfma4(vp, a4[i], b4[i]);
+            }
         }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ws_vp[(item * C + rw + 4 * jj + i) * DV + v0 + nn] = vp[i];
+        *reinterpret_cast<float4_t *>(svpt + nn * TP + rw + 4 * jj) = vp;
         __syncthreads();
         // S^T <- gamma_last S^T + K^T diag(kappa) V' on the wave's tiles
 #pragma unroll
@@ -461,8 +476,15 @@ __global__ __launch_bounds__(256) void bwd_fwd_pass_kernel(int H, int DV, int T,
             const int a = w + 4 * t;
             if (a < NA) {
                 float4_t acc = glast * s[t];
-                tile_mm(acc, 0, 4, [&](int rr, int kx) { return sk[kx * KP + 16 * a + rr] * sv[C + kx]; },
-                        [&](int kx, int cc) { return svp[kx * SP + cc]; });
+#pragma unroll
+                for (int kt = 0; kt < 4; ++kt) {
+                    const float4_t b4 = *reinterpret_cast<const float4_t *>(svpt + nn * TP + 16 * kt + 4 * jj);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int kx = 16 * kt + 4 * jj + i;
+                        mfma4(acc, sk[kx * KP + 16 * a + nn] * sv[C + kx], b4[i]);
+                    }
+                }
                 s[t] = acc;
             }
         }
@@ -493,11 +515,11 @@ __global__ __launch_bounds__(256) void bwd_rev_pass_kernel(int H, int DV, int T,
                                                            float *__restrict__ ws_ds, float *__restrict__ ws_dvp,
                                                            float *__restrict__ dv, float *__restrict__ d_init) {
     using L = PassSmem<DK>;
-    constexpr int KP = L::KP, SP = L::SP, MP = L::MP, NA = DK / 16, NT = (NA + 3) / 4;
+    constexpr int KP = L::KP, TP = L::TP, NA = DK / 16, NT = (NA + 3) / 4;
     extern __shared__ __align__(16) float smem[];
-    float *sk = smem + L::off_k, *ss = smem + L::off_s;
-    float *so = smem + L::off_a, *sdvp = smem + L::off_b, *sdy = smem + L::off_c, *sv = smem + L::off_v;
-    float *sm = smem + L::off_m, *sp = smem + L::off_p, *sq = smem + L::off_q;
+    float *sk = smem + L::off_k, *ss = smem + L::off_s, *sot = smem + L::off_a, *sdvpt = smem + L::off_b;
+    float *sdyt = smem + L::off_c, *smt = smem + L::off_m, *sv = smem + L::off_v, *spt = smem + L::off_p;
+    float *sq = smem + L::off_q;
     if (!cpr && meta[1] != 0) return;
     const int nh = blockIdx.x / nvt, vt = blockIdx.x % nvt;
     const int n = nh / H, h = nh % H, v0 = vt * 16;
@@ -517,6 +539,7 @@ __global__ __launch_bounds__(256) void bwd_rev_pass_kernel(int H, int DV, int T,
     if (nrows > 0)
         pass_load(S, r0 + nrows - 1, H, h, DV, v0, T, cpr, row_tok, row_len, q, k, (const in_t *)nullptr, d_o, ws_t,
                   ws_p, ws_vec);
+    const int rw = 16 * w;
     for (int c = nrows - 1; c >= 0; --c) {
         const int tok0 = S.tok0, len = S.len;
         const int64_t item = S.item;
@@ -526,43 +549,57 @@ __global__ __launch_bounds__(256) void bwd_rev_pass_kernel(int H, int DV, int T,
             const int a = w + 4 * t;
             if (a < NA) {
                 *reinterpret_cast<float4_t *>(ws_ds + (item * DV + v0 + nn) * DK + 16 * a + 4 * jj) = s[t];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) ss[(16 * a + 4 * jj + i) * SP + nn] = s[t][i];
+                *reinterpret_cast<float4_t *>(ss + nn * KP + 16 * a + 4 * jj) = s[t];   // row v0 + n of dS
             }
         }
-        pass_store(S, sk, sq, sm, sp, so, sv);
+        pass_store(S, smem);
         if (c > 0)   // the next chunk's operands load while this one computes
             pass_load(S, r0 + c - 1, H, h, DV, v0, T, cpr, row_tok, row_len, q, k, (const in_t *)nullptr, d_o, ws_t,
                       ws_p, ws_vec);
         __syncthreads();
         const float glast = len > 0 ? sv[len - 1] : 1.f;
-        const int rw = 16 * w;
         // dV' = P^T dO + diag(kappa) K dS^T on the wave's rows
         float4_t x = zero4();
-        tile_mm(x, 0, NA, [&](int rr, int kx) { return sk[(rw + rr) * KP + kx]; },
-                [&](int kx, int cc) { return ss[kx * SP + cc]; });
+#pragma unroll
+        for (int kt = 0; kt < NA; ++kt) {
+            const float4_t a4 = *reinterpret_cast<const float4_t *>(sk + (rw + nn) * KP + 16 * kt + 4 * jj);
+            const float4_t b4 = *reinterpret_cast<const float4_t *>(ss + nn * KP + 16 * kt + 4 * jj);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mfma4(x, a4[i], b4[i]);
+        }
         float4_t dvp;
 #pragma unroll
         for (int i = 0; i < 4; ++i) dvp[i] = sv[C + rw + 4 * jj + i] * x[i];
-        tile_mm(dvp, w, 4, [&](int rr, int kx) { return sp[kx * MP + rw + rr]; },
-                [&](int kx, int cc) { return so[kx * SP + cc]; });
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = rw + 4 * jj + i;
-            sdvp[r * SP + nn] = dvp[i];
-            ws_dvp[(item * C + r) * DV + v0 + nn] = dvp[i];
+        for (int kt = 0; kt < 4; ++kt) {
+            if (kt >= w) {
+                const float4_t a4 = *reinterpret_cast<const float4_t *>(spt + (rw + nn) * TP + 16 * kt + 4 * jj);
+                const float4_t b4 = *reinterpret_cast<const float4_t *>(sot + nn * TP + 16 * kt + 4 * jj);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) mfma4(dvp, a4[i], b4[i]);
+            }
         }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ws_dvp[(item * C + rw + 4 * jj + i) * DV + v0 + nn] = dvp[i];
+        *reinterpret_cast<float4_t *>(sdvpt + nn * TP + rw + 4 * jj) = dvp;
         __syncthreads();
-        // dY = M^T dV', M^T[r][x] = T[x][r] beta[r]
+        // dY = M^T dV'
         float4_t dy = zero4();
-        tile_mm(dy, w, 4, [&](int rr, int kx) { return sm[kx * MP + rw + rr]; },
-                [&](int kx, int cc) { return sdvp[kx * SP + cc]; });
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+            if (kt >= w) {
+                const float4_t a4 = *reinterpret_cast<const float4_t *>(smt + (rw + nn) * TP + 16 * kt + 4 * jj);
+                const float4_t b4 = *reinterpret_cast<const float4_t *>(sdvpt + nn * TP + 16 * kt + 4 * jj);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) mfma4(dy, a4[i], b4[i]);
+            }
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = rw + 4 * jj + i;
-            sdy[r * SP + nn] = dy[i];
             if (r < len) dv[((int64_t)(tok0 + r) * H + h) * DV + v0 + nn] = dy[i];
         }
+        *reinterpret_cast<float4_t *>(sdyt + nn * TP + rw + 4 * jj) = dy;
         __syncthreads();
         // dS^T <- gamma_last dS^T + Q^T diag(gamma) dO - K^T diag(gamma) dY on the wave's tiles
 #pragma unroll
@@ -570,10 +607,18 @@ __global__ __launch_bounds__(256) void bwd_rev_pass_kernel(int H, int DV, int T,
             const int a = w + 4 * t;
             if (a < NA) {
                 float4_t acc = glast * s[t];
-                tile_mm(acc, 0, 4, [&](int rr, int kx) { return sq[kx * KP + 16 * a + rr] * sv[kx]; },
-                        [&](int kx, int cc) { return so[kx * SP + cc]; });
-                tile_mm(acc, 0, 4, [&](int rr, int kx) { return -sk[kx * KP + 16 * a + rr] * sv[kx]; },
-                        [&](int kx, int cc) { return sdy[kx * SP + cc]; });
+#pragma unroll
+                for (int kt = 0; kt < 4; ++kt) {
+                    const float4_t bo = *reinterpret_cast<const float4_t *>(sot + nn * TP + 16 * kt + 4 * jj);
+                    const float4_t by = *reinterpret_cast<const float4_t *>(sdyt + nn * TP + 16 * kt + 4 * jj);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int kx = 16 * kt + 4 * jj + i;
+                        const float g = sv[kx];
+                        mfma4(acc, sq[kx * KP + 16 * a + nn] * g, bo[i]);
+                        mfma4(acc, -sk[kx * KP + 16 * a + nn] * g, by[i]);
+                    }
+                }
                 s[t] = acc;
             }
         }
@@ -598,25 +643,27 @@ __global__ __launch_bounds__(256) void bwd_rev_pass_kernel(int H, int DV, int T,
 // ============================================================================
 template <int DK>
 struct GradSmem {
-    static constexpr int KP = DK + 4;       // Q, K, S and dS block rows
+    static constexpr int KP = DK + 4;       // Q, K rows
     static constexpr int CP = C + 4;        // C x C matrices
-    static constexpr int BP = 16 + 1;       // C x 16 value blocks (scalar access only)
+    static constexpr int BP = 16 + 4;       // value blocks [C][16] and transposed S / dS blocks [DK][16]
     static constexpr int off_q = 0;
     static constexpr int off_k = off_q + C * KP;
     static constexpr int off_t = off_k + C * KP;
-    static constexpr int off_p = off_t + C * CP;          // P, later dP o Gamma
-    static constexpr int off_s = off_p + C * CP;          // S block [16][KP], later dT
-    static constexpr int off_ds = off_s + 16 * KP;        // dS block [16][KP]
-    static constexpr int off_o = off_ds + 16 * KP;        // dO block [C][BP]
-    static constexpr int off_y = off_o + C * BP;          // Y block
-    static constexpr int off_vp = off_y + C * BP;         // V' block
-    static constexpr int off_dvp = off_vp + C * BP;       // dV' block
-    static constexpr int off_dy = off_dvp + C * BP;       // dY block
-    static constexpr int off_w = off_dy + C * BP;         // W = T^T dT, later dK o (sym)
+    // value loop: S^T, dS^T, dO, Y, V', dV', dY blocks; afterwards dT / E and dP o Gamma
+    static constexpr int off_s = off_t + C * CP;
+    static constexpr int off_ds = off_s + DK * BP;
+    static constexpr int off_o = off_ds + DK * BP;
+    static constexpr int off_y = off_o + C * BP;
+    static constexpr int off_vp = off_y + C * BP;
+    static constexpr int off_dvp = off_vp + C * BP;
+    static constexpr int off_dy = off_dvp + C * BP;
+    static constexpr int off_dt = off_s;                  // after the loop
+    static constexpr int off_p = off_s + C * CP;          // after the loop: dP o Gamma
+    static constexpr int off_w = (off_dy + C * BP > off_p + C * CP) ? off_dy + C * BP : off_p + C * CP;  // W, later dK o
     static constexpr int off_vec = off_w + C * CP;        // g, gamma, kappa, beta, dgamma, dkappa, dbeta
     static constexpr int floats = off_vec + 7 * C + 4;
     static constexpr size_t bytes = sizeof(float) * floats;
-    static_assert(off_s + 16 * KP + 16 * KP + 5 * C * BP >= off_s + C * CP, "dT fits the S/dS/value blocks");
+    static_assert(off_p + C * CP <= off_w, "dT and dP o Gamma fit the value-loop area");
     static_assert(bytes <= 160 * 1024, "one block per CU: at most the 160 KiB of LDS");
 };
 
@@ -642,6 +689,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(int H, int DV, int T, int
     extern __shared__ __align__(16) float smem[];
     float *sq = smem + L::off_q, *sk = smem + L::off_k, *st = smem + L::off_t, *sp = smem + L::off_p;
     float *ss = smem + L::off_s, *sds = smem + L::off_ds, *so = smem + L::off_o, *sy = smem + L::off_y;
+    // ss, sds: S and dS_next blocks transposed, ss[c * BP + kk] = S[vb0 + kk][c]
     float *svp = smem + L::off_vp, *sdvp = smem + L::off_dvp, *sdy = smem + L::off_dy, *sw = smem + L::off_w;
     float *vg = smem + L::off_vec, *vgam = vg + C, *vkap = vg + 2 * C, *vb = vg + 3 * C;
     float *vdgam = vg + 4 * C, *vdkap = vg + 5 * C, *vdb = vg + 6 * C;
@@ -672,11 +720,10 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(int H, int DV, int T, int
         *reinterpret_cast<float4_t *>(sk + r * KP + c) = float4_t{xk[0], xk[1], xk[2], xk[3]};
         *reinterpret_cast<float4_t *>(sk + r * KP + c + 4) = float4_t{xk[4], xk[5], xk[6], xk[7]};
     }
-    const float *Tg = ws_t + it64 * C * C, *Pg = ws_p + it64 * C * C;
+    const float *Tg = ws_t + it64 * C * C;
     for (int e = tid * 4; e < C * C; e += 256 * 4) {
         const int r = e / C, c = e % C;
         *reinterpret_cast<float4_t *>(st + r * CP + c) = *reinterpret_cast<const float4_t *>(Tg + e);
-        *reinterpret_cast<float4_t *>(sp + r * CP + c) = *reinterpret_cast<const float4_t *>(Pg + e);
     }
     if (tid < 4 * C) vg[tid] = ws_vec[it64 * kVecFloats + tid];
     if (tid < C) vdb[tid] = 0.f;
@@ -733,8 +780,11 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(int H, int DV, int T, int
             const int e = tid * 4 + 1024 * m;
             if (e < 16 * DK) {
                 const int r = e / DK, c = e % DK;
-                *reinterpret_cast<float4_t *>(ss + r * KP + c) = ga[m];
-                *reinterpret_cast<float4_t *>(sds + r * KP + c) = gb[m];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    ss[(c + i) * BP + r] = ga[m][i];
+                    sds[(c + i) * BP + r] = gb[m][i];
+                }
                 pgl += ga[m][0] * gb[m][0] + ga[m][1] * gb[m][1] + ga[m][2] * gb[m][2] + ga[m][3] * gb[m][3];
             }
         }
@@ -749,27 +799,34 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(int H, int DV, int T, int
         }
         if (vb0 + 16 < DV) load_block(vb0 + 16);
         __syncthreads();
-        // dP += dO V'^T and dM += dV' Y^T on tiles (w, c), c <= w (one k-tile: the 16 columns)
+        // One k-tile (the block's 16 value columns): lane (n, j) supplies columns 4j .. 4j + 3.
+        const float4_t ao = *reinterpret_cast<const float4_t *>(so + (rw + nn) * BP + 4 * jj);
+        const float4_t ayv = *reinterpret_cast<const float4_t *>(sdy + (rw + nn) * BP + 4 * jj);
+        const float4_t avp = *reinterpret_cast<const float4_t *>(svp + (rw + nn) * BP + 4 * jj);
+        const float4_t advp = *reinterpret_cast<const float4_t *>(sdvp + (rw + nn) * BP + 4 * jj);
+        // dP += dO V'^T and dM += dV' Y^T on tiles (w, c), c <= w
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             if (c <= w) {
-                tile_mm(dp[c], 0, 1, [&](int rr, int kk) { return so[(rw + rr) * BP + kk]; },
-                        [&](int kk, int cc) { return svp[(16 * c + cc) * BP + kk]; });
-                tile_mm(dm[c], 0, 1, [&](int rr, int kk) { return sdvp[(rw + rr) * BP + kk]; },
-                        [&](int kk, int cc) { return sy[(16 * c + cc) * BP + kk]; });
+                const float4_t bv = *reinterpret_cast<const float4_t *>(svp + (16 * c + nn) * BP + 4 * jj);
+                const float4_t by = *reinterpret_cast<const float4_t *>(sy + (16 * c + nn) * BP + 4 * jj);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    mfma4(dp[c], ao[i], bv[i]);
+                    mfma4(dm[c], advp[i], by[i]);
+                }
             }
         }
         // U += dO S,  Z += dY S,  W2 += V' dS_next
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int kk = 4 * jj + i;
-            const float ao = so[(rw + nn) * BP + kk], ay = sdy[(rw + nn) * BP + kk], av = svp[(rw + nn) * BP + kk];
+        for (int a = 0; a < NA; ++a) {
+            const float4_t bs = *reinterpret_cast<const float4_t *>(ss + (16 * a + nn) * BP + 4 * jj);
+            const float4_t bd = *reinterpret_cast<const float4_t *>(sds + (16 * a + nn) * BP + 4 * jj);
 #pragma unroll
-            for (int a = 0; a < NA; ++a) {
-                const float bs = ss[kk * KP + 16 * a + nn], bd = sds[kk * KP + 16 * a + nn];
-                mfma4(au[a], ao, bs);
-                mfma4(az[a], ay, bs);
-                mfma4(aw[a], av, bd);
+            for (int i = 0; i < 4; ++i) {
+                mfma4(au[a], ao[i], bs[i]);
+                mfma4(az[a], ayv[i], bs[i]);
+                mfma4(aw[a], avp[i], bd[i]);
             }
         }
     }
@@ -807,8 +864,8 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(int H, int DV, int T, int
         }
     atomicAdd(vgl, pgl);
     __syncthreads();
-    // dT = dM diag(beta) on the lower tiles (into the S-block area), dbeta's first part
-    float *sdt = ss;   // [C][CP]
+    // dT = dM diag(beta) on the lower tiles (into the value-loop area), dbeta's first part
+    float *sdt = smem + L::off_dt;   // [C][CP]
     for (int e = tid; e < C * CP; e += 256) sdt[e] = 0.f;
     __syncthreads();
 #pragma unroll
