@@ -30,7 +30,7 @@
 //                   dgamma_r = dO_r . (Q S^T)_r - dY_r . X_r, dkappa_r = V'_r . (K dS_next^T)_r.
 //
 // Four kernels:
-//   B1 bwd_prep_kernel      per (chunk row, head): g, gamma, kappa, T, P (fp32, VALU).
+//   B1 bwd_prep_kernel      per (chunk row, head): g, gamma, kappa, T, P and G = (K K^T) o Gamma.
 //   B2 bwd_fwd_pass_kernel  per (sequence, head, 16 value columns), four waves, chunks in order:
 //                           replays the state pass and stores the state at every
 //                           chunk start (the checkpoints).
@@ -126,7 +126,8 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(int H, int T, int cpr, in
                                                        const in_t *__restrict__ q, const in_t *__restrict__ k,
                                                        const float *__restrict__ log_alpha,
                                                        const float *__restrict__ beta, float *__restrict__ ws_t,
-                                                       float *__restrict__ ws_p, float *__restrict__ ws_vec) {
+                                                       float *__restrict__ ws_p, float *__restrict__ ws_g,
+                                                       float *__restrict__ ws_vec) {
     constexpr int KP = DK + 4, NA = DK / 16, AP = C + 1;
     extern __shared__ __align__(16) float smem[];
     float *sq = smem;                 // [C][KP]
@@ -182,15 +183,19 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(int H, int T, int cpr, in
         vec[2 * C + tid] = expf(glast - sg[tid]);
         vec[3 * C + tid] = sb[tid];
     }
-    // K K^T and Q K^T tiles; A (strictly lower) to LDS, P (lower with the diagonal) to HBM.
-    float *P = ws_p + (int64_t)item * C * C;
+    // K K^T and Q K^T tiles; A (strictly lower) to LDS; P = (Q K^T) o Gamma and
+    // G = (K K^T) o Gamma (lower with the diagonal) to HBM.
+    float *P = ws_p + (int64_t)item * C * C, *G = ws_g + (int64_t)item * C * C;
     for (int t = w; t < 16; t += 4) {
         if (t >= 10) {   // upper tiles of P are zero
             const int a = (t - 10) / 3 < 1 ? 0 : ((t - 10) < 5 ? 1 : 2);
             const int b = a == 0 ? 1 + (t - 10) : (a == 1 ? (t - 10) - 1 : 3);
             // (0,1) (0,2) (0,3) (1,2) (1,3) (2,3)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) P[(16 * a + 4 * jj + i) * C + 16 * b + nn] = 0.f;
+            for (int i = 0; i < 4; ++i) {
+                P[(16 * a + 4 * jj + i) * C + 16 * b + nn] = 0.f;
+                G[(16 * a + 4 * jj + i) * C + 16 * b + nn] = 0.f;
+            }
             continue;
         }
         int a, b;
@@ -205,6 +210,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(int H, int T, int cpr, in
             const int r = 16 * a + 4 * jj + i, c = 16 * b + nn;
             const float gm = c <= r ? expf(sg[r] - sg[c]) : 0.f;
             P[r * C + c] = qk[i] * gm;
+            G[r * C + c] = kk[i] * gm;
             sa[r * AP + c] = c < r ? sb[r] * gm * kk[i] : 0.f;
         }
     }
@@ -676,6 +682,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(int H, int DV, int T, int
                                                        const float *__restrict__ d_o,
                                                        const float *__restrict__ ws_t,
                                                        const float *__restrict__ ws_p,
+                                                       const float *__restrict__ ws_g,
                                                        const float *__restrict__ ws_vec,
                                                        const float *__restrict__ ws_ck,
                                                        const float *__restrict__ ws_ds,
@@ -720,7 +727,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(int H, int DV, int T, int
         *reinterpret_cast<float4_t *>(sk + r * KP + c) = float4_t{xk[0], xk[1], xk[2], xk[3]};
         *reinterpret_cast<float4_t *>(sk + r * KP + c + 4) = float4_t{xk[4], xk[5], xk[6], xk[7]};
     }
-    const float *Tg = ws_t + it64 * C * C;
+    const float *Tg = ws_t + it64 * C * C, *Pg = ws_p + it64 * C * C, *Gg = ws_g + it64 * C * C;
     for (int e = tid * 4; e < C * C; e += 256 * 4) {
         const int r = e / C, c = e % C;
         *reinterpret_cast<float4_t *>(st + r * CP + c) = *reinterpret_cast<const float4_t *>(Tg + e);
@@ -897,24 +904,21 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(int H, int DV, int T, int
     for (int c = 0; c < 4; ++c) {
         dkk[c] = zero4();
         if (c > w) continue;
-        float4_t da = zero4(), kk = zero4(), qk = zero4();
+        float4_t da = zero4();
         tile_mm(da, 0, 4, [&](int rr, int kx) { return -sw[(rw + rr) * CP + kx]; },
                 [&](int kx, int cc) { return st[(16 * c + cc) * CP + kx]; });
-        tile_mm(kk, 0, NA, [&](int rr, int kx) { return sk[(rw + rr) * KP + kx]; },
-                [&](int kx, int cc) { return sk[(16 * c + cc) * KP + kx]; });
-        tile_mm(qk, 0, NA, [&](int rr, int kx) { return sq[(rw + rr) * KP + kx]; },
-                [&](int kx, int cc) { return sk[(16 * c + cc) * KP + kx]; });
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = rw + 4 * jj + i, cc = 16 * c + nn;
             const float gm = cc <= r ? expf(vg[r] - vg[cc]) : 0.f;
+            const float pv = Pg[r * C + cc], gv = Gg[r * C + cc];   // (Q K^T) o Gamma, (K K^T) o Gamma
             const float dav = cc < r ? da[i] : 0.f;
-            const float db2 = dav * gm * kk[i];
+            const float db2 = dav * gv;
             const float dB = vb[r] * dav;
             dkk[c][i] = dB * gm;
             const float dpv = dp[c][i];
-            const float dG = (cc <= r ? dpv * qk[i] : 0.f) + dB * kk[i];
-            const float dgg = dG * gm;
+            // E = dGamma o Gamma with dGamma = dP o Q K^T + dB o K K^T
+            const float dgg = (cc <= r ? dpv * pv : 0.f) + dB * gv;
             sp[r * CP + cc] = cc <= r ? dpv * gm : 0.f;   // dP o Gamma (P is no longer needed)
             const float rs = row16_sum(db2);
             if (nn == 0) atomicAdd(&vdb[r], rs);
@@ -1007,6 +1011,7 @@ hipError_t launch_bwd_dk(const ChunkArgs &a, const BwdArgs &g, const BwdWorkspac
     const int32_t *rtok = reinterpret_cast<const int32_t *>(ws + w.fwd.off_rowtok);
     const int32_t *rlen = reinterpret_cast<const int32_t *>(ws + w.fwd.off_rowlen);
     float *wt = reinterpret_cast<float *>(ws + w.off_t), *wp = reinterpret_cast<float *>(ws + w.off_p);
+    float *wg = reinterpret_cast<float *>(ws + w.off_gk);
     float *wv = reinterpret_cast<float *>(ws + w.off_vec), *wck = reinterpret_cast<float *>(ws + w.off_ck);
     float *wds = reinterpret_cast<float *>(ws + w.off_ds);
     float *wy = reinterpret_cast<float *>(ws + w.off_y), *wvp = reinterpret_cast<float *>(ws + w.off_vp);
@@ -1026,7 +1031,7 @@ hipError_t launch_bwd_dk(const ChunkArgs &a, const BwdArgs &g, const BwdWorkspac
         if ((e = bwd_allow_smem(kern, sb)) != hipSuccess) return e;
         ProfScope prof("gdn_bwd_prep", st);
         kern<<<dim3((unsigned)items), dim3(256), sb, st>>>(a.H, a.T, cpr, urows, meta, rtok, rlen, q, k,
-                                                           a.log_alpha, a.beta, wt, wp, wv);
+                                                           a.log_alpha, a.beta, wt, wp, wg, wv);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (chains > 0) {
@@ -1056,7 +1061,7 @@ hipError_t launch_bwd_dk(const ChunkArgs &a, const BwdArgs &g, const BwdWorkspac
         if ((e = bwd_allow_smem(kern, L::bytes)) != hipSuccess) return e;
         ProfScope prof("gdn_bwd_grad", st);
         kern<<<dim3((unsigned)items), dim3(256), L::bytes, st>>>(a.H, a.dv, a.T, cpr, urows, meta, rtok, rlen, q, k,
-                                                                 g.d_o, wt, wp, wv, wck, wds, wy, wvp, wdvp, g.dq,
+                                                                 g.d_o, wt, wp, wg, wv, wck, wds, wy, wvp, wdvp, g.dq,
                                                                  g.dk, g.dv, g.dlog_alpha, g.dbeta);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
@@ -1085,6 +1090,7 @@ BwdWorkspace chunk_bwd_workspace_layout(int32_t B, int32_t T, int32_t N, bool pa
     size_t off = bwd_align256(w.fwd.off_g);   // only the table part of the forward layout is used
     w.off_t = off;   off = bwd_align256(off + sizeof(float) * items * C * C);
     w.off_p = off;   off = bwd_align256(off + sizeof(float) * items * C * C);
+    w.off_gk = off;  off = bwd_align256(off + sizeof(float) * items * C * C);
     w.off_vec = off; off = bwd_align256(off + sizeof(float) * items * kVecFloats);
     w.off_ck = off;  off = bwd_align256(off + sizeof(float) * items * (size_t)dv * dk);
     w.off_ds = off;  off = bwd_align256(off + sizeof(float) * items * (size_t)dv * dk);

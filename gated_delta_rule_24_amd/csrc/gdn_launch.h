@@ -71,11 +71,11 @@ struct BwdArgs {
 };
 
 // Workspace carve-up for one gdn_chunk_bwd call: the chunk table of the
-// forward layout, then per (chunk row, head) T, P and the decay vectors, the
+// forward layout, then per (chunk row, head) T, P, G and the decay vectors, the
 // state and state-gradient checkpoints, and the chunk's Y, V' and dV'.
 struct BwdWorkspace {
     ChunkWorkspace fwd;
-    size_t off_t, off_p, off_vec, off_ck, off_ds, off_y, off_vp, off_dvp, total;
+    size_t off_t, off_p, off_gk, off_vec, off_ck, off_ds, off_y, off_vp, off_dvp, total;
 };
 BwdWorkspace chunk_bwd_workspace_layout(int32_t B, int32_t T, int32_t N, bool packed, int32_t H, int32_t dk,
                                         int32_t dv);

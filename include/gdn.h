@@ -200,7 +200,8 @@ gdn_status gdn_chunk_fwd(const gdn_chunk_desc *desc,
  * Workspace for gdn_chunk_bwd, in bytes, written to *bytes (host pointer).
  * Depends only on the descriptor.  Besides the chunk table it holds, per
  * (chunk, head), the fp32 UT-transform matrix T = (I + A)^{-1}, the
- * decay-masked Q K^T block and the decay vectors (33 KiB at C = 64), the
+ * decay-masked Q K^T and K K^T blocks and the decay vectors (49 KiB at
+ * C = 64), the
  * state and the state's gradient at every chunk boundary (2 * dv * dk * 4
  * bytes) and three C x dv fp32 chunk intermediates.  Prefill with B = 4,
  * T = 4096, H = 16, dk = dv = 128 needs about 1 GiB.
