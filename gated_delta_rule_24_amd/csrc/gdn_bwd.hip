@@ -260,6 +260,12 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(int H, int T, int cpr, in
 // = S[v0 + n][16 a + 4 j + i].  Per chunk wave w forms rows 16 w .. 16 w + 15
 // of X = K S^T, Y and V' = M Y; the tiles, Y and V' pass through LDS.
 // ============================================================================
+// Position of element (x, r) of a transposed C x C matrix (row x) in LDS:
+// the row's 4-float groups are XOR-permuted by a function of x, so the
+// staging writes (16 lanes, x = 4 t + i, one r) fall in distinct banks
+// while a lane's four consecutive r of one row stay one 16-byte read.
+__device__ __forceinline__ int tswz(int x, int r) { return x * (C + 4) + (r ^ (4 * ((x >> 2) & 15))); }
+
 template <int DK>
 struct PassSmem {
     static constexpr int KP = DK + 4;   // rows of K; rows of the state tile (S or dS, 16 x DK)
@@ -269,7 +275,7 @@ struct PassSmem {
     static constexpr int off_a = off_s + 16 * KP;      // Y^T (forward) or dO^T (reverse)
     static constexpr int off_b = off_a + 16 * TP;      // V'^T (forward) or dV'^T (reverse)
     static constexpr int off_c = off_b + 16 * TP;      // dY^T (reverse)
-    static constexpr int off_m = off_c + 16 * TP;      // M (forward) or M^T (reverse), M = T diag(beta)
+    static constexpr int off_m = off_c + 16 * TP;      // M = T diag(beta) (forward) or T^T (reverse)
     static constexpr int off_v = off_m + C * TP;       // gamma, kappa, beta
     static constexpr int off_p = off_v + 3 * C;        // P^T (reverse only)
     static constexpr int off_q = off_p + C * TP;       // Q rows (reverse only)
@@ -361,15 +367,16 @@ __device__ __forceinline__ void pass_store(const PassStage<in_t, DK, REV> &S, fl
     }
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-        const int e = tid * 4 + 1024 * m, r = e / C, cc = e % C;
         if constexpr (REV) {
             float *spt = smem + L::off_p;
+            const int e = tid * 4 + 1024 * m, r = e / C, cc = e % C;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                sm[(cc + i) * TP + r] = S.t4[m][i] * S.b4[i];
-                spt[(cc + i) * TP + r] = S.p4[m][i];
+            for (int i = 0; i < 4; ++i) {   // T^T (diag(beta) is applied to T^T dV') and P^T, swizzled
+                sm[tswz(cc + i, r)] = S.t4[m][i];
+                spt[tswz(cc + i, r)] = S.p4[m][i];
             }
         } else {
+            const int e = tid * 4 + 1024 * m, r = e / C, cc = e % C;
             *reinterpret_cast<float4_t *>(sm + r * TP + cc) = S.t4[m] * S.b4;
         }
     }
@@ -579,7 +586,7 @@ __global__ __launch_bounds__(256) void bwd_rev_pass_kernel(int H, int DV, int T,
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
             if (kt >= w) {
-                const float4_t a4 = *reinterpret_cast<const float4_t *>(spt + (rw + nn) * TP + 16 * kt + 4 * jj);
+                const float4_t a4 = *reinterpret_cast<const float4_t *>(spt + tswz(rw + nn, 16 * kt + 4 * jj));
                 const float4_t b4 = *reinterpret_cast<const float4_t *>(sot + nn * TP + 16 * kt + 4 * jj);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) mfma4(dvp, a4[i], b4[i]);
@@ -589,12 +596,12 @@ __global__ __launch_bounds__(256) void bwd_rev_pass_kernel(int H, int DV, int T,
         for (int i = 0; i < 4; ++i) ws_dvp[(item * C + rw + 4 * jj + i) * DV + v0 + nn] = dvp[i];
         *reinterpret_cast<float4_t *>(sdvpt + nn * TP + rw + 4 * jj) = dvp;
         __syncthreads();
-        // dY = M^T dV'
+        // dY = M^T dV' = diag(beta) T^T dV'
         float4_t dy = zero4();
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
             if (kt >= w) {
-                const float4_t a4 = *reinterpret_cast<const float4_t *>(smt + (rw + nn) * TP + 16 * kt + 4 * jj);
+                const float4_t a4 = *reinterpret_cast<const float4_t *>(smt + tswz(rw + nn, 16 * kt + 4 * jj));
                 const float4_t b4 = *reinterpret_cast<const float4_t *>(sdvpt + nn * TP + 16 * kt + 4 * jj);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) mfma4(dy, a4[i], b4[i]);
@@ -603,6 +610,7 @@ __global__ __launch_bounds__(256) void bwd_rev_pass_kernel(int H, int DV, int T,
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = rw + 4 * jj + i;
+            dy[i] *= sv[2 * C + r];
             if (r < len) dv[((int64_t)(tok0 + r) * H + h) * DV + v0 + nn] = dy[i];
         }
         *reinterpret_cast<float4_t *>(sdyt + nn * TP + rw + 4 * jj) = dy;
@@ -753,15 +761,17 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(int H, int DV, int T, int
     // One value block's operands, loaded into registers while the previous
     // block computes: S and dS_next rows (float4 e = tid * 4 + 1024 m) and the
     // dO, dY, Y, V', dV' columns (element tid + 256 m of the C x 16 block).
-    constexpr int NS = (16 * DK + 1023) / 1024;
+    // S / dS_next block: lane tid takes row tid % 16 and columns 4 (tid / 16 + 16 m) .. + 3,
+    // so the transposed LDS stores of a wave hit consecutive banks.
+    constexpr int NS = (DK / 4 + 15) / 16;
     float4_t ga[NS], gb[NS];
     float go[4], gdy[4], gyv[4], gvp4[4], gdvp4[4];
     auto load_block = [&](int vb) {
 #pragma unroll
         for (int m = 0; m < NS; ++m) {
-            const int e = tid * 4 + 1024 * m;
-            if (e < 16 * DK) {
-                const int r = e / DK, c = e % DK;
+            const int cg = tid / 16 + 16 * m;
+            if (cg < DK / 4) {
+                const int r = tid % 16, c = 4 * cg;
                 ga[m] = *reinterpret_cast<const float4_t *>(ck + (int64_t)(vb + r) * DK + c);
                 gb[m] = *reinterpret_cast<const float4_t *>(dsn + (int64_t)(vb + r) * DK + c);
             }
@@ -784,9 +794,9 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(int H, int DV, int T, int
         __syncthreads();   // the previous blocks are no longer read
 #pragma unroll
         for (int m = 0; m < NS; ++m) {
-            const int e = tid * 4 + 1024 * m;
-            if (e < 16 * DK) {
-                const int r = e / DK, c = e % DK;
+            const int cg = tid / 16 + 16 * m;
+            if (cg < DK / 4) {
+                const int r = tid % 16, c = 4 * cg;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     ss[(c + i) * BP + r] = ga[m][i];
