@@ -883,17 +883,30 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(int H, int DV, int T, int
     __syncthreads();
     // dT = dM diag(beta) on the lower tiles (into the value-loop area), dbeta's first part
     float *sdt = smem + L::off_dt;   // [C][CP]
-    for (int e = tid; e < C * CP; e += 256) sdt[e] = 0.f;
-    __syncthreads();
+    // (Q K^T) o Gamma and (K K^T) o Gamma at the wave's lower tiles, for the dA step below
+    float pvr[4][4], gvr[4][4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = rw + 4 * jj + i, cc = 16 * c + nn;
+            pvr[c][i] = c <= w ? Pg[r * C + cc] : 0.f;
+            gvr[c][i] = c <= w ? Gg[r * C + cc] : 0.f;
+        }
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-        if (c <= w) {
+        float cs = 0.f;   // column sum of dM o T over the tile's rows
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = rw + 4 * jj + i, cc = 16 * c + nn;
-                if (cc <= r) sdt[r * CP + cc] = dm[c][i] * vb[cc];
-                atomicAdd(&vdb[cc], cc <= r ? dm[c][i] * st[r * CP + cc] : 0.f);
-            }
+        for (int i = 0; i < 4; ++i) {
+            const int r = rw + 4 * jj + i, cc = 16 * c + nn;
+            const bool in = c <= w && cc <= r;
+            sdt[r * CP + cc] = in ? dm[c][i] * vb[cc] : 0.f;
+            cs += in ? dm[c][i] * st[r * CP + cc] : 0.f;
+        }
+        if (c <= w) {
+            cs += __shfl_xor(cs, 16, 64);
+            cs += __shfl_xor(cs, 32, 64);
+            if (jj == 0) atomicAdd(&vdb[16 * c + nn], cs);
         }
     }
     __syncthreads();
@@ -921,7 +934,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(int H, int DV, int T, int
         for (int i = 0; i < 4; ++i) {
             const int r = rw + 4 * jj + i, cc = 16 * c + nn;
             const float gm = cc <= r ? expf(vg[r] - vg[cc]) : 0.f;
-            const float pv = Pg[r * C + cc], gv = Gg[r * C + cc];   // (Q K^T) o Gamma, (K K^T) o Gamma
+            const float pv = pvr[c][i], gv = gvr[c][i];
             const float dav = cc < r ? da[i] : 0.f;
             const float db2 = dav * gv;
             const float dB = vb[r] * dav;

@@ -109,3 +109,17 @@ def test_bwd_malformed_cu_reported():
     assert gdn.chunk_fwd_check(ws) == 0
     dq, *_ = gdn.chunk_bwd(q, k, v, la, b, dev(d_o), cu_seqlens=bad, workspace=ws)
     assert gdn.chunk_fwd_check(ws) == 2
+
+
+def test_bwd_empty_inputs():
+    """No tokens: the initial state's gradient is the final state's gradient
+    (the state passes through unchanged), and nothing else is written."""
+    for lens in ([0, 0, 0], None):
+        if lens is None:
+            inp = W.chunk_inputs(2, 0, 2, 64, 32, "fp32", seed=70, init_std=0.1, name="bwd empty batch")
+        else:
+            inp = W.packed_inputs(lens, H=2, dk=64, dv=32, in_dtype="fp32", seed=71, name="bwd empty packed")
+        d_o, d_final = W.incoming_grads(inp, seed=72)
+        got = _run(inp, d_o, d_final)
+        assert got[0].size == 0 and got[3].size == 0
+        assert np.array_equal(got[5], d_final)
