@@ -34,8 +34,9 @@
 //   B2 bwd_fwd_pass_kernel  per (sequence, head, 16 value columns), four waves, chunks in order:
 //                           replays the state pass and stores the state at every
 //                           chunk start (the checkpoints).
-//   B3 bwd_rev_pass_kernel  the same, chunks in reverse: the gradient of the state
-//                           at every chunk end, and of the initial state.
+//   B3 bwd_rev_pass_kernel  per (sequence, head, two 16-column tiles), chunks in reverse:
+//                           the gradient of the state at every chunk end, and of
+//                           the initial state.
 //   B4 bwd_grad_kernel      per (chunk row, head): every per-token gradient of the
 //                           chunk from its checkpoint and state gradient.
 // B2 also stores each chunk's Y and V', B3 its dV' and dY (= dV, written to
@@ -268,127 +269,99 @@ __device__ __forceinline__ int tswz(int x, int r) { return x * (C + 4) + (r ^ (4
 
 template <int DK>
 struct PassSmem {
-    static constexpr int KP = DK + 4;   // rows of K; rows of the state tile (S or dS, 16 x DK)
-    static constexpr int TP = C + 4;    // transposed value blocks [16][C]; C x C matrices; K^T, Q^T [DK][C]
+    static constexpr int KP = DK + 4;   // rows of K; rows of the state tile (S, 16 x DK)
+    static constexpr int TP = C + 4;    // transposed value blocks [16][C]; C x C matrices
     static constexpr int off_k = 0;
     static constexpr int off_s = off_k + C * KP;
-    static constexpr int off_a = off_s + 16 * KP;      // Y^T (forward) or dO^T (reverse)
-    static constexpr int off_b = off_a + 16 * TP;      // V'^T (forward) or dV'^T (reverse)
-    static constexpr int off_c = off_b + 16 * TP;      // dY^T (reverse)
-    static constexpr int off_m = off_c + 16 * TP;      // M = T diag(beta) (forward) or T^T (reverse)
+    static constexpr int off_a = off_s + 16 * KP;      // Y^T
+    static constexpr int off_b = off_a + 16 * TP;      // V'^T
+    static constexpr int off_m = off_b + 16 * TP;      // M = T diag(beta)
     static constexpr int off_v = off_m + C * TP;       // gamma, kappa, beta
-    static constexpr int off_p = off_v + 3 * C;        // P^T (reverse only)
-    static constexpr int off_q = off_p + C * TP;       // Q rows (reverse only)
-    static constexpr size_t bytes_fwd = sizeof(float) * off_p;
-    static constexpr size_t bytes_rev = sizeof(float) * (off_q + C * KP);
-    static_assert(bytes_rev <= 160 * 1024, "reverse pass fits the 160 KiB of LDS");
+    static constexpr size_t bytes_fwd = sizeof(float) * (off_v + 3 * C);
 };
 
-// One chunk's operands of a serial pass, loaded into registers while the
-// previous chunk computes (thread tid covers K / Q elements tid * 8 + 2048 m,
-// T / P elements tid * 4 + 1024 m, dO element tid + 256 m of the value block,
+// LDS of the reverse pass (two 16-column tiles per block): shared K, Q rows,
+// T^T and P^T (swizzled, tswz), the decay vectors; per tile the dS rows and
+// the transposed dO, dV', dY blocks.
+template <int DK>
+struct RevSmem {
+    static constexpr int KP = DK + 4, TP = C + 4;
+    static constexpr int off_k = 0;
+    static constexpr int off_q = off_k + C * KP;
+    static constexpr int off_m = off_q + C * KP;       // T^T
+    static constexpr int off_p = off_m + C * TP;       // P^T
+    static constexpr int off_v = off_p + C * TP;       // gamma, kappa, beta
+    static constexpr int off_t0 = off_v + 3 * C;       // per-tile blocks
+    static constexpr int TILE = 16 * KP + 3 * 16 * TP; //   dS rows, dO^T, dV'^T, dY^T
+    static constexpr int t_s = 0, t_o = 16 * KP, t_dvp = t_o + 16 * TP, t_dy = t_dvp + 16 * TP;
+    static constexpr size_t bytes = sizeof(float) * (off_t0 + 2 * TILE);
+    static_assert(bytes <= 160 * 1024, "reverse pass fits the 160 KiB of LDS");
+};
+
+// One chunk's operands of the forward pass, loaded into registers while the
+// previous chunk computes (thread tid covers K elements tid * 8 + 2048 m,
+// T elements tid * 4 + 1024 m, the V values of its lane's accumulator rows,
 // and vector element tid).
-template <typename in_t, int DK, bool REV>
+template <typename in_t, int DK>
 struct PassStage {
     static constexpr int MK = C * DK / 2048;
     int tok0, len;
     int64_t item;
-    Raw8<in_t> kr[MK], qr[REV ? MK : 1];
-    float4_t t4[4], p4[REV ? 4 : 1], b4;
-    float dov[REV ? 4 : 1], vv[REV ? 1 : 4];
+    Raw8<in_t> kr[MK];
+    float4_t t4[4], b4;
+    float vv[4];
     float vec;
 };
 
-template <typename in_t, int DK, bool REV>
-__device__ __forceinline__ void pass_load(PassStage<in_t, DK, REV> &S, int row, int H, int h, int DV, int v0, int T,
-                                          int cpr, const int32_t *row_tok, const int32_t *row_len, const in_t *q,
-                                          const in_t *k, const in_t *v, const float *d_o, const float *ws_t,
-                                          const float *ws_p, const float *ws_vec) {
+template <typename in_t, int DK>
+__device__ __forceinline__ void pass_load(PassStage<in_t, DK> &S, int row, int H, int h, int DV, int v0, int T,
+                                          int cpr, const int32_t *row_tok, const int32_t *row_len, const in_t *k,
+                                          const in_t *v, const float *ws_t, const float *ws_vec) {
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, nn = l & 15, jj = l >> 4;
     row_span(row, T, cpr, row_tok, row_len, S.tok0, S.len);
     S.item = (int64_t)row * H + h;
 #pragma unroll
-    for (int m = 0; m < PassStage<in_t, DK, REV>::MK; ++m) {
+    for (int m = 0; m < PassStage<in_t, DK>::MK; ++m) {
         const int idx = tid * 8 + 2048 * m, r = idx / DK, cc = idx % DK;
-        const int64_t off = ((int64_t)(S.tok0 + r) * H + h) * DK + cc;
-        if (r < S.len) {
-            S.kr[m].load(k + off);
-            if constexpr (REV) S.qr[m].load(q + off);
-        } else {
+        if (r < S.len)
+            S.kr[m].load(k + ((int64_t)(S.tok0 + r) * H + h) * DK + cc);
+        else
             S.kr[m].zero();
-            if constexpr (REV) S.qr[m].zero();
-        }
     }
-    const float *Tm = ws_t + S.item * C * C, *Pm = ws_p + S.item * C * C, *vec = ws_vec + S.item * kVecFloats;
+    const float *Tm = ws_t + S.item * C * C, *vec = ws_vec + S.item * kVecFloats;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        S.t4[m] = *reinterpret_cast<const float4_t *>(Tm + tid * 4 + 1024 * m);
-        if constexpr (REV) S.p4[m] = *reinterpret_cast<const float4_t *>(Pm + tid * 4 + 1024 * m);
-    }
+    for (int m = 0; m < 4; ++m) S.t4[m] = *reinterpret_cast<const float4_t *>(Tm + tid * 4 + 1024 * m);
     S.b4 = *reinterpret_cast<const float4_t *>(vec + 3 * C + (tid * 4) % C);
     S.vec = tid < 3 * C ? vec[C + tid] : 0.f;
-    if constexpr (REV) {
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const int e = tid + 256 * m, r = e / 16, cc = e % 16;
-            S.dov[m] = r < S.len ? d_o[((int64_t)(S.tok0 + r) * H + h) * DV + v0 + cc] : 0.f;
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = 16 * w + 4 * jj + i;
-            S.vv[i] = r < S.len ? to_f32(v[((int64_t)(S.tok0 + r) * H + h) * DV + v0 + nn]) : 0.f;
-        }
+    for (int i = 0; i < 4; ++i) {
+        const int r = 16 * w + 4 * jj + i;
+        S.vv[i] = r < S.len ? to_f32(v[((int64_t)(S.tok0 + r) * H + h) * DV + v0 + nn]) : 0.f;
     }
 }
 
-// Writes a staged chunk into LDS (layout of PassSmem): K rows (and Q rows
-// for the reverse pass); M (forward) or M^T and P^T (reverse); dO^T
-// (reverse); gamma, kappa, beta.
-template <typename in_t, int DK, bool REV>
-__device__ __forceinline__ void pass_store(const PassStage<in_t, DK, REV> &S, float *smem) {
+// Writes a staged chunk into LDS (layout of PassSmem): K rows, M = T diag(beta),
+// gamma, kappa, beta.
+template <typename in_t, int DK>
+__device__ __forceinline__ void pass_store(const PassStage<in_t, DK> &S, float *smem) {
     using L = PassSmem<DK>;
     constexpr int KP = L::KP, TP = L::TP;
     float *sk = smem + L::off_k, *sm = smem + L::off_m, *sv = smem + L::off_v;
     const int tid = threadIdx.x;
 #pragma unroll
-    for (int m = 0; m < PassStage<in_t, DK, REV>::MK; ++m) {
+    for (int m = 0; m < PassStage<in_t, DK>::MK; ++m) {
         const int idx = tid * 8 + 2048 * m, r = idx / DK, cc = idx % DK;
         float x[8];
         S.kr[m].to_f32(x);
         *reinterpret_cast<float4_t *>(sk + r * KP + cc) = float4_t{x[0], x[1], x[2], x[3]};
         *reinterpret_cast<float4_t *>(sk + r * KP + cc + 4) = float4_t{x[4], x[5], x[6], x[7]};
-        if constexpr (REV) {
-            float *sq = smem + L::off_q;
-            S.qr[m].to_f32(x);
-            *reinterpret_cast<float4_t *>(sq + r * KP + cc) = float4_t{x[0], x[1], x[2], x[3]};
-            *reinterpret_cast<float4_t *>(sq + r * KP + cc + 4) = float4_t{x[4], x[5], x[6], x[7]};
-        }
     }
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-        if constexpr (REV) {
-            float *spt = smem + L::off_p;
-            const int e = tid * 4 + 1024 * m, r = e / C, cc = e % C;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {   // T^T (diag(beta) is applied to T^T dV') and P^T, swizzled
-                sm[tswz(cc + i, r)] = S.t4[m][i];
-                spt[tswz(cc + i, r)] = S.p4[m][i];
-            }
-        } else {
-            const int e = tid * 4 + 1024 * m, r = e / C, cc = e % C;
-            *reinterpret_cast<float4_t *>(sm + r * TP + cc) = S.t4[m] * S.b4;
-        }
+        const int e = tid * 4 + 1024 * m, r = e / C, cc = e % C;
+        *reinterpret_cast<float4_t *>(sm + r * TP + cc) = S.t4[m] * S.b4;
     }
     if (tid < 3 * C) sv[tid] = S.vec;
-    if constexpr (REV) {
-        float *sot = smem + L::off_a;
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const int e = tid + 256 * m;
-            sot[(e % 16) * TP + e / 16] = S.dov[m];
-        }
-    }
 }
 
 template <typename in_t, int DK>
@@ -424,10 +397,8 @@ __global__ __launch_bounds__(256) void bwd_fwd_pass_kernel(int H, int DV, int T,
                    ? *reinterpret_cast<const float4_t *>(init_state + ((int64_t)nh * DV + v0 + nn) * DK + 16 * a + 4 * jj)
                    : zero4();
     }
-    PassStage<in_t, DK, false> S;
-    if (nrows > 0)
-        pass_load(S, r0, H, h, DV, v0, T, cpr, row_tok, row_len, (const in_t *)nullptr, k, v, (const float *)nullptr,
-                  ws_t, (const float *)nullptr, ws_vec);
+    PassStage<in_t, DK> S;
+    if (nrows > 0) pass_load(S, r0, H, h, DV, v0, T, cpr, row_tok, row_len, k, v, ws_t, ws_vec);
     const int rw = 16 * w;
     for (int c = 0; c < nrows; ++c) {
         const int len = S.len;
@@ -446,8 +417,7 @@ __global__ __launch_bounds__(256) void bwd_fwd_pass_kernel(int H, int DV, int T,
         }
         pass_store(S, smem);
         if (c + 1 < nrows)   // the next chunk's operands load while this one computes
-            pass_load(S, r0 + c + 1, H, h, DV, v0, T, cpr, row_tok, row_len, (const in_t *)nullptr, k, v,
-                      (const float *)nullptr, ws_t, (const float *)nullptr, ws_vec);
+            pass_load(S, r0 + c + 1, H, h, DV, v0, T, cpr, row_tok, row_len, k, v, ws_t, ws_vec);
         __syncthreads();
         const float glast = len > 0 ? sv[len - 1] : 1.f;
         // rows of the wave: X = K S^T, Y = V - diag(gamma) X
@@ -505,15 +475,99 @@ __global__ __launch_bounds__(256) void bwd_fwd_pass_kernel(int H, int DV, int T,
 }
 
 // ============================================================================
-// B3: the reverse state pass, in the layout of B2 with dS^T in the tiles.
-// Chunks in reverse: store dS (the gradient of the state at the chunk's
-// end), then
-//   dV' = P^T dO + diag(kappa) K dS^T,  dY = M^T dV',
+// B3: the reverse state pass.  One 8-wave block per (sequence, head, pair of
+// 16-column value tiles): waves 4 p .. 4 p + 3 carry tile p's dS^T in the
+// layout of B2 (wave w & 3 holds tiles (w & 3) + 4 t and computes chunk rows
+// 16 (w & 3) ..), and the two tiles share the staged K, Q, T and P.  Chunks
+// in reverse: store dS (the gradient of the state at the chunk's end), then
+//   dV' = P^T dO + diag(kappa) K dS^T,  dY = M^T dV' = diag(beta) T^T dV',
 //   dS  <- gamma_last dS + dO^T diag(gamma) Q - dY^T diag(gamma) K.
 // What is left after the first chunk is the initial state's gradient.
 // ============================================================================
 template <typename in_t, int DK>
-__global__ __launch_bounds__(256) void bwd_rev_pass_kernel(int H, int DV, int T, int cpr, int nvt,
+struct RevStage {
+    static constexpr int MK = (C * DK + 4095) / 4096;   // K / Q elements tid * 8 + 4096 m
+    int tok0, len;
+    int64_t item;
+    Raw8<in_t> kr[MK], qr[MK];
+    float4_t t4[2], p4[2];   // T / P elements tid * 4 + 2048 m
+    float dov[4];            // dO element tid + 512 m of the two tiles' value blocks
+    float vec;
+};
+
+template <typename in_t, int DK>
+__device__ __forceinline__ void rev_load(RevStage<in_t, DK> &S, int row, int H, int h, int DV, int vpair, int nvt,
+                                         int T, int cpr, const int32_t *row_tok, const int32_t *row_len,
+                                         const in_t *q, const in_t *k, const float *d_o, const float *ws_t,
+                                         const float *ws_p, const float *ws_vec) {
+    const int tid = threadIdx.x;
+    row_span(row, T, cpr, row_tok, row_len, S.tok0, S.len);
+    S.item = (int64_t)row * H + h;
+#pragma unroll
+    for (int m = 0; m < RevStage<in_t, DK>::MK; ++m) {
+        const int idx = tid * 8 + 4096 * m, r = idx / DK, cc = idx % DK;
+        const int64_t off = ((int64_t)(S.tok0 + r) * H + h) * DK + cc;
+        if (idx < C * DK && r < S.len) {
+            S.kr[m].load(k + off);
+            S.qr[m].load(q + off);
+        } else {
+            S.kr[m].zero();
+            S.qr[m].zero();
+        }
+    }
+    const float *Tm = ws_t + S.item * C * C, *Pm = ws_p + S.item * C * C, *vec = ws_vec + S.item * kVecFloats;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+        S.t4[m] = *reinterpret_cast<const float4_t *>(Tm + tid * 4 + 2048 * m);
+        S.p4[m] = *reinterpret_cast<const float4_t *>(Pm + tid * 4 + 2048 * m);
+    }
+    S.vec = tid < 3 * C ? vec[C + tid] : 0.f;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const int e = tid + 512 * m, tile = e / 1024, r = (e % 1024) / 16, cc = e % 16;
+        const int vt = 2 * vpair + tile;
+        S.dov[m] = (vt < nvt && r < S.len) ? d_o[((int64_t)(S.tok0 + r) * H + h) * DV + 16 * vt + cc] : 0.f;
+    }
+}
+
+template <typename in_t, int DK>
+__device__ __forceinline__ void rev_store(const RevStage<in_t, DK> &S, float *smem) {
+    using L = RevSmem<DK>;
+    constexpr int KP = L::KP, TP = L::TP;
+    float *sk = smem + L::off_k, *sq = smem + L::off_q, *sm = smem + L::off_m, *sp = smem + L::off_p;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int m = 0; m < RevStage<in_t, DK>::MK; ++m) {
+        const int idx = tid * 8 + 4096 * m, r = idx / DK, cc = idx % DK;
+        if (idx < C * DK) {
+            float x[8];
+            S.kr[m].to_f32(x);
+            *reinterpret_cast<float4_t *>(sk + r * KP + cc) = float4_t{x[0], x[1], x[2], x[3]};
+            *reinterpret_cast<float4_t *>(sk + r * KP + cc + 4) = float4_t{x[4], x[5], x[6], x[7]};
+            S.qr[m].to_f32(x);
+            *reinterpret_cast<float4_t *>(sq + r * KP + cc) = float4_t{x[0], x[1], x[2], x[3]};
+            *reinterpret_cast<float4_t *>(sq + r * KP + cc + 4) = float4_t{x[4], x[5], x[6], x[7]};
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+        const int e = tid * 4 + 2048 * m, r = e / C, cc = e % C;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {   // T^T (diag(beta) is applied to T^T dV') and P^T, swizzled
+            sm[tswz(cc + i, r)] = S.t4[m][i];
+            sp[tswz(cc + i, r)] = S.p4[m][i];
+        }
+    }
+    if (tid < 3 * C) smem[L::off_v + tid] = S.vec;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const int e = tid + 512 * m, tile = e / 1024, r = (e % 1024) / 16, cc = e % 16;
+        smem[L::off_t0 + tile * L::TILE + L::t_o + cc * TP + r] = S.dov[m];
+    }
+}
+
+template <typename in_t, int DK>
+__global__ __launch_bounds__(512) void bwd_rev_pass_kernel(int H, int DV, int T, int cpr, int nvt,
                                                            const int32_t *__restrict__ meta,
                                                            const int32_t *__restrict__ cu_ws,
                                                            const int32_t *__restrict__ row0,
@@ -527,120 +581,130 @@ __global__ __launch_bounds__(256) void bwd_rev_pass_kernel(int H, int DV, int T,
                                                            const float *__restrict__ d_final,
                                                            float *__restrict__ ws_ds, float *__restrict__ ws_dvp,
                                                            float *__restrict__ dv, float *__restrict__ d_init) {
-    using L = PassSmem<DK>;
+    using L = RevSmem<DK>;
     constexpr int KP = L::KP, TP = L::TP, NA = DK / 16, NT = (NA + 3) / 4;
     extern __shared__ __align__(16) float smem[];
-    float *sk = smem + L::off_k, *ss = smem + L::off_s, *sot = smem + L::off_a, *sdvpt = smem + L::off_b;
-    float *sdyt = smem + L::off_c, *smt = smem + L::off_m, *sv = smem + L::off_v, *spt = smem + L::off_p;
-    float *sq = smem + L::off_q;
     if (!cpr && meta[1] != 0) return;
-    const int nh = blockIdx.x / nvt, vt = blockIdx.x % nvt;
-    const int n = nh / H, h = nh % H, v0 = vt * 16;
+    const int npair = (nvt + 1) / 2;
+    const int nh = blockIdx.x / npair, vpair = blockIdx.x % npair;
+    const int n = nh / H, h = nh % H;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, nn = l & 15, jj = l >> 4;
+    const int tile = w >> 2, wr = w & 3, vt = 2 * vpair + tile, v0 = 16 * vt;
+    const bool active = vt < nvt;
+    const float *sk = smem + L::off_k, *sq = smem + L::off_q, *smt = smem + L::off_m, *spt = smem + L::off_p;
+    const float *sv = smem + L::off_v;
+    float *tb = smem + L::off_t0 + tile * L::TILE;
+    float *ss = tb + L::t_s, *sot = tb + L::t_o, *sdvpt = tb + L::t_dvp, *sdyt = tb + L::t_dy;
     int r0, nrows;
     seq_rows(n, T, cpr, cu_ws, row0, r0, nrows);
 
     float4_t s[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-        const int a = w + 4 * t;
-        s[t] = (d_final && a < NA)
+        const int a = wr + 4 * t;
+        s[t] = (active && d_final && a < NA)
                    ? *reinterpret_cast<const float4_t *>(d_final + ((int64_t)nh * DV + v0 + nn) * DK + 16 * a + 4 * jj)
                    : zero4();
     }
-    PassStage<in_t, DK, true> S;
+    RevStage<in_t, DK> S;
     if (nrows > 0)
-        pass_load(S, r0 + nrows - 1, H, h, DV, v0, T, cpr, row_tok, row_len, q, k, (const in_t *)nullptr, d_o, ws_t,
-                  ws_p, ws_vec);
-    const int rw = 16 * w;
+        rev_load(S, r0 + nrows - 1, H, h, DV, vpair, nvt, T, cpr, row_tok, row_len, q, k, d_o, ws_t, ws_p, ws_vec);
+    const int rw = 16 * wr;
     for (int c = nrows - 1; c >= 0; --c) {
         const int tok0 = S.tok0, len = S.len;
         const int64_t item = S.item;
         __syncthreads();
+        if (active) {
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            const int a = w + 4 * t;
-            if (a < NA) {
-                *reinterpret_cast<float4_t *>(ws_ds + (item * DV + v0 + nn) * DK + 16 * a + 4 * jj) = s[t];
-                *reinterpret_cast<float4_t *>(ss + nn * KP + 16 * a + 4 * jj) = s[t];   // row v0 + n of dS
+            for (int t = 0; t < NT; ++t) {
+                const int a = wr + 4 * t;
+                if (a < NA) {
+                    *reinterpret_cast<float4_t *>(ws_ds + (item * DV + v0 + nn) * DK + 16 * a + 4 * jj) = s[t];
+                    *reinterpret_cast<float4_t *>(ss + nn * KP + 16 * a + 4 * jj) = s[t];   // row v0 + n of dS
+                }
             }
         }
-        pass_store(S, smem);
+        rev_store(S, smem);
         if (c > 0)   // the next chunk's operands load while this one computes
-            pass_load(S, r0 + c - 1, H, h, DV, v0, T, cpr, row_tok, row_len, q, k, (const in_t *)nullptr, d_o, ws_t,
-                      ws_p, ws_vec);
+            rev_load(S, r0 + c - 1, H, h, DV, vpair, nvt, T, cpr, row_tok, row_len, q, k, d_o, ws_t, ws_p, ws_vec);
         __syncthreads();
         const float glast = len > 0 ? sv[len - 1] : 1.f;
         // dV' = P^T dO + diag(kappa) K dS^T on the wave's rows
-        float4_t x = zero4();
+        if (active) {
+            float4_t x = zero4();
 #pragma unroll
-        for (int kt = 0; kt < NA; ++kt) {
-            const float4_t a4 = *reinterpret_cast<const float4_t *>(sk + (rw + nn) * KP + 16 * kt + 4 * jj);
-            const float4_t b4 = *reinterpret_cast<const float4_t *>(ss + nn * KP + 16 * kt + 4 * jj);
+            for (int kt = 0; kt < NA; ++kt) {
+                const float4_t a4 = *reinterpret_cast<const float4_t *>(sk + (rw + nn) * KP + 16 * kt + 4 * jj);
+                const float4_t b4 = *reinterpret_cast<const float4_t *>(ss + nn * KP + 16 * kt + 4 * jj);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) mfma4(x, a4[i], b4[i]);
-        }
-        float4_t dvp;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dvp[i] = sv[C + rw + 4 * jj + i] * x[i];
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-            if (kt >= w) {
-                const float4_t a4 = *reinterpret_cast<const float4_t *>(spt + tswz(rw + nn, 16 * kt + 4 * jj));
-                const float4_t b4 = *reinterpret_cast<const float4_t *>(sot + nn * TP + 16 * kt + 4 * jj);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) mfma4(dvp, a4[i], b4[i]);
+                for (int i = 0; i < 4; ++i) mfma4(x, a4[i], b4[i]);
             }
-        }
+            float4_t dvp;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ws_dvp[(item * C + rw + 4 * jj + i) * DV + v0 + nn] = dvp[i];
-        *reinterpret_cast<float4_t *>(sdvpt + nn * TP + rw + 4 * jj) = dvp;
+            for (int i = 0; i < 4; ++i) dvp[i] = sv[C + rw + 4 * jj + i] * x[i];
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt) {
+                if (kt >= wr) {
+                    const float4_t a4 = *reinterpret_cast<const float4_t *>(spt + tswz(rw + nn, 16 * kt + 4 * jj));
+                    const float4_t b4 = *reinterpret_cast<const float4_t *>(sot + nn * TP + 16 * kt + 4 * jj);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) mfma4(dvp, a4[i], b4[i]);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ws_dvp[(item * C + rw + 4 * jj + i) * DV + v0 + nn] = dvp[i];
+            *reinterpret_cast<float4_t *>(sdvpt + nn * TP + rw + 4 * jj) = dvp;
+        }
         __syncthreads();
         // dY = M^T dV' = diag(beta) T^T dV'
-        float4_t dy = zero4();
+        if (active) {
+            float4_t dy = zero4();
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-            if (kt >= w) {
-                const float4_t a4 = *reinterpret_cast<const float4_t *>(smt + tswz(rw + nn, 16 * kt + 4 * jj));
-                const float4_t b4 = *reinterpret_cast<const float4_t *>(sdvpt + nn * TP + 16 * kt + 4 * jj);
+            for (int kt = 0; kt < 4; ++kt) {
+                if (kt >= wr) {
+                    const float4_t a4 = *reinterpret_cast<const float4_t *>(smt + tswz(rw + nn, 16 * kt + 4 * jj));
+                    const float4_t b4 = *reinterpret_cast<const float4_t *>(sdvpt + nn * TP + 16 * kt + 4 * jj);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) mfma4(dy, a4[i], b4[i]);
+                    for (int i = 0; i < 4; ++i) mfma4(dy, a4[i], b4[i]);
+                }
             }
-        }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = rw + 4 * jj + i;
-            dy[i] *= sv[2 * C + r];
-            if (r < len) dv[((int64_t)(tok0 + r) * H + h) * DV + v0 + nn] = dy[i];
+            for (int i = 0; i < 4; ++i) {
+                const int r = rw + 4 * jj + i;
+                dy[i] *= sv[2 * C + r];
+                if (r < len) dv[((int64_t)(tok0 + r) * H + h) * DV + v0 + nn] = dy[i];
+            }
+            *reinterpret_cast<float4_t *>(sdyt + nn * TP + rw + 4 * jj) = dy;
         }
-        *reinterpret_cast<float4_t *>(sdyt + nn * TP + rw + 4 * jj) = dy;
         __syncthreads();
         // dS^T <- gamma_last dS^T + Q^T diag(gamma) dO - K^T diag(gamma) dY on the wave's tiles
+        if (active) {
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            const int a = w + 4 * t;
-            if (a < NA) {
-                float4_t acc = glast * s[t];
+            for (int t = 0; t < NT; ++t) {
+                const int a = wr + 4 * t;
+                if (a < NA) {
+                    float4_t acc = glast * s[t];
 #pragma unroll
-                for (int kt = 0; kt < 4; ++kt) {
-                    const float4_t bo = *reinterpret_cast<const float4_t *>(sot + nn * TP + 16 * kt + 4 * jj);
-                    const float4_t by = *reinterpret_cast<const float4_t *>(sdyt + nn * TP + 16 * kt + 4 * jj);
+                    for (int kt = 0; kt < 4; ++kt) {
+                        const float4_t bo = *reinterpret_cast<const float4_t *>(sot + nn * TP + 16 * kt + 4 * jj);
+                        const float4_t by = *reinterpret_cast<const float4_t *>(sdyt + nn * TP + 16 * kt + 4 * jj);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int kx = 16 * kt + 4 * jj + i;
-                        const float g = sv[kx];
-                        mfma4(acc, sq[kx * KP + 16 * a + nn] * g, bo[i]);
-                        mfma4(acc, -sk[kx * KP + 16 * a + nn] * g, by[i]);
+                        for (int i = 0; i < 4; ++i) {
+                            const int kx = 16 * kt + 4 * jj + i;
+                            const float g = sv[kx];
+                            mfma4(acc, sq[kx * KP + 16 * a + nn] * g, bo[i]);
+                            mfma4(acc, -sk[kx * KP + 16 * a + nn] * g, by[i]);
+                        }
                     }
+                    s[t] = acc;
                 }
-                s[t] = acc;
             }
         }
     }
-    if (d_init) {
+    if (active && d_init) {
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            const int a = w + 4 * t;
+            const int a = wr + 4 * t;
             if (a < NA)
                 *reinterpret_cast<float4_t *>(d_init + ((int64_t)nh * DV + v0 + nn) * DK + 16 * a + 4 * jj) = s[t];
         }
@@ -1068,11 +1132,12 @@ hipError_t launch_bwd_dk(const ChunkArgs &a, const BwdArgs &g, const BwdWorkspac
             if ((e = hipGetLastError()) != hipSuccess) return e;
         }
         {
-            const size_t sb = PassSmem<DK>::bytes_rev;
+            const size_t sb = RevSmem<DK>::bytes;
             auto kern = bwd_rev_pass_kernel<in_t, DK>;
             if ((e = bwd_allow_smem(kern, sb)) != hipSuccess) return e;
             ProfScope prof("gdn_bwd_rev_pass", st);
-            kern<<<dim3((unsigned)chains), dim3(256), sb, st>>>(a.H, a.dv, a.T, cpr, nvt, meta, cu_ws, row0, rtok,
+            const int64_t pairs = (int64_t)a.N * a.H * ((nvt + 1) / 2);
+            kern<<<dim3((unsigned)pairs), dim3(512), sb, st>>>(a.H, a.dv, a.T, cpr, nvt, meta, cu_ws, row0, rtok,
                                                                 rlen, q, k, g.d_o, wt, wp, wv, g.d_final, wds,
                                                                 wdvp, g.dv, g.d_init);
             if ((e = hipGetLastError()) != hipSuccess) return e;
