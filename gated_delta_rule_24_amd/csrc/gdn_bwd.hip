@@ -739,14 +739,14 @@ struct GradSmem {
     static constexpr int off_p = off_s + C * CP;          // after the loop: dP o Gamma
     static constexpr int off_w = (off_dy + C * BP > off_p + C * CP) ? off_dy + C * BP : off_p + C * CP;  // W, later dK o
     static constexpr int off_vec = off_w + C * CP;        // g, gamma, kappa, beta, dgamma, dkappa, dbeta
-    static constexpr int floats = off_vec + 7 * C + 4;
+    static constexpr int floats = off_vec + 7 * C + 8;   // + one <dS_next, S> part per wave
     static constexpr size_t bytes = sizeof(float) * floats;
     static_assert(off_p + C * CP <= off_w, "dT and dP o Gamma fit the value-loop area");
     static_assert(bytes <= 160 * 1024, "one block per CU: at most the 160 KiB of LDS");
 };
 
 template <typename in_t, int DK>
-__global__ __launch_bounds__(256) void bwd_grad_kernel(int H, int DV, int T, int cpr, int urows,
+__global__ __launch_bounds__(512) void bwd_grad_kernel(int H, int DV, int T, int cpr, int urows,
                                                        const int32_t *__restrict__ meta,
                                                        const int32_t *__restrict__ row_tok,
                                                        const int32_t *__restrict__ row_len,
@@ -764,7 +764,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(int H, int DV, int T, int
                                                        float *__restrict__ dk, const float *__restrict__ dv,
                                                        float *__restrict__ dla, float *__restrict__ dbeta) {
     using L = GradSmem<DK>;
-    constexpr int KP = L::KP, CP = L::CP, BP = L::BP, NA = DK / 16;
+    constexpr int KP = L::KP, CP = L::CP, BP = L::BP, NA = DK / 16, NH = NA / 2;
     extern __shared__ __align__(16) float smem[];
     float *sq = smem + L::off_q, *sk = smem + L::off_k, *st = smem + L::off_t, *sp = smem + L::off_p;
     float *ss = smem + L::off_s, *sds = smem + L::off_ds, *so = smem + L::off_o, *sy = smem + L::off_y;
@@ -772,18 +772,22 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(int H, int DV, int T, int
     float *svp = smem + L::off_vp, *sdvp = smem + L::off_dvp, *sdy = smem + L::off_dy, *sw = smem + L::off_w;
     float *vg = smem + L::off_vec, *vgam = vg + C, *vkap = vg + 2 * C, *vb = vg + 3 * C;
     float *vdgam = vg + 4 * C, *vdkap = vg + 5 * C, *vdb = vg + 6 * C;
-    float *vgl = vg + 7 * C;   // [0] = <dS_next, S>
+    float *vgl = vg + 7 * C;   // per-wave parts of <dS_next, S>
     if (!cpr && meta[1] != 0) return;
     const int nrows = cpr ? urows : meta[0];
     const int item = blockIdx.x, row = item / H, h = item % H;
     if (row >= nrows) return;
     int tok0, len;
     row_span(row, T, cpr, row_tok, row_len, tok0, len);
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, nn = l & 15, jj = l >> 4;
+    // Eight waves: wave w owns chunk rows 16 (w % 4) .. + 15; the two halves of
+    // the block (w / 4) split the key-column tiles of U, Z, W2, dQ and dK, and
+    // the decay-mask steps (half 0 holds dP, half 1 holds dM).
+    const int tid = threadIdx.x, w = tid >> 6, wr = w & 3, half = w >> 2, l = tid & 63, nn = l & 15, jj = l >> 4;
+    const int a0 = half * NH;
     const int64_t it64 = (int64_t)item;
 
-    // ---- stage Q, K, T, P and the vectors ----
-    for (int idx = tid * 8; idx < C * DK; idx += 256 * 8) {
+    // ---- stage Q, K, T and the vectors ----
+    for (int idx = tid * 8; idx < C * DK; idx += 512 * 8) {
         const int r = idx / DK, c = idx % DK;
         float xq[8], xk[8];
         if (r < len) {
@@ -800,40 +804,40 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(int H, int DV, int T, int
         *reinterpret_cast<float4_t *>(sk + r * KP + c + 4) = float4_t{xk[4], xk[5], xk[6], xk[7]};
     }
     const float *Tg = ws_t + it64 * C * C, *Pg = ws_p + it64 * C * C, *Gg = ws_g + it64 * C * C;
-    for (int e = tid * 4; e < C * C; e += 256 * 4) {
+    for (int e = tid * 4; e < C * C; e += 512 * 4) {
         const int r = e / C, c = e % C;
         *reinterpret_cast<float4_t *>(st + r * CP + c) = *reinterpret_cast<const float4_t *>(Tg + e);
     }
     if (tid < 4 * C) vg[tid] = ws_vec[it64 * kVecFloats + tid];
-    if (tid < C) vdb[tid] = 0.f;
-    if (tid == 0) vgl[0] = 0.f;
+    if (tid < 3 * C) vdgam[tid] = 0.f;   // dgamma, dkappa and dbeta accumulate atomically
     __syncthreads();
 
-    const int rw = 16 * w;           // the wave's first chunk row
-    // Sums over the value dimension, rows of the wave, tile a = key columns 16 a ..:
-    //   U = dO S,  Z = dY S,  W2 = V' dS_next;  dP, dM tiles (w, c) for c <= w.
-    float4_t au[NA], az[NA], aw[NA];
+    const int rw = 16 * wr;          // the wave's first chunk row
+    // Sums over the value dimension, rows of the wave, key tiles a0 + a:
+    //   U = dO S,  Z = dY S,  W2 = V' dS_next;  and tiles (wr, c <= wr) of
+    //   dP = dO V'^T (half 0) or dM = dV' Y^T (half 1).
+    float4_t au[NH], az[NH], aw[NH], dx[4];
 #pragma unroll
-    for (int a = 0; a < NA; ++a) au[a] = az[a] = aw[a] = zero4();
-    float4_t dp[4], dm[4];
+    for (int a = 0; a < NH; ++a) au[a] = az[a] = aw[a] = zero4();
 #pragma unroll
-    for (int c = 0; c < 4; ++c) dp[c] = dm[c] = zero4();
+    for (int c = 0; c < 4; ++c) dx[c] = zero4();
     float pgl = 0.f;
+    const float *sxa = half ? sdvp : so, *sxb = half ? sy : svp;
 
     const float *ck = ws_ck + it64 * DV * DK, *dsn = ws_ds + it64 * DV * DK;
     const float *gy = ws_y + it64 * C * DV, *gvp = ws_vp + it64 * C * DV, *gdvp = ws_dvp + it64 * C * DV;
     // One value block's operands, loaded into registers while the previous
-    // block computes: S and dS_next rows (float4 e = tid * 4 + 1024 m) and the
-    // dO, dY, Y, V', dV' columns (element tid + 256 m of the C x 16 block).
-    // S / dS_next block: lane tid takes row tid % 16 and columns 4 (tid / 16 + 16 m) .. + 3,
-    // so the transposed LDS stores of a wave hit consecutive banks.
-    constexpr int NS = (DK / 4 + 15) / 16;
+    // block computes.  S / dS_next block: lane tid takes row tid % 16 and
+    // columns 4 (tid / 16 + 32 m) .. + 3, so the transposed LDS stores of a
+    // wave hit consecutive banks; dO, dY, Y, V', dV': element tid + 512 m of
+    // the C x 16 block.
+    constexpr int NS = (DK / 4 + 31) / 32;
     float4_t ga[NS], gb[NS];
-    float go[4], gdy[4], gyv[4], gvp4[4], gdvp4[4];
+    float go[2], gdy[2], gyv[2], gvp2[2], gdvp2[2];
     auto load_block = [&](int vb) {
 #pragma unroll
         for (int m = 0; m < NS; ++m) {
-            const int cg = tid / 16 + 16 * m;
+            const int cg = tid / 16 + 32 * m;
             if (cg < DK / 4) {
                 const int r = tid % 16, c = 4 * cg;
                 ga[m] = *reinterpret_cast<const float4_t *>(ck + (int64_t)(vb + r) * DK + c);
@@ -841,16 +845,16 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(int H, int DV, int T, int
             }
         }
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const int e = tid + 256 * m, r = e / 16, c = e % 16;
+        for (int m = 0; m < 2; ++m) {
+            const int e = tid + 512 * m, r = e / 16, c = e % 16;
             const bool in = r < len;
             const int64_t tv = ((int64_t)(tok0 + r) * H + h) * DV + vb + c;
             const int64_t wv = (int64_t)r * DV + vb + c;
             go[m] = in ? d_o[tv] : 0.f;
             gdy[m] = in ? dv[tv] : 0.f;
             gyv[m] = gy[wv];
-            gvp4[m] = gvp[wv];
-            gdvp4[m] = gdvp[wv];
+            gvp2[m] = gvp[wv];
+            gdvp2[m] = gdvp[wv];
         }
     };
     load_block(0);
@@ -858,7 +862,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(int H, int DV, int T, int
         __syncthreads();   // the previous blocks are no longer read
 #pragma unroll
         for (int m = 0; m < NS; ++m) {
-            const int cg = tid / 16 + 16 * m;
+            const int cg = tid / 16 + 32 * m;
             if (cg < DK / 4) {
                 const int r = tid % 16, c = 4 * cg;
 #pragma unroll
@@ -870,13 +874,13 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(int H, int DV, int T, int
             }
         }
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const int e = tid + 256 * m, r = e / 16, c = e % 16;
+        for (int m = 0; m < 2; ++m) {
+            const int e = tid + 512 * m, r = e / 16, c = e % 16;
             so[r * BP + c] = go[m];
             sdy[r * BP + c] = gdy[m];
             sy[r * BP + c] = gyv[m];
-            svp[r * BP + c] = gvp4[m];
-            sdvp[r * BP + c] = gdvp4[m];
+            svp[r * BP + c] = gvp2[m];
+            sdvp[r * BP + c] = gdvp2[m];
         }
         if (vb0 + 16 < DV) load_block(vb0 + 16);
         __syncthreads();
@@ -884,25 +888,19 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(int H, int DV, int T, int
         const float4_t ao = *reinterpret_cast<const float4_t *>(so + (rw + nn) * BP + 4 * jj);
         const float4_t ayv = *reinterpret_cast<const float4_t *>(sdy + (rw + nn) * BP + 4 * jj);
         const float4_t avp = *reinterpret_cast<const float4_t *>(svp + (rw + nn) * BP + 4 * jj);
-        const float4_t advp = *reinterpret_cast<const float4_t *>(sdvp + (rw + nn) * BP + 4 * jj);
-        // dP += dO V'^T and dM += dV' Y^T on tiles (w, c), c <= w
+        const float4_t ax = *reinterpret_cast<const float4_t *>(sxa + (rw + nn) * BP + 4 * jj);
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            if (c <= w) {
-                const float4_t bv = *reinterpret_cast<const float4_t *>(svp + (16 * c + nn) * BP + 4 * jj);
-                const float4_t by = *reinterpret_cast<const float4_t *>(sy + (16 * c + nn) * BP + 4 * jj);
+            if (c <= wr) {
+                const float4_t bx = *reinterpret_cast<const float4_t *>(sxb + (16 * c + nn) * BP + 4 * jj);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    mfma4(dp[c], ao[i], bv[i]);
-                    mfma4(dm[c], advp[i], by[i]);
-                }
+                for (int i = 0; i < 4; ++i) mfma4(dx[c], ax[i], bx[i]);
             }
         }
-        // U += dO S,  Z += dY S,  W2 += V' dS_next
 #pragma unroll
-        for (int a = 0; a < NA; ++a) {
-            const float4_t bs = *reinterpret_cast<const float4_t *>(ss + (16 * a + nn) * BP + 4 * jj);
-            const float4_t bd = *reinterpret_cast<const float4_t *>(sds + (16 * a + nn) * BP + 4 * jj);
+        for (int a = 0; a < NH; ++a) {
+            const float4_t bs = *reinterpret_cast<const float4_t *>(ss + (16 * (a0 + a) + nn) * BP + 4 * jj);
+            const float4_t bd = *reinterpret_cast<const float4_t *>(sds + (16 * (a0 + a) + nn) * BP + 4 * jj);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 mfma4(au[a], ao[i], bs[i]);
@@ -913,13 +911,15 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(int H, int DV, int T, int
     }
 
     // ---- decay sums: dgamma_r = q_r . U_r - k_r . Z_r,  dkappa_r = k_r . W2_r ----
+    // Each half adds its key tiles' part to a zeroed slot: two addends, so
+    // the result does not depend on their order.
     {
         float pg[4] = {0.f, 0.f, 0.f, 0.f}, pk[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int a = 0; a < NA; ++a)
+        for (int a = 0; a < NH; ++a)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int r = rw + 4 * jj + i, c = 16 * a + nn;
+                const int r = rw + 4 * jj + i, c = 16 * (a0 + a) + nn;
                 const float qv = sq[r * KP + c], kv = sk[r * KP + c];
                 pg[i] += qv * au[a][i] - kv * az[a][i];
                 pk[i] += kv * aw[a][i];
@@ -928,123 +928,135 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(int H, int DV, int T, int
         for (int i = 0; i < 4; ++i) {
             const float g1 = row16_sum(pg[i]), k1 = row16_sum(pk[i]);
             if (nn == 0) {
-                vdgam[rw + 4 * jj + i] = g1;
-                vdkap[rw + 4 * jj + i] = k1;
+                atomicAdd(&vdgam[rw + 4 * jj + i], g1);
+                atomicAdd(&vdkap[rw + 4 * jj + i], k1);
             }
         }
     }
     // dQ and dK rows of the wave so far: diag(gamma) U and -diag(gamma) Z + diag(kappa) W2
-    float4_t accq[NA], acck[NA];
+    float4_t accq[NH], acck[NH];
 #pragma unroll
-    for (int a = 0; a < NA; ++a)
+    for (int a = 0; a < NH; ++a)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = rw + 4 * jj + i;
             accq[a][i] = vgam[r] * au[a][i];
             acck[a][i] = vkap[r] * aw[a][i] - vgam[r] * az[a][i];
         }
-    atomicAdd(vgl, pgl);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) pgl += __shfl_xor(pgl, o, 64);
+    if (l == 0) vgl[w] = pgl;
     __syncthreads();
-    // dT = dM diag(beta) on the lower tiles (into the value-loop area), dbeta's first part
+    // The wave's decay-mask tiles: (wr, c) for c = 2 ci + half <= wr.  Their
+    // (Q K^T) o Gamma and (K K^T) o Gamma, loaded ahead of use.
     float *sdt = smem + L::off_dt;   // [C][CP]
-    // (Q K^T) o Gamma and (K K^T) o Gamma at the wave's lower tiles, for the dA step below
-    float pvr[4][4], gvr[4][4];
+    float pvr[2][4], gvr[2][4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = rw + 4 * jj + i, cc = 16 * c + nn;
-            pvr[c][i] = c <= w ? Pg[r * C + cc] : 0.f;
-            gvr[c][i] = c <= w ? Gg[r * C + cc] : 0.f;
-        }
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        float cs = 0.f;   // column sum of dM o T over the tile's rows
+    for (int ci = 0; ci < 2; ++ci)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int r = rw + 4 * jj + i, cc = 16 * c + nn;
-            const bool in = c <= w && cc <= r;
-            sdt[r * CP + cc] = in ? dm[c][i] * vb[cc] : 0.f;
-            cs += in ? dm[c][i] * st[r * CP + cc] : 0.f;
+            const int c = 2 * ci + half, r = rw + 4 * jj + i, cc = 16 * c + nn;
+            pvr[ci][i] = c <= wr ? Pg[r * C + cc] : 0.f;
+            gvr[ci][i] = c <= wr ? Gg[r * C + cc] : 0.f;
         }
-        if (c <= w) {
-            cs += __shfl_xor(cs, 16, 64);
-            cs += __shfl_xor(cs, 32, 64);
-            if (jj == 0) atomicAdd(&vdb[16 * c + nn], cs);
+    if (half) {
+        // dT = dM diag(beta) on the lower triangle (zero above), into the
+        // value-loop area; dbeta's first part, column sums of dM o T
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            float cs = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = rw + 4 * jj + i, cc = 16 * c + nn;
+                const bool in = c <= wr && cc <= r;
+                sdt[r * CP + cc] = in ? dx[c][i] * vb[cc] : 0.f;
+                cs += in ? dx[c][i] * st[r * CP + cc] : 0.f;
+            }
+            if (c <= wr) {
+                cs += __shfl_xor(cs, 16, 64);
+                cs += __shfl_xor(cs, 32, 64);
+                if (jj == 0) atomicAdd(&vdb[16 * c + nn], cs);
+            }
         }
+    } else {
+        // dP on the lower triangle (zero above)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = rw + 4 * jj + i, cc = 16 * c + nn;
+                sp[r * CP + cc] = c <= wr && cc <= r ? dx[c][i] : 0.f;
+            }
     }
     __syncthreads();
-    // W = T^T dT (rows of the wave, all column blocks), to LDS
+    // W = T^T dT, rows of the wave, column blocks 2 half and 2 half + 1.  T is
+    // lower triangular, so k-tiles before the wave's rows add nothing.
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int ci = 0; ci < 2; ++ci) {
+        const int c = 2 * half + ci;
         float4_t wt = zero4();
-        tile_mm(wt, 0, 4, [&](int rr, int kk) { return st[kk * CP + rw + rr]; },
+        tile_mm(wt, wr, 4, [&](int rr, int kk) { return st[kk * CP + rw + rr]; },
                 [&](int kk, int cc) { return sdt[kk * CP + 16 * c + cc]; });
 #pragma unroll
         for (int i = 0; i < 4; ++i) sw[(rw + 4 * jj + i) * CP + 16 * c + nn] = wt[i];
     }
     __syncthreads();
-    // dA = -W T^T on tiles (w, c <= w); with K K^T, Q K^T and Gamma form
-    // dbeta's second part, dK o, dP o Gamma and the sums of dGamma o Gamma.
-    float4_t dkk[4];
+    // dA = -W T^T on the wave's tiles (T^T is upper triangular: k-tiles up to
+    // c); with K K^T, Q K^T and Gamma form dbeta's second part, dK o, dP o
+    // Gamma and E = dGamma o Gamma.
+    float4_t dkk[2];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        dkk[c] = zero4();
-        if (c > w) continue;
+    for (int ci = 0; ci < 2; ++ci) {
+        const int c = 2 * ci + half;
+        dkk[ci] = zero4();
+        if (c > wr) continue;
         float4_t da = zero4();
-        tile_mm(da, 0, 4, [&](int rr, int kx) { return -sw[(rw + rr) * CP + kx]; },
+        tile_mm(da, 0, c + 1, [&](int rr, int kx) { return -sw[(rw + rr) * CP + kx]; },
                 [&](int kx, int cc) { return st[(16 * c + cc) * CP + kx]; });
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = rw + 4 * jj + i, cc = 16 * c + nn;
             const float gm = cc <= r ? expf(vg[r] - vg[cc]) : 0.f;
-            const float pv = pvr[c][i], gv = gvr[c][i];
+            const float pv = pvr[ci][i], gv = gvr[ci][i];
             const float dav = cc < r ? da[i] : 0.f;
             const float db2 = dav * gv;
             const float dB = vb[r] * dav;
-            dkk[c][i] = dB * gm;
-            const float dpv = dp[c][i];
+            dkk[ci][i] = dB * gm;
+            const float dpv = sp[r * CP + cc];   // zero above the diagonal
             // E = dGamma o Gamma with dGamma = dP o Q K^T + dB o K K^T
-            const float dgg = (cc <= r ? dpv * pv : 0.f) + dB * gv;
-            sp[r * CP + cc] = cc <= r ? dpv * gm : 0.f;   // dP o Gamma (P is no longer needed)
+            const float dgg = dpv * pv + dB * gv;
+            sp[r * CP + cc] = dpv * gm;         // dP o Gamma
             const float rs = row16_sum(db2);
             if (nn == 0) atomicAdd(&vdb[r], rs);
-            sdt[r * CP + cc] = cc < r ? dgg : 0.f;   // E = dGamma o Gamma, strictly lower
+            sdt[r * CP + cc] = cc < r ? dgg : 0.f;   // strictly lower; the upper tiles hold dT's zeros
         }
     }
-    // the upper tiles of dP o Gamma and of E are zero
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-        if (c > w)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                sp[(rw + 4 * jj + i) * CP + 16 * c + nn] = 0.f;
-                sdt[(rw + 4 * jj + i) * CP + 16 * c + nn] = 0.f;
-            }
     __syncthreads();
     // dK o (strictly lower) into sw (W is no longer needed)
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
+    for (int ci = 0; ci < 2; ++ci)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sw[(rw + 4 * jj + i) * CP + 16 * c + nn] = dkk[c][i];
+        for (int i = 0; i < 4; ++i) sw[(rw + 4 * jj + i) * CP + 16 * (2 * ci + half) + nn] = dkk[ci][i];
     __syncthreads();
-    // dQ += (dP o Gamma) K;  dK += (dP o Gamma)^T Q + (dK o + dK o^T) K
+    // dQ += (dP o Gamma) K;  dK += (dP o Gamma)^T Q + (dK o + dK o^T) K.  dP o Gamma
+    // is lower triangular: k-tiles up to the wave's rows for dQ, from them on for dK.
 #pragma unroll
-    for (int a = 0; a < NA; ++a) {
-        tile_mm(accq[a], 0, 4, [&](int rr, int kx) { return sp[(rw + rr) * CP + kx]; },
-                [&](int kx, int cc) { return sk[kx * KP + 16 * a + cc]; });
-        tile_mm(acck[a], 0, 4, [&](int rr, int kx) { return sp[kx * CP + rw + rr]; },
-                [&](int kx, int cc) { return sq[kx * KP + 16 * a + cc]; });
+    for (int a = 0; a < NH; ++a) {
+        const int ka = 16 * (a0 + a);
+        tile_mm(accq[a], 0, wr + 1, [&](int rr, int kx) { return sp[(rw + rr) * CP + kx]; },
+                [&](int kx, int cc) { return sk[kx * KP + ka + cc]; });
+        tile_mm(acck[a], wr, 4, [&](int rr, int kx) { return sp[kx * CP + rw + rr]; },
+                [&](int kx, int cc) { return sq[kx * KP + ka + cc]; });
         tile_mm(acck[a], 0, 4, [&](int rr, int kx) { return sw[(rw + rr) * CP + kx] + sw[kx * CP + rw + rr]; },
-                [&](int kx, int cc) { return sk[kx * KP + 16 * a + cc]; });
+                [&](int kx, int cc) { return sk[kx * KP + ka + cc]; });
     }
 #pragma unroll
-    for (int a = 0; a < NA; ++a)
+    for (int a = 0; a < NH; ++a)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = rw + 4 * jj + i;
             if (r < len) {
-                const int64_t off = ((int64_t)(tok0 + r) * H + h) * DK + 16 * a + nn;
+                const int64_t off = ((int64_t)(tok0 + r) * H + h) * DK + 16 * (a0 + a) + nn;
                 dq[off] = accq[a][i];
                 dk[off] = acck[a][i];
             }
@@ -1066,7 +1078,10 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(int H, int DV, int T, int
     __syncthreads();
     if (tid < len) {
         const int i = tid;
-        float x = vgl[0] * vgam[len - 1];
+        float gl = 0.f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) gl += vgl[u];
+        float x = gl * vgam[len - 1];
         for (int r = i; r < len; ++r) x += sdt[r * CP + i] + vdgam[r] * vgam[r];
         for (int r = 0; r < i; ++r) x += vdkap[r] * vkap[r];
         const int64_t th = (int64_t)(tok0 + i) * H + h;
@@ -1148,7 +1163,7 @@ hipError_t launch_bwd_dk(const ChunkArgs &a, const BwdArgs &g, const BwdWorkspac
         auto kern = bwd_grad_kernel<in_t, DK>;
         if ((e = bwd_allow_smem(kern, L::bytes)) != hipSuccess) return e;
         ProfScope prof("gdn_bwd_grad", st);
-        kern<<<dim3((unsigned)items), dim3(256), L::bytes, st>>>(a.H, a.dv, a.T, cpr, urows, meta, rtok, rlen, q, k,
+        kern<<<dim3((unsigned)items), dim3(512), L::bytes, st>>>(a.H, a.dv, a.T, cpr, urows, meta, rtok, rlen, q, k,
                                                                  g.d_o, wt, wp, wg, wv, wck, wds, wy, wvp, wdvp, g.dq,
                                                                  g.dk, g.dv, g.dlog_alpha, g.dbeta);
         if ((e = hipGetLastError()) != hipSuccess) return e;
