@@ -365,7 +365,7 @@ __device__ __forceinline__ void pass_store(const PassStage<in_t, DK> &S, float *
 }
 
 template <typename in_t, int DK>
-__global__ __launch_bounds__(256) void bwd_fwd_pass_kernel(int H, int DV, int T, int cpr, int nvt,
+__global__ __launch_bounds__(256) void bwd_fwd_pass_kernel(int NH, int H, int DV, int T, int cpr, int nvt,
                                                            const int32_t *__restrict__ meta,
                                                            const int32_t *__restrict__ cu_ws,
                                                            const int32_t *__restrict__ row0,
@@ -383,7 +383,12 @@ __global__ __launch_bounds__(256) void bwd_fwd_pass_kernel(int H, int DV, int T,
     float *sk = smem + L::off_k, *ss = smem + L::off_s, *syt = smem + L::off_a, *svpt = smem + L::off_b;
     float *sm = smem + L::off_m, *sv = smem + L::off_v;   // sv: gamma [C], kappa [C], beta [C]
     if (!cpr && meta[1] != 0) return;
-    const int nh = blockIdx.x / nvt, vt = blockIdx.x % nvt;
+    // The value tiles of one (sequence, head) read the same K and T.  Blocks
+    // are dealt to the 8 XCDs in turn, so give a head's tiles block indices
+    // equal mod 8: they then share one XCD's L2.
+    const int bid = blockIdx.x, slot = bid >> 3;
+    const int nh = (slot / nvt) * 8 + (bid & 7), vt = slot % nvt;
+    if (nh >= NH) return;
     const int n = nh / H, h = nh % H, v0 = vt * 16;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, nn = l & 15, jj = l >> 4;
     int r0, nrows;
@@ -567,7 +572,7 @@ __device__ __forceinline__ void rev_store(const RevStage<in_t, DK> &S, float *sm
 }
 
 template <typename in_t, int DK>
-__global__ __launch_bounds__(512) void bwd_rev_pass_kernel(int H, int DV, int T, int cpr, int nvt,
+__global__ __launch_bounds__(512) void bwd_rev_pass_kernel(int NH, int H, int DV, int T, int cpr, int nvt,
                                                            const int32_t *__restrict__ meta,
                                                            const int32_t *__restrict__ cu_ws,
                                                            const int32_t *__restrict__ row0,
@@ -586,7 +591,9 @@ __global__ __launch_bounds__(512) void bwd_rev_pass_kernel(int H, int DV, int T,
     extern __shared__ __align__(16) float smem[];
     if (!cpr && meta[1] != 0) return;
     const int npair = (nvt + 1) / 2;
-    const int nh = blockIdx.x / npair, vpair = blockIdx.x % npair;
+    const int bid = blockIdx.x, slot = bid >> 3;   // a head's tile pairs on one XCD, as in the forward pass
+    const int nh = (slot / npair) * 8 + (bid & 7), vpair = slot % npair;
+    if (nh >= NH) return;
     const int n = nh / H, h = nh % H;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, nn = l & 15, jj = l >> 4;
     const int tile = w >> 2, wr = w & 3, vt = 2 * vpair + tile, v0 = 16 * vt;
@@ -1125,7 +1132,8 @@ hipError_t launch_bwd_dk(const ChunkArgs &a, const BwdArgs &g, const BwdWorkspac
     const int urows = cpr ? (int)w.fwd.max_rows : 0;
     const int64_t items = w.fwd.max_rows * a.H;
     const int nvt = a.dv / 16;
-    const int64_t chains = (int64_t)a.N * a.H * nvt;
+    const int NH = a.N * a.H;
+    const int64_t chains = (int64_t)NH * nvt, heads8 = (NH + 7) / 8 * 8;
     hipError_t e;
     if (items > 0) {
         const size_t sb = sizeof(float) * (2 * C * (DK + 4) + 2 * C * (C + 1) + 2 * C);
@@ -1142,8 +1150,9 @@ hipError_t launch_bwd_dk(const ChunkArgs &a, const BwdArgs &g, const BwdWorkspac
             auto kern = bwd_fwd_pass_kernel<in_t, DK>;
             if ((e = bwd_allow_smem(kern, sb)) != hipSuccess) return e;
             ProfScope prof("gdn_bwd_fwd_pass", st);
-            kern<<<dim3((unsigned)chains), dim3(256), sb, st>>>(a.H, a.dv, a.T, cpr, nvt, meta, cu_ws, row0, rtok,
-                                                                rlen, k, v, wt, wv, a.init_state, wck, wy, wvp);
+            kern<<<dim3((unsigned)(heads8 * nvt)), dim3(256), sb, st>>>(NH, a.H, a.dv, a.T, cpr, nvt, meta, cu_ws,
+                                                                        row0, rtok, rlen, k, v, wt, wv,
+                                                                        a.init_state, wck, wy, wvp);
             if ((e = hipGetLastError()) != hipSuccess) return e;
         }
         {
@@ -1151,10 +1160,9 @@ hipError_t launch_bwd_dk(const ChunkArgs &a, const BwdArgs &g, const BwdWorkspac
             auto kern = bwd_rev_pass_kernel<in_t, DK>;
             if ((e = bwd_allow_smem(kern, sb)) != hipSuccess) return e;
             ProfScope prof("gdn_bwd_rev_pass", st);
-            const int64_t pairs = (int64_t)a.N * a.H * ((nvt + 1) / 2);
-            kern<<<dim3((unsigned)pairs), dim3(512), sb, st>>>(a.H, a.dv, a.T, cpr, nvt, meta, cu_ws, row0, rtok,
-                                                                rlen, q, k, g.d_o, wt, wp, wv, g.d_final, wds,
-                                                                wdvp, g.dv, g.d_init);
+            const unsigned grid = (unsigned)(heads8 * ((nvt + 1) / 2));
+            kern<<<dim3(grid), dim3(512), sb, st>>>(NH, a.H, a.dv, a.T, cpr, nvt, meta, cu_ws, row0, rtok, rlen, q, k,
+                                                    g.d_o, wt, wp, wv, g.d_final, wds, wdvp, g.dv, g.d_init);
             if ((e = hipGetLastError()) != hipSuccess) return e;
         }
     }
