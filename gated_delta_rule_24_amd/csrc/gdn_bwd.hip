@@ -108,149 +108,237 @@ constexpr int kVecFloats = 4 * C;
 }  // namespace
 
 // ============================================================================
-// B1: g, gamma, kappa, T = (I + A)^{-1} and P per (chunk row, head).
-// One 256-thread block per item; Q and K rows staged in LDS as fp32.  The
-// 10 lower 16 x 16 tiles of K K^T and Q K^T come from the matrix cores
-// (waves take tiles w, w + 4, w + 8); T blockwise: the 16 x 16 diagonal
-// blocks by substitution, the others from matrix-core products.
+// B1: g, gamma, kappa, T = (I + A)^{-1}, P and G per (chunk row, head).
+// One wave per item.  The Q and K rows stay in registers as matrix-core
+// operands: 16-bit rows on their 16x16x32 instruction (the product of two
+// 16-bit values is exact in fp32 and the sums are fp32, so this is the fp32
+// Gram matrix), fp32 rows on 16x16x4.  Lane (n, j) holds elements
+// 32 p + 8 j .. + 7 of rows 16 b + n, so the accumulator of lower tile (a, b)
+// holds row 16 a + n, columns 16 b + 4 j .. + 3: every row of P, G and T
+// leaves as 16-byte stores.
+//
+// T blockwise.  The diagonal 16 x 16 blocks by substitution: T_aa (I + N_a)
+// = I gives row n of T_aa from its own later entries and the columns of N_a
+// (the strictly lower part of A_aa), so lane (n, j) solves row n of T_jj
+// alone.  The others by distance from the diagonal:
+//   T_ab = T_aa W,  W = sum_{b <= m < a} (-A_am) T_mb,
+// on the matrix cores.  A 16 x 16 block X is held as R(X) (lane (n, j):
+// X[n][4j .. 4j + 3]) or C(X) (lane (n, j): X[4j .. 4j + 3][n], the
+// accumulator layout); C(X Y) = mm(R(X), C(Y)) and R(X Y) = mm(C(Y), R(X)).
 // ============================================================================
 __device__ __forceinline__ void tri_tile(int t, int &a, int &b) {
     a = t < 1 ? 0 : (t < 3 ? 1 : (t < 6 ? 2 : 3));
     b = t - a * (a + 1) / 2;
 }
+__host__ __device__ constexpr int tri_of(int a, int b) { return a * (a + 1) / 2 + b; }
+
+// 16 x 16 x 16 product on the 16x16x4 instruction: acc + X Y with x, y in the
+// operand layouts above.
+__device__ __forceinline__ float4_t mm16(const float4_t &x, const float4_t &y, float4_t acc) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x[i], y[i], acc, 0, 0, 0);
+    return acc;
+}
+
+// Register passes over dk: the raw Q and K rows of one pass take at most 128
+// registers per lane.
+template <typename in_t, int DK>
+struct BwdPrepShape {
+    static constexpr int KPAIR = DK / 32;                                // 32-wide k slices
+    static constexpr int REGS = KPAIR * 8 * (int)sizeof(Raw8<in_t>) / 4;  // Q and K, 4 row blocks
+    static constexpr int NPASS = REGS > 128 ? REGS / 128 : 1;
+    static constexpr int PP = KPAIR / NPASS;
+    static_assert(PP * NPASS == KPAIR, "dk splits evenly into passes");
+};
 
 template <typename in_t, int DK>
-__global__ __launch_bounds__(256) void bwd_prep_kernel(int H, int T, int cpr, int urows,
-                                                       const int32_t *__restrict__ meta,
-                                                       const int32_t *__restrict__ row_tok,
-                                                       const int32_t *__restrict__ row_len,
-                                                       const in_t *__restrict__ q, const in_t *__restrict__ k,
-                                                       const float *__restrict__ log_alpha,
-                                                       const float *__restrict__ beta, float *__restrict__ ws_t,
-                                                       float *__restrict__ ws_p, float *__restrict__ ws_g,
-                                                       float *__restrict__ ws_vec) {
-    constexpr int KP = DK + 4, NA = DK / 16, AP = C + 1;
-    extern __shared__ __align__(16) float smem[];
-    float *sq = smem;                 // [C][KP]
-    float *sk = sq + C * KP;          // [C][KP]
-    float *sa = sk + C * KP;          // [C][AP]  A (strictly lower)
-    float *st = sa + C * AP;          // [C][AP]  T
-    float *sg = st + C * AP;          // [C]
-    float *sb = sg + C;               // [C]
+__global__ __launch_bounds__(64) void bwd_prep_kernel(int H, int T, int cpr, int urows,
+                                                      const int32_t *__restrict__ meta,
+                                                      const int32_t *__restrict__ row_tok,
+                                                      const int32_t *__restrict__ row_len,
+                                                      const in_t *__restrict__ q, const in_t *__restrict__ k,
+                                                      const float *__restrict__ log_alpha,
+                                                      const float *__restrict__ beta, float *__restrict__ ws_t,
+                                                      float *__restrict__ ws_p, float *__restrict__ ws_g,
+                                                      float *__restrict__ ws_vec) {
+    using Sh = BwdPrepShape<in_t, DK>;
+    constexpr int PP = Sh::PP, NPASS = Sh::NPASS;
+    constexpr int BP = 20, BS = 16 * BP + 4;   // one 16 x 16 block in LDS (row pitch, block pitch)
+    __shared__ __align__(16) float lds[2 * C + 4 * BS];
+    float *sg = lds, *sb = lds + C, *blk = lds + 2 * C;
     if (!cpr && meta[1] != 0) return;   // malformed cu_seqlens: nothing is written
     const int nrows = cpr ? urows : meta[0];
     const int item = blockIdx.x, row = item / H, h = item % H;
     if (row >= nrows) return;
     int tok0, len;
     row_span(row, T, cpr, row_tok, row_len, tok0, len);
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, nn = l & 15, jj = l >> 4;
+    const int l = threadIdx.x, nn = l & 15, jj = l >> 4;
 
-    for (int idx = tid * 8; idx < C * DK; idx += 256 * 8) {
-        const int r = idx / DK, c = idx % DK;
-        float xq[8], xk[8];
-        if (r < len) {
-            const int64_t off = ((int64_t)(tok0 + r) * H + h) * DK + c;
-            load8_f32(q + off, xq);
-            load8_f32(k + off, xk);
-        } else {
+    // Rows past the end of the sequence: log alpha = beta = 0 and zero Q, K
+    // rows, inert in every product, and g stays flat there.
+    Raw8<in_t> kr[4][PP], qr[4][PP];
+    auto load = [&](int s) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) xq[e] = xk[e] = 0.f;
-        }
-        *reinterpret_cast<float4_t *>(sq + r * KP + c) = float4_t{xq[0], xq[1], xq[2], xq[3]};
-        *reinterpret_cast<float4_t *>(sq + r * KP + c + 4) = float4_t{xq[4], xq[5], xq[6], xq[7]};
-        *reinterpret_cast<float4_t *>(sk + r * KP + c) = float4_t{xk[0], xk[1], xk[2], xk[3]};
-        *reinterpret_cast<float4_t *>(sk + r * KP + c + 4) = float4_t{xk[4], xk[5], xk[6], xk[7]};
-    }
-    if (tid < C) {
-        const bool in = tid < len;
-        const int64_t th = (int64_t)(tok0 + tid) * H + h;
-        sg[tid] = in ? log_alpha[th] : 0.f;
-        sb[tid] = in ? beta[th] : 0.f;
-    }
-    __syncthreads();
-    float *vec = ws_vec + (int64_t)item * kVecFloats;
-    if (tid == 0) {
-        float acc = 0.f;
-        for (int r = 0; r < C; ++r) {
-            acc += sg[r];
-            sg[r] = acc;
-        }
-    }
-    __syncthreads();
-    const float glast = len > 0 ? sg[len - 1] : 0.f;
-    if (tid < C) {
-        vec[tid] = sg[tid];
-        vec[C + tid] = expf(sg[tid]);
-        vec[2 * C + tid] = expf(glast - sg[tid]);
-        vec[3 * C + tid] = sb[tid];
-    }
-    // K K^T and Q K^T tiles; A (strictly lower) to LDS; P = (Q K^T) o Gamma and
-    // G = (K K^T) o Gamma (lower with the diagonal) to HBM.
-    float *P = ws_p + (int64_t)item * C * C, *G = ws_g + (int64_t)item * C * C;
-    for (int t = w; t < 16; t += 4) {
-        if (t >= 10) {   // upper tiles of P are zero
-            const int a = (t - 10) / 3 < 1 ? 0 : ((t - 10) < 5 ? 1 : 2);
-            const int b = a == 0 ? 1 + (t - 10) : (a == 1 ? (t - 10) - 1 : 3);
-            // (0,1) (0,2) (0,3) (1,2) (1,3) (2,3)
+        for (int b = 0; b < 4; ++b) {
+            const int r = 16 * b + nn;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                P[(16 * a + 4 * jj + i) * C + 16 * b + nn] = 0.f;
-                G[(16 * a + 4 * jj + i) * C + 16 * b + nn] = 0.f;
+            for (int p = 0; p < PP; ++p) {
+                if (r < len) {
+                    const int64_t off = ((int64_t)(tok0 + r) * H + h) * DK + 32 * (s * PP + p) + 8 * jj;
+                    kr[b][p].load(k + off);
+                    qr[b][p].load(q + off);
+                } else {
+                    kr[b][p].zero();
+                    qr[b][p].zero();
+                }
             }
-            continue;
         }
+    };
+    load(0);
+    float la = 0.f, bt = 0.f;
+    if (l < len) {
+        const int64_t th = (int64_t)(tok0 + l) * H + h;
+        la = log_alpha[th];
+        bt = beta[th];
+    }
+    const float g = wave_inclusive_scan(la);
+    const float glast = __shfl(g, C - 1, 64);
+    sg[l] = g;
+    sb[l] = bt;
+    float *vec = ws_vec + (int64_t)item * kVecFloats;
+    vec[l] = g;
+    vec[C + l] = expf(g);
+    vec[2 * C + l] = expf(glast - g);
+    vec[3 * C + l] = bt;
+
+    // Lower tiles t = (a, b) of K K^T and Q K^T, R layout.
+    float4_t kk[kTriTiles], qk[kTriTiles];
+#pragma unroll
+    for (int t = 0; t < kTriTiles; ++t) kk[t] = qk[t] = zero4();
+#pragma unroll
+    for (int s = 0; s < NPASS; ++s) {
+        if (s > 0) load(s);
+#pragma unroll
+        for (int t = 0; t < kTriTiles; ++t) {
+            int a, b;
+            tri_tile(t, a, b);
+#pragma unroll
+            for (int p = 0; p < PP; ++p) {
+                gram_mma(kk[t], kr[b][p], kr[a][p]);
+                gram_mma(qk[t], kr[b][p], qr[a][p]);
+            }
+        }
+    }
+
+    // Decay masks.  P = (Q K^T) o Gamma and G = (K K^T) o Gamma (lower with the
+    // diagonal) to HBM; -A for the off-diagonal tiles in registers, N_a^T of
+    // the diagonal blocks to LDS (blk[a][c][m] = A[16a + m][16a + c], m > c).
+    float *P = ws_p + (int64_t)item * C * C, *G = ws_g + (int64_t)item * C * C, *Tm = ws_t + (int64_t)item * C * C;
+    float gr[4], br[4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+        gr[a] = sg[16 * a + nn];
+        br[a] = sb[16 * a + nn];
+    }
+    float4_t naR[kTriTiles];   // R(-A_ab), a > b
+#pragma unroll
+    for (int t = 0; t < kTriTiles; ++t) {
         int a, b;
         tri_tile(t, a, b);
-        float4_t kk = zero4(), qk = zero4();
-        tile_mm(kk, 0, NA, [&](int rr, int kx) { return sk[(16 * a + rr) * KP + kx]; },
-                [&](int kx, int cc) { return sk[(16 * b + cc) * KP + kx]; });
-        tile_mm(qk, 0, NA, [&](int rr, int kx) { return sq[(16 * a + rr) * KP + kx]; },
-                [&](int kx, int cc) { return sk[(16 * b + cc) * KP + kx]; });
+        const float4_t gc = *reinterpret_cast<const float4_t *>(sg + 16 * b + 4 * jj);
+        float4_t pv, gv, av;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int r = 16 * a + 4 * jj + i, c = 16 * b + nn;
-            const float gm = c <= r ? expf(sg[r] - sg[c]) : 0.f;
-            P[r * C + c] = qk[i] * gm;
-            G[r * C + c] = kk[i] * gm;
-            sa[r * AP + c] = c < r ? sb[r] * gm * kk[i] : 0.f;
+            const int r = 16 * a + nn, c = 16 * b + 4 * jj + i;
+            const float gm = c <= r ? expf(gr[a] - gc[i]) : 0.f;
+            pv[i] = qk[t][i] * gm;
+            gv[i] = kk[t][i] * gm;
+            av[i] = c < r ? br[a] * gm * kk[t][i] : 0.f;
+        }
+        const int64_t o = (int64_t)(16 * a + nn) * C + 16 * b + 4 * jj;
+        *reinterpret_cast<float4_t *>(P + o) = pv;
+        *reinterpret_cast<float4_t *>(G + o) = gv;
+        if (a > b) {
+            naR[t] = -av;
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) blk[a * BS + (4 * jj + i) * BP + nn] = av[i];
+            naR[t] = zero4();
         }
     }
-    // T = (I + A)^{-1} on 16 x 16 blocks.  Diagonal blocks: lane n of wave w
-    // solves column n of T_ww by substitution in registers.  Off-diagonal,
-    // by distance d = a - b: T_ab = -T_aa sum_{b <= m < a} A_am T_mb on the
-    // matrix cores, wave a taking block (a, a - d).
-    for (int e = tid; e < C * AP; e += 256) st[e] = 0.f;
-    __syncthreads();
-    if (l < 16) {
-        const int a = w, c = l;
-        float tc[16];
+    // the upper tiles of P, G and T are zero
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float x = r == c ? 1.f : 0.f;
+    for (int a = 0; a < 3; ++a)
 #pragma unroll
-            for (int i = 0; i < r; ++i) x -= sa[(16 * a + r) * AP + 16 * a + i] * tc[i];
-            tc[r] = r < c ? 0.f : x;
+        for (int b = a + 1; b < 4; ++b) {
+            const int64_t o = (int64_t)(16 * a + nn) * C + 16 * b + 4 * jj;
+            *reinterpret_cast<float4_t *>(P + o) = zero4();
+            *reinterpret_cast<float4_t *>(G + o) = zero4();
+            *reinterpret_cast<float4_t *>(Tm + o) = zero4();
         }
+    // One wave: its LDS accesses are performed in program order, so only the
+    // compiler has to be kept from moving them.
+    asm volatile("" ::: "memory");
+
+    // Diagonal blocks: lane (n, j) solves row n of T_jj,
+    //   x[c] = [c == n] - sum_{m > c} x[m] N[m][c],  c = 15 .. 0.
+    {
+        const float *nt = blk + jj * BS;
+        float x[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) st[(16 * a + r) * AP + 16 * a + c] = tc[r];
-    }
-    for (int d = 1; d < 4; ++d) {
-        __syncthreads();
-        if (w >= d) {
-            const int a = w, b = w - d;
-            float4_t u = zero4();
-            tile_mm(u, b, a, [&](int rr, int kx) { return sa[(16 * a + rr) * AP + kx]; },
-                    [&](int kx, int cc) { return st[kx * AP + 16 * b + cc]; });
-            float4_t t = zero4();
+        for (int c = 15; c >= 0; --c) {
+            float acc = c == nn ? 1.f : 0.f;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) mfma4(t, -st[(16 * a + nn) * AP + 16 * a + 4 * jj + i], u[i]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) st[(16 * a + 4 * jj + i) * AP + 16 * b + nn] = t[i];
+            for (int m = c + 1; m < 16; ++m) acc -= x[m] * nt[c * BP + m];
+            x[c] = acc;
         }
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            *reinterpret_cast<float4_t *>(blk + jj * BS + nn * BP + 4 * e) =
+                float4_t{x[4 * e], x[4 * e + 1], x[4 * e + 2], x[4 * e + 3]};
     }
-    __syncthreads();
-    float *Tm = ws_t + (int64_t)item * C * C;
-    for (int e = tid; e < C * C; e += 256) Tm[e] = st[(e / C) * AP + e % C];
+    asm volatile("" ::: "memory");
+    float4_t tR[4], tC[3];   // R(T_aa), C(T_bb)
+#pragma unroll
+    for (int a = 0; a < 4; ++a) tR[a] = *reinterpret_cast<const float4_t *>(blk + a * BS + nn * BP + 4 * jj);
+#pragma unroll
+    for (int b = 0; b < 3; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) tC[b][i] = blk[b * BS + (4 * jj + i) * BP + nn];
+
+    // Off-diagonal blocks by distance; C layouts where a later W needs them.
+    const float4_t z = zero4();
+    float4_t W, T10, T21, T32, T20, T31, T30, C10, C21, C20;
+    W = mm16(naR[tri_of(1, 0)], tC[0], z);
+    T10 = mm16(W, tR[1], z);
+    C10 = mm16(tR[1], W, z);
+    W = mm16(naR[tri_of(2, 1)], tC[1], z);
+    T21 = mm16(W, tR[2], z);
+    C21 = mm16(tR[2], W, z);
+    W = mm16(naR[tri_of(3, 2)], tC[2], z);
+    T32 = mm16(W, tR[3], z);
+    W = mm16(naR[tri_of(2, 1)], C10, mm16(naR[tri_of(2, 0)], tC[0], z));
+    T20 = mm16(W, tR[2], z);
+    C20 = mm16(tR[2], W, z);
+    W = mm16(naR[tri_of(3, 2)], C21, mm16(naR[tri_of(3, 1)], tC[1], z));
+    T31 = mm16(W, tR[3], z);
+    W = mm16(naR[tri_of(3, 2)], C20, mm16(naR[tri_of(3, 1)], C10, mm16(naR[tri_of(3, 0)], tC[0], z)));
+    T30 = mm16(W, tR[3], z);
+
+    auto put = [&](int a, int b, const float4_t &x) {
+        *reinterpret_cast<float4_t *>(Tm + (int64_t)(16 * a + nn) * C + 16 * b + 4 * jj) = x;
+    };
+    put(0, 0, tR[0]);
+    put(1, 0, T10);
+    put(1, 1, tR[1]);
+    put(2, 0, T20);
+    put(2, 1, T21);
+    put(2, 2, tR[2]);
+    put(3, 0, T30);
+    put(3, 1, T31);
+    put(3, 2, T32);
+    put(3, 3, tR[3]);
 }
 
 // ============================================================================
@@ -1136,12 +1224,9 @@ hipError_t launch_bwd_dk(const ChunkArgs &a, const BwdArgs &g, const BwdWorkspac
     const int64_t chains = (int64_t)NH * nvt, heads8 = (NH + 7) / 8 * 8;
     hipError_t e;
     if (items > 0) {
-        const size_t sb = sizeof(float) * (2 * C * (DK + 4) + 2 * C * (C + 1) + 2 * C);
-        auto kern = bwd_prep_kernel<in_t, DK>;
-        if ((e = bwd_allow_smem(kern, sb)) != hipSuccess) return e;
         ProfScope prof("gdn_bwd_prep", st);
-        kern<<<dim3((unsigned)items), dim3(256), sb, st>>>(a.H, a.T, cpr, urows, meta, rtok, rlen, q, k,
-                                                           a.log_alpha, a.beta, wt, wp, wg, wv);
+        bwd_prep_kernel<in_t, DK><<<dim3((unsigned)items), dim3(64), 0, st>>>(a.H, a.T, cpr, urows, meta, rtok, rlen,
+                                                                             q, k, a.log_alpha, a.beta, wt, wp, wg, wv);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (chains > 0) {

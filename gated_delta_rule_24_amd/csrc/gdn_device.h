@@ -283,6 +283,27 @@ struct Raw8<float> {
     }
 };
 
+// acc += (row block X) (row block Y)^T over one k-tile pair of raw inputs.
+// bf16 and fp16 rows use their own 16x16x32 instruction (exact products,
+// fp32 sums); fp32 rows take eight 16x16x4 fp32 instructions.
+__device__ __forceinline__ void gram_mma(float4_t &acc, const Raw8<bf16_t> &x, const Raw8<bf16_t> &y) {
+    typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, x.x),
+                                                 __builtin_bit_cast(bf16x8_t, y.x), acc, 0, 0, 0);
+}
+__device__ __forceinline__ void gram_mma(float4_t &acc, const Raw8<_Float16> &x, const Raw8<_Float16> &y) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, x.x),
+                                                __builtin_bit_cast(half8_t, y.x), acc, 0, 0, 0);
+}
+__device__ __forceinline__ void gram_mma(float4_t &acc, const Raw8<float> &x, const Raw8<float> &y) {
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+        const float4_t a = __builtin_bit_cast(float4_t, x.x[hh]), b = __builtin_bit_cast(float4_t, y.x[hh]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[i], acc, 0, 0, 0);
+    }
+}
+
 template <typename in_t>
 __device__ __forceinline__ in_t zero_elem() { return in_t{}; }
 
