@@ -389,7 +389,9 @@ struct RevSmem {
 // One chunk's operands of the forward pass, loaded into registers while the
 // previous chunk computes (thread tid covers K elements tid * 8 + 2048 m,
 // T elements tid * 4 + 1024 m, the V values of its lane's accumulator rows,
-// and vector element tid).
+// and vector element tid).  Every load is unconditional (rows past the
+// chunk's end re-read its last row and are zeroed on use), so no wait is
+// attached to a load right after it is issued.
 template <typename in_t, int DK>
 struct PassStage {
     static constexpr int MK = C * DK / 2048;
@@ -397,7 +399,7 @@ struct PassStage {
     int64_t item;
     Raw8<in_t> kr[MK];
     float4_t t4[4], b4;
-    float vv[4];
+    in_t vv[4];
     float vec;
 };
 
@@ -410,21 +412,18 @@ __device__ __forceinline__ void pass_load(PassStage<in_t, DK> &S, int row, int H
     S.item = (int64_t)row * H + h;
 #pragma unroll
     for (int m = 0; m < PassStage<in_t, DK>::MK; ++m) {
-        const int idx = tid * 8 + 2048 * m, r = idx / DK, cc = idx % DK;
-        if (r < S.len)
-            S.kr[m].load(k + ((int64_t)(S.tok0 + r) * H + h) * DK + cc);
-        else
-            S.kr[m].zero();
+        const int idx = tid * 8 + 2048 * m, r = min(idx / DK, S.len - 1), cc = idx % DK;
+        S.kr[m].load(k + ((int64_t)(S.tok0 + r) * H + h) * DK + cc);
     }
     const float *Tm = ws_t + S.item * C * C, *vec = ws_vec + S.item * kVecFloats;
 #pragma unroll
     for (int m = 0; m < 4; ++m) S.t4[m] = *reinterpret_cast<const float4_t *>(Tm + tid * 4 + 1024 * m);
     S.b4 = *reinterpret_cast<const float4_t *>(vec + 3 * C + (tid * 4) % C);
-    S.vec = tid < 3 * C ? vec[C + tid] : 0.f;
+    S.vec = vec[C + min(tid, 3 * C - 1)];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int r = 16 * w + 4 * jj + i;
-        S.vv[i] = r < S.len ? to_f32(v[((int64_t)(S.tok0 + r) * H + h) * DV + v0 + nn]) : 0.f;
+        const int r = min(16 * w + 4 * jj + i, S.len - 1);
+        S.vv[i] = v[((int64_t)(S.tok0 + r) * H + h) * DV + v0 + nn];
     }
 }
 
@@ -441,6 +440,9 @@ __device__ __forceinline__ void pass_store(const PassStage<in_t, DK> &S, float *
         const int idx = tid * 8 + 2048 * m, r = idx / DK, cc = idx % DK;
         float x[8];
         S.kr[m].to_f32(x);
+        if (r >= S.len)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = 0.f;
         *reinterpret_cast<float4_t *>(sk + r * KP + cc) = float4_t{x[0], x[1], x[2], x[3]};
         *reinterpret_cast<float4_t *>(sk + r * KP + cc + 4) = float4_t{x[4], x[5], x[6], x[7]};
     }
@@ -493,24 +495,43 @@ __global__ __launch_bounds__(256) void bwd_fwd_pass_kernel(int NH, int H, int DV
     PassStage<in_t, DK> S;
     if (nrows > 0) pass_load(S, r0, H, h, DV, v0, T, cpr, row_tok, row_len, k, v, ws_t, ws_vec);
     const int rw = 16 * w;
+    // Y and V' of the previous chunk, stored once the next chunk's operands
+    // have landed: a wave's loads and stores share one completion counter that
+    // need not drain in order, so a wait for loads also waits for every store
+    // issued before it.  Stores therefore go out right after a wait and
+    // before the next loads, a whole chunk ahead of the next wait.
+    float4_t py = zero4(), pvp = zero4();
+    int64_t pitem = -1;
+    auto store_yv = [&]() {
+        if (pitem >= 0) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t o = (pitem * C + rw + 4 * jj + i) * DV + v0 + nn;
+                ws_y[o] = py[i];
+                ws_vp[o] = pvp[i];
+            }
+        }
+    };
     for (int c = 0; c < nrows; ++c) {
         const int len = S.len;
         const int64_t item = S.item;
         float vv[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) vv[i] = S.vv[i];
+        for (int i = 0; i < 4; ++i) vv[i] = 16 * w + 4 * jj + i < len ? to_f32(S.vv[i]) : 0.f;
         __syncthreads();   // the previous chunk's LDS contents are no longer read
+        pass_store(S, smem);
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             const int a = w + 4 * t;
             if (a < NA) {
-                *reinterpret_cast<float4_t *>(ws_ck + (item * DV + v0 + nn) * DK + 16 * a + 4 * jj) = s[t];
                 *reinterpret_cast<float4_t *>(ss + nn * KP + 16 * a + 4 * jj) = s[t];   // row v0 + n of S
+                *reinterpret_cast<float4_t *>(ws_ck + (item * DV + v0 + nn) * DK + 16 * a + 4 * jj) = s[t];
             }
         }
-        pass_store(S, smem);
-        if (c + 1 < nrows)   // the next chunk's operands load while this one computes
-            pass_load(S, r0 + c + 1, H, h, DV, v0, T, cpr, row_tok, row_len, k, v, ws_t, ws_vec);
+        store_yv();
+        // the next chunk's operands load while this one computes (the last
+        // chunk loads itself again)
+        pass_load(S, r0 + min(c + 1, nrows - 1), H, h, DV, v0, T, cpr, row_tok, row_len, k, v, ws_t, ws_vec);
         __syncthreads();
         const float glast = len > 0 ? sv[len - 1] : 1.f;
         // rows of the wave: X = K S^T, Y = V - diag(gamma) X
@@ -524,11 +545,7 @@ __global__ __launch_bounds__(256) void bwd_fwd_pass_kernel(int NH, int H, int DV
         }
         float4_t y;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = rw + 4 * jj + i;
-            y[i] = vv[i] - sv[r] * x[i];
-            ws_y[(item * C + r) * DV + v0 + nn] = y[i];
-        }
+        for (int i = 0; i < 4; ++i) y[i] = vv[i] - sv[rw + 4 * jj + i] * x[i];
         *reinterpret_cast<float4_t *>(syt + nn * TP + rw + 4 * jj) = y;
         __syncthreads();
         // V' = M Y, M lower block triangular
@@ -542,8 +559,9 @@ __global__ __launch_bounds__(256) void bwd_fwd_pass_kernel(int NH, int H, int DV
                 for (int i = 0; i < 4; ++i) mfma4(vp, a4[i], b4[i]);
             }
         }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ws_vp[(item * C + rw + 4 * jj + i) * DV + v0 + nn] = vp[i];
+        py = y;
+        pvp = vp;
+        pitem = item;
         *reinterpret_cast<float4_t *>(svpt + nn * TP + rw + 4 * jj) = vp;
         __syncthreads();
         // S^T <- gamma_last S^T + K^T diag(kappa) V' on the wave's tiles
@@ -565,6 +583,7 @@ __global__ __launch_bounds__(256) void bwd_fwd_pass_kernel(int NH, int H, int DV
             }
         }
     }
+    store_yv();
 }
 
 // ============================================================================
@@ -919,24 +938,38 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(int H, int DV, int T, int
     float pgl = 0.f;
     const float *sxa = half ? sdvp : so, *sxb = half ? sy : svp;
 
+    // The wave's decay-mask tiles: (wr, c) for c = 2 ci + half <= wr.  Their
+    // (Q K^T) o Gamma and (K K^T) o Gamma, loaded here to land during the loop.
+    float pvr[2][4], gvr[2][4];
+#pragma unroll
+    for (int ci = 0; ci < 2; ++ci)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int c = 2 * ci + half, r = rw + 4 * jj + i, cc = 16 * c + nn;
+            pvr[ci][i] = c <= wr ? Pg[r * C + cc] : 0.f;
+            gvr[ci][i] = c <= wr ? Gg[r * C + cc] : 0.f;
+        }
+
     const float *ck = ws_ck + it64 * DV * DK, *dsn = ws_ds + it64 * DV * DK;
     const float *gy = ws_y + it64 * C * DV, *gvp = ws_vp + it64 * C * DV, *gdvp = ws_dvp + it64 * C * DV;
-    // One value block's operands, loaded into registers while the previous
-    // block computes.  S / dS_next block: lane tid takes row tid % 16 and
-    // columns 4 (tid / 16 + 32 m) .. + 3, so the transposed LDS stores of a
-    // wave hit consecutive banks; dO, dY, Y, V', dV': element tid + 512 m of
-    // the C x 16 block.
+    // One value block's operands in registers.  S / dS_next block: lane tid
+    // takes row tid % 16 and columns 4 (tid / 16 + 32 m) .. + 3, so the
+    // transposed LDS stores of a wave hit consecutive banks; dO, dY, Y, V',
+    // dV': element tid + 512 m of the C x 16 block.  Two sets alternate, so
+    // each block's loads are issued two blocks ahead of its use.
     constexpr int NS = (DK / 4 + 31) / 32;
-    float4_t ga[NS], gb[NS];
-    float go[2], gdy[2], gyv[2], gvp2[2], gdvp2[2];
-    auto load_block = [&](int vb) {
+    struct VBlock {
+        float4_t ga[NS], gb[NS];
+        float go[2], gdy[2], gyv[2], gvp[2], gdvp[2];
+    };
+    auto load_block = [&](VBlock &B, int vb) {
 #pragma unroll
         for (int m = 0; m < NS; ++m) {
             const int cg = tid / 16 + 32 * m;
             if (cg < DK / 4) {
                 const int r = tid % 16, c = 4 * cg;
-                ga[m] = *reinterpret_cast<const float4_t *>(ck + (int64_t)(vb + r) * DK + c);
-                gb[m] = *reinterpret_cast<const float4_t *>(dsn + (int64_t)(vb + r) * DK + c);
+                B.ga[m] = *reinterpret_cast<const float4_t *>(ck + (int64_t)(vb + r) * DK + c);
+                B.gb[m] = *reinterpret_cast<const float4_t *>(dsn + (int64_t)(vb + r) * DK + c);
             }
         }
 #pragma unroll
@@ -945,15 +978,15 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(int H, int DV, int T, int
             const bool in = r < len;
             const int64_t tv = ((int64_t)(tok0 + r) * H + h) * DV + vb + c;
             const int64_t wv = (int64_t)r * DV + vb + c;
-            go[m] = in ? d_o[tv] : 0.f;
-            gdy[m] = in ? dv[tv] : 0.f;
-            gyv[m] = gy[wv];
-            gvp2[m] = gvp[wv];
-            gdvp2[m] = gdvp[wv];
+            B.go[m] = in ? d_o[tv] : 0.f;
+            B.gdy[m] = in ? dv[tv] : 0.f;
+            B.gyv[m] = gy[wv];
+            B.gvp[m] = gvp[wv];
+            B.gdvp[m] = gdvp[wv];
         }
     };
-    load_block(0);
-    for (int vb0 = 0; vb0 < DV; vb0 += 16) {
+    // Block vb0 from B (then B takes block vb0 + 32): stage, compute.
+    auto value_block = [&](VBlock &B, int vb0) {
         __syncthreads();   // the previous blocks are no longer read
 #pragma unroll
         for (int m = 0; m < NS; ++m) {
@@ -962,22 +995,23 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(int H, int DV, int T, int
                 const int r = tid % 16, c = 4 * cg;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    ss[(c + i) * BP + r] = ga[m][i];
-                    sds[(c + i) * BP + r] = gb[m][i];
+                    ss[(c + i) * BP + r] = B.ga[m][i];
+                    sds[(c + i) * BP + r] = B.gb[m][i];
                 }
-                pgl += ga[m][0] * gb[m][0] + ga[m][1] * gb[m][1] + ga[m][2] * gb[m][2] + ga[m][3] * gb[m][3];
+                pgl += B.ga[m][0] * B.gb[m][0] + B.ga[m][1] * B.gb[m][1] + B.ga[m][2] * B.gb[m][2] +
+                       B.ga[m][3] * B.gb[m][3];
             }
         }
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
             const int e = tid + 512 * m, r = e / 16, c = e % 16;
-            so[r * BP + c] = go[m];
-            sdy[r * BP + c] = gdy[m];
-            sy[r * BP + c] = gyv[m];
-            svp[r * BP + c] = gvp2[m];
-            sdvp[r * BP + c] = gdvp2[m];
+            so[r * BP + c] = B.go[m];
+            sdy[r * BP + c] = B.gdy[m];
+            sy[r * BP + c] = B.gyv[m];
+            svp[r * BP + c] = B.gvp[m];
+            sdvp[r * BP + c] = B.gdvp[m];
         }
-        if (vb0 + 16 < DV) load_block(vb0 + 16);
+        if (vb0 + 32 < DV) load_block(B, vb0 + 32);
         __syncthreads();
         // One k-tile (the block's 16 value columns): lane (n, j) supplies columns 4j .. 4j + 3.
         const float4_t ao = *reinterpret_cast<const float4_t *>(so + (rw + nn) * BP + 4 * jj);
@@ -1003,6 +1037,13 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(int H, int DV, int T, int
                 mfma4(aw[a], avp[i], bd[i]);
             }
         }
+    };
+    VBlock B0, B1;
+    load_block(B0, 0);
+    if (16 < DV) load_block(B1, 16);
+    for (int vb0 = 0; vb0 < DV; vb0 += 32) {
+        value_block(B0, vb0);
+        if (vb0 + 16 < DV) value_block(B1, vb0 + 16);
     }
 
     // ---- decay sums: dgamma_r = q_r . U_r - k_r . Z_r,  dkappa_r = k_r . W2_r ----
@@ -1042,18 +1083,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(int H, int DV, int T, int
     for (int o = 32; o >= 1; o >>= 1) pgl += __shfl_xor(pgl, o, 64);
     if (l == 0) vgl[w] = pgl;
     __syncthreads();
-    // The wave's decay-mask tiles: (wr, c) for c = 2 ci + half <= wr.  Their
-    // (Q K^T) o Gamma and (K K^T) o Gamma, loaded ahead of use.
     float *sdt = smem + L::off_dt;   // [C][CP]
-    float pvr[2][4], gvr[2][4];
-#pragma unroll
-    for (int ci = 0; ci < 2; ++ci)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int c = 2 * ci + half, r = rw + 4 * jj + i, cc = 16 * c + nn;
-            pvr[ci][i] = c <= wr ? Pg[r * C + cc] : 0.f;
-            gvr[ci][i] = c <= wr ? Gg[r * C + cc] : 0.f;
-        }
     if (half) {
         // dT = dM diag(beta) on the lower triangle (zero above), into the
         // value-loop area; dbeta's first part, column sums of dM o T
