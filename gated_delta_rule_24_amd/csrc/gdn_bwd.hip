@@ -59,20 +59,6 @@ __device__ __forceinline__ void mfma4(float4_t &acc, float a, float b) {
     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
 }
 
-// acc += A B over the k-tiles kt0 .. kt1 - 1; fa(r, k) returns A[r][k] for the
-// lane's row r = n, fb(k, c) returns B[k][c] for the lane's column c = n.
-template <typename FA, typename FB>
-__device__ __forceinline__ void tile_mm(float4_t &acc, int kt0, int kt1, FA fa, FB fb) {
-    const int l = threadIdx.x & 63, n = l & 15, j = l >> 4;
-    for (int kt = kt0; kt < kt1; ++kt) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int k = 16 * kt + 4 * j + i;
-            mfma4(acc, fa(n, k), fb(k, n));
-        }
-    }
-}
-
 // Sum over the 16 lanes of a DPP row (lanes 16 j .. 16 j + 15); every lane
 // of the row gets the same bits.
 template <int CTRL>
@@ -826,12 +812,13 @@ __global__ __launch_bounds__(512) void bwd_rev_pass_kernel(int NH, int H, int DV
 }
 
 // ============================================================================
-// B4: per (chunk row, head), every per-token gradient of the chunk.  Four
-// waves; wave w owns rows 16 w .. 16 w + 15 of the chunk.  The value
-// dimension is walked in blocks of 16 columns: the products that sum over it
-// (dP, dM, U = dO S, Z = dY S, W2 = V' dS_next) accumulate in registers.
-// The decay sums follow from them: dO_r . (Q S^T)_r = q_r . U_r,
-// dY_r . X_r = k_r . Z_r and V'_r . (K dS_next^T)_r = k_r . W2_r.
+// B4: per (chunk row, head), every per-token gradient of the chunk.  Eight
+// waves; wave w owns rows 16 (w % 4) .. + 15 of the chunk and half w / 4 of
+// the key tiles.  The value dimension is walked in blocks of 16 columns: the
+// products that sum over it (dP, dM, U = dO S, Z = dY S, W2 = V' dS_next)
+// accumulate in registers.  The decay sums follow from them:
+// dO_r . (Q S^T)_r = q_r . U_r, dY_r . X_r = k_r . Z_r and
+// V'_r . (K dS_next^T)_r = k_r . W2_r.
 // ============================================================================
 template <int DK>
 struct GradSmem {
@@ -853,7 +840,8 @@ struct GradSmem {
     static constexpr int off_p = off_s + C * CP;          // after the loop: dP o Gamma
     static constexpr int off_w = (off_dy + C * BP > off_p + C * CP) ? off_dy + C * BP : off_p + C * CP;  // W, later dK o
     static constexpr int off_vec = off_w + C * CP;        // g, gamma, kappa, beta, dgamma, dkappa, dbeta
-    static constexpr int floats = off_vec + 7 * C + 8;   // + one <dS_next, S> part per wave
+    static constexpr int off_f = off_vec + 7 * C + 8;    // (after one <dS_next, S> part per wave)
+    static constexpr int floats = off_f + 4 * C;         // E L column sums, one row per row block
     static constexpr size_t bytes = sizeof(float) * floats;
     static_assert(off_p + C * CP <= off_w, "dT and dP o Gamma fit the value-loop area");
     static_assert(bytes <= 160 * 1024, "one block per CU: at most the 160 KiB of LDS");
@@ -887,6 +875,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(int H, int DV, int T, int
     float *vg = smem + L::off_vec, *vgam = vg + C, *vkap = vg + 2 * C, *vb = vg + 3 * C;
     float *vdgam = vg + 4 * C, *vdkap = vg + 5 * C, *vdb = vg + 6 * C;
     float *vgl = vg + 7 * C;   // per-wave parts of <dS_next, S>
+    float *vF = smem + L::off_f;   // [4][C]
     if (!cpr && meta[1] != 0) return;
     const int nrows = cpr ? urows : meta[0];
     const int item = blockIdx.x, row = item / H, h = item % H;
@@ -924,6 +913,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(int H, int DV, int T, int
     }
     if (tid < 4 * C) vg[tid] = ws_vec[it64 * kVecFloats + tid];
     if (tid < 3 * C) vdgam[tid] = 0.f;   // dgamma, dkappa and dbeta accumulate atomically
+    if (tid < 4 * C) vF[tid] = 0.f;
     __syncthreads();
 
     const int rw = 16 * wr;          // the wave's first chunk row
@@ -1114,16 +1104,34 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(int H, int DV, int T, int
             }
     }
     __syncthreads();
-    // W = T^T dT, rows of the wave, column blocks 2 half and 2 half + 1.  T is
-    // lower triangular, so k-tiles before the wave's rows add nothing.
+    // W = T^T dT, rows of the wave, column blocks 2 half and 2 half + 1 (one
+    // read of T per k-tile for both).  T is lower triangular, so k-tiles
+    // before the wave's rows add nothing.
+    {
+        const int c0 = 2 * half;
+        float4_t wt0 = zero4(), wt1 = zero4();
 #pragma unroll
-    for (int ci = 0; ci < 2; ++ci) {
-        const int c = 2 * half + ci;
-        float4_t wt = zero4();
-        tile_mm(wt, wr, 4, [&](int rr, int kk) { return st[kk * CP + rw + rr]; },
-                [&](int kk, int cc) { return sdt[kk * CP + 16 * c + cc]; });
+        for (int kt = 0; kt < 4; ++kt) {
+            if (kt < wr) continue;
+            float ta[4], b0[4], b1[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sw[(rw + 4 * jj + i) * CP + 16 * c + nn] = wt[i];
+            for (int i = 0; i < 4; ++i) {
+                const int kk = 16 * kt + 4 * jj + i;
+                ta[i] = st[kk * CP + rw + nn];
+                b0[i] = sdt[kk * CP + 16 * c0 + nn];
+                b1[i] = sdt[kk * CP + 16 * c0 + 16 + nn];
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                mfma4(wt0, ta[i], b0[i]);
+                mfma4(wt1, ta[i], b1[i]);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            sw[(rw + 4 * jj + i) * CP + 16 * c0 + nn] = wt0[i];
+            sw[(rw + 4 * jj + i) * CP + 16 * c0 + 16 + nn] = wt1[i];
+        }
     }
     __syncthreads();
     // dA = -W T^T on the wave's tiles (T^T is upper triangular: k-tiles up to
@@ -1136,8 +1144,14 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(int H, int DV, int T, int
         dkk[ci] = zero4();
         if (c > wr) continue;
         float4_t da = zero4();
-        tile_mm(da, 0, c + 1, [&](int rr, int kx) { return -sw[(rw + rr) * CP + kx]; },
-                [&](int kx, int cc) { return st[(16 * c + cc) * CP + kx]; });
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+            if (kt > c) continue;
+            const float4_t wa = *reinterpret_cast<const float4_t *>(sw + (rw + nn) * CP + 16 * kt + 4 * jj);
+            const float4_t tb = *reinterpret_cast<const float4_t *>(st + (16 * c + nn) * CP + 16 * kt + 4 * jj);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mfma4(da, -wa[i], tb[i]);
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = rw + 4 * jj + i, cc = 16 * c + nn;
@@ -1162,18 +1176,67 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(int H, int DV, int T, int
     for (int ci = 0; ci < 2; ++ci)
 #pragma unroll
         for (int i = 0; i < 4; ++i) sw[(rw + 4 * jj + i) * CP + 16 * (2 * ci + half) + nn] = dkk[ci][i];
-    __syncthreads();
-    // dQ += (dP o Gamma) K;  dK += (dP o Gamma)^T Q + (dK o + dK o^T) K.  dP o Gamma
-    // is lower triangular: k-tiles up to the wave's rows for dQ, from them on for dK.
+    // The sums of E = dGamma o Gamma that dlog alpha needs,
+    //   F_i = sum_{r >= i} sum_{c < i} E_rc = sum_{r >= i} (E L)_ri,  L_ci = [c < i],
+    // one column tile (wr, c) of E L per wave tile c = 2 ci + half <= wr (the
+    // rows r >= i of a column block c lie in row blocks >= c); L is formed in
+    // registers, E is strictly lower, so k-tiles up to c.  Each tile's masked
+    // column sums go to its own slot of vF, added in a fixed order below.
 #pragma unroll
-    for (int a = 0; a < NH; ++a) {
-        const int ka = 16 * (a0 + a);
-        tile_mm(accq[a], 0, wr + 1, [&](int rr, int kx) { return sp[(rw + rr) * CP + kx]; },
-                [&](int kx, int cc) { return sk[kx * KP + ka + cc]; });
-        tile_mm(acck[a], wr, 4, [&](int rr, int kx) { return sp[kx * CP + rw + rr]; },
-                [&](int kx, int cc) { return sq[kx * KP + ka + cc]; });
-        tile_mm(acck[a], 0, 4, [&](int rr, int kx) { return sw[(rw + rr) * CP + kx] + sw[kx * CP + rw + rr]; },
-                [&](int kx, int cc) { return sk[kx * KP + ka + cc]; });
+    for (int ci = 0; ci < 2; ++ci) {
+        const int c = 2 * ci + half;
+        if (c > wr) continue;
+        float4_t el = zero4();
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+            if (kt > c) continue;
+            const float4_t ea = *reinterpret_cast<const float4_t *>(sdt + (rw + nn) * CP + 16 * kt + 4 * jj);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mfma4(el, ea[i], 16 * kt + 4 * jj + i < 16 * c + nn ? 1.f : 0.f);
+        }
+        float cs = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cs += rw + 4 * jj + i >= 16 * c + nn ? el[i] : 0.f;
+        cs += __shfl_xor(cs, 16, 64);
+        cs += __shfl_xor(cs, 32, 64);
+        if (jj == 0) vF[wr * C + 16 * c + nn] = cs;
+    }
+    __syncthreads();
+    // dQ += (dP o Gamma) K;  dK += (dP o Gamma)^T Q + (dK o + dK o^T) K.  The
+    // row-side operands do not depend on the key tile: read once per k-tile.
+    // dP o Gamma is lower triangular: k-tiles up to the wave's rows for dQ,
+    // from them on for dK.
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+        const bool lo = kt <= wr, hi = kt >= wr;
+        const float4_t a1 = *reinterpret_cast<const float4_t *>(sp + (rw + nn) * CP + 16 * kt + 4 * jj);
+        const float4_t w1 = *reinterpret_cast<const float4_t *>(sw + (rw + nn) * CP + 16 * kt + 4 * jj);
+        float a2[4], a3[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int kx = 16 * kt + 4 * jj + i;
+            a2[i] = sp[kx * CP + rw + nn];
+            a3[i] = w1[i] + sw[kx * CP + rw + nn];
+        }
+#pragma unroll
+        for (int a = 0; a < NH; ++a) {
+            const int ka = 16 * (a0 + a);
+            float bk[4], bq[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int kx = 16 * kt + 4 * jj + i;
+                bk[i] = sk[kx * KP + ka + nn];
+                bq[i] = sq[kx * KP + ka + nn];
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mfma4(acck[a], a3[i], bk[i]);
+            if (lo)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) mfma4(accq[a], a1[i], bk[i]);
+            if (hi)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) mfma4(acck[a], a2[i], bq[i]);
+        }
     }
 #pragma unroll
     for (int a = 0; a < NH; ++a)
@@ -1188,30 +1251,26 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(int H, int DV, int T, int
         }
     // dlog alpha_i is the sum over r >= i of dg_r.  Written out term by term
     // it is sum_{r>=i} gamma_r dgamma_r + sum_{r<i} kappa_r dkappa_r
-    // + gamma_last <dS_next, S> + sum_{r>=i, c<i} E_rc: every term already
-    // carries its decay factor, so a tiny gradient (strong decay) is not the
-    // difference of large partial sums.  E's exclusive row prefix sums first.
-    if (tid < C) {
-        float *er = sdt + tid * CP;
-        float acc = 0.f;
-        for (int c = 0; c < C; ++c) {
-            const float x = er[c];
-            er[c] = acc;
-            acc += x;
-        }
-    }
-    __syncthreads();
-    if (tid < len) {
-        const int i = tid;
+    // + gamma_last <dS_next, S> + F_i: every term already carries its decay
+    // factor, so a tiny gradient (strong decay) is not the difference of large
+    // partial sums.  Wave 0, lane i: the suffix sum as a scan over the
+    // reversed lanes, the exclusive prefix as the scan shifted by one lane.
+    if (w == 0) {
+        const int i = l;
+        const float sfx_in = vdgam[C - 1 - l] * vgam[C - 1 - l];
+        const float sfx = __shfl(wave_inclusive_scan(sfx_in), C - 1 - l, 64);   // sum_{r >= i}
+        const float pin = wave_inclusive_scan(vdkap[l] * vkap[l]);
+        float pre = __shfl_up(pin, 1, 64);                                      // sum_{r < i}
+        if (l == 0) pre = 0.f;
         float gl = 0.f;
 #pragma unroll
         for (int u = 0; u < 8; ++u) gl += vgl[u];
-        float x = gl * vgam[len - 1];
-        for (int r = i; r < len; ++r) x += sdt[r * CP + i] + vdgam[r] * vgam[r];
-        for (int r = 0; r < i; ++r) x += vdkap[r] * vkap[r];
-        const int64_t th = (int64_t)(tok0 + i) * H + h;
-        dla[th] = x;
-        dbeta[th] = vdb[i];
+        const float f = ((vF[i] + vF[C + i]) + vF[2 * C + i]) + vF[3 * C + i];
+        if (i < len) {
+            const int64_t th = (int64_t)(tok0 + i) * H + h;
+            dla[th] = gl * vgam[len - 1] + sfx + pre + f;
+            dbeta[th] = vdb[i];
+        }
     }
 }
 
