@@ -882,6 +882,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(int H, int DV, int T, int
     if (row >= nrows) return;
     int tok0, len;
     row_span(row, T, cpr, row_tok, row_len, tok0, len);
+    if (len == 0) return;   // an empty sequence's row: it has no gradients
     // Eight waves: wave w owns chunk rows 16 (w % 4) .. + 15; the two halves of
     // the block (w / 4) split the key-column tiles of U, Z, W2, dQ and dK, and
     // the decay-mask steps (half 0 holds dP, half 1 holds dM).
@@ -889,33 +890,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(int H, int DV, int T, int
     const int a0 = half * NH;
     const int64_t it64 = (int64_t)item;
 
-    // ---- stage Q, K, T and the vectors ----
-    for (int idx = tid * 8; idx < C * DK; idx += 512 * 8) {
-        const int r = idx / DK, c = idx % DK;
-        float xq[8], xk[8];
-        if (r < len) {
-            const int64_t off = ((int64_t)(tok0 + r) * H + h) * DK + c;
-            load8_f32(q + off, xq);
-            load8_f32(k + off, xk);
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) xq[e] = xk[e] = 0.f;
-        }
-        *reinterpret_cast<float4_t *>(sq + r * KP + c) = float4_t{xq[0], xq[1], xq[2], xq[3]};
-        *reinterpret_cast<float4_t *>(sq + r * KP + c + 4) = float4_t{xq[4], xq[5], xq[6], xq[7]};
-        *reinterpret_cast<float4_t *>(sk + r * KP + c) = float4_t{xk[0], xk[1], xk[2], xk[3]};
-        *reinterpret_cast<float4_t *>(sk + r * KP + c + 4) = float4_t{xk[4], xk[5], xk[6], xk[7]};
-    }
     const float *Tg = ws_t + it64 * C * C, *Pg = ws_p + it64 * C * C, *Gg = ws_g + it64 * C * C;
-    for (int e = tid * 4; e < C * C; e += 512 * 4) {
-        const int r = e / C, c = e % C;
-        *reinterpret_cast<float4_t *>(st + r * CP + c) = *reinterpret_cast<const float4_t *>(Tg + e);
-    }
-    if (tid < 4 * C) vg[tid] = ws_vec[it64 * kVecFloats + tid];
-    if (tid < 3 * C) vdgam[tid] = 0.f;   // dgamma, dkappa and dbeta accumulate atomically
-    if (tid < 4 * C) vF[tid] = 0.f;
-    __syncthreads();
-
     const int rw = 16 * wr;          // the wave's first chunk row
     // Sums over the value dimension, rows of the wave, key tiles a0 + a:
     //   U = dO S,  Z = dY S,  W2 = V' dS_next;  and tiles (wr, c <= wr) of
@@ -1031,6 +1006,48 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(int H, int DV, int T, int
     VBlock B0, B1;
     load_block(B0, 0);
     if (16 < DV) load_block(B1, 16);
+    // ---- stage Q, K, T and the vectors (issued after the first value blocks'
+    // loads, so the two latencies overlap; rows past the end re-read the last
+    // row and are zeroed when staged) ----
+    constexpr int NQ = (C * DK + 4095) / 4096;
+    Raw8<in_t> qs[NQ], ks[NQ];
+#pragma unroll
+    for (int m = 0; m < NQ; ++m) {
+        const int idx = min(tid * 8 + 4096 * m, C * DK - 8), r = min(idx / DK, len - 1), c = idx % DK;
+        const int64_t off = ((int64_t)(tok0 + r) * H + h) * DK + c;
+        qs[m].load(q + off);
+        ks[m].load(k + off);
+    }
+    float4_t ts[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) ts[m] = *reinterpret_cast<const float4_t *>(Tg + tid * 4 + 2048 * m);
+    const float vv0 = ws_vec[it64 * kVecFloats + min(tid, 4 * C - 1)];
+#pragma unroll
+    for (int m = 0; m < NQ; ++m) {
+        const int idx = tid * 8 + 4096 * m, r = idx / DK, c = idx % DK;
+        if (idx < C * DK) {
+            float xq[8], xk[8];
+            qs[m].to_f32(xq);
+            ks[m].to_f32(xk);
+            if (r >= len)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) xq[e] = xk[e] = 0.f;
+            *reinterpret_cast<float4_t *>(sq + r * KP + c) = float4_t{xq[0], xq[1], xq[2], xq[3]};
+            *reinterpret_cast<float4_t *>(sq + r * KP + c + 4) = float4_t{xq[4], xq[5], xq[6], xq[7]};
+            *reinterpret_cast<float4_t *>(sk + r * KP + c) = float4_t{xk[0], xk[1], xk[2], xk[3]};
+            *reinterpret_cast<float4_t *>(sk + r * KP + c + 4) = float4_t{xk[4], xk[5], xk[6], xk[7]};
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+        const int e = tid * 4 + 2048 * m, r = e / C, c = e % C;
+        *reinterpret_cast<float4_t *>(st + r * CP + c) = ts[m];
+    }
+    if (tid < 4 * C) vg[tid] = vv0;
+    if (tid < 3 * C) vdgam[tid] = 0.f;   // dgamma, dkappa and dbeta accumulate atomically
+    if (tid < 4 * C) vF[tid] = 0.f;
+    __syncthreads();
+
     for (int vb0 = 0; vb0 < DV; vb0 += 32) {
         value_block(B0, vb0);
         if (vb0 + 16 < DV) value_block(B1, vb0 + 16);
