@@ -354,15 +354,16 @@ struct PassSmem {
     static constexpr size_t bytes_fwd = sizeof(float) * (off_v + 3 * C);
 };
 
-// LDS of the reverse pass (two 16-column tiles per block): shared K, Q rows,
-// T^T and P^T (swizzled, tswz), the decay vectors; per tile the dS rows and
-// the transposed dO, dV', dY blocks.
+// LDS of the reverse pass (two 16-column tiles per block): shared K rows,
+// (diag(gamma) Q)^T, T^T and P^T (all three swizzled, tswz), the decay
+// vectors; per tile the dS rows and the transposed dO, dV', -diag(gamma) dY
+// blocks.
 template <int DK>
 struct RevSmem {
     static constexpr int KP = DK + 4, TP = C + 4;
     static constexpr int off_k = 0;
-    static constexpr int off_q = off_k + C * KP;
-    static constexpr int off_m = off_q + C * KP;       // T^T
+    static constexpr int off_q = off_k + C * KP;       // (diag(gamma) Q)^T
+    static constexpr int off_m = off_q + DK * TP;      // T^T
     static constexpr int off_p = off_m + C * TP;       // P^T
     static constexpr int off_v = off_p + C * TP;       // gamma, kappa, beta
     static constexpr int off_t0 = off_v + 3 * C;       // per-tile blocks
@@ -588,6 +589,7 @@ struct RevStage {
     int tok0, len;
     int64_t item;
     Raw8<in_t> kr[MK], qr[MK];
+    float gq[MK];            // gamma of the row of K / Q group m
     float4_t t4[2], p4[2];   // T / P elements tid * 4 + 2048 m
     float dov[4];            // dO element tid + 512 m of the two tiles' value blocks
     float vec;
@@ -601,6 +603,7 @@ __device__ __forceinline__ void rev_load(RevStage<in_t, DK> &S, int row, int H, 
     const int tid = threadIdx.x;
     row_span(row, T, cpr, row_tok, row_len, S.tok0, S.len);
     S.item = (int64_t)row * H + h;
+    const float *Tm = ws_t + S.item * C * C, *Pm = ws_p + S.item * C * C, *vec = ws_vec + S.item * kVecFloats;
 #pragma unroll
     for (int m = 0; m < RevStage<in_t, DK>::MK; ++m) {
         const int idx = tid * 8 + 4096 * m, r = idx / DK, cc = idx % DK;
@@ -608,12 +611,13 @@ __device__ __forceinline__ void rev_load(RevStage<in_t, DK> &S, int row, int H, 
         if (idx < C * DK && r < S.len) {
             S.kr[m].load(k + off);
             S.qr[m].load(q + off);
+            S.gq[m] = vec[C + r];
         } else {
             S.kr[m].zero();
             S.qr[m].zero();
+            S.gq[m] = 0.f;
         }
     }
-    const float *Tm = ws_t + S.item * C * C, *Pm = ws_p + S.item * C * C, *vec = ws_vec + S.item * kVecFloats;
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
         S.t4[m] = *reinterpret_cast<const float4_t *>(Tm + tid * 4 + 2048 * m);
@@ -632,7 +636,7 @@ template <typename in_t, int DK>
 __device__ __forceinline__ void rev_store(const RevStage<in_t, DK> &S, float *smem) {
     using L = RevSmem<DK>;
     constexpr int KP = L::KP, TP = L::TP;
-    float *sk = smem + L::off_k, *sq = smem + L::off_q, *sm = smem + L::off_m, *sp = smem + L::off_p;
+    float *sk = smem + L::off_k, *sqt = smem + L::off_q, *sm = smem + L::off_m, *sp = smem + L::off_p;
     const int tid = threadIdx.x;
 #pragma unroll
     for (int m = 0; m < RevStage<in_t, DK>::MK; ++m) {
@@ -643,8 +647,8 @@ __device__ __forceinline__ void rev_store(const RevStage<in_t, DK> &S, float *sm
             *reinterpret_cast<float4_t *>(sk + r * KP + cc) = float4_t{x[0], x[1], x[2], x[3]};
             *reinterpret_cast<float4_t *>(sk + r * KP + cc + 4) = float4_t{x[4], x[5], x[6], x[7]};
             S.qr[m].to_f32(x);
-            *reinterpret_cast<float4_t *>(sq + r * KP + cc) = float4_t{x[0], x[1], x[2], x[3]};
-            *reinterpret_cast<float4_t *>(sq + r * KP + cc + 4) = float4_t{x[4], x[5], x[6], x[7]};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sqt[tswz(cc + e, r)] = S.gq[m] * x[e];   // (diag(gamma) Q)^T
         }
     }
 #pragma unroll
@@ -691,7 +695,7 @@ __global__ __launch_bounds__(512) void bwd_rev_pass_kernel(int NH, int H, int DV
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, nn = l & 15, jj = l >> 4;
     const int tile = w >> 2, wr = w & 3, vt = 2 * vpair + tile, v0 = 16 * vt;
     const bool active = vt < nvt;
-    const float *sk = smem + L::off_k, *sq = smem + L::off_q, *smt = smem + L::off_m, *spt = smem + L::off_p;
+    const float *sk = smem + L::off_k, *sqt = smem + L::off_q, *smt = smem + L::off_m, *spt = smem + L::off_p;
     const float *sv = smem + L::off_v;
     float *tb = smem + L::off_t0 + tile * L::TILE;
     float *ss = tb + L::t_s, *sot = tb + L::t_o, *sdvpt = tb + L::t_dvp, *sdyt = tb + L::t_dy;
@@ -774,10 +778,13 @@ __global__ __launch_bounds__(512) void bwd_rev_pass_kernel(int NH, int H, int DV
                 dy[i] *= sv[2 * C + r];
                 if (r < len) dv[((int64_t)(tok0 + r) * H + h) * DV + v0 + nn] = dy[i];
             }
-            *reinterpret_cast<float4_t *>(sdyt + nn * TP + rw + 4 * jj) = dy;
+            float4_t ndy;   // -diag(gamma) dY, the operand of the state update
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ndy[i] = -sv[rw + 4 * jj + i] * dy[i];
+            *reinterpret_cast<float4_t *>(sdyt + nn * TP + rw + 4 * jj) = ndy;
         }
         __syncthreads();
-        // dS^T <- gamma_last dS^T + Q^T diag(gamma) dO - K^T diag(gamma) dY on the wave's tiles
+        // dS^T <- gamma_last dS^T + (diag(gamma) Q)^T dO + K^T (-diag(gamma) dY) on the wave's tiles
         if (active) {
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
@@ -788,12 +795,12 @@ __global__ __launch_bounds__(512) void bwd_rev_pass_kernel(int NH, int H, int DV
                     for (int kt = 0; kt < 4; ++kt) {
                         const float4_t bo = *reinterpret_cast<const float4_t *>(sot + nn * TP + 16 * kt + 4 * jj);
                         const float4_t by = *reinterpret_cast<const float4_t *>(sdyt + nn * TP + 16 * kt + 4 * jj);
+                        const float4_t aq = *reinterpret_cast<const float4_t *>(sqt + tswz(16 * a + nn, 16 * kt + 4 * jj));
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
                             const int kx = 16 * kt + 4 * jj + i;
-                            const float g = sv[kx];
-                            mfma4(acc, sq[kx * KP + 16 * a + nn] * g, bo[i]);
-                            mfma4(acc, -sk[kx * KP + 16 * a + nn] * g, by[i]);
+                            mfma4(acc, aq[i], bo[i]);
+                            mfma4(acc, sk[kx * KP + 16 * a + nn], by[i]);
                         }
                     }
                     s[t] = acc;
