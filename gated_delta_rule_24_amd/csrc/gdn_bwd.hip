@@ -348,7 +348,7 @@ struct PassSmem {
     static constexpr int off_k = 0;
     static constexpr int off_s = off_k + C * KP;
     static constexpr int off_a = off_s + 16 * KP;      // Y^T
-    static constexpr int off_b = off_a + 16 * TP;      // V'^T
+    static constexpr int off_b = off_a + 16 * TP;      // (diag(kappa) V')^T
     static constexpr int off_m = off_b + 16 * TP;      // M = T diag(beta)
     static constexpr int off_v = off_m + C * TP;       // gamma, kappa, beta
     static constexpr size_t bytes_fwd = sizeof(float) * (off_v + 3 * C);
@@ -549,9 +549,12 @@ __global__ __launch_bounds__(256) void bwd_fwd_pass_kernel(int NH, int H, int DV
         py = y;
         pvp = vp;
         pitem = item;
-        *reinterpret_cast<float4_t *>(svpt + nn * TP + rw + 4 * jj) = vp;
+        float4_t kvp;   // diag(kappa) V', the operand of the state update
+#pragma unroll
+        for (int i = 0; i < 4; ++i) kvp[i] = sv[C + rw + 4 * jj + i] * vp[i];
+        *reinterpret_cast<float4_t *>(svpt + nn * TP + rw + 4 * jj) = kvp;
         __syncthreads();
-        // S^T <- gamma_last S^T + K^T diag(kappa) V' on the wave's tiles
+        // S^T <- gamma_last S^T + K^T (diag(kappa) V') on the wave's tiles
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             const int a = w + 4 * t;
@@ -563,7 +566,7 @@ __global__ __launch_bounds__(256) void bwd_fwd_pass_kernel(int NH, int H, int DV
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int kx = 16 * kt + 4 * jj + i;
-                        mfma4(acc, sk[kx * KP + 16 * a + nn] * sv[C + kx], b4[i]);
+                        mfma4(acc, sk[kx * KP + 16 * a + nn], b4[i]);
                     }
                 }
                 s[t] = acc;
