@@ -375,11 +375,18 @@ def main():
         n = 64 * 1024 * 1024                      # 256 MiB of fp32
         a = torch.ones(n, dtype=torch.float32, device=dev)
         b = torch.empty_like(a)
-        for _ in range(max(1, args.steps)):
-            torch.mul(a, 1.0, out=b)
+        launches = max(1, args.steps)
+        torch.mul(a, 1.0, out=b)                  # warm-up launch
         torch.cuda.synchronize()
-        print(json.dumps({"copy": {"bytes_read": 4 * n, "bytes_written": 4 * n, "launches": max(1, args.steps)}}),
-              flush=True)
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()                               # torch's current stream, the one the copies run on
+        for _ in range(launches):
+            torch.mul(a, 1.0, out=b)
+        t1.record()
+        torch.cuda.synchronize()
+        us = t0.elapsed_time(t1) * 1e3 / launches
+        print(json.dumps({"copy": {"bytes_read": 4 * n, "bytes_written": 4 * n, "launches": launches + 1,
+                                   "avg_us": us, "GB/s": 8 * n / us / 1e3}}), flush=True)
         return
     pre, inp = run_prefill(args, gdn, W, dev)
     if args.only == "prefill":

@@ -341,16 +341,60 @@ __global__ __launch_bounds__(64) void bwd_prep_kernel(int H, int T, int cpr, int
 // while a lane's four consecutive r of one row stay one 16-byte read.
 __device__ __forceinline__ int tswz(int x, int r) { return x * (C + 4) + (r ^ (4 * ((x >> 2) & 15))); }
 
-template <int DK>
+// bf16 form of the state-pass products for bf16 inputs.  K's values are bf16,
+// and an fp32 value is the exact sum of three bf16 values: its upper 8
+// significant bits, the next 8 (the remainder after the first cut is exact in
+// fp32) and the last 8.  A product with K then takes three bf16 matrix-core
+// instructions (products exact, sums fp32) for each 32-wide k slice instead of
+// eight fp32 ones, at the precision of the fp32 product.
+template <typename T>
+struct SplitState {
+    static constexpr bool value = false;
+};
+template <>
+struct SplitState<bf16_t> {
+    static constexpr bool value = true;
+};
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+// acc += A B over one 32-wide k slice: lane (n, j) supplies A[n][8j .. 8j + 7]
+// and B[8j .. 8j + 7][n] as four packed bf16 pairs each.
+__device__ __forceinline__ void mfma_bf16(float4_t &acc, const uint4 &a, const uint4 &b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), acc,
+                                                 0, 0, 0);
+}
+// The upper halves of two fp32 words as one bf16 pair, x0 first (exact when
+// both values are bf16 values).
+__device__ __forceinline__ uint32_t pack_bf16(float x0, float x1) {
+    return __builtin_amdgcn_perm(__float_as_uint(x1), __float_as_uint(x0), 0x07060302u);
+}
+// x = hi + mid + lo exactly, each a bf16 value, as packed pairs.
+__device__ __forceinline__ void split3(const float4_t &x, uint2 &hi, uint2 &mid, uint2 &lo) {
+    float h[4], m[4], r[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        h[e] = __uint_as_float(__float_as_uint(x[e]) & 0xffff0000u);
+        const float r1 = x[e] - h[e];
+        m[e] = __uint_as_float(__float_as_uint(r1) & 0xffff0000u);
+        r[e] = r1 - m[e];
+    }
+    hi = uint2{pack_bf16(h[0], h[1]), pack_bf16(h[2], h[3])};
+    mid = uint2{pack_bf16(m[0], m[1]), pack_bf16(m[2], m[3])};
+    lo = uint2{pack_bf16(r[0], r[1]), pack_bf16(r[2], r[3])};
+}
+
+template <int DK, bool SPL>
 struct PassSmem {
     static constexpr int KP = DK + 4;   // rows of K; rows of the state tile (S, 16 x DK)
     static constexpr int TP = C + 4;    // transposed value blocks [16][C]; C x C matrices
+    static constexpr int SBP = DK + 8;  // split form: bf16 rows of the three state terms
+    static constexpr int VBP = C + 8;   // split form: bf16 rows of the three (diag(kappa) V')^T terms
     static constexpr int off_k = 0;
-    static constexpr int off_s = off_k + C * KP;
-    static constexpr int off_a = off_s + 16 * KP;      // Y^T
-    static constexpr int off_b = off_a + 16 * TP;      // (diag(kappa) V')^T
-    static constexpr int off_m = off_b + 16 * TP;      // M = T diag(beta)
-    static constexpr int off_v = off_m + C * TP;       // gamma, kappa, beta
+    static constexpr int off_s = off_k + C * KP;                          // S rows (or their three bf16 terms)
+    static constexpr int off_a = off_s + (SPL ? 3 * 16 * SBP / 2 : 16 * KP);  // Y^T
+    static constexpr int off_b = off_a + 16 * TP;                         // (diag(kappa) V')^T (or its terms)
+    static constexpr int off_m = off_b + (SPL ? 3 * 16 * VBP / 2 : 16 * TP);  // M = T diag(beta)
+    static constexpr int off_v = off_m + C * TP;                          // gamma, kappa, beta
     static constexpr size_t bytes_fwd = sizeof(float) * (off_v + 3 * C);
 };
 
@@ -418,7 +462,7 @@ __device__ __forceinline__ void pass_load(PassStage<in_t, DK> &S, int row, int H
 // gamma, kappa, beta.
 template <typename in_t, int DK>
 __device__ __forceinline__ void pass_store(const PassStage<in_t, DK> &S, float *smem) {
-    using L = PassSmem<DK>;
+    using L = PassSmem<DK, SplitState<in_t>::value>;
     constexpr int KP = L::KP, TP = L::TP;
     float *sk = smem + L::off_k, *sm = smem + L::off_m, *sv = smem + L::off_v;
     const int tid = threadIdx.x;
@@ -454,11 +498,13 @@ __global__ __launch_bounds__(256) void bwd_fwd_pass_kernel(int NH, int H, int DV
                                                            const float *__restrict__ init_state,
                                                            float *__restrict__ ws_ck, float *__restrict__ ws_y,
                                                            float *__restrict__ ws_vp) {
-    using L = PassSmem<DK>;
-    constexpr int KP = L::KP, TP = L::TP, NA = DK / 16, NT = (NA + 3) / 4;
+    constexpr bool SPL = SplitState<in_t>::value;
+    using L = PassSmem<DK, SPL>;
+    constexpr int KP = L::KP, TP = L::TP, SBP = L::SBP, VBP = L::VBP, NA = DK / 16, NT = (NA + 3) / 4;
     extern __shared__ __align__(16) float smem[];
     float *sk = smem + L::off_k, *ss = smem + L::off_s, *syt = smem + L::off_a, *svpt = smem + L::off_b;
     float *sm = smem + L::off_m, *sv = smem + L::off_v;   // sv: gamma [C], kappa [C], beta [C]
+    uint16_t *ssb = reinterpret_cast<uint16_t *>(ss), *svb = reinterpret_cast<uint16_t *>(svpt);   // split form
     if (!cpr && meta[1] != 0) return;
     // The value tiles of one (sequence, head) read the same K and T.  Blocks
     // are dealt to the 8 XCDs in turn, so give a head's tiles block indices
@@ -511,7 +557,16 @@ __global__ __launch_bounds__(256) void bwd_fwd_pass_kernel(int NH, int H, int DV
         for (int t = 0; t < NT; ++t) {
             const int a = w + 4 * t;
             if (a < NA) {
-                *reinterpret_cast<float4_t *>(ss + nn * KP + 16 * a + 4 * jj) = s[t];   // row v0 + n of S
+                if constexpr (SPL) {   // row v0 + n of S as three bf16 terms
+                    uint2 hi, mid, lo;
+                    split3(s[t], hi, mid, lo);
+                    const int o = nn * SBP + 16 * a + 4 * jj;
+                    *reinterpret_cast<uint2 *>(ssb + o) = hi;
+                    *reinterpret_cast<uint2 *>(ssb + 16 * SBP + o) = mid;
+                    *reinterpret_cast<uint2 *>(ssb + 32 * SBP + o) = lo;
+                } else {
+                    *reinterpret_cast<float4_t *>(ss + nn * KP + 16 * a + 4 * jj) = s[t];   // row v0 + n of S
+                }
                 *reinterpret_cast<float4_t *>(ws_ck + (item * DV + v0 + nn) * DK + 16 * a + 4 * jj) = s[t];
             }
         }
@@ -523,12 +578,25 @@ __global__ __launch_bounds__(256) void bwd_fwd_pass_kernel(int NH, int H, int DV
         const float glast = len > 0 ? sv[len - 1] : 1.f;
         // rows of the wave: X = K S^T, Y = V - diag(gamma) X
         float4_t x = zero4();
+        if constexpr (SPL) {
 #pragma unroll
-        for (int kt = 0; kt < NA; ++kt) {
-            const float4_t a4 = *reinterpret_cast<const float4_t *>(sk + (rw + nn) * KP + 16 * kt + 4 * jj);
-            const float4_t b4 = *reinterpret_cast<const float4_t *>(ss + nn * KP + 16 * kt + 4 * jj);
+            for (int ks = 0; ks < DK / 32; ++ks) {
+                const float4_t k0 = *reinterpret_cast<const float4_t *>(sk + (rw + nn) * KP + 32 * ks + 8 * jj);
+                const float4_t k1 = *reinterpret_cast<const float4_t *>(sk + (rw + nn) * KP + 32 * ks + 8 * jj + 4);
+                const uint4 ka = uint4{pack_bf16(k0[0], k0[1]), pack_bf16(k0[2], k0[3]), pack_bf16(k1[0], k1[1]),
+                                       pack_bf16(k1[2], k1[3])};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) mfma4(x, a4[i], b4[i]);
+                for (int term = 0; term < 3; ++term)
+                    mfma_bf16(x, ka, *reinterpret_cast<const uint4 *>(ssb + (16 * term + nn) * SBP + 32 * ks + 8 * jj));
+            }
+        } else {
+#pragma unroll
+            for (int kt = 0; kt < NA; ++kt) {
+                const float4_t a4 = *reinterpret_cast<const float4_t *>(sk + (rw + nn) * KP + 16 * kt + 4 * jj);
+                const float4_t b4 = *reinterpret_cast<const float4_t *>(ss + nn * KP + 16 * kt + 4 * jj);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) mfma4(x, a4[i], b4[i]);
+            }
         }
         float4_t y;
 #pragma unroll
@@ -552,7 +620,16 @@ __global__ __launch_bounds__(256) void bwd_fwd_pass_kernel(int NH, int H, int DV
         float4_t kvp;   // diag(kappa) V', the operand of the state update
 #pragma unroll
         for (int i = 0; i < 4; ++i) kvp[i] = sv[C + rw + 4 * jj + i] * vp[i];
-        *reinterpret_cast<float4_t *>(svpt + nn * TP + rw + 4 * jj) = kvp;
+        if constexpr (SPL) {
+            uint2 hi, mid, lo;
+            split3(kvp, hi, mid, lo);
+            const int o = nn * VBP + rw + 4 * jj;
+            *reinterpret_cast<uint2 *>(svb + o) = hi;
+            *reinterpret_cast<uint2 *>(svb + 16 * VBP + o) = mid;
+            *reinterpret_cast<uint2 *>(svb + 32 * VBP + o) = lo;
+        } else {
+            *reinterpret_cast<float4_t *>(svpt + nn * TP + rw + 4 * jj) = kvp;
+        }
         __syncthreads();
         // S^T <- gamma_last S^T + K^T (diag(kappa) V') on the wave's tiles
 #pragma unroll
@@ -560,13 +637,28 @@ __global__ __launch_bounds__(256) void bwd_fwd_pass_kernel(int NH, int H, int DV
             const int a = w + 4 * t;
             if (a < NA) {
                 float4_t acc = glast * s[t];
+                if constexpr (SPL) {
 #pragma unroll
-                for (int kt = 0; kt < 4; ++kt) {
-                    const float4_t b4 = *reinterpret_cast<const float4_t *>(svpt + nn * TP + 16 * kt + 4 * jj);
+                    for (int ks = 0; ks < C / 32; ++ks) {
+                        float kc[8];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int kx = 16 * kt + 4 * jj + i;
-                        mfma4(acc, sk[kx * KP + 16 * a + nn], b4[i]);
+                        for (int e = 0; e < 8; ++e) kc[e] = sk[(32 * ks + 8 * jj + e) * KP + 16 * a + nn];
+                        const uint4 ka = uint4{pack_bf16(kc[0], kc[1]), pack_bf16(kc[2], kc[3]), pack_bf16(kc[4], kc[5]),
+                                               pack_bf16(kc[6], kc[7])};
+#pragma unroll
+                        for (int term = 0; term < 3; ++term)
+                            mfma_bf16(acc, ka,
+                                      *reinterpret_cast<const uint4 *>(svb + (16 * term + nn) * VBP + 32 * ks + 8 * jj));
+                    }
+                } else {
+#pragma unroll
+                    for (int kt = 0; kt < 4; ++kt) {
+                        const float4_t b4 = *reinterpret_cast<const float4_t *>(svpt + nn * TP + 16 * kt + 4 * jj);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int kx = 16 * kt + 4 * jj + i;
+                            mfma4(acc, sk[kx * KP + 16 * a + nn], b4[i]);
+                        }
                     }
                 }
                 s[t] = acc;
@@ -1347,7 +1439,7 @@ hipError_t launch_bwd_dk(const ChunkArgs &a, const BwdArgs &g, const BwdWorkspac
     }
     if (chains > 0) {
         {
-            const size_t sb = PassSmem<DK>::bytes_fwd;
+            const size_t sb = PassSmem<DK, SplitState<in_t>::value>::bytes_fwd;
             auto kern = bwd_fwd_pass_kernel<in_t, DK>;
             if ((e = bwd_allow_smem(kern, sb)) != hipSuccess) return e;
             ProfScope prof("gdn_bwd_fwd_pass", st);
