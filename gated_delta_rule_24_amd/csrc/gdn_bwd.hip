@@ -402,19 +402,28 @@ struct PassSmem {
 // (diag(gamma) Q)^T, T^T and P^T (all three swizzled, tswz), the decay
 // vectors; per tile the dS rows and the transposed dO, dV', -diag(gamma) dY
 // blocks.
-template <int DK>
+// In the split form (bf16 inputs, see SplitState) K and Q are bf16 rows, and
+// the dS rows, -diag(gamma) dY and an extra (diag(gamma) dO)^T hold three bf16
+// terms each.
+template <int DK, bool SPL>
 struct RevSmem {
     static constexpr int KP = DK + 4, TP = C + 4;
-    static constexpr int off_k = 0;
-    static constexpr int off_q = off_k + C * KP;       // (diag(gamma) Q)^T
-    static constexpr int off_m = off_q + DK * TP;      // T^T
+    static constexpr int KB = DK + 8;   // split form: bf16 rows of K, Q and of the dS terms
+    static constexpr int VB = C + 8;    // split form: bf16 rows of the transposed value-side terms
+    static constexpr int off_k = 0;                                       // K rows
+    static constexpr int off_q = off_k + (SPL ? C * KB / 2 : C * KP);    // Q rows, or (diag(gamma) Q)^T
+    static constexpr int off_m = off_q + (SPL ? C * KB / 2 : DK * TP);   // T^T
     static constexpr int off_p = off_m + C * TP;       // P^T
     static constexpr int off_v = off_p + C * TP;       // gamma, kappa, beta
-    static constexpr int off_t0 = off_v + 3 * C;       // per-tile blocks
-    static constexpr int TILE = 16 * KP + 3 * 16 * TP; //   dS rows, dO^T, dV'^T, dY^T
-    static constexpr int t_s = 0, t_o = 16 * KP, t_dvp = t_o + 16 * TP, t_dy = t_dvp + 16 * TP;
+    static constexpr int off_t0 = off_v + 3 * C;       // per-tile blocks:
+    static constexpr int S_FL = SPL ? 3 * 16 * KB / 2 : 16 * KP;   //   dS rows
+    static constexpr int Y_FL = SPL ? 3 * 16 * VB / 2 : 16 * TP;   //   (-diag(gamma) dY)^T
+    static constexpr int G_FL = SPL ? 3 * 16 * VB / 2 : 0;         //   (diag(gamma) dO)^T
+    static constexpr int t_s = 0, t_o = S_FL, t_dvp = t_o + 16 * TP, t_dy = t_dvp + 16 * TP, t_og = t_dy + Y_FL;
+    static constexpr int TILE = t_og + G_FL;           //   (with dO^T and dV'^T)
     static constexpr size_t bytes = sizeof(float) * (off_t0 + 2 * TILE);
     static_assert(bytes <= 160 * 1024, "reverse pass fits the 160 KiB of LDS");
+    static_assert(off_t0 % 4 == 0 && TILE % 4 == 0, "16-byte aligned blocks");
 };
 
 // One chunk's operands of the forward pass, loaded into registers while the
@@ -685,6 +694,7 @@ struct RevStage {
     int64_t item;
     Raw8<in_t> kr[MK], qr[MK];
     float gq[MK];            // gamma of the row of K / Q group m
+    float gdo[4];            // gamma of the row of dO element m
     float4_t t4[2], p4[2];   // T / P elements tid * 4 + 2048 m
     float dov[4];            // dO element tid + 512 m of the two tiles' value blocks
     float vec;
@@ -724,19 +734,24 @@ __device__ __forceinline__ void rev_load(RevStage<in_t, DK> &S, int row, int H, 
         const int e = tid + 512 * m, tile = e / 1024, r = (e % 1024) / 16, cc = e % 16;
         const int vt = 2 * vpair + tile;
         S.dov[m] = (vt < nvt && r < S.len) ? d_o[((int64_t)(S.tok0 + r) * H + h) * DV + 16 * vt + cc] : 0.f;
+        if constexpr (SplitState<in_t>::value) S.gdo[m] = r < S.len ? vec[C + r] : 0.f;
     }
 }
 
 template <typename in_t, int DK>
 __device__ __forceinline__ void rev_store(const RevStage<in_t, DK> &S, float *smem) {
-    using L = RevSmem<DK>;
-    constexpr int KP = L::KP, TP = L::TP;
+    constexpr bool SPL = SplitState<in_t>::value;
+    using L = RevSmem<DK, SPL>;
+    constexpr int KP = L::KP, TP = L::TP, KB = L::KB, VB = L::VB;
     float *sk = smem + L::off_k, *sqt = smem + L::off_q, *sm = smem + L::off_m, *sp = smem + L::off_p;
     const int tid = threadIdx.x;
 #pragma unroll
     for (int m = 0; m < RevStage<in_t, DK>::MK; ++m) {
         const int idx = tid * 8 + 4096 * m, r = idx / DK, cc = idx % DK;
-        if (idx < C * DK) {
+        if (SPL && idx < C * DK) {   // K and Q rows as they are (bf16)
+            S.kr[m].store_lds(reinterpret_cast<in_t *>(sk) + r * KB + cc);
+            S.qr[m].store_lds(reinterpret_cast<in_t *>(sqt) + r * KB + cc);
+        } else if (idx < C * DK) {
             float x[8];
             S.kr[m].to_f32(x);
             *reinterpret_cast<float4_t *>(sk + r * KP + cc) = float4_t{x[0], x[1], x[2], x[3]};
@@ -760,6 +775,15 @@ __device__ __forceinline__ void rev_store(const RevStage<in_t, DK> &S, float *sm
     for (int m = 0; m < 4; ++m) {
         const int e = tid + 512 * m, tile = e / 1024, r = (e % 1024) / 16, cc = e % 16;
         smem[L::off_t0 + tile * L::TILE + L::t_o + cc * TP + r] = S.dov[m];
+        if constexpr (SPL) {   // (diag(gamma) dO)^T as three bf16 terms
+            uint16_t *og = reinterpret_cast<uint16_t *>(smem + L::off_t0 + tile * L::TILE + L::t_og) + cc * VB + r;
+            const float g = S.gdo[m] * S.dov[m];
+            const float hi = __uint_as_float(__float_as_uint(g) & 0xffff0000u), r1 = g - hi;
+            const float mid = __uint_as_float(__float_as_uint(r1) & 0xffff0000u), lo = r1 - mid;
+            og[0] = (uint16_t)(__float_as_uint(hi) >> 16);
+            og[16 * VB] = (uint16_t)(__float_as_uint(mid) >> 16);
+            og[32 * VB] = (uint16_t)(__float_as_uint(lo) >> 16);
+        }
     }
 }
 
@@ -778,8 +802,9 @@ __global__ __launch_bounds__(512) void bwd_rev_pass_kernel(int NH, int H, int DV
                                                            const float *__restrict__ d_final,
                                                            float *__restrict__ ws_ds, float *__restrict__ ws_dvp,
                                                            float *__restrict__ dv, float *__restrict__ d_init) {
-    using L = RevSmem<DK>;
-    constexpr int KP = L::KP, TP = L::TP, NA = DK / 16, NT = (NA + 3) / 4;
+    constexpr bool SPL = SplitState<in_t>::value;
+    using L = RevSmem<DK, SPL>;
+    constexpr int KP = L::KP, TP = L::TP, KB = L::KB, VB = L::VB, NA = DK / 16, NT = (NA + 3) / 4;
     extern __shared__ __align__(16) float smem[];
     if (!cpr && meta[1] != 0) return;
     const int npair = (nvt + 1) / 2;
@@ -794,6 +819,10 @@ __global__ __launch_bounds__(512) void bwd_rev_pass_kernel(int NH, int H, int DV
     const float *sv = smem + L::off_v;
     float *tb = smem + L::off_t0 + tile * L::TILE;
     float *ss = tb + L::t_s, *sot = tb + L::t_o, *sdvpt = tb + L::t_dvp, *sdyt = tb + L::t_dy;
+    // split form: bf16 K and Q rows, the terms of dS, of -diag(gamma) dY and of diag(gamma) dO
+    const uint16_t *skb = reinterpret_cast<const uint16_t *>(sk), *sqb = reinterpret_cast<const uint16_t *>(sqt);
+    uint16_t *ssb = reinterpret_cast<uint16_t *>(ss), *syb = reinterpret_cast<uint16_t *>(sdyt);
+    const uint16_t *sgb = reinterpret_cast<const uint16_t *>(tb + L::t_og);
     int r0, nrows;
     seq_rows(n, T, cpr, cu_ws, row0, r0, nrows);
 
@@ -819,7 +848,16 @@ __global__ __launch_bounds__(512) void bwd_rev_pass_kernel(int NH, int H, int DV
                 const int a = wr + 4 * t;
                 if (a < NA) {
                     *reinterpret_cast<float4_t *>(ws_ds + (item * DV + v0 + nn) * DK + 16 * a + 4 * jj) = s[t];
-                    *reinterpret_cast<float4_t *>(ss + nn * KP + 16 * a + 4 * jj) = s[t];   // row v0 + n of dS
+                    if constexpr (SPL) {   // row v0 + n of dS as three bf16 terms
+                        uint2 hi, mid, lo;
+                        split3(s[t], hi, mid, lo);
+                        const int o = nn * KB + 16 * a + 4 * jj;
+                        *reinterpret_cast<uint2 *>(ssb + o) = hi;
+                        *reinterpret_cast<uint2 *>(ssb + 16 * KB + o) = mid;
+                        *reinterpret_cast<uint2 *>(ssb + 32 * KB + o) = lo;
+                    } else {
+                        *reinterpret_cast<float4_t *>(ss + nn * KP + 16 * a + 4 * jj) = s[t];   // row v0 + n of dS
+                    }
                 }
             }
         }
@@ -831,12 +869,22 @@ __global__ __launch_bounds__(512) void bwd_rev_pass_kernel(int NH, int H, int DV
         // dV' = P^T dO + diag(kappa) K dS^T on the wave's rows
         if (active) {
             float4_t x = zero4();
+            if constexpr (SPL) {
 #pragma unroll
-            for (int kt = 0; kt < NA; ++kt) {
-                const float4_t a4 = *reinterpret_cast<const float4_t *>(sk + (rw + nn) * KP + 16 * kt + 4 * jj);
-                const float4_t b4 = *reinterpret_cast<const float4_t *>(ss + nn * KP + 16 * kt + 4 * jj);
+                for (int ks = 0; ks < DK / 32; ++ks) {
+                    const uint4 ka = *reinterpret_cast<const uint4 *>(skb + (rw + nn) * KB + 32 * ks + 8 * jj);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) mfma4(x, a4[i], b4[i]);
+                    for (int term = 0; term < 3; ++term)
+                        mfma_bf16(x, ka, *reinterpret_cast<const uint4 *>(ssb + (16 * term + nn) * KB + 32 * ks + 8 * jj));
+                }
+            } else {
+#pragma unroll
+                for (int kt = 0; kt < NA; ++kt) {
+                    const float4_t a4 = *reinterpret_cast<const float4_t *>(sk + (rw + nn) * KP + 16 * kt + 4 * jj);
+                    const float4_t b4 = *reinterpret_cast<const float4_t *>(ss + nn * KP + 16 * kt + 4 * jj);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) mfma4(x, a4[i], b4[i]);
+                }
             }
             float4_t dvp;
 #pragma unroll
@@ -876,7 +924,16 @@ __global__ __launch_bounds__(512) void bwd_rev_pass_kernel(int NH, int H, int DV
             float4_t ndy;   // -diag(gamma) dY, the operand of the state update
 #pragma unroll
             for (int i = 0; i < 4; ++i) ndy[i] = -sv[rw + 4 * jj + i] * dy[i];
-            *reinterpret_cast<float4_t *>(sdyt + nn * TP + rw + 4 * jj) = ndy;
+            if constexpr (SPL) {
+                uint2 hi, mid, lo;
+                split3(ndy, hi, mid, lo);
+                const int o = nn * VB + rw + 4 * jj;
+                *reinterpret_cast<uint2 *>(syb + o) = hi;
+                *reinterpret_cast<uint2 *>(syb + 16 * VB + o) = mid;
+                *reinterpret_cast<uint2 *>(syb + 32 * VB + o) = lo;
+            } else {
+                *reinterpret_cast<float4_t *>(sdyt + nn * TP + rw + 4 * jj) = ndy;
+            }
         }
         __syncthreads();
         // dS^T <- gamma_last dS^T + (diag(gamma) Q)^T dO + K^T (-diag(gamma) dY) on the wave's tiles
@@ -886,16 +943,36 @@ __global__ __launch_bounds__(512) void bwd_rev_pass_kernel(int NH, int H, int DV
                 const int a = wr + 4 * t;
                 if (a < NA) {
                     float4_t acc = glast * s[t];
+                    if constexpr (SPL) {   // Q^T (diag(gamma) dO) + K^T (-diag(gamma) dY)
 #pragma unroll
-                    for (int kt = 0; kt < 4; ++kt) {
-                        const float4_t bo = *reinterpret_cast<const float4_t *>(sot + nn * TP + 16 * kt + 4 * jj);
-                        const float4_t by = *reinterpret_cast<const float4_t *>(sdyt + nn * TP + 16 * kt + 4 * jj);
-                        const float4_t aq = *reinterpret_cast<const float4_t *>(sqt + tswz(16 * a + nn, 16 * kt + 4 * jj));
+                        for (int ks = 0; ks < C / 32; ++ks) {
+                            uint4 qa, ka;
+                            uint32_t *qw = reinterpret_cast<uint32_t *>(&qa), *kw = reinterpret_cast<uint32_t *>(&ka);
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const int kx = 16 * kt + 4 * jj + i;
-                            mfma4(acc, aq[i], bo[i]);
-                            mfma4(acc, sk[kx * KP + 16 * a + nn], by[i]);
+                            for (int e = 0; e < 4; ++e) {
+                                const int r2 = 32 * ks + 8 * jj + 2 * e;
+                                qw[e] = (uint32_t)sqb[r2 * KB + 16 * a + nn] | ((uint32_t)sqb[(r2 + 1) * KB + 16 * a + nn] << 16);
+                                kw[e] = (uint32_t)skb[r2 * KB + 16 * a + nn] | ((uint32_t)skb[(r2 + 1) * KB + 16 * a + nn] << 16);
+                            }
+#pragma unroll
+                            for (int term = 0; term < 3; ++term) {
+                                const int o = (16 * term + nn) * VB + 32 * ks + 8 * jj;
+                                mfma_bf16(acc, qa, *reinterpret_cast<const uint4 *>(sgb + o));
+                                mfma_bf16(acc, ka, *reinterpret_cast<const uint4 *>(syb + o));
+                            }
+                        }
+                    } else {
+#pragma unroll
+                        for (int kt = 0; kt < 4; ++kt) {
+                            const float4_t bo = *reinterpret_cast<const float4_t *>(sot + nn * TP + 16 * kt + 4 * jj);
+                            const float4_t by = *reinterpret_cast<const float4_t *>(sdyt + nn * TP + 16 * kt + 4 * jj);
+                            const float4_t aq = *reinterpret_cast<const float4_t *>(sqt + tswz(16 * a + nn, 16 * kt + 4 * jj));
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                const int kx = 16 * kt + 4 * jj + i;
+                                mfma4(acc, aq[i], bo[i]);
+                                mfma4(acc, sk[kx * KP + 16 * a + nn], by[i]);
+                            }
                         }
                     }
                     s[t] = acc;
@@ -1449,7 +1526,7 @@ hipError_t launch_bwd_dk(const ChunkArgs &a, const BwdArgs &g, const BwdWorkspac
             if ((e = hipGetLastError()) != hipSuccess) return e;
         }
         {
-            const size_t sb = RevSmem<DK>::bytes;
+            const size_t sb = RevSmem<DK, SplitState<in_t>::value>::bytes;
             auto kern = bwd_rev_pass_kernel<in_t, DK>;
             if ((e = bwd_allow_smem(kern, sb)) != hipSuccess) return e;
             ProfScope prof("gdn_bwd_rev_pass", st);

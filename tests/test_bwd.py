@@ -78,15 +78,17 @@ def test_bwd_packed():
     _check(inp, d_o, d_final, "packed [5,0,64,1,130,63,65]")
 
 
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 @pytest.mark.parametrize("gate", ["-60", "0", "beta2"])
-def test_bwd_gates(gate):
-    inp = W.chunk_inputs(1, 150, 2, 64, 64, "fp32", seed=64, init_std=0.1)
+def test_bwd_gates(gate, dtype):
+    """Gate extremes; bf16 inputs take the kernels' split-bf16 products."""
+    inp = W.chunk_inputs(1, 150, 2, 64, 64, dtype, seed=64, init_std=0.1)
     if gate == "beta2":
         inp.beta[:] = np.random.default_rng(64).uniform(0.0, 2.0, size=inp.beta.shape).astype(np.float32)
     else:
         inp.log_alpha[:] = float(gate)
     d_o, d_final = W.incoming_grads(inp, seed=65)
-    _check(inp, d_o, d_final, f"gates {gate}")
+    _check(inp, d_o, d_final, f"gates {gate} {dtype}")
 
 
 def test_bwd_prefill_shape_sampled():
