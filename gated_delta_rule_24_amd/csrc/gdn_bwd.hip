@@ -1402,36 +1402,85 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(int H, int DV, int T, int
     // row-side operands do not depend on the key tile: read once per k-tile.
     // dP o Gamma is lower triangular: k-tiles up to the wave's rows for dQ,
     // from them on for dK.
+    if constexpr (SplitState<in_t>::value) {
+        // bf16 inputs: K and Q are bf16 values, so each product takes the row-side
+        // operand as three exact bf16 terms, per 32-wide k slice.
+        auto split8 = [](const float (&x)[8], uint4 (&t)[3]) {
+            uint2 h0, m0, l0, h1, m1, l1;
+            split3(float4_t{x[0], x[1], x[2], x[3]}, h0, m0, l0);
+            split3(float4_t{x[4], x[5], x[6], x[7]}, h1, m1, l1);
+            t[0] = uint4{h0.x, h0.y, h1.x, h1.y};
+            t[1] = uint4{m0.x, m0.y, m1.x, m1.y};
+            t[2] = uint4{l0.x, l0.y, l1.x, l1.y};
+        };
+        // Every slice takes all three products: where a slice lies wholly above
+        // (dQ) or below (dK) the wave's rows, dP o Gamma is zero there and adds
+        // nothing.
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-        const bool lo = kt <= wr, hi = kt >= wr;
-        const float4_t a1 = *reinterpret_cast<const float4_t *>(sp + (rw + nn) * CP + 16 * kt + 4 * jj);
-        const float4_t w1 = *reinterpret_cast<const float4_t *>(sw + (rw + nn) * CP + 16 * kt + 4 * jj);
-        float a2[4], a3[4];
+        for (int ks = 0; ks < C / 32; ++ks) {
+            float x1[8], x2[8], x3[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int kx = 16 * kt + 4 * jj + i;
-            a2[i] = sp[kx * CP + rw + nn];
-            a3[i] = w1[i] + sw[kx * CP + rw + nn];
+            for (int e = 0; e < 8; ++e) {
+                const int kx = 32 * ks + 8 * jj + e;
+                x1[e] = sp[(rw + nn) * CP + kx];
+                x2[e] = sp[kx * CP + rw + nn];
+                x3[e] = sw[(rw + nn) * CP + kx] + sw[kx * CP + rw + nn];
+            }
+            uint4 t1[3], t2[3], t3[3];
+            split8(x1, t1);
+            split8(x2, t2);
+            split8(x3, t3);
+#pragma unroll
+            for (int a = 0; a < NH; ++a) {
+                const int ka = 16 * (a0 + a);
+                uint32_t bk[4], bq[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int kx = 32 * ks + 8 * jj + 2 * e;
+                    bk[e] = pack_bf16(sk[kx * KP + ka + nn], sk[(kx + 1) * KP + ka + nn]);
+                    bq[e] = pack_bf16(sq[kx * KP + ka + nn], sq[(kx + 1) * KP + ka + nn]);
+                }
+                const uint4 kb = uint4{bk[0], bk[1], bk[2], bk[3]}, qb = uint4{bq[0], bq[1], bq[2], bq[3]};
+#pragma unroll
+                for (int term = 0; term < 3; ++term) {
+                    mfma_bf16(acck[a], t3[term], kb);
+                    mfma_bf16(accq[a], t1[term], kb);
+                    mfma_bf16(acck[a], t2[term], qb);
+                }
+            }
         }
+    } else {
 #pragma unroll
-        for (int a = 0; a < NH; ++a) {
-            const int ka = 16 * (a0 + a);
-            float bk[4], bq[4];
+        for (int kt = 0; kt < 4; ++kt) {
+            const bool lo = kt <= wr, hi = kt >= wr;
+            const float4_t a1 = *reinterpret_cast<const float4_t *>(sp + (rw + nn) * CP + 16 * kt + 4 * jj);
+            const float4_t w1 = *reinterpret_cast<const float4_t *>(sw + (rw + nn) * CP + 16 * kt + 4 * jj);
+            float a2[4], a3[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int kx = 16 * kt + 4 * jj + i;
-                bk[i] = sk[kx * KP + ka + nn];
-                bq[i] = sq[kx * KP + ka + nn];
+                a2[i] = sp[kx * CP + rw + nn];
+                a3[i] = w1[i] + sw[kx * CP + rw + nn];
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) mfma4(acck[a], a3[i], bk[i]);
-            if (lo)
+            for (int a = 0; a < NH; ++a) {
+                const int ka = 16 * (a0 + a);
+                float bk[4], bq[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) mfma4(accq[a], a1[i], bk[i]);
-            if (hi)
+                for (int i = 0; i < 4; ++i) {
+                    const int kx = 16 * kt + 4 * jj + i;
+                    bk[i] = sk[kx * KP + ka + nn];
+                    bq[i] = sq[kx * KP + ka + nn];
+                }
 #pragma unroll
-                for (int i = 0; i < 4; ++i) mfma4(acck[a], a2[i], bq[i]);
+                for (int i = 0; i < 4; ++i) mfma4(acck[a], a3[i], bk[i]);
+                if (lo)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) mfma4(accq[a], a1[i], bk[i]);
+                if (hi)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) mfma4(acck[a], a2[i], bq[i]);
+            }
         }
     }
 #pragma unroll
