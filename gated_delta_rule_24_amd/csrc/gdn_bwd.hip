@@ -41,8 +41,12 @@
 //                           chunk from its checkpoint and state gradient.
 // B2 also stores each chunk's Y and V', B3 its dV' and dY (= dV, written to
 // the output), so B4 recomputes none of the state products.
-// All arithmetic is fp32 (products on the fp32 matrix-core instruction), so the
-// gradients carry the same precision for every input dtype.  Matrix-core
+// All arithmetic has fp32 precision, so the gradients carry the same precision
+// for every input dtype: products run on the fp32 matrix-core instruction,
+// except those with q or k as a factor, which take the 16-bit instruction when
+// that is exact (the Gram products of 16-bit q and k in B1; for bf16 inputs the
+// products of q or k with an fp32 factor split exactly into three bf16 terms,
+// see SplitState).  Matrix-core
 // tiles use the lane convention of gdn_device.h: lane l, n = l % 16,
 // j = l / 16; an accumulator holds X[4j + i][n]; on issue i of a k-tile kt
 // lane (n, j) supplies A[n][16 kt + 4j + i] and B[16 kt + 4j + i][n].
