@@ -1003,30 +1003,34 @@ __global__ __launch_bounds__(512) void bwd_rev_pass_kernel(int NH, int H, int DV
 // dO_r . (Q S^T)_r = q_r . U_r, dY_r . X_r = k_r . Z_r and
 // V'_r . (K dS_next^T)_r = k_r . W2_r.
 // ============================================================================
-template <int DK>
+// LDS of B4.  In the split form (bf16 inputs) Q and K are bf16 rows, which
+// leaves room for two value-block buffers: one is staged while the other is
+// read, one barrier per block.  After the loop dT / E and dP o Gamma overlay
+// the first buffer and W / dK o follows.
+template <int DK, bool SPL>
 struct GradSmem {
-    static constexpr int KP = DK + 4;       // Q, K rows
+    static constexpr int KP = DK + 4;       // Q, K rows (fp32)
+    static constexpr int KB = DK + 8;       // Q, K rows (bf16, split form)
     static constexpr int CP = C + 4;        // C x C matrices
     static constexpr int BP = 16 + 4;       // value blocks [C][16] and transposed S / dS blocks [DK][16]
+    static constexpr int NBUF = SPL ? 2 : 1;
+    static constexpr int QK_FL = SPL ? C * KB / 2 : C * KP;
     static constexpr int off_q = 0;
-    static constexpr int off_k = off_q + C * KP;
-    static constexpr int off_t = off_k + C * KP;
-    // value loop: S^T, dS^T, dO, Y, V', dV', dY blocks; afterwards dT / E and dP o Gamma
-    static constexpr int off_s = off_t + C * CP;
-    static constexpr int off_ds = off_s + DK * BP;
-    static constexpr int off_o = off_ds + DK * BP;
-    static constexpr int off_y = off_o + C * BP;
-    static constexpr int off_vp = off_y + C * BP;
-    static constexpr int off_dvp = off_vp + C * BP;
-    static constexpr int off_dy = off_dvp + C * BP;
-    static constexpr int off_dt = off_s;                  // after the loop
-    static constexpr int off_p = off_s + C * CP;          // after the loop: dP o Gamma
-    static constexpr int off_w = (off_dy + C * BP > off_p + C * CP) ? off_dy + C * BP : off_p + C * CP;  // W, later dK o
-    static constexpr int off_vec = off_w + C * CP;        // g, gamma, kappa, beta, dgamma, dkappa, dbeta
+    static constexpr int off_k = off_q + QK_FL;
+    static constexpr int off_t = off_k + QK_FL;
+    // one value-block buffer: S^T, dS^T, dO, Y, V', dV', dY blocks
+    static constexpr int b_s = 0, b_ds = DK * BP, b_o = 2 * DK * BP, b_y = b_o + C * BP, b_vp = b_y + C * BP;
+    static constexpr int b_dvp = b_vp + C * BP, b_dy = b_dvp + C * BP, VBUF = b_dy + C * BP;
+    static constexpr int off_buf = off_t + C * CP;
+    static constexpr int off_dt = off_buf;                // after the loop
+    static constexpr int off_p = off_buf + C * CP;        // after the loop: dP o Gamma
+    static constexpr int off_w = (off_buf + VBUF > off_p + C * CP) ? off_buf + VBUF : off_p + C * CP;  // W, later dK o
+    static constexpr int END = (off_buf + NBUF * VBUF > off_w + C * CP) ? off_buf + NBUF * VBUF : off_w + C * CP;
+    static constexpr int off_vec = END;                   // g, gamma, kappa, beta, dgamma, dkappa, dbeta
     static constexpr int off_f = off_vec + 7 * C + 8;    // (after one <dS_next, S> part per wave)
     static constexpr int floats = off_f + 4 * C;         // E L column sums, one row per row block
     static constexpr size_t bytes = sizeof(float) * floats;
-    static_assert(off_p + C * CP <= off_w, "dT and dP o Gamma fit the value-loop area");
+    static_assert(off_buf % 4 == 0 && VBUF % 4 == 0, "16-byte aligned buffers");
     static_assert(bytes <= 160 * 1024, "one block per CU: at most the 160 KiB of LDS");
 };
 
@@ -1048,13 +1052,16 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(int H, int DV, int T, int
                                                        const float *__restrict__ ws_dvp, float *__restrict__ dq,
                                                        float *__restrict__ dk, const float *__restrict__ dv,
                                                        float *__restrict__ dla, float *__restrict__ dbeta) {
-    using L = GradSmem<DK>;
-    constexpr int KP = L::KP, CP = L::CP, BP = L::BP, NA = DK / 16, NH = NA / 2;
+    constexpr bool SPL = SplitState<in_t>::value;
+    using L = GradSmem<DK, SPL>;
+    constexpr int KP = L::KP, KB = L::KB, CP = L::CP, BP = L::BP, NA = DK / 16, NH = NA / 2;
     extern __shared__ __align__(16) float smem[];
     float *sq = smem + L::off_q, *sk = smem + L::off_k, *st = smem + L::off_t, *sp = smem + L::off_p;
-    float *ss = smem + L::off_s, *sds = smem + L::off_ds, *so = smem + L::off_o, *sy = smem + L::off_y;
-    // ss, sds: S and dS_next blocks transposed, ss[c * BP + kk] = S[vb0 + kk][c]
-    float *svp = smem + L::off_vp, *sdvp = smem + L::off_dvp, *sdy = smem + L::off_dy, *sw = smem + L::off_w;
+    const uint16_t *sqb = reinterpret_cast<const uint16_t *>(sq), *skb = reinterpret_cast<const uint16_t *>(sk);
+    float *sw = smem + L::off_w;
+    // Q and K element (r, c) as fp32, from fp32 or (split form) bf16 rows
+    auto q_at = [&](int r, int c) { return SPL ? __uint_as_float((uint32_t)sqb[r * KB + c] << 16) : sq[r * KP + c]; };
+    auto k_at = [&](int r, int c) { return SPL ? __uint_as_float((uint32_t)skb[r * KB + c] << 16) : sk[r * KP + c]; };
     float *vg = smem + L::off_vec, *vgam = vg + C, *vkap = vg + 2 * C, *vb = vg + 3 * C;
     float *vdgam = vg + 4 * C, *vdkap = vg + 5 * C, *vdb = vg + 6 * C;
     float *vgl = vg + 7 * C;   // per-wave parts of <dS_next, S>
@@ -1084,7 +1091,6 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(int H, int DV, int T, int
 #pragma unroll
     for (int c = 0; c < 4; ++c) dx[c] = zero4();
     float pgl = 0.f;
-    const float *sxa = half ? sdvp : so, *sxb = half ? sy : svp;
 
     // The wave's decay-mask tiles: (wr, c) for c = 2 ci + half <= wr.  Their
     // (Q K^T) o Gamma and (K K^T) o Gamma, loaded here to land during the loop.
@@ -1103,8 +1109,8 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(int H, int DV, int T, int
     // One value block's operands in registers.  S / dS_next block: lane tid
     // takes row tid % 16 and columns 4 (tid / 16 + 32 m) .. + 3, so the
     // transposed LDS stores of a wave hit consecutive banks; dO, dY, Y, V',
-    // dV': element tid + 512 m of the C x 16 block.  Two sets alternate, so
-    // each block's loads are issued two blocks ahead of its use.
+    // dV': element tid + 512 m of the C x 16 block.  Each block's loads are
+    // issued a block ahead of its staging.
     constexpr int NS = (DK / 4 + 31) / 32;
     struct VBlock {
         float4_t ga[NS], gb[NS];
@@ -1133,9 +1139,11 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(int H, int DV, int T, int
             B.gdvp[m] = gdvp[wv];
         }
     };
-    // Block vb0 from B (then B takes block vb0 + 32): stage, compute.
-    auto value_block = [&](VBlock &B, int vb0) {
-        __syncthreads();   // the previous blocks are no longer read
+    // Write a loaded block into value-block buffer bb (S^T and dS_next^T
+    // transposed: ss[c * BP + kk] = S[vb + kk][c]).
+    auto stage_block = [&](const VBlock &B, float *bb) {
+        float *ss = bb + L::b_s, *sds = bb + L::b_ds, *so = bb + L::b_o, *sy = bb + L::b_y;
+        float *svp = bb + L::b_vp, *sdvp = bb + L::b_dvp, *sdy = bb + L::b_dy;
 #pragma unroll
         for (int m = 0; m < NS; ++m) {
             const int cg = tid / 16 + 32 * m;
@@ -1159,9 +1167,13 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(int H, int DV, int T, int
             svp[r * BP + c] = B.gvp[m];
             sdvp[r * BP + c] = B.gdvp[m];
         }
-        if (vb0 + 32 < DV) load_block(B, vb0 + 32);
-        __syncthreads();
-        // One k-tile (the block's 16 value columns): lane (n, j) supplies columns 4j .. 4j + 3.
+    };
+    // The products of the block in buffer bb: one k-tile (its 16 value
+    // columns), lane (n, j) supplying columns 4j .. 4j + 3.
+    auto compute_block = [&](const float *bb) {
+        const float *ss = bb + L::b_s, *sds = bb + L::b_ds, *so = bb + L::b_o, *sy = bb + L::b_y;
+        const float *svp = bb + L::b_vp, *sdvp = bb + L::b_dvp, *sdy = bb + L::b_dy;
+        const float *sxa = half ? sdvp : so, *sxb = half ? sy : svp;
         const float4_t ao = *reinterpret_cast<const float4_t *>(so + (rw + nn) * BP + 4 * jj);
         const float4_t ayv = *reinterpret_cast<const float4_t *>(sdy + (rw + nn) * BP + 4 * jj);
         const float4_t avp = *reinterpret_cast<const float4_t *>(svp + (rw + nn) * BP + 4 * jj);
@@ -1186,9 +1198,9 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(int H, int DV, int T, int
             }
         }
     };
-    VBlock B0, B1;
-    load_block(B0, 0);
-    if (16 < DV) load_block(B1, 16);
+    float *buf0 = smem + L::off_buf;
+    VBlock VB;
+    load_block(VB, 0);
     // ---- stage Q, K, T and the vectors (issued after the first value blocks'
     // loads, so the two latencies overlap; rows past the end re-read the last
     // row and are zeroed when staged) ----
@@ -1208,7 +1220,14 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(int H, int DV, int T, int
 #pragma unroll
     for (int m = 0; m < NQ; ++m) {
         const int idx = tid * 8 + 4096 * m, r = idx / DK, c = idx % DK;
-        if (idx < C * DK) {
+        if (SPL && idx < C * DK) {   // bf16 rows as they are
+            if (r >= len) {
+                qs[m].zero();
+                ks[m].zero();
+            }
+            qs[m].store_lds(reinterpret_cast<in_t *>(sq) + r * KB + c);
+            ks[m].store_lds(reinterpret_cast<in_t *>(sk) + r * KB + c);
+        } else if (idx < C * DK) {
             float xq[8], xk[8];
             qs[m].to_f32(xq);
             ks[m].to_f32(xk);
@@ -1229,11 +1248,32 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(int H, int DV, int T, int
     if (tid < 4 * C) vg[tid] = vv0;
     if (tid < 3 * C) vdgam[tid] = 0.f;   // dgamma, dkappa and dbeta accumulate atomically
     if (tid < 4 * C) vF[tid] = 0.f;
+    if constexpr (L::NBUF == 2) {   // block 0 staged with the rest
+        stage_block(VB, buf0);
+        load_block(VB, min(16, DV - 16));
+    }
     __syncthreads();
 
-    for (int vb0 = 0; vb0 < DV; vb0 += 32) {
-        value_block(B0, vb0);
-        if (vb0 + 16 < DV) value_block(B1, vb0 + 16);
+    if constexpr (L::NBUF == 2) {
+        // Block i is read from buffer i % 2 while block i + 1 is staged into
+        // the other; the barrier after both makes block i + 1 visible and
+        // frees buffer i % 2 for block i + 2.
+        for (int vb0 = 0, i = 0; vb0 < DV; vb0 += 16, ++i) {
+            compute_block(buf0 + (i & 1) * L::VBUF);
+            if (vb0 + 16 < DV) {
+                stage_block(VB, buf0 + ((i + 1) & 1) * L::VBUF);
+                load_block(VB, min(vb0 + 32, DV - 16));   // (the last blocks load themselves again)
+            }
+            __syncthreads();
+        }
+    } else {
+        for (int vb0 = 0; vb0 < DV; vb0 += 16) {
+            __syncthreads();   // the previous block is no longer read
+            stage_block(VB, buf0);
+            if (vb0 + 16 < DV) load_block(VB, vb0 + 16);
+            __syncthreads();
+            compute_block(buf0);
+        }
     }
 
     // ---- decay sums: dgamma_r = q_r . U_r - k_r . Z_r,  dkappa_r = k_r . W2_r ----
@@ -1246,7 +1286,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(int H, int DV, int T, int
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = rw + 4 * jj + i, c = 16 * (a0 + a) + nn;
-                const float qv = sq[r * KP + c], kv = sk[r * KP + c];
+                const float qv = q_at(r, c), kv = k_at(r, c);
                 pg[i] += qv * au[a][i] - kv * az[a][i];
                 pk[i] += kv * aw[a][i];
             }
@@ -1407,7 +1447,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(int H, int DV, int T, int
     // dP o Gamma is lower triangular: k-tiles up to the wave's rows for dQ,
     // from them on for dK.
     if constexpr (SplitState<in_t>::value) {
-        // bf16 inputs: K and Q are bf16 values, so each product takes the row-side
+        // bf16 inputs: K and Q are bf16 rows, so each product takes the row-side
         // operand as three exact bf16 terms, per 32-wide k slice.
         auto split8 = [](const float (&x)[8], uint4 (&t)[3]) {
             uint2 h0, m0, l0, h1, m1, l1;
@@ -1441,8 +1481,8 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(int H, int DV, int T, int
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int kx = 32 * ks + 8 * jj + 2 * e;
-                    bk[e] = pack_bf16(sk[kx * KP + ka + nn], sk[(kx + 1) * KP + ka + nn]);
-                    bq[e] = pack_bf16(sq[kx * KP + ka + nn], sq[(kx + 1) * KP + ka + nn]);
+                    bk[e] = (uint32_t)skb[kx * KB + ka + nn] | ((uint32_t)skb[(kx + 1) * KB + ka + nn] << 16);
+                    bq[e] = (uint32_t)sqb[kx * KB + ka + nn] | ((uint32_t)sqb[(kx + 1) * KB + ka + nn] << 16);
                 }
                 const uint4 kb = uint4{bk[0], bk[1], bk[2], bk[3]}, qb = uint4{bq[0], bq[1], bq[2], bq[3]};
 #pragma unroll
@@ -1590,7 +1630,7 @@ hipError_t launch_bwd_dk(const ChunkArgs &a, const BwdArgs &g, const BwdWorkspac
         }
     }
     if (items > 0) {
-        using L = GradSmem<DK>;
+        using L = GradSmem<DK, SplitState<in_t>::value>;
         auto kern = bwd_grad_kernel<in_t, DK>;
         if ((e = bwd_allow_smem(kern, L::bytes)) != hipSuccess) return e;
         ProfScope prof("gdn_bwd_grad", st);
