@@ -391,10 +391,10 @@ template <int DK, bool SPL>
 struct PassSmem {
     static constexpr int KP = DK + 4;   // rows of K; rows of the state tile (S, 16 x DK)
     static constexpr int TP = C + 4;    // transposed value blocks [16][C]; C x C matrices
-    static constexpr int SBP = DK + 8;  // split form: bf16 rows of the three state terms
+    static constexpr int SBP = DK + 8;  // split form: bf16 rows of K and of the three state terms
     static constexpr int VBP = C + 8;   // split form: bf16 rows of the three (diag(kappa) V')^T terms
-    static constexpr int off_k = 0;
-    static constexpr int off_s = off_k + C * KP;                          // S rows (or their three bf16 terms)
+    static constexpr int off_k = 0;                                       // K rows (bf16 in split form)
+    static constexpr int off_s = off_k + (SPL ? C * SBP / 2 : C * KP);    // S rows (or their three bf16 terms)
     static constexpr int off_a = off_s + (SPL ? 3 * 16 * SBP / 2 : 16 * KP);  // Y^T
     static constexpr int off_b = off_a + 16 * TP;                         // (diag(kappa) V')^T (or its terms)
     static constexpr int off_m = off_b + (SPL ? 3 * 16 * VBP / 2 : 16 * TP);  // M = T diag(beta)
@@ -475,13 +475,20 @@ __device__ __forceinline__ void pass_load(PassStage<in_t, DK> &S, int row, int H
 // gamma, kappa, beta.
 template <typename in_t, int DK>
 __device__ __forceinline__ void pass_store(const PassStage<in_t, DK> &S, float *smem) {
-    using L = PassSmem<DK, SplitState<in_t>::value>;
-    constexpr int KP = L::KP, TP = L::TP;
+    constexpr bool SPL = SplitState<in_t>::value;
+    using L = PassSmem<DK, SPL>;
+    constexpr int KP = L::KP, TP = L::TP, SBP = L::SBP;
     float *sk = smem + L::off_k, *sm = smem + L::off_m, *sv = smem + L::off_v;
     const int tid = threadIdx.x;
 #pragma unroll
     for (int m = 0; m < PassStage<in_t, DK>::MK; ++m) {
         const int idx = tid * 8 + 2048 * m, r = idx / DK, cc = idx % DK;
+        if constexpr (SPL) {   // bf16 rows as they are
+            Raw8<in_t> kk = S.kr[m];
+            if (r >= S.len) kk.zero();
+            kk.store_lds(reinterpret_cast<in_t *>(sk) + r * SBP + cc);
+            continue;
+        }
         float x[8];
         S.kr[m].to_f32(x);
         if (r >= S.len)
@@ -518,6 +525,7 @@ __global__ __launch_bounds__(256) void bwd_fwd_pass_kernel(int NH, int H, int DV
     float *sk = smem + L::off_k, *ss = smem + L::off_s, *syt = smem + L::off_a, *svpt = smem + L::off_b;
     float *sm = smem + L::off_m, *sv = smem + L::off_v;   // sv: gamma [C], kappa [C], beta [C]
     uint16_t *ssb = reinterpret_cast<uint16_t *>(ss), *svb = reinterpret_cast<uint16_t *>(svpt);   // split form
+    const uint16_t *skb = reinterpret_cast<const uint16_t *>(sk);                                   // split form: K rows
     if (!cpr && meta[1] != 0) return;
     // The value tiles of one (sequence, head) read the same K and T.  Blocks
     // are dealt to the 8 XCDs in turn, so give a head's tiles block indices
@@ -594,10 +602,7 @@ __global__ __launch_bounds__(256) void bwd_fwd_pass_kernel(int NH, int H, int DV
         if constexpr (SPL) {
 #pragma unroll
             for (int ks = 0; ks < DK / 32; ++ks) {
-                const float4_t k0 = *reinterpret_cast<const float4_t *>(sk + (rw + nn) * KP + 32 * ks + 8 * jj);
-                const float4_t k1 = *reinterpret_cast<const float4_t *>(sk + (rw + nn) * KP + 32 * ks + 8 * jj + 4);
-                const uint4 ka = uint4{pack_bf16(k0[0], k0[1]), pack_bf16(k0[2], k0[3]), pack_bf16(k1[0], k1[1]),
-                                       pack_bf16(k1[2], k1[3])};
+                const uint4 ka = *reinterpret_cast<const uint4 *>(skb + (rw + nn) * SBP + 32 * ks + 8 * jj);
 #pragma unroll
                 for (int term = 0; term < 3; ++term)
                     mfma_bf16(x, ka, *reinterpret_cast<const uint4 *>(ssb + (16 * term + nn) * SBP + 32 * ks + 8 * jj));
@@ -653,11 +658,13 @@ __global__ __launch_bounds__(256) void bwd_fwd_pass_kernel(int NH, int H, int DV
                 if constexpr (SPL) {
 #pragma unroll
                     for (int ks = 0; ks < C / 32; ++ks) {
-                        float kc[8];
+                        uint4 ka;
+                        uint32_t *kw = reinterpret_cast<uint32_t *>(&ka);
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) kc[e] = sk[(32 * ks + 8 * jj + e) * KP + 16 * a + nn];
-                        const uint4 ka = uint4{pack_bf16(kc[0], kc[1]), pack_bf16(kc[2], kc[3]), pack_bf16(kc[4], kc[5]),
-                                               pack_bf16(kc[6], kc[7])};
+                        for (int e = 0; e < 4; ++e) {
+                            const int r2 = 32 * ks + 8 * jj + 2 * e;
+                            kw[e] = (uint32_t)skb[r2 * SBP + 16 * a + nn] | ((uint32_t)skb[(r2 + 1) * SBP + 16 * a + nn] << 16);
+                        }
 #pragma unroll
                         for (int term = 0; term < 3; ++term)
                             mfma_bf16(acc, ka,
