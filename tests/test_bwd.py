@@ -91,6 +91,16 @@ def test_bwd_gates(gate, dtype):
     _check(inp, d_o, d_final, f"gates {gate} {dtype}")
 
 
+@pytest.mark.parametrize("gate", ["-60", "-5"])
+def test_bwd_gates_d128_bf16(gate):
+    """Strong decay at the benchmark head size: every split bf16 product (dk = dv = 128)
+    with gamma down to e^-60 per token."""
+    inp = W.chunk_inputs(1, 200, 2, 128, 128, "bf16", seed=70, init_std=0.1)
+    inp.log_alpha[:] = float(gate)
+    d_o, d_final = W.incoming_grads(inp, seed=71)
+    _check(inp, d_o, d_final, f"gates {gate} d128 bf16")
+
+
 def test_bwd_prefill_shape_sampled():
     """H=16, dk=dv=128, bf16, 1024 tokens per sequence (16 chunks), two
     heads checked against the oracle."""
