@@ -231,7 +231,9 @@ gdn_status gdn_chunk_bwd_workspace_size(const gdn_chunk_desc *desc, size_t *byte
  *
  * Supported: dk 32, 64 or 128; dv a multiple of 16 up to 1024; flags 0
  * (GDN_QK_L2NORM is not differentiated: GDN_ERR_UNSUPPORTED).  All
- * gradient arithmetic is fp32 for every input dtype.  Tokens past a
+ * gradient arithmetic has fp32 precision for every input dtype (products
+ * with a 16-bit q or k factor may run on the 16-bit matrix cores with the
+ * other factor split exactly into three bf16 terms).  Tokens past a
  * sequence's end are not written.  With cu_seqlens the array is checked on
  * the device as in gdn_chunk_fwd; a malformed one makes the kernels write
  * nothing and gdn_chunk_fwd_check(workspace, ...) reports it.
