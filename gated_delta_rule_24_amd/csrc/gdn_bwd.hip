@@ -38,9 +38,14 @@
 //                           the gradient of the state at every chunk end, and of
 //                           the initial state.
 //   B4 bwd_grad_kernel      per (chunk row, head): every per-token gradient of the
-//                           chunk from its checkpoint and state gradient.
+//                           chunk from its checkpoint and state gradient.  One
+//                           block per resident slot steps through the items and
+//                           loads the next item's first operands during the
+//                           current item's last steps.
 // B2 also stores each chunk's Y and V', B3 its dV' and dY (= dV, written to
-// the output), so B4 recomputes none of the state products.
+// the output), so B4 recomputes none of the state products.  Y, V' and dV'
+// are kept block-major, [item][DV / 16][C][16], so that each 16-column block
+// B4 loads is one contiguous run of whole cache lines.
 // All arithmetic has fp32 precision, so the gradients carry the same precision
 // for every input dtype: products run on the fp32 matrix-core instruction,
 // except those with q or k as a factor, which take the 16-bit instruction when
@@ -50,6 +55,8 @@
 // tiles use the lane convention of gdn_device.h: lane l, n = l % 16,
 // j = l / 16; an accumulator holds X[4j + i][n]; on issue i of a k-tile kt
 // lane (n, j) supplies A[n][16 kt + 4j + i] and B[16 kt + 4j + i][n].
+#include <algorithm>
+
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
@@ -560,7 +567,7 @@ __global__ __launch_bounds__(256) void bwd_fwd_pass_kernel(int NH, int H, int DV
         if (pitem >= 0) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int64_t o = (pitem * C + rw + 4 * jj + i) * DV + v0 + nn;
+                const int64_t o = pitem * C * DV + (int64_t)v0 * C + (rw + 4 * jj + i) * 16 + nn;   // block-major
                 ws_y[o] = py[i];
                 ws_vp[o] = pvp[i];
             }
@@ -910,7 +917,7 @@ __global__ __launch_bounds__(512) void bwd_rev_pass_kernel(int NH, int H, int DV
                 }
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) ws_dvp[(item * C + rw + 4 * jj + i) * DV + v0 + nn] = dvp[i];
+            for (int i = 0; i < 4; ++i) ws_dvp[(int64_t)item * C * DV + (int64_t)v0 * C + (rw + 4 * jj + i) * 16 + nn] = dvp[i];
             *reinterpret_cast<float4_t *>(sdvpt + nn * TP + rw + 4 * jj) = dvp;
         }
         __syncthreads();
@@ -1074,17 +1081,92 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(int H, int DV, int T, int
     float *vgl = vg + 7 * C;   // per-wave parts of <dS_next, S>
     float *vF = smem + L::off_f;   // [4][C]
     if (!cpr && meta[1] != 0) return;
-    const int nrows = cpr ? urows : meta[0];
-    const int item = blockIdx.x, row = item / H, h = item % H;
-    if (row >= nrows) return;
-    int tok0, len;
-    row_span(row, T, cpr, row_tok, row_len, tok0, len);
-    if (len == 0) return;   // an empty sequence's row: it has no gradients
+    const int nitems = (cpr ? urows : meta[0]) * H;
+    int tid = threadIdx.x;
+    // One value block's operands in registers.  S / dS_next block: lane tid
+    // takes row tid % 16 and columns 4 (tid / 16 + 32 m) .. + 3, so the
+    // transposed LDS stores of a wave hit consecutive banks; dO, dY, Y, V',
+    // dV': element tid + 512 m of the C x 16 block.
+    constexpr int NS = (DK / 4 + 31) / 32;
+    struct VBlock {
+        float4_t ga[NS], gb[NS];
+        float go[2], gdy[2], gyv[2], gvp[2], gdvp[2];
+    };
+    auto load_block_of = [&](VBlock &B, int vb, int64_t it, int tok0, int len, int h) {
+        const float *ck = ws_ck + it * DV * DK, *dsn = ws_ds + it * DV * DK;
+        const float *gy = ws_y + it * C * DV, *gvp = ws_vp + it * C * DV, *gdvp = ws_dvp + it * C * DV;
+#pragma unroll
+        for (int m = 0; m < NS; ++m) {
+            const int cg = tid / 16 + 32 * m;
+            if (cg < DK / 4) {
+                const int r = tid % 16, c = 4 * cg;
+                B.ga[m] = *reinterpret_cast<const float4_t *>(ck + (int64_t)(vb + r) * DK + c);
+                B.gb[m] = *reinterpret_cast<const float4_t *>(dsn + (int64_t)(vb + r) * DK + c);
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const int e = tid + 512 * m, r = e / 16, c = e % 16;
+            const bool in = r < len;
+            const int64_t tv = ((int64_t)(tok0 + r) * H + h) * DV + vb + c;
+            const int64_t wv = (int64_t)vb * C + e;   // block-major: the C x 16 block is contiguous
+            B.go[m] = in ? d_o[tv] : 0.f;
+            B.gdy[m] = in ? dv[tv] : 0.f;
+            B.gyv[m] = gy[wv];
+            B.gvp[m] = gvp[wv];
+            B.gdvp[m] = gdvp[wv];
+        }
+    };
+    // The operands an item starts with (its first value block, Q, K, T and
+    // decay vectors), loaded into registers during the previous item's
+    // post-loop steps: the block steps through items item0, item0 + grid, ...
+    // Rows past the end re-read the last row and are zeroed when staged.
+    constexpr int NQ = (C * DK + 4095) / 4096;
+    VBlock VB;
+    Raw8<in_t> qs[NQ], ks[NQ];
+    float4_t ts[2];
+    float vv0 = 0.f;
+    auto item_span = [&](int item, int &tok0, int &len) {
+        row_span(item / H, T, cpr, row_tok, row_len, tok0, len);
+    };
+    auto load_item = [&](int item) {
+        int tok0, len;
+        item_span(item, tok0, len);
+        if (len == 0) return;   // (an empty sequence's row is skipped)
+        const int h = item % H;
+        const int64_t it = item;
+        load_block_of(VB, 0, it, tok0, len, h);
+#pragma unroll
+        for (int m = 0; m < NQ; ++m) {
+            const int idx = min(tid * 8 + 4096 * m, C * DK - 8), r = min(idx / DK, len - 1), c = idx % DK;
+            const int64_t off = ((int64_t)(tok0 + r) * H + h) * DK + c;
+            qs[m].load(q + off);
+            ks[m].load(k + off);
+        }
+        const float *Tg = ws_t + it * C * C;
+#pragma unroll
+        for (int m = 0; m < 2; ++m) ts[m] = *reinterpret_cast<const float4_t *>(Tg + tid * 4 + 2048 * m);
+        vv0 = ws_vec[it * kVecFloats + min(tid, 4 * C - 1)];
+    };
+    if ((int)blockIdx.x < nitems) load_item(blockIdx.x);
+    for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
+    __syncthreads();   // the previous item's LDS contents are no longer read
+    // (The lane index is re-issued per item so that the many addresses derived
+    // from it are formed where they are used, not held across the item loop.)
+    asm volatile("" : "+v"(tid));
     // Eight waves: wave w owns chunk rows 16 (w % 4) .. + 15; the two halves of
     // the block (w / 4) split the key-column tiles of U, Z, W2, dQ and dK, and
     // the decay-mask steps (half 0 holds dP, half 1 holds dM).
-    const int tid = threadIdx.x, w = tid >> 6, wr = w & 3, half = w >> 2, l = tid & 63, nn = l & 15, jj = l >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6), wr = w & 3, half = w >> 2;
+    const int l = tid & 63, nn = l & 15, jj = l >> 4;
     const int a0 = half * NH;
+    const int h = item % H, next = item + (int)gridDim.x;
+    int tok0, len;
+    item_span(item, tok0, len);
+    if (len == 0) {   // an empty sequence's row: it has no gradients
+        if (next < nitems) load_item(next);
+        continue;
+    }
     const int64_t it64 = (int64_t)item;
 
     const float *Tg = ws_t + it64 * C * C, *Pg = ws_p + it64 * C * C, *Gg = ws_g + it64 * C * C;
@@ -1111,41 +1193,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(int H, int DV, int T, int
             gvr[ci][i] = c <= wr ? Gg[r * C + cc] : 0.f;
         }
 
-    const float *ck = ws_ck + it64 * DV * DK, *dsn = ws_ds + it64 * DV * DK;
-    const float *gy = ws_y + it64 * C * DV, *gvp = ws_vp + it64 * C * DV, *gdvp = ws_dvp + it64 * C * DV;
-    // One value block's operands in registers.  S / dS_next block: lane tid
-    // takes row tid % 16 and columns 4 (tid / 16 + 32 m) .. + 3, so the
-    // transposed LDS stores of a wave hit consecutive banks; dO, dY, Y, V',
-    // dV': element tid + 512 m of the C x 16 block.  Each block's loads are
-    // issued a block ahead of its staging.
-    constexpr int NS = (DK / 4 + 31) / 32;
-    struct VBlock {
-        float4_t ga[NS], gb[NS];
-        float go[2], gdy[2], gyv[2], gvp[2], gdvp[2];
-    };
-    auto load_block = [&](VBlock &B, int vb) {
-#pragma unroll
-        for (int m = 0; m < NS; ++m) {
-            const int cg = tid / 16 + 32 * m;
-            if (cg < DK / 4) {
-                const int r = tid % 16, c = 4 * cg;
-                B.ga[m] = *reinterpret_cast<const float4_t *>(ck + (int64_t)(vb + r) * DK + c);
-                B.gb[m] = *reinterpret_cast<const float4_t *>(dsn + (int64_t)(vb + r) * DK + c);
-            }
-        }
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-            const int e = tid + 512 * m, r = e / 16, c = e % 16;
-            const bool in = r < len;
-            const int64_t tv = ((int64_t)(tok0 + r) * H + h) * DV + vb + c;
-            const int64_t wv = (int64_t)r * DV + vb + c;
-            B.go[m] = in ? d_o[tv] : 0.f;
-            B.gdy[m] = in ? dv[tv] : 0.f;
-            B.gyv[m] = gy[wv];
-            B.gvp[m] = gvp[wv];
-            B.gdvp[m] = gdvp[wv];
-        }
-    };
+    auto load_block = [&](VBlock &B, int vb) { load_block_of(B, vb, it64, tok0, len, h); };
     // Write a loaded block into value-block buffer bb (S^T and dS_next^T
     // transposed: ss[c * BP + kk] = S[vb + kk][c]).
     auto stage_block = [&](const VBlock &B, float *bb) {
@@ -1206,24 +1254,8 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(int H, int DV, int T, int
         }
     };
     float *buf0 = smem + L::off_buf;
-    VBlock VB;
-    load_block(VB, 0);
-    // ---- stage Q, K, T and the vectors (issued after the first value blocks'
-    // loads, so the two latencies overlap; rows past the end re-read the last
-    // row and are zeroed when staged) ----
-    constexpr int NQ = (C * DK + 4095) / 4096;
-    Raw8<in_t> qs[NQ], ks[NQ];
-#pragma unroll
-    for (int m = 0; m < NQ; ++m) {
-        const int idx = min(tid * 8 + 4096 * m, C * DK - 8), r = min(idx / DK, len - 1), c = idx % DK;
-        const int64_t off = ((int64_t)(tok0 + r) * H + h) * DK + c;
-        qs[m].load(q + off);
-        ks[m].load(k + off);
-    }
-    float4_t ts[2];
-#pragma unroll
-    for (int m = 0; m < 2; ++m) ts[m] = *reinterpret_cast<const float4_t *>(Tg + tid * 4 + 2048 * m);
-    const float vv0 = ws_vec[it64 * kVecFloats + min(tid, 4 * C - 1)];
+    // ---- stage Q, K, T and the vectors (loaded with the first value block
+    // during the previous item) ----
 #pragma unroll
     for (int m = 0; m < NQ; ++m) {
         const int idx = tid * 8 + 4096 * m, r = idx / DK, c = idx % DK;
@@ -1449,6 +1481,9 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(int H, int DV, int T, int
         if (jj == 0) vF[wr * C + 16 * c + nn] = cs;
     }
     __syncthreads();
+    // Start the next item's loads, to land during this item's last products
+    // (late, where fewer registers are live).
+    if (next < nitems) load_item(next);
     // dQ += (dP o Gamma) K;  dK += (dP o Gamma)^T Q + (dK o + dK o^T) K.  The
     // row-side operands do not depend on the key tile: read once per k-tile.
     // dP o Gamma is lower triangular: k-tiles up to the wave's rows for dQ,
@@ -1568,6 +1603,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(int H, int DV, int T, int
             dbeta[th] = vdb[i];
         }
     }
+    }   // items
 }
 
 // ============================================================================
@@ -1580,6 +1616,19 @@ hipError_t bwd_allow_smem(K kernel, size_t bytes) {
     if (bytes <= 64 * 1024) return hipSuccess;
     return hipFuncSetAttribute(reinterpret_cast<const void *>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
                                (int)bytes);
+}
+
+// Compute units of the current device (cached after the first query).
+int bwd_cu_count() {
+    static int cus = 0;
+    if (cus == 0) {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cus = n;
+    }
+    return cus;
 }
 
 int bwd_cpr(const ChunkArgs &a) { return a.cu_seqlens ? 0 : (a.T + C - 1) / C + (a.T == 0); }
@@ -1640,8 +1689,16 @@ hipError_t launch_bwd_dk(const ChunkArgs &a, const BwdArgs &g, const BwdWorkspac
         using L = GradSmem<DK, SplitState<in_t>::value>;
         auto kern = bwd_grad_kernel<in_t, DK>;
         if ((e = bwd_allow_smem(kern, L::bytes)) != hipSuccess) return e;
+        // A block per resident slot, each stepping through the items, so the
+        // next item's first loads overlap the current item's last steps.
+        int per_cu = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(kern), 512,
+                                                         L::bytes) != hipSuccess ||
+            per_cu < 1)
+            per_cu = 1;
+        const int64_t grid = std::min<int64_t>(items, (int64_t)per_cu * bwd_cu_count());
         ProfScope prof("gdn_bwd_grad", st);
-        kern<<<dim3((unsigned)items), dim3(512), L::bytes, st>>>(a.H, a.dv, a.T, cpr, urows, meta, rtok, rlen, q, k,
+        kern<<<dim3((unsigned)grid), dim3(512), L::bytes, st>>>(a.H, a.dv, a.T, cpr, urows, meta, rtok, rlen, q, k,
                                                                  g.d_o, wt, wp, wg, wv, wck, wds, wy, wvp, wdvp, g.dq,
                                                                  g.dk, g.dv, g.dlog_alpha, g.dbeta);
         if ((e = hipGetLastError()) != hipSuccess) return e;
