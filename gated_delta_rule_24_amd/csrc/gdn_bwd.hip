@@ -1169,7 +1169,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(int H, int DV, int T, int
     }
     const int64_t it64 = (int64_t)item;
 
-    const float *Tg = ws_t + it64 * C * C, *Pg = ws_p + it64 * C * C, *Gg = ws_g + it64 * C * C;
+    const float *Pg = ws_p + it64 * C * C, *Gg = ws_g + it64 * C * C;
     const int rw = 16 * wr;          // the wave's first chunk row
     // Sums over the value dimension, rows of the wave, key tiles a0 + a:
     //   U = dO S,  Z = dY S,  W2 = V' dS_next;  and tiles (wr, c <= wr) of
