@@ -1085,12 +1085,16 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(int H, int DV, int T, int
     int tid = threadIdx.x;
     // One value block's operands in registers.  S / dS_next block: lane tid
     // takes row tid % 16 and columns 4 (tid / 16 + 32 m) .. + 3, so the
-    // transposed LDS stores of a wave hit consecutive banks; dO, dY, Y, V',
-    // dV': element tid + 512 m of the C x 16 block.
-    constexpr int NS = (DK / 4 + 31) / 32;
+    // transposed LDS stores of a wave hit consecutive banks; Y, V', dV':
+    // element tid + 512 m of the C x 16 block.  dO and dY: element tid + 512 m
+    // of C x PW columns, read when the first block of the PW columns is loaded.
+    // In the split form (registers to spare) PW = 32, whole 128-byte lines for
+    // a pair of blocks, and the lanes holding the second block's half keep it
+    // until that block is staged; otherwise PW = 16.
+    constexpr int NS = (DK / 4 + 31) / 32, PW = SPL ? 32 : 16, NP = PW / 8;
     struct VBlock {
         float4_t ga[NS], gb[NS];
-        float go[2], gdy[2], gyv[2], gvp[2], gdvp[2];
+        float go[NP], gdy[NP], gyv[2], gvp[2], gdvp[2];
     };
     auto load_block_of = [&](VBlock &B, int vb, int64_t it, int tok0, int len, int h) {
         const float *ck = ws_ck + it * DV * DK, *dsn = ws_ds + it * DV * DK;
@@ -1104,14 +1108,20 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(int H, int DV, int T, int
                 B.gb[m] = *reinterpret_cast<const float4_t *>(dsn + (int64_t)(vb + r) * DK + c);
             }
         }
+        if (vb % PW == 0) {   // the first block of the PW columns
+#pragma unroll
+            for (int m = 0; m < NP; ++m) {
+                const int e = tid + 512 * m, r = e / PW, c = e % PW;
+                const bool in = r < len && vb + c < DV;
+                const int64_t tv = ((int64_t)(tok0 + r) * H + h) * DV + vb + c;
+                B.go[m] = in ? d_o[tv] : 0.f;
+                B.gdy[m] = in ? dv[tv] : 0.f;
+            }
+        }
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-            const int e = tid + 512 * m, r = e / 16, c = e % 16;
-            const bool in = r < len;
-            const int64_t tv = ((int64_t)(tok0 + r) * H + h) * DV + vb + c;
+            const int e = tid + 512 * m;
             const int64_t wv = (int64_t)vb * C + e;   // block-major: the C x 16 block is contiguous
-            B.go[m] = in ? d_o[tv] : 0.f;
-            B.gdy[m] = in ? dv[tv] : 0.f;
             B.gyv[m] = gy[wv];
             B.gvp[m] = gvp[wv];
             B.gdvp[m] = gdvp[wv];
@@ -1196,7 +1206,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(int H, int DV, int T, int
     auto load_block = [&](VBlock &B, int vb) { load_block_of(B, vb, it64, tok0, len, h); };
     // Write a loaded block into value-block buffer bb (S^T and dS_next^T
     // transposed: ss[c * BP + kk] = S[vb + kk][c]).
-    auto stage_block = [&](const VBlock &B, float *bb) {
+    auto stage_block = [&](const VBlock &B, int vb, float *bb) {
         float *ss = bb + L::b_s, *sds = bb + L::b_ds, *so = bb + L::b_o, *sy = bb + L::b_y;
         float *svp = bb + L::b_vp, *sdvp = bb + L::b_dvp, *sdy = bb + L::b_dy;
 #pragma unroll
@@ -1213,11 +1223,17 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(int H, int DV, int T, int
                        B.ga[m][3] * B.gb[m][3];
             }
         }
+        if (PW == 16 || ((tid >> 4) & 1) == ((vb >> 4) & 1)) {   // the lanes holding this block's part
+#pragma unroll
+            for (int m = 0; m < NP; ++m) {
+                const int e = tid + 512 * m, r = e / PW, c = e % 16;
+                so[r * BP + c] = B.go[m];
+                sdy[r * BP + c] = B.gdy[m];
+            }
+        }
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
             const int e = tid + 512 * m, r = e / 16, c = e % 16;
-            so[r * BP + c] = B.go[m];
-            sdy[r * BP + c] = B.gdy[m];
             sy[r * BP + c] = B.gyv[m];
             svp[r * BP + c] = B.gvp[m];
             sdvp[r * BP + c] = B.gdvp[m];
@@ -1288,7 +1304,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(int H, int DV, int T, int
     if (tid < 3 * C) vdgam[tid] = 0.f;   // dgamma, dkappa and dbeta accumulate atomically
     if (tid < 4 * C) vF[tid] = 0.f;
     if constexpr (L::NBUF == 2) {   // block 0 staged with the rest
-        stage_block(VB, buf0);
+        stage_block(VB, 0, buf0);
         load_block(VB, min(16, DV - 16));
     }
     __syncthreads();
@@ -1300,7 +1316,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(int H, int DV, int T, int
         for (int vb0 = 0, i = 0; vb0 < DV; vb0 += 16, ++i) {
             compute_block(buf0 + (i & 1) * L::VBUF);
             if (vb0 + 16 < DV) {
-                stage_block(VB, buf0 + ((i + 1) & 1) * L::VBUF);
+                stage_block(VB, vb0 + 16, buf0 + ((i + 1) & 1) * L::VBUF);
                 load_block(VB, min(vb0 + 32, DV - 16));   // (the last blocks load themselves again)
             }
             __syncthreads();
@@ -1308,7 +1324,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(int H, int DV, int T, int
     } else {
         for (int vb0 = 0; vb0 < DV; vb0 += 16) {
             __syncthreads();   // the previous block is no longer read
-            stage_block(VB, buf0);
+            stage_block(VB, vb0, buf0);
             if (vb0 + 16 < DV) load_block(VB, vb0 + 16);
             __syncthreads();
             compute_block(buf0);
