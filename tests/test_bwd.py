@@ -62,6 +62,7 @@ CASES = [
     (2, 200, 2, 128, 128, "bf16", 0.1, True),
     (1, 100, 1, 128, 256, "fp16", 0.1, True),
     (1, 257, 3, 32, 48, "fp32", None, True),
+    (1, 190, 2, 64, 48, "bf16", 0.1, True),   # an odd count of 16-column value blocks above one
 ]
 
 
