@@ -1,19 +1,23 @@
 """Benchmark of the gated delta rule core on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
-                    [--only prefill|decode]
+                    [--only prefill|long|packed|decode|continuation|backward|copy]
 
 A step is one chunked prefill over the prefill workload (B=4, H=16, L=4096,
 dk=dv=128, C=64, bf16 q/k/v, fp32 gates, fp32 o and states), inputs resident
-in HBM.  `value` is prefill tokens/s.  The same run times 1000 in-place decode
-steps of the decode workload (256 sequences x 16 heads, 128x128 fp32 states)
-and reports steps/s under "decode", the continuation call (256 resident states
-take 2..16 tokens each) under "continuation" and the backward pass over the
-prefill workload under "backward".  Each kernel's average duration comes from
-HIP events the library records around its launches on the launch stream; the
-roofline objects use the algorithmic bytes and flops of the method (counted
-below) over that duration.  The CPU baseline is the fp64 oracle on a bounded
-sample of the prefill workload, on all host cores.
+in HBM.  `value` is prefill tokens/s (mean over K back-to-back steps; the
+median and minimum of K individually timed steps are reported beside it).
+The same run times the long-context workload (B=1, H=16, L=32768, dk=128,
+dv=256, half the heads slow-forgetting) under "long", the packed batch (eight
+sequences of 512..8192 tokens with initial states) under "packed", 1000
+in-place decode steps (256 sequences x 16 heads, 128x128 fp32 states) under
+"decode", the continuation call (256 resident states take 2..16 tokens each)
+under "continuation" and the backward pass over the prefill workload under
+"backward".  Each kernel's average duration comes from HIP events the library
+records around its launches on the launch stream; the roofline objects use
+the algorithmic bytes and flops of the method (counted below) over that
+duration.  The CPU baselines are the fp64 oracle on a bounded sample of each
+chunked workload, on all host cores.
 
 Prints ONE JSON line.  --only runs a single leg (for profiler runs) and
 prints that leg's part of the line.
@@ -79,17 +83,17 @@ def kernel_sources_digest(files):
     return h.hexdigest()
 
 
-def measured_traffic(kernel):
-    """HBM bytes per launch of `kernel` from the committed FETCH_SIZE / WRITE_SIZE readings, each scaled
-    by what the same counter reads for a copy of known size; None when the kernel's sources have changed
-    since the counters were taken (or none were taken)."""
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` from the committed FETCH_SIZE / WRITE_SIZE
+    readings, each scaled by what the same counter reads for a copy of known size; None when the
+    kernel's sources have changed since the counters were taken (or none were taken)."""
     try:
         with open(TRAFFIC_FILE) as fh:
             rec = json.load(fh)
     except OSError:
         return None
-    k = rec.get("kernels", {}).get(kernel)
-    if not k or kernel_sources_digest(k["sources"]) != k["sources_sha256"]:
+    k = rec.get("kernels", {}).get(f"{kernel}@{workload}")
+    if not k or k.get("workload") != workload or kernel_sources_digest(k["sources"]) != k["sources_sha256"]:
         return None
     cal = rec["copy_calibration"]
     return 1024.0 * (k["fetch_kib"] * cal["fetch_scale"] + k["write_kib"] * cal["write_scale"])
@@ -101,40 +105,73 @@ def _to(x, dev, dt):
     return torch.from_numpy(np.ascontiguousarray(x)).to(dev, dt)
 
 
-def run_prefill(args, gdn, W, dev):
+def time_steps(step, steps, warmup):
+    """Mean step time over `steps` back-to-back steps bracketed by device synchronisation, then the
+    median and minimum of the same number of individually timed steps (events on torch's current
+    stream, the one every call here launches on)."""
+    import statistics
+
     import torch
-    inp = W.prefill()
-    B, T, H, dk, dv = inp.B, inp.T, inp.H, inp.dk, inp.dv
-    q, k, v = (_to(x, dev, torch.bfloat16) for x in (inp.q, inp.k, inp.v))
-    la, be = _to(inp.log_alpha, dev, torch.float32), _to(inp.beta, dev, torch.float32)
-    odt = {"fp32": torch.float32, "bf16": torch.bfloat16}[args.out_dtype]
-    o = torch.empty((B, T, H, dv), dtype=odt, device=dev)
-    fin = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
-    ws = torch.empty(gdn.chunk_fwd_workspace_size(B, T, H, dk, dv, B, out_dtype=odt), dtype=torch.uint8, device=dev)
-
-    def step():
-        gdn.chunk_fwd(q, k, v, la, be, o=o, final_state=fin, workspace=ws, out_dtype=odt)
-
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     ev0.record()
-    for _ in range(args.steps):
+    for _ in range(steps):
         step()
     ev1.record()
     torch.cuda.synchronize()
-    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    mean_ms = ev0.elapsed_time(ev1) / steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in evs:
+        a.record()
+        step()
+        b.record()
+    torch.cuda.synchronize()
+    each = [a.elapsed_time(b) for a, b in evs]
+    return mean_ms, statistics.median(each), min(each)
+
+
+CHUNK_WORKLOADS = {
+    # name: (generator, has_init, description of the shape)
+    "prefill": ("prefill", False),
+    "long": ("long_context", False),
+    "packed": ("packed", True),
+}
+
+
+def run_chunk_workload(args, gdn, W, dev, name, out_dtype="fp32"):
+    """One gdn_chunk_fwd call over a whole workload (inputs resident in HBM), timed as in time_steps;
+    per-kernel durations from the library's own events on the launch stream."""
+    import torch
+    gen, has_init = CHUNK_WORKLOADS[name]
+    inp = getattr(W, gen)()
+    B, T, H, dk, dv, N = inp.B, inp.T, inp.H, inp.dk, inp.dv, inp.num_seqs
+    q, k, v = (_to(x, dev, torch.bfloat16) for x in (inp.q, inp.k, inp.v))
+    la, be = _to(inp.log_alpha, dev, torch.float32), _to(inp.beta, dev, torch.float32)
+    S0 = _to(inp.init_state, dev, torch.float32) if has_init else None
+    cu = torch.from_numpy(inp.cu_seqlens).to(dev) if inp.cu_seqlens is not None else None
+    odt = {"fp32": torch.float32, "bf16": torch.bfloat16, "fp16": torch.float16}[out_dtype]
+    o = torch.empty((B, T, H, dv), dtype=odt, device=dev)
+    fin = torch.empty((N, H, dv, dk), dtype=torch.float32, device=dev)
+    ws = torch.empty(gdn.chunk_fwd_workspace_size(B, T, H, dk, dv, N, out_dtype=odt), dtype=torch.uint8,
+                     device=dev)
+
+    def step():
+        gdn.chunk_fwd(q, k, v, la, be, init_state=S0, cu_seqlens=cu, o=o, final_state=fin, workspace=ws,
+                      out_dtype=odt)
+
+    ms_per_step, ms_med, ms_min = time_steps(step, args.steps, args.warmup)
 
     # per-kernel durations (events recorded by the library around each launch)
     with gdn.profile() as prof:
         for _ in range(args.steps):
             step()
     torch.cuda.synchronize()
-    kernels = {name: {"launches": n, "avg_us": 1e3 * ms / n} for name, (n, ms) in prof.results.items()}
+    kernels = {kn: {"launches": n, "avg_us": 1e3 * ms / n} for kn, (n, ms) in prof.results.items()}
 
     flops = chunk_flops_per_token_head(dk, dv) * B * T * H
-    min_bytes = chunk_min_bytes(B, T, H, dk, dv, B, 2, o.element_size(), False, True)
+    min_bytes = chunk_min_bytes(B, T, H, dk, dv, N, 2, o.element_size(), has_init, True)
     dom = max(kernels, key=lambda n: kernels[n]["avg_us"] * kernels[n]["launches"])
     dom_s = kernels[dom]["avg_us"] * 1e-6
     path_s = ms_per_step * 1e-3
@@ -145,17 +182,20 @@ def run_prefill(args, gdn, W, dev):
         "peak": HBM_PEAK_GBS,
         "unit": "GB/s",
         "frac": min_bytes / dom_s / 1e9 / HBM_PEAK_GBS,
-        "traffic": measured_traffic(dom),
+        "traffic": measured_traffic(dom, name),
         "algorithmic_bytes": min_bytes,
         "mfma_tflops": flops / dom_s / 1e12,
         "mfma_frac": flops / dom_s / 1e12 / MFMA_F16_PEAK_TFLOPS,
         "path_hbm_frac": min_bytes / path_s / 1e9 / HBM_PEAK_GBS,
         "path_mfma_frac": flops / path_s / 1e12 / MFMA_F16_PEAK_TFLOPS,
     }
-    res = {"value": B * T / path_s, "ms_per_step": ms_per_step, "roofline": roofline, "kernels": kernels,
-           "config": {"workload": "prefill", "B": B, "L": T, "H": H, "dk": dk, "dv": dv, "chunk": C,
-                      "in_dtype": "bf16", "out_dtype": args.out_dtype, "init_state": None, "final_state": "fp32"}}
-    del q, k, v, la, be, o, fin, ws
+    cfg = {"workload": name, "B": B, "L": T, "H": H, "dk": dk, "dv": dv, "chunk": C, "in_dtype": "bf16",
+           "out_dtype": out_dtype, "init_state": "fp32" if has_init else None, "final_state": "fp32"}
+    if inp.cu_seqlens is not None:
+        cfg["lengths"] = [int(x) for x in (inp.cu_seqlens[1:] - inp.cu_seqlens[:-1])]
+    res = {"value": B * T / path_s, "unit": "tokens/s", "ms_per_step": ms_per_step, "ms_median": ms_med,
+           "ms_min": ms_min, "roofline": roofline, "kernels": kernels, "config": cfg}
+    del q, k, v, la, be, S0, cu, o, fin, ws
     torch.cuda.empty_cache()
     return res, inp
 
@@ -191,7 +231,7 @@ def run_decode(args, gdn, W, dev):
                    "in_dtype": "bf16", "state": "fp32 in place"},
         "roofline": {"kernel": "gdn_decode_step", "bound": "hbm", "achieved": dbytes / dec_kernel_s / 1e9,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dbytes / dec_kernel_s / 1e9 / HBM_PEAK_GBS,
-                     "traffic": measured_traffic("gdn_decode_step"), "algorithmic_bytes": dbytes, "avg_us": dec_kernel_s * 1e6},
+                     "traffic": measured_traffic("gdn_decode_step", "decode"), "algorithmic_bytes": dbytes, "avg_us": dec_kernel_s * 1e6},
     }
     del state, pool, od
     torch.cuda.empty_cache()
@@ -239,7 +279,7 @@ def run_continuation(args, gdn, W, dev):
                    "tokens": int(T), "lengths": f"{int(lens.min())}..{int(lens.max())}", "in_dtype": "bf16",
                    "out_dtype": "fp32", "state": "fp32, initial and final aliased in place"},
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": nbytes / dom_s / 1e9, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": nbytes / dom_s / 1e9 / HBM_PEAK_GBS, "traffic": measured_traffic(dom),
+                     "unit": "GB/s", "frac": nbytes / dom_s / 1e9 / HBM_PEAK_GBS, "traffic": measured_traffic(dom, "continuation"),
                      "algorithmic_bytes": nbytes, "path_hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
         "kernels": kernels,
     }
@@ -291,7 +331,7 @@ def run_backward(args, gdn, W, dev):
         "roofline": {"kernel": "gdn_bwd_grad", "bound": "mfma", "achieved": gflops / g_s / 1e12,
                      "peak": MFMA_F32_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": gflops / g_s / 1e12 / MFMA_F32_PEAK_TFLOPS,
-                     "traffic": measured_traffic("gdn_bwd_grad"), "algorithmic_flops": gflops,
+                     "traffic": measured_traffic("gdn_bwd_grad", "backward"), "algorithmic_flops": gflops,
                      "dominant_kernel": dom},
         "kernels": kernels,
     }
@@ -300,33 +340,49 @@ def run_backward(args, gdn, W, dev):
     return res
 
 
-def run_cpu_baseline(args, inp):
-    """The fp64 oracle on the prefill workload's inputs: a prefix of every sequence, grown until one
-    pass takes about --cpu-seconds; once the prefix is the whole workload, whole passes are repeated
-    until the total reaches --cpu-seconds."""
+def run_cpu_baseline(inp, seconds):
+    """The fp64 oracle on a workload's inputs, on all host cores: a prefix of every sequence, grown until
+    one pass takes about `seconds`; once the prefix is the whole workload, whole passes are repeated
+    until the total reaches `seconds`.  Packed batches are cut per sequence (the same prefix length of
+    each, capped at its own length)."""
+    import numpy as np
+
     import oracle
     threads = oracle.num_threads()
-    B, T, H = inp.B, inp.T, inp.H
+    H = inp.H
+    bounds = inp.seq_bounds()
+    longest = max(e - s for _, s, e in bounds)
 
     def one(sl):
+        # the sample is cut and widened to fp64 outside the timed region
+        if inp.cu_seqlens is None:
+            idx, cu = np.arange(sl), None
+        else:
+            idx = np.concatenate([np.arange(s, min(e, s + sl)) for _, s, e in bounds])
+            cu = np.concatenate([[0], np.cumsum([min(e - s, sl) for _, s, e in bounds])])
+        args = [np.ascontiguousarray(x[:, idx], dtype=np.float64)
+                for x in (inp.q, inp.k, inp.v, inp.log_alpha, inp.beta)]
         t0 = time.perf_counter()
-        oracle.recurrent(inp.q[:, :sl], inp.k[:, :sl], inp.v[:, :sl], inp.log_alpha[:, :sl], inp.beta[:, :sl],
-                         threads=threads)
-        return time.perf_counter() - t0
+        oracle.recurrent(*args, init_state=inp.init_state, cu_seqlens=cu, threads=threads)
+        return time.perf_counter() - t0, inp.B * len(idx)
 
     sl = 64
     while True:
-        el = one(sl)
-        if el >= args.cpu_seconds or sl >= T:
+        el, ntok = one(sl)
+        if el >= seconds or sl >= longest:
             break
-        sl = min(T, max(sl * 2, int(sl * args.cpu_seconds / max(el, 1e-3) * 1.1)))
-    passes = 1
-    while el < args.cpu_seconds:
-        el += one(sl)
+        sl = min(longest, max(sl * 2, int(sl * seconds / max(el, 1e-3) * 1.1)))
+    passes, total = 1, ntok
+    while el < seconds:
+        dt, n = one(sl)
+        el += dt
+        total += n
         passes += 1
-    return {"value": passes * B * sl / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"prefill workload, first {sl} of {T} tokens of each of the {B} sequences, all {H} heads, "
-                      f"{passes} pass(es) (fp64 token recurrence, {el:.1f} s)"}
+    what = (f"first {sl} of {inp.T} tokens of each of the {inp.B} sequences" if inp.cu_seqlens is None else
+            f"first min({sl}, length) tokens of each of the {len(bounds)} packed sequences ({ntok} of {inp.T})")
+    return {"value": total / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{inp.name} workload, {what}, all {H} heads, {passes} pass(es) "
+                      f"(fp64 token recurrence, {el:.1f} s)"}
 
 
 def main():
@@ -337,9 +393,10 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--out-dtype", choices=["fp32", "bf16"], default="fp32",
+    ap.add_argument("--out-dtype", choices=["fp32", "bf16", "fp16"], default="fp32",
                     help="prefill output dtype (the state is fp32 either way)")
-    ap.add_argument("--only", choices=["prefill", "decode", "continuation", "backward", "copy"], default=None,
+    ap.add_argument("--only", choices=["prefill", "long", "packed", "decode", "continuation", "backward", "copy"],
+                    default=None,
                     help="run one leg only (for profiler runs) and print its part of the line; "
                          "'copy' runs a plain 256 MiB read + 256 MiB write elementwise kernel used to "
                          "calibrate the FETCH_SIZE / WRITE_SIZE counters")
@@ -388,14 +445,27 @@ def main():
         print(json.dumps({"copy": {"bytes_read": 4 * n, "bytes_written": 4 * n, "launches": launches + 1,
                                    "avg_us": us, "GB/s": 8 * n / us / 1e3}}), flush=True)
         return
-    pre, inp = run_prefill(args, gdn, W, dev)
-    if args.only == "prefill":
-        print(json.dumps({"prefill": pre}), flush=True)
+    legs = {}
+    for name in ("prefill", "long", "packed"):
+        if args.only not in (None, name):
+            continue
+        legs[name] = run_chunk_workload(args, gdn, W, dev, name, args.out_dtype)
+    if args.only is not None:
+        res = legs[args.only][0]
+        print(json.dumps({args.only: res}), flush=True)
         return
+    pre, inp = legs["prefill"]
     decode = run_decode(args, gdn, W, dev)
     cont = run_continuation(args, gdn, W, dev)
     bwd = run_backward(args, gdn, W, dev)
-    cpu = None if args.no_cpu_baseline else run_cpu_baseline(args, inp)
+    cpu = None if args.no_cpu_baseline else run_cpu_baseline(inp, args.cpu_seconds)
+    extra = {}
+    for name in ("long", "packed"):
+        res, winp = legs[name]
+        if not args.no_cpu_baseline:
+            res["cpu_baseline"] = run_cpu_baseline(winp, args.cpu_seconds / 3)
+        extra[name] = res
+    del legs, inp
     out = {
         "metric": METRIC,
         "value": pre["value"],
@@ -404,6 +474,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": pre["ms_per_step"],
+        "ms_median": pre["ms_median"],
+        "ms_min": pre["ms_min"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -413,6 +485,8 @@ def main():
         "config": pre["config"],
         "roofline": pre["roofline"],
         "cpu_baseline": cpu,
+        "long": extra["long"],
+        "packed": extra["packed"],
         "decode": decode,
         "continuation": cont,
         "backward": bwd,

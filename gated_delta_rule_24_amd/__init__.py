@@ -18,8 +18,8 @@ from typing import Optional
 
 import torch
 
-__all__ = ["GdnError", "chunk_fwd", "decode_step", "chunk_fwd_workspace_size", "chunk_fwd_check",
-           "load", "lib_path", "profile", "CHUNK"]
+__all__ = ["GdnError", "chunk_fwd", "decode_step", "chunk_bwd", "chunk_fwd_workspace_size",
+           "chunk_bwd_workspace_size", "chunk_fwd_check", "load", "lib_path", "profile", "CHUNK"]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CHUNK = 64

@@ -47,7 +47,10 @@
  *     computed as given); q and k normalised upstream (the paper normalises
  *     them in the token-mixing block, section 3.4).  With 16-bit inputs the
  *     matrix-core operands are fp16, so |q|, |k|, |v| and the state entries
- *     must stay below 65504.
+ *     must stay below 65504.  Outside that range nothing reports an error:
+ *     bf16 q, k and v reach their fp16 operands through a round-toward-zero
+ *     conversion and saturate silently at +-65504, and a state entry that is
+ *     rounded to an fp16 operand (round to nearest) becomes infinite.
  */
 #ifndef GDN_H
 #define GDN_H
@@ -89,7 +92,7 @@ typedef enum {
  *   GDN_QK_L2NORM  q and k are L2-normalised per (token, head) inside the
  *                  kernels, q / ||q||_2 and k / ||k||_2, as the Gated
  *                  DeltaNet paper's token-mixing block does before the delta
- *                  rule (section 3.3, "Token mixer block"; the paper notes
+ *                  rule (section 3.4, "Token mixer block"; the paper notes
  *                  list it for training stability).  The input buffers are
  *                  not modified.  An all-zero vector stays zero.
  */

@@ -11,9 +11,9 @@ Functions:
                       brute force on tiny inputs
   chunked(...)        the chunkwise WY/UT form in numpy fp64, exposing the
                       per-chunk intermediates (see oracle/chunked.py)
-  step_strict(...)    one token with the input checks of the tutorial's
-                      reference step function (shape, finiteness, gates in
-                      [0, 1], unit key)
+  checked_step(...)   one token on a single head with the method's
+                      preconditions enforced (shapes, finite entries, gates
+                      in [0, 1], unit key)
   l2_normalise(x)     x / ||x||_2 per vector (fp64), the q/k normalisation of
                       the paper's token-mixer block; recurrent(...,
                       qk_l2norm=True) applies it to q and k first
@@ -112,7 +112,7 @@ def _flatten(q, k, v, log_alpha, beta, cu_seqlens):
 
 def l2_normalise(x):
     """x / ||x||_2 over the last axis, in fp64.  The Gated DeltaNet paper
-    L2-normalises q and k before the gated delta rule (section 3.3, token
+    L2-normalises q and k before the gated delta rule (section 3.4, token
     mixer block; the paper notes list it for training stability).  The pages
     give no epsilon; an all-zero vector is left as zero."""
     x = _f64(x)
@@ -204,31 +204,45 @@ chunked = _chunked_mod.chunked
 chunked_single = _chunked_mod.chunked_single
 
 
-def step_strict(state, key, value, decay, write):
-    """One gated-delta step on plain nested lists, with the input checks the
-    tutorial's reference step function applies (it raises ValueError on an
-    empty or mismatched shape, non-finite entries, gates outside [0, 1] and a
-    key that is not unit length within 1e-9).  Returns the new state (lists).
+def _step_violations(S, k, v, alpha, beta, unit_tol):
+    """The preconditions of one gated-delta step on a single head, as
+    (violated?, reason) pairs in the order they are checked.  Later entries
+    assume the earlier ones hold (shapes before values)."""
+    yield (S.ndim != 2 or S.size == 0 or k.ndim != 1 or v.ndim != 1,
+           "the state must be a non-empty dv x dk matrix, key and value vectors")
+    yield (S.shape != (v.shape[0], k.shape[0]),
+           f"state shape {S.shape} does not match (len(value), len(key)) = {(v.shape[0], k.shape[0])}")
+    yield (not (np.isfinite(S).all() and np.isfinite(k).all() and np.isfinite(v).all()
+                and np.isfinite([alpha, beta]).all()),
+           "every entry must be finite")
+    yield (not (0.0 <= alpha <= 1.0) or not (0.0 <= beta <= 1.0),
+           f"gate alpha = {alpha} and write strength beta = {beta} must lie in [0, 1]")
+    yield (abs(float(np.linalg.norm(k)) - 1.0) > unit_tol,
+           f"the key must have unit L2 norm (got {float(np.linalg.norm(k)):.12g})")
 
-    The arithmetic goes through the C recurrence (one token, fp64); only the
-    checks are done here.
+
+def checked_step(S, k, v, alpha, beta, unit_tol=1e-9):
+    """One token of the gated delta rule, S_t = alpha S (I - beta k k^T) +
+    beta v k^T (the Gated DeltaNet paper's eq. (10), section 3.1), on a
+    single head with its preconditions enforced: ValueError if the state is
+    not a non-empty dv x dk matrix matching len(v) x len(k), if anything is
+    not finite, if alpha or beta leaves [0, 1] (the gate and write strength,
+    section 2.2 and 3.1), or if k is not a unit vector within `unit_tol` (the
+    token-mixer block L2-normalises keys before the rule, section 3.4).
+
+    S: (dv, dk) array-like, k: (dk,), v: (dv,).  Returns the new state as a
+    float64 (dv, dk) array.  The arithmetic is the C recurrence (one token,
+    fp64); only the checks live here.
     """
-    if not key or not state or len(state) != len(value):
-        raise ValueError("invalid state, key or value shape")
-    if any(len(row) != len(key) for row in state):
-        raise ValueError("state rows must match the key dimension")
-    scalars = [decay, write, *key, *value, *(x for row in state for x in row)]
-    if any(not math.isfinite(float(x)) for x in scalars):
-        raise ValueError("inputs must be finite")
-    if not (0.0 <= decay <= 1.0 and 0.0 <= write <= 1.0):
-        raise ValueError("gates must lie in [0, 1]")
-    if not math.isclose(sum(float(x) * float(x) for x in key), 1.0, abs_tol=1e-9):
-        raise ValueError("key must be unit length")
-    dv, dk = len(state), len(key)
-    S0 = np.asarray(state, dtype=np.float64).reshape(1, 1, dv, dk)
-    kk = np.asarray(key, dtype=np.float64).reshape(1, 1, 1, dk)
-    vv = np.asarray(value, dtype=np.float64).reshape(1, 1, 1, dv)
-    la = np.full((1, 1, 1), -np.inf if decay == 0.0 else math.log(decay))
-    bb = np.full((1, 1, 1), float(write))
-    _, fin = recurrent(np.zeros_like(kk), kk, vv, la, bb, init_state=S0)
-    return fin[0, 0].tolist()
+    S = np.asarray(S, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    alpha, beta = float(alpha), float(beta)
+    for bad, reason in _step_violations(S, k, v, alpha, beta, unit_tol):
+        if bad:
+            raise ValueError(reason)
+    dv, dk = S.shape
+    la = np.full((1, 1, 1), -np.inf if alpha == 0.0 else math.log(alpha))
+    _, fin = recurrent(np.zeros((1, 1, 1, dk)), k.reshape(1, 1, 1, dk), v.reshape(1, 1, 1, dv), la,
+                       np.full((1, 1, 1), beta), init_state=S.reshape(1, 1, dv, dk))
+    return fin[0, 0]

@@ -19,6 +19,12 @@ import oracle
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
 
+def golden():
+    """The tutorial's worked two-cell example and its printed results (tests/golden/)."""
+    with open(os.path.join(GOLDEN, "worked_example.json")) as fh:
+        return json.load(fh)
+
+
 def _unit(x):
     return x / np.linalg.norm(x, axis=-1, keepdims=True)
 

@@ -1,6 +1,6 @@
 """GPU parity of the fused q/k L2 normalisation (GDN_QK_L2NORM): the HIP path
 on q and k of arbitrary per-token lengths against the fp64 oracle that
-normalises them first (paper section 3.3, token mixer block)."""
+normalises them first (paper section 3.4, token mixer block)."""
 import numpy as np
 import pytest
 import torch

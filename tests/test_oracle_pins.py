@@ -26,9 +26,11 @@ def test_pin(lib, pin):
     pin(lib)
 
 
-def test_strict_step_matches_worked_example():
-    assert oracle.step_strict([[2.0, 10.0]], [1.0, 0.0], [6.0], 0.5, 0.25) == [[2.25, 5.0]]
-    assert oracle.step_strict([[2.0, 10.0]], [1.0, 0.0], [6.0], 1.0, 1.0) == [[6.0, 10.0]]
+def test_checked_step_matches_worked_example():
+    # tests/golden/worked_example.json: the tutorial's two-cell example and its two printed results
+    for case in pins.golden()["cases"]:
+        got = oracle.checked_step(case["state"], case["key"], case["value"], case["alpha"], case["beta"])
+        assert np.array_equal(got, np.array(case["expected"]))
 
 
 @pytest.mark.parametrize("args", [
@@ -36,21 +38,23 @@ def test_strict_step_matches_worked_example():
     ([[1.0, 2.0]], [], [1.0], 0.5, 0.5),               # empty key
     ([[1.0, 2.0]], [1.0, 0.0], [1.0, 2.0], 0.5, 0.5),  # value/state rows mismatch
     ([[1.0, 2.0, 3.0]], [1.0, 0.0], [1.0], 0.5, 0.5),  # row length != key length
+    ([1.0, 2.0], [1.0, 0.0], [1.0], 0.5, 0.5),         # state not a matrix
     ([[float("nan"), 2.0]], [1.0, 0.0], [1.0], 0.5, 0.5),
     ([[1.0, 2.0]], [1.0, 0.0], [float("inf")], 0.5, 0.5),
+    ([[1.0, 2.0]], [1.0, 0.0], [1.0], float("nan"), 0.5),
     ([[1.0, 2.0]], [1.0, 0.0], [1.0], 1.5, 0.5),       # decay outside [0, 1]
     ([[1.0, 2.0]], [1.0, 0.0], [1.0], 0.5, -0.1),      # write outside [0, 1]
     ([[1.0, 2.0]], [1.0, 1.0], [1.0], 0.5, 0.5),       # key not unit
 ])
-def test_strict_step_rejects(args):
+def test_checked_step_rejects(args):
     with pytest.raises(ValueError):
-        oracle.step_strict(*args)
+        oracle.checked_step(*args)
 
 
-def test_strict_step_endpoints():
+def test_checked_step_endpoints():
     # alpha = 0 wipes the memory before the write; beta = 0 only decays.
-    assert oracle.step_strict([[2.0, 10.0]], [1.0, 0.0], [6.0], 0.0, 0.25) == [[1.5, 0.0]]
-    assert oracle.step_strict([[2.0, 10.0]], [0.0, 1.0], [6.0], 0.5, 0.0) == [[1.0, 5.0]]
+    assert np.array_equal(oracle.checked_step([[2.0, 10.0]], [1.0, 0.0], [6.0], 0.0, 0.25), [[1.5, 0.0]])
+    assert np.array_equal(oracle.checked_step([[2.0, 10.0]], [0.0, 1.0], [6.0], 0.5, 0.0), [[1.0, 5.0]])
 
 
 def test_malformed_cu_rejected(lib):
