@@ -148,9 +148,9 @@ gdn_status gdn_chunk_fwd_workspace_size(const gdn_chunk_desc *desc, size_t *byte
     // Size for the larger of the packed and batched layouts, so the answer
     // does not depend on whether cu_seqlens is passed later.
     const auto a = gdn::chunk_workspace_layout(desc->batch, desc->seqlen, desc->num_seqs, true,
-                                               desc->heads, desc->in_dtype);
+                                               desc->heads, desc->in_dtype, desc->dk, desc->dv);
     const auto b = gdn::chunk_workspace_layout(desc->batch, desc->seqlen, desc->num_seqs, false,
-                                               desc->heads, desc->in_dtype);
+                                               desc->heads, desc->in_dtype, desc->dk, desc->dv);
     *bytes = a.total > b.total ? a.total : b.total;
     return ok();
 }
@@ -170,7 +170,8 @@ gdn_status gdn_chunk_fwd(const gdn_chunk_desc *desc, const void *q, const void *
     if (toks > 0 && (!q || !k || !v || !log_alpha || !beta || !o))
         return fail(GDN_ERR_NULL, "q, k, v, log_alpha, beta and o are required");
     if (!workspace) return fail(GDN_ERR_WORKSPACE, "workspace is NULL");
-    const auto w = gdn::chunk_workspace_layout(d.batch, d.seqlen, d.num_seqs, packed, d.heads, d.in_dtype);
+    const auto w = gdn::chunk_workspace_layout(d.batch, d.seqlen, d.num_seqs, packed, d.heads, d.in_dtype, d.dk,
+                                               d.dv);
     if (workspace_bytes < w.total)
         return fail(GDN_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, w.total);
     const void *ptrs[] = {q, k, v, init_state, o, final_state, workspace};

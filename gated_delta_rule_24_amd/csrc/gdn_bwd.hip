@@ -1739,7 +1739,7 @@ static size_t bwd_align256(size_t x) { return (x + 255) & ~(size_t)255; }
 BwdWorkspace chunk_bwd_workspace_layout(int32_t B, int32_t T, int32_t N, bool packed, int32_t H, int32_t dk,
                                         int32_t dv) {
     BwdWorkspace w{};
-    w.fwd = chunk_workspace_layout(B, T, N, packed, H, DT_FP32);
+    w.fwd = chunk_workspace_layout(B, T, N, packed, H, DT_FP32, dk, dv);
     const size_t items = (size_t)w.fwd.max_rows * H;
     size_t off = bwd_align256(w.fwd.off_g);   // only the table part of the forward layout is used
     w.off_t = off;   off = bwd_align256(off + sizeof(float) * items * C * C);
@@ -1764,7 +1764,8 @@ hipError_t launch_chunk_bwd(const ChunkArgs &a, const BwdArgs &g, hipStream_t st
                                           reinterpret_cast<int32_t *>(ws + w.fwd.off_cu),
                                           reinterpret_cast<int32_t *>(ws + w.fwd.off_row0),
                                           reinterpret_cast<int32_t *>(ws + w.fwd.off_rowtok),
-                                          reinterpret_cast<int32_t *>(ws + w.fwd.off_rowlen), st);
+                                          reinterpret_cast<int32_t *>(ws + w.fwd.off_rowlen), 0, nullptr, nullptr,
+                                          nullptr, st);
         if (e != hipSuccess) return e;
     }
     switch (a.in_dtype) {

@@ -49,6 +49,8 @@
 
 #include <stdlib.h>
 
+#include <algorithm>
+
 namespace gdn {
 
 constexpr int C = kChunk;
@@ -78,27 +80,58 @@ __device__ __forceinline__ void lds_store8(OP *p, const float (&x)[8]) {
 
 // ============================================================================
 // G0: chunk table of a packed batch (cu_seqlens given).
-//   meta[0] = number of rows, meta[1] = cu_seqlens error code (0 = valid)
+//   meta[0] = number of rows, meta[1] = cu_seqlens error code (0 = valid),
+//   meta[2] = number of segment units (segmented state pass only)
 //   cu_ws[N+1] = token offsets, row0[N] = first row of each sequence,
 //   row_tok / row_len = token start and length of each row.
+// With seg_chunks > 0 each sequence's chunks are also cut into segments of
+// seg_chunks chunks (at least one segment, so an empty sequence still carries
+// its initial state to its final state): seg_first[n] / seg_cnt[n] = first
+// unit and unit count of sequence n, seg_tab[2u], seg_tab[2u + 1] = (n, s).
 // A batch of equal-length sequences needs no table: G1 and G2 derive a row's
 // span from its index (row_span, gdn_launch.h) and G0 is not launched.
 // ============================================================================
-__global__ __launch_bounds__(256) void chunk_table_kernel(int N, int T,
-                                                          const int32_t *__restrict__ cu_in,
+
+// Exclusive prefix sums of cnt(n), n < N, into out[n] by one 256-thread block;
+// returns the total.  Every thread of the block must call it.
+template <typename F>
+__device__ int block_exclusive_scan(int N, F cnt, int32_t *__restrict__ out, int *s_scan, int *s_offset) {
+    const int tid = threadIdx.x;
+    if (tid == 0) *s_offset = 0;
+    __syncthreads();
+    for (int base = 0; base < N; base += 256) {
+        const int n = base + tid;
+        const int c = n < N ? cnt(n) : 0;
+        s_scan[tid] = c;
+        __syncthreads();
+        for (int off = 1; off < 256; off <<= 1) {
+            const int x = tid >= off ? s_scan[tid - off] : 0;
+            __syncthreads();
+            s_scan[tid] += x;
+            __syncthreads();
+        }
+        if (n < N) out[n] = *s_offset + s_scan[tid] - c;
+        __syncthreads();
+        if (tid == 0) *s_offset += s_scan[255];
+        __syncthreads();
+    }
+    return *s_offset;
+}
+
+__global__ __launch_bounds__(256) void chunk_table_kernel(int N, int T, const int32_t *__restrict__ cu_in,
                                                           int32_t *__restrict__ meta,
                                                           int32_t *__restrict__ cu_ws,
                                                           int32_t *__restrict__ row0,
                                                           int32_t *__restrict__ row_tok,
-                                                          int32_t *__restrict__ row_len) {
+                                                          int32_t *__restrict__ row_len, int seg_chunks,
+                                                          int32_t *__restrict__ seg_first,
+                                                          int32_t *__restrict__ seg_cnt,
+                                                          int32_t *__restrict__ seg_tab) {
     __shared__ int s_code;
     __shared__ int s_scan[256];
     __shared__ int s_offset;
     const int tid = threadIdx.x;
-    if (tid == 0) {
-        s_code = 0;
-        s_offset = 0;
-    }
+    if (tid == 0) s_code = 0;
     __syncthreads();
     for (int n = tid; n <= N; n += 256) {
         const int val = cu_in[n];
@@ -113,31 +146,29 @@ __global__ __launch_bounds__(256) void chunk_table_kernel(int N, int T,
         if (tid == 0) {
             meta[0] = 0;
             meta[1] = (code & 1) ? 1 : ((code & 2) ? 2 : 3);
+            meta[2] = 0;
         }
         return;
     }
-    for (int base = 0; base < N; base += 256) {
-        const int n = base + tid;
-        int cnt = 0;
-        if (n < N) {
-            cnt = (cu_in[n + 1] - cu_in[n] + C - 1) / C;
+    auto chunks = [&](int n) { return (cu_in[n + 1] - cu_in[n] + C - 1) / C; };
+    const int rows = block_exclusive_scan(N, chunks, row0, s_scan, &s_offset);
+    int units = 0;
+    if (seg_chunks > 0) {
+        auto segs = [&](int n) { return max(1, (chunks(n) + seg_chunks - 1) / seg_chunks); };
+        units = block_exclusive_scan(N, segs, seg_first, s_scan, &s_offset);
+        for (int n = tid; n < N; n += 256) {
+            const int ns = segs(n), u0 = seg_first[n];
+            seg_cnt[n] = ns;
+            for (int j = 0; j < ns; ++j) {
+                seg_tab[2 * (u0 + j)] = n;
+                seg_tab[2 * (u0 + j) + 1] = j;
+            }
         }
-        s_scan[tid] = cnt;
-        __syncthreads();
-        for (int off = 1; off < 256; off <<= 1) {
-            const int x = tid >= off ? s_scan[tid - off] : 0;
-            __syncthreads();
-            s_scan[tid] += x;
-            __syncthreads();
-        }
-        if (n < N) row0[n] = s_offset + s_scan[tid] - cnt;
-        __syncthreads();
-        if (tid == 0) s_offset += s_scan[255];
-        __syncthreads();
     }
     if (tid == 0) {
-        meta[0] = s_offset;
+        meta[0] = rows;
         meta[1] = 0;
+        meta[2] = units;
     }
     for (int n = tid; n < N; n += 256) {
         const int s0 = cu_in[n], s1 = cu_in[n + 1];
@@ -542,7 +573,7 @@ __global__ __launch_bounds__(64) void chunk_prep_kernel(int H, int T, int cpr, i
 // Waves of a state-pass block that stage inputs (the others compute).
 constexpr int kStagers = 4;
 
-template <typename in_t, typename OP, int DK, int NW>
+template <typename in_t, typename OP, int DK, int NW, bool OUT>
 struct StateSmem {
     static constexpr int BV = 16 * NW;                                  // value columns per block
     static constexpr int QROW = DK * (int)sizeof(OP) + 32;              // bytes per Q / K row
@@ -550,19 +581,32 @@ struct StateSmem {
     static constexpr int VUNITS = VROW / 16;                            // 16-byte units per V row
     static constexpr int VSWZ = VUNITS >= 8 ? 7 : VUNITS - 1;           // unit XOR mask (row bits)
     static constexpr size_t QK = (size_t)C * QROW;                      // one Q or K block
+    static constexpr int NQK = OUT ? 2 : 1;                             // Q and K, or K alone
     static constexpr size_t VB = (size_t)C * VROW;
     static constexpr size_t MP = sizeof(OP) * kTriTiles * kTileElems;   // one M or P block
+    static constexpr int NMP = OUT ? 2 : 1;                             // M and P, or M alone
     static constexpr size_t GB = 1024;                                  // the four decay vectors
-    static constexpr size_t DMA = VB + 2 * MP + GB;                     // directly loaded inputs
-    static constexpr int QKB = (4 * QK + 2 * DMA <= 160 * 1024) ? 2 : 1;   // Q/K buffers
-    static constexpr size_t qk_off(int b) { return (size_t)b * 2 * QK; }   // Q, then K
-    static constexpr size_t dma_off(int b) { return (size_t)QKB * 2 * QK + (size_t)b * DMA; }
-    static constexpr size_t m_rel = VB, p_rel = VB + MP, g_rel = VB + 2 * MP;
-    static constexpr size_t bytes = (size_t)QKB * 2 * QK + 2 * DMA;
+    static constexpr size_t DMA = VB + NMP * MP + GB;                   // directly loaded inputs
+    static constexpr int QKB = (2 * NQK * QK + 2 * DMA <= 160 * 1024) ? 2 : 1;   // Q/K buffers
+    static constexpr size_t qk_off(int b) { return (size_t)b * NQK * QK; }       // Q (if any), then K
+    static constexpr size_t k_rel = OUT ? QK : 0;
+    static constexpr size_t dma_off(int b) { return (size_t)QKB * NQK * QK + (size_t)b * DMA; }
+    static constexpr size_t m_rel = VB, p_rel = VB + MP, g_rel = VB + NMP * MP;
+    static constexpr size_t bytes = (size_t)QKB * NQK * QK + 2 * DMA;
     static constexpr int NV = (int)(VB / 1024), NM = (int)(MP / 1024);
-    static constexpr int NDMA = NV + 2 * NM + 1;                         // 1 KiB wave copies per chunk
+    static constexpr int NDMA = NV + NMP * NM + 1;                       // 1 KiB wave copies per chunk
     static_assert(VB % 1024 == 0 && MP % 1024 == 0, "direct loads move whole 1 KiB wave blocks");
     static_assert(QROW % 16 == 0 && VROW % 16 == 0, "16-byte rows");
+};
+
+// Segmentation of the state pass (see the launcher): chunks per segment
+// (0 = whole sequences), segments per sequence of an equal-length batch, the
+// packed batch's unit tables, and the two per-unit state buffers.
+struct SegArgs {
+    int seg_chunks, nsegc;
+    const int32_t *seg_cnt, *seg_tab;
+    float *ws_end;          // per (unit, head): (DV + DK) x DK, the segment's map from zero / identity
+    float *ws_sin;          // per (unit, head): DV x DK, the state entering the segment
 };
 
 
@@ -636,17 +680,17 @@ __device__ __forceinline__ void dma16(const void *g, uint32_t lds) {
         : "memory");
 }
 
-template <typename in_t, typename OP, int DK, int NW>
+template <typename in_t, typename OP, int DK, int NW, bool OUT>
 __global__ __launch_bounds__(64 * (NW + kStagers)) void chunk_state_kernel(
-    int NH, int H, int DV, int nvt, int odt, int T, int cpr, int32_t *__restrict__ meta,
-    const int32_t *__restrict__ cu_ws, const int32_t *__restrict__ row0,
+    int NU, int H, int DV, int nvt, int odt, int T, int cpr, int32_t *__restrict__ meta,
+    const int32_t *__restrict__ cu_ws, const int32_t *__restrict__ row0, SegArgs sg,
     const in_t *__restrict__ q, const in_t *__restrict__ k, const in_t *__restrict__ v,
     const float *__restrict__ ws_g, const OP *__restrict__ ws_m, const OP *__restrict__ ws_p,
     const float *init_state, float *final_state, void *__restrict__ o) {
     using M = Mma<OP>;
     using frag = typename M::frag;
     using F2 = Frag2<OP>;
-    using L = StateSmem<in_t, OP, DK, NW>;
+    using L = StateSmem<in_t, OP, DK, NW, OUT>;
     constexpr int QROW = L::QROW, VROW = L::VROW, BV = L::BV, QKB = L::QKB;
     constexpr int NT = 64 * kStagers;                        // staging threads
     constexpr int KT = DK / 16;                              // state tiles along dk
@@ -660,28 +704,56 @@ __global__ __launch_bounds__(64 * (NW + kStagers)) void chunk_state_kernel(
     if (cpr) {
         // Equal-length batch: no table pass ran, so report its row count and
         // a clean status for the host-side check here.
-        if (blockIdx.x == 0 && threadIdx.x == 0) {
-            meta[0] = (NH / H) * ((T + C - 1) / C);
+        if (OUT && blockIdx.x == 0 && threadIdx.x == 0) {
+            meta[0] = (int)((int64_t)NU / H / (sg.seg_chunks ? sg.nsegc : 1)) * ((T + C - 1) / C);
             meta[1] = 0;
         }
     } else if (meta[1] != 0) {
         return;
     }
+    // Block -> (unit, value tile).  A unit is one (sequence, segment, head);
+    // the blocks of a unit sit on one XCD (workgroups go to the 8 XCDs
+    // round-robin by block id) so they share its Q, K, M, P lines in L2.
     const int bid = blockIdx.x, xcd = bid & 7, slot = bid >> 3;
-    const int chain = (slot / nvt) * 8 + xcd, vt = slot % nvt;
-    if (chain >= NH) return;
-    const int n = chain / H, h = chain % H;
+    const int unit = (slot / nvt) * 8 + xcd, vt = slot % nvt;
+    if (unit >= NU) return;
+    const int useg = unit / H, h = unit % H;
+    int n, seg, nseg;   // sequence, segment within it, its segment count
+    if (sg.seg_chunks == 0) {
+        n = useg, seg = 0, nseg = 1;
+    } else if (cpr) {
+        n = useg / sg.nsegc, seg = useg - n * sg.nsegc, nseg = sg.nsegc;
+    } else {
+        if (useg >= meta[2]) return;
+        n = sg.seg_tab[2 * useg], seg = sg.seg_tab[2 * useg + 1], nseg = sg.seg_cnt[n];
+    }
+    // The transition of a sequence's last segment is never needed.
+    if (!OUT && seg == nseg - 1) return;
+    // Columns of the running state: the value columns, and for a transition
+    // pass over a segment after the first, DK more that start as the
+    // identity and see zero values (they carry the segment's map F).
+    const int DVA = (!OUT && seg > 0) ? DV + DK : DV;
+    const int vb = vt * BV;                 // first value column of the block
+    if (vb >= DVA) return;
+    const int chain = n * H + h;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, nn = l & 15, jj = l >> 4;
     // Waves 0..NW-1 compute (16 value columns each); the kStagers waves after
     // them stage the next chunk's inputs into LDS.
     const bool stager = w >= NW;
     const int sw = w - NW, stid = tid - 64 * NW;  // stager wave / thread index
-    const int vb = vt * BV;                 // first value column of the block
     const int v0 = vb + w * 16;             // first value column of a compute wave
-    const bool active = !stager && v0 < DV;
-    const int tok0 = cpr ? n * T : cu_ws[n];
-    const int len_seq = cpr ? T : cu_ws[n + 1] - tok0;
-    const int r0 = cpr ? n * cpr : row0[n];
+    const bool active = !stager && v0 < DVA;
+    const bool ident = v0 >= DV;            // a column of F (transition pass only)
+    // The chunks this block runs: all of the sequence's, or one segment.
+    int tok0 = cpr ? n * T : cu_ws[n];
+    int len_seq = cpr ? T : cu_ws[n + 1] - tok0;
+    int r0 = cpr ? n * cpr : row0[n];
+    if (sg.seg_chunks) {
+        const int cb = seg * sg.seg_chunks;
+        tok0 += cb * C;
+        r0 += cb;
+        len_seq = max(0, min(len_seq - cb * C, sg.seg_chunks * C));
+    }
     const int nchunks = (len_seq + C - 1) / C;
 
     // ---- per-lane LDS byte offsets ----
@@ -706,16 +778,31 @@ __global__ __launch_bounds__(64 * (NW + kStagers)) void chunk_state_kernel(
     }
     const int tile_lane = 4 * l;                                    // M / P tiles (elements)
 
-    // S^T tiles in the dk order described above.
+    // S^T tiles in the dk order described above.  The state entering the
+    // block's chunks: the caller's initial state (whole sequences, or the
+    // transition pass over a first segment), the segment's incoming state
+    // from the combine pass (output pass over segments), or zero / identity
+    // (transition pass over a later segment).
     float4_t sT[KT];
-    const int64_t st_base = ((int64_t)chain * DV + v0 + nn) * DK + 8 * jj;
+    const float *s_in = nullptr;
+    int64_t s_in_row = 0;   // element offset of the lane's state row
+    if (OUT && sg.seg_chunks) {
+        s_in = sg.ws_sin;
+        s_in_row = ((int64_t)unit * DV + v0 + nn) * DK;
+    } else if (seg == 0) {
+        s_in = init_state;
+        s_in_row = ((int64_t)chain * DV + v0 + nn) * DK;
+    }
 #pragma unroll
     for (int t = 0; t < KT; ++t) {
         const int off = 32 * (t >> 1) + 4 * (t & 1);
-        if (active && init_state)
-            sT[t] = *reinterpret_cast<const float4_t *>(init_state + st_base + off);
-        else
-            sT[t] = float4_t{0.f, 0.f, 0.f, 0.f};
+        if (active && s_in && !ident) {
+            sT[t] = *reinterpret_cast<const float4_t *>(s_in + s_in_row + 8 * jj + off);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)   // S^T[d][c] = [d == c - DV] on identity columns
+                sT[t][i] = (active && ident && 8 * jj + off + i == v0 + nn - DV) ? 1.f : 0.f;
+        }
     }
 
     // ---- Q / K register prefetch ----
@@ -743,7 +830,7 @@ __global__ __launch_bounds__(64 * (NW + kStagers)) void chunk_state_kernel(
         if (last == C - 1) {
 #pragma unroll
             for (int it = 0; it < QK_IT; ++it) {
-                R.q[it].load(qc + offq[it]);
+                if constexpr (OUT) R.q[it].load(qc + offq[it]);
                 R.k[it].load(kc + offq[it]);
             }
         } else {
@@ -751,26 +838,28 @@ __global__ __launch_bounds__(64 * (NW + kStagers)) void chunk_state_kernel(
             for (int it = 0; it < QK_IT; ++it) {
                 const int u = (stid + it * NT) % QK_UNITS;
                 const int off = min(u / (DK / 8), last) * rowq + (u % (DK / 8)) * 8;
-                R.q[it].load(qc + off);
+                if constexpr (OUT) R.q[it].load(qc + off);
                 R.k[it].load(kc + off);
             }
         }
     };
     auto commit_qk = [&](int b, int len, QKRegs &R) {
         OP *Qb = reinterpret_cast<OP *>(smem + L::qk_off(b));
-        OP *Kb = reinterpret_cast<OP *>(smem + L::qk_off(b) + L::QK);
+        OP *Kb = reinterpret_cast<OP *>(smem + L::qk_off(b) + L::k_rel);
 #pragma unroll
         for (int it = 0; it < QK_IT; ++it) {
             const int u = stid + it * NT;
             if (u >= QK_UNITS) continue;
             const int r = u / (DK / 8), c8 = (u % (DK / 8)) * 8;
             if (len < C && r >= len) {
-                R.q[it].zero();
+                if constexpr (OUT) R.q[it].zero();
                 R.k[it].zero();
             }
             frag lo, hi;
-            to_op(R.q[it], lo, hi);
-            store_row8(Qb + r * (QROW / OPB) + c8, lo, hi);
+            if constexpr (OUT) {
+                to_op(R.q[it], lo, hi);
+                store_row8(Qb + r * (QROW / OPB) + c8, lo, hi);
+            }
             to_op(R.k[it], lo, hi);
             store_row8(Kb + r * (QROW / OPB) + c8, lo, hi);
         }
@@ -778,10 +867,12 @@ __global__ __launch_bounds__(64 * (NW + kStagers)) void chunk_state_kernel(
     // ---- direct global -> LDS copies of V, M, P and the decay factors ----
     // Copy ii of a chunk (stager wave sw issues ii = sw, sw + kStagers, ...) fills LDS bytes
     // [1024 ii, 1024 ii + 1024) of the chunk's buffer: V blocks first, then
-    // M, P and the 4C decay factors.  Per-lane source offsets do not depend
-    // on the chunk and are computed once.  Rows past the end of a partial
-    // chunk re-read the last valid row: M and P are exactly zero in those
-    // rows and columns, so they stay inert.
+    // M, P (output pass only) and the 4C decay factors.  Per-lane source
+    // offsets do not depend on the chunk and are computed once.  Rows past the
+    // end of a partial chunk re-read the last valid row: M and P are exactly
+    // zero in those rows and columns, so they stay inert.  Columns past DV
+    // (inactive waves, or the F columns of a transition pass, which use zero
+    // values) read column 0 and are not used.
     constexpr int KD = (L::NDMA + kStagers - 1) / kStagers;
     int dsrc[KD];   // V: elements from the chunk's first row; M, P, g: bytes
 #pragma unroll
@@ -791,9 +882,9 @@ __global__ __launch_bounds__(64 * (NW + kStagers)) void chunk_state_kernel(
             const int byte = ii * 1024 + 16 * l;
             const int row = byte / VROW, unit = (byte % VROW) / 16;
             int col = vb + (unit ^ (row & L::VSWZ)) * (16 / (int)sizeof(in_t));
-            if (col >= DV) col = vb;                     // columns of inactive waves
+            if (col >= DV) col = 0;
             dsrc[kx] = row * H * DV + col;
-        } else if (ii < L::NV + 2 * L::NM) {
+        } else if (ii < L::NV + L::NMP * L::NM) {
             dsrc[kx] = ((ii - L::NV) % L::NM) * 1024 + 16 * l;
         } else {
             dsrc[kx] = 16 * l;
@@ -820,7 +911,7 @@ __global__ __launch_bounds__(64 * (NW + kStagers)) void chunk_state_kernel(
                 dma16(vc + off, base + (uint32_t)(ii * 1024));
             } else if (ii < L::NV + L::NM) {
                 dma16(mc + dsrc[kx], base + (uint32_t)(L::m_rel + (ii - L::NV) * 1024));
-            } else if (ii < L::NV + 2 * L::NM) {
+            } else if (OUT && ii < L::NV + 2 * L::NM) {
                 dma16(pc + dsrc[kx], base + (uint32_t)(L::p_rel + (ii - L::NV - L::NM) * 1024));
             } else {
                 dma16(gc + dsrc[kx], base + (uint32_t)L::g_rel);
@@ -897,7 +988,7 @@ __global__ __launch_bounds__(64 * (NW + kStagers)) void chunk_state_kernel(
         if constexpr (QKB == 2) {
 #pragma unroll
             for (int it = 0; it < QK_IT; ++it) {
-                cur.q[it].touch();
+                if constexpr (OUT) cur.q[it].touch();
                 cur.k[it].touch();
             }
             // (near the end the last chunk is loaded again: the register
@@ -910,7 +1001,7 @@ __global__ __launch_bounds__(64 * (NW + kStagers)) void chunk_state_kernel(
         } else {
 #pragma unroll
             for (int it = 0; it < QK_IT; ++it) {
-                cur.q[it].touch();
+                if constexpr (OUT) cur.q[it].touch();
                 cur.k[it].touch();
             }
             prefetch_qk(min(ci + 1, nchunks - 1), nxt);
@@ -926,8 +1017,8 @@ __global__ __launch_bounds__(64 * (NW + kStagers)) void chunk_state_kernel(
         if constexpr (QKB == 1) asm volatile("s_barrier" ::: "memory");
         if (!active) return;
 
-        const unsigned char *Qb = smem + L::qk_off(QKB == 2 ? b : 0);
-        const unsigned char *Kb = Qb + L::QK;
+        const unsigned char *Qb = smem + L::qk_off(QKB == 2 ? b : 0);   // (output pass only)
+        const unsigned char *Kb = Qb + L::k_rel;
         const unsigned char *Db = smem + L::dma_off(b);
         const OP *Ms = reinterpret_cast<const OP *>(Db + L::m_rel);
         const OP *Ps = reinterpret_cast<const OP *>(Db + L::p_rel);
@@ -1005,8 +1096,10 @@ __global__ __launch_bounds__(64 * (NW + kStagers)) void chunk_state_kernel(
         for (int jx = 0; jx < 6; ++jx) mpair[jx] = tri_pair(Ms, PMT[jx], PP[jx]);
         constexpr int NQ1 = NX / 2;                     // Q S^T items before the update
         F2 qf[WQ];
+        if constexpr (OUT) {
 #pragma unroll
-        for (int i = 0; i < WQ; ++i) qf[i] = rd_row(Qb, i);
+            for (int i = 0; i < WQ; ++i) qf[i] = rd_row(Qb, i);
+        }
         __builtin_amdgcn_sched_barrier(0);
 
         // -- phase 2: Y = V - diag(gamma) X_K as B operand --
@@ -1014,7 +1107,8 @@ __global__ __launch_bounds__(64 * (NW + kStagers)) void chunk_state_kernel(
         {
             float4_t y[4];
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) y[mt] = VFrag<in_t>::to_f32(vraw[mt]) - gm[mt] * x[mt];
+            for (int mt = 0; mt < 4; ++mt)   // the F columns of a transition pass see v = 0
+                y[mt] = (ident ? float4_t{0.f, 0.f, 0.f, 0.f} : VFrag<in_t>::to_f32(vraw[mt])) - gm[mt] * x[mt];
             yB[0] = F2::cvt(y[0], y[1]);
             yB[1] = F2::cvt(y[2], y[3]);
         }
@@ -1042,10 +1136,12 @@ __global__ __launch_bounds__(64 * (NW + kStagers)) void chunk_state_kernel(
         float4_t qs[4];
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) qs[rt] = float4_t{0.f, 0.f, 0.f, 0.f};
+        if constexpr (OUT) {
 #pragma unroll
-        for (int i = 0; i < NQ1; ++i) {
-            mma2(qs[i % 4], sB[i / 4], qf[i % WQ]);
-            if (i + WQ < NX) qf[i % WQ] = rd_row(Qb, i + WQ);
+            for (int i = 0; i < NQ1; ++i) {
+                mma2(qs[i % 4], sB[i / 4], qf[i % WQ]);
+                if (i + WQ < NX) qf[i % WQ] = rd_row(Qb, i + WQ);
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
 
@@ -1075,6 +1171,7 @@ __global__ __launch_bounds__(64 * (NW + kStagers)) void chunk_state_kernel(
             }
             if (t >= NT1) mma2(sT[t - NT1], ka[t - NT1][1], dB[1]);
         }
+        if constexpr (!OUT) return;   // a transition pass stops at the update
         F2 ppair[6];
 #pragma unroll
         for (int jx = 0; jx < 6; ++jx) ppair[jx] = tri_pair(Ps, PMT[jx], PP[jx]);
@@ -1131,10 +1228,133 @@ __global__ __launch_bounds__(64 * (NW + kStagers)) void chunk_state_kernel(
     }
     for (int ci = 0; ci < nchunks; ++ci) compute(ci);
 
-    if (active && final_state) {
+    // The state leaving the block's chunks: the sequence's final state (output
+    // pass over its last segment), or the segment's map (transition pass).
+    float *s_out = nullptr;
+    int64_t s_out_row = 0;
+    if (!OUT) {
+        s_out = sg.ws_end;
+        s_out_row = ((int64_t)unit * (DV + DK) + v0 + nn) * DK;
+    } else if (seg == nseg - 1 && final_state) {
+        s_out = final_state;
+        s_out_row = ((int64_t)chain * DV + v0 + nn) * DK;
+    }
+    if (active && s_out) {
 #pragma unroll
         for (int t = 0; t < KT; ++t)
-            *reinterpret_cast<float4_t *>(final_state + st_base + 32 * (t >> 1) + 4 * (t & 1)) = sT[t];
+            *reinterpret_cast<float4_t *>(s_out + s_out_row + 8 * jj + 32 * (t >> 1) + 4 * (t & 1)) = sT[t];
+    }
+}
+
+// ============================================================================
+// Combine pass of a segmented state pass.  Segment s of a sequence maps the
+// state entering it to the state leaving it as S -> S F_s + G_s (every chunk
+// step is affine in S: S_next = S (gamma_C I - K^T diag(gamma) M^T diag(kappa) K)
+// + V^T M^T diag(kappa) K, and a segment composes its chunks' maps).  The
+// transition pass left [G_s; F_s] in ws_end (G_s from a zero state, F_s from
+// the identity through the same chunks with zero values); for the first
+// segment it left the true leaving state.  Per (sequence, head, 16 state
+// rows) this pass walks the segments in order and writes the state entering
+// each one to ws_sin:
+//   S_in(0) = initial state (or 0),  S_in(1) = ws_end(0),
+//   S_in(s + 1) = S_in(s) F_s + G_s.
+// fp32 throughout.  Thread t owns row 16 rt + t / 16 and DK / 16 consecutive
+// columns.  For each product the block's 16 rows of S sit in LDS, and F goes
+// through LDS in slabs of SLAB rows (16-byte loads, all issued before one
+// wait), so each thread's sums read LDS only.
+// ============================================================================
+template <int DK>
+struct CombineSmem {
+    static constexpr int SLAB = DK <= 64 ? DK : 8192 / DK;   // F rows per slab (at most 32 KiB)
+    static constexpr int LD = (SLAB * DK / 4 + 255) / 256;    // 16-byte loads per thread per slab
+};
+
+template <int DK>
+__global__ __launch_bounds__(256) void chunk_combine_kernel(int NSEQ, int H, int DV, int cpr, const int32_t *meta,
+                                                            SegArgs sg, const int32_t *__restrict__ seg_first,
+                                                            const float *init_state) {
+    constexpr int CPT = DK / 16;   // columns per thread
+    using L = CombineSmem<DK>;
+    constexpr int SLAB = L::SLAB;
+    __shared__ __align__(16) float rows[16][DK + 4];
+    __shared__ __align__(16) float fs[SLAB][DK];
+    const int nrt = DV / 16;
+    const int rt = blockIdx.x % nrt, nh = blockIdx.x / nrt;
+    const int n = nh / H, h = nh % H;
+    if (n >= NSEQ) return;
+    if (!cpr && meta[1] != 0) return;   // malformed cu_seqlens: nothing is written
+    const int nseg = cpr ? sg.nsegc : sg.seg_cnt[n];
+    const int u0 = cpr ? n * sg.nsegc : seg_first[n];
+    const int t = threadIdx.x, r = 16 * rt + t / 16, c0 = (t % 16) * CPT;
+    auto unit = [&](int s) { return (int64_t)(u0 + s) * H + h; };
+    float S[CPT];
+    const float *src = init_state ? init_state + ((int64_t)nh * DV + r) * DK + c0 : nullptr;
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) S[j] = src ? src[j] : 0.f;
+    auto put = [&](int s) {
+        float *dst = sg.ws_sin + (unit(s) * DV + r) * DK + c0;
+        if constexpr (CPT % 4 == 0) {
+#pragma unroll
+            for (int j = 0; j < CPT; j += 4)
+                *reinterpret_cast<float4_t *>(dst + j) = float4_t{S[j], S[j + 1], S[j + 2], S[j + 3]};
+        } else {
+#pragma unroll
+            for (int j = 0; j < CPT; ++j) dst[j] = S[j];
+        }
+    };
+    put(0);
+    if (nseg < 2) return;
+    {
+        const float *e = sg.ws_end + (unit(0) * (DV + DK) + r) * DK + c0;
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) S[j] = e[j];
+    }
+    put(1);
+    for (int s = 1; s + 1 < nseg; ++s) {
+        const float *E = sg.ws_end + unit(s) * (DV + DK) * DK;
+        const float *G = E + (int64_t)r * DK + c0, *F = E + (int64_t)DV * DK;
+        __syncthreads();   // the previous product's reads of `rows` are done
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) rows[t / 16][c0 + j] = S[j];
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) S[j] = G[j];
+#pragma unroll 1
+        for (int e0 = 0; e0 < DK; e0 += SLAB) {
+            float4_t ld[L::LD];
+#pragma unroll
+            for (int i = 0; i < L::LD; ++i) {
+                const int x = 4 * (t + 256 * i);   // element of the slab
+                if (x < SLAB * DK) ld[i] = *reinterpret_cast<const float4_t *>(F + (int64_t)e0 * DK + x);
+            }
+            __syncthreads();   // the previous slab's reads of `fs` are done
+#pragma unroll
+            for (int i = 0; i < L::LD; ++i) {
+                const int x = 4 * (t + 256 * i);
+                if (x < SLAB * DK) *reinterpret_cast<float4_t *>(&fs[0][0] + x) = ld[i];
+            }
+            __syncthreads();
+#pragma unroll 2
+            for (int e = 0; e < SLAB; e += 4) {
+                const float4_t a = *reinterpret_cast<const float4_t *>(&rows[t / 16][e0 + e]);
+#pragma unroll
+                for (int ee = 0; ee < 4; ++ee) {
+                    float f[CPT];
+                    if constexpr (CPT % 4 == 0) {
+#pragma unroll
+                        for (int j = 0; j < CPT; j += 4) {
+                            const float4_t x = *reinterpret_cast<const float4_t *>(&fs[e + ee][c0 + j]);
+                            f[j] = x[0], f[j + 1] = x[1], f[j + 2] = x[2], f[j + 3] = x[3];
+                        }
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < CPT; ++j) f[j] = fs[e + ee][c0 + j];
+                    }
+#pragma unroll
+                    for (int j = 0; j < CPT; ++j) S[j] = fmaf(a[ee], f[j], S[j]);
+                }
+            }
+        }
+        put(s + 1);
     }
 }
 
@@ -1143,11 +1363,46 @@ __global__ __launch_bounds__(64 * (NW + kStagers)) void chunk_state_kernel(
 // ============================================================================
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Segmented state pass.  Without it the state pass runs one chain of chunks
+// per (sequence, head) and value tile, so a batch with few (sequence, head)
+// pairs leaves most of the GPU idle while it walks its long chains.  Cutting
+// each sequence into segments of `seg` chunks and running
+//   (a) a transition pass per segment but the last (the state pass without
+//       outputs, from a zero state with DK extra columns that start as the
+//       identity: it leaves the segment's affine map [G; F]),
+//   (b) a combine pass that walks the segments' maps to each segment's
+//       incoming state, and
+//   (c) the output pass per segment from that state,
+// turns one chain of n chunks into two of `seg` (plus the walk).  It pays one
+// more pass over K, V and M for all but the last segments, so it is used only
+// when the value columns of all chains together are too few to fill the GPU:
+// the segments then multiply them to about 16K columns (1024 waves of 16).
+// GDN_SEG_CHUNKS overrides the choice (0 disables), for tests and tuning.
+int32_t chunk_seg_chunks(int32_t B, int32_t T, int32_t N, bool packed, int32_t H, int32_t dv) {
+    const char *env = getenv("GDN_SEG_CHUNKS");
+    if (env && *env) {
+        const int x = atoi(env);
+        if (x >= 0) return x;
+    }
+    const int64_t rows = packed ? (T + C - 1) / C : (int64_t)B * ((T + C - 1) / C);
+    if (N <= 0 || rows <= 0) return 0;
+    const int64_t cols = (int64_t)N * H * dv;
+    if (cols >= 8192) return 0;
+    const int64_t nseg = std::min<int64_t>(16, 16384 / cols);
+    const int64_t avg = (rows + N - 1) / N;             // chunks per sequence, on average
+    const int64_t seg = std::max<int64_t>(8, (avg + nseg - 1) / nseg);
+    return seg >= avg ? 0 : (int32_t)seg;
+}
+
 ChunkWorkspace chunk_workspace_layout(int32_t B, int32_t T, int32_t N, bool packed, int32_t H,
-                                      int32_t in_dtype) {
+                                      int32_t in_dtype, int32_t dk, int32_t dv) {
     ChunkWorkspace w{};
     const int64_t per_row = (T + C - 1) / C;
     w.max_rows = packed ? per_row + N : (int64_t)B * per_row;
+    w.seg_chunks = chunk_seg_chunks(B, T, N, packed, H, dv);
+    if (w.seg_chunks > 0)
+        w.max_units = packed ? (w.max_rows + w.seg_chunks - 1) / w.seg_chunks + N
+                             : (int64_t)B * ((per_row + w.seg_chunks - 1) / w.seg_chunks);
     const size_t op = in_dtype == DT_FP32 ? 4 : 2;
     size_t off = 0;
     w.off_meta = off;   off = align256(off + 8 * sizeof(int32_t));
@@ -1158,6 +1413,14 @@ ChunkWorkspace chunk_workspace_layout(int32_t B, int32_t T, int32_t N, bool pack
     w.off_g = off;      off = align256(off + sizeof(float) * (size_t)w.max_rows * H * 4 * C);
     w.off_m = off;      off = align256(off + op * (size_t)w.max_rows * H * kTriTiles * kTileElems);
     w.off_p = off;      off = align256(off + op * (size_t)w.max_rows * H * kTriTiles * kTileElems);
+    if (w.seg_chunks > 0) {
+        const size_t units = (size_t)w.max_units;
+        w.off_segfirst = off; off = align256(off + sizeof(int32_t) * (size_t)N);
+        w.off_segcnt = off;   off = align256(off + sizeof(int32_t) * (size_t)N);
+        w.off_segtab = off;   off = align256(off + sizeof(int32_t) * 2 * units);
+        w.off_end = off;      off = align256(off + sizeof(float) * units * H * (size_t)(dv + dk) * dk);
+        w.off_sin = off;      off = align256(off + sizeof(float) * units * H * (size_t)dv * dk);
+    }
     w.total = off;
     return w;
 }
@@ -1180,10 +1443,11 @@ static int cu_count() {
     return cus;
 }
 
-static int state_waves_per_block(int DV, int64_t NH) {
+// cols: value columns per unit; units: (sequence or segment, head) units.
+static int state_waves_per_block(int cols, int64_t units, const char *env_name) {
     const int cus = cu_count();
-    const int tiles = (DV + 15) / 16;
-    const int64_t slots = ((NH + 7) / 8) * 8;
+    const int tiles = (cols + 15) / 16;
+    const int64_t slots = ((units + 7) / 8) * 8;
     int nw = 4;
     for (int c = 2; c <= 4; c *= 2)
         if (slots * ((tiles + c - 1) / c) <= cus) {
@@ -1191,7 +1455,7 @@ static int state_waves_per_block(int DV, int64_t NH) {
             break;
         }
     if (tiles < nw) nw = tiles >= 2 ? 2 : 1;
-    const char *env = getenv("GDN_STATE_WAVES");
+    const char *env = getenv(env_name);
     if (env) {
         const int x = atoi(env);
         if (x == 1 || x == 2 || x == 4) nw = x;
@@ -1210,24 +1474,38 @@ static hipError_t allow_smem(K kernel, size_t bytes) {
 // empty batch still reads as equal-length), 0 for a packed one.
 static int uniform_cpr(const ChunkArgs &a) { return a.cu_seqlens ? 0 : (a.T + C - 1) / C + (a.T == 0); }
 
-template <typename in_t, typename OP, int DK, int NW>
-static hipError_t launch_state(const ChunkArgs &a, const ChunkWorkspace &w, hipStream_t st) {
-    using L = StateSmem<in_t, OP, DK, NW>;
-    auto kern = chunk_state_kernel<in_t, OP, DK, NW>;
+template <typename in_t, typename OP, int DK, int NW, bool OUT>
+static hipError_t launch_state(const ChunkArgs &a, const ChunkWorkspace &w, const SegArgs &sg, int64_t NU,
+                               hipStream_t st) {
+    using L = StateSmem<in_t, OP, DK, NW, OUT>;
+    auto kern = chunk_state_kernel<in_t, OP, DK, NW, OUT>;
     hipError_t e = allow_smem(kern, L::bytes);
     if (e != hipSuccess) return e;
     char *ws = static_cast<char *>(a.workspace);
-    const int64_t NH = (int64_t)a.N * a.H;
-    const int nvt = ((a.dv + 15) / 16 + NW - 1) / NW;
-    const int64_t blocks = ((NH + 7) / 8) * 8 * nvt;
-    ProfScope prof("gdn_chunk_state", st);
+    const int cols = OUT ? a.dv : a.dv + a.dk;
+    const int nvt = ((cols + 15) / 16 + NW - 1) / NW;
+    const int64_t blocks = ((NU + 7) / 8) * 8 * nvt;
+    ProfScope prof(OUT ? "gdn_chunk_state" : "gdn_chunk_transition", st);
     kern<<<dim3((unsigned)blocks), dim3(64 * (NW + kStagers)), L::bytes, st>>>(
-        (int)NH, a.H, a.dv, nvt, a.out_dtype, a.T, uniform_cpr(a), reinterpret_cast<int32_t *>(ws + w.off_meta),
-        reinterpret_cast<const int32_t *>(ws + w.off_cu), reinterpret_cast<const int32_t *>(ws + w.off_row0),
+        (int)NU, a.H, a.dv, nvt, a.out_dtype, a.T, uniform_cpr(a), reinterpret_cast<int32_t *>(ws + w.off_meta),
+        reinterpret_cast<const int32_t *>(ws + w.off_cu), reinterpret_cast<const int32_t *>(ws + w.off_row0), sg,
         static_cast<const in_t *>(a.q), static_cast<const in_t *>(a.k), static_cast<const in_t *>(a.v),
         reinterpret_cast<const float *>(ws + w.off_g), reinterpret_cast<const OP *>(ws + w.off_m),
         reinterpret_cast<const OP *>(ws + w.off_p), a.init_state, a.final_state, a.o);
     return hipGetLastError();
+}
+
+template <typename in_t, typename OP, int DK, bool OUT>
+static hipError_t launch_state_nw(const ChunkArgs &a, const ChunkWorkspace &w, const SegArgs &sg, int64_t NU,
+                                  hipStream_t st) {
+    const int cols = OUT ? a.dv : a.dv + a.dk;
+    switch (state_waves_per_block(cols, NU, OUT ? "GDN_STATE_WAVES" : "GDN_TRANSITION_WAVES")) {
+    case 4: return launch_state<in_t, OP, DK, 4, OUT>(a, w, sg, NU, st);
+    case 2: return launch_state<in_t, OP, DK, 2, OUT>(a, w, sg, NU, st);
+    default:
+        if constexpr (OUT) return launch_state<in_t, OP, DK, 1, OUT>(a, w, sg, NU, st);
+        return launch_state<in_t, OP, DK, 2, OUT>(a, w, sg, NU, st);
+    }
 }
 
 template <typename in_t, typename OP, int DK>
@@ -1248,11 +1526,29 @@ static hipError_t launch_dk(const ChunkArgs &a, const ChunkWorkspace &w, hipStre
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    switch (state_waves_per_block(a.dv, (int64_t)a.N * a.H)) {
-    case 4: return launch_state<in_t, OP, DK, 4>(a, w, st);
-    case 2: return launch_state<in_t, OP, DK, 2>(a, w, st);
-    default: return launch_state<in_t, OP, DK, 1>(a, w, st);
+    SegArgs sg{};
+    if (w.seg_chunks == 0) return launch_state_nw<in_t, OP, DK, true>(a, w, sg, (int64_t)a.N * a.H, st);
+
+    const int cpr = uniform_cpr(a);
+    sg.seg_chunks = w.seg_chunks;
+    sg.nsegc = cpr ? (cpr + w.seg_chunks - 1) / w.seg_chunks : 0;
+    sg.seg_cnt = reinterpret_cast<const int32_t *>(ws + w.off_segcnt);
+    sg.seg_tab = reinterpret_cast<const int32_t *>(ws + w.off_segtab);
+    sg.ws_end = reinterpret_cast<float *>(ws + w.off_end);
+    sg.ws_sin = reinterpret_cast<float *>(ws + w.off_sin);
+    const int64_t NU = w.max_units * a.H;
+    hipError_t e = launch_state_nw<in_t, OP, DK, false>(a, w, sg, NU, st);
+    if (e != hipSuccess) return e;
+    {
+        ProfScope prof("gdn_chunk_combine", st);
+        const int64_t blocks = (int64_t)a.N * a.H * (a.dv / 16);
+        chunk_combine_kernel<DK><<<dim3((unsigned)blocks), dim3(256), 0, st>>>(
+            a.N, a.H, a.dv, cpr, reinterpret_cast<const int32_t *>(ws + w.off_meta), sg,
+            reinterpret_cast<const int32_t *>(ws + w.off_segfirst), a.init_state);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
     }
+    return launch_state_nw<in_t, OP, DK, true>(a, w, sg, NU, st);
 }
 
 template <typename in_t, typename OP>
@@ -1269,22 +1565,27 @@ static hipError_t launch_typed(const ChunkArgs &a, const ChunkWorkspace &w, hipS
 }
 
 hipError_t launch_chunk_table(int32_t N, int32_t T, const int32_t *cu_seqlens, int32_t *meta, int32_t *cu_ws,
-                              int32_t *row0, int32_t *row_tok, int32_t *row_len, hipStream_t st) {
+                              int32_t *row0, int32_t *row_tok, int32_t *row_len, int32_t seg_chunks,
+                              int32_t *seg_first, int32_t *seg_cnt, int32_t *seg_tab, hipStream_t st) {
     ProfScope prof("gdn_chunk_table", st);
-    chunk_table_kernel<<<1, 256, 0, st>>>(N, T, cu_seqlens, meta, cu_ws, row0, row_tok, row_len);
+    chunk_table_kernel<<<1, 256, 0, st>>>(N, T, cu_seqlens, meta, cu_ws, row0, row_tok, row_len, seg_chunks,
+                                          seg_first, seg_cnt, seg_tab);
     return hipGetLastError();
 }
 
 hipError_t launch_chunk_fwd(const ChunkArgs &a, hipStream_t st) {
     const bool packed = a.cu_seqlens != nullptr;
-    const ChunkWorkspace w = chunk_workspace_layout(a.B, a.T, a.N, packed, a.H, a.in_dtype);
+    const ChunkWorkspace w = chunk_workspace_layout(a.B, a.T, a.N, packed, a.H, a.in_dtype, a.dk, a.dv);
     char *ws = static_cast<char *>(a.workspace);
     if (packed) {
         hipError_t e = launch_chunk_table(a.N, a.T, a.cu_seqlens, reinterpret_cast<int32_t *>(ws + w.off_meta),
                                           reinterpret_cast<int32_t *>(ws + w.off_cu),
                                           reinterpret_cast<int32_t *>(ws + w.off_row0),
                                           reinterpret_cast<int32_t *>(ws + w.off_rowtok),
-                                          reinterpret_cast<int32_t *>(ws + w.off_rowlen), st);
+                                          reinterpret_cast<int32_t *>(ws + w.off_rowlen), w.seg_chunks,
+                                          reinterpret_cast<int32_t *>(ws + w.off_segfirst),
+                                          reinterpret_cast<int32_t *>(ws + w.off_segcnt),
+                                          reinterpret_cast<int32_t *>(ws + w.off_segtab), st);
         if (e != hipSuccess) return e;
     }
     // Few tokens per sequence (e.g. appending to resident states): the

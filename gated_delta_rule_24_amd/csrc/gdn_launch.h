@@ -49,12 +49,23 @@ struct ChunkArgs {
 };
 
 // Workspace carve-up for one gdn_chunk_fwd call (byte offsets from the base).
+// With a segmented state pass (seg_chunks > 0) each sequence's chunks are cut
+// into segments of seg_chunks chunks; a "segment unit" is one (sequence,
+// segment) pair and max_units bounds their number (per head).
 struct ChunkWorkspace {
-    int64_t max_rows;   // upper bound on (sequence, chunk) rows
-    size_t off_meta, off_cu, off_row0, off_rowtok, off_rowlen, off_g, off_m, off_p, total;
+    int64_t max_rows;    // upper bound on (sequence, chunk) rows
+    int32_t seg_chunks;  // chunks per segment, 0 = one segment per sequence
+    int64_t max_units;   // upper bound on segment units (0 when not segmented)
+    size_t off_meta, off_cu, off_row0, off_rowtok, off_rowlen, off_g, off_m, off_p;
+    size_t off_segfirst, off_segcnt, off_segtab;   // packed: first unit and unit count per sequence, unit -> (n, s)
+    size_t off_end;      // per (unit, head): the segment's map [S-part; F-part], (dv + dk) x dk fp32
+    size_t off_sin;      // per (unit, head): the state entering the segment, dv x dk fp32
+    size_t total;
 };
 ChunkWorkspace chunk_workspace_layout(int32_t B, int32_t T, int32_t N, bool packed, int32_t H,
-                                      int32_t in_dtype);
+                                      int32_t in_dtype, int32_t dk, int32_t dv);
+// Chunks per segment that gdn_chunk_fwd uses for this shape (0 = unsegmented).
+int32_t chunk_seg_chunks(int32_t B, int32_t T, int32_t N, bool packed, int32_t H, int32_t dv);
 
 hipError_t launch_decode_step(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_chunk_fwd(const ChunkArgs &a, hipStream_t stream);
@@ -81,8 +92,12 @@ BwdWorkspace chunk_bwd_workspace_layout(int32_t B, int32_t T, int32_t N, bool pa
                                         int32_t dv);
 hipError_t launch_chunk_bwd(const ChunkArgs &a, const BwdArgs &g, hipStream_t stream);
 // G0 on its own (validates cu_seqlens and builds the chunk-row table).
+// With seg_chunks > 0 it also lays out the segment units: seg_first[n] and
+// seg_cnt[n] per sequence, seg_tab[2u], seg_tab[2u + 1] = (n, s) per unit, and
+// meta[2] = the number of units.
 hipError_t launch_chunk_table(int32_t N, int32_t T, const int32_t *cu_seqlens, int32_t *meta, int32_t *cu_ws,
-                              int32_t *row0, int32_t *row_tok, int32_t *row_len, hipStream_t stream);
+                              int32_t *row0, int32_t *row_tok, int32_t *row_len, int32_t seg_chunks,
+                              int32_t *seg_first, int32_t *seg_cnt, int32_t *seg_tab, hipStream_t stream);
 
 // Host-side launch timing (see gdn_profile_* in gdn.h).  While profiling is
 // enabled the scope records a HIP event pair around the launches it covers.
