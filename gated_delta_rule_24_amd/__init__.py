@@ -18,7 +18,7 @@ from typing import Optional
 
 import torch
 
-__all__ = ["GdnError", "chunk_fwd", "decode_step", "chunk_bwd", "chunk_fwd_workspace_size",
+__all__ = ["GdnError", "chunk_fwd", "chunk_fwd_noalloc", "decode_step", "chunk_bwd", "chunk_fwd_workspace_size",
            "chunk_bwd_workspace_size", "chunk_fwd_check", "load", "lib_path", "profile", "CHUNK"]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -26,6 +26,7 @@ CHUNK = 64
 
 GDN_FP32, GDN_BF16, GDN_FP16 = 0, 1, 2
 GDN_QK_L2NORM = 1
+NOALLOC_SCRATCH_BYTES = 64 << 20   # GDN_NOALLOC_SCRATCH_BYTES in gdn.h
 _DT = {torch.float32: GDN_FP32, torch.bfloat16: GDN_BF16, torch.float16: GDN_FP16}
 _STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_DTYPE", 4: "GDN_ERR_ALIGN",
            5: "GDN_ERR_UNSUPPORTED", 6: "GDN_ERR_WORKSPACE", 7: "GDN_ERR_HIP", 8: "GDN_ERR_ALIAS",
@@ -76,6 +77,8 @@ def load():
     lib.gdn_chunk_bwd_workspace_size.argtypes = [ctypes.POINTER(ChunkDesc), ctypes.POINTER(sz)]
     lib.gdn_chunk_bwd.restype = ctypes.c_int
     lib.gdn_chunk_bwd.argtypes = [ctypes.POINTER(ChunkDesc)] + [vp] * 16 + [sz, vp]
+    lib.gdn_chunk_fwd_noalloc.restype = ctypes.c_int
+    lib.gdn_chunk_fwd_noalloc.argtypes = [ctypes.POINTER(ChunkDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.gdn_chunk_fwd_check.restype = ctypes.c_int
     lib.gdn_chunk_fwd_check.argtypes = [vp, vp, ctypes.POINTER(i32)]
     lib.gdn_decode_step.restype = ctypes.c_int
@@ -87,7 +90,7 @@ def load():
     lib.gdn_profile_read.restype = ctypes.c_int
     lib.gdn_profile_read.argtypes = [i32, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_int64),
                                      ctypes.POINTER(ctypes.c_double)]
-    if lib.gdn_abi_version() != 3:
+    if lib.gdn_abi_version() != 4:
         raise RuntimeError(f"{p}: unexpected ABI version {lib.gdn_abi_version()}")
     _lib = lib
     return lib
@@ -131,18 +134,11 @@ def chunk_fwd_workspace_size(B, T, H, dk, dv, num_seqs, in_dtype=torch.bfloat16,
     return int(n.value)
 
 
-def chunk_fwd(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, *, out_dtype=torch.float32,
-              o=None, final_state=True, workspace=None, chunk=CHUNK, qk_l2norm=False):
-    """Chunkwise-parallel prefill.
-
-    q, k [B,T,H,dk], v [B,T,H,dv] (fp32/bf16/fp16, same dtype);
-    log_alpha, beta [B,T,H] fp32; init_state [N,H,dv,dk] fp32 or None;
-    cu_seqlens int32 [N+1] (packed batch, B == 1) or None.
-    final_state: True (allocate), False/None (not returned) or a tensor to
-    write (it may be init_state itself).  qk_l2norm: normalise q and k per
-    (token, head) inside the kernels.  Returns (o, final_state or None).
-    """
-    lib = load()
+def _chunk_call_args(q, k, v, log_alpha, beta, init_state, cu_seqlens, out_dtype, o, final_state, chunk,
+                     qk_l2norm):
+    """Checks and marshals the arguments shared by chunk_fwd and chunk_fwd_noalloc.
+    Returns (descriptor, o, final_state or None, the leading pointer arguments)."""
+    load()
     dev = q.device
     dts = (torch.float32, torch.bfloat16, torch.float16)
     _need(q, "q", dts, dev, 4)
@@ -180,13 +176,44 @@ def chunk_fwd(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, *, out
         if tuple(final_state.shape) != (N, H, dv, dk):
             raise ValueError("final_state has the wrong shape")
     desc = _desc(B, T, H, dk, dv, N, _DT[q.dtype], _DT[o.dtype], chunk, GDN_QK_L2NORM if qk_l2norm else 0)
+    ptrs = [_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(init_state), _ptr(cu_seqlens), _ptr(o),
+            _ptr(final_state)]
+    return desc, o, final_state, ptrs
+
+
+def chunk_fwd(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, *, out_dtype=torch.float32,
+              o=None, final_state=True, workspace=None, chunk=CHUNK, qk_l2norm=False):
+    """Chunkwise-parallel prefill.
+
+    q, k [B,T,H,dk], v [B,T,H,dv] (fp32/bf16/fp16, same dtype);
+    log_alpha, beta [B,T,H] fp32; init_state [N,H,dv,dk] fp32 or None;
+    cu_seqlens int32 [N+1] (packed batch, B == 1) or None.
+    final_state: True (allocate), False/None (not returned) or a tensor to
+    write (it may be init_state itself).  qk_l2norm: normalise q and k per
+    (token, head) inside the kernels.  Returns (o, final_state or None).
+    """
+    lib = load()
+    desc, o, final_state, ptrs = _chunk_call_args(q, k, v, log_alpha, beta, init_state, cu_seqlens, out_dtype, o,
+                                                  final_state, chunk, qk_l2norm)
     need = ctypes.c_size_t(0)
     _check(lib.gdn_chunk_fwd_workspace_size(ctypes.byref(desc), ctypes.byref(need)))
     if workspace is None:
-        workspace = torch.empty(int(need.value), dtype=torch.uint8, device=dev)
-    _check(lib.gdn_chunk_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
-                             _ptr(init_state), _ptr(cu_seqlens), _ptr(o), _ptr(final_state), _ptr(workspace),
-                             ctypes.c_size_t(workspace.numel() * workspace.element_size()), _stream(dev)))
+        workspace = torch.empty(int(need.value), dtype=torch.uint8, device=q.device)
+    _check(lib.gdn_chunk_fwd(ctypes.byref(desc), *ptrs, _ptr(workspace),
+                             ctypes.c_size_t(workspace.numel() * workspace.element_size()), _stream(q.device)))
+    return o, final_state
+
+
+def chunk_fwd_noalloc(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, *, out_dtype=torch.float32,
+                      o=None, final_state=True, chunk=CHUNK, qk_l2norm=False):
+    """chunk_fwd through gdn_chunk_fwd_noalloc: the library's per-GPU scratch
+    array (NOALLOC_SCRATCH_BYTES) stands in for the workspace, so with `o` and
+    `final_state` passed in (or final_state=False) nothing is allocated.
+    Calls that overlap in time on one GPU race on the scratch array."""
+    lib = load()
+    desc, o, final_state, ptrs = _chunk_call_args(q, k, v, log_alpha, beta, init_state, cu_seqlens, out_dtype, o,
+                                                  final_state, chunk, qk_l2norm)
+    _check(lib.gdn_chunk_fwd_noalloc(ctypes.byref(desc), *ptrs, _stream(q.device)))
     return o, final_state
 
 

@@ -155,10 +155,10 @@ gdn_status gdn_chunk_fwd_workspace_size(const gdn_chunk_desc *desc, size_t *byte
     return ok();
 }
 
-gdn_status gdn_chunk_fwd(const gdn_chunk_desc *desc, const void *q, const void *k, const void *v,
-                         const float *log_alpha, const float *beta, const float *init_state,
-                         const int32_t *cu_seqlens, void *o, float *final_state, void *workspace,
-                         size_t workspace_bytes, hipStream_t stream) {
+static gdn_status chunk_fwd_impl(const gdn_chunk_desc *desc, const void *q, const void *k, const void *v,
+                                 const float *log_alpha, const float *beta, const float *init_state,
+                                 const int32_t *cu_seqlens, void *o, float *final_state, void *workspace,
+                                 size_t workspace_bytes, hipStream_t stream, const char *ws_name) {
     gdn_status s = check_chunk_desc(desc);
     if (s != GDN_OK) return s;
     const gdn_chunk_desc &d = *desc;
@@ -173,7 +173,7 @@ gdn_status gdn_chunk_fwd(const gdn_chunk_desc *desc, const void *q, const void *
     const auto w = gdn::chunk_workspace_layout(d.batch, d.seqlen, d.num_seqs, packed, d.heads, d.in_dtype, d.dk,
                                                d.dv);
     if (workspace_bytes < w.total)
-        return fail(GDN_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, w.total);
+        return fail(GDN_ERR_WORKSPACE, "%s has %zu bytes, this call needs %zu", ws_name, workspace_bytes, w.total);
     const void *ptrs[] = {q, k, v, init_state, o, final_state, workspace};
     const char *names[] = {"q", "k", "v", "init_state", "o", "final_state", "workspace"};
     for (int i = 0; i < 7; ++i)
@@ -206,6 +206,66 @@ gdn_status gdn_chunk_fwd(const gdn_chunk_desc *desc, const void *q, const void *
     hipError_t e = gdn::launch_chunk_fwd(a, stream);
     if (e != hipSuccess) return hip_fail(e, "gdn_chunk_fwd launch");
     return ok();
+}
+
+gdn_status gdn_chunk_fwd(const gdn_chunk_desc *desc, const void *q, const void *k, const void *v,
+                         const float *log_alpha, const float *beta, const float *init_state,
+                         const int32_t *cu_seqlens, void *o, float *final_state, void *workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+    return chunk_fwd_impl(desc, q, k, v, log_alpha, beta, init_state, cu_seqlens, o, final_state, workspace,
+                          workspace_bytes, stream, "workspace");
+}
+
+// ---- gdn_chunk_fwd without a caller workspace -----------------------------------
+// The workspace of gdn_chunk_fwd_noalloc is this array: one copy per GPU,
+// allocated when the code object is loaded and held until the process ends.
+// Its name is only a host-side handle; the device address of the current
+// GPU's copy comes from hipGetSymbolAddress, looked up once per device on the
+// first call made with that device current and kept in g_scratch_ptr.
+static __device__ __align__(256) unsigned char scratch[GDN_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+static gdn_status scratch_for_current_device(void **ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(GDN_ERR_UNSUPPORTED, "device %d out of range", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!p) return fail(GDN_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return GDN_OK;
+}
+
+gdn_status gdn_chunk_fwd_noalloc(const gdn_chunk_desc *desc, const void *q, const void *k, const void *v,
+                                 const float *log_alpha, const float *beta, const float *init_state,
+                                 const int32_t *cu_seqlens, void *o, float *final_state, hipStream_t stream) {
+    // The size limit is checked first, on the host, so an oversized call
+    // fails the same way with or without a GPU.
+    gdn_status s = check_chunk_desc(desc);
+    if (s != GDN_OK) return s;
+    const auto w = gdn::chunk_workspace_layout(desc->batch, desc->seqlen, desc->num_seqs, cu_seqlens != nullptr,
+                                               desc->heads, desc->in_dtype, desc->dk, desc->dv);
+    if (w.total > (size_t)GDN_NOALLOC_SCRATCH_BYTES)
+        return fail(GDN_ERR_WORKSPACE,
+                    "this call needs %zu bytes of workspace, more than the %zu-byte scratch array of "
+                    "gdn_chunk_fwd_noalloc; use gdn_chunk_fwd with a workspace",
+                    w.total, (size_t)GDN_NOALLOC_SCRATCH_BYTES);
+    void *ws = nullptr;
+    s = scratch_for_current_device(&ws);
+    if (s != GDN_OK) return s;
+    return chunk_fwd_impl(desc, q, k, v, log_alpha, beta, init_state, cu_seqlens, o, final_state, ws,
+                          (size_t)GDN_NOALLOC_SCRATCH_BYTES, stream, "the no-allocation scratch array");
 }
 
 gdn_status gdn_chunk_bwd_workspace_size(const gdn_chunk_desc *desc, size_t *bytes) {

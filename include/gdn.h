@@ -19,6 +19,9 @@
  * and differentiated:
  *   gdn_chunk_bwd    -- gradients of gdn_chunk_fwd's outputs with respect to
  *                       all of its inputs (for training).
+ * gdn_chunk_fwd_noalloc is gdn_chunk_fwd for callers that cannot allocate
+ * device memory: it uses a scratch array of the library instead of a
+ * workspace argument.
  *
  * Both return the same numbers as the recurrence up to floating-point
  * rounding.  Chunked, single-step and save-then-resume evaluations agree
@@ -29,7 +32,9 @@
  *   - Every pointer argument except `stream` is a DEVICE pointer (HBM) unless
  *     stated otherwise.  Tensors are dense, row-major, last index fastest.
  *   - The caller owns every buffer.  The library keeps no pointer after the
- *     call returns and allocates no device memory on these paths.
+ *     call returns and allocates no device memory on these paths (the one
+ *     device array it owns is gdn_chunk_fwd_noalloc's scratch array, which
+ *     exists while the library is loaded).
  *   - Work is enqueued on `stream` (NULL = the default stream) and the call
  *     returns without waiting.  Buffers must stay valid until the stream
  *     reaches that point.  A kernel fault shows up at the caller's next
@@ -64,7 +69,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 3
+#define GDN_ABI_VERSION 4
 
 typedef enum {
     GDN_OK = 0,
@@ -142,12 +147,21 @@ const char *gdn_last_error_message(void);
 
 /*
  * Workspace for gdn_chunk_fwd, in bytes, written to *bytes (host pointer).
- * Depends only on the descriptor.  The workspace holds the chunk table built
- * from cu_seqlens and, per (chunk, head), the UT-transform matrix
- * T diag(beta), the decay-masked Q K^T block and the chunk's decay factors
- * (exp of the cumulative log-decay from the chunk start, and to the chunk
- * end).  It need not be initialised and may be reused by later calls
- * that are ordered after this one on the stream.
+ * Depends only on the descriptor (and on GDN_SEG_CHUNKS, below).  The
+ * workspace holds the chunk table built from cu_seqlens and, per (chunk,
+ * head), the UT-transform matrix T diag(beta), the decay-masked Q K^T block
+ * and the chunk's decay factors (exp of the cumulative log-decay from the
+ * chunk start, and to the chunk end).  When the state pass is segmented (a
+ * batch with too few (sequence, head) pairs to fill the GPU: each sequence's
+ * chunks are cut into segments whose affine state maps S -> S F + G are
+ * formed in parallel and then chained, the algebra of the paper's chunk-level
+ * state recurrence, section 3.3, applied to runs of chunks) it also holds the
+ * segment table and, per (segment, head), the map [G; F] ((dv + dk) x dk
+ * fp32) and the segment's incoming state (dv x dk fp32).  The environment
+ * variable GDN_SEG_CHUNKS, read at every call, fixes the segment length in
+ * chunks (0 = never segment); unset, the library chooses.  The workspace
+ * need not be initialised and may be reused by later calls that are ordered
+ * after this one on the stream.
  * Errors: GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_DTYPE, GDN_ERR_UNSUPPORTED.
  */
 gdn_status gdn_chunk_fwd_workspace_size(const gdn_chunk_desc *desc, size_t *bytes);
@@ -198,6 +212,35 @@ gdn_status gdn_chunk_fwd(const gdn_chunk_desc *desc,
                          void *o, float *final_state,
                          void *workspace, size_t workspace_bytes,
                          hipStream_t stream);
+
+/*
+ * gdn_chunk_fwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Same arguments, semantics and errors as gdn_chunk_fwd, without the
+ * workspace: the library's own scratch array stands in for it, a
+ * GDN_NOALLOC_SCRATCH_BYTES device array per GPU that exists from the moment
+ * the library is loaded until the process ends.  Its device address is
+ * looked up (hipGetSymbolAddress) on the first call on each device; the call
+ * itself allocates nothing.
+ *   - A call whose gdn_chunk_fwd_workspace_size exceeds
+ *     GDN_NOALLOC_SCRATCH_BYTES returns GDN_ERR_WORKSPACE and writes nothing
+ *     (64 MiB covers, e.g., B = 4, T = 4096, H = 16, dk = dv = 128 with
+ *     16-bit inputs).
+ *   - Every call on a GPU uses that GPU's one array.  Calls that may overlap
+ *     in time on one GPU (different streams, or different host threads
+ *     without ordering) race on it and must not be issued; calls ordered on
+ *     one stream are safe.  Nothing in the array has to start at a known
+ *     value: each call writes every part of it that it reads.
+ *   - A malformed cu_seqlens makes the kernels write nothing, as in
+ *     gdn_chunk_fwd, but is not reported (gdn_chunk_fwd_check needs the
+ *     workspace pointer).
+ */
+#define GDN_NOALLOC_SCRATCH_BYTES (64u << 20)
+gdn_status gdn_chunk_fwd_noalloc(const gdn_chunk_desc *desc,
+                                 const void *q, const void *k, const void *v,
+                                 const float *log_alpha, const float *beta,
+                                 const float *init_state, const int32_t *cu_seqlens,
+                                 void *o, float *final_state, hipStream_t stream);
 
 /*
  * Workspace for gdn_chunk_bwd, in bytes, written to *bytes (host pointer).

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.gdn_abi_version() == 3
+    assert lib.gdn_abi_version() == 4
     for code, name in [(0, b"GDN_OK"), (2, b"GDN_ERR_SHAPE"), (9, b"GDN_ERR_DEVICE_INPUT")]:
         assert lib.gdn_status_string(code) == name
 
@@ -160,3 +160,17 @@ def test_python_binding_requires_library(monkeypatch, tmp_path):
     monkeypatch.setattr(gdn, "_lib", None)
     with pytest.raises(RuntimeError, match="not built"):
         gdn.load()
+
+
+def test_noalloc_rejects_oversized_calls(lib):
+    """gdn_chunk_fwd_noalloc refuses, on the host, a call whose workspace would exceed its scratch
+    array (GDN_NOALLOC_SCRATCH_BYTES), with GDN_ERR_WORKSPACE and a message that names the limit."""
+    vp = ctypes.c_void_p
+    big = desc(batch=8, seqlen=8192, heads=16, num_seqs=8)
+    assert ws_size(lib, big)[1] > gdn.NOALLOC_SCRATCH_BYTES
+    st = lib.gdn_chunk_fwd_noalloc(ctypes.byref(big), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), None, None,
+                                   vp(FAKE2), None, None)
+    assert st == 6
+    assert str(gdn.NOALLOC_SCRATCH_BYTES).encode() in lib.gdn_last_error_message()
+    assert lib.gdn_chunk_fwd_noalloc(ctypes.byref(desc(in_dtype=7)), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE),
+                                     vp(FAKE), None, None, vp(FAKE2), None, None) == 3
