@@ -1040,9 +1040,10 @@ struct GradSmem {
     static constexpr int off_p = off_buf + C * CP;        // after the loop: dP o Gamma
     static constexpr int off_w = (off_buf + VBUF > off_p + C * CP) ? off_buf + VBUF : off_p + C * CP;  // W, later dK o
     static constexpr int END = (off_buf + NBUF * VBUF > off_w + C * CP) ? off_buf + NBUF * VBUF : off_w + C * CP;
-    static constexpr int off_vec = END;                   // g, gamma, kappa, beta, dgamma, dkappa, dbeta
-    static constexpr int off_f = off_vec + 7 * C + 8;    // (after one <dS_next, S> part per wave)
-    static constexpr int floats = off_f + 4 * C;         // E L column sums, one row per row block
+    static constexpr int off_vec = END;                   // g, gamma, kappa, beta, dgamma, dkappa
+    static constexpr int off_f = off_vec + 6 * C + 8;    // (after one <dS_next, S> part per wave)
+    static constexpr int off_db = off_f + 4 * C;         // E L column sums, one row per row block
+    static constexpr int floats = off_db + 6 * C;        // dbeta parts: [4][C] by row block, [2][C] by half
     static constexpr size_t bytes = sizeof(float) * floats;
     static_assert(off_buf % 4 == 0 && VBUF % 4 == 0, "16-byte aligned buffers");
     static_assert(bytes <= 160 * 1024, "one block per CU: at most the 160 KiB of LDS");
@@ -1077,9 +1078,13 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(int H, int DV, int T, int
     auto q_at = [&](int r, int c) { return SPL ? __uint_as_float((uint32_t)sqb[r * KB + c] << 16) : sq[r * KP + c]; };
     auto k_at = [&](int r, int c) { return SPL ? __uint_as_float((uint32_t)skb[r * KB + c] << 16) : sk[r * KP + c]; };
     float *vg = smem + L::off_vec, *vgam = vg + C, *vkap = vg + 2 * C, *vb = vg + 3 * C;
-    float *vdgam = vg + 4 * C, *vdkap = vg + 5 * C, *vdb = vg + 6 * C;
-    float *vgl = vg + 7 * C;   // per-wave parts of <dS_next, S>
+    float *vdgam = vg + 4 * C, *vdkap = vg + 5 * C;
+    float *vgl = vg + 6 * C;   // per-wave parts of <dS_next, S>
     float *vF = smem + L::off_f;   // [4][C]
+    // dbeta's parts, one slot per writer, summed in a fixed order at the end:
+    // column sums of dM o T by the row block that formed them, and row sums
+    // of dA o (Gamma o K K^T) by the half that formed them
+    float *vdbc = smem + L::off_db, *vdbr = vdbc + 4 * C;
     if (!cpr && meta[1] != 0) return;
     const int nitems = (cpr ? urows : meta[0]) * H;
     int tid = threadIdx.x;
@@ -1301,7 +1306,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(int H, int DV, int T, int
         *reinterpret_cast<float4_t *>(st + r * CP + c) = ts[m];
     }
     if (tid < 4 * C) vg[tid] = vv0;
-    if (tid < 3 * C) vdgam[tid] = 0.f;   // dgamma, dkappa and dbeta accumulate atomically
+    if (tid < 2 * C) vdgam[tid] = 0.f;   // dgamma and dkappa: two addends per slot
     if (tid < 4 * C) vF[tid] = 0.f;
     if constexpr (L::NBUF == 2) {   // block 0 staged with the rest
         stage_block(VB, 0, buf0);
@@ -1385,7 +1390,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(int H, int DV, int T, int
             if (c <= wr) {
                 cs += __shfl_xor(cs, 16, 64);
                 cs += __shfl_xor(cs, 32, 64);
-                if (jj == 0) atomicAdd(&vdb[16 * c + nn], cs);
+                if (jj == 0) vdbc[wr * C + 16 * c + nn] = cs;
             }
         }
     } else {
@@ -1433,6 +1438,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(int H, int DV, int T, int
     // c); with K K^T, Q K^T and Gamma form dbeta's second part, dK o, dP o
     // Gamma and E = dGamma o Gamma.
     float4_t dkk[2];
+    float dbr[4] = {0.f, 0.f, 0.f, 0.f};   // the wave's row sums for dbeta, tile by tile
 #pragma unroll
     for (int ci = 0; ci < 2; ++ci) {
         const int c = 2 * ci + half;
@@ -1460,11 +1466,13 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(int H, int DV, int T, int
             // E = dGamma o Gamma with dGamma = dP o Q K^T + dB o K K^T
             const float dgg = dpv * pv + dB * gv;
             sp[r * CP + cc] = dpv * gm;         // dP o Gamma
-            const float rs = row16_sum(db2);
-            if (nn == 0) atomicAdd(&vdb[r], rs);
+            dbr[i] += row16_sum(db2);
             sdt[r * CP + cc] = cc < r ? dgg : 0.f;   // strictly lower; the upper tiles hold dT's zeros
         }
     }
+    if (nn == 0)   // every wave writes its rows' slot, zero where it had no tile
+#pragma unroll
+        for (int i = 0; i < 4; ++i) vdbr[half * C + rw + 4 * jj + i] = dbr[i];
     __syncthreads();
     // dK o (strictly lower) into sw (W is no longer needed)
 #pragma unroll
@@ -1552,9 +1560,10 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(int H, int DV, int T, int
             }
         }
     } else {
+        // fp32 products, every k-tile issued (as in the split form): where a
+        // tile lies above (dQ) or below (dK) the wave's rows dP o Gamma is zero.
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
-            const bool lo = kt <= wr, hi = kt >= wr;
             const float4_t a1 = *reinterpret_cast<const float4_t *>(sp + (rw + nn) * CP + 16 * kt + 4 * jj);
             const float4_t w1 = *reinterpret_cast<const float4_t *>(sw + (rw + nn) * CP + 16 * kt + 4 * jj);
             float a2[4], a3[4];
@@ -1576,12 +1585,10 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(int H, int DV, int T, int
                 }
 #pragma unroll
                 for (int i = 0; i < 4; ++i) mfma4(acck[a], a3[i], bk[i]);
-                if (lo)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) mfma4(accq[a], a1[i], bk[i]);
-                if (hi)
+                for (int i = 0; i < 4; ++i) mfma4(accq[a], a1[i], bk[i]);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) mfma4(acck[a], a2[i], bq[i]);
+                for (int i = 0; i < 4; ++i) mfma4(acck[a], a2[i], bq[i]);
             }
         }
     }
@@ -1616,7 +1623,10 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(int H, int DV, int T, int
         if (i < len) {
             const int64_t th = (int64_t)(tok0 + i) * H + h;
             dla[th] = gl * vgam[len - 1] + sfx + pre + f;
-            dbeta[th] = vdb[i];
+            // column-sum parts of the row blocks at or below column i's block, then the row sums
+            float db = 0.f;
+            for (int b = i / 16; b < 4; ++b) db += vdbc[b * C + i];
+            dbeta[th] = (db + vdbr[i]) + vdbr[C + i];
         }
     }
     }   // items
