@@ -573,7 +573,7 @@ __global__ __launch_bounds__(64) void chunk_prep_kernel(int H, int T, int cpr, i
 // Waves of a state-pass block that stage inputs (the others compute).
 constexpr int kStagers = 4;
 
-template <typename in_t, typename OP, int DK, int NW, bool OUT>
+template <typename in_t, typename OP, int DK, int NW, bool OUT, int SPLIT = 1>
 struct StateSmem {
     static constexpr int BV = 16 * NW;                                  // value columns per block
     static constexpr int QROW = DK * (int)sizeof(OP) + 32;              // bytes per Q / K row
@@ -592,7 +592,13 @@ struct StateSmem {
     static constexpr size_t k_rel = OUT ? QK : 0;
     static constexpr size_t dma_off(int b) { return (size_t)QKB * NQK * QK + (size_t)b * DMA; }
     static constexpr size_t m_rel = VB, p_rel = VB + MP, g_rel = VB + NMP * MP;
-    static constexpr size_t bytes = (size_t)QKB * NQK * QK + 2 * DMA;
+    // Split waves (SPLIT == 2): per column group and dk half, the lane-major
+    // partial K S^T (4 tiles) and the partial Q S^T of the partner's two row
+    // tiles, 16 bytes per (tile, lane).
+    static constexpr size_t XCH_X = 4 * 64 * 16, XCH_Q = 2 * 64 * 16;
+    static constexpr size_t xch_off = (size_t)QKB * NQK * QK + 2 * DMA;
+    static constexpr size_t xch_bytes = SPLIT == 2 ? (size_t)NW * 2 * (XCH_X + XCH_Q) : 0;
+    static constexpr size_t bytes = xch_off + xch_bytes;
     static constexpr int NV = (int)(VB / 1024), NM = (int)(MP / 1024);
     static constexpr int NDMA = NV + NMP * NM + 1;                       // 1 KiB wave copies per chunk
     static_assert(VB % 1024 == 0 && MP % 1024 == 0, "direct loads move whole 1 KiB wave blocks");
@@ -680,8 +686,8 @@ __device__ __forceinline__ void dma16(const void *g, uint32_t lds) {
         : "memory");
 }
 
-template <typename in_t, typename OP, int DK, int NW, bool OUT>
-__global__ __launch_bounds__(64 * (NW + kStagers)) void chunk_state_kernel(
+template <typename in_t, typename OP, int DK, int NW, bool OUT, int SPLIT>
+__global__ __launch_bounds__(64 * (NW * SPLIT + kStagers)) void chunk_state_kernel(
     int NU, int H, int DV, int nvt, int odt, int T, int cpr, int32_t *__restrict__ meta,
     const int32_t *__restrict__ cu_ws, const int32_t *__restrict__ row0, SegArgs sg,
     const in_t *__restrict__ q, const in_t *__restrict__ k, const in_t *__restrict__ v,
@@ -690,8 +696,12 @@ __global__ __launch_bounds__(64 * (NW + kStagers)) void chunk_state_kernel(
     using M = Mma<OP>;
     using frag = typename M::frag;
     using F2 = Frag2<OP>;
-    using L = StateSmem<in_t, OP, DK, NW, OUT>;
+    using L = StateSmem<in_t, OP, DK, NW, OUT, SPLIT>;
     constexpr int QROW = L::QROW, VROW = L::VROW, BV = L::BV, QKB = L::QKB;
+    static_assert(SPLIT == 1 || (SPLIT == 2 && OUT && QKB == 2 && DK >= 64 && L::bytes <= 160 * 1024),
+                  "split waves: output pass, two Q/K buffers, dk >= 64, one block per compute unit");
+    constexpr int NCW = NW * SPLIT;                          // compute waves
+    constexpr int KTW = DK / 16 / SPLIT;                     // state tiles per compute wave
     constexpr int NT = 64 * kStagers;                        // staging threads
     constexpr int KT = DK / 16;                              // state tiles along dk
     constexpr int KP = DK / 32;                              // k-tile pairs along dk
@@ -737,11 +747,13 @@ __global__ __launch_bounds__(64 * (NW + kStagers)) void chunk_state_kernel(
     if (vb >= DVA) return;
     const int chain = n * H + h;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, nn = l & 15, jj = l >> 4;
-    // Waves 0..NW-1 compute (16 value columns each); the kStagers waves after
-    // them stage the next chunk's inputs into LDS.
-    const bool stager = w >= NW;
-    const int sw = w - NW, stid = tid - 64 * NW;  // stager wave / thread index
-    const int v0 = vb + w * 16;             // first value column of a compute wave
+    // Waves 0..NCW-1 compute: wave w holds 16 value columns (column group
+    // cg = w / SPLIT) and, with split waves, one half of dk (hh = w % SPLIT);
+    // the kStagers waves after them stage the next chunk's inputs into LDS.
+    const bool stager = w >= NCW;
+    const int sw = w - NCW, stid = tid - 64 * NCW;  // stager wave / thread index
+    const int cg = w / SPLIT, hh = w % SPLIT;
+    const int v0 = vb + cg * 16;            // first value column of a compute wave
     const bool active = !stager && v0 < DVA;
     const bool ident = v0 >= DV;            // a column of F (transition pass only)
     // The chunks this block runs: all of the sequence's, or one segment.
@@ -765,11 +777,11 @@ __global__ __launch_bounds__(64 * (NW + kStagers)) void chunk_state_kernel(
         kt_lane = 4 * jj * QROW + 4 * (8 * (nn >> 2) + (nn & 3));
     int v_lane[4];                                                  // V in accumulator layout
     if constexpr (sizeof(in_t) == 2) {
-        const int row = 4 * jj + (nn >> 2), unit = 2 * w + ((nn & 3) >> 1);
+        const int row = 4 * jj + (nn >> 2), unit = 2 * cg + ((nn & 3) >> 1);
         v_lane[0] = row * VROW + 16 * (unit ^ (row & L::VSWZ)) + 8 * (nn & 1);
         v_lane[1] = v_lane[2] = v_lane[3] = v_lane[0];
     } else {
-        const int unit = 4 * w + (nn >> 2);
+        const int unit = 4 * cg + (nn >> 2);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row = 4 * jj + i;
@@ -783,7 +795,8 @@ __global__ __launch_bounds__(64 * (NW + kStagers)) void chunk_state_kernel(
     // transition pass over a first segment), the segment's incoming state
     // from the combine pass (output pass over segments), or zero / identity
     // (transition pass over a later segment).
-    float4_t sT[KT];
+    // With split waves a wave holds the KTW tiles hh KTW .. hh KTW + KTW - 1.
+    float4_t sT[KTW];
     const float *s_in = nullptr;
     int64_t s_in_row = 0;   // element offset of the lane's state row
     if (OUT && sg.seg_chunks) {
@@ -794,8 +807,9 @@ __global__ __launch_bounds__(64 * (NW + kStagers)) void chunk_state_kernel(
         s_in_row = ((int64_t)chain * DV + v0 + nn) * DK;
     }
 #pragma unroll
-    for (int t = 0; t < KT; ++t) {
-        const int off = 32 * (t >> 1) + 4 * (t & 1);
+    for (int t = 0; t < KTW; ++t) {
+        const int tg = hh * KTW + t;
+        const int off = 32 * (tg >> 1) + 4 * (tg & 1);
         if (active && s_in && !ident) {
             sT[t] = *reinterpret_cast<const float4_t *>(s_in + s_in_row + 8 * jj + off);
         } else {
@@ -924,7 +938,7 @@ __global__ __launch_bounds__(64 * (NW + kStagers)) void chunk_state_kernel(
     // these loads.
     __builtin_amdgcn_s_waitcnt(0);
 #pragma unroll
-    for (int t = 0; t < KT; ++t) asm volatile("" : "+v"(sT[t]));
+    for (int t = 0; t < KTW; ++t) asm volatile("" : "+v"(sT[t]));
 
     // Output stores of the last chunk.  Their data and address registers are
     // left untouched until the next chunk rewrites them (phase 7): reusing
@@ -959,6 +973,37 @@ __global__ __launch_bounds__(64 * (NW + kStagers)) void chunk_state_kernel(
                     __builtin_nontemporal_store(oq[rt], reinterpret_cast<__attribute__((address_space(1))) float4_t *>(oa[rt]));
                 else
                     __builtin_nontemporal_store(oh[rt], reinterpret_cast<__attribute__((address_space(1))) u32x2_t *>(oa[rt]));
+            }
+        }
+    };
+
+    // Output stores of a split wave: its two row tiles 2 hh, 2 hh + 1 (the
+    // data and address registers are kept as above).
+    auto keep_stores2 = [&]() {
+        asm volatile("" ::"v"(oq[0]), "v"(oq[1]), "v"(oh[0]), "v"(oh[1]), "v"(oa[0]), "v"(oa[1]));
+    };
+    auto store_o2 = [&](int t0, int len) {
+        const int64_t obase = ((int64_t)t0 * H + h) * DV + v0 + 4 * jj + (int64_t)nn * H * DV;
+        const int64_t ostep = (int64_t)16 * H * DV;
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+            const int rt = 2 * hh + k2;
+            oa[k2] = reinterpret_cast<uint64_t>(o) + (uint64_t)((obase + rt * ostep) * osize);
+            if (odt == DT_BF16) {
+                oh[k2] = u32x2_t{from_f32<bf16_t>(oq[k2][0]).bits | ((uint32_t)from_f32<bf16_t>(oq[k2][1]).bits << 16),
+                                 from_f32<bf16_t>(oq[k2][2]).bits | ((uint32_t)from_f32<bf16_t>(oq[k2][3]).bits << 16)};
+            } else if (odt == DT_FP16) {
+                oh[k2] = __builtin_bit_cast(u32x2_t, half4_t{(_Float16)oq[k2][0], (_Float16)oq[k2][1],
+                                                             (_Float16)oq[k2][2], (_Float16)oq[k2][3]});
+            }
+        }
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+            if (len == C || 16 * (2 * hh + k2) + nn < len) {
+                if (odt == DT_FP32)
+                    __builtin_nontemporal_store(oq[k2], reinterpret_cast<__attribute__((address_space(1))) float4_t *>(oa[k2]));
+                else
+                    __builtin_nontemporal_store(oh[k2], reinterpret_cast<__attribute__((address_space(1))) u32x2_t *>(oa[k2]));
             }
         }
     };
@@ -998,6 +1043,7 @@ __global__ __launch_bounds__(64 * (NW + kStagers)) void chunk_state_kernel(
                 dma(ci + 1, b ^ 1);
                 commit_qk(b ^ 1, min(C, len_seq - (ci + 1) * C), cur);
             }
+            if constexpr (SPLIT == 2) asm volatile("s_barrier" ::: "memory");   // the split waves' exchange
         } else {
 #pragma unroll
             for (int it = 0; it < QK_IT; ++it) {
@@ -1009,7 +1055,7 @@ __global__ __launch_bounds__(64 * (NW + kStagers)) void chunk_state_kernel(
         }
     };
     // Compute step ci.
-    auto compute = [&](int ci) {
+    auto compute = [&](auto ci) {   // (generic: instantiated only where called)
         const int t0 = tok0 + ci * C;
         const int len = min(C, len_seq - ci * C);
         const int b = ci & 1;
@@ -1198,6 +1244,181 @@ __global__ __launch_bounds__(64 * (NW + kStagers)) void chunk_state_kernel(
         store_o(t0, len);
     };
 
+    // Compute step ci with split waves (SPLIT == 2).  The two waves of a
+    // column group hold the two dk halves of its S^T slice.  Each forms its
+    // half of K S^T and of Q S^T from its own k-tile pairs; the halves meet
+    // in LDS at one extra block barrier per chunk (the stagers take it too).
+    // Both waves then add the two K S^T halves in the same order (low half
+    // first), so they form bit-identical Y, V' and kappa o V'; each updates
+    // its own state half, and outputs its own two row tiles of O, adding the
+    // partner's Q S^T half for them.  The chain per chunk is half of K S^T,
+    // V' = M Y and half of the update.
+    auto compute2 = [&](auto ci) {
+        const int t0 = tok0 + ci * C;
+        const int len = min(C, len_seq - ci * C);
+        const int b = ci & 1;
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        if (!active) {
+            asm volatile("s_barrier" ::: "memory");
+            return;
+        }
+        constexpr int KPH = KP / 2 > 0 ? KP / 2 : 1;    // the wave's k-tile pairs
+        constexpr int NXH = 4 * KPH;                    // its K (and Q) row fragments
+        const int p0 = hh * KPH;
+        const unsigned char *Qb = smem + L::qk_off(b);
+        const unsigned char *Kb = Qb + L::k_rel;
+        const unsigned char *Db = smem + L::dma_off(b);
+        const OP *Ms = reinterpret_cast<const OP *>(Db + L::m_rel);
+        const OP *Ps = reinterpret_cast<const OP *>(Db + L::p_rel);
+        const float *gam_s = reinterpret_cast<const float *>(Db + L::g_rel);
+        const float *kap_s = gam_s + C;
+        const float *gao_s = gam_s + 2 * C;
+        // exchange slots (lane-major, 16 bytes per tile and lane)
+        unsigned char *xch = smem + L::xch_off + (size_t)cg * 2 * (L::XCH_X + L::XCH_Q);
+        float4_t *x_mine = reinterpret_cast<float4_t *>(xch + hh * L::XCH_X) + l;
+        const float4_t *x_part = reinterpret_cast<const float4_t *>(xch + (1 - hh) * L::XCH_X) + l;
+        float4_t *q_mine = reinterpret_cast<float4_t *>(xch + 2 * L::XCH_X + hh * L::XCH_Q) + l;
+        const float4_t *q_part = reinterpret_cast<const float4_t *>(xch + 2 * L::XCH_X + (1 - hh) * L::XCH_Q) + l;
+
+        auto rd_row = [&](const unsigned char *blk, int i) {   // item i: (pair p0 + i / 4, row tile i % 4)
+            return row_frag2(reinterpret_cast<const OP *>(blk + 16 * (i % 4) * QROW + frag_lane) + 32 * (p0 + i / 4));
+        };
+        auto tri_pair = [&](const OP *T, int mt, int p) {
+            const int k0 = 2 * p, k1 = 2 * p + 1;
+            const frag lo = k0 <= mt ? lds_frag(T + tri_index(mt, k0) * kTileElems + tile_lane) : M::zero();
+            const frag hi = k1 <= mt ? lds_frag(T + tri_index(mt, k1) * kTileElems + tile_lane) : M::zero();
+            return F2::make(lo, hi);
+        };
+        constexpr int PMT[6] = {0, 1, 2, 3, 2, 3}, PP[6] = {0, 0, 0, 0, 1, 1};
+        auto rd_kt = [&](int t, int tp) {   // t: the wave's tile index
+            const int tg = hh * KTW + t, p = tg >> 1, hs = tg & 1;
+            const unsigned char *kt = Kb + kt_lane + OPB * (32 * p + 4 * hs) + 32 * tp * QROW;
+            return F2::make(kt_frag(kt, QROW, (OP *)nullptr), kt_frag(kt + 16 * QROW, QROW, (OP *)nullptr));
+        };
+
+        // -- phase 0: the wave's K and Q fragments, V, gamma; its S half as an operand --
+        const float gC = gam_s[4 * C - 1];
+        F2 kf[NXH], qf[NXH];
+#pragma unroll
+        for (int i = 0; i < NXH; ++i) kf[i] = rd_row(Kb, i);
+#pragma unroll
+        for (int i = 0; i < NXH; ++i) qf[i] = rd_row(Qb, i);
+        typename VFrag<in_t>::raw vraw[4];
+        float4_t gm[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            vraw[mt] = VFrag<in_t>::read(Db + 16 * mt * VROW, v_lane);
+            gm[mt] = *reinterpret_cast<const float4_t *>(gam_s + 16 * mt + 4 * jj);
+        }
+        F2 sB[KPH];
+#pragma unroll
+        for (int p = 0; p < KPH; ++p) sB[p] = F2::cvt(sT[2 * p], sT[2 * p + 1]);
+        __builtin_amdgcn_sched_barrier(0);
+
+        // -- phase 1: the halves of X_K = K S^T and of Q S^T; they go to LDS --
+        float4_t x[4], qs[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) x[mt] = qs[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < NXH; ++i) mma2(x[i % 4], kf[i], sB[i / 4]);
+#pragma unroll
+        for (int i = 0; i < NXH; ++i) mma2(qs[i % 4], sB[i / 4], qf[i]);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) x_mine[64 * mt] = x[mt];
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) q_mine[64 * k2] = hh == 0 ? qs[2 + k2] : qs[k2];   // the partner's rows
+        F2 mpair[6];
+#pragma unroll
+        for (int jx = 0; jx < 6; ++jx) mpair[jx] = tri_pair(Ms, PMT[jx], PP[jx]);
+#pragma unroll
+        for (int t = 0; t < KTW; ++t) sT[t] *= gC;   // the update adds K^T (kappa o V') later
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+
+        // -- phase 2: the whole X_K (low half + high half), Y = V - diag(gamma) X_K --
+        F2 yB[2];
+        {
+            float4_t y[4];
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                const float4_t xp = x_part[64 * mt];
+                const float4_t xs = hh == 0 ? x[mt] + xp : xp + x[mt];
+                y[mt] = VFrag<in_t>::to_f32(vraw[mt]) - gm[mt] * xs;
+            }
+            yB[0] = F2::cvt(y[0], y[1]);
+            yB[1] = F2::cvt(y[2], y[3]);
+        }
+        float4_t qp[2];
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) qp[k2] = q_part[64 * k2];
+        __builtin_amdgcn_sched_barrier(0);
+
+        // -- phase 3: V' = M Y; kappa; the wave's K^T fragments --
+        float4_t Vp[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) Vp[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int jx = 0; jx < 6; ++jx) mma2(Vp[PMT[jx]], mpair[jx], yB[PP[jx]]);
+        float4_t kp4[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) kp4[mt] = *reinterpret_cast<const float4_t *>(kap_s + 16 * mt + 4 * jj);
+        F2 ka[KTW][2];
+#pragma unroll
+        for (int t = 0; t < KTW; ++t) {
+            ka[t][0] = rd_kt(t, 0);
+            ka[t][1] = rd_kt(t, 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+
+        // -- phase 5: kappa o V' and the operand forms of V' --
+        F2 vB[2], dB[2];
+        {
+            float4_t d[4];
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) d[mt] = kp4[mt] * Vp[mt];
+            vB[0] = F2::cvt(Vp[0], Vp[1]);
+            vB[1] = F2::cvt(Vp[2], Vp[3]);
+            dB[0] = F2::cvt(d[0], d[1]);
+            dB[1] = F2::cvt(d[2], d[3]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+
+        // -- phase 6: the update of the wave's state half --
+#pragma unroll
+        for (int t = 0; t < KTW; ++t) mma2(sT[t], ka[t][0], dB[0]);
+#pragma unroll
+        for (int t = 0; t < KTW; ++t) mma2(sT[t], ka[t][1], dB[1]);
+        // P tiles of the wave's row tiles mt = 2 hh + k2 as k-tile pairs 0
+        // and 1 (pair 1 is zero for the upper half's partner rows 0 and 1)
+        F2 ppA[2], ppB[2];
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+            ppA[k2] = tri_pair(Ps, 2 * hh + k2, 0);
+            ppB[k2] = tri_pair(Ps, 2 * hh + k2, 1);
+        }
+        float g1[2];
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) g1[k2] = gao_s[16 * (2 * hh + k2) + nn];
+        __builtin_amdgcn_sched_barrier(0);
+
+        // -- phase 7: the wave's two row tiles of O^T = (S Q^T) diag(gamma) + V'^T P^T --
+        // (no matrix instruction here depends on hh by a branch: the zero
+        // pair of the lower half's rows is multiplied like any other)
+        float4_t pv[2] = {float4_t{0.f, 0.f, 0.f, 0.f}, float4_t{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) mma2(pv[k2], vB[0], ppA[k2]);
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) mma2(pv[k2], vB[1], ppB[k2]);
+        keep_stores2();
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+            const float4_t q = hh == 0 ? qs[k2] : qs[2 + k2];
+            const float4_t sum = hh == 0 ? q + qp[k2] : qp[k2] + q;
+            oq[k2] = sum * g1[k2] + pv[k2];
+        }
+        store_o2(t0, len);
+    };
+
     if (stager) {
         if (nchunks > 0) {
             prefetch_qk(0, RA);
@@ -1226,7 +1447,11 @@ __global__ __launch_bounds__(64 * (NW + kStagers)) void chunk_state_kernel(
         }
         return;
     }
-    for (int ci = 0; ci < nchunks; ++ci) compute(ci);
+    if constexpr (SPLIT == 2) {
+        for (int ci = 0; ci < nchunks; ++ci) compute2(ci);
+    } else {
+        for (int ci = 0; ci < nchunks; ++ci) compute(ci);
+    }
 
     // The state leaving the block's chunks: the sequence's final state (output
     // pass over its last segment), or the segment's map (transition pass).
@@ -1241,8 +1466,10 @@ __global__ __launch_bounds__(64 * (NW + kStagers)) void chunk_state_kernel(
     }
     if (active && s_out) {
 #pragma unroll
-        for (int t = 0; t < KT; ++t)
-            *reinterpret_cast<float4_t *>(s_out + s_out_row + 8 * jj + 32 * (t >> 1) + 4 * (t & 1)) = sT[t];
+        for (int t = 0; t < KTW; ++t) {
+            const int tg = hh * KTW + t;
+            *reinterpret_cast<float4_t *>(s_out + s_out_row + 8 * jj + 32 * (tg >> 1) + 4 * (tg & 1)) = sT[t];
+        }
     }
 }
 
@@ -1474,11 +1701,11 @@ static hipError_t allow_smem(K kernel, size_t bytes) {
 // empty batch still reads as equal-length), 0 for a packed one.
 static int uniform_cpr(const ChunkArgs &a) { return a.cu_seqlens ? 0 : (a.T + C - 1) / C + (a.T == 0); }
 
-template <typename in_t, typename OP, int DK, int NW, bool OUT>
+template <typename in_t, typename OP, int DK, int NW, bool OUT, int SPLIT = 1>
 static hipError_t launch_state(const ChunkArgs &a, const ChunkWorkspace &w, const SegArgs &sg, int64_t NU,
                                hipStream_t st) {
-    using L = StateSmem<in_t, OP, DK, NW, OUT>;
-    auto kern = chunk_state_kernel<in_t, OP, DK, NW, OUT>;
+    using L = StateSmem<in_t, OP, DK, NW, OUT, SPLIT>;
+    auto kern = chunk_state_kernel<in_t, OP, DK, NW, OUT, SPLIT>;
     hipError_t e = allow_smem(kern, L::bytes);
     if (e != hipSuccess) return e;
     char *ws = static_cast<char *>(a.workspace);
@@ -1486,7 +1713,7 @@ static hipError_t launch_state(const ChunkArgs &a, const ChunkWorkspace &w, cons
     const int nvt = ((cols + 15) / 16 + NW - 1) / NW;
     const int64_t blocks = ((NU + 7) / 8) * 8 * nvt;
     ProfScope prof(OUT ? "gdn_chunk_state" : "gdn_chunk_transition", st);
-    kern<<<dim3((unsigned)blocks), dim3(64 * (NW + kStagers)), L::bytes, st>>>(
+    kern<<<dim3((unsigned)blocks), dim3(64 * (NW * SPLIT + kStagers)), L::bytes, st>>>(
         (int)NU, a.H, a.dv, nvt, a.out_dtype, a.T, uniform_cpr(a), reinterpret_cast<int32_t *>(ws + w.off_meta),
         reinterpret_cast<const int32_t *>(ws + w.off_cu), reinterpret_cast<const int32_t *>(ws + w.off_row0), sg,
         static_cast<const in_t *>(a.q), static_cast<const in_t *>(a.k), static_cast<const in_t *>(a.v),
@@ -1495,9 +1722,33 @@ static hipError_t launch_state(const ChunkArgs &a, const ChunkWorkspace &w, cons
     return hipGetLastError();
 }
 
+// Split waves for the output pass: each 16-column slice of the state is held
+// by two waves, one per dk half, which halves the serial chain of a chunk
+// step and doubles the waves in flight, at the price of one more block
+// barrier and an LDS exchange per chunk.  Measured on the prefill workload
+// it is slower (143 against 115 us: the exchange triples the waves' LDS wait
+// cycles and the extra barrier ties the compute waves to the stagers), so
+// it is off unless GDN_STATE_SPLIT=1 asks for it (dk >= 64, 16-bit inputs).
+static bool use_split_waves(int dk, int dv, int64_t units) {
+    (void)dv;
+    (void)units;
+    const char *env = getenv("GDN_STATE_SPLIT");
+    return env && *env && dk >= 64 && atoi(env) != 0;
+}
+
+// Whether a split-wave block (two column groups) is built for these types.
+template <typename in_t, typename OP, int DK>
+constexpr bool split_built() {
+    using L = StateSmem<in_t, OP, DK, 2, true, 2>;
+    return DK >= 64 && L::QKB == 2 && L::bytes <= 160 * 1024;
+}
+
 template <typename in_t, typename OP, int DK, bool OUT>
 static hipError_t launch_state_nw(const ChunkArgs &a, const ChunkWorkspace &w, const SegArgs &sg, int64_t NU,
                                   hipStream_t st) {
+    if constexpr (OUT && split_built<in_t, OP, DK>()) {
+        if (use_split_waves(DK, a.dv, NU)) return launch_state<in_t, OP, DK, 2, true, 2>(a, w, sg, NU, st);
+    }
     const int cols = OUT ? a.dv : a.dv + a.dk;
     switch (state_waves_per_block(cols, NU, OUT ? "GDN_STATE_WAVES" : "GDN_TRANSITION_WAVES")) {
     case 4: return launch_state<in_t, OP, DK, 4, OUT>(a, w, sg, NU, st);

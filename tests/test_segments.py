@@ -101,3 +101,22 @@ def test_segmented_malformed_cu(monkeypatch):
     torch.cuda.synchronize()
     assert gdn.chunk_fwd_check(ws) != 0
     assert bool((o == 7.0).all()) and bool((fin == 5.0).all())
+
+
+@pytest.mark.parametrize("B,T,H,dk,dv,dt", [(2, 300, 3, 128, 128, "bf16"), (1, 257, 2, 64, 96, "fp16"),
+                                            (3, 130, 2, 128, 32, "bf16")])
+def test_split_waves_parity(B, T, H, dk, dv, dt, monkeypatch):
+    """The output pass with each state slice split over two waves (one per dk
+    half, forced with GDN_STATE_SPLIT) against the oracle and against the
+    unsplit pass."""
+    inp = W.chunk_inputs(B, T, H, dk, dv, dt, seed=T + dv, init_std=0.1, name=f"split waves B{B} T{T} dk{dk} dv{dv}")
+    monkeypatch.setenv("GDN_SEG_CHUNKS", "0")
+    monkeypatch.setenv("GDN_STATE_SPLIT", "1")
+    o, S = run_chunk(inp)
+    check_parity(inp, o, S)
+    monkeypatch.setenv("GDN_STATE_SPLIT", "0")
+    o0, S0 = run_chunk(inp)
+    rms = float(o0.float().pow(2).mean().sqrt())
+    e = max(float((o - o0).abs().max()), float((S - S0).abs().max())) / rms
+    log(f"[split vs unsplit] {inp.name}: {e:.3e}")
+    assert e <= TOL[dt]
