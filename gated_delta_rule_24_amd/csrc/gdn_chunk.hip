@@ -264,7 +264,10 @@ struct PrepRegs {
     float la, bt;
 };
 
-template <typename in_t, typename OP, int DK>
+// WITH_P = false: the state pass forms P itself (see chunk_state_kernel), so
+// G1 reads no Q and writes no P; the third decay vector (gamma / ||q||) is
+// then written by the state pass too.
+template <typename in_t, typename OP, int DK, bool WITH_P = true>
 __global__ __launch_bounds__(64) void chunk_prep_kernel(int H, int T, int cpr, int urows, int qk_norm,
                                                         const int32_t *__restrict__ meta,
                                                         const int32_t *__restrict__ row_tok,
@@ -306,11 +309,13 @@ __global__ __launch_bounds__(64) void chunk_prep_kernel(int H, int T, int cpr, i
 #pragma unroll
             for (int p = 0; p < PP; ++p) R.k[b][p].load(k + off + 32 * p);
         }
+        if constexpr (WITH_P) {
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const int64_t off = base + (int64_t)min(16 * b + nn, len - 1) * tok_stride;
+            for (int b = 0; b < 4; ++b) {
+                const int64_t off = base + (int64_t)min(16 * b + nn, len - 1) * tok_stride;
 #pragma unroll
-            for (int p = 0; p < PP; ++p) R.q[b][p].load(q + off + 32 * p);
+                for (int p = 0; p < PP; ++p) R.q[b][p].load(q + off + 32 * p);
+            }
         }
     };
 
@@ -332,7 +337,7 @@ __global__ __launch_bounds__(64) void chunk_prep_kernel(int H, int T, int cpr, i
 #pragma unroll
                         for (int p = 0; p < PP; ++p) {
                             R.k[b][p].zero();
-                            R.q[b][p].zero();
+                            if constexpr (WITH_P) R.q[b][p].zero();
                         }
             }
         };
@@ -367,9 +372,11 @@ __global__ __launch_bounds__(64) void chunk_prep_kernel(int H, int T, int cpr, i
                         R.k[b][p].to_f32(f);
 #pragma unroll
                         for (int e = 0; e < 8; ++e) ssk[b] += f[e] * f[e];
-                        R.q[b][p].to_f32(f);
+                        if constexpr (WITH_P) {
+                            R.q[b][p].to_f32(f);
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) ssq[b] += f[e] * f[e];
+                            for (int e = 0; e < 8; ++e) ssq[b] += f[e] * f[e];
+                        }
                     }
             }
 #pragma unroll
@@ -379,7 +386,7 @@ __global__ __launch_bounds__(64) void chunk_prep_kernel(int H, int T, int cpr, i
 #pragma unroll
                 for (int p = 0; p < PP; ++p) {
                     gram_mma(gacc[t], R.k[b][p], R.k[a][p]);
-                    gram_mma(pacc[t], R.k[b][p], R.q[a][p]);
+                    if constexpr (WITH_P) gram_mma(pacc[t], R.k[b][p], R.q[a][p]);
                 }
             }
         }
@@ -403,6 +410,7 @@ __global__ __launch_bounds__(64) void chunk_prep_kernel(int H, int T, int cpr, i
             const float sq = jj == 0 ? ssq[0] : (jj == 1 ? ssq[1] : (jj == 2 ? ssq[2] : ssq[3]));
             rk = sk > 0.f ? rsqrtf(sk) : 0.f;
             rq = sq > 0.f ? rsqrtf(sq) : 0.f;
+            if constexpr (!WITH_P) rq = 1.f;
         }
         qn[l] = rq;
         kn[l] = rk;
@@ -457,7 +465,8 @@ __global__ __launch_bounds__(64) void chunk_prep_kernel(int H, int T, int cpr, i
                 *reinterpret_cast<float4_t *>(blk + a * BS + nn * BP + 4 * jj) = av;
                 aR[t] = float4_t{0.f, 0.f, 0.f, 0.f};
             }
-            *reinterpret_cast<typename M::frag *>(ws_p + (rh * kTriTiles + t) * kTileElems + 4 * l) = M::cvt(pv);
+            if constexpr (WITH_P)
+                *reinterpret_cast<typename M::frag *>(ws_p + (rh * kTriTiles + t) * kTileElems + 4 * l) = M::cvt(pv);
         }
         asm volatile("" ::: "memory");
 
@@ -573,8 +582,13 @@ __global__ __launch_bounds__(64) void chunk_prep_kernel(int H, int T, int cpr, i
 // Waves of a state-pass block that stage inputs (the others compute).
 constexpr int kStagers = 4;
 
-template <typename in_t, typename OP, int DK, int NW, bool OUT, int SPLIT = 1>
+template <typename in_t, typename OP, int DK, int NW, bool OUT, int SPLIT = 1, bool FP = false>
 struct StateSmem {
+    // Loading waves (the stagers) and, with FP, two more waves that form P
+    // for alternate chunks.
+    static constexpr int NMK = FP ? 2 : 0;
+    static constexpr int NLD = (FP && NW * SPLIT >= 4) ? kStagers - 2 : kStagers;
+    static constexpr int WAVES = NW * SPLIT + NLD + NMK;
     static constexpr int BV = 16 * NW;                                  // value columns per block
     static constexpr int QROW = DK * (int)sizeof(OP) + 32;              // bytes per Q / K row
     static constexpr int VROW = BV * (int)sizeof(in_t);                 // bytes per V row
@@ -586,21 +600,25 @@ struct StateSmem {
     static constexpr size_t MP = sizeof(OP) * kTriTiles * kTileElems;   // one M or P block
     static constexpr int NMP = OUT ? 2 : 1;                             // M and P, or M alone
     static constexpr size_t GB = 1024;                                  // the four decay vectors
-    static constexpr size_t DMA = VB + NMP * MP + GB;                   // directly loaded inputs
+    static constexpr size_t GQ = FP ? 256 : 0;                          // gamma / ||q|| from the P wave
+    static constexpr size_t DMA = VB + NMP * MP + GB + GQ;              // a chunk's inputs (copied or formed)
     static constexpr int QKB = (2 * NQK * QK + 2 * DMA <= 160 * 1024) ? 2 : 1;   // Q/K buffers
     static constexpr size_t qk_off(int b) { return (size_t)b * NQK * QK; }       // Q (if any), then K
     static constexpr size_t k_rel = OUT ? QK : 0;
     static constexpr size_t dma_off(int b) { return (size_t)QKB * NQK * QK + (size_t)b * DMA; }
-    static constexpr size_t m_rel = VB, p_rel = VB + MP, g_rel = VB + NMP * MP;
+    static constexpr size_t m_rel = VB, p_rel = VB + MP, g_rel = VB + NMP * MP, gq_rel = g_rel + GB;
     // Split waves (SPLIT == 2): per column group and dk half, the lane-major
     // partial K S^T (4 tiles) and the partial Q S^T of the partner's two row
     // tiles, 16 bytes per (tile, lane).
     static constexpr size_t XCH_X = 4 * 64 * 16, XCH_Q = 2 * 64 * 16;
     static constexpr size_t xch_off = (size_t)QKB * NQK * QK + 2 * DMA;
     static constexpr size_t xch_bytes = SPLIT == 2 ? (size_t)NW * 2 * (XCH_X + XCH_Q) : 0;
-    static constexpr size_t bytes = xch_off + xch_bytes;
+    // each P wave's g (base 2) and row-norm factors
+    static constexpr size_t mk_off = xch_off + xch_bytes, mk_bytes = NMK * 3 * 64 * 4;
+    static constexpr size_t bytes = mk_off + mk_bytes;
     static constexpr int NV = (int)(VB / 1024), NM = (int)(MP / 1024);
-    static constexpr int NDMA = NV + NMP * NM + 1;                       // 1 KiB wave copies per chunk
+    static constexpr int NPC = (OUT && !FP) ? NM : 0;                    // copies of P
+    static constexpr int NDMA = NV + NM + NPC + 1;                       // 1 KiB wave copies per chunk
     static_assert(VB % 1024 == 0 && MP % 1024 == 0, "direct loads move whole 1 KiB wave blocks");
     static_assert(QROW % 16 == 0 && VROW % 16 == 0, "16-byte rows");
 };
@@ -686,23 +704,26 @@ __device__ __forceinline__ void dma16(const void *g, uint32_t lds) {
         : "memory");
 }
 
-template <typename in_t, typename OP, int DK, int NW, bool OUT, int SPLIT>
-__global__ __launch_bounds__(64 * (NW * SPLIT + kStagers)) void chunk_state_kernel(
+template <typename in_t, typename OP, int DK, int NW, bool OUT, int SPLIT, bool FP>
+__global__ __launch_bounds__((64 * StateSmem<in_t, OP, DK, NW, OUT, SPLIT, FP>::WAVES)) void chunk_state_kernel(
     int NU, int H, int DV, int nvt, int odt, int T, int cpr, int32_t *__restrict__ meta,
     const int32_t *__restrict__ cu_ws, const int32_t *__restrict__ row0, SegArgs sg,
     const in_t *__restrict__ q, const in_t *__restrict__ k, const in_t *__restrict__ v,
+    const float *__restrict__ log_alpha, int qk_norm,
     const float *__restrict__ ws_g, const OP *__restrict__ ws_m, const OP *__restrict__ ws_p,
     const float *init_state, float *final_state, void *__restrict__ o) {
     using M = Mma<OP>;
     using frag = typename M::frag;
     using F2 = Frag2<OP>;
-    using L = StateSmem<in_t, OP, DK, NW, OUT, SPLIT>;
+    using L = StateSmem<in_t, OP, DK, NW, OUT, SPLIT, FP>;
     constexpr int QROW = L::QROW, VROW = L::VROW, BV = L::BV, QKB = L::QKB;
+    constexpr int NLD = L::NLD;                              // loading waves
+    static_assert(!FP || (OUT && SPLIT == 1 && sizeof(OP) == 2 && DK <= 128), "P formed in the state pass: output pass, 16-bit operands, dk <= 128");
     static_assert(SPLIT == 1 || (SPLIT == 2 && OUT && QKB == 2 && DK >= 64 && L::bytes <= 160 * 1024),
                   "split waves: output pass, two Q/K buffers, dk >= 64, one block per compute unit");
     constexpr int NCW = NW * SPLIT;                          // compute waves
     constexpr int KTW = DK / 16 / SPLIT;                     // state tiles per compute wave
-    constexpr int NT = 64 * kStagers;                        // staging threads
+    constexpr int NT = 64 * NLD;                             // loading threads
     constexpr int KT = DK / 16;                              // state tiles along dk
     constexpr int KP = DK / 32;                              // k-tile pairs along dk
     constexpr int QK_UNITS = C * (DK / 8);                   // 8-element pieces of Q (and K)
@@ -750,11 +771,13 @@ __global__ __launch_bounds__(64 * (NW * SPLIT + kStagers)) void chunk_state_kern
     // Waves 0..NCW-1 compute: wave w holds 16 value columns (column group
     // cg = w / SPLIT) and, with split waves, one half of dk (hh = w % SPLIT);
     // the kStagers waves after them stage the next chunk's inputs into LDS.
-    const bool stager = w >= NCW;
+    const bool stager = w >= NCW && w < NCW + NLD;
+    const bool maker = FP && w >= NCW + NLD;        // the two waves that form P (FP)
+    const int mk = w - NCW - NLD;                   // P wave index: it forms P of chunks mk, mk + 2, ...
     const int sw = w - NCW, stid = tid - 64 * NCW;  // stager wave / thread index
     const int cg = w / SPLIT, hh = w % SPLIT;
     const int v0 = vb + cg * 16;            // first value column of a compute wave
-    const bool active = !stager && v0 < DVA;
+    const bool active = !stager && !maker && v0 < DVA;
     const bool ident = v0 >= DV;            // a column of F (transition pass only)
     // The chunks this block runs: all of the sequence's, or one segment.
     int tok0 = cpr ? n * T : cu_ws[n];
@@ -887,18 +910,18 @@ __global__ __launch_bounds__(64 * (NW * SPLIT + kStagers)) void chunk_state_kern
     // zero in those rows and columns, so they stay inert.  Columns past DV
     // (inactive waves, or the F columns of a transition pass, which use zero
     // values) read column 0 and are not used.
-    constexpr int KD = (L::NDMA + kStagers - 1) / kStagers;
+    constexpr int KD = (L::NDMA + NLD - 1) / NLD;
     int dsrc[KD];   // V: elements from the chunk's first row; M, P, g: bytes
 #pragma unroll
     for (int kx = 0; kx < KD; ++kx) {
-        const int ii = sw + kStagers * kx;
+        const int ii = sw + NLD * kx;
         if (ii < L::NV) {
             const int byte = ii * 1024 + 16 * l;
             const int row = byte / VROW, unit = (byte % VROW) / 16;
             int col = vb + (unit ^ (row & L::VSWZ)) * (16 / (int)sizeof(in_t));
             if (col >= DV) col = 0;
             dsrc[kx] = row * H * DV + col;
-        } else if (ii < L::NV + L::NMP * L::NM) {
+        } else if (ii < L::NV + L::NM + L::NPC) {
             dsrc[kx] = ((ii - L::NV) % L::NM) * 1024 + 16 * l;
         } else {
             dsrc[kx] = 16 * l;
@@ -914,7 +937,7 @@ __global__ __launch_bounds__(64 * (NW * SPLIT + kStagers)) void chunk_state_kern
         const unsigned char *gc = reinterpret_cast<const unsigned char *>(ws_g + rh * 4 * C);
 #pragma unroll
         for (int kx = 0; kx < KD; ++kx) {
-            const int ii = sw + kStagers * kx;
+            const int ii = sw + NLD * kx;
             if (ii >= L::NDMA) break;
             if (ii < L::NV) {
                 int off = dsrc[kx];
@@ -925,7 +948,7 @@ __global__ __launch_bounds__(64 * (NW * SPLIT + kStagers)) void chunk_state_kern
                 dma16(vc + off, base + (uint32_t)(ii * 1024));
             } else if (ii < L::NV + L::NM) {
                 dma16(mc + dsrc[kx], base + (uint32_t)(L::m_rel + (ii - L::NV) * 1024));
-            } else if (OUT && ii < L::NV + 2 * L::NM) {
+            } else if (ii < L::NV + L::NM + L::NPC) {
                 dma16(pc + dsrc[kx], base + (uint32_t)(L::p_rel + (ii - L::NV - L::NM) * 1024));
             } else {
                 dma16(gc + dsrc[kx], base + (uint32_t)L::g_rel);
@@ -1071,7 +1094,7 @@ __global__ __launch_bounds__(64 * (NW * SPLIT + kStagers)) void chunk_state_kern
         // decay factors (G1): gamma / ||k||, kappa / ||k||, gamma / ||q||, gamma
         const float *gam_s = reinterpret_cast<const float *>(Db + L::g_rel);
         const float *kap_s = gam_s + C;
-        const float *gao_s = gam_s + 2 * C;
+        const float *gao_s = FP ? reinterpret_cast<const float *>(Db + L::gq_rel) : gam_s + 2 * C;
 
         // The chunk is software-pipelined: each phase issues the LDS reads of
         // a later phase before its own products, and the phases are pinned
@@ -1419,6 +1442,136 @@ __global__ __launch_bounds__(64 * (NW * SPLIT + kStagers)) void chunk_state_kern
         store_o2(t0, len);
     };
 
+    // ---- the P waves (FP) ----
+    // They form each chunk's P = (Q K^T) o Gamma, with the q/k normalisation
+    // factors, and gamma / ||q|| into the chunk's LDS buffer one chunk ahead,
+    // the way G1 would (Q and K straight from global memory into matrix-core
+    // operand registers, 16-bit products exact, fp32 sums, the decay mask
+    // masked before the exponential), so P never goes through HBM and G1
+    // reads no Q.  Wave mk takes chunks mk, mk + 2, ...: it loads a chunk's
+    // Q and K right after forming the one before, so the loads have two chunk
+    // steps to land, and its barriers do not wait for them.  Both join the
+    // block barrier once per chunk like the stagers.
+    if constexpr (FP) {
+        if (maker) {
+            PrepRegs<in_t, KP> R;
+            float *mg = reinterpret_cast<float *>(smem + L::mk_off) + mk * 192;   // g in base-2 units
+            float *mqn = mg + 64, *mkn = mg + 128;                      // 1 / ||q_r||, 1 / ||k_r||
+            const int64_t tok_stride = (int64_t)H * DK;
+            auto load_p = [&](int ci) {   // rows past the end re-read the last row (zeroed in make_p)
+                const int t0 = tok0 + ci * C, len = min(C, len_seq - ci * C);
+                R.la = log_alpha[(int64_t)(t0 + min(l, len - 1)) * H + h];
+                const int64_t base = ((int64_t)t0 * H + h) * DK + 8 * jj;
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const int64_t off = base + (int64_t)min(16 * b + nn, len - 1) * tok_stride;
+#pragma unroll
+                    for (int p = 0; p < KP; ++p) {
+                        R.k[b][p].load(k + off + 32 * p);
+                        R.q[b][p].load(q + off + 32 * p);
+                    }
+                }
+            };
+            auto make_p = [&](int ci, int buf) {
+                const int len = min(C, len_seq - ci * C);
+                if (len < C) {
+#pragma unroll
+                    for (int b = 0; b < 4; ++b)
+                        if (16 * b + nn >= len)
+#pragma unroll
+                            for (int p = 0; p < KP; ++p) {
+                                R.k[b][p].zero();
+                                R.q[b][p].zero();
+                            }
+                }
+                const float g = wave_inclusive_scan(l < len ? R.la : 0.f);
+                float rq = 1.f, rk = 1.f;
+                if (qk_norm) {
+                    float ssk[4] = {0.f, 0.f, 0.f, 0.f}, ssq[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int b = 0; b < 4; ++b)
+#pragma unroll
+                        for (int p = 0; p < KP; ++p) {
+                            float f[8];
+                            R.k[b][p].to_f32(f);
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) ssk[b] += f[e] * f[e];
+                            R.q[b][p].to_f32(f);
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) ssq[b] += f[e] * f[e];
+                        }
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) {
+                        ssk[b] += __shfl_xor(ssk[b], 16, 64);
+                        ssk[b] += __shfl_xor(ssk[b], 32, 64);
+                        ssq[b] += __shfl_xor(ssq[b], 16, 64);
+                        ssq[b] += __shfl_xor(ssq[b], 32, 64);
+                    }
+                    const float sk = jj == 0 ? ssk[0] : (jj == 1 ? ssk[1] : (jj == 2 ? ssk[2] : ssk[3]));
+                    const float sq = jj == 0 ? ssq[0] : (jj == 1 ? ssq[1] : (jj == 2 ? ssq[2] : ssq[3]));
+                    rk = sk > 0.f ? rsqrtf(sk) : 0.f;
+                    rq = sq > 0.f ? rsqrtf(sq) : 0.f;
+                }
+                mg[l] = g * kLog2e;
+                mqn[l] = rq;
+                mkn[l] = rk;
+                reinterpret_cast<float *>(smem + L::dma_off(buf) + L::gq_rel)[l] = expf(g) * rq;
+                float4_t pacc[kTriTiles];
+#pragma unroll
+                for (int t = 0; t < kTriTiles; ++t) pacc[t] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int t = 0; t < kTriTiles; ++t) {
+                    int a, b;
+                    tri_decode(t, a, b);
+#pragma unroll
+                    for (int p = 0; p < KP; ++p) gram_mma(pacc[t], R.k[b][p], R.q[a][p]);
+                }
+                asm volatile("" ::: "memory");
+                float gr[4], iqr[4];
+#pragma unroll
+                for (int a = 0; a < 4; ++a) {
+                    gr[a] = mg[16 * a + nn];
+                    iqr[a] = mqn[16 * a + nn];
+                }
+                OP *pt = reinterpret_cast<OP *>(smem + L::dma_off(buf) + L::p_rel);
+#pragma unroll
+                for (int t = 0; t < kTriTiles; ++t) {
+                    int a, b;
+                    tri_decode(t, a, b);
+                    const float4_t gc = *reinterpret_cast<const float4_t *>(mg + 16 * b + 4 * jj);
+                    const float4_t kc = *reinterpret_cast<const float4_t *>(mkn + 16 * b + 4 * jj);
+                    float4_t pv;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const bool lower = a > b || 4 * jj + i <= nn;
+                        const float x = gr[a] - gc[i];
+                        const float e = exp2_neg(lower ? x : -x) * kc[i];
+                        pv[i] = lower ? e * iqr[a] * pacc[t][i] : 0.f;
+                    }
+                    *reinterpret_cast<frag *>(pt + t * kTileElems + 4 * l) = M::cvt(pv);
+                }
+                asm volatile("" ::: "memory");   // the scratch is rewritten for the next chunk
+            };
+            if (mk < nchunks) {
+                load_p(mk);
+                if (mk == 0) {
+                    make_p(0, 0);
+                    if (2 < nchunks) load_p(2);
+                }
+            }
+            for (int ci = 0; ci < nchunks; ++ci) {
+                // (no wait for this wave's loads: they are awaited where used)
+                asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+                const int j = ci + 1;
+                if (j < nchunks && (j & 1) == mk) {
+                    make_p(j, j & 1);
+                    if (j + 2 < nchunks) load_p(j + 2);
+                }
+            }
+            return;
+        }
+    }
+
     if (stager) {
         if (nchunks > 0) {
             prefetch_qk(0, RA);
@@ -1701,11 +1854,11 @@ static hipError_t allow_smem(K kernel, size_t bytes) {
 // empty batch still reads as equal-length), 0 for a packed one.
 static int uniform_cpr(const ChunkArgs &a) { return a.cu_seqlens ? 0 : (a.T + C - 1) / C + (a.T == 0); }
 
-template <typename in_t, typename OP, int DK, int NW, bool OUT, int SPLIT = 1>
+template <typename in_t, typename OP, int DK, int NW, bool OUT, int SPLIT = 1, bool FP = false>
 static hipError_t launch_state(const ChunkArgs &a, const ChunkWorkspace &w, const SegArgs &sg, int64_t NU,
                                hipStream_t st) {
-    using L = StateSmem<in_t, OP, DK, NW, OUT, SPLIT>;
-    auto kern = chunk_state_kernel<in_t, OP, DK, NW, OUT, SPLIT>;
+    using L = StateSmem<in_t, OP, DK, NW, OUT, SPLIT, FP>;
+    auto kern = chunk_state_kernel<in_t, OP, DK, NW, OUT, SPLIT, FP>;
     hipError_t e = allow_smem(kern, L::bytes);
     if (e != hipSuccess) return e;
     char *ws = static_cast<char *>(a.workspace);
@@ -1713,13 +1866,29 @@ static hipError_t launch_state(const ChunkArgs &a, const ChunkWorkspace &w, cons
     const int nvt = ((cols + 15) / 16 + NW - 1) / NW;
     const int64_t blocks = ((NU + 7) / 8) * 8 * nvt;
     ProfScope prof(OUT ? "gdn_chunk_state" : "gdn_chunk_transition", st);
-    kern<<<dim3((unsigned)blocks), dim3(64 * (NW * SPLIT + kStagers)), L::bytes, st>>>(
+    kern<<<dim3((unsigned)blocks), dim3(64 * L::WAVES), L::bytes, st>>>(
         (int)NU, a.H, a.dv, nvt, a.out_dtype, a.T, uniform_cpr(a), reinterpret_cast<int32_t *>(ws + w.off_meta),
         reinterpret_cast<const int32_t *>(ws + w.off_cu), reinterpret_cast<const int32_t *>(ws + w.off_row0), sg,
         static_cast<const in_t *>(a.q), static_cast<const in_t *>(a.k), static_cast<const in_t *>(a.v),
+        a.log_alpha, (a.flags & kFlagQkL2Norm) ? 1 : 0,
         reinterpret_cast<const float *>(ws + w.off_g), reinterpret_cast<const OP *>(ws + w.off_m),
         reinterpret_cast<const OP *>(ws + w.off_p), a.init_state, a.final_state, a.o);
     return hipGetLastError();
+}
+
+// P formed in the output pass (FP): two more waves per block form each
+// chunk's P = (Q K^T) o Gamma from Q and K ahead of the chunk, so G1 reads
+// no Q and P never goes through HBM.  Built for 16-bit inputs with
+// dk <= 128 and off unless GDN_FUSE_P=1: on the prefill workload G1 drops
+// from 34.6 to 21.8 us but the state pass rises from 115 to 149 us (the P
+// waves' Q / K reads and products slow the chunk steps more than G1 saves).
+template <typename in_t, typename OP, int DK>
+constexpr bool fuse_p_built() {
+    return sizeof(OP) == 2 && DK <= 128;
+}
+static bool use_fuse_p() {
+    const char *env = getenv("GDN_FUSE_P");
+    return env && *env && atoi(env) != 0;
 }
 
 // Split waves for the output pass: each 16-column slice of the state is held
@@ -1743,14 +1912,25 @@ constexpr bool split_built() {
     return DK >= 64 && L::QKB == 2 && L::bytes <= 160 * 1024;
 }
 
+// fuse_p: the output pass forms P itself (G1 ran without it).
 template <typename in_t, typename OP, int DK, bool OUT>
 static hipError_t launch_state_nw(const ChunkArgs &a, const ChunkWorkspace &w, const SegArgs &sg, int64_t NU,
-                                  hipStream_t st) {
+                                  bool fuse_p, hipStream_t st) {
     if constexpr (OUT && split_built<in_t, OP, DK>()) {
-        if (use_split_waves(DK, a.dv, NU)) return launch_state<in_t, OP, DK, 2, true, 2>(a, w, sg, NU, st);
+        if (!fuse_p && use_split_waves(DK, a.dv, NU)) return launch_state<in_t, OP, DK, 2, true, 2>(a, w, sg, NU, st);
     }
     const int cols = OUT ? a.dv : a.dv + a.dk;
-    switch (state_waves_per_block(cols, NU, OUT ? "GDN_STATE_WAVES" : "GDN_TRANSITION_WAVES")) {
+    const int nw = state_waves_per_block(cols, NU, OUT ? "GDN_STATE_WAVES" : "GDN_TRANSITION_WAVES");
+    if constexpr (OUT && fuse_p_built<in_t, OP, DK>()) {
+        if (fuse_p) {
+            switch (nw) {
+            case 4: return launch_state<in_t, OP, DK, 4, true, 1, true>(a, w, sg, NU, st);
+            case 2: return launch_state<in_t, OP, DK, 2, true, 1, true>(a, w, sg, NU, st);
+            default: return launch_state<in_t, OP, DK, 1, true, 1, true>(a, w, sg, NU, st);
+            }
+        }
+    }
+    switch (nw) {
     case 4: return launch_state<in_t, OP, DK, 4, OUT>(a, w, sg, NU, st);
     case 2: return launch_state<in_t, OP, DK, 2, OUT>(a, w, sg, NU, st);
     default:
@@ -1762,12 +1942,14 @@ static hipError_t launch_state_nw(const ChunkArgs &a, const ChunkWorkspace &w, c
 template <typename in_t, typename OP, int DK>
 static hipError_t launch_dk(const ChunkArgs &a, const ChunkWorkspace &w, hipStream_t st) {
     char *ws = static_cast<char *>(a.workspace);
+    const bool fuse_p = fuse_p_built<in_t, OP, DK>() && use_fuse_p();
     if (w.max_rows > 0) {   // no tokens at all: only the state pass runs (final = initial)
         ProfScope prof("gdn_chunk_prep", st);
         // One wave per (row, head) item; very large batches loop.
         const int64_t items = w.max_rows * a.H;
         const int64_t grid = items < (1 << 22) ? items : (1 << 22);
-        chunk_prep_kernel<in_t, OP, DK><<<dim3((unsigned)grid), dim3(64), 0, st>>>(
+        auto prep = fuse_p ? chunk_prep_kernel<in_t, OP, DK, false> : chunk_prep_kernel<in_t, OP, DK, true>;
+        prep<<<dim3((unsigned)grid), dim3(64), 0, st>>>(
             a.H, a.T, uniform_cpr(a), (int)(uniform_cpr(a) ? w.max_rows : 0), (a.flags & kFlagQkL2Norm) ? 1 : 0,
             reinterpret_cast<const int32_t *>(ws + w.off_meta),
             reinterpret_cast<const int32_t *>(ws + w.off_rowtok),
@@ -1778,7 +1960,7 @@ static hipError_t launch_dk(const ChunkArgs &a, const ChunkWorkspace &w, hipStre
         if (e != hipSuccess) return e;
     }
     SegArgs sg{};
-    if (w.seg_chunks == 0) return launch_state_nw<in_t, OP, DK, true>(a, w, sg, (int64_t)a.N * a.H, st);
+    if (w.seg_chunks == 0) return launch_state_nw<in_t, OP, DK, true>(a, w, sg, (int64_t)a.N * a.H, fuse_p, st);
 
     const int cpr = uniform_cpr(a);
     sg.seg_chunks = w.seg_chunks;
@@ -1788,7 +1970,7 @@ static hipError_t launch_dk(const ChunkArgs &a, const ChunkWorkspace &w, hipStre
     sg.ws_end = reinterpret_cast<float *>(ws + w.off_end);
     sg.ws_sin = reinterpret_cast<float *>(ws + w.off_sin);
     const int64_t NU = w.max_units * a.H;
-    hipError_t e = launch_state_nw<in_t, OP, DK, false>(a, w, sg, NU, st);
+    hipError_t e = launch_state_nw<in_t, OP, DK, false>(a, w, sg, NU, false, st);
     if (e != hipSuccess) return e;
     {
         ProfScope prof("gdn_chunk_combine", st);
@@ -1799,7 +1981,7 @@ static hipError_t launch_dk(const ChunkArgs &a, const ChunkWorkspace &w, hipStre
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    return launch_state_nw<in_t, OP, DK, true>(a, w, sg, NU, st);
+    return launch_state_nw<in_t, OP, DK, true>(a, w, sg, NU, fuse_p, st);
 }
 
 template <typename in_t, typename OP>
