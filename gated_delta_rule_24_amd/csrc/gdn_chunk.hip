@@ -244,6 +244,142 @@ struct InvMma<float> {
     }
 };
 
+// The UT transform and the decay-masked Q K^T of one chunk from the wave's
+// Gram accumulators (R layout, the 10 lower tiles; pacc = Q K^T, gacc =
+// K K^T): P = (Q K^T) o Gamma with the normalisation factors, A =
+// strictLower(diag(beta)(Gamma o K K^T)), T = (I + A)^{-1} and M = T diag(beta),
+// P and M written in fragment order (tile t at t * 256, lane l's four values
+// at 4 l) to p_out / m_out (global or LDS).  The scratch holds, per row r of
+// the chunk (lane r wrote them): gs = g_r log2 e, bs = beta_r, qn = 1 / ||q_r||,
+// kn = 1 / ||k_r||, then the four 16 x 16 blocks of the diagonal inverse.
+// One wave, no block barriers.  DO_P / DO_M leave out P or M.
+template <typename OP, bool DO_P, bool DO_M>
+__device__ __forceinline__ void ut_epilogue(const float4_t (&pacc)[kTriTiles], const float4_t (&gacc)[kTriTiles],
+                                            float *lds, OP *p_out, OP *m_out) {
+    using M = Mma<OP>;
+    using MI = InvMma<OP>;
+    constexpr int BP = kPrepBP, BS = kPrepBS;
+    const float *gs = lds, *bs = lds + C, *qn = lds + 2 * C, *kn = lds + 3 * C;
+    float *blk = lds + 4 * C;
+    const int l = lane_id(), nn = l & 15, jj = l >> 4;
+    // Decay masks (g in base-2 units).  Off-diagonal tiles: row r = 16a + n, columns
+    // c = 16b + 4j + i < r, one exponential shared by P and A.  Diagonal
+    // tiles: the lane's positions with c <= r belong to P; the others
+    // give N^T[n][c - 16a] = A[c][r] of the same block, whose decay is
+    // e^{g_c - g_r}, so again one exponential per position.
+    float gr[4], br[4], iqr[4], ikr[4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+        gr[a] = gs[16 * a + nn];
+        br[a] = bs[16 * a + nn];
+        iqr[a] = qn[16 * a + nn];
+        ikr[a] = kn[16 * a + nn];
+    }
+    float4_t aR[kTriTiles];   // R(-A_ab) for a > b
+#pragma unroll
+    for (int t = 0; t < kTriTiles; ++t) {
+        int a, b;
+        tri_decode(t, a, b);
+        const float4_t gc = *reinterpret_cast<const float4_t *>(gs + 16 * b + 4 * jj);
+        const float4_t kc = *reinterpret_cast<const float4_t *>(kn + 16 * b + 4 * jj);   // column factors
+        float4_t pv, av;
+        if (a > b) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float e = exp2_neg(gr[a] - gc[i]) * kc[i];
+                pv[i] = e * iqr[a] * pacc[t][i];
+                av[i] = -br[a] * ikr[a] * e * gacc[t][i];
+            }
+            aR[t] = av;
+        } else {
+            const float4_t bc = *reinterpret_cast<const float4_t *>(bs + 16 * a + 4 * jj);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bool lower = 4 * jj + i <= nn;
+                const float x = gr[a] - gc[i];
+                const float e = exp2_neg(lower ? x : -x) * kc[i];
+                pv[i] = lower ? e * iqr[a] * pacc[t][i] : 0.f;
+                av[i] = lower ? 0.f : bc[i] * ikr[a] * e * gacc[t][i];
+            }
+            if constexpr (DO_M) *reinterpret_cast<float4_t *>(blk + a * BS + nn * BP + 4 * jj) = av;
+            aR[t] = float4_t{0.f, 0.f, 0.f, 0.f};
+        }
+        if constexpr (DO_P) *reinterpret_cast<typename M::frag *>(p_out + t * kTileElems + 4 * l) = M::cvt(pv);
+    }
+    asm volatile("" ::: "memory");
+    if constexpr (!DO_M) return;
+
+    // Diagonal blocks: lane (n, j) computes row n of T_jj,
+    //   x[c] = [c == n] - sum_{i > c} x[i] N[i][c],  c = 15 .. 0,
+    // reading row c of N^T (broadcast to the 16 lanes of the block).
+    {
+        const float *nt = blk + jj * BS;
+        float x[16];
+#pragma unroll
+        for (int c = 15; c >= 0; --c) {
+            float acc = (c == nn) ? 1.f : 0.f;
+#pragma unroll
+            for (int qd = (c + 1) / 4; qd < 4; ++qd) {
+                const float4_t v = *reinterpret_cast<const float4_t *>(nt + c * BP + 4 * qd);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (4 * qd + e > c) acc -= x[4 * qd + e] * v[e];
+            }
+            x[c] = acc;
+        }
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd)
+            *reinterpret_cast<float4_t *>(blk + jj * BS + nn * BP + 4 * qd) =
+                float4_t{x[4 * qd], x[4 * qd + 1], x[4 * qd + 2], x[4 * qd + 3]};
+    }
+    asm volatile("" ::: "memory");
+    float4_t tR[4], tC[3];   // R(T_aa), C(T_bb)
+#pragma unroll
+    for (int a = 0; a < 4; ++a) tR[a] = *reinterpret_cast<const float4_t *>(blk + a * BS + nn * BP + 4 * jj);
+#pragma unroll
+    for (int b = 0; b < 3; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) tC[b][i] = blk[b * BS + (4 * jj + i) * BP + nn];
+
+    // Off-diagonal blocks by distance from the diagonal.
+    const float4_t z = {0.f, 0.f, 0.f, 0.f};
+    float4_t TR[kTriTiles];   // R(T_ab)
+#pragma unroll
+    for (int a = 0; a < 4; ++a) TR[tri_index(a, a)] = tR[a];
+    // W = -U_ab (from the negated A tiles); T_ab = T_aa W in R layout, and
+    // in C layout where a later U needs it.
+    float4_t W, C10, C21, C20;
+    W = MI::mm(aR[tri_index(1, 0)], tC[0], z);
+    TR[tri_index(1, 0)] = MI::mm(W, tR[1], z);
+    C10 = MI::mm(tR[1], W, z);
+    W = MI::mm(aR[tri_index(2, 1)], tC[1], z);
+    TR[tri_index(2, 1)] = MI::mm(W, tR[2], z);
+    C21 = MI::mm(tR[2], W, z);
+    W = MI::mm(aR[tri_index(3, 2)], tC[2], z);
+    TR[tri_index(3, 2)] = MI::mm(W, tR[3], z);
+    W = MI::mm(aR[tri_index(2, 1)], C10, MI::mm(aR[tri_index(2, 0)], tC[0], z));
+    TR[tri_index(2, 0)] = MI::mm(W, tR[2], z);
+    C20 = MI::mm(tR[2], W, z);
+    W = MI::mm(aR[tri_index(3, 2)], C21, MI::mm(aR[tri_index(3, 1)], tC[1], z));
+    TR[tri_index(3, 1)] = MI::mm(W, tR[3], z);
+    W = MI::mm(aR[tri_index(3, 2)], C20, MI::mm(aR[tri_index(3, 1)], C10, MI::mm(aR[tri_index(3, 0)], tC[0], z)));
+    TR[tri_index(3, 0)] = MI::mm(W, tR[3], z);
+
+    // M = T diag(beta), R layout = fragment order.
+#pragma unroll
+    for (int t = 0; t < kTriTiles; ++t) {
+        int a, b;
+        tri_decode(t, a, b);
+        const float4_t bc = *reinterpret_cast<const float4_t *>(bs + 16 * b + 4 * jj);
+        float4_t mv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mv[i] = TR[t][i] * bc[i];
+        *reinterpret_cast<typename M::frag *>(m_out + t * kTileElems + 4 * l) = M::cvt(mv);
+    }
+    asm volatile("" ::: "memory");   // the scratch is reused by the wave's next item
+}
+
 // Register passes over dk in G1: the raw Q and K registers of one pass
 // stay within 128 per lane, so two waves fit on a SIMD and one computes
 // while the other waits for its loads.
@@ -264,9 +400,9 @@ struct PrepRegs {
     float la, bt;
 };
 
-// WITH_P = false: the state pass forms P itself (see chunk_state_kernel), so
-// G1 reads no Q and writes no P; the third decay vector (gamma / ||q||) is
-// then written by the state pass too.
+// WITH_P = false: the state pass forms P itself from the Q and K rows it
+// stages (chunk_state_kernel, FUSE), so G1 reads no Q and writes no P, and
+// the third decay vector (gamma / ||q||) is the state pass's too.
 template <typename in_t, typename OP, int DK, bool WITH_P = true>
 __global__ __launch_bounds__(64) void chunk_prep_kernel(int H, int T, int cpr, int urows, int qk_norm,
                                                         const int32_t *__restrict__ meta,
@@ -410,7 +546,6 @@ __global__ __launch_bounds__(64) void chunk_prep_kernel(int H, int T, int cpr, i
             const float sq = jj == 0 ? ssq[0] : (jj == 1 ? ssq[1] : (jj == 2 ? ssq[2] : ssq[3]));
             rk = sk > 0.f ? rsqrtf(sk) : 0.f;
             rq = sq > 0.f ? rsqrtf(sq) : 0.f;
-            if constexpr (!WITH_P) rq = 1.f;
         }
         qn[l] = rq;
         kn[l] = rk;
@@ -423,122 +558,8 @@ __global__ __launch_bounds__(64) void chunk_prep_kernel(int H, int T, int cpr, i
         ws_g[rh * 4 * C + 3 * C + l] = gam;
         asm volatile("" ::: "memory");
 
-        // Decay masks (g in base-2 units).  Off-diagonal tiles: row r = 16a + n, columns
-        // c = 16b + 4j + i < r, one exponential shared by P and A.  Diagonal
-        // tiles: the lane's positions with c <= r belong to P; the others
-        // give N^T[n][c - 16a] = A[c][r] of the same block, whose decay is
-        // e^{g_c - g_r}, so again one exponential per position.
-        float gr[4], br[4], iqr[4], ikr[4];
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-            gr[a] = gs[16 * a + nn];
-            br[a] = bs[16 * a + nn];
-            iqr[a] = qn[16 * a + nn];
-            ikr[a] = kn[16 * a + nn];
-        }
-        float4_t aR[kTriTiles];   // R(-A_ab) for a > b
-#pragma unroll
-        for (int t = 0; t < kTriTiles; ++t) {
-            int a, b;
-            tri_decode(t, a, b);
-            const float4_t gc = *reinterpret_cast<const float4_t *>(gs + 16 * b + 4 * jj);
-            const float4_t kc = *reinterpret_cast<const float4_t *>(kn + 16 * b + 4 * jj);   // column factors
-            float4_t pv, av;
-            if (a > b) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float e = exp2_neg(gr[a] - gc[i]) * kc[i];
-                    pv[i] = e * iqr[a] * pacc[t][i];
-                    av[i] = -br[a] * ikr[a] * e * gacc[t][i];
-                }
-                aR[t] = av;
-            } else {
-                const float4_t bc = *reinterpret_cast<const float4_t *>(bs + 16 * a + 4 * jj);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const bool lower = 4 * jj + i <= nn;
-                    const float x = gr[a] - gc[i];
-                    const float e = exp2_neg(lower ? x : -x) * kc[i];
-                    pv[i] = lower ? e * iqr[a] * pacc[t][i] : 0.f;
-                    av[i] = lower ? 0.f : bc[i] * ikr[a] * e * gacc[t][i];
-                }
-                *reinterpret_cast<float4_t *>(blk + a * BS + nn * BP + 4 * jj) = av;
-                aR[t] = float4_t{0.f, 0.f, 0.f, 0.f};
-            }
-            if constexpr (WITH_P)
-                *reinterpret_cast<typename M::frag *>(ws_p + (rh * kTriTiles + t) * kTileElems + 4 * l) = M::cvt(pv);
-        }
-        asm volatile("" ::: "memory");
-
-        // Diagonal blocks: lane (n, j) computes row n of T_jj,
-        //   x[c] = [c == n] - sum_{i > c} x[i] N[i][c],  c = 15 .. 0,
-        // reading row c of N^T (broadcast to the 16 lanes of the block).
-        {
-            const float *nt = blk + jj * BS;
-            float x[16];
-#pragma unroll
-            for (int c = 15; c >= 0; --c) {
-                float acc = (c == nn) ? 1.f : 0.f;
-#pragma unroll
-                for (int qd = (c + 1) / 4; qd < 4; ++qd) {
-                    const float4_t v = *reinterpret_cast<const float4_t *>(nt + c * BP + 4 * qd);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (4 * qd + e > c) acc -= x[4 * qd + e] * v[e];
-                }
-                x[c] = acc;
-            }
-            asm volatile("" ::: "memory");
-#pragma unroll
-            for (int qd = 0; qd < 4; ++qd)
-                *reinterpret_cast<float4_t *>(blk + jj * BS + nn * BP + 4 * qd) =
-                    float4_t{x[4 * qd], x[4 * qd + 1], x[4 * qd + 2], x[4 * qd + 3]};
-        }
-        asm volatile("" ::: "memory");
-        float4_t tR[4], tC[3];   // R(T_aa), C(T_bb)
-#pragma unroll
-        for (int a = 0; a < 4; ++a) tR[a] = *reinterpret_cast<const float4_t *>(blk + a * BS + nn * BP + 4 * jj);
-#pragma unroll
-        for (int b = 0; b < 3; ++b)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) tC[b][i] = blk[b * BS + (4 * jj + i) * BP + nn];
-
-        // Off-diagonal blocks by distance from the diagonal.
-        const float4_t z = {0.f, 0.f, 0.f, 0.f};
-        float4_t TR[kTriTiles];   // R(T_ab)
-#pragma unroll
-        for (int a = 0; a < 4; ++a) TR[tri_index(a, a)] = tR[a];
-        // W = -U_ab (from the negated A tiles); T_ab = T_aa W in R layout, and
-        // in C layout where a later U needs it.
-        float4_t W, C10, C21, C20;
-        W = MI::mm(aR[tri_index(1, 0)], tC[0], z);
-        TR[tri_index(1, 0)] = MI::mm(W, tR[1], z);
-        C10 = MI::mm(tR[1], W, z);
-        W = MI::mm(aR[tri_index(2, 1)], tC[1], z);
-        TR[tri_index(2, 1)] = MI::mm(W, tR[2], z);
-        C21 = MI::mm(tR[2], W, z);
-        W = MI::mm(aR[tri_index(3, 2)], tC[2], z);
-        TR[tri_index(3, 2)] = MI::mm(W, tR[3], z);
-        W = MI::mm(aR[tri_index(2, 1)], C10, MI::mm(aR[tri_index(2, 0)], tC[0], z));
-        TR[tri_index(2, 0)] = MI::mm(W, tR[2], z);
-        C20 = MI::mm(tR[2], W, z);
-        W = MI::mm(aR[tri_index(3, 2)], C21, MI::mm(aR[tri_index(3, 1)], tC[1], z));
-        TR[tri_index(3, 1)] = MI::mm(W, tR[3], z);
-        W = MI::mm(aR[tri_index(3, 2)], C20, MI::mm(aR[tri_index(3, 1)], C10, MI::mm(aR[tri_index(3, 0)], tC[0], z)));
-        TR[tri_index(3, 0)] = MI::mm(W, tR[3], z);
-
-        // M = T diag(beta), R layout = fragment order.
-#pragma unroll
-        for (int t = 0; t < kTriTiles; ++t) {
-            int a, b;
-            tri_decode(t, a, b);
-            const float4_t bc = *reinterpret_cast<const float4_t *>(bs + 16 * b + 4 * jj);
-            float4_t mv;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) mv[i] = TR[t][i] * bc[i];
-            *reinterpret_cast<typename M::frag *>(ws_m + (rh * kTriTiles + t) * kTileElems + 4 * l) = M::cvt(mv);
-        }
-        asm volatile("" ::: "memory");   // LDS is reused by the wave's next item
+        ut_epilogue<OP, WITH_P, true>(pacc, gacc, lds, ws_p + rh * kTriTiles * kTileElems,
+                                      ws_m + rh * kTriTiles * kTileElems);
     };
 
     PrepRegs<in_t, PP> R;
@@ -582,12 +603,12 @@ __global__ __launch_bounds__(64) void chunk_prep_kernel(int H, int T, int cpr, i
 // Waves of a state-pass block that stage inputs (the others compute).
 constexpr int kStagers = 4;
 
-template <typename in_t, typename OP, int DK, int NW, bool OUT, int SPLIT = 1, bool FP = false>
+template <typename in_t, typename OP, int DK, int NW, bool OUT, int SPLIT = 1, bool FUSE = false>
 struct StateSmem {
-    // Loading waves (the stagers) and, with FP, two more waves that form P
-    // for alternate chunks.
-    static constexpr int NMK = FP ? 2 : 0;
-    static constexpr int NLD = (FP && NW * SPLIT >= 4) ? kStagers - 2 : kStagers;
+    // Loading waves (the stagers) and, with FUSE, one more wave that forms
+    // each chunk's P in the block.
+    static constexpr int NMK = FUSE ? 1 : 0;
+    static constexpr int NLD = (FUSE && NW * SPLIT >= 4) ? kStagers - 1 : kStagers;
     static constexpr int WAVES = NW * SPLIT + NLD + NMK;
     static constexpr int BV = 16 * NW;                                  // value columns per block
     static constexpr int QROW = DK * (int)sizeof(OP) + 32;              // bytes per Q / K row
@@ -600,7 +621,7 @@ struct StateSmem {
     static constexpr size_t MP = sizeof(OP) * kTriTiles * kTileElems;   // one M or P block
     static constexpr int NMP = OUT ? 2 : 1;                             // M and P, or M alone
     static constexpr size_t GB = 1024;                                  // the four decay vectors
-    static constexpr size_t GQ = FP ? 256 : 0;                          // gamma / ||q|| from the P wave
+    static constexpr size_t GQ = FUSE ? 256 : 0;                        // gamma / ||q|| (FUSE: formed here)
     static constexpr size_t DMA = VB + NMP * MP + GB + GQ;              // a chunk's inputs (copied or formed)
     static constexpr int QKB = (2 * NQK * QK + 2 * DMA <= 160 * 1024) ? 2 : 1;   // Q/K buffers
     static constexpr size_t qk_off(int b) { return (size_t)b * NQK * QK; }       // Q (if any), then K
@@ -613,12 +634,17 @@ struct StateSmem {
     static constexpr size_t XCH_X = 4 * 64 * 16, XCH_Q = 2 * 64 * 16;
     static constexpr size_t xch_off = (size_t)QKB * NQK * QK + 2 * DMA;
     static constexpr size_t xch_bytes = SPLIT == 2 ? (size_t)NW * 2 * (XCH_X + XCH_Q) : 0;
-    // each P wave's g (base 2) and row-norm factors
-    static constexpr size_t mk_off = xch_off + xch_bytes, mk_bytes = NMK * 3 * 64 * 4;
-    static constexpr size_t bytes = mk_off + mk_bytes;
+    // each forming wave's scratch (g, beta and norm factors per row, the
+    // diagonal blocks of the inverse), then the count of committed Q / K
+    // pieces the forming waves wait for
+    static constexpr size_t mk_off = xch_off + xch_bytes, mk_bytes = NMK * sizeof(float) * kPrepLds;
+    static constexpr size_t cnt_off = mk_off + mk_bytes;
+    static constexpr size_t bytes = cnt_off + (FUSE ? 16 : 0);
     static constexpr int NV = (int)(VB / 1024), NM = (int)(MP / 1024);
-    static constexpr int NPC = (OUT && !FP) ? NM : 0;                    // copies of P
-    static constexpr int NDMA = NV + NM + NPC + 1;                       // 1 KiB wave copies per chunk
+    static constexpr int NMC = NM;                                        // copies of M
+    static constexpr int NPC = (OUT && !FUSE) ? NM : 0;                   // copies of P
+    static constexpr int NGC = 1;                                         // copies of the decay factors
+    static constexpr int NDMA = NV + NMC + NPC + NGC;                     // 1 KiB wave copies per chunk
     static_assert(VB % 1024 == 0 && MP % 1024 == 0, "direct loads move whole 1 KiB wave blocks");
     static_assert(QROW % 16 == 0 && VROW % 16 == 0, "16-byte rows");
 };
@@ -704,21 +730,22 @@ __device__ __forceinline__ void dma16(const void *g, uint32_t lds) {
         : "memory");
 }
 
-template <typename in_t, typename OP, int DK, int NW, bool OUT, int SPLIT, bool FP>
-__global__ __launch_bounds__((64 * StateSmem<in_t, OP, DK, NW, OUT, SPLIT, FP>::WAVES)) void chunk_state_kernel(
+template <typename in_t, typename OP, int DK, int NW, bool OUT, int SPLIT, bool FUSE>
+__global__ __launch_bounds__((64 * StateSmem<in_t, OP, DK, NW, OUT, SPLIT, FUSE>::WAVES)) void chunk_state_kernel(
     int NU, int H, int DV, int nvt, int odt, int T, int cpr, int32_t *__restrict__ meta,
     const int32_t *__restrict__ cu_ws, const int32_t *__restrict__ row0, SegArgs sg,
     const in_t *__restrict__ q, const in_t *__restrict__ k, const in_t *__restrict__ v,
-    const float *__restrict__ log_alpha, int qk_norm,
+    const float *__restrict__ log_alpha, const float *__restrict__ beta, int qk_norm,
     const float *__restrict__ ws_g, const OP *__restrict__ ws_m, const OP *__restrict__ ws_p,
     const float *init_state, float *final_state, void *__restrict__ o) {
     using M = Mma<OP>;
     using frag = typename M::frag;
     using F2 = Frag2<OP>;
-    using L = StateSmem<in_t, OP, DK, NW, OUT, SPLIT, FP>;
+    using L = StateSmem<in_t, OP, DK, NW, OUT, SPLIT, FUSE>;
     constexpr int QROW = L::QROW, VROW = L::VROW, BV = L::BV, QKB = L::QKB;
     constexpr int NLD = L::NLD;                              // loading waves
-    static_assert(!FP || (OUT && SPLIT == 1 && sizeof(OP) == 2 && DK <= 128), "P formed in the state pass: output pass, 16-bit operands, dk <= 128");
+    static_assert(!FUSE || (OUT && SPLIT == 1 && QKB == 2 && sizeof(OP) == 2 && DK <= 128 && L::bytes <= 160 * 1024),
+                  "P formed in the state pass: output pass, two Q/K buffers, 16-bit operands, dk <= 128");
     static_assert(SPLIT == 1 || (SPLIT == 2 && OUT && QKB == 2 && DK >= 64 && L::bytes <= 160 * 1024),
                   "split waves: output pass, two Q/K buffers, dk >= 64, one block per compute unit");
     constexpr int NCW = NW * SPLIT;                          // compute waves
@@ -772,8 +799,7 @@ __global__ __launch_bounds__((64 * StateSmem<in_t, OP, DK, NW, OUT, SPLIT, FP>::
     // cg = w / SPLIT) and, with split waves, one half of dk (hh = w % SPLIT);
     // the kStagers waves after them stage the next chunk's inputs into LDS.
     const bool stager = w >= NCW && w < NCW + NLD;
-    const bool maker = FP && w >= NCW + NLD;        // the two waves that form P (FP)
-    const int mk = w - NCW - NLD;                   // P wave index: it forms P of chunks mk, mk + 2, ...
+    const bool maker = FUSE && w == NCW + NLD;      // the wave that forms P (FUSE)
     const int sw = w - NCW, stid = tid - 64 * NCW;  // stager wave / thread index
     const int cg = w / SPLIT, hh = w % SPLIT;
     const int v0 = vb + cg * 16;            // first value column of a compute wave
@@ -901,6 +927,12 @@ __global__ __launch_bounds__((64 * StateSmem<in_t, OP, DK, NW, OUT, SPLIT, FP>::
             store_row8(Kb + r * (QROW / OPB) + c8, lo, hi);
         }
     };
+    // FUSE: this stager wave's part of a chunk's Q and K is in LDS (its
+    // writes complete first), counted for the forming waves.
+    auto count_commit = [&]() {
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        if (l == 0) __atomic_fetch_add(reinterpret_cast<unsigned *>(smem + L::cnt_off), 1u, __ATOMIC_RELAXED);
+    };
     // ---- direct global -> LDS copies of V, M, P and the decay factors ----
     // Copy ii of a chunk (stager wave sw issues ii = sw, sw + kStagers, ...) fills LDS bytes
     // [1024 ii, 1024 ii + 1024) of the chunk's buffer: V blocks first, then
@@ -921,7 +953,7 @@ __global__ __launch_bounds__((64 * StateSmem<in_t, OP, DK, NW, OUT, SPLIT, FP>::
             int col = vb + (unit ^ (row & L::VSWZ)) * (16 / (int)sizeof(in_t));
             if (col >= DV) col = 0;
             dsrc[kx] = row * H * DV + col;
-        } else if (ii < L::NV + L::NM + L::NPC) {
+        } else if (ii < L::NV + L::NMC + L::NPC) {
             dsrc[kx] = ((ii - L::NV) % L::NM) * 1024 + 16 * l;
         } else {
             dsrc[kx] = 16 * l;
@@ -946,10 +978,10 @@ __global__ __launch_bounds__((64 * StateSmem<in_t, OP, DK, NW, OUT, SPLIT, FP>::
                     if (row >= len) off -= (row - (len - 1)) * H * DV;
                 }
                 dma16(vc + off, base + (uint32_t)(ii * 1024));
-            } else if (ii < L::NV + L::NM) {
+            } else if (ii < L::NV + L::NMC) {
                 dma16(mc + dsrc[kx], base + (uint32_t)(L::m_rel + (ii - L::NV) * 1024));
-            } else if (ii < L::NV + L::NM + L::NPC) {
-                dma16(pc + dsrc[kx], base + (uint32_t)(L::p_rel + (ii - L::NV - L::NM) * 1024));
+            } else if (ii < L::NV + L::NMC + L::NPC) {
+                dma16(pc + dsrc[kx], base + (uint32_t)(L::p_rel + (ii - L::NV - L::NMC) * 1024));
             } else {
                 dma16(gc + dsrc[kx], base + (uint32_t)L::g_rel);
             }
@@ -1065,6 +1097,7 @@ __global__ __launch_bounds__((64 * StateSmem<in_t, OP, DK, NW, OUT, SPLIT, FP>::
             if (ci + 1 < nchunks) {
                 dma(ci + 1, b ^ 1);
                 commit_qk(b ^ 1, min(C, len_seq - (ci + 1) * C), cur);
+                if constexpr (FUSE) count_commit();
             }
             if constexpr (SPLIT == 2) asm volatile("s_barrier" ::: "memory");   // the split waves' exchange
         } else {
@@ -1094,7 +1127,7 @@ __global__ __launch_bounds__((64 * StateSmem<in_t, OP, DK, NW, OUT, SPLIT, FP>::
         // decay factors (G1): gamma / ||k||, kappa / ||k||, gamma / ||q||, gamma
         const float *gam_s = reinterpret_cast<const float *>(Db + L::g_rel);
         const float *kap_s = gam_s + C;
-        const float *gao_s = FP ? reinterpret_cast<const float *>(Db + L::gq_rel) : gam_s + 2 * C;
+        const float *gao_s = FUSE ? reinterpret_cast<const float *>(Db + L::gq_rel) : gam_s + 2 * C;
 
         // The chunk is software-pipelined: each phase issues the LDS reads of
         // a later phase before its own products, and the phases are pinned
@@ -1295,7 +1328,7 @@ __global__ __launch_bounds__((64 * StateSmem<in_t, OP, DK, NW, OUT, SPLIT, FP>::
         const OP *Ps = reinterpret_cast<const OP *>(Db + L::p_rel);
         const float *gam_s = reinterpret_cast<const float *>(Db + L::g_rel);
         const float *kap_s = gam_s + C;
-        const float *gao_s = gam_s + 2 * C;
+        const float *gao_s = FUSE ? reinterpret_cast<const float *>(Db + L::gq_rel) : gam_s + 2 * C;
         // exchange slots (lane-major, 16 bytes per tile and lane)
         unsigned char *xch = smem + L::xch_off + (size_t)cg * 2 * (L::XCH_X + L::XCH_Q);
         float4_t *x_mine = reinterpret_cast<float4_t *>(xch + hh * L::XCH_X) + l;
@@ -1442,131 +1475,108 @@ __global__ __launch_bounds__((64 * StateSmem<in_t, OP, DK, NW, OUT, SPLIT, FP>::
         store_o2(t0, len);
     };
 
-    // ---- the P waves (FP) ----
-    // They form each chunk's P = (Q K^T) o Gamma, with the q/k normalisation
-    // factors, and gamma / ||q|| into the chunk's LDS buffer one chunk ahead,
-    // the way G1 would (Q and K straight from global memory into matrix-core
-    // operand registers, 16-bit products exact, fp32 sums, the decay mask
-    // masked before the exponential), so P never goes through HBM and G1
-    // reads no Q.  Wave mk takes chunks mk, mk + 2, ...: it loads a chunk's
-    // Q and K right after forming the one before, so the loads have two chunk
-    // steps to land, and its barriers do not wait for them.  Both join the
-    // block barrier once per chunk like the stagers.
-    if constexpr (FP) {
+    // ---- the forming wave (FUSE) ----
+    // With FUSE, G1 leaves out P: one more wave of the block forms each
+    // chunk's P = (Q K^T) o Gamma (with the normalisation factors) and
+    // gamma / ||q|| into the chunk's LDS buffer, one chunk ahead, from the Q
+    // and K rows the stagers have just committed to LDS (16-bit operands:
+    // exact products, fp32 sums, as in G1), so P never goes through HBM and
+    // G1 reads no Q.  Each stager wave adds 1 to an LDS count once its part of
+    // a chunk's Q and K is written; the forming wave reads that chunk's rows
+    // once the count shows all of them (a wait with a bounded number of
+    // polls).  It joins the block barrier once per chunk like the stagers.
+    unsigned *kcnt = reinterpret_cast<unsigned *>(smem + L::cnt_off);
+    if constexpr (FUSE) {
+        if (tid == 0) *kcnt = 0u;
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
+    if constexpr (FUSE) {
         if (maker) {
-            PrepRegs<in_t, KP> R;
-            float *mg = reinterpret_cast<float *>(smem + L::mk_off) + mk * 192;   // g in base-2 units
-            float *mqn = mg + 64, *mkn = mg + 128;                      // 1 / ||q_r||, 1 / ||k_r||
-            const int64_t tok_stride = (int64_t)H * DK;
-            auto load_p = [&](int ci) {   // rows past the end re-read the last row (zeroed in make_p)
+            float *scr = reinterpret_cast<float *>(smem + L::mk_off);
+            float *gs = scr, *qn = scr + 2 * C, *kn = scr + 3 * C;
+            float la = 0.f;
+            auto load_gates = [&](int ci) {   // rows past the end re-read the last row (masked in form)
                 const int t0 = tok0 + ci * C, len = min(C, len_seq - ci * C);
-                R.la = log_alpha[(int64_t)(t0 + min(l, len - 1)) * H + h];
-                const int64_t base = ((int64_t)t0 * H + h) * DK + 8 * jj;
-#pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    const int64_t off = base + (int64_t)min(16 * b + nn, len - 1) * tok_stride;
-#pragma unroll
-                    for (int p = 0; p < KP; ++p) {
-                        R.k[b][p].load(k + off + 32 * p);
-                        R.q[b][p].load(q + off + 32 * p);
-                    }
-                }
+                la = log_alpha[(int64_t)(t0 + min(l, len - 1)) * H + h];
             };
-            auto make_p = [&](int ci, int buf) {
-                const int len = min(C, len_seq - ci * C);
-                if (len < C) {
-#pragma unroll
-                    for (int b = 0; b < 4; ++b)
-                        if (16 * b + nn >= len)
-#pragma unroll
-                            for (int p = 0; p < KP; ++p) {
-                                R.k[b][p].zero();
-                                R.q[b][p].zero();
-                            }
+            auto form = [&](int ci) {
+                const int len = min(C, len_seq - ci * C), buf = ci & 1;
+                // wait for every stager's part of chunk ci's Q and K
+                const unsigned want = (unsigned)(NLD * (ci + 1));
+                for (int poll = 0; poll < (1 << 24); ++poll) {
+                    if (__atomic_load_n(kcnt, __ATOMIC_RELAXED) >= want) break;
+                    __builtin_amdgcn_s_sleep(1);
                 }
-                const float g = wave_inclusive_scan(l < len ? R.la : 0.f);
+                const unsigned char *Qb = smem + L::qk_off(buf);
+                const unsigned char *Kb = Qb + L::k_rel;
+                auto row = [&](const unsigned char *blk, int x, int p) {   // row block x, k-tile pair p
+                    return row_frag2(reinterpret_cast<const OP *>(blk + 16 * x * QROW + frag_lane) + 32 * p);
+                };
+                const float g = wave_inclusive_scan(l < len ? la : 0.f);
+                // 1 / ||row|| (lane l: row l), when asked for
                 float rq = 1.f, rk = 1.f;
                 if (qk_norm) {
-                    float ssk[4] = {0.f, 0.f, 0.f, 0.f}, ssq[4] = {0.f, 0.f, 0.f, 0.f};
+                    float sq[4] = {0.f, 0.f, 0.f, 0.f}, sk[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int b = 0; b < 4; ++b)
 #pragma unroll
                         for (int p = 0; p < KP; ++p) {
-                            float f[8];
-                            R.k[b][p].to_f32(f);
+                            const half8_t vq = row(Qb, b, p).v, vk = row(Kb, b, p).v;
 #pragma unroll
-                            for (int e = 0; e < 8; ++e) ssk[b] += f[e] * f[e];
-                            R.q[b][p].to_f32(f);
-#pragma unroll
-                            for (int e = 0; e < 8; ++e) ssq[b] += f[e] * f[e];
+                            for (int e = 0; e < 8; ++e) {
+                                sq[b] += (float)vq[e] * (float)vq[e];
+                                sk[b] += (float)vk[e] * (float)vk[e];
+                            }
                         }
 #pragma unroll
                     for (int b = 0; b < 4; ++b) {
-                        ssk[b] += __shfl_xor(ssk[b], 16, 64);
-                        ssk[b] += __shfl_xor(ssk[b], 32, 64);
-                        ssq[b] += __shfl_xor(ssq[b], 16, 64);
-                        ssq[b] += __shfl_xor(ssq[b], 32, 64);
+                        sq[b] += __shfl_xor(sq[b], 16, 64);
+                        sq[b] += __shfl_xor(sq[b], 32, 64);
+                        sk[b] += __shfl_xor(sk[b], 16, 64);
+                        sk[b] += __shfl_xor(sk[b], 32, 64);
                     }
-                    const float sk = jj == 0 ? ssk[0] : (jj == 1 ? ssk[1] : (jj == 2 ? ssk[2] : ssk[3]));
-                    const float sq = jj == 0 ? ssq[0] : (jj == 1 ? ssq[1] : (jj == 2 ? ssq[2] : ssq[3]));
-                    rk = sk > 0.f ? rsqrtf(sk) : 0.f;
-                    rq = sq > 0.f ? rsqrtf(sq) : 0.f;
+                    const float xq = jj == 0 ? sq[0] : (jj == 1 ? sq[1] : (jj == 2 ? sq[2] : sq[3]));
+                    const float xk = jj == 0 ? sk[0] : (jj == 1 ? sk[1] : (jj == 2 ? sk[2] : sk[3]));
+                    rq = xq > 0.f ? rsqrtf(xq) : 0.f;
+                    rk = xk > 0.f ? rsqrtf(xk) : 0.f;
                 }
-                mg[l] = g * kLog2e;
-                mqn[l] = rq;
-                mkn[l] = rk;
+                gs[l] = g * kLog2e;
+                qn[l] = rq;
+                kn[l] = rk;
                 reinterpret_cast<float *>(smem + L::dma_off(buf) + L::gq_rel)[l] = expf(g) * rq;
-                float4_t pacc[kTriTiles];
+                // Gram tiles (a, b), b <= a: first operand row block b of K,
+                // second row block a of Q.  Rows past the end are zero in LDS
+                // (the stagers commit them so).
+                float4_t acc[kTriTiles];
 #pragma unroll
-                for (int t = 0; t < kTriTiles; ++t) pacc[t] = float4_t{0.f, 0.f, 0.f, 0.f};
+                for (int t = 0; t < kTriTiles; ++t) acc[t] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int t = 0; t < kTriTiles; ++t) {
-                    int a, b;
-                    tri_decode(t, a, b);
+                for (int p = 0; p < KP; ++p) {
+                    F2 kr[4], qr[4];
 #pragma unroll
-                    for (int p = 0; p < KP; ++p) gram_mma(pacc[t], R.k[b][p], R.q[a][p]);
+                    for (int b = 0; b < 4; ++b) {
+                        kr[b] = row(Kb, b, p);
+                        qr[b] = row(Qb, b, p);
+                    }
+#pragma unroll
+                    for (int t = 0; t < kTriTiles; ++t) {
+                        int a, b;
+                        tri_decode(t, a, b);
+                        mma2(acc[t], kr[b], qr[a]);
+                    }
                 }
                 asm volatile("" ::: "memory");
-                float gr[4], iqr[4];
-#pragma unroll
-                for (int a = 0; a < 4; ++a) {
-                    gr[a] = mg[16 * a + nn];
-                    iqr[a] = mqn[16 * a + nn];
-                }
-                OP *pt = reinterpret_cast<OP *>(smem + L::dma_off(buf) + L::p_rel);
-#pragma unroll
-                for (int t = 0; t < kTriTiles; ++t) {
-                    int a, b;
-                    tri_decode(t, a, b);
-                    const float4_t gc = *reinterpret_cast<const float4_t *>(mg + 16 * b + 4 * jj);
-                    const float4_t kc = *reinterpret_cast<const float4_t *>(mkn + 16 * b + 4 * jj);
-                    float4_t pv;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const bool lower = a > b || 4 * jj + i <= nn;
-                        const float x = gr[a] - gc[i];
-                        const float e = exp2_neg(lower ? x : -x) * kc[i];
-                        pv[i] = lower ? e * iqr[a] * pacc[t][i] : 0.f;
-                    }
-                    *reinterpret_cast<frag *>(pt + t * kTileElems + 4 * l) = M::cvt(pv);
-                }
-                asm volatile("" ::: "memory");   // the scratch is rewritten for the next chunk
+                OP *dst = reinterpret_cast<OP *>(smem + L::dma_off(buf) + L::p_rel);
+                ut_epilogue<OP, true, false>(acc, acc, scr, dst, dst);
             };
-            if (mk < nchunks) {
-                load_p(mk);
-                if (mk == 0) {
-                    make_p(0, 0);
-                    if (2 < nchunks) load_p(2);
-                }
+            if (nchunks > 0) {
+                load_gates(0);
+                form(0);
             }
             for (int ci = 0; ci < nchunks; ++ci) {
-                // (no wait for this wave's loads: they are awaited where used)
+                if (ci + 1 < nchunks) load_gates(ci + 1);
                 asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-                const int j = ci + 1;
-                if (j < nchunks && (j & 1) == mk) {
-                    make_p(j, j & 1);
-                    if (j + 2 < nchunks) load_p(j + 2);
-                }
+                if (ci + 1 < nchunks) form(ci + 1);
             }
             return;
         }
@@ -1577,6 +1587,7 @@ __global__ __launch_bounds__((64 * StateSmem<in_t, OP, DK, NW, OUT, SPLIT, FP>::
             prefetch_qk(0, RA);
             dma(0, 0);
             commit_qk(0, min(C, len_seq), RA);
+            if constexpr (FUSE) count_commit();
             if (QKB == 2 && nchunks > 1) prefetch_qk(1, RB);
         }
         // Register sets alternate: with QKB == 2, chunk ci+1 sits in RB for
@@ -1854,11 +1865,11 @@ static hipError_t allow_smem(K kernel, size_t bytes) {
 // empty batch still reads as equal-length), 0 for a packed one.
 static int uniform_cpr(const ChunkArgs &a) { return a.cu_seqlens ? 0 : (a.T + C - 1) / C + (a.T == 0); }
 
-template <typename in_t, typename OP, int DK, int NW, bool OUT, int SPLIT = 1, bool FP = false>
+template <typename in_t, typename OP, int DK, int NW, bool OUT, int SPLIT = 1, bool FUSE = false>
 static hipError_t launch_state(const ChunkArgs &a, const ChunkWorkspace &w, const SegArgs &sg, int64_t NU,
                                hipStream_t st) {
-    using L = StateSmem<in_t, OP, DK, NW, OUT, SPLIT, FP>;
-    auto kern = chunk_state_kernel<in_t, OP, DK, NW, OUT, SPLIT, FP>;
+    using L = StateSmem<in_t, OP, DK, NW, OUT, SPLIT, FUSE>;
+    auto kern = chunk_state_kernel<in_t, OP, DK, NW, OUT, SPLIT, FUSE>;
     hipError_t e = allow_smem(kern, L::bytes);
     if (e != hipSuccess) return e;
     char *ws = static_cast<char *>(a.workspace);
@@ -1870,24 +1881,27 @@ static hipError_t launch_state(const ChunkArgs &a, const ChunkWorkspace &w, cons
         (int)NU, a.H, a.dv, nvt, a.out_dtype, a.T, uniform_cpr(a), reinterpret_cast<int32_t *>(ws + w.off_meta),
         reinterpret_cast<const int32_t *>(ws + w.off_cu), reinterpret_cast<const int32_t *>(ws + w.off_row0), sg,
         static_cast<const in_t *>(a.q), static_cast<const in_t *>(a.k), static_cast<const in_t *>(a.v),
-        a.log_alpha, (a.flags & kFlagQkL2Norm) ? 1 : 0,
+        a.log_alpha, a.beta, (a.flags & kFlagQkL2Norm) ? 1 : 0,
         reinterpret_cast<const float *>(ws + w.off_g), reinterpret_cast<const OP *>(ws + w.off_m),
         reinterpret_cast<const OP *>(ws + w.off_p), a.init_state, a.final_state, a.o);
     return hipGetLastError();
 }
 
-// P formed in the output pass (FP): two more waves per block form each
-// chunk's P = (Q K^T) o Gamma from Q and K ahead of the chunk, so G1 reads
-// no Q and P never goes through HBM.  Built for 16-bit inputs with
-// dk <= 128 and off unless GDN_FUSE_P=1: on the prefill workload G1 drops
-// from 34.6 to 21.8 us but the state pass rises from 115 to 149 us (the P
-// waves' Q / K reads and products slow the chunk steps more than G1 saves).
+// P formed in the output pass (FUSE): one more wave per block forms each
+// chunk's P from the Q and K rows already staged in LDS (see
+// chunk_state_kernel), so G1 reads no Q and writes no P.  Built for 16-bit
+// inputs with dk <= 128 (two Q/K buffers), for unsegmented calls, and off
+// unless GDN_FUSE=1: on the prefill workload G1 drops from 34 to 22 us but
+// the state pass rises from 114 to 174 us, because the forming wave's work
+// lengthens every chunk step (its end is a block barrier).  A version that
+// also formed M and the decay factors (G1 not run at all) took 259 us.
 template <typename in_t, typename OP, int DK>
-constexpr bool fuse_p_built() {
-    return sizeof(OP) == 2 && DK <= 128;
+constexpr bool fuse_built() {
+    return sizeof(OP) == 2 && DK <= 128 && StateSmem<in_t, OP, DK, 4, true, 1, true>::bytes <= 160 * 1024 &&
+           StateSmem<in_t, OP, DK, 4, true, 1, true>::QKB == 2;
 }
-static bool use_fuse_p() {
-    const char *env = getenv("GDN_FUSE_P");
+static bool use_fuse() {
+    const char *env = getenv("GDN_FUSE");
     return env && *env && atoi(env) != 0;
 }
 
@@ -1912,17 +1926,17 @@ constexpr bool split_built() {
     return DK >= 64 && L::QKB == 2 && L::bytes <= 160 * 1024;
 }
 
-// fuse_p: the output pass forms P itself (G1 ran without it).
+// fuse: the output pass forms P itself (G1 ran without it).
 template <typename in_t, typename OP, int DK, bool OUT>
 static hipError_t launch_state_nw(const ChunkArgs &a, const ChunkWorkspace &w, const SegArgs &sg, int64_t NU,
-                                  bool fuse_p, hipStream_t st) {
+                                  bool fuse, hipStream_t st) {
     if constexpr (OUT && split_built<in_t, OP, DK>()) {
-        if (!fuse_p && use_split_waves(DK, a.dv, NU)) return launch_state<in_t, OP, DK, 2, true, 2>(a, w, sg, NU, st);
+        if (!fuse && use_split_waves(DK, a.dv, NU)) return launch_state<in_t, OP, DK, 2, true, 2>(a, w, sg, NU, st);
     }
     const int cols = OUT ? a.dv : a.dv + a.dk;
     const int nw = state_waves_per_block(cols, NU, OUT ? "GDN_STATE_WAVES" : "GDN_TRANSITION_WAVES");
-    if constexpr (OUT && fuse_p_built<in_t, OP, DK>()) {
-        if (fuse_p) {
+    if constexpr (OUT && fuse_built<in_t, OP, DK>()) {
+        if (fuse) {
             switch (nw) {
             case 4: return launch_state<in_t, OP, DK, 4, true, 1, true>(a, w, sg, NU, st);
             case 2: return launch_state<in_t, OP, DK, 2, true, 1, true>(a, w, sg, NU, st);
@@ -1942,13 +1956,13 @@ static hipError_t launch_state_nw(const ChunkArgs &a, const ChunkWorkspace &w, c
 template <typename in_t, typename OP, int DK>
 static hipError_t launch_dk(const ChunkArgs &a, const ChunkWorkspace &w, hipStream_t st) {
     char *ws = static_cast<char *>(a.workspace);
-    const bool fuse_p = fuse_p_built<in_t, OP, DK>() && use_fuse_p();
+    const bool fuse = fuse_built<in_t, OP, DK>() && w.seg_chunks == 0 && use_fuse();
     if (w.max_rows > 0) {   // no tokens at all: only the state pass runs (final = initial)
         ProfScope prof("gdn_chunk_prep", st);
         // One wave per (row, head) item; very large batches loop.
         const int64_t items = w.max_rows * a.H;
         const int64_t grid = items < (1 << 22) ? items : (1 << 22);
-        auto prep = fuse_p ? chunk_prep_kernel<in_t, OP, DK, false> : chunk_prep_kernel<in_t, OP, DK, true>;
+        auto prep = fuse ? chunk_prep_kernel<in_t, OP, DK, false> : chunk_prep_kernel<in_t, OP, DK, true>;
         prep<<<dim3((unsigned)grid), dim3(64), 0, st>>>(
             a.H, a.T, uniform_cpr(a), (int)(uniform_cpr(a) ? w.max_rows : 0), (a.flags & kFlagQkL2Norm) ? 1 : 0,
             reinterpret_cast<const int32_t *>(ws + w.off_meta),
@@ -1960,7 +1974,7 @@ static hipError_t launch_dk(const ChunkArgs &a, const ChunkWorkspace &w, hipStre
         if (e != hipSuccess) return e;
     }
     SegArgs sg{};
-    if (w.seg_chunks == 0) return launch_state_nw<in_t, OP, DK, true>(a, w, sg, (int64_t)a.N * a.H, fuse_p, st);
+    if (w.seg_chunks == 0) return launch_state_nw<in_t, OP, DK, true>(a, w, sg, (int64_t)a.N * a.H, fuse, st);
 
     const int cpr = uniform_cpr(a);
     sg.seg_chunks = w.seg_chunks;
@@ -1981,7 +1995,7 @@ static hipError_t launch_dk(const ChunkArgs &a, const ChunkWorkspace &w, hipStre
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    return launch_state_nw<in_t, OP, DK, true>(a, w, sg, NU, fuse_p, st);
+    return launch_state_nw<in_t, OP, DK, true>(a, w, sg, NU, false, st);
 }
 
 template <typename in_t, typename OP>
