@@ -50,6 +50,7 @@
 #include <stdlib.h>
 
 #include <algorithm>
+#include <type_traits>
 
 namespace gdn {
 
@@ -639,7 +640,17 @@ struct StateSmem {
     // pieces the forming waves wait for
     static constexpr size_t mk_off = xch_off + xch_bytes, mk_bytes = NMK * sizeof(float) * kPrepLds;
     static constexpr size_t cnt_off = mk_off + mk_bytes;
-    static constexpr size_t bytes = cnt_off + (FUSE ? 16 : 0);
+    // Output staging (OBUF): two buffers of a chunk's output rows for the
+    // block's BV value columns (fp32 or 16-bit, OPITCH bytes per token), so
+    // that the rows go to HBM as whole cache lines rather than as each
+    // wave's 16-column pieces.  Used when a block holds at least two column
+    // groups and the buffers fit beside the rest.
+    static constexpr int OPITCH = BV * 4 + 16;
+    static constexpr size_t ob_off = (cnt_off + (FUSE ? 16 : 0) + 15) / 16 * 16;
+    static constexpr bool OBUF = OUT && SPLIT == 1 && QKB == 2 && NW >= 2 &&
+                                 ob_off + 2 * (size_t)C * OPITCH <= 160 * 1024;
+    static constexpr size_t ob_bytes = OBUF ? (size_t)C * OPITCH : 0;
+    static constexpr size_t bytes = OBUF ? ob_off + 2 * ob_bytes : cnt_off + (FUSE ? 16 : 0);
     static constexpr int NV = (int)(VB / 1024), NM = (int)(MP / 1024);
     static constexpr int NMC = NM;                                        // copies of M
     static constexpr int NPC = (OUT && !FUSE) ? NM : 0;                   // copies of P
@@ -995,73 +1006,115 @@ __global__ __launch_bounds__((64 * StateSmem<in_t, OP, DK, NW, OUT, SPLIT, FUSE>
 #pragma unroll
     for (int t = 0; t < KTW; ++t) asm volatile("" : "+v"(sT[t]));
 
-    // Output stores of the last chunk.  Their data and address registers are
-    // left untouched until the next chunk rewrites them (phase 7): reusing
-    // them earlier would make the next chunk wait for those stores to finish.
+    // Output tiles (fp32, and rounded to 16 bits and packed) and store addresses.
     typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-    float4_t oq[4] = {};        // output tiles, fp32 (the data of fp32 stores)
-    u32x2_t oh[4] = {};         // the same rounded to 16 bits and packed
-    uint64_t oa[4] = {};        // store addresses
-    auto keep_stores = [&]() {
-        asm volatile("" ::"v"(oq[0]), "v"(oq[1]), "v"(oq[2]), "v"(oq[3]), "v"(oh[0]), "v"(oh[1]), "v"(oh[2]),
-                     "v"(oh[3]), "v"(oa[0]), "v"(oa[1]), "v"(oa[2]), "v"(oa[3]));
-    };
+    float4_t oq[4] = {};
+    u32x2_t oh[4] = {};
+    uint64_t oa[4] = {};
     const int osize = odt == DT_FP32 ? 4 : 2;
-    auto store_o = [&](int t0, int len) {
-        const int64_t obase = ((int64_t)t0 * H + h) * DV + v0 + 4 * jj + (int64_t)nn * H * DV;
-        const int64_t ostep = (int64_t)16 * H * DV;
+    // The lane's output address in the block's first chunk; a chunk and a
+    // row tile further on are uniform byte offsets.
+    const uint64_t o_lane = reinterpret_cast<uint64_t>(o) +
+                            (uint64_t)((((int64_t)tok0 * H + h) * DV + v0 + 4 * jj + (int64_t)nn * H * DV) * osize);
+    const int64_t o_chunk = (int64_t)C * H * DV * osize, o_tile = (int64_t)16 * H * DV * osize;
+    // Stores of NR row tiles (row tile rt0 + r from oq[r]).  The output type
+    // and a partial chunk are decided once for all of them, so the stores
+    // issue as straight-line code.
+    auto store_rows = [&](int ci, int len, auto NRc, int rt0) {
+        constexpr int NR = decltype(NRc)::value;
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-            oa[rt] = reinterpret_cast<uint64_t>(o) + (uint64_t)((obase + rt * ostep) * osize);
-            if (odt == DT_BF16) {
-                oh[rt] = u32x2_t{from_f32<bf16_t>(oq[rt][0]).bits | ((uint32_t)from_f32<bf16_t>(oq[rt][1]).bits << 16),
-                                 from_f32<bf16_t>(oq[rt][2]).bits | ((uint32_t)from_f32<bf16_t>(oq[rt][3]).bits << 16)};
-            } else if (odt == DT_FP16) {
-                oh[rt] = __builtin_bit_cast(u32x2_t, half4_t{(_Float16)oq[rt][0], (_Float16)oq[rt][1],
-                                                             (_Float16)oq[rt][2], (_Float16)oq[rt][3]});
+        for (int r = 0; r < NR; ++r) oa[r] = o_lane + (uint64_t)(ci * o_chunk + (rt0 + r) * o_tile);
+        if (odt == DT_FP32) {
+            if (len == C) {
+#pragma unroll
+                for (int r = 0; r < NR; ++r)
+                    __builtin_nontemporal_store(oq[r], reinterpret_cast<__attribute__((address_space(1))) float4_t *>(oa[r]));
+            } else {
+#pragma unroll
+                for (int r = 0; r < NR; ++r)
+                    if (16 * (rt0 + r) + nn < len)
+                        __builtin_nontemporal_store(oq[r], reinterpret_cast<__attribute__((address_space(1))) float4_t *>(oa[r]));
             }
+            return;
+        }
+        if (odt == DT_BF16) {
+#pragma unroll
+            for (int r = 0; r < NR; ++r)
+                oh[r] = u32x2_t{pack_bf16x2(oq[r][0], oq[r][1]), pack_bf16x2(oq[r][2], oq[r][3])};
+        } else {
+#pragma unroll
+            for (int r = 0; r < NR; ++r)
+                oh[r] = __builtin_bit_cast(u32x2_t, half4_t{(_Float16)oq[r][0], (_Float16)oq[r][1],
+                                                            (_Float16)oq[r][2], (_Float16)oq[r][3]});
+        }
+        if (len == C) {
+#pragma unroll
+            for (int r = 0; r < NR; ++r)
+                __builtin_nontemporal_store(oh[r], reinterpret_cast<__attribute__((address_space(1))) u32x2_t *>(oa[r]));
+        } else {
+#pragma unroll
+            for (int r = 0; r < NR; ++r)
+                if (16 * (rt0 + r) + nn < len)
+                    __builtin_nontemporal_store(oh[r], reinterpret_cast<__attribute__((address_space(1))) u32x2_t *>(oa[r]));
+        }
+    };
+    auto store_o = [&](int ci, int len) { store_rows(ci, len, std::integral_constant<int, 4>{}, 0); };
+
+    // OBUF: chunk ci's output tiles go to staging buffer ci & 1 (each lane
+    // its four rows' 4 values, fp32 or rounded to 16 bits); after the next
+    // block barrier every compute wave stores an equal share of the chunk's
+    // rows, each store instruction covering whole rows of the block's
+    // columns (OB_N per wave: the rows' bytes are BV * osize, 16 per lane).
+    // (only in blocks whose column groups are all within DV)
+    const bool obuf = L::OBUF && vb + BV <= DV;
+    const uint64_t o_blk = reinterpret_cast<uint64_t>(o) + (uint64_t)((((int64_t)tok0 * H + h) * DV + vb) * osize);
+    const int64_t o_row = (int64_t)H * DV * osize;
+    auto stage_o = [&](int ci) {
+        unsigned char *ob = smem + L::ob_off + (size_t)(ci & 1) * L::ob_bytes;
+        if (odt == DT_FP32) {
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+                *reinterpret_cast<float4_t *>(ob + (16 * rt + nn) * L::OPITCH + 4 * (16 * cg + 4 * jj)) = oq[rt];
+            return;
         }
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
-            if (len == C || 16 * rt + nn < len) {
-                if (odt == DT_FP32)
-                    __builtin_nontemporal_store(oq[rt], reinterpret_cast<__attribute__((address_space(1))) float4_t *>(oa[rt]));
-                else
-                    __builtin_nontemporal_store(oh[rt], reinterpret_cast<__attribute__((address_space(1))) u32x2_t *>(oa[rt]));
+            oh[rt] = odt == DT_BF16 ? u32x2_t{pack_bf16x2(oq[rt][0], oq[rt][1]), pack_bf16x2(oq[rt][2], oq[rt][3])}
+                                    : __builtin_bit_cast(u32x2_t, half4_t{(_Float16)oq[rt][0], (_Float16)oq[rt][1],
+                                                                         (_Float16)oq[rt][2], (_Float16)oq[rt][3]});
+            *reinterpret_cast<u32x2_t *>(ob + (16 * rt + nn) * L::OPITCH + 2 * (16 * cg + 4 * jj)) = oh[rt];
+        }
+    };
+    // Rows of staged chunk cs (a whole chunk: only a sequence's last chunk
+    // can be partial, and that one is stored directly).
+    auto flush_o = [&](int cs) {
+        const unsigned char *ob = smem + L::ob_off + (size_t)(cs & 1) * L::ob_bytes;
+        const uint64_t oc = o_blk + (uint64_t)(cs * o_chunk);
+        if (odt == DT_FP32) {
+            constexpr int LPR = BV * 4 / 16, TPI = 64 / LPR, PER = LPR / NW;   // lanes per row, rows per store
+            const int tr = l / LPR, cb = 16 * (l % LPR);
+#pragma unroll
+            for (int j = 0; j < PER; ++j) {
+                const int tok = (cg * PER + j) * TPI + tr;
+                const float4_t d = *reinterpret_cast<const float4_t *>(ob + tok * L::OPITCH + cb);
+                __builtin_nontemporal_store(d, reinterpret_cast<__attribute__((address_space(1))) float4_t *>(
+                                                   oc + (uint64_t)(tok * o_row + cb)));
+            }
+        } else {
+            constexpr int LPR = BV * 2 / 16, TPI = 64 / LPR, PER = LPR / NW;
+            const int tr = l / LPR, cb = 16 * (l % LPR);
+#pragma unroll
+            for (int j = 0; j < PER; ++j) {
+                const int tok = (cg * PER + j) * TPI + tr;
+                const float4_t d = *reinterpret_cast<const float4_t *>(ob + tok * L::OPITCH + cb);
+                __builtin_nontemporal_store(d, reinterpret_cast<__attribute__((address_space(1))) float4_t *>(
+                                                   oc + (uint64_t)(tok * o_row + cb)));
             }
         }
     };
 
-    // Output stores of a split wave: its two row tiles 2 hh, 2 hh + 1 (the
-    // data and address registers are kept as above).
-    auto keep_stores2 = [&]() {
-        asm volatile("" ::"v"(oq[0]), "v"(oq[1]), "v"(oh[0]), "v"(oh[1]), "v"(oa[0]), "v"(oa[1]));
-    };
-    auto store_o2 = [&](int t0, int len) {
-        const int64_t obase = ((int64_t)t0 * H + h) * DV + v0 + 4 * jj + (int64_t)nn * H * DV;
-        const int64_t ostep = (int64_t)16 * H * DV;
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-            const int rt = 2 * hh + k2;
-            oa[k2] = reinterpret_cast<uint64_t>(o) + (uint64_t)((obase + rt * ostep) * osize);
-            if (odt == DT_BF16) {
-                oh[k2] = u32x2_t{from_f32<bf16_t>(oq[k2][0]).bits | ((uint32_t)from_f32<bf16_t>(oq[k2][1]).bits << 16),
-                                 from_f32<bf16_t>(oq[k2][2]).bits | ((uint32_t)from_f32<bf16_t>(oq[k2][3]).bits << 16)};
-            } else if (odt == DT_FP16) {
-                oh[k2] = __builtin_bit_cast(u32x2_t, half4_t{(_Float16)oq[k2][0], (_Float16)oq[k2][1],
-                                                             (_Float16)oq[k2][2], (_Float16)oq[k2][3]});
-            }
-        }
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-            if (len == C || 16 * (2 * hh + k2) + nn < len) {
-                if (odt == DT_FP32)
-                    __builtin_nontemporal_store(oq[k2], reinterpret_cast<__attribute__((address_space(1))) float4_t *>(oa[k2]));
-                else
-                    __builtin_nontemporal_store(oh[k2], reinterpret_cast<__attribute__((address_space(1))) u32x2_t *>(oa[k2]));
-            }
-        }
-    };
+    // Output stores of a split wave: its two row tiles 2 hh, 2 hh + 1.
+    auto store_o2 = [&](int ci, int len) { store_rows(ci, len, std::integral_constant<int, 2>{}, 2 * hh); };
 
     // The two roles run separate loops with the same barriers: one per chunk
     // (two with a single Q/K buffer).  Before a barrier a stager waits for
@@ -1110,9 +1163,17 @@ __global__ __launch_bounds__((64 * StateSmem<in_t, OP, DK, NW, OUT, SPLIT, FUSE>
             if (ci + 1 < nchunks) dma(ci + 1, b ^ 1);
         }
     };
+    // Register budgets of a compute step (see its phases): K (and Q) row
+    // fragments, registers per fragment pair, registers for read-ahead
+    // fragments, and how many K and Q fragments are held at once.
+    constexpr int NX = 4 * KP;
+    constexpr int FR = 4 * OPB / 2;
+    constexpr int RBR = KT > 8 ? 32 : 64;
+    constexpr int WX = NX < RBR / FR ? NX : RBR / FR;
+    constexpr int WQ = NX / 2 < RBR / 2 / FR ? NX / 2 : RBR / 2 / FR;
+    constexpr int NQ1 = NX / 2;                     // Q S^T items before the update
     // Compute step ci.
     auto compute = [&](auto ci) {   // (generic: instantiated only where called)
-        const int t0 = tok0 + ci * C;
         const int len = min(C, len_seq - ci * C);
         const int b = ci & 1;
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -1135,11 +1196,6 @@ __global__ __launch_bounds__((64 * StateSmem<in_t, OP, DK, NW, OUT, SPLIT, FUSE>
         // matrix-core and vector work.  Row-fragment item i of K or Q is
         // (k-tile pair i / 4, row tile i % 4); consecutive products of a phase
         // go to different accumulators.
-        constexpr int NX = 4 * KP;                      // K (and Q) row fragments
-        constexpr int FR = 4 * OPB / 2;                 // registers per fragment pair
-        constexpr int RB = KT > 8 ? 32 : 64;            // registers for read-ahead fragments
-        constexpr int WX = NX < RB / FR ? NX : RB / FR; // K fragments held at once
-        constexpr int WQ = NX / 2 < RB / 2 / FR ? NX / 2 : RB / 2 / FR;   // Q fragments held at once
         auto rd_row = [&](const unsigned char *blk, int i) {
             return row_frag2(reinterpret_cast<const OP *>(blk + 16 * (i % 4) * QROW + frag_lane) + 32 * (i / 4));
         };
@@ -1196,7 +1252,6 @@ __global__ __launch_bounds__((64 * StateSmem<in_t, OP, DK, NW, OUT, SPLIT, FUSE>
         F2 mpair[6];
 #pragma unroll
         for (int jx = 0; jx < 6; ++jx) mpair[jx] = tri_pair(Ms, PMT[jx], PP[jx]);
-        constexpr int NQ1 = NX / 2;                     // Q S^T items before the update
         F2 qf[WQ];
         if constexpr (OUT) {
 #pragma unroll
@@ -1225,7 +1280,7 @@ __global__ __launch_bounds__((64 * StateSmem<in_t, OP, DK, NW, OUT, SPLIT, FUSE>
         float4_t kp4[4];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) kp4[mt] = *reinterpret_cast<const float4_t *>(kap_s + 16 * mt + 4 * jj);
-        constexpr int NT1 = KT < RB / 4 / FR ? KT : RB / 4 / FR;   // K^T tiles read ahead
+        constexpr int NT1 = KT < RBR / 4 / FR ? KT : RBR / 4 / FR;   // K^T tiles read ahead
         F2 ka[KT][2];
 #pragma unroll
         for (int t = 0; t < NT1; ++t) {
@@ -1260,6 +1315,11 @@ __global__ __launch_bounds__((64 * StateSmem<in_t, OP, DK, NW, OUT, SPLIT, FUSE>
         }
         __builtin_amdgcn_sched_barrier(0);
 
+        // The previous chunk's rows (staged before this chunk's barrier) go
+        // out here, after the stagers have issued this step's loads.
+        if constexpr (L::OBUF) {
+            if (obuf && ci > 0) flush_o(ci - 1);
+        }
         // -- phase 6: state update, K^T fragments read NT1 tiles ahead; the
         // two products of a tile are NT1 apart, not back to back --
 #pragma unroll
@@ -1294,10 +1354,15 @@ __global__ __launch_bounds__((64 * StateSmem<in_t, OP, DK, NW, OUT, SPLIT, FUSE>
 #pragma unroll
         for (int jx = 0; jx < 6; ++jx) mma2(pv[PMT[jx]], vB[PP[jx]], ppair[jx]);
         // O^T = (S Q^T) diag(gamma) + V'^T P^T
-        keep_stores();
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) oq[rt] = qs[rt] * g1[rt] + pv[rt];
-        store_o(t0, len);
+        if constexpr (L::OBUF) {
+            if (obuf && ci + 1 < nchunks) {
+                stage_o(ci);
+                return;
+            }
+        }
+        store_o(ci, len);
     };
 
     // Compute step ci with split waves (SPLIT == 2).  The two waves of a
@@ -1310,7 +1375,6 @@ __global__ __launch_bounds__((64 * StateSmem<in_t, OP, DK, NW, OUT, SPLIT, FUSE>
     // partner's Q S^T half for them.  The chain per chunk is half of K S^T,
     // V' = M Y and half of the update.
     auto compute2 = [&](auto ci) {
-        const int t0 = tok0 + ci * C;
         const int len = min(C, len_seq - ci * C);
         const int b = ci & 1;
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -1465,14 +1529,13 @@ __global__ __launch_bounds__((64 * StateSmem<in_t, OP, DK, NW, OUT, SPLIT, FUSE>
         for (int k2 = 0; k2 < 2; ++k2) mma2(pv[k2], vB[0], ppA[k2]);
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) mma2(pv[k2], vB[1], ppB[k2]);
-        keep_stores2();
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
             const float4_t q = hh == 0 ? qs[k2] : qs[2 + k2];
             const float4_t sum = hh == 0 ? q + qp[k2] : qp[k2] + q;
             oq[k2] = sum * g1[k2] + pv[k2];
         }
-        store_o2(t0, len);
+        store_o2(ci, len);
     };
 
     // ---- the forming wave (FUSE) ----

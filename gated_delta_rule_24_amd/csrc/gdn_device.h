@@ -47,16 +47,16 @@ template <>
 __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <>
 __device__ __forceinline__ _Float16 from_f32<_Float16>(float x) { return (_Float16)x; }
+// Round to nearest even with gfx950's conversion instruction (NaN stays NaN).
 template <>
 __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) {
-    uint32_t u = __float_as_uint(x);
-    bf16_t r;
-    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) {
-        r.bits = (uint16_t)((u >> 16) | 0x40u);  // quiet NaN
-    } else {
-        r.bits = (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);  // round to nearest even
-    }
-    return r;
+    return bf16_t{__builtin_bit_cast(uint16_t, (__bf16)x)};
+}
+// Two values rounded to bf16 by one instruction, the first in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{a, b}), bf16x2_t));
 }
 
 // ---- matrix-core tile products --------------------------------------------------
