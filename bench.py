@@ -99,6 +99,21 @@ def measured_traffic(kernel, workload):
     return 1024.0 * (k["fetch_kib"] * cal["fetch_scale"] + k["write_kib"] * cal["write_scale"])
 
 
+def measured_mfma_busy(kernel, workload):
+    """Share of all matrix-core cycles `kernel` kept busy on `workload`, from the committed SQ counter
+    readings: SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs).  None when the
+    kernel's sources have changed since the counters were taken (or none were taken)."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)
+    except OSError:
+        return None
+    k = rec.get("sq", {}).get(f"{kernel}@{workload}")
+    if not k or kernel_sources_digest(k["sources"]) != k["sources_sha256"]:
+        return None
+    return k["SQ_VALU_MFMA_BUSY_CYCLES"] / (k["GRBM_GUI_ACTIVE"] / 8 * 1024)
+
+
 def _to(x, dev, dt):
     import numpy as np
     import torch
@@ -186,6 +201,7 @@ def run_chunk_workload(args, gdn, W, dev, name, out_dtype="fp32"):
         "algorithmic_bytes": min_bytes,
         "mfma_tflops": flops / dom_s / 1e12,
         "mfma_frac": flops / dom_s / 1e12 / MFMA_F16_PEAK_TFLOPS,
+        "mfma_busy_counter": measured_mfma_busy(dom, name),
         "path_hbm_frac": min_bytes / path_s / 1e9 / HBM_PEAK_GBS,
         "path_mfma_frac": flops / path_s / 1e12 / MFMA_F16_PEAK_TFLOPS,
     }
@@ -332,6 +348,10 @@ def run_backward(args, gdn, W, dev):
                      "peak": MFMA_F32_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": gflops / g_s / 1e12 / MFMA_F32_PEAK_TFLOPS,
                      "traffic": measured_traffic("gdn_bwd_grad", "backward"), "algorithmic_flops": gflops,
+                     "mfma_busy_counter": measured_mfma_busy("gdn_bwd_grad", "backward"),
+                     "note": "flops priced at the fp32 matrix peak although the bf16-input dQ/dK products run as "
+                             "exact three-term bf16 splits on the bf16 instruction; mfma_busy_counter is the "
+                             "hardware share of matrix-core cycles, independent of that pricing",
                      "dominant_kernel": dom},
         "kernels": kernels,
     }
