@@ -16,11 +16,13 @@
 //   O        = diag(gamma) Q S^T + (Q K^T o Gamma) V'
 //   S_next   = gamma^C S + V'^T diag(exp(g_C - g_r)) K
 //
-// The kernels use the same algebra with one regrouping:
-//   V' = (T diag(beta)) (V - diag(gamma) (K S^T)),
-// i.e. W S^T is formed as (T diag(beta)) (diag(gamma) K S^T) instead of
-// materialising W, which saves a C x C x dk product per chunk and keeps the
-// per-chunk matrices handed from G1 to G2 at C x C size.
+// The kernels use the same algebra regrouped:
+//   V' = M Y,  M = T diag(beta),  Y = V - diag(gamma) (K S^T),
+// i.e. W S^T is formed as M (diag(gamma) K S^T) instead of materialising W,
+// which saves a C x C x dk product per chunk and keeps the per-chunk matrices
+// handed from G1 to G2 at C x C size; and V' itself is never formed: the
+// update takes diag(kappa) V' = (diag(kappa) M) Y and the output (P o
+// Gamma-masked) V' = (P M) Y, with diag(kappa) M and P M made by G1.
 //
 // Kernels (all launched on the caller's stream):
 //   G0 chunk_table_kernel  packed batches only, one block: validates
@@ -31,16 +33,17 @@
 //                          cumulative log-decay g, the decay-masked Q K^T
 //                          block P, A, T = (I + A)^{-1} (diagonal 16x16
 //                          blocks by back substitution, the rest by blocked
-//                          products), and M = T diag(beta).  Writes the decay
-//                          factors, M and P to the workspace.
+//                          products), M = T diag(beta) and the products
+//                          diag(kappa) M and P M, which it writes to the
+//                          workspace with the decay factors.
 //   G2 chunk_state_kernel  one block per (sequence, head, value tile), serial
 //                          over the sequence's chunks.  Each wave owns 16
 //                          value columns and keeps its slice of S^T in
 //                          registers (fp32 MFMA accumulators) for the whole
 //                          sequence.  Per chunk:  X = [Q; K] S^T,
-//                          Y = V - diag(gamma) X_K,  V' = M Y,
-//                          O = diag(gamma) X_Q + P V',
-//                          S^T <- gamma^C S^T + K^T (diag(exp(g_C - g)) V').
+//                          Y = V - diag(gamma) X_K,
+//                          O = diag(gamma) X_Q + (P M) Y,
+//                          S^T <- gamma^C S^T + K^T ((diag(kappa) M) Y).
 //                          Accumulator tiles feed the next product as B
 //                          operands directly (see gdn_device.h), so only the
 //                          shared Q, K, K^T, M, P blocks go through LDS.
@@ -214,14 +217,14 @@ __global__ __launch_bounds__(256) void chunk_table_kernel(int N, int T, const in
 constexpr float kLog2e = 1.4426950408889634f;
 __device__ __forceinline__ float exp2_neg(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// LDS of one G1 wave, in floats: g, beta and the reciprocal row norms of Q and
-// K for the 64 rows, then four 16 x 16 blocks (N^T of each diagonal block
-// during the solve, T_aa after it).  Row pitch 20 and block pitch 324 keep the
+// LDS of one G1 wave, in floats: g, beta, the reciprocal row norms of Q and
+// K and kappa / ||k|| for the 64 rows, then four 16 x 16 blocks (N^T of each
+// diagonal block during the solve, T_aa after it).  Row pitch 20 and block pitch 324 keep the
 // 16-byte row reads, the column reads and the four-block broadcast reads free
 // of bank conflicts.
 constexpr int kPrepBP = 20;
 constexpr int kPrepBS = 16 * kPrepBP + 4;
-constexpr int kPrepLds = 4 * C + 4 * kPrepBS;
+constexpr int kPrepLds = 5 * C + 4 * kPrepBS;
 
 // One 16 x 16 x 16 tile product of the inverse: (R(A), C(B)) -> C(AB) + acc,
 // or equally (C(U), R(T)) -> R(TU) + acc, fp32 sums.  When M is stored in
@@ -248,20 +251,24 @@ struct InvMma<float> {
 // The UT transform and the decay-masked Q K^T of one chunk from the wave's
 // Gram accumulators (R layout, the 10 lower tiles; pacc = Q K^T, gacc =
 // K K^T): P = (Q K^T) o Gamma with the normalisation factors, A =
-// strictLower(diag(beta)(Gamma o K K^T)), T = (I + A)^{-1} and M = T diag(beta),
-// P and M written in fragment order (tile t at t * 256, lane l's four values
-// at 4 l) to p_out / m_out (global or LDS).  The scratch holds, per row r of
-// the chunk (lane r wrote them): gs = g_r log2 e, bs = beta_r, qn = 1 / ||q_r||,
-// kn = 1 / ||k_r||, then the four 16 x 16 blocks of the diagonal inverse.
-// One wave, no block barriers.  DO_P / DO_M leave out P or M.
-template <typename OP, bool DO_P, bool DO_M>
+// strictLower(diag(beta)(Gamma o K K^T)), T = (I + A)^{-1} and M = T diag(beta).
+// Written in fragment order (tile t at t * 256, lane l's four values at 4 l):
+//   m_out = diag(kappa / ||k||) M   (the state pass's update takes
+//           diag(kappa / ||k||) V' = m_out Y, and V' itself is not needed)
+//   p_out = P M                     (the output's intra-chunk term P V' =
+//           (P M) Y, lower triangular like P and M)
+// The scratch holds, per row r of the chunk (lane r wrote them): gs = g_r
+// log2 e, bs = beta_r, qn = 1 / ||q_r||, kn = 1 / ||k_r||, kh = kappa_r /
+// ||k_r||, then the four 16 x 16 blocks of the diagonal inverse.  One wave, no
+// block barriers.
+template <typename OP>
 __device__ __forceinline__ void ut_epilogue(const float4_t (&pacc)[kTriTiles], const float4_t (&gacc)[kTriTiles],
                                             float *lds, OP *p_out, OP *m_out) {
     using M = Mma<OP>;
     using MI = InvMma<OP>;
     constexpr int BP = kPrepBP, BS = kPrepBS;
-    const float *gs = lds, *bs = lds + C, *qn = lds + 2 * C, *kn = lds + 3 * C;
-    float *blk = lds + 4 * C;
+    const float *gs = lds, *bs = lds + C, *qn = lds + 2 * C, *kn = lds + 3 * C, *kh = lds + 4 * C;
+    float *blk = lds + 5 * C;
     const int l = lane_id(), nn = l & 15, jj = l >> 4;
     // Decay masks (g in base-2 units).  Off-diagonal tiles: row r = 16a + n, columns
     // c = 16b + 4j + i < r, one exponential shared by P and A.  Diagonal
@@ -277,6 +284,7 @@ __device__ __forceinline__ void ut_epilogue(const float4_t (&pacc)[kTriTiles], c
         ikr[a] = kn[16 * a + nn];
     }
     float4_t aR[kTriTiles];   // R(-A_ab) for a > b
+    float4_t pR[kTriTiles];   // R(P_ab)
 #pragma unroll
     for (int t = 0; t < kTriTiles; ++t) {
         int a, b;
@@ -302,13 +310,12 @@ __device__ __forceinline__ void ut_epilogue(const float4_t (&pacc)[kTriTiles], c
                 pv[i] = lower ? e * iqr[a] * pacc[t][i] : 0.f;
                 av[i] = lower ? 0.f : bc[i] * ikr[a] * e * gacc[t][i];
             }
-            if constexpr (DO_M) *reinterpret_cast<float4_t *>(blk + a * BS + nn * BP + 4 * jj) = av;
+            *reinterpret_cast<float4_t *>(blk + a * BS + nn * BP + 4 * jj) = av;
             aR[t] = float4_t{0.f, 0.f, 0.f, 0.f};
         }
-        if constexpr (DO_P) *reinterpret_cast<typename M::frag *>(p_out + t * kTileElems + 4 * l) = M::cvt(pv);
+        pR[t] = pv;
     }
     asm volatile("" ::: "memory");
-    if constexpr (!DO_M) return;
 
     // Diagonal blocks: lane (n, j) computes row n of T_jj,
     //   x[c] = [c == n] - sum_{i > c} x[i] N[i][c],  c = 15 .. 0,
@@ -335,39 +342,51 @@ __device__ __forceinline__ void ut_epilogue(const float4_t (&pacc)[kTriTiles], c
                 float4_t{x[4 * qd], x[4 * qd + 1], x[4 * qd + 2], x[4 * qd + 3]};
     }
     asm volatile("" ::: "memory");
-    float4_t tR[4], tC[3];   // R(T_aa), C(T_bb)
+    float4_t tR[4], tC[4];   // R(T_aa), C(T_bb)
 #pragma unroll
     for (int a = 0; a < 4; ++a) tR[a] = *reinterpret_cast<const float4_t *>(blk + a * BS + nn * BP + 4 * jj);
 #pragma unroll
-    for (int b = 0; b < 3; ++b)
+    for (int b = 0; b < 4; ++b)
 #pragma unroll
         for (int i = 0; i < 4; ++i) tC[b][i] = blk[b * BS + (4 * jj + i) * BP + nn];
 
     // Off-diagonal blocks by distance from the diagonal.
     const float4_t z = {0.f, 0.f, 0.f, 0.f};
-    float4_t TR[kTriTiles];   // R(T_ab)
+    float4_t TR[kTriTiles], TC[kTriTiles];   // R(T_ab), C(T_ab)
 #pragma unroll
-    for (int a = 0; a < 4; ++a) TR[tri_index(a, a)] = tR[a];
-    // W = -U_ab (from the negated A tiles); T_ab = T_aa W in R layout, and
-    // in C layout where a later U needs it.
-    float4_t W, C10, C21, C20;
+    for (int a = 0; a < 4; ++a) {
+        TR[tri_index(a, a)] = tR[a];
+        TC[tri_index(a, a)] = tC[a];
+    }
+    // W = -U_ab (from the negated A tiles); T_ab = T_aa W in R layout and in
+    // C layout (C layout feeds the later U's and the products with M below).
+    float4_t W;
     W = MI::mm(aR[tri_index(1, 0)], tC[0], z);
     TR[tri_index(1, 0)] = MI::mm(W, tR[1], z);
-    C10 = MI::mm(tR[1], W, z);
+    TC[tri_index(1, 0)] = MI::mm(tR[1], W, z);
     W = MI::mm(aR[tri_index(2, 1)], tC[1], z);
     TR[tri_index(2, 1)] = MI::mm(W, tR[2], z);
-    C21 = MI::mm(tR[2], W, z);
+    TC[tri_index(2, 1)] = MI::mm(tR[2], W, z);
     W = MI::mm(aR[tri_index(3, 2)], tC[2], z);
     TR[tri_index(3, 2)] = MI::mm(W, tR[3], z);
-    W = MI::mm(aR[tri_index(2, 1)], C10, MI::mm(aR[tri_index(2, 0)], tC[0], z));
+    TC[tri_index(3, 2)] = MI::mm(tR[3], W, z);
+    W = MI::mm(aR[tri_index(2, 1)], TC[tri_index(1, 0)], MI::mm(aR[tri_index(2, 0)], tC[0], z));
     TR[tri_index(2, 0)] = MI::mm(W, tR[2], z);
-    C20 = MI::mm(tR[2], W, z);
-    W = MI::mm(aR[tri_index(3, 2)], C21, MI::mm(aR[tri_index(3, 1)], tC[1], z));
+    TC[tri_index(2, 0)] = MI::mm(tR[2], W, z);
+    W = MI::mm(aR[tri_index(3, 2)], TC[tri_index(2, 1)], MI::mm(aR[tri_index(3, 1)], tC[1], z));
     TR[tri_index(3, 1)] = MI::mm(W, tR[3], z);
-    W = MI::mm(aR[tri_index(3, 2)], C20, MI::mm(aR[tri_index(3, 1)], C10, MI::mm(aR[tri_index(3, 0)], tC[0], z)));
+    TC[tri_index(3, 1)] = MI::mm(tR[3], W, z);
+    W = MI::mm(aR[tri_index(3, 2)], TC[tri_index(2, 0)],
+               MI::mm(aR[tri_index(3, 1)], TC[tri_index(1, 0)], MI::mm(aR[tri_index(3, 0)], tC[0], z)));
     TR[tri_index(3, 0)] = MI::mm(W, tR[3], z);
+    TC[tri_index(3, 0)] = MI::mm(tR[3], W, z);
 
-    // M = T diag(beta), R layout = fragment order.
+    // M = T diag(beta): in C layout (lane (n, j) holds column 16 b + n) for
+    // the products P M, and in R layout scaled by kappa / ||k|| per row for
+    // the state pass.
+    float kr[4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) kr[a] = kh[16 * a + nn];
 #pragma unroll
     for (int t = 0; t < kTriTiles; ++t) {
         int a, b;
@@ -375,8 +394,20 @@ __device__ __forceinline__ void ut_epilogue(const float4_t (&pacc)[kTriTiles], c
         const float4_t bc = *reinterpret_cast<const float4_t *>(bs + 16 * b + 4 * jj);
         float4_t mv;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) mv[i] = TR[t][i] * bc[i];
+        for (int i = 0; i < 4; ++i) mv[i] = TR[t][i] * bc[i] * kr[a];
         *reinterpret_cast<typename M::frag *>(m_out + t * kTileElems + 4 * l) = M::cvt(mv);
+        TC[t] = TC[t] * bs[16 * b + nn];
+    }
+    // (P M)_ab = sum over b <= m <= a of P_am M_mb: R(P_am M_mb) from
+    // (C(M_mb), R(P_am)).
+#pragma unroll
+    for (int t = 0; t < kTriTiles; ++t) {
+        int a, b;
+        tri_decode(t, a, b);
+        float4_t acc = z;
+#pragma unroll
+        for (int m = b; m <= a; ++m) acc = MI::mm(TC[tri_index(m, b)], pR[tri_index(a, m)], acc);
+        *reinterpret_cast<typename M::frag *>(p_out + t * kTileElems + 4 * l) = M::cvt(acc);
     }
     asm volatile("" ::: "memory");   // the scratch is reused by the wave's next item
 }
@@ -401,10 +432,7 @@ struct PrepRegs {
     float la, bt;
 };
 
-// WITH_P = false: the state pass forms P itself from the Q and K rows it
-// stages (chunk_state_kernel, FUSE), so G1 reads no Q and writes no P, and
-// the third decay vector (gamma / ||q||) is the state pass's too.
-template <typename in_t, typename OP, int DK, bool WITH_P = true>
+template <typename in_t, typename OP, int DK>
 __global__ __launch_bounds__(64) void chunk_prep_kernel(int H, int T, int cpr, int urows, int qk_norm,
                                                         const int32_t *__restrict__ meta,
                                                         const int32_t *__restrict__ row_tok,
@@ -422,7 +450,7 @@ __global__ __launch_bounds__(64) void chunk_prep_kernel(int H, int T, int cpr, i
     constexpr int NPASS = L::NPASS, PP = L::PP;
     constexpr int BP = kPrepBP, BS = kPrepBS;
     __shared__ __align__(16) float lds[kPrepLds];
-    float *gs = lds, *bs = lds + C, *qn = lds + 2 * C, *kn = lds + 3 * C, *blk = lds + 4 * C;
+    float *gs = lds, *bs = lds + C, *qn = lds + 2 * C, *kn = lds + 3 * C, *kh = lds + 4 * C, *blk = lds + 5 * C;
 
     const int l = threadIdx.x, nn = l & 15, jj = l >> 4;
     const int items = (cpr ? urows : meta[0]) * H;
@@ -446,13 +474,11 @@ __global__ __launch_bounds__(64) void chunk_prep_kernel(int H, int T, int cpr, i
 #pragma unroll
             for (int p = 0; p < PP; ++p) R.k[b][p].load(k + off + 32 * p);
         }
-        if constexpr (WITH_P) {
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                const int64_t off = base + (int64_t)min(16 * b + nn, len - 1) * tok_stride;
+        for (int b = 0; b < 4; ++b) {
+            const int64_t off = base + (int64_t)min(16 * b + nn, len - 1) * tok_stride;
 #pragma unroll
-                for (int p = 0; p < PP; ++p) R.q[b][p].load(q + off + 32 * p);
-            }
+            for (int p = 0; p < PP; ++p) R.q[b][p].load(q + off + 32 * p);
         }
     };
 
@@ -474,7 +500,7 @@ __global__ __launch_bounds__(64) void chunk_prep_kernel(int H, int T, int cpr, i
 #pragma unroll
                         for (int p = 0; p < PP; ++p) {
                             R.k[b][p].zero();
-                            if constexpr (WITH_P) R.q[b][p].zero();
+                            R.q[b][p].zero();
                         }
             }
         };
@@ -509,11 +535,9 @@ __global__ __launch_bounds__(64) void chunk_prep_kernel(int H, int T, int cpr, i
                         R.k[b][p].to_f32(f);
 #pragma unroll
                         for (int e = 0; e < 8; ++e) ssk[b] += f[e] * f[e];
-                        if constexpr (WITH_P) {
-                            R.q[b][p].to_f32(f);
+                        R.q[b][p].to_f32(f);
 #pragma unroll
-                            for (int e = 0; e < 8; ++e) ssq[b] += f[e] * f[e];
-                        }
+                        for (int e = 0; e < 8; ++e) ssq[b] += f[e] * f[e];
                     }
             }
 #pragma unroll
@@ -523,7 +547,7 @@ __global__ __launch_bounds__(64) void chunk_prep_kernel(int H, int T, int cpr, i
 #pragma unroll
                 for (int p = 0; p < PP; ++p) {
                     gram_mma(gacc[t], R.k[b][p], R.k[a][p]);
-                    if constexpr (WITH_P) gram_mma(pacc[t], R.k[b][p], R.q[a][p]);
+                    gram_mma(pacc[t], R.k[b][p], R.q[a][p]);
                 }
             }
         }
@@ -550,6 +574,7 @@ __global__ __launch_bounds__(64) void chunk_prep_kernel(int H, int T, int cpr, i
         }
         qn[l] = rq;
         kn[l] = rk;
+        kh[l] = kap * rk;
         // Decay factors for the state pass, with the normalisation folded in:
         // gamma / ||k|| (scales K S^T in Y), kappa / ||k|| (the update), gamma
         // / ||q|| (the output), and gamma itself (the chunk's total decay).
@@ -559,8 +584,8 @@ __global__ __launch_bounds__(64) void chunk_prep_kernel(int H, int T, int cpr, i
         ws_g[rh * 4 * C + 3 * C + l] = gam;
         asm volatile("" ::: "memory");
 
-        ut_epilogue<OP, WITH_P, true>(pacc, gacc, lds, ws_p + rh * kTriTiles * kTileElems,
-                                      ws_m + rh * kTriTiles * kTileElems);
+        ut_epilogue<OP>(pacc, gacc, lds, ws_p + rh * kTriTiles * kTileElems,
+                                    ws_m + rh * kTriTiles * kTileElems);
     };
 
     PrepRegs<in_t, PP> R;
@@ -577,11 +602,12 @@ __global__ __launch_bounds__(64) void chunk_prep_kernel(int H, int T, int cpr, i
 // the Q, K, M, P blocks they all read are shared through that XCD's L2.
 //
 // Products per chunk and wave (16 value columns v, S^T slice in sT):
-//   X_K = K S^T                          (C x 16)   A: K rows,         B: sT
-//   Y   = V - diag(gamma) X_K                       V read transposed
-//   V'  = M Y                            (C x 16)   A: M,              B: Y
-//   O^T = (S Q^T) diag(gamma) + V'^T P^T (16 x C)   A: sT / V',        B: Q, P rows
-//   S^T = gamma_C S^T + K^T (kappa o V') (dk x 16)  A: K read transposed, B: kappa o V'
+//   X_K = K S^T                            (C x 16)   A: K rows,     B: sT
+//   Y   = V - diag(gamma) X_K                         V read transposed
+//   D   = (diag(kappa) M) Y                (C x 16)   A: diag(kappa) M, B: Y
+//   O^T = (S Q^T) diag(gamma) + Y^T (P M)^T (16 x C)  A: sT / Y,     B: Q, P M rows
+//   S^T = gamma_C S^T + K^T D              (dk x 16)  A: K read transposed, B: D
+// (M, P and kappa here carry the q/k normalisation factors G1 folds in.)
 // O is produced transposed so each lane holds four consecutive value columns
 // of one token row and writes them with one vector store.
 //
@@ -604,13 +630,10 @@ __global__ __launch_bounds__(64) void chunk_prep_kernel(int H, int T, int cpr, i
 // Waves of a state-pass block that stage inputs (the others compute).
 constexpr int kStagers = 4;
 
-template <typename in_t, typename OP, int DK, int NW, bool OUT, int SPLIT = 1, bool FUSE = false>
+template <typename in_t, typename OP, int DK, int NW, bool OUT>
 struct StateSmem {
-    // Loading waves (the stagers) and, with FUSE, one more wave that forms
-    // each chunk's P in the block.
-    static constexpr int NMK = FUSE ? 1 : 0;
-    static constexpr int NLD = (FUSE && NW * SPLIT >= 4) ? kStagers - 1 : kStagers;
-    static constexpr int WAVES = NW * SPLIT + NLD + NMK;
+    static constexpr int NLD = kStagers;                                // loading waves
+    static constexpr int WAVES = NW + NLD;
     static constexpr int BV = 16 * NW;                                  // value columns per block
     static constexpr int QROW = DK * (int)sizeof(OP) + 32;              // bytes per Q / K row
     static constexpr int VROW = BV * (int)sizeof(in_t);                 // bytes per V row
@@ -622,38 +645,26 @@ struct StateSmem {
     static constexpr size_t MP = sizeof(OP) * kTriTiles * kTileElems;   // one M or P block
     static constexpr int NMP = OUT ? 2 : 1;                             // M and P, or M alone
     static constexpr size_t GB = 1024;                                  // the four decay vectors
-    static constexpr size_t GQ = FUSE ? 256 : 0;                        // gamma / ||q|| (FUSE: formed here)
-    static constexpr size_t DMA = VB + NMP * MP + GB + GQ;              // a chunk's inputs (copied or formed)
+    static constexpr size_t DMA = VB + NMP * MP + GB;                   // a chunk's copied inputs
     static constexpr int QKB = (2 * NQK * QK + 2 * DMA <= 160 * 1024) ? 2 : 1;   // Q/K buffers
     static constexpr size_t qk_off(int b) { return (size_t)b * NQK * QK; }       // Q (if any), then K
     static constexpr size_t k_rel = OUT ? QK : 0;
     static constexpr size_t dma_off(int b) { return (size_t)QKB * NQK * QK + (size_t)b * DMA; }
-    static constexpr size_t m_rel = VB, p_rel = VB + MP, g_rel = VB + NMP * MP, gq_rel = g_rel + GB;
-    // Split waves (SPLIT == 2): per column group and dk half, the lane-major
-    // partial K S^T (4 tiles) and the partial Q S^T of the partner's two row
-    // tiles, 16 bytes per (tile, lane).
-    static constexpr size_t XCH_X = 4 * 64 * 16, XCH_Q = 2 * 64 * 16;
-    static constexpr size_t xch_off = (size_t)QKB * NQK * QK + 2 * DMA;
-    static constexpr size_t xch_bytes = SPLIT == 2 ? (size_t)NW * 2 * (XCH_X + XCH_Q) : 0;
-    // each forming wave's scratch (g, beta and norm factors per row, the
-    // diagonal blocks of the inverse), then the count of committed Q / K
-    // pieces the forming waves wait for
-    static constexpr size_t mk_off = xch_off + xch_bytes, mk_bytes = NMK * sizeof(float) * kPrepLds;
-    static constexpr size_t cnt_off = mk_off + mk_bytes;
+    static constexpr size_t m_rel = VB, p_rel = VB + MP, g_rel = VB + NMP * MP;
+    static constexpr size_t in_bytes = (size_t)QKB * NQK * QK + 2 * DMA;
     // Output staging (OBUF): two buffers of a chunk's output rows for the
     // block's BV value columns (fp32 or 16-bit, OPITCH bytes per token), so
     // that the rows go to HBM as whole cache lines rather than as each
     // wave's 16-column pieces.  Used when a block holds at least two column
     // groups and the buffers fit beside the rest.
     static constexpr int OPITCH = BV * 4 + 16;
-    static constexpr size_t ob_off = (cnt_off + (FUSE ? 16 : 0) + 15) / 16 * 16;
-    static constexpr bool OBUF = OUT && SPLIT == 1 && QKB == 2 && NW >= 2 &&
-                                 ob_off + 2 * (size_t)C * OPITCH <= 160 * 1024;
+    static constexpr size_t ob_off = (in_bytes + 15) / 16 * 16;
+    static constexpr bool OBUF = OUT && QKB == 2 && NW >= 2 && ob_off + 2 * (size_t)C * OPITCH <= 160 * 1024;
     static constexpr size_t ob_bytes = OBUF ? (size_t)C * OPITCH : 0;
-    static constexpr size_t bytes = OBUF ? ob_off + 2 * ob_bytes : cnt_off + (FUSE ? 16 : 0);
+    static constexpr size_t bytes = OBUF ? ob_off + 2 * ob_bytes : in_bytes;
     static constexpr int NV = (int)(VB / 1024), NM = (int)(MP / 1024);
     static constexpr int NMC = NM;                                        // copies of M
-    static constexpr int NPC = (OUT && !FUSE) ? NM : 0;                   // copies of P
+    static constexpr int NPC = OUT ? NM : 0;                              // copies of P
     static constexpr int NGC = 1;                                         // copies of the decay factors
     static constexpr int NDMA = NV + NMC + NPC + NGC;                     // 1 KiB wave copies per chunk
     static_assert(VB % 1024 == 0 && MP % 1024 == 0, "direct loads move whole 1 KiB wave blocks");
@@ -741,26 +752,19 @@ __device__ __forceinline__ void dma16(const void *g, uint32_t lds) {
         : "memory");
 }
 
-template <typename in_t, typename OP, int DK, int NW, bool OUT, int SPLIT, bool FUSE>
-__global__ __launch_bounds__((64 * StateSmem<in_t, OP, DK, NW, OUT, SPLIT, FUSE>::WAVES)) void chunk_state_kernel(
+template <typename in_t, typename OP, int DK, int NW, bool OUT>
+__global__ __launch_bounds__((64 * StateSmem<in_t, OP, DK, NW, OUT>::WAVES)) void chunk_state_kernel(
     int NU, int H, int DV, int nvt, int odt, int T, int cpr, int32_t *__restrict__ meta,
     const int32_t *__restrict__ cu_ws, const int32_t *__restrict__ row0, SegArgs sg,
     const in_t *__restrict__ q, const in_t *__restrict__ k, const in_t *__restrict__ v,
-    const float *__restrict__ log_alpha, const float *__restrict__ beta, int qk_norm,
     const float *__restrict__ ws_g, const OP *__restrict__ ws_m, const OP *__restrict__ ws_p,
     const float *init_state, float *final_state, void *__restrict__ o) {
     using M = Mma<OP>;
     using frag = typename M::frag;
     using F2 = Frag2<OP>;
-    using L = StateSmem<in_t, OP, DK, NW, OUT, SPLIT, FUSE>;
+    using L = StateSmem<in_t, OP, DK, NW, OUT>;
     constexpr int QROW = L::QROW, VROW = L::VROW, BV = L::BV, QKB = L::QKB;
     constexpr int NLD = L::NLD;                              // loading waves
-    static_assert(!FUSE || (OUT && SPLIT == 1 && QKB == 2 && sizeof(OP) == 2 && DK <= 128 && L::bytes <= 160 * 1024),
-                  "P formed in the state pass: output pass, two Q/K buffers, 16-bit operands, dk <= 128");
-    static_assert(SPLIT == 1 || (SPLIT == 2 && OUT && QKB == 2 && DK >= 64 && L::bytes <= 160 * 1024),
-                  "split waves: output pass, two Q/K buffers, dk >= 64, one block per compute unit");
-    constexpr int NCW = NW * SPLIT;                          // compute waves
-    constexpr int KTW = DK / 16 / SPLIT;                     // state tiles per compute wave
     constexpr int NT = 64 * NLD;                             // loading threads
     constexpr int KT = DK / 16;                              // state tiles along dk
     constexpr int KP = DK / 32;                              // k-tile pairs along dk
@@ -806,15 +810,14 @@ __global__ __launch_bounds__((64 * StateSmem<in_t, OP, DK, NW, OUT, SPLIT, FUSE>
     if (vb >= DVA) return;
     const int chain = n * H + h;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, nn = l & 15, jj = l >> 4;
-    // Waves 0..NCW-1 compute: wave w holds 16 value columns (column group
-    // cg = w / SPLIT) and, with split waves, one half of dk (hh = w % SPLIT);
-    // the kStagers waves after them stage the next chunk's inputs into LDS.
-    const bool stager = w >= NCW && w < NCW + NLD;
-    const bool maker = FUSE && w == NCW + NLD;      // the wave that forms P (FUSE)
-    const int sw = w - NCW, stid = tid - 64 * NCW;  // stager wave / thread index
-    const int cg = w / SPLIT, hh = w % SPLIT;
+    // Waves 0..NW-1 compute: wave w holds 16 value columns (column group
+    // cg = w); the kStagers waves after them stage the next chunk's inputs
+    // into LDS.
+    const bool stager = w >= NW;
+    const int sw = w - NW, stid = tid - 64 * NW;    // stager wave / thread index
+    const int cg = w;
     const int v0 = vb + cg * 16;            // first value column of a compute wave
-    const bool active = !stager && !maker && v0 < DVA;
+    const bool active = !stager && v0 < DVA;
     const bool ident = v0 >= DV;            // a column of F (transition pass only)
     // The chunks this block runs: all of the sequence's, or one segment.
     int tok0 = cpr ? n * T : cu_ws[n];
@@ -855,8 +858,7 @@ __global__ __launch_bounds__((64 * StateSmem<in_t, OP, DK, NW, OUT, SPLIT, FUSE>
     // transition pass over a first segment), the segment's incoming state
     // from the combine pass (output pass over segments), or zero / identity
     // (transition pass over a later segment).
-    // With split waves a wave holds the KTW tiles hh KTW .. hh KTW + KTW - 1.
-    float4_t sT[KTW];
+    float4_t sT[KT];
     const float *s_in = nullptr;
     int64_t s_in_row = 0;   // element offset of the lane's state row
     if (OUT && sg.seg_chunks) {
@@ -867,9 +869,8 @@ __global__ __launch_bounds__((64 * StateSmem<in_t, OP, DK, NW, OUT, SPLIT, FUSE>
         s_in_row = ((int64_t)chain * DV + v0 + nn) * DK;
     }
 #pragma unroll
-    for (int t = 0; t < KTW; ++t) {
-        const int tg = hh * KTW + t;
-        const int off = 32 * (tg >> 1) + 4 * (tg & 1);
+    for (int t = 0; t < KT; ++t) {
+        const int off = 32 * (t >> 1) + 4 * (t & 1);
         if (active && s_in && !ident) {
             sT[t] = *reinterpret_cast<const float4_t *>(s_in + s_in_row + 8 * jj + off);
         } else {
@@ -938,12 +939,6 @@ __global__ __launch_bounds__((64 * StateSmem<in_t, OP, DK, NW, OUT, SPLIT, FUSE>
             store_row8(Kb + r * (QROW / OPB) + c8, lo, hi);
         }
     };
-    // FUSE: this stager wave's part of a chunk's Q and K is in LDS (its
-    // writes complete first), counted for the forming waves.
-    auto count_commit = [&]() {
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        if (l == 0) __atomic_fetch_add(reinterpret_cast<unsigned *>(smem + L::cnt_off), 1u, __ATOMIC_RELAXED);
-    };
     // ---- direct global -> LDS copies of V, M, P and the decay factors ----
     // Copy ii of a chunk (stager wave sw issues ii = sw, sw + kStagers, ...) fills LDS bytes
     // [1024 ii, 1024 ii + 1024) of the chunk's buffer: V blocks first, then
@@ -1004,7 +999,7 @@ __global__ __launch_bounds__((64 * StateSmem<in_t, OP, DK, NW, OUT, SPLIT, FUSE>
     // these loads.
     __builtin_amdgcn_s_waitcnt(0);
 #pragma unroll
-    for (int t = 0; t < KTW; ++t) asm volatile("" : "+v"(sT[t]));
+    for (int t = 0; t < KT; ++t) asm volatile("" : "+v"(sT[t]));
 
     // Output tiles (fp32, and rounded to 16 bits and packed) and store addresses.
     typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
@@ -1113,8 +1108,6 @@ __global__ __launch_bounds__((64 * StateSmem<in_t, OP, DK, NW, OUT, SPLIT, FUSE>
         }
     };
 
-    // Output stores of a split wave: its two row tiles 2 hh, 2 hh + 1.
-    auto store_o2 = [&](int ci, int len) { store_rows(ci, len, std::integral_constant<int, 2>{}, 2 * hh); };
 
     // The two roles run separate loops with the same barriers: one per chunk
     // (two with a single Q/K buffer).  Before a barrier a stager waits for
@@ -1150,9 +1143,7 @@ __global__ __launch_bounds__((64 * StateSmem<in_t, OP, DK, NW, OUT, SPLIT, FUSE>
             if (ci + 1 < nchunks) {
                 dma(ci + 1, b ^ 1);
                 commit_qk(b ^ 1, min(C, len_seq - (ci + 1) * C), cur);
-                if constexpr (FUSE) count_commit();
             }
-            if constexpr (SPLIT == 2) asm volatile("s_barrier" ::: "memory");   // the split waves' exchange
         } else {
 #pragma unroll
             for (int it = 0; it < QK_IT; ++it) {
@@ -1185,10 +1176,10 @@ __global__ __launch_bounds__((64 * StateSmem<in_t, OP, DK, NW, OUT, SPLIT, FUSE>
         const unsigned char *Db = smem + L::dma_off(b);
         const OP *Ms = reinterpret_cast<const OP *>(Db + L::m_rel);
         const OP *Ps = reinterpret_cast<const OP *>(Db + L::p_rel);
-        // decay factors (G1): gamma / ||k||, kappa / ||k||, gamma / ||q||, gamma
+        // decay factors (G1): gamma / ||k||, kappa / ||k|| (folded into M here,
+        // not read), gamma / ||q||, gamma
         const float *gam_s = reinterpret_cast<const float *>(Db + L::g_rel);
-        const float *kap_s = gam_s + C;
-        const float *gao_s = FUSE ? reinterpret_cast<const float *>(Db + L::gq_rel) : gam_s + 2 * C;
+        const float *gao_s = gam_s + 2 * C;
 
         // The chunk is software-pipelined: each phase issues the LDS reads of
         // a later phase before its own products, and the phases are pinned
@@ -1199,7 +1190,7 @@ __global__ __launch_bounds__((64 * StateSmem<in_t, OP, DK, NW, OUT, SPLIT, FUSE>
         auto rd_row = [&](const unsigned char *blk, int i) {
             return row_frag2(reinterpret_cast<const OP *>(blk + 16 * (i % 4) * QROW + frag_lane) + 32 * (i / 4));
         };
-        // V' = M Y and V'^T P^T use the lower-triangular tiles of M and P as
+        // D = (diag(kappa) M) Y and Y^T (P M)^T use the lower-triangular tiles of M and P as
         // k-tile pairs: row tile mt takes pair 0 (tiles (mt,0),(mt,1)) and,
         // for mt >= 2, pair 1 (tiles (mt,2),(mt,3)); absent tiles are zero.
         auto tri_pair = [&](const OP *T, int mt, int p) {
@@ -1237,7 +1228,7 @@ __global__ __launch_bounds__((64 * StateSmem<in_t, OP, DK, NW, OUT, SPLIT, FUSE>
 #pragma unroll
         for (int p = 0; p < KP; ++p) sB[p] = F2::cvt(sT[2 * p], sT[2 * p + 1]);
 #pragma unroll
-        for (int t = 0; t < KT; ++t) sT[t] *= gC;   // the update adds K^T (kappa o V') later
+        for (int t = 0; t < KT; ++t) sT[t] *= gC;   // the update adds K^T D later
         __builtin_amdgcn_sched_barrier(0);
 
         // -- phase 1: X_K = K S^T; reads of M and the first Q fragments --
@@ -1271,15 +1262,12 @@ __global__ __launch_bounds__((64 * StateSmem<in_t, OP, DK, NW, OUT, SPLIT, FUSE>
         }
         __builtin_amdgcn_sched_barrier(0);
 
-        // -- phase 3: V' = M Y; reads of kappa and the first K^T fragments --
-        float4_t Vp[4];
+        // -- phase 3: D = diag(kappa) V' = (diag(kappa) M) Y; the first K^T fragments --
+        float4_t Dk[4];
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) Vp[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
+        for (int mt = 0; mt < 4; ++mt) Dk[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int jx = 0; jx < 6; ++jx) mma2(Vp[PMT[jx]], mpair[jx], yB[PP[jx]]);
-        float4_t kp4[4];
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) kp4[mt] = *reinterpret_cast<const float4_t *>(kap_s + 16 * mt + 4 * jj);
+        for (int jx = 0; jx < 6; ++jx) mma2(Dk[PMT[jx]], mpair[jx], yB[PP[jx]]);
         constexpr int NT1 = KT < RBR / 4 / FR ? KT : RBR / 4 / FR;   // K^T tiles read ahead
         F2 ka[KT][2];
 #pragma unroll
@@ -1302,17 +1290,10 @@ __global__ __launch_bounds__((64 * StateSmem<in_t, OP, DK, NW, OUT, SPLIT, FUSE>
         }
         __builtin_amdgcn_sched_barrier(0);
 
-        // -- phase 5: kappa o V' and the operand forms of V' --
-        F2 vB[2], dB[2];
-        {
-            float4_t d[4];
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) d[mt] = kp4[mt] * Vp[mt];
-            vB[0] = F2::cvt(Vp[0], Vp[1]);
-            vB[1] = F2::cvt(Vp[2], Vp[3]);
-            dB[0] = F2::cvt(d[0], d[1]);
-            dB[1] = F2::cvt(d[2], d[3]);
-        }
+        // -- phase 5: the operand form of D --
+        F2 dB[2];
+        dB[0] = F2::cvt(Dk[0], Dk[1]);
+        dB[1] = F2::cvt(Dk[2], Dk[3]);
         __builtin_amdgcn_sched_barrier(0);
 
         // The previous chunk's rows (staged before this chunk's barrier) go
@@ -1342,7 +1323,7 @@ __global__ __launch_bounds__((64 * StateSmem<in_t, OP, DK, NW, OUT, SPLIT, FUSE>
         for (int rt = 0; rt < 4; ++rt) g1[rt] = gao_s[16 * rt + nn];
         __builtin_amdgcn_sched_barrier(0);
 
-        // -- phase 7: rest of Q S^T, then V'^T P^T into a separate sum --
+        // -- phase 7: rest of Q S^T, then Y^T (P M)^T into a separate sum --
 #pragma unroll
         for (int i = NQ1; i < NX; ++i) {
             mma2(qs[i % 4], sB[i / 4], qf[i % WQ]);
@@ -1352,8 +1333,8 @@ __global__ __launch_bounds__((64 * StateSmem<in_t, OP, DK, NW, OUT, SPLIT, FUSE>
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) pv[rt] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int jx = 0; jx < 6; ++jx) mma2(pv[PMT[jx]], vB[PP[jx]], ppair[jx]);
-        // O^T = (S Q^T) diag(gamma) + V'^T P^T
+        for (int jx = 0; jx < 6; ++jx) mma2(pv[PMT[jx]], yB[PP[jx]], ppair[jx]);
+        // O^T = (S Q^T) diag(gamma) + Y^T (P M)^T
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) oq[rt] = qs[rt] * g1[rt] + pv[rt];
         if constexpr (L::OBUF) {
@@ -1365,292 +1346,11 @@ __global__ __launch_bounds__((64 * StateSmem<in_t, OP, DK, NW, OUT, SPLIT, FUSE>
         store_o(ci, len);
     };
 
-    // Compute step ci with split waves (SPLIT == 2).  The two waves of a
-    // column group hold the two dk halves of its S^T slice.  Each forms its
-    // half of K S^T and of Q S^T from its own k-tile pairs; the halves meet
-    // in LDS at one extra block barrier per chunk (the stagers take it too).
-    // Both waves then add the two K S^T halves in the same order (low half
-    // first), so they form bit-identical Y, V' and kappa o V'; each updates
-    // its own state half, and outputs its own two row tiles of O, adding the
-    // partner's Q S^T half for them.  The chain per chunk is half of K S^T,
-    // V' = M Y and half of the update.
-    auto compute2 = [&](auto ci) {
-        const int len = min(C, len_seq - ci * C);
-        const int b = ci & 1;
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        if (!active) {
-            asm volatile("s_barrier" ::: "memory");
-            return;
-        }
-        constexpr int KPH = KP / 2 > 0 ? KP / 2 : 1;    // the wave's k-tile pairs
-        constexpr int NXH = 4 * KPH;                    // its K (and Q) row fragments
-        const int p0 = hh * KPH;
-        const unsigned char *Qb = smem + L::qk_off(b);
-        const unsigned char *Kb = Qb + L::k_rel;
-        const unsigned char *Db = smem + L::dma_off(b);
-        const OP *Ms = reinterpret_cast<const OP *>(Db + L::m_rel);
-        const OP *Ps = reinterpret_cast<const OP *>(Db + L::p_rel);
-        const float *gam_s = reinterpret_cast<const float *>(Db + L::g_rel);
-        const float *kap_s = gam_s + C;
-        const float *gao_s = FUSE ? reinterpret_cast<const float *>(Db + L::gq_rel) : gam_s + 2 * C;
-        // exchange slots (lane-major, 16 bytes per tile and lane)
-        unsigned char *xch = smem + L::xch_off + (size_t)cg * 2 * (L::XCH_X + L::XCH_Q);
-        float4_t *x_mine = reinterpret_cast<float4_t *>(xch + hh * L::XCH_X) + l;
-        const float4_t *x_part = reinterpret_cast<const float4_t *>(xch + (1 - hh) * L::XCH_X) + l;
-        float4_t *q_mine = reinterpret_cast<float4_t *>(xch + 2 * L::XCH_X + hh * L::XCH_Q) + l;
-        const float4_t *q_part = reinterpret_cast<const float4_t *>(xch + 2 * L::XCH_X + (1 - hh) * L::XCH_Q) + l;
-
-        auto rd_row = [&](const unsigned char *blk, int i) {   // item i: (pair p0 + i / 4, row tile i % 4)
-            return row_frag2(reinterpret_cast<const OP *>(blk + 16 * (i % 4) * QROW + frag_lane) + 32 * (p0 + i / 4));
-        };
-        auto tri_pair = [&](const OP *T, int mt, int p) {
-            const int k0 = 2 * p, k1 = 2 * p + 1;
-            const frag lo = k0 <= mt ? lds_frag(T + tri_index(mt, k0) * kTileElems + tile_lane) : M::zero();
-            const frag hi = k1 <= mt ? lds_frag(T + tri_index(mt, k1) * kTileElems + tile_lane) : M::zero();
-            return F2::make(lo, hi);
-        };
-        constexpr int PMT[6] = {0, 1, 2, 3, 2, 3}, PP[6] = {0, 0, 0, 0, 1, 1};
-        auto rd_kt = [&](int t, int tp) {   // t: the wave's tile index
-            const int tg = hh * KTW + t, p = tg >> 1, hs = tg & 1;
-            const unsigned char *kt = Kb + kt_lane + OPB * (32 * p + 4 * hs) + 32 * tp * QROW;
-            return F2::make(kt_frag(kt, QROW, (OP *)nullptr), kt_frag(kt + 16 * QROW, QROW, (OP *)nullptr));
-        };
-
-        // -- phase 0: the wave's K and Q fragments, V, gamma; its S half as an operand --
-        const float gC = gam_s[4 * C - 1];
-        F2 kf[NXH], qf[NXH];
-#pragma unroll
-        for (int i = 0; i < NXH; ++i) kf[i] = rd_row(Kb, i);
-#pragma unroll
-        for (int i = 0; i < NXH; ++i) qf[i] = rd_row(Qb, i);
-        typename VFrag<in_t>::raw vraw[4];
-        float4_t gm[4];
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-            vraw[mt] = VFrag<in_t>::read(Db + 16 * mt * VROW, v_lane);
-            gm[mt] = *reinterpret_cast<const float4_t *>(gam_s + 16 * mt + 4 * jj);
-        }
-        F2 sB[KPH];
-#pragma unroll
-        for (int p = 0; p < KPH; ++p) sB[p] = F2::cvt(sT[2 * p], sT[2 * p + 1]);
-        __builtin_amdgcn_sched_barrier(0);
-
-        // -- phase 1: the halves of X_K = K S^T and of Q S^T; they go to LDS --
-        float4_t x[4], qs[4];
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) x[mt] = qs[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int i = 0; i < NXH; ++i) mma2(x[i % 4], kf[i], sB[i / 4]);
-#pragma unroll
-        for (int i = 0; i < NXH; ++i) mma2(qs[i % 4], sB[i / 4], qf[i]);
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) x_mine[64 * mt] = x[mt];
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) q_mine[64 * k2] = hh == 0 ? qs[2 + k2] : qs[k2];   // the partner's rows
-        F2 mpair[6];
-#pragma unroll
-        for (int jx = 0; jx < 6; ++jx) mpair[jx] = tri_pair(Ms, PMT[jx], PP[jx]);
-#pragma unroll
-        for (int t = 0; t < KTW; ++t) sT[t] *= gC;   // the update adds K^T (kappa o V') later
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        __builtin_amdgcn_sched_barrier(0);
-
-        // -- phase 2: the whole X_K (low half + high half), Y = V - diag(gamma) X_K --
-        F2 yB[2];
-        {
-            float4_t y[4];
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                const float4_t xp = x_part[64 * mt];
-                const float4_t xs = hh == 0 ? x[mt] + xp : xp + x[mt];
-                y[mt] = VFrag<in_t>::to_f32(vraw[mt]) - gm[mt] * xs;
-            }
-            yB[0] = F2::cvt(y[0], y[1]);
-            yB[1] = F2::cvt(y[2], y[3]);
-        }
-        float4_t qp[2];
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) qp[k2] = q_part[64 * k2];
-        __builtin_amdgcn_sched_barrier(0);
-
-        // -- phase 3: V' = M Y; kappa; the wave's K^T fragments --
-        float4_t Vp[4];
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) Vp[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int jx = 0; jx < 6; ++jx) mma2(Vp[PMT[jx]], mpair[jx], yB[PP[jx]]);
-        float4_t kp4[4];
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) kp4[mt] = *reinterpret_cast<const float4_t *>(kap_s + 16 * mt + 4 * jj);
-        F2 ka[KTW][2];
-#pragma unroll
-        for (int t = 0; t < KTW; ++t) {
-            ka[t][0] = rd_kt(t, 0);
-            ka[t][1] = rd_kt(t, 1);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-
-        // -- phase 5: kappa o V' and the operand forms of V' --
-        F2 vB[2], dB[2];
-        {
-            float4_t d[4];
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) d[mt] = kp4[mt] * Vp[mt];
-            vB[0] = F2::cvt(Vp[0], Vp[1]);
-            vB[1] = F2::cvt(Vp[2], Vp[3]);
-            dB[0] = F2::cvt(d[0], d[1]);
-            dB[1] = F2::cvt(d[2], d[3]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-
-        // -- phase 6: the update of the wave's state half --
-#pragma unroll
-        for (int t = 0; t < KTW; ++t) mma2(sT[t], ka[t][0], dB[0]);
-#pragma unroll
-        for (int t = 0; t < KTW; ++t) mma2(sT[t], ka[t][1], dB[1]);
-        // P tiles of the wave's row tiles mt = 2 hh + k2 as k-tile pairs 0
-        // and 1 (pair 1 is zero for the upper half's partner rows 0 and 1)
-        F2 ppA[2], ppB[2];
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-            ppA[k2] = tri_pair(Ps, 2 * hh + k2, 0);
-            ppB[k2] = tri_pair(Ps, 2 * hh + k2, 1);
-        }
-        float g1[2];
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) g1[k2] = gao_s[16 * (2 * hh + k2) + nn];
-        __builtin_amdgcn_sched_barrier(0);
-
-        // -- phase 7: the wave's two row tiles of O^T = (S Q^T) diag(gamma) + V'^T P^T --
-        // (no matrix instruction here depends on hh by a branch: the zero
-        // pair of the lower half's rows is multiplied like any other)
-        float4_t pv[2] = {float4_t{0.f, 0.f, 0.f, 0.f}, float4_t{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) mma2(pv[k2], vB[0], ppA[k2]);
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) mma2(pv[k2], vB[1], ppB[k2]);
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-            const float4_t q = hh == 0 ? qs[k2] : qs[2 + k2];
-            const float4_t sum = hh == 0 ? q + qp[k2] : qp[k2] + q;
-            oq[k2] = sum * g1[k2] + pv[k2];
-        }
-        store_o2(ci, len);
-    };
-
-    // ---- the forming wave (FUSE) ----
-    // With FUSE, G1 leaves out P: one more wave of the block forms each
-    // chunk's P = (Q K^T) o Gamma (with the normalisation factors) and
-    // gamma / ||q|| into the chunk's LDS buffer, one chunk ahead, from the Q
-    // and K rows the stagers have just committed to LDS (16-bit operands:
-    // exact products, fp32 sums, as in G1), so P never goes through HBM and
-    // G1 reads no Q.  Each stager wave adds 1 to an LDS count once its part of
-    // a chunk's Q and K is written; the forming wave reads that chunk's rows
-    // once the count shows all of them (a wait with a bounded number of
-    // polls).  It joins the block barrier once per chunk like the stagers.
-    unsigned *kcnt = reinterpret_cast<unsigned *>(smem + L::cnt_off);
-    if constexpr (FUSE) {
-        if (tid == 0) *kcnt = 0u;
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    }
-    if constexpr (FUSE) {
-        if (maker) {
-            float *scr = reinterpret_cast<float *>(smem + L::mk_off);
-            float *gs = scr, *qn = scr + 2 * C, *kn = scr + 3 * C;
-            float la = 0.f;
-            auto load_gates = [&](int ci) {   // rows past the end re-read the last row (masked in form)
-                const int t0 = tok0 + ci * C, len = min(C, len_seq - ci * C);
-                la = log_alpha[(int64_t)(t0 + min(l, len - 1)) * H + h];
-            };
-            auto form = [&](int ci) {
-                const int len = min(C, len_seq - ci * C), buf = ci & 1;
-                // wait for every stager's part of chunk ci's Q and K
-                const unsigned want = (unsigned)(NLD * (ci + 1));
-                for (int poll = 0; poll < (1 << 24); ++poll) {
-                    if (__atomic_load_n(kcnt, __ATOMIC_RELAXED) >= want) break;
-                    __builtin_amdgcn_s_sleep(1);
-                }
-                const unsigned char *Qb = smem + L::qk_off(buf);
-                const unsigned char *Kb = Qb + L::k_rel;
-                auto row = [&](const unsigned char *blk, int x, int p) {   // row block x, k-tile pair p
-                    return row_frag2(reinterpret_cast<const OP *>(blk + 16 * x * QROW + frag_lane) + 32 * p);
-                };
-                const float g = wave_inclusive_scan(l < len ? la : 0.f);
-                // 1 / ||row|| (lane l: row l), when asked for
-                float rq = 1.f, rk = 1.f;
-                if (qk_norm) {
-                    float sq[4] = {0.f, 0.f, 0.f, 0.f}, sk[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int b = 0; b < 4; ++b)
-#pragma unroll
-                        for (int p = 0; p < KP; ++p) {
-                            const half8_t vq = row(Qb, b, p).v, vk = row(Kb, b, p).v;
-#pragma unroll
-                            for (int e = 0; e < 8; ++e) {
-                                sq[b] += (float)vq[e] * (float)vq[e];
-                                sk[b] += (float)vk[e] * (float)vk[e];
-                            }
-                        }
-#pragma unroll
-                    for (int b = 0; b < 4; ++b) {
-                        sq[b] += __shfl_xor(sq[b], 16, 64);
-                        sq[b] += __shfl_xor(sq[b], 32, 64);
-                        sk[b] += __shfl_xor(sk[b], 16, 64);
-                        sk[b] += __shfl_xor(sk[b], 32, 64);
-                    }
-                    const float xq = jj == 0 ? sq[0] : (jj == 1 ? sq[1] : (jj == 2 ? sq[2] : sq[3]));
-                    const float xk = jj == 0 ? sk[0] : (jj == 1 ? sk[1] : (jj == 2 ? sk[2] : sk[3]));
-                    rq = xq > 0.f ? rsqrtf(xq) : 0.f;
-                    rk = xk > 0.f ? rsqrtf(xk) : 0.f;
-                }
-                gs[l] = g * kLog2e;
-                qn[l] = rq;
-                kn[l] = rk;
-                reinterpret_cast<float *>(smem + L::dma_off(buf) + L::gq_rel)[l] = expf(g) * rq;
-                // Gram tiles (a, b), b <= a: first operand row block b of K,
-                // second row block a of Q.  Rows past the end are zero in LDS
-                // (the stagers commit them so).
-                float4_t acc[kTriTiles];
-#pragma unroll
-                for (int t = 0; t < kTriTiles; ++t) acc[t] = float4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int p = 0; p < KP; ++p) {
-                    F2 kr[4], qr[4];
-#pragma unroll
-                    for (int b = 0; b < 4; ++b) {
-                        kr[b] = row(Kb, b, p);
-                        qr[b] = row(Qb, b, p);
-                    }
-#pragma unroll
-                    for (int t = 0; t < kTriTiles; ++t) {
-                        int a, b;
-                        tri_decode(t, a, b);
-                        mma2(acc[t], kr[b], qr[a]);
-                    }
-                }
-                asm volatile("" ::: "memory");
-                OP *dst = reinterpret_cast<OP *>(smem + L::dma_off(buf) + L::p_rel);
-                ut_epilogue<OP, true, false>(acc, acc, scr, dst, dst);
-            };
-            if (nchunks > 0) {
-                load_gates(0);
-                form(0);
-            }
-            for (int ci = 0; ci < nchunks; ++ci) {
-                if (ci + 1 < nchunks) load_gates(ci + 1);
-                asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-                if (ci + 1 < nchunks) form(ci + 1);
-            }
-            return;
-        }
-    }
-
     if (stager) {
         if (nchunks > 0) {
             prefetch_qk(0, RA);
             dma(0, 0);
             commit_qk(0, min(C, len_seq), RA);
-            if constexpr (FUSE) count_commit();
             if (QKB == 2 && nchunks > 1) prefetch_qk(1, RB);
         }
         // Register sets alternate: with QKB == 2, chunk ci+1 sits in RB for
@@ -1674,11 +1374,7 @@ __global__ __launch_bounds__((64 * StateSmem<in_t, OP, DK, NW, OUT, SPLIT, FUSE>
         }
         return;
     }
-    if constexpr (SPLIT == 2) {
-        for (int ci = 0; ci < nchunks; ++ci) compute2(ci);
-    } else {
-        for (int ci = 0; ci < nchunks; ++ci) compute(ci);
-    }
+    for (int ci = 0; ci < nchunks; ++ci) compute(ci);
 
     // The state leaving the block's chunks: the sequence's final state (output
     // pass over its last segment), or the segment's map (transition pass).
@@ -1693,10 +1389,8 @@ __global__ __launch_bounds__((64 * StateSmem<in_t, OP, DK, NW, OUT, SPLIT, FUSE>
     }
     if (active && s_out) {
 #pragma unroll
-        for (int t = 0; t < KTW; ++t) {
-            const int tg = hh * KTW + t;
-            *reinterpret_cast<float4_t *>(s_out + s_out_row + 8 * jj + 32 * (tg >> 1) + 4 * (tg & 1)) = sT[t];
-        }
+        for (int t = 0; t < KT; ++t)
+            *reinterpret_cast<float4_t *>(s_out + s_out_row + 8 * jj + 32 * (t >> 1) + 4 * (t & 1)) = sT[t];
     }
 }
 
@@ -1928,11 +1622,11 @@ static hipError_t allow_smem(K kernel, size_t bytes) {
 // empty batch still reads as equal-length), 0 for a packed one.
 static int uniform_cpr(const ChunkArgs &a) { return a.cu_seqlens ? 0 : (a.T + C - 1) / C + (a.T == 0); }
 
-template <typename in_t, typename OP, int DK, int NW, bool OUT, int SPLIT = 1, bool FUSE = false>
+template <typename in_t, typename OP, int DK, int NW, bool OUT>
 static hipError_t launch_state(const ChunkArgs &a, const ChunkWorkspace &w, const SegArgs &sg, int64_t NU,
                                hipStream_t st) {
-    using L = StateSmem<in_t, OP, DK, NW, OUT, SPLIT, FUSE>;
-    auto kern = chunk_state_kernel<in_t, OP, DK, NW, OUT, SPLIT, FUSE>;
+    using L = StateSmem<in_t, OP, DK, NW, OUT>;
+    auto kern = chunk_state_kernel<in_t, OP, DK, NW, OUT>;
     hipError_t e = allow_smem(kern, L::bytes);
     if (e != hipSuccess) return e;
     char *ws = static_cast<char *>(a.workspace);
@@ -1944,69 +1638,16 @@ static hipError_t launch_state(const ChunkArgs &a, const ChunkWorkspace &w, cons
         (int)NU, a.H, a.dv, nvt, a.out_dtype, a.T, uniform_cpr(a), reinterpret_cast<int32_t *>(ws + w.off_meta),
         reinterpret_cast<const int32_t *>(ws + w.off_cu), reinterpret_cast<const int32_t *>(ws + w.off_row0), sg,
         static_cast<const in_t *>(a.q), static_cast<const in_t *>(a.k), static_cast<const in_t *>(a.v),
-        a.log_alpha, a.beta, (a.flags & kFlagQkL2Norm) ? 1 : 0,
         reinterpret_cast<const float *>(ws + w.off_g), reinterpret_cast<const OP *>(ws + w.off_m),
         reinterpret_cast<const OP *>(ws + w.off_p), a.init_state, a.final_state, a.o);
     return hipGetLastError();
 }
 
-// P formed in the output pass (FUSE): one more wave per block forms each
-// chunk's P from the Q and K rows already staged in LDS (see
-// chunk_state_kernel), so G1 reads no Q and writes no P.  Built for 16-bit
-// inputs with dk <= 128 (two Q/K buffers), for unsegmented calls, and off
-// unless GDN_FUSE=1: on the prefill workload G1 drops from 34 to 22 us but
-// the state pass rises from 114 to 174 us, because the forming wave's work
-// lengthens every chunk step (its end is a block barrier).  A version that
-// also formed M and the decay factors (G1 not run at all) took 259 us.
-template <typename in_t, typename OP, int DK>
-constexpr bool fuse_built() {
-    return sizeof(OP) == 2 && DK <= 128 && StateSmem<in_t, OP, DK, 4, true, 1, true>::bytes <= 160 * 1024 &&
-           StateSmem<in_t, OP, DK, 4, true, 1, true>::QKB == 2;
-}
-static bool use_fuse() {
-    const char *env = getenv("GDN_FUSE");
-    return env && *env && atoi(env) != 0;
-}
-
-// Split waves for the output pass: each 16-column slice of the state is held
-// by two waves, one per dk half, which halves the serial chain of a chunk
-// step and doubles the waves in flight, at the price of one more block
-// barrier and an LDS exchange per chunk.  Measured on the prefill workload
-// it is slower (143 against 115 us: the exchange triples the waves' LDS wait
-// cycles and the extra barrier ties the compute waves to the stagers), so
-// it is off unless GDN_STATE_SPLIT=1 asks for it (dk >= 64, 16-bit inputs).
-static bool use_split_waves(int dk, int dv, int64_t units) {
-    (void)dv;
-    (void)units;
-    const char *env = getenv("GDN_STATE_SPLIT");
-    return env && *env && dk >= 64 && atoi(env) != 0;
-}
-
-// Whether a split-wave block (two column groups) is built for these types.
-template <typename in_t, typename OP, int DK>
-constexpr bool split_built() {
-    using L = StateSmem<in_t, OP, DK, 2, true, 2>;
-    return DK >= 64 && L::QKB == 2 && L::bytes <= 160 * 1024;
-}
-
-// fuse: the output pass forms P itself (G1 ran without it).
 template <typename in_t, typename OP, int DK, bool OUT>
 static hipError_t launch_state_nw(const ChunkArgs &a, const ChunkWorkspace &w, const SegArgs &sg, int64_t NU,
-                                  bool fuse, hipStream_t st) {
-    if constexpr (OUT && split_built<in_t, OP, DK>()) {
-        if (!fuse && use_split_waves(DK, a.dv, NU)) return launch_state<in_t, OP, DK, 2, true, 2>(a, w, sg, NU, st);
-    }
+                                  hipStream_t st) {
     const int cols = OUT ? a.dv : a.dv + a.dk;
     const int nw = state_waves_per_block(cols, NU, OUT ? "GDN_STATE_WAVES" : "GDN_TRANSITION_WAVES");
-    if constexpr (OUT && fuse_built<in_t, OP, DK>()) {
-        if (fuse) {
-            switch (nw) {
-            case 4: return launch_state<in_t, OP, DK, 4, true, 1, true>(a, w, sg, NU, st);
-            case 2: return launch_state<in_t, OP, DK, 2, true, 1, true>(a, w, sg, NU, st);
-            default: return launch_state<in_t, OP, DK, 1, true, 1, true>(a, w, sg, NU, st);
-            }
-        }
-    }
     switch (nw) {
     case 4: return launch_state<in_t, OP, DK, 4, OUT>(a, w, sg, NU, st);
     case 2: return launch_state<in_t, OP, DK, 2, OUT>(a, w, sg, NU, st);
@@ -2019,14 +1660,12 @@ static hipError_t launch_state_nw(const ChunkArgs &a, const ChunkWorkspace &w, c
 template <typename in_t, typename OP, int DK>
 static hipError_t launch_dk(const ChunkArgs &a, const ChunkWorkspace &w, hipStream_t st) {
     char *ws = static_cast<char *>(a.workspace);
-    const bool fuse = fuse_built<in_t, OP, DK>() && w.seg_chunks == 0 && use_fuse();
     if (w.max_rows > 0) {   // no tokens at all: only the state pass runs (final = initial)
         ProfScope prof("gdn_chunk_prep", st);
         // One wave per (row, head) item; very large batches loop.
         const int64_t items = w.max_rows * a.H;
         const int64_t grid = items < (1 << 22) ? items : (1 << 22);
-        auto prep = fuse ? chunk_prep_kernel<in_t, OP, DK, false> : chunk_prep_kernel<in_t, OP, DK, true>;
-        prep<<<dim3((unsigned)grid), dim3(64), 0, st>>>(
+        chunk_prep_kernel<in_t, OP, DK><<<dim3((unsigned)grid), dim3(64), 0, st>>>(
             a.H, a.T, uniform_cpr(a), (int)(uniform_cpr(a) ? w.max_rows : 0), (a.flags & kFlagQkL2Norm) ? 1 : 0,
             reinterpret_cast<const int32_t *>(ws + w.off_meta),
             reinterpret_cast<const int32_t *>(ws + w.off_rowtok),
@@ -2037,7 +1676,7 @@ static hipError_t launch_dk(const ChunkArgs &a, const ChunkWorkspace &w, hipStre
         if (e != hipSuccess) return e;
     }
     SegArgs sg{};
-    if (w.seg_chunks == 0) return launch_state_nw<in_t, OP, DK, true>(a, w, sg, (int64_t)a.N * a.H, fuse, st);
+    if (w.seg_chunks == 0) return launch_state_nw<in_t, OP, DK, true>(a, w, sg, (int64_t)a.N * a.H, st);
 
     const int cpr = uniform_cpr(a);
     sg.seg_chunks = w.seg_chunks;
@@ -2047,7 +1686,7 @@ static hipError_t launch_dk(const ChunkArgs &a, const ChunkWorkspace &w, hipStre
     sg.ws_end = reinterpret_cast<float *>(ws + w.off_end);
     sg.ws_sin = reinterpret_cast<float *>(ws + w.off_sin);
     const int64_t NU = w.max_units * a.H;
-    hipError_t e = launch_state_nw<in_t, OP, DK, false>(a, w, sg, NU, false, st);
+    hipError_t e = launch_state_nw<in_t, OP, DK, false>(a, w, sg, NU, st);
     if (e != hipSuccess) return e;
     {
         ProfScope prof("gdn_chunk_combine", st);
@@ -2058,7 +1697,7 @@ static hipError_t launch_dk(const ChunkArgs &a, const ChunkWorkspace &w, hipStre
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    return launch_state_nw<in_t, OP, DK, true>(a, w, sg, NU, false, st);
+    return launch_state_nw<in_t, OP, DK, true>(a, w, sg, NU, st);
 }
 
 template <typename in_t, typename OP>

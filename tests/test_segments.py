@@ -101,44 +101,3 @@ def test_segmented_malformed_cu(monkeypatch):
     torch.cuda.synchronize()
     assert gdn.chunk_fwd_check(ws) != 0
     assert bool((o == 7.0).all()) and bool((fin == 5.0).all())
-
-
-@pytest.mark.parametrize("B,T,H,dk,dv,dt", [(2, 300, 3, 128, 128, "bf16"), (1, 257, 2, 64, 96, "fp16"),
-                                            (3, 130, 2, 128, 32, "bf16")])
-def test_split_waves_parity(B, T, H, dk, dv, dt, monkeypatch):
-    """The output pass with each state slice split over two waves (one per dk
-    half, forced with GDN_STATE_SPLIT) against the oracle and against the
-    unsplit pass."""
-    inp = W.chunk_inputs(B, T, H, dk, dv, dt, seed=T + dv, init_std=0.1, name=f"split waves B{B} T{T} dk{dk} dv{dv}")
-    monkeypatch.setenv("GDN_SEG_CHUNKS", "0")
-    monkeypatch.setenv("GDN_STATE_SPLIT", "1")
-    o, S = run_chunk(inp)
-    check_parity(inp, o, S)
-    monkeypatch.setenv("GDN_STATE_SPLIT", "0")
-    o0, S0 = run_chunk(inp)
-    rms = float(o0.float().pow(2).mean().sqrt())
-    e = max(float((o - o0).abs().max()), float((S - S0).abs().max())) / rms
-    log(f"[split vs unsplit] {inp.name}: {e:.3e}")
-    assert e <= TOL[dt]
-
-
-@pytest.mark.parametrize("B,T,H,dk,dv,dt,qk", [(2, 300, 3, 128, 128, "bf16", False), (1, 257, 2, 64, 96, "fp16", True),
-                                               (1, 200, 2, 32, 256, "bf16", False), (3, 129, 2, 128, 16, "bf16", True)])
-def test_fused_prep_parity(B, T, H, dk, dv, dt, qk, monkeypatch):
-    """The chunk's M, P and decay factors formed inside the output pass from
-    the staged Q and K (the default for 16-bit inputs with dk <= 128; G1 does
-    not run) against the oracle, and against the path through G1
-    (GDN_FUSE=0)."""
-    inp = W.chunk_inputs(B, T, H, dk, dv, dt, seed=T + dk, init_std=0.1, name=f"fused B{B} T{T} dk{dk} dv{dv}")
-    if qk:   # off-unit rows (powers of two keep the values exact) for the normalisation to undo
-        inp.q[:] = inp.q * 2.0
-        inp.k[:] = inp.k * 0.25
-    monkeypatch.setenv("GDN_FUSE", "1")
-    o, S = run_chunk(inp, qk_l2norm=qk)
-    check_parity(inp, o, S, qk_l2norm=qk)
-    monkeypatch.setenv("GDN_FUSE", "0")
-    o0, S0 = run_chunk(inp, qk_l2norm=qk)
-    rms = float(o0.float().pow(2).mean().sqrt())
-    e = max(float((o - o0).abs().max()), float((S - S0).abs().max())) / rms
-    log(f"[fused vs G1] {inp.name}: {e:.3e}")
-    assert e <= TOL[dt]
