@@ -194,12 +194,14 @@ gdn_status gdn_chunk_fwd_workspace_size(const gdn_chunk_desc *desc, size_t *byte
  *   stream      HIP stream the kernels are launched on
  *
  * Evaluation: when the call averages more than 16 tokens per sequence
- * (B*T > 16*N) it runs the chunkwise algorithm (paper section 3.3);
- * otherwise it steps through the tokens with the recurrence itself (one
- * state read and one write per (sequence, head)), which is cheaper for a
- * few tokens per sequence.  Both compute eq. (10) with fp32 state and
- * accumulation and meet the same bounds; bit-identical results are
- * guaranteed between calls that take the same branch.
+ * (B*T > 16*N) it runs the chunkwise algorithm (paper section 3.3) with
+ * 64-token chunks.  Otherwise each (sequence, head) state is read and
+ * written once by one kernel: for 16-bit inputs with dk <= 128 the same
+ * chunkwise algorithm with 16-token chunks on the matrix cores, else the
+ * recurrence itself token by token; either is cheaper for a few tokens per
+ * sequence.  All compute eq. (10) with fp32 state and accumulation and meet
+ * the same bounds; bit-identical results are guaranteed between calls that
+ * take the same branch.
  *
  * o must not overlap any input or the state buffers (GDN_ERR_ALIAS).
  * Errors: GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_DTYPE, GDN_ERR_ALIGN,

@@ -297,3 +297,76 @@ def test_short_path_qk_l2norm():
     inp.k[:, 3] = 0.0     # an all-zero key row stays zero after normalisation
     o, S = run_chunk(inp, qk_l2norm=True)
     check_parity(inp, o, S, qk_l2norm=True)
+
+
+# ---- the same calls in 16-token chunks on the matrix cores (16-bit inputs, dk <= 128) ----
+# GDN_SMALL_CHUNKS=0 sends them to the token-serial kernel instead: the two
+# kernels agree with the oracle and with each other.
+
+SMALL_CASES = [
+    # lengths, H, dk, dv, in dtype, out dtype
+    ([1, 16, 5, 0, 9, 2, 3, 7], 2, 128, 128, "bf16", "fp32"),
+    ([17, 33, 1, 0], 2, 128, 256, "bf16", "bf16"),      # chunks 16 + 1 and 16 + 16 + 1
+    ([4, 4, 4, 4], 3, 32, 96, "fp16", "fp16"),
+    ([40, 0, 0, 1], 2, 64, 48, "fp16", "fp32"),
+    ([2, 2], 2, 128, 16, "bf16", "fp32"),
+]
+_OUT = {"fp32": torch.float32, "bf16": BF, "fp16": torch.float16}
+
+
+def _small_vs_serial(inp, monkeypatch, label, **kw):
+    o, S = run_chunk(inp, **kw)
+    check_parity(inp, o, S, label=label, qk_l2norm=kw.get("qk_l2norm", False))
+    monkeypatch.setenv("GDN_SMALL_CHUNKS", "0")
+    o1, S1 = run_chunk(inp, **kw)
+    monkeypatch.delenv("GDN_SMALL_CHUNKS")
+    rms = max(float(o1.float().pow(2).mean().sqrt()), 1e-6)
+    # a 16-bit o is rounded by each kernel on its own: one unit in the last
+    # place of the largest |o| on top of the tolerance
+    ulp = {BF: 2.0 ** -7, torch.float16: 2.0 ** -10}.get(o.dtype, 0.0) * float(o1.float().abs().max()) / rms
+    e_o = float((o.float() - o1.float()).abs().max()) / rms
+    e_s = float((S - S1).abs().max()) / rms if S is not None else 0.0
+    log(f"[16-token chunks vs token-serial] {label}: o {e_o:.3e} (ulp {ulp:.1e}) S {e_s:.3e}")
+    assert e_o <= TOL[inp.in_dtype] + ulp
+    assert e_s <= TOL[inp.in_dtype]
+
+
+@pytest.mark.parametrize("lens,H,dk,dv,dt,odt", SMALL_CASES, ids=lambda x: str(x))
+def test_small_chunks_parity(lens, H, dk, dv, dt, odt, monkeypatch):
+    assert sum(lens) <= SHORT_AVG * len(lens)
+    inp = W.packed_inputs(lens, H=H, dk=dk, dv=dv, in_dtype=dt, seed=60 + dk + dv, init_std=0.1,
+                          name=f"small chunks {lens} H{H} dk{dk} dv{dv} {dt}->{odt}")
+    _small_vs_serial(inp, monkeypatch, inp.name, out_dtype=_OUT[odt])
+
+
+@pytest.mark.parametrize("gate", ["-60", "-5", "0", "mixed", "beta2"])
+def test_small_chunks_gates(gate, monkeypatch):
+    """Decay extremes in 16-token chunks: every gate product inside a chunk is
+    taken relative to the chunk, so -60 per token underflows to zero without
+    overflowing anywhere; beta in (0, 2)."""
+    inp = W.packed_inputs([16, 9, 1, 14, 31], H=2, dk=128, dv=128, in_dtype="bf16", seed=61, init_std=0.1,
+                          name=f"small chunks gates {gate}")
+    if gate == "mixed":
+        inp.log_alpha[:] = -0.5
+        inp.log_alpha[:, ::3] = -60.0
+    elif gate == "beta2":
+        inp.beta[:] = np.random.default_rng(61).uniform(0.0, 2.0, size=inp.beta.shape).astype(np.float32)
+    else:
+        inp.log_alpha[:] = float(gate)
+    _small_vs_serial(inp, monkeypatch, inp.name)
+
+
+def test_small_chunks_batched_no_state(monkeypatch):
+    """Equal-length batch without cu_seqlens, zero initial state, final state
+    not returned; then L2-normalised q and k on a packed batch."""
+    inp = W.chunk_inputs(6, 10, 2, 64, 64, "bf16", seed=62, name="small chunks batched")
+    inp.init_state = None
+    _small_vs_serial(inp, monkeypatch, inp.name, init_override=None)
+    o, S = run_chunk(inp, init_override=None, final=False)
+    assert S is None
+    o_ref, _ = run_chunk(inp, init_override=None)
+    assert torch.equal(o, o_ref)
+    inp = W.packed_inputs([5, 11, 0, 16, 20], H=2, dk=128, dv=64, in_dtype="fp16", seed=63, init_std=0.1,
+                          name="small chunks l2norm")
+    inp.k[:, 3] = 0.0
+    _small_vs_serial(inp, monkeypatch, inp.name, qk_l2norm=True)
