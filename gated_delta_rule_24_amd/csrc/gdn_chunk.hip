@@ -1626,29 +1626,34 @@ static hipError_t allow_smem(K kernel, size_t bytes) {
 // M = T diag(beta), P = (Q K^T) o Gamma, and
 //   X_K = K S^T,  Y = V - diag(gamma) X_K,  V' = M Y,
 //   O   = diag(gamma) Q S^T + P V',  S^T <- gamma_C S^T + K^T (kappa o V').
-// One wave per (sequence, head, 16-column value slice): the wave holds its
-// slice of S^T (dk x 16 fp32, in matrix-core accumulators) through the
-// sequence's chunks, so the state is read and written once.  The waves are
-// independent (no block barrier): each loads the chunk's K and Q rows
-// straight into operand fragments (fp16, L2-normalised first when asked
-// for), forms the chunk's matrices itself and stages only K, for the
-// transposed reads of the state update, in its own LDS region.  A chunk's
-// global loads (K, Q, v, gates) are all issued before the first is used.
-// Per slice and chunk that is about 30 matrix instructions at dk = 128, so
-// the kernel is bound by its state traffic.  16-bit inputs, dk <= 128.
+// One block per (sequence, head), one wave per 16-column value slice (up to
+// kSmallMaxWaves; wider states run the block over the slices in groups): a
+// wave holds its slice of S^T (dk x 16 fp32, in matrix-core accumulators)
+// through the sequence's chunks, so the state is read and written once.
+// What does not depend on the slice is done once per chunk and shared
+// through LDS: all threads stage the chunk's K and Q rows as fp16 operands
+// (L2-normalised first when asked for), wave 0 scans the gates, and after a
+// barrier wave 0 forms G, Q K^T, A, T, M and P while every wave forms its
+// X_K and S Q^T; after a second barrier every wave finishes its slice.  The
+// shared buffers alternate by chunk parity, so a chunk needs no third
+// barrier before the next one overwrites them.  16-bit inputs, dk <= 128.
 // ============================================================================
-constexpr int kSmallC = 16;       // tokens per chunk
-constexpr int kSmallWaves = 4;    // waves (slices) per block
+constexpr int kSmallC = 16;          // tokens per chunk
+constexpr int kSmallMaxWaves = 16;   // value slices (waves) per block
 
 template <int DK>
 struct SmallSmem {
-    static constexpr int KROW = DK * 2 + 16;                              // bytes per staged K row (fp16)
-    static constexpr int NTP = 20;                                        // floats per N^T row
-    static constexpr size_t NT_OFF = 0;
-    static constexpr size_t VEC_OFF = NT_OFF + (size_t)kSmallC * NTP * 4;   // g log2 e, beta, gamma, kappa
-    static constexpr size_t K_OFF = VEC_OFF + 4 * kSmallC * 4;
-    static constexpr size_t WAVE = K_OFF + (size_t)kSmallC * KROW;
-    static constexpr size_t bytes = kSmallWaves * WAVE;
+    static constexpr int KROW = DK * 2 + 16;                        // bytes per staged K / Q row (fp16)
+    static constexpr int NTP = 20;                                  // floats per N^T row
+    static constexpr size_t KQ = (size_t)kSmallC * KROW;
+    // one chunk's shared operands (two sets, by chunk parity): K, Q, M in
+    // the A-operand layout and P in the B-operand layout (four fp16 per
+    // lane), gamma, kappa, g log2 e, beta per token and gamma_C
+    static constexpr size_t K_REL = 0, Q_REL = KQ, M_REL = 2 * KQ, P_REL = M_REL + 512, VEC_REL = P_REL + 512;
+    static constexpr size_t BUF = VEC_REL + (4 * kSmallC + 4) * 4;
+    static constexpr size_t NT_OFF = 2 * BUF;                       // wave 0's N^T (and its T row)
+    static constexpr size_t bytes = NT_OFF + (size_t)kSmallC * NTP * 4;
+    static_assert(KQ % 16 == 0 && BUF % 16 == 0, "16-byte aligned regions");
 };
 
 __device__ __forceinline__ float4_t mma16(half4_t a, half4_t b, float4_t acc) {
@@ -1666,15 +1671,30 @@ __device__ __forceinline__ float row16_scan(float x) {
     return x;
 }
 
+// Sum over aligned groups of RL lanes (RL = 4, 8 or 16) by DPP moves: swaps
+// within quads, then the mirrored lane of the half row and of the row.
+template <int RL>
+__device__ __forceinline__ float group_sum(float x) {
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));   // quad [1,0,3,2]
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));   // quad [2,3,0,1]
+    if constexpr (RL >= 8)
+        x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));   // half-row mirror
+    if constexpr (RL >= 16)
+        x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false));   // row mirror
+    return x;
+}
+
 template <typename in_t, typename out_t, int DK>
-__global__ __launch_bounds__(64 * kSmallWaves) __attribute__((amdgpu_waves_per_eu(4))) void chunk_small_kernel(
-    int N, int H, int DV, int T, int qk_norm, const int32_t *__restrict__ cu, int32_t *__restrict__ meta,
+__global__ __launch_bounds__(64 * kSmallMaxWaves) void chunk_small_kernel(
+    int N, int H, int DV, int T, int ng, int qk_norm, const int32_t *__restrict__ cu, int32_t *__restrict__ meta,
     const in_t *__restrict__ q, const in_t *__restrict__ k, const in_t *__restrict__ v,
     const float *__restrict__ log_alpha, const float *__restrict__ beta, const float *init_state,
     float *final_state, out_t *__restrict__ o) {
     using L = SmallSmem<DK>;
     using F2 = Frag2<_Float16>;
     constexpr int KROW = L::KROW, KT = DK / 16, KP = DK / 32;
+    constexpr int RL = DK / 8;          // staging lanes per K / Q row (8 elements each)
+    constexpr int PIECES = 4 * DK;      // 8-element pieces of the chunk's K and Q
     extern __shared__ __align__(16) unsigned char smem[];
     if (cu) {
         if (meta[1] != 0) return;   // cu_seqlens rejected by the table pass: write nothing
@@ -1682,204 +1702,218 @@ __global__ __launch_bounds__(64 * kSmallWaves) __attribute__((amdgpu_waves_per_e
         meta[0] = N * ((T + kChunk - 1) / kChunk);
         meta[1] = 0;
     }
+    // Block -> (sequence, head, first slice group); a block takes slice
+    // groups g, g + ng, ... of nwv slices each.
+    const int nwv = (int)(blockDim.x >> 6);
     const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-    const int ns = DV / 16;
-    const int64_t task = (int64_t)blockIdx.x * kSmallWaves + w;
-    if (task >= (int64_t)N * H * ns) return;
-    const int nh = (int)(task / ns), v0 = 16 * (int)(task % ns), n = nh / H, h = nh % H;
+    const int nh = blockIdx.x / ng, g0 = blockIdx.x % ng, n = nh / H, h = nh % H;
     const int tb = cu ? cu[n] : n * T, te = cu ? cu[n + 1] : (n + 1) * T;
-    unsigned char *wl = smem + w * L::WAVE;
-    float *NT = reinterpret_cast<float *>(wl + L::NT_OFF);
-    float *gv = reinterpret_cast<float *>(wl + L::VEC_OFF), *bv = gv + kSmallC, *gam = gv + 2 * kSmallC,
-          *kap = gv + 3 * kSmallC;
-    unsigned char *Kb = wl + L::K_OFF;
-    const int64_t rowq = (int64_t)H * DK;   // elements between tokens
+    const int ns = DV / 16;
+    float *NT = reinterpret_cast<float *>(smem + L::NT_OFF);
+    int par = 0;   // buffer parity, carried across slice groups
 
-    // S^T slice: tile 2p + hs, lane (n, j), element i = S^T[32p + 8j + 4hs + i][v0 + n]
-    float4_t sT[KT];
-    {
-        const int l = threadIdx.x & 63, nn = l & 15, jj = l >> 4;
-        const float *src = init_state + ((int64_t)nh * DV + v0 + nn) * DK + 8 * jj;
+    for (int s0 = g0 * nwv; s0 < ns; s0 += ng * nwv) {
+        const bool has = s0 + w < ns;   // this wave has a slice in the group
+        const int v0 = 16 * (s0 + w);
+        // S^T slice: tile 2p + hs, lane (n, j), element i = S^T[32p + 8j + 4hs + i][v0 + n]
+        float4_t sT[KT];
+        {
+            const int l = threadIdx.x & 63, nn = l & 15, jj = l >> 4;
+            const float *src = init_state + ((int64_t)nh * DV + v0 + nn) * DK + 8 * jj;
 #pragma unroll
-        for (int t = 0; t < KT; ++t)
-            sT[t] = init_state ? *reinterpret_cast<const float4_t *>(src + 32 * (t >> 1) + 4 * (t & 1))
-                               : float4_t{0.f, 0.f, 0.f, 0.f};
-    }
-    for (int t0 = tb; t0 < te; t0 += kSmallC) {
-        const int nt = min(kSmallC, te - t0);
-        // Lane-dependent values are formed anew in every chunk (the lane
-        // index is opaque to the compiler here), not hoisted out of the
-        // loop and held in registers across it.
-        int l = threadIdx.x & 63;
-        asm volatile("" : "+v"(l));
-        const int nn = l & 15, jj = l >> 4;
-
-        // ---- the chunk's loads: lane (n, j) takes row n (clamped to the
-        // chunk), dk 32p + 8j .. +7 of K and Q, token n's gates, and
-        // v[token 4j + i][v0 + n].  Indices are clamped, not branched on, so
-        // that every load is in flight before the first is waited for; the
-        // values of tokens past the end are replaced by zeros where used. ----
-        const int64_t th = (int64_t)t0 * H + h;
-        const int64_t rb = (th + (int64_t)min(nn, nt - 1) * H) * DK + 8 * jj;
-        const float la_in = log_alpha[th + (int64_t)min(nn, nt - 1) * H];
-        const float bt_in = beta[th + (int64_t)min(nn, nt - 1) * H];
-        const in_t *vp = v + th * DV + v0 + nn;
-        in_t vr[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) vr[i] = vp[(int64_t)min(4 * jj + i, nt - 1) * H * DV];
-        Raw8<in_t> kr[KP], qr[KP];
-#pragma unroll
-        for (int p = 0; p < KP; ++p) {
-            kr[p].load(k + rb + 32 * p);
-            qr[p].load(q + rb + 32 * p);
+            for (int t = 0; t < KT; ++t)
+                sT[t] = has && init_state ? *reinterpret_cast<const float4_t *>(src + 32 * (t >> 1) + 4 * (t & 1))
+                                          : float4_t{0.f, 0.f, 0.f, 0.f};
         }
-        __builtin_amdgcn_sched_barrier(0);   // all of them issued before any is used
+        for (int t0 = tb; t0 < te; t0 += kSmallC, par ^= 1) {
+            const int nt = min(kSmallC, te - t0);
+            // Lane-dependent values are formed anew in every chunk (the lane
+            // index is opaque to the compiler here), not hoisted out of the
+            // loop and held in registers across it.
+            int tid = threadIdx.x;
+            asm volatile("" : "+v"(tid));
+            const int l = tid & 63, nn = l & 15, jj = l >> 4;
+            unsigned char *buf = smem + par * L::BUF;
+            unsigned char *Kb = buf + L::K_REL, *Qb = buf + L::Q_REL;
+            float *gam = reinterpret_cast<float *>(buf + L::VEC_REL), *kap = gam + kSmallC,
+                  *gl2 = gam + 2 * kSmallC, *bv = gam + 3 * kSmallC, *gCp = gam + 4 * kSmallC;
+            const int64_t th = (int64_t)t0 * H + h;
 
-        // ---- K and Q operand fragments (rows past the end are zero); K to LDS ----
-        float rk = 1.f, rq = 1.f;
-        if (qk_norm) {   // the four lanes n, n + 16, n + 32, n + 48 hold row n
-            float sk = 0.f, sq = 0.f;
+            // ---- phase A: loads (indices clamped to the chunk, not branched
+            // on, so they are all in flight together; values of tokens past
+            // the end are replaced where they are used) ----
+            float la_in = 0.f, bt_in = 0.f;
+            if (w == 0) {
+                la_in = log_alpha[th + (int64_t)min(nn, nt - 1) * H];
+                bt_in = beta[th + (int64_t)min(nn, nt - 1) * H];
+            }
+            in_t vr[4];
+            if (has) {
+                const in_t *vp = v + th * DV + v0 + nn;
 #pragma unroll
-            for (int p = 0; p < KP; ++p) {
-                float f[8], g8[8];
-                kr[p].to_f32(f);
-                qr[p].to_f32(g8);
+                for (int i = 0; i < 4; ++i) vr[i] = vp[(int64_t)min(4 * jj + i, nt - 1) * H * DV];
+            }
+            // K and Q rows as fp16 operands.  Rows past the end (copies of
+            // the last row) need no zeroing: their beta is 0, so their rows
+            // of A and T are e_n, their rows of Y and V' are 0 and they add
+            // nothing to the state; their outputs are not stored.
+            for (int p = tid; p < PIECES; p += 64 * nwv) {
+                const int mat = p / (2 * DK), rem = p - mat * 2 * DK, r = rem / RL, c8 = rem - r * RL;
+                Raw8<in_t> raw;
+                raw.load((mat ? q : k) + (th + (int64_t)min(r, nt - 1) * H) * DK + 8 * c8);
+                float f[8];
+                raw.to_f32(f);
+                float sc = 1.f;
+                if (qk_norm) {
+                    float ss = 0.f;
 #pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    sk += f[u] * f[u];
-                    sq += g8[u] * g8[u];
+                    for (int u = 0; u < 8; ++u) ss += f[u] * f[u];
+                    ss = group_sum<RL>(ss);
+                    sc = ss > 0.f ? rsqrtf(ss) : 0.f;
+                }
+                half8_t hv;
+#pragma unroll
+                for (int u = 0; u < 8; ++u) hv[u] = (_Float16)(f[u] * sc);
+                *reinterpret_cast<half8_t *>((mat ? Qb : Kb) + r * KROW + 16 * c8) = hv;
+            }
+            if (w == 0) {   // gates: token n of the chunk in every row of 16 lanes
+                const float bt = nn < nt ? bt_in : 0.f;
+                const float g = row16_scan(nn < nt ? la_in : 0.f);
+                const float g_last = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(g), 15));
+                if (jj == 0) {
+                    gam[nn] = expf(g);
+                    kap[nn] = expf(g_last - g);
+                    gl2[nn] = g * kLog2e;
+                    bv[nn] = bt;
+                    if (nn == 0) gCp[0] = expf(g_last);
                 }
             }
-            const int a16 = (l ^ 16) << 2, a32 = (l ^ 32) << 2;
-            sk += __int_as_float(__builtin_amdgcn_ds_bpermute(a16, __float_as_int(sk)));
-            sq += __int_as_float(__builtin_amdgcn_ds_bpermute(a16, __float_as_int(sq)));
-            sk += __int_as_float(__builtin_amdgcn_ds_bpermute(a32, __float_as_int(sk)));
-            sq += __int_as_float(__builtin_amdgcn_ds_bpermute(a32, __float_as_int(sq)));
-            rk = sk > 0.f ? rsqrtf(sk) : 0.f;
-            rq = sq > 0.f ? rsqrtf(sq) : 0.f;
-        }
-        // Rows past the end (copies of the last row) need no zeroing: their
-        // beta is 0, so row n of A and of T is e_n there, their rows of Y
-        // and V' are 0 and they add nothing to the state; their outputs are
-        // not stored.
-        F2 kf[KP], qf[KP];
-#pragma unroll
-        for (int p = 0; p < KP; ++p) {
-            float f[8], g8[8];
-            kr[p].to_f32(f);
-            qr[p].to_f32(g8);
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                kf[p].v[u] = (_Float16)(f[u] * rk);
-                qf[p].v[u] = (_Float16)(g8[u] * rq);
-            }
-            *reinterpret_cast<half8_t *>(Kb + nn * KROW + 2 * (32 * p + 8 * jj)) = kf[p].v;
-        }
+            __syncthreads();
 
-        // ---- gates: token n of the chunk in every row of 16 lanes ----
-        const float bt = nn < nt ? bt_in : 0.f;
-        const float g = row16_scan(nn < nt ? la_in : 0.f);
-        const float g_last = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(g), 15));   // same in every row
-        if (jj == 0) {
-            gv[nn] = g * kLog2e;
-            bv[nn] = bt;
-            gam[nn] = expf(g);
-            kap[nn] = expf(g_last - g);
-        }
-        const float gC = expf(g_last);
+            // ---- phase B: products of every slice with S; wave 0 also forms
+            // the chunk's shared matrices (lane (n, j) holds rows 4j .. 4j + 3,
+            // column n of each product) ----
+            F2 kf[KP], qf[KP];
+#pragma unroll
+            for (int p = 0; p < KP; ++p) {
+                kf[p] = row_frag2(reinterpret_cast<const _Float16 *>(Kb + nn * KROW + 16 * jj + 64 * p));
+                qf[p] = row_frag2(reinterpret_cast<const _Float16 *>(Qb + nn * KROW + 16 * jj + 64 * p));
+            }
+            float4_t X = {0.f, 0.f, 0.f, 0.f}, QS = X;
+            if (has) {
+#pragma unroll
+                for (int p = 0; p < KP; ++p) {
+                    const F2 sB = F2::cvt(sT[2 * p], sT[2 * p + 1]);
+                    mma2(X, kf[p], sB);    // X_K[4j + i][v0 + n]
+                    mma2(QS, sB, qf[p]);   // (S Q^T)[v0 + 4j + i][n]
+                }
+            }
+            if (w == 0) {
+                float4_t G = {0.f, 0.f, 0.f, 0.f}, PK = G;
+#pragma unroll
+                for (int p = 0; p < KP; ++p) {
+                    mma2(G, kf[p], kf[p]);    // k_{4j+i} . k_n (symmetric)
+                    mma2(PK, kf[p], qf[p]);   // k_{4j+i} . q_n = (Q K^T)[n][4j + i]
+                }
+                const float gn = gl2[nn], bn = bv[nn];
+                const float4_t gc = *reinterpret_cast<const float4_t *>(gl2 + 4 * jj);
+                float4_t Pr;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int c = 4 * jj + i;
+                    const float e = c <= nn ? exp2_neg(gn - gc[i]) : 0.f;
+                    Pr[i] = e * PK[i];
+                    NT[c * L::NTP + nn] = c < nn ? bn * e * G[i] : 0.f;   // N^T[c][n] = A[n][c]
+                }
+                __builtin_amdgcn_wave_barrier();
+                // row n of T = (I + A)^{-1}: x (I + A) = e_n, c = 15 .. 0 (row c
+                // of N^T read as float4 broadcasts)
+                float x[16];
+#pragma unroll
+                for (int c = 15; c >= 0; --c) {
+                    float acc = 0.f;
+#pragma unroll
+                    for (int q4 = (c + 1) / 4; q4 < 4; ++q4) {
+                        const float4_t r = *reinterpret_cast<const float4_t *>(NT + c * L::NTP + 4 * q4);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            if (4 * q4 + i > c) acc -= x[4 * q4 + i] * r[i];
+                    }
+                    x[c] = c == nn ? 1.f : acc;
+                }
+                // the row goes through LDS (over N^T, whose reads are done) so
+                // that lane (n, j) can take its four entries 4j .. 4j + 3
+                __builtin_amdgcn_wave_barrier();
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4)
+                    *reinterpret_cast<float4_t *>(NT + nn * L::NTP + 4 * q4) =
+                        float4_t{x[4 * q4], x[4 * q4 + 1], x[4 * q4 + 2], x[4 * q4 + 3]};
+                __builtin_amdgcn_wave_barrier();
+                const float4_t bc = *reinterpret_cast<const float4_t *>(bv + 4 * jj);
+                const float4_t Mr = *reinterpret_cast<const float4_t *>(NT + nn * L::NTP + 4 * jj) * bc;   // M = T diag(beta)
+                *reinterpret_cast<half4_t *>(buf + L::M_REL + 8 * l) = to_half4(Mr);
+                *reinterpret_cast<half4_t *>(buf + L::P_REL + 8 * l) = to_half4(Pr);
+            }
+            __syncthreads();
 
-        // ---- products (lane (n, j) holds rows 4j .. 4j + 3, column n) ----
-        float4_t G = {0.f, 0.f, 0.f, 0.f}, PK = G, X = G, QS = G;
+            // ---- phase C: the slice's V', output rows and state update ----
+            if (has) {
+                const half4_t Mh = *reinterpret_cast<const half4_t *>(buf + L::M_REL + 8 * l);
+                const half4_t Ph = *reinterpret_cast<const half4_t *>(buf + L::P_REL + 8 * l);
+                const float4_t gm = *reinterpret_cast<const float4_t *>(gam + 4 * jj);
+                float4_t y;
 #pragma unroll
-        for (int p = 0; p < KP; ++p) {
-            mma2(G, kf[p], kf[p]);    // k_{4j+i} . k_n (symmetric)
-            mma2(PK, kf[p], qf[p]);   // k_{4j+i} . q_n = (Q K^T)[n][4j + i]
-        }
+                for (int i = 0; i < 4; ++i) y[i] = 4 * jj + i < nt ? to_f32(vr[i]) - gm[i] * X[i] : 0.f;
+                const float4_t Vp = mma16(Mh, to_half4(y), float4_t{0.f, 0.f, 0.f, 0.f});   // V' = M Y
+                // O^T = (S Q^T) diag(gamma) + V'^T P^T: lane (n, j) holds O[token n][v0 + 4j + i]
+                const float4_t pv = mma16(to_half4(Vp), Ph, float4_t{0.f, 0.f, 0.f, 0.f});
+                const float4_t oo = QS * gam[nn] + pv;
+                if (nn < nt) {
+                    out_t *dst = o + (th + (int64_t)nn * H) * DV + v0 + 4 * jj;
+                    if constexpr (sizeof(out_t) == 4) {
+                        *reinterpret_cast<float4_t *>(dst) = oo;
+                    } else if constexpr (std::is_same<out_t, bf16_t>::value) {
+                        *reinterpret_cast<uint2 *>(dst) = make_uint2(pack_bf16x2(oo[0], oo[1]), pack_bf16x2(oo[2], oo[3]));
+                    } else {
+                        *reinterpret_cast<half4_t *>(dst) = to_half4(oo);
+                    }
+                }
+                // S^T <- gamma_C S^T + K^T (kappa o V')
+                const float gC = gCp[0];
+                const float4_t kp = *reinterpret_cast<const float4_t *>(kap + 4 * jj);
+                const half4_t dh = to_half4(kp * Vp);
+                const unsigned char *kt = Kb + (4 * jj + (nn >> 2)) * KROW + 16 * (nn & 3);   // transposed K reads
 #pragma unroll
-        for (int p = 0; p < KP; ++p) {
-            const F2 sB = F2::cvt(sT[2 * p], sT[2 * p + 1]);
-            mma2(X, kf[p], sB);    // X_K[4j + i][v0 + n]
-            mma2(QS, sB, qf[p]);   // (S Q^T)[v0 + 4j + i][n]
-        }
-        __builtin_amdgcn_wave_barrier();   // the gate and K writes above before the reads below
-        const float gn = gv[nn], bn = bv[nn];
-        const float4_t gc = *reinterpret_cast<const float4_t *>(gv + 4 * jj);
-        float4_t Pr;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int c = 4 * jj + i;
-            const float e = c <= nn ? exp2_neg(gn - gc[i]) : 0.f;
-            Pr[i] = e * PK[i];
-            NT[c * L::NTP + nn] = c < nn ? bn * e * G[i] : 0.f;   // N^T[c][n] = A[n][c]
-        }
-        __builtin_amdgcn_wave_barrier();
-        // row n of T = (I + A)^{-1}: x (I + A) = e_n, c = 15 .. 0 (row c of
-        // N^T read as float4 broadcasts)
-        float x[16];
-#pragma unroll
-        for (int c = 15; c >= 0; --c) {
-            float acc = 0.f;
-#pragma unroll
-            for (int q4 = (c + 1) / 4; q4 < 4; ++q4) {
-                const float4_t r = *reinterpret_cast<const float4_t *>(NT + c * L::NTP + 4 * q4);
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (4 * q4 + i > c) acc -= x[4 * q4 + i] * r[i];
-            }
-            x[c] = c == nn ? 1.f : acc;
-        }
-        // the row goes through LDS (over N^T, whose reads are done) so that
-        // lane (n, j) can take its four entries 4j .. 4j + 3
-        __builtin_amdgcn_wave_barrier();
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-            *reinterpret_cast<float4_t *>(NT + nn * L::NTP + 4 * q4) =
-                float4_t{x[4 * q4], x[4 * q4 + 1], x[4 * q4 + 2], x[4 * q4 + 3]};
-        __builtin_amdgcn_wave_barrier();
-        const float4_t bc = *reinterpret_cast<const float4_t *>(bv + 4 * jj);
-        const float4_t Mr = *reinterpret_cast<const float4_t *>(NT + nn * L::NTP + 4 * jj) * bc;   // M = T diag(beta)
-        const float4_t gm = *reinterpret_cast<const float4_t *>(gam + 4 * jj);
-        float4_t y;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) y[i] = 4 * jj + i < nt ? to_f32(vr[i]) - gm[i] * X[i] : 0.f;
-        const float4_t Vp = mma16(to_half4(Mr), to_half4(y), float4_t{0.f, 0.f, 0.f, 0.f});   // V' = M Y
-        // O^T = (S Q^T) diag(gamma) + V'^T P^T: lane (n, j) holds O[token n][v0 + 4j + i]
-        const float4_t pv = mma16(to_half4(Vp), to_half4(Pr), float4_t{0.f, 0.f, 0.f, 0.f});
-        const float4_t oo = QS * gam[nn] + pv;
-        if (nn < nt) {
-            out_t *dst = o + (th + (int64_t)nn * H) * DV + v0 + 4 * jj;
-            if constexpr (sizeof(out_t) == 4) {
-                *reinterpret_cast<float4_t *>(dst) = oo;
-            } else if constexpr (std::is_same<out_t, bf16_t>::value) {
-                *reinterpret_cast<uint2 *>(dst) = make_uint2(pack_bf16x2(oo[0], oo[1]), pack_bf16x2(oo[2], oo[3]));
-            } else {
-                *reinterpret_cast<half4_t *>(dst) = to_half4(oo);
+                for (int t = 0; t < KT; ++t) {
+                    const half4_t a = __builtin_bit_cast(half4_t, lds_read_tr16(kt + 2 * (32 * (t >> 1) + 4 * (t & 1))));
+                    sT[t] = mma16(a, dh, sT[t] * gC);
+                }
             }
         }
-        // S^T <- gamma_C S^T + K^T (kappa o V')
-        const float4_t kp = *reinterpret_cast<const float4_t *>(kap + 4 * jj);
-        const half4_t dh = to_half4(kp * Vp);
-        const unsigned char *kt = Kb + (4 * jj + (nn >> 2)) * KROW + 16 * (nn & 3);   // transposed K reads
+        if (has && final_state) {
+            const int l = threadIdx.x & 63, nn = l & 15, jj = l >> 4;
+            float *dst = final_state + ((int64_t)nh * DV + v0 + nn) * DK + 8 * jj;
 #pragma unroll
-        for (int t = 0; t < KT; ++t) {
-            const half4_t a = __builtin_bit_cast(half4_t, lds_read_tr16(kt + 2 * (32 * (t >> 1) + 4 * (t & 1))));
-            sT[t] = mma16(a, dh, sT[t] * gC);
+            for (int t = 0; t < KT; ++t)
+                *reinterpret_cast<float4_t *>(dst + 32 * (t >> 1) + 4 * (t & 1)) = sT[t];
         }
-        __builtin_amdgcn_wave_barrier();   // this chunk's LDS reads before the next chunk's writes
     }
-    if (final_state) {
-        const int l = threadIdx.x & 63, nn = l & 15, jj = l >> 4;
-        float *dst = final_state + ((int64_t)nh * DV + v0 + nn) * DK + 8 * jj;
-#pragma unroll
-        for (int t = 0; t < KT; ++t)
-            *reinterpret_cast<float4_t *>(dst + 32 * (t >> 1) + 4 * (t & 1)) = sT[t];
-    }
+}
+
+// Waves (value slices) per G6 block; GDN_SMALL_WAVES overrides, for experiments.
+static int small_waves(const ChunkArgs &a) {
+    const int ns = a.dv / 16;
+    int waves = min(ns, kSmallMaxWaves);
+    const char *env = getenv("GDN_SMALL_WAVES");
+    if (env && atoi(env) >= 1 && atoi(env) <= kSmallMaxWaves) waves = min(ns, atoi(env));
+    return waves;
 }
 
 template <typename in_t, typename out_t>
 static hipError_t launch_small_out(const ChunkArgs &a, int32_t *meta, hipStream_t st) {
-    const int64_t tasks = (int64_t)a.N * a.H * (a.dv / 16);
-    const dim3 grid((unsigned)((tasks + kSmallWaves - 1) / kSmallWaves)), block(64 * kSmallWaves);
+    const int ns = a.dv / 16, waves = small_waves(a);
+    const int ng = (ns + waves - 1) / waves;   // blocks per (sequence, head)
+    const dim3 grid((unsigned)((int64_t)a.N * a.H * ng)), block(64 * waves);
     auto *q = static_cast<const in_t *>(a.q);
     auto *k = static_cast<const in_t *>(a.k);
     auto *v = static_cast<const in_t *>(a.v);
@@ -1889,15 +1923,18 @@ static hipError_t launch_small_out(const ChunkArgs &a, int32_t *meta, hipStream_
     switch (a.dk) {
     case 32:
         chunk_small_kernel<in_t, out_t, 32><<<grid, block, SmallSmem<32>::bytes, st>>>(
-            a.N, a.H, a.dv, a.T, qn, a.cu_seqlens, meta, q, k, v, a.log_alpha, a.beta, a.init_state, a.final_state, o);
+            a.N, a.H, a.dv, a.T, ng, qn, a.cu_seqlens, meta, q, k, v, a.log_alpha, a.beta, a.init_state,
+            a.final_state, o);
         break;
     case 64:
         chunk_small_kernel<in_t, out_t, 64><<<grid, block, SmallSmem<64>::bytes, st>>>(
-            a.N, a.H, a.dv, a.T, qn, a.cu_seqlens, meta, q, k, v, a.log_alpha, a.beta, a.init_state, a.final_state, o);
+            a.N, a.H, a.dv, a.T, ng, qn, a.cu_seqlens, meta, q, k, v, a.log_alpha, a.beta, a.init_state,
+            a.final_state, o);
         break;
     case 128:
         chunk_small_kernel<in_t, out_t, 128><<<grid, block, SmallSmem<128>::bytes, st>>>(
-            a.N, a.H, a.dv, a.T, qn, a.cu_seqlens, meta, q, k, v, a.log_alpha, a.beta, a.init_state, a.final_state, o);
+            a.N, a.H, a.dv, a.T, ng, qn, a.cu_seqlens, meta, q, k, v, a.log_alpha, a.beta, a.init_state,
+            a.final_state, o);
         break;
     default:
         return hipErrorInvalidValue;
@@ -2044,9 +2081,9 @@ hipError_t launch_chunk_fwd(const ChunkArgs &a, hipStream_t st) {
                                           reinterpret_cast<int32_t *>(ws + w.off_segtab), st);
         if (e != hipSuccess) return e;
     }
-    // Few tokens per sequence (e.g. appending to resident states): the
-    // token-serial kernel reads and writes each state once and skips the
-    // chunk intermediates.
+    // Few tokens per sequence (e.g. appending to resident states): one kernel
+    // reads and writes each state once and no chunk intermediates are formed
+    // (G6, or the token-serial G5).
     if ((int64_t)a.B * a.T <= (int64_t)kShortAvg * a.N) {
         int32_t *meta = reinterpret_cast<int32_t *>(ws + w.off_meta);
         return use_chunk_small(a) ? launch_chunk_small(a, meta, st) : launch_chunk_short(a, meta, st);

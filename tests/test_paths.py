@@ -162,15 +162,17 @@ def test_in_place_state_continuation():
     assert torch.equal(o_a, o_b) and torch.equal(S_a, S_inplace)
 
 
+@pytest.mark.parametrize("dt", ["bf16", "fp32"])   # checked by G6 itself / by the table pass before G5
 @pytest.mark.parametrize("cu,code", [([0, 10, 5, 20], 2), ([1, 10, 20], 1), ([0, 10, 19], 3)])
-def test_malformed_cu_seqlens_reported(cu, code):
+def test_malformed_cu_seqlens_reported(cu, code, dt):
     T = 20
-    inp = W.chunk_inputs(1, T, 2, 64, 32, "bf16", seed=38)
+    inp = W.chunk_inputs(1, T, 2, 64, 32, dt, seed=38)
     q, k, v, la, b = _dev_inputs(inp)
     o = torch.full((1, T, 2, 32), 7.0, device="cuda")
     N = len(cu) - 1
     fin = torch.full((N, 2, 32, 64), 3.0, device="cuda")
-    ws = torch.empty(gdn.chunk_fwd_workspace_size(1, T, 2, 64, 32, N), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(gdn.chunk_fwd_workspace_size(1, T, 2, 64, 32, N, in_dtype=q.dtype), dtype=torch.uint8,
+                     device="cuda")
     gdn.chunk_fwd(q, k, v, la, b, cu_seqlens=dev(np.array(cu), torch.int32), o=o, final_state=fin, workspace=ws)
     assert gdn.chunk_fwd_check(ws) == code
     assert bool((o == 7.0).all()) and bool((fin == 3.0).all())    # nothing written
@@ -310,6 +312,7 @@ SMALL_CASES = [
     ([4, 4, 4, 4], 3, 32, 96, "fp16", "fp16"),
     ([40, 0, 0, 1], 2, 64, 48, "fp16", "fp32"),
     ([2, 2], 2, 128, 16, "bf16", "fp32"),
+    ([5, 12, 3, 0, 20], 2, 64, 320, "bf16", "fp32"),   # 20 value slices: two groups of waves
 ]
 _OUT = {"fp32": torch.float32, "bf16": BF, "fp16": torch.float16}
 
