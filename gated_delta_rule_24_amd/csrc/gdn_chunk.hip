@@ -130,7 +130,7 @@ __global__ __launch_bounds__(256) void chunk_table_kernel(int N, int T, const in
                                                           int32_t *__restrict__ row_len, int seg_chunks,
                                                           int32_t *__restrict__ seg_first,
                                                           int32_t *__restrict__ seg_cnt,
-                                                          int32_t *__restrict__ seg_tab) {
+                                                          int32_t *__restrict__ seg_tab, int tables) {
     __shared__ int s_code;
     __shared__ int s_scan[256];
     __shared__ int s_offset;
@@ -150,6 +150,14 @@ __global__ __launch_bounds__(256) void chunk_table_kernel(int N, int T, const in
         if (tid == 0) {
             meta[0] = 0;
             meta[1] = (code & 1) ? 1 : ((code & 2) ? 2 : 3);
+            meta[2] = 0;
+        }
+        return;
+    }
+    if (!tables) {   // the call's kernels need only the check
+        if (tid == 0) {
+            meta[0] = 0;
+            meta[1] = 0;
             meta[2] = 0;
         }
         return;
@@ -2059,10 +2067,11 @@ static hipError_t launch_typed(const ChunkArgs &a, const ChunkWorkspace &w, hipS
 
 hipError_t launch_chunk_table(int32_t N, int32_t T, const int32_t *cu_seqlens, int32_t *meta, int32_t *cu_ws,
                               int32_t *row0, int32_t *row_tok, int32_t *row_len, int32_t seg_chunks,
-                              int32_t *seg_first, int32_t *seg_cnt, int32_t *seg_tab, hipStream_t st) {
+                              int32_t *seg_first, int32_t *seg_cnt, int32_t *seg_tab, hipStream_t st,
+                              bool tables) {
     ProfScope prof("gdn_chunk_table", st);
     chunk_table_kernel<<<1, 256, 0, st>>>(N, T, cu_seqlens, meta, cu_ws, row0, row_tok, row_len, seg_chunks,
-                                          seg_first, seg_cnt, seg_tab);
+                                          seg_first, seg_cnt, seg_tab, tables ? 1 : 0);
     return hipGetLastError();
 }
 
@@ -2070,6 +2079,7 @@ hipError_t launch_chunk_fwd(const ChunkArgs &a, hipStream_t st) {
     const bool packed = a.cu_seqlens != nullptr;
     const ChunkWorkspace w = chunk_workspace_layout(a.B, a.T, a.N, packed, a.H, a.in_dtype, a.dk, a.dv);
     char *ws = static_cast<char *>(a.workspace);
+    const bool short_call = (int64_t)a.B * a.T <= (int64_t)kShortAvg * a.N;
     if (packed) {
         hipError_t e = launch_chunk_table(a.N, a.T, a.cu_seqlens, reinterpret_cast<int32_t *>(ws + w.off_meta),
                                           reinterpret_cast<int32_t *>(ws + w.off_cu),
@@ -2078,13 +2088,13 @@ hipError_t launch_chunk_fwd(const ChunkArgs &a, hipStream_t st) {
                                           reinterpret_cast<int32_t *>(ws + w.off_rowlen), w.seg_chunks,
                                           reinterpret_cast<int32_t *>(ws + w.off_segfirst),
                                           reinterpret_cast<int32_t *>(ws + w.off_segcnt),
-                                          reinterpret_cast<int32_t *>(ws + w.off_segtab), st);
+                                          reinterpret_cast<int32_t *>(ws + w.off_segtab), st, !short_call);
         if (e != hipSuccess) return e;
     }
     // Few tokens per sequence (e.g. appending to resident states): one kernel
     // reads and writes each state once and no chunk intermediates are formed
     // (G6, or the token-serial G5).
-    if ((int64_t)a.B * a.T <= (int64_t)kShortAvg * a.N) {
+    if (short_call) {   // (the table pass above only checked cu_seqlens)
         int32_t *meta = reinterpret_cast<int32_t *>(ws + w.off_meta);
         return use_chunk_small(a) ? launch_chunk_small(a, meta, st) : launch_chunk_short(a, meta, st);
     }

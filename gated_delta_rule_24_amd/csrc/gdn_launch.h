@@ -97,7 +97,8 @@ hipError_t launch_chunk_bwd(const ChunkArgs &a, const BwdArgs &g, hipStream_t st
 // meta[2] = the number of units.
 hipError_t launch_chunk_table(int32_t N, int32_t T, const int32_t *cu_seqlens, int32_t *meta, int32_t *cu_ws,
                               int32_t *row0, int32_t *row_tok, int32_t *row_len, int32_t seg_chunks,
-                              int32_t *seg_first, int32_t *seg_cnt, int32_t *seg_tab, hipStream_t stream);
+                              int32_t *seg_first, int32_t *seg_cnt, int32_t *seg_tab, hipStream_t stream,
+                              bool tables = true);   // false: only check cu_seqlens and set meta
 
 // Host-side launch timing (see gdn_profile_* in gdn.h).  While profiling is
 // enabled the scope records a HIP event pair around the launches it covers.
