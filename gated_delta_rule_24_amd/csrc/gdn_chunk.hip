@@ -1119,34 +1119,47 @@ __global__ __launch_bounds__((64 * StateSmem<in_t, OP, DK, NW, OUT>::WAVES)) voi
 
     // The two roles run separate loops with the same barriers: one per chunk
     // (two with a single Q/K buffer).  Before a barrier a stager waits for
-    // its direct loads, Q/K register loads and LDS writes; a compute wave
+    // its direct loads, Q/K register loads (in the output pass all but the
+    // newest chunk's) and LDS writes; a compute wave
     // waits only for its LDS reads, never for its output stores, which drain
     // in the background.  After the barrier the staged chunk is visible and
     // every wave is done with chunk ci-1's buffers.  The barriers are written
     // out (rather than __syncthreads) so that no wait for outstanding global
     // stores is attached to them.
     //
-    // Stager step ci (QKB == 2): load chunk ci+2's Q and K into `nxt` and
-    // copy chunk ci+1's V, M, P and decay factors first, so the loads have
-    // the whole chunk to land, then commit chunk ci+1's Q and K from `cur`
-    // (complete since the barrier's wait; `touch` keeps the compiler from
-    // waiting again behind the new loads).  With a single Q/K buffer
-    // (QKB == 1) chunk ci is committed between the two barriers.
+    // Stager step ci (QKB == 2): issue chunk ci+2's Q and K loads into `nxt`
+    // and copy chunk ci+1's V, M, P and decay factors, then commit chunk
+    // ci+1's Q and K from `cur` (the order differs between the passes, see
+    // below).  With a single Q/K buffer (QKB == 1) chunk ci is committed
+    // between the two barriers.
     auto stage = [&](int ci, QKRegs &cur, QKRegs &nxt) {
         const int b = ci & 1;
-        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        if constexpr (QKB == 2 && OUT)   // all but this wave's newest Q/K prefetch (below)
+            asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * QK_IT) : "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
         if constexpr (QKB == 1) {
             if (ci > 0) commit_qk(0, min(C, len_seq - ci * C), cur);
             asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
         }
-        if constexpr (QKB == 2) {
-#pragma unroll
-            for (int it = 0; it < QK_IT; ++it) {
-                if constexpr (OUT) cur.q[it].touch();
-                cur.k[it].touch();
-            }
+        if constexpr (QKB == 2 && OUT) {
+            // Output pass: chunk ci+1's copies first, then chunk ci+2's Q and K,
+            // then chunk ci+1's Q and K committed from `cur` (the compiler's
+            // wait for `cur` also covers the copies, which are older than the
+            // new Q/K loads).  The next barrier waits for everything but those
+            // Q/K loads, so they have two chunk steps to land.
             // (near the end the last chunk is loaded again: the register
             // sets are then written on every path, which keeps them in place)
+            if (ci + 1 < nchunks) dma(ci + 1, b ^ 1);
+            prefetch_qk(min(ci + 2, nchunks - 1), nxt);
+            if (ci + 1 < nchunks) commit_qk(b ^ 1, min(C, len_seq - (ci + 1) * C), cur);
+        } else if constexpr (QKB == 2) {
+            // Transition pass: chunk ci+2's K loads and chunk ci+1's copies,
+            // then chunk ci+1's K committed from `cur` (complete since the
+            // barrier's wait; `touch` keeps the compiler from waiting again
+            // behind the new loads).
+#pragma unroll
+            for (int it = 0; it < QK_IT; ++it) cur.k[it].touch();
             prefetch_qk(min(ci + 2, nchunks - 1), nxt);
             if (ci + 1 < nchunks) {
                 dma(ci + 1, b ^ 1);
