@@ -373,3 +373,15 @@ def test_small_chunks_batched_no_state(monkeypatch):
                           name="small chunks l2norm")
     inp.k[:, 3] = 0.0
     _small_vs_serial(inp, monkeypatch, inp.name, qk_l2norm=True)
+
+
+@pytest.mark.parametrize("dk", [32, 64])
+def test_small_chunks_l2norm_narrow_keys(dk, monkeypatch):
+    """q/k L2 normalisation in 16-token chunks when a key row spans 4 or 8
+    staging lanes (the row sums take fewer lane exchanges than at dk = 128)."""
+    inp = W.packed_inputs([7, 16, 3, 0, 21], H=3, dk=dk, dv=48, in_dtype="bf16", seed=64 + dk, init_std=0.1,
+                          name=f"small chunks l2norm dk{dk}")
+    inp.q[:] = inp.q * 2.0        # not unit rows (scaled exactly): the normalisation must act
+    inp.k[:] = inp.k * 0.5
+    inp.k[:, 5] = 0.0
+    _small_vs_serial(inp, monkeypatch, inp.name, qk_l2norm=True)
