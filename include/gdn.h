@@ -199,9 +199,10 @@ gdn_status gdn_chunk_fwd_workspace_size(const gdn_chunk_desc *desc, size_t *byte
  * written once by one kernel: for 16-bit inputs with dk <= 128 the same
  * chunkwise algorithm with 16-token chunks on the matrix cores, else the
  * recurrence itself token by token; either is cheaper for a few tokens per
- * sequence.  All compute eq. (10) with fp32 state and accumulation and meet
- * the same bounds; bit-identical results are guaranteed between calls that
- * take the same branch.
+ * sequence.  The environment variable GDN_SMALL_CHUNKS=0, read at every
+ * call, sends such calls to the token-by-token kernel.  All compute eq. (10)
+ * with fp32 state and accumulation and meet the same bounds; bit-identical
+ * results are guaranteed between calls that take the same branch.
  *
  * o must not overlap any input or the state buffers (GDN_ERR_ALIAS).
  * Errors: GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_DTYPE, GDN_ERR_ALIGN,
