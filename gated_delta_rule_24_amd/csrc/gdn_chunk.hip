@@ -1705,7 +1705,7 @@ __device__ __forceinline__ float group_sum(float x) {
     return x;
 }
 
-template <typename in_t, typename out_t, int DK>
+template <typename in_t, typename out_t, int DK, bool INIT>
 __global__ __launch_bounds__(64 * kSmallMaxWaves) void chunk_small_kernel(
     int N, int H, int DV, int T, int ng, int qk_norm, const int32_t *__restrict__ cu, int32_t *__restrict__ meta,
     const in_t *__restrict__ q, const in_t *__restrict__ k, const in_t *__restrict__ v,
@@ -1736,17 +1736,30 @@ __global__ __launch_bounds__(64 * kSmallMaxWaves) void chunk_small_kernel(
     for (int s0 = g0 * nwv; s0 < ns; s0 += ng * nwv) {
         const bool has = s0 + w < ns;   // this wave has a slice in the group
         const int v0 = 16 * (s0 + w);
-        // S^T slice: tile 2p + hs, lane (n, j), element i = S^T[32p + 8j + 4hs + i][v0 + n]
+        // S^T slice: tile 2p + hs, lane (n, j), element i = S^T[32p + 8j + 4hs + i][v0 + n].
+        // Its loads go out in the first chunk after the chunk's K and Q loads,
+        // so the staging, the gate scan and wave 0's matrices proceed while
+        // they are in flight (loads complete in issue order); only the
+        // products with S wait for them.
         float4_t sT[KT];
-        {
-            const int l = threadIdx.x & 63, nn = l & 15, jj = l >> 4;
-            const float *src = init_state + ((int64_t)nh * DV + v0 + nn) * DK + 8 * jj;
+        // (No branch around the loads, which would make the compiler wait for
+        // them at the join: a wave without a slice reads the last slice and
+        // never uses it.)
+        auto load_state = [&]() {
+            if constexpr (INIT) {
+                const int l = threadIdx.x & 63, nn = l & 15, jj = l >> 4;
+                const float *src = init_state + ((int64_t)nh * DV + (has ? v0 : DV - 16) + nn) * DK + 8 * jj;
 #pragma unroll
-            for (int t = 0; t < KT; ++t)
-                sT[t] = has && init_state ? *reinterpret_cast<const float4_t *>(src + 32 * (t >> 1) + 4 * (t & 1))
-                                          : float4_t{0.f, 0.f, 0.f, 0.f};
-        }
-        for (int t0 = tb; t0 < te; t0 += kSmallC, par ^= 1) {
+                for (int t = 0; t < KT; ++t)
+                    sT[t] = *reinterpret_cast<const float4_t *>(src + 32 * (t >> 1) + 4 * (t & 1));
+            } else {
+#pragma unroll
+                for (int t = 0; t < KT; ++t) sT[t] = float4_t{0.f, 0.f, 0.f, 0.f};
+            }
+        };
+        // One chunk; the first (FIRST, peeled: no branch around the state
+        // loads) issues the state loads behind its K and Q loads.
+        auto chunk = [&](int t0, auto FIRST) {
             const int nt = min(kSmallC, te - t0);
             // Lane-dependent values are formed anew in every chunk (the lane
             // index is opaque to the compiler here), not hoisted out of the
@@ -1760,28 +1773,29 @@ __global__ __launch_bounds__(64 * kSmallMaxWaves) void chunk_small_kernel(
                   *gl2 = gam + 2 * kSmallC, *bv = gam + 3 * kSmallC, *gCp = gam + 4 * kSmallC;
             const int64_t th = (int64_t)t0 * H + h;
 
-            // ---- phase A: loads (indices clamped to the chunk, not branched
-            // on, so they are all in flight together; values of tokens past
-            // the end are replaced where they are used) ----
-            float la_in = 0.f, bt_in = 0.f;
-            if (w == 0) {
-                la_in = log_alpha[th + (int64_t)min(nn, nt - 1) * H];
-                bt_in = beta[th + (int64_t)min(nn, nt - 1) * H];
-            }
+            // ---- phase A: loads.  Every load is unconditional, with indices
+            // clamped to the chunk (and to the last slice for a wave without
+            // one): a branch around a load makes the compiler wait for it where
+            // the paths join.  Values past the end are replaced where used. ----
+            const float la_in = log_alpha[th + (int64_t)min(nn, nt - 1) * H];   // (used by wave 0)
+            const float bt_in = beta[th + (int64_t)min(nn, nt - 1) * H];
             in_t vr[4];
-            if (has) {
-                const in_t *vp = v + th * DV + v0 + nn;
+            {
+                const in_t *vp = v + th * DV + (has ? v0 : DV - 16) + nn;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) vr[i] = vp[(int64_t)min(4 * jj + i, nt - 1) * H * DV];
             }
-            // K and Q rows as fp16 operands.  Rows past the end (copies of
-            // the last row) need no zeroing: their beta is 0, so their rows
-            // of A and T are e_n, their rows of Y and V' are 0 and they add
-            // nothing to the state; their outputs are not stored.
-            for (int p = tid; p < PIECES; p += 64 * nwv) {
+            // K and Q rows as fp16 operands, in 8-element pieces p = tid,
+            // tid + 64 nwv, ...  Rows past the end (copies of the last row)
+            // need no zeroing: their beta is 0, so their rows of A and T are
+            // e_n, their rows of Y and V' are 0 and they add nothing to the
+            // state; their outputs are not stored.
+            auto piece_src = [&](int p) {
                 const int mat = p / (2 * DK), rem = p - mat * 2 * DK, r = rem / RL, c8 = rem - r * RL;
-                Raw8<in_t> raw;
-                raw.load((mat ? q : k) + (th + (int64_t)min(r, nt - 1) * H) * DK + 8 * c8);
+                return (mat ? q : k) + (th + (int64_t)min(r, nt - 1) * H) * DK + 8 * c8;
+            };
+            auto piece_store = [&](int p, const Raw8<in_t> &raw) {
+                const int mat = p / (2 * DK), rem = p - mat * 2 * DK, r = rem / RL, c8 = rem - r * RL;
                 float f[8];
                 raw.to_f32(f);
                 float sc = 1.f;
@@ -1796,6 +1810,21 @@ __global__ __launch_bounds__(64 * kSmallMaxWaves) void chunk_small_kernel(
 #pragma unroll
                 for (int u = 0; u < 8; ++u) hv[u] = (_Float16)(f[u] * sc);
                 *reinterpret_cast<half8_t *>((mat ? Qb : Kb) + r * KROW + 16 * c8) = hv;
+            };
+            {
+                Raw8<in_t> raw0;
+                raw0.load(piece_src(min(tid, PIECES - 1)));
+                if constexpr (decltype(FIRST)::value) {   // behind the first K/Q loads (order pinned)
+                    __builtin_amdgcn_sched_barrier(0);
+                    load_state();
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                if (tid < PIECES) piece_store(tid, raw0);   // (wave-uniform: PIECES is a multiple of 64)
+            }
+            for (int p = tid + 64 * nwv; p < PIECES; p += 64 * nwv) {
+                Raw8<in_t> raw;
+                raw.load(piece_src(p));
+                piece_store(p, raw);
             }
             if (w == 0) {   // gates: token n of the chunk in every row of 16 lanes
                 const float bt = nn < nt ? bt_in : 0.f;
@@ -1910,6 +1939,13 @@ __global__ __launch_bounds__(64 * kSmallMaxWaves) void chunk_small_kernel(
                     sT[t] = mma16(a, dh, sT[t] * gC);
                 }
             }
+            par ^= 1;
+        };
+        if (tb < te) {
+            chunk(tb, std::true_type{});
+            for (int t0 = tb + kSmallC; t0 < te; t0 += kSmallC) chunk(t0, std::false_type{});
+        } else {   // no chunk: the state passes through
+            load_state();
         }
         if (has && final_state) {
             const int l = threadIdx.x & 63, nn = l & 15, jj = l >> 4;
@@ -1941,21 +1977,23 @@ static hipError_t launch_small_out(const ChunkArgs &a, int32_t *meta, hipStream_
     auto *o = static_cast<out_t *>(a.o);
     const int qn = (a.flags & kFlagQkL2Norm) ? 1 : 0;
     ProfScope prof("gdn_chunk_small", st);
+    auto go = [&](auto kern, size_t lds) {
+        kern<<<grid, block, lds, st>>>(a.N, a.H, a.dv, a.T, ng, qn, a.cu_seqlens, meta, q, k, v, a.log_alpha, a.beta,
+                                       a.init_state, a.final_state, o);
+    };
+    const bool init = a.init_state != nullptr;
     switch (a.dk) {
     case 32:
-        chunk_small_kernel<in_t, out_t, 32><<<grid, block, SmallSmem<32>::bytes, st>>>(
-            a.N, a.H, a.dv, a.T, ng, qn, a.cu_seqlens, meta, q, k, v, a.log_alpha, a.beta, a.init_state,
-            a.final_state, o);
+        init ? go(chunk_small_kernel<in_t, out_t, 32, true>, SmallSmem<32>::bytes)
+             : go(chunk_small_kernel<in_t, out_t, 32, false>, SmallSmem<32>::bytes);
         break;
     case 64:
-        chunk_small_kernel<in_t, out_t, 64><<<grid, block, SmallSmem<64>::bytes, st>>>(
-            a.N, a.H, a.dv, a.T, ng, qn, a.cu_seqlens, meta, q, k, v, a.log_alpha, a.beta, a.init_state,
-            a.final_state, o);
+        init ? go(chunk_small_kernel<in_t, out_t, 64, true>, SmallSmem<64>::bytes)
+             : go(chunk_small_kernel<in_t, out_t, 64, false>, SmallSmem<64>::bytes);
         break;
     case 128:
-        chunk_small_kernel<in_t, out_t, 128><<<grid, block, SmallSmem<128>::bytes, st>>>(
-            a.N, a.H, a.dv, a.T, ng, qn, a.cu_seqlens, meta, q, k, v, a.log_alpha, a.beta, a.init_state,
-            a.final_state, o);
+        init ? go(chunk_small_kernel<in_t, out_t, 128, true>, SmallSmem<128>::bytes)
+             : go(chunk_small_kernel<in_t, out_t, 128, false>, SmallSmem<128>::bytes);
         break;
     default:
         return hipErrorInvalidValue;
