@@ -1648,7 +1648,7 @@ static hipError_t allow_smem(K kernel, size_t bytes) {
 //   X_K = K S^T,  Y = V - diag(gamma) X_K,  V' = M Y,
 //   O   = diag(gamma) Q S^T + P V',  S^T <- gamma_C S^T + K^T (kappa o V').
 // One block per (sequence, head), one wave per 16-column value slice (up to
-// kSmallMaxWaves; wider states run the block over the slices in groups): a
+// kSmallMaxWaves; a wider state takes several blocks per head): a
 // wave holds its slice of S^T (dk x 16 fp32, in matrix-core accumulators)
 // through the sequence's chunks, so the state is read and written once.
 // What does not depend on the slice is done once per chunk and shared
