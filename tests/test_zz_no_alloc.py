@@ -1,7 +1,7 @@
 """gdn_chunk_fwd_noalloc (the library's scratch array instead of a workspace)
-against gdn_chunk_fwd on the same inputs, through the C ABI: two calls in a
-row, the second smaller than the first, so the second runs on the scratch the
-first left behind.  Both entry points share their kernels and are
+against gdn_chunk_fwd on the same inputs, through the C ABI: calls in a
+row, each smaller than the one before, so each runs on the scratch the
+previous one left behind (the last a short call).  Both entry points share their kernels and are
 deterministic, so the outputs must match bit for bit; each is also checked
 against the fp64 oracle."""
 import ctypes
@@ -47,6 +47,9 @@ def test_noalloc_matches_workspace_call_twice():
     cases = [
         W.chunk_inputs(4, 1000, 8, 128, 128, "bf16", seed=81, init_std=0.1, name="noalloc first (larger)"),
         W.packed_inputs([70, 0, 129, 5], H=3, dk=64, dv=48, in_dtype="bf16", seed=82, name="noalloc second (smaller)"),
+        # a short call (at most 16 tokens per sequence on average: the
+        # 16-token-chunk kernel) on the scratch the two before left behind
+        W.packed_inputs([5, 12, 0, 9], H=2, dk=128, dv=64, in_dtype="bf16", seed=83, name="noalloc third (short)"),
     ]
     ws_first = gdn.chunk_fwd_workspace_size(4, 1000, 8, 128, 128, 4)
     ws_second = gdn.chunk_fwd_workspace_size(1, 204, 3, 64, 48, 4)
