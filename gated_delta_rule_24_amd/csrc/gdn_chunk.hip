@@ -461,7 +461,7 @@ __global__ __launch_bounds__(64) void chunk_prep_kernel(int H, int T, int cpr, i
     float *gs = lds, *bs = lds + C, *qn = lds + 2 * C, *kn = lds + 3 * C, *kh = lds + 4 * C, *blk = lds + 5 * C;
 
     const int l = threadIdx.x, nn = l & 15, jj = l >> 4;
-    const int items = (cpr ? urows : meta[0]) * H;
+    const int rows = cpr ? urows : meta[0];
     const int64_t tok_stride = (int64_t)H * DK;
 
     // Issue the loads of pass s of an item (no waits).  Row indices are
@@ -596,8 +596,17 @@ __global__ __launch_bounds__(64) void chunk_prep_kernel(int H, int T, int cpr, i
                                     ws_m + rh * kTriTiles * kTileElems);
     };
 
+    // Block b takes row 8 (b / 8 / H) + b mod 8, head (b / 8) mod H: the H
+    // items of a chunk row then share one XCD (workgroups go to the 8 XCDs
+    // round-robin by block id, and the grid is a multiple of 8), so the
+    // row's [token][head] lines of log alpha and beta are fetched into one
+    // L2 rather than eight.
+    const int vitems = (rows + 7) / 8 * 8 * H;
     PrepRegs<in_t, PP> R;
-    for (int item = blockIdx.x; item < items; item += gridDim.x) {
+    for (int vb = blockIdx.x; vb < vitems; vb += gridDim.x) {
+        const int slot = vb >> 3, row = slot / H * 8 + (vb & 7);
+        if (row >= rows) continue;
+        const int item = row * H + slot % H;
         load(item, 0, R);
         process(item, R);
     }
@@ -2065,8 +2074,9 @@ static hipError_t launch_dk(const ChunkArgs &a, const ChunkWorkspace &w, hipStre
     char *ws = static_cast<char *>(a.workspace);
     if (w.max_rows > 0) {   // no tokens at all: only the state pass runs (final = initial)
         ProfScope prof("gdn_chunk_prep", st);
-        // One wave per (row, head) item; very large batches loop.
-        const int64_t items = w.max_rows * a.H;
+        // One wave per (row, head) item, rows padded to a multiple of 8 (the
+        // kernel's XCD placement); very large batches loop.
+        const int64_t items = (w.max_rows + 7) / 8 * 8 * a.H;
         const int64_t grid = items < (1 << 22) ? items : (1 << 22);
         chunk_prep_kernel<in_t, OP, DK><<<dim3((unsigned)grid), dim3(64), 0, st>>>(
             a.H, a.T, uniform_cpr(a), (int)(uniform_cpr(a) ? w.max_rows : 0), (a.flags & kFlagQkL2Norm) ? 1 : 0,
