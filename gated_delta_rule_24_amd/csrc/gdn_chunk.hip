@@ -1438,13 +1438,14 @@ __global__ __launch_bounds__((64 * StateSmem<in_t, OP, DK, NW, OUT>::WAVES)) voi
 //   S_in(s + 1) = S_in(s) F_s + G_s.
 // fp32 throughout.  Thread t owns row 16 rt + t / 16 and DK / 16 consecutive
 // columns.  For each product the block's 16 rows of S sit in LDS, and F goes
-// through LDS in slabs of SLAB rows (16-byte loads, all issued before one
-// wait), so each thread's sums read LDS only.
+// through LDS in slabs of SLAB rows (16-byte loads into registers, issued one
+// slab ahead), so each thread's sums read LDS only.
 // ============================================================================
 template <int DK>
 struct CombineSmem {
     static constexpr int SLAB = DK <= 64 ? DK : 8192 / DK;   // F rows per slab (at most 32 KiB)
-    static constexpr int LD = (SLAB * DK / 4 + 255) / 256;    // 16-byte loads per thread per slab
+    static constexpr int LD = SLAB * DK / 4 / 256;            // 16-byte loads per thread per slab
+    static_assert(LD * 256 * 4 == SLAB * DK, "a slab is whole 16-byte loads of all 256 threads");
 };
 
 template <int DK>
@@ -1488,51 +1489,64 @@ __global__ __launch_bounds__(256) void chunk_combine_kernel(int NSEQ, int H, int
         for (int j = 0; j < CPT; ++j) S[j] = e[j];
     }
     put(1);
-    for (int s = 1; s + 1 < nseg; ++s) {
-        const float *E = sg.ws_end + unit(s) * (DV + DK) * DK;
-        const float *G = E + (int64_t)r * DK + c0, *F = E + (int64_t)DV * DK;
-        __syncthreads();   // the previous product's reads of `rows` are done
+    // The products S_in(s + 1) = S_in(s) F_s + G_s for s = 1 .. nseg - 2, as
+    // one sequence of slab steps; each step issues the next step's F slab
+    // and G rows (indices clamped at the last step, so no branch surrounds a
+    // load) before it computes, so the walk waits on L2 / HBM only once.
+    constexpr int NSL = DK / SLAB;
+    const int nsteps = (nseg - 2) * NSL;
+    if (nsteps <= 0) return;
+    auto slab = [&](int step) {
+        const int s = 1 + step / NSL;
+        return sg.ws_end + unit(s) * (DV + DK) * DK + (int64_t)(DV + step % NSL * SLAB) * DK;
+    };
+    auto grow = [&](int step) { return sg.ws_end + (unit(1 + step / NSL) * (DV + DK) + r) * DK + c0; };
+    float4_t ld[L::LD];
+    float gn[CPT];
+    auto load = [&](int step) {
+        const float *F = slab(step), *G = grow(step);
 #pragma unroll
-        for (int j = 0; j < CPT; ++j) rows[t / 16][c0 + j] = S[j];
+        for (int i = 0; i < L::LD; ++i) ld[i] = *reinterpret_cast<const float4_t *>(F + 4 * (t + 256 * i));
 #pragma unroll
-        for (int j = 0; j < CPT; ++j) S[j] = G[j];
+        for (int j = 0; j < CPT; ++j) gn[j] = G[j];
+    };
+    load(0);
 #pragma unroll 1
-        for (int e0 = 0; e0 < DK; e0 += SLAB) {
-            float4_t ld[L::LD];
+    for (int step = 0; step < nsteps; ++step) {
+        const int sl = step % NSL;
+        __syncthreads();   // the previous step's reads of `fs` and `rows` are done
+        if (sl == 0) {     // a new product: S_in(s) to `rows`, the sum starts from G_s
 #pragma unroll
-            for (int i = 0; i < L::LD; ++i) {
-                const int x = 4 * (t + 256 * i);   // element of the slab
-                if (x < SLAB * DK) ld[i] = *reinterpret_cast<const float4_t *>(F + (int64_t)e0 * DK + x);
-            }
-            __syncthreads();   // the previous slab's reads of `fs` are done
+            for (int j = 0; j < CPT; ++j) rows[t / 16][c0 + j] = S[j];
 #pragma unroll
-            for (int i = 0; i < L::LD; ++i) {
-                const int x = 4 * (t + 256 * i);
-                if (x < SLAB * DK) *reinterpret_cast<float4_t *>(&fs[0][0] + x) = ld[i];
-            }
-            __syncthreads();
+            for (int j = 0; j < CPT; ++j) S[j] = gn[j];
+        }
+#pragma unroll
+        for (int i = 0; i < L::LD; ++i) *reinterpret_cast<float4_t *>(&fs[0][0] + 4 * (t + 256 * i)) = ld[i];
+        load(min(step + 1, nsteps - 1));
+        __syncthreads();
+        const int e0 = sl * SLAB;
 #pragma unroll 2
-            for (int e = 0; e < SLAB; e += 4) {
-                const float4_t a = *reinterpret_cast<const float4_t *>(&rows[t / 16][e0 + e]);
+        for (int e = 0; e < SLAB; e += 4) {
+            const float4_t a = *reinterpret_cast<const float4_t *>(&rows[t / 16][e0 + e]);
 #pragma unroll
-                for (int ee = 0; ee < 4; ++ee) {
-                    float f[CPT];
-                    if constexpr (CPT % 4 == 0) {
+            for (int ee = 0; ee < 4; ++ee) {
+                float f[CPT];
+                if constexpr (CPT % 4 == 0) {
 #pragma unroll
-                        for (int j = 0; j < CPT; j += 4) {
-                            const float4_t x = *reinterpret_cast<const float4_t *>(&fs[e + ee][c0 + j]);
-                            f[j] = x[0], f[j + 1] = x[1], f[j + 2] = x[2], f[j + 3] = x[3];
-                        }
-                    } else {
-#pragma unroll
-                        for (int j = 0; j < CPT; ++j) f[j] = fs[e + ee][c0 + j];
+                    for (int j = 0; j < CPT; j += 4) {
+                        const float4_t x = *reinterpret_cast<const float4_t *>(&fs[e + ee][c0 + j]);
+                        f[j] = x[0], f[j + 1] = x[1], f[j + 2] = x[2], f[j + 3] = x[3];
                     }
+                } else {
 #pragma unroll
-                    for (int j = 0; j < CPT; ++j) S[j] = fmaf(a[ee], f[j], S[j]);
+                    for (int j = 0; j < CPT; ++j) f[j] = fs[e + ee][c0 + j];
                 }
+#pragma unroll
+                for (int j = 0; j < CPT; ++j) S[j] = fmaf(a[ee], f[j], S[j]);
             }
         }
-        put(s + 1);
+        if (sl == NSL - 1) put(2 + step / NSL);
     }
 }
 
