@@ -123,19 +123,6 @@ constexpr int kVecFloats = 4 * C;
 // X[n][4j .. 4j + 3]) or C(X) (lane (n, j): X[4j .. 4j + 3][n], the
 // accumulator layout); C(X Y) = mm(R(X), C(Y)) and R(X Y) = mm(C(Y), R(X)).
 // ============================================================================
-__device__ __forceinline__ void tri_tile(int t, int &a, int &b) {
-    a = t < 1 ? 0 : (t < 3 ? 1 : (t < 6 ? 2 : 3));
-    b = t - a * (a + 1) / 2;
-}
-__host__ __device__ constexpr int tri_of(int a, int b) { return a * (a + 1) / 2 + b; }
-
-// 16 x 16 x 16 product on the 16x16x4 instruction: acc + X Y with x, y in the
-// operand layouts above.
-__device__ __forceinline__ float4_t mm16(const float4_t &x, const float4_t &y, float4_t acc) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x[i], y[i], acc, 0, 0, 0);
-    return acc;
-}
 
 // Register passes over dk: the raw Q and K rows of one pass take at most 128
 // registers per lane.
@@ -218,7 +205,7 @@ __global__ __launch_bounds__(64) void bwd_prep_kernel(int H, int T, int cpr, int
 #pragma unroll
         for (int t = 0; t < kTriTiles; ++t) {
             int a, b;
-            tri_tile(t, a, b);
+            tri_decode(t, a, b);
 #pragma unroll
             for (int p = 0; p < PP; ++p) {
                 gram_mma(kk[t], kr[b][p], kr[a][p]);
@@ -241,7 +228,7 @@ __global__ __launch_bounds__(64) void bwd_prep_kernel(int H, int T, int cpr, int
 #pragma unroll
     for (int t = 0; t < kTriTiles; ++t) {
         int a, b;
-        tri_tile(t, a, b);
+        tri_decode(t, a, b);
         const float4_t gc = *reinterpret_cast<const float4_t *>(sg + 16 * b + 4 * jj);
         float4_t pv, gv, av;
 #pragma unroll
@@ -273,29 +260,9 @@ __global__ __launch_bounds__(64) void bwd_prep_kernel(int H, int T, int cpr, int
             *reinterpret_cast<float4_t *>(G + o) = zero4();
             *reinterpret_cast<float4_t *>(Tm + o) = zero4();
         }
-    // One wave: its LDS accesses are performed in program order, so only the
-    // compiler has to be kept from moving them.
-    asm volatile("" ::: "memory");
-
-    // Diagonal blocks: lane (n, j) solves row n of T_jj,
-    //   x[c] = [c == n] - sum_{m > c} x[m] N[m][c],  c = 15 .. 0.
-    {
-        const float *nt = blk + jj * BS;
-        float x[16];
-#pragma unroll
-        for (int c = 15; c >= 0; --c) {
-            float acc = c == nn ? 1.f : 0.f;
-#pragma unroll
-            for (int m = c + 1; m < 16; ++m) acc -= x[m] * nt[c * BP + m];
-            x[c] = acc;
-        }
-        asm volatile("" ::: "memory");
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            *reinterpret_cast<float4_t *>(blk + jj * BS + nn * BP + 4 * e) =
-                float4_t{x[4 * e], x[4 * e + 1], x[4 * e + 2], x[4 * e + 3]};
-    }
-    asm volatile("" ::: "memory");
+    asm volatile("" ::: "memory");   // one wave: only the compiler could reorder its LDS accesses
+    // Diagonal blocks: lane (n, j) solves row n of T_jj.
+    diag_block_inverse<BP, BS>(blk, nn, jj);
     float4_t tR[4], tC[3];   // R(T_aa), C(T_bb)
 #pragma unroll
     for (int a = 0; a < 4; ++a) tR[a] = *reinterpret_cast<const float4_t *>(blk + a * BS + nn * BP + 4 * jj);
@@ -307,21 +274,21 @@ __global__ __launch_bounds__(64) void bwd_prep_kernel(int H, int T, int cpr, int
     // Off-diagonal blocks by distance; C layouts where a later W needs them.
     const float4_t z = zero4();
     float4_t W, T10, T21, T32, T20, T31, T30, C10, C21, C20;
-    W = mm16(naR[tri_of(1, 0)], tC[0], z);
-    T10 = mm16(W, tR[1], z);
-    C10 = mm16(tR[1], W, z);
-    W = mm16(naR[tri_of(2, 1)], tC[1], z);
-    T21 = mm16(W, tR[2], z);
-    C21 = mm16(tR[2], W, z);
-    W = mm16(naR[tri_of(3, 2)], tC[2], z);
-    T32 = mm16(W, tR[3], z);
-    W = mm16(naR[tri_of(2, 1)], C10, mm16(naR[tri_of(2, 0)], tC[0], z));
-    T20 = mm16(W, tR[2], z);
-    C20 = mm16(tR[2], W, z);
-    W = mm16(naR[tri_of(3, 2)], C21, mm16(naR[tri_of(3, 1)], tC[1], z));
-    T31 = mm16(W, tR[3], z);
-    W = mm16(naR[tri_of(3, 2)], C20, mm16(naR[tri_of(3, 1)], C10, mm16(naR[tri_of(3, 0)], tC[0], z)));
-    T30 = mm16(W, tR[3], z);
+    W = mm16_f32(naR[tri_index(1, 0)], tC[0], z);
+    T10 = mm16_f32(W, tR[1], z);
+    C10 = mm16_f32(tR[1], W, z);
+    W = mm16_f32(naR[tri_index(2, 1)], tC[1], z);
+    T21 = mm16_f32(W, tR[2], z);
+    C21 = mm16_f32(tR[2], W, z);
+    W = mm16_f32(naR[tri_index(3, 2)], tC[2], z);
+    T32 = mm16_f32(W, tR[3], z);
+    W = mm16_f32(naR[tri_index(2, 1)], C10, mm16_f32(naR[tri_index(2, 0)], tC[0], z));
+    T20 = mm16_f32(W, tR[2], z);
+    C20 = mm16_f32(tR[2], W, z);
+    W = mm16_f32(naR[tri_index(3, 2)], C21, mm16_f32(naR[tri_index(3, 1)], tC[1], z));
+    T31 = mm16_f32(W, tR[3], z);
+    W = mm16_f32(naR[tri_index(3, 2)], C20, mm16_f32(naR[tri_index(3, 1)], C10, mm16_f32(naR[tri_index(3, 0)], tC[0], z)));
+    T30 = mm16_f32(W, tR[3], z);
 
     auto put = [&](int a, int b, const float4_t &x) {
         *reinterpret_cast<float4_t *>(Tm + (int64_t)(16 * a + nn) * C + 16 * b + 4 * jj) = x;

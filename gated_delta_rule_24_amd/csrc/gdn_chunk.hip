@@ -59,12 +59,6 @@ namespace gdn {
 
 constexpr int C = kChunk;
 
-__host__ __device__ constexpr int tri_index(int a, int b) { return a * (a + 1) / 2 + b; }
-__device__ __forceinline__ void tri_decode(int t, int &a, int &b) {
-    a = t < 1 ? 0 : (t < 3 ? 1 : (t < 6 ? 2 : 3));
-    b = t - a * (a + 1) / 2;
-}
-
 __device__ __forceinline__ void store_out(void *o, int64_t idx, int odt, float val) {
     if (odt == DT_FP32)
         static_cast<float *>(o)[idx] = val;
@@ -250,9 +244,7 @@ struct InvMma<_Float16> {
 template <>
 struct InvMma<float> {
     __device__ __forceinline__ static float4_t mm(const float4_t &x, const float4_t &y, float4_t acc) {
-#pragma unroll
-        for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x[s], y[s], acc, 0, 0, 0);
-        return acc;
+        return mm16_f32(x, y, acc);
     }
 };
 
@@ -325,31 +317,8 @@ __device__ __forceinline__ void ut_epilogue(const float4_t (&pacc)[kTriTiles], c
     }
     asm volatile("" ::: "memory");
 
-    // Diagonal blocks: lane (n, j) computes row n of T_jj,
-    //   x[c] = [c == n] - sum_{i > c} x[i] N[i][c],  c = 15 .. 0,
-    // reading row c of N^T (broadcast to the 16 lanes of the block).
-    {
-        const float *nt = blk + jj * BS;
-        float x[16];
-#pragma unroll
-        for (int c = 15; c >= 0; --c) {
-            float acc = (c == nn) ? 1.f : 0.f;
-#pragma unroll
-            for (int qd = (c + 1) / 4; qd < 4; ++qd) {
-                const float4_t v = *reinterpret_cast<const float4_t *>(nt + c * BP + 4 * qd);
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (4 * qd + e > c) acc -= x[4 * qd + e] * v[e];
-            }
-            x[c] = acc;
-        }
-        asm volatile("" ::: "memory");
-#pragma unroll
-        for (int qd = 0; qd < 4; ++qd)
-            *reinterpret_cast<float4_t *>(blk + jj * BS + nn * BP + 4 * qd) =
-                float4_t{x[4 * qd], x[4 * qd + 1], x[4 * qd + 2], x[4 * qd + 3]};
-    }
-    asm volatile("" ::: "memory");
+    // Diagonal blocks: lane (n, j) computes row n of T_jj.
+    diag_block_inverse<BP, BS>(blk, nn, jj);
     float4_t tR[4], tC[4];   // R(T_aa), C(T_bb)
 #pragma unroll
     for (int a = 0; a < 4; ++a) tR[a] = *reinterpret_cast<const float4_t *>(blk + a * BS + nn * BP + 4 * jj);
@@ -430,6 +399,10 @@ struct PrepShape {
     static constexpr int NPASS = KP * REGS_PER_PAIR > 128 ? KP * REGS_PER_PAIR / 128 : 1;
     static constexpr int PP = KP / NPASS;   // k-tile pairs per pass
     static_assert(PP * NPASS == KP, "dk must split evenly into passes");
+    // Resident waves per SIMD the register allocation must allow: two up to
+    // dk = 128 for 16-bit inputs and dk = 64 for fp32 (one wave's loads
+    // overlap the other's products); the larger forms take what they need.
+    static constexpr int WAVES = DK * (int)sizeof(in_t) <= 256 ? 2 : 1;
 };
 
 // Raw Q and K operand registers of one item (one pass over dk) and its
@@ -441,7 +414,7 @@ struct PrepRegs {
 };
 
 template <typename in_t, typename OP, int DK>
-__global__ __launch_bounds__(64) void chunk_prep_kernel(int H, int T, int cpr, int urows, int qk_norm,
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PrepShape<in_t, DK>::WAVES))) void chunk_prep_kernel(int H, int T, int cpr, int urows, int qk_norm,
                                                         const int32_t *__restrict__ meta,
                                                         const int32_t *__restrict__ row_tok,
                                                         const int32_t *__restrict__ row_len,

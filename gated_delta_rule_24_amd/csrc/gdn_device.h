@@ -347,4 +347,57 @@ __device__ __forceinline__ float wave_inclusive_scan(float x) {
     return x;
 }
 
+// ---- unit lower-triangular chunk matrices as 16 x 16 tiles ----------------------
+
+// The lower tiles (a >= b) of a 64 x 64 chunk matrix, numbered row by row:
+// tile t = a (a + 1) / 2 + b.
+__host__ __device__ constexpr int tri_index(int a, int b) { return a * (a + 1) / 2 + b; }
+__device__ __forceinline__ void tri_decode(int t, int &a, int &b) {
+    a = t < 1 ? 0 : (t < 3 ? 1 : (t < 6 ? 2 : 3));
+    b = t - a * (a + 1) / 2;
+}
+
+// acc + X Y for 16 x 16 fp32 blocks on four 16x16x4 instructions, x in the
+// A-operand layout and y in the B-operand layout (x[s], y[s]: k = 4 j + s).
+__device__ __forceinline__ float4_t mm16_f32(const float4_t &x, const float4_t &y, float4_t acc) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x[s], y[s], acc, 0, 0, 0);
+    return acc;
+}
+
+// The inverses T_j = (I + N_j)^{-1} of the four unit lower-triangular 16 x 16
+// diagonal blocks of a chunk matrix, by one wave.  On entry block j of `blk`
+// (at j * BS floats, row pitch BP) holds N_j transposed: row c holds N_j[m][c]
+// for m > c (other entries are not read).  Lane (n, j) solves row n of T_j,
+//   x[c] = [c == n] - sum_{m > c} x[m] N_j[m][c],  c = 15 .. 0
+// (row c of the transposed block is broadcast to the block's 16 lanes, the
+// sum taken in increasing m), and writes it over row n of block j.  Only the
+// wave itself touches `blk`: its LDS accesses are performed in program
+// order, so the compiler alone has to be kept from moving them (the caller
+// fences its writes of N before the call).  nn, jj: the lane's l mod 16 and
+// l / 16, as the caller holds them.
+template <int BP, int BS>
+__device__ __forceinline__ void diag_block_inverse(float *blk, int nn, int jj) {
+    const float *nt = blk + jj * BS;
+    float x[16];
+#pragma unroll
+    for (int c = 15; c >= 0; --c) {
+        float acc = (c == nn) ? 1.f : 0.f;
+#pragma unroll
+        for (int qd = (c + 1) / 4; qd < 4; ++qd) {
+            const float4_t v = *reinterpret_cast<const float4_t *>(nt + c * BP + 4 * qd);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (4 * qd + e > c) acc -= x[4 * qd + e] * v[e];
+        }
+        x[c] = acc;
+    }
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int qd = 0; qd < 4; ++qd)
+        *reinterpret_cast<float4_t *>(blk + jj * BS + nn * BP + 4 * qd) =
+            float4_t{x[4 * qd], x[4 * qd + 1], x[4 * qd + 2], x[4 * qd + 3]};
+    asm volatile("" ::: "memory");
+}
+
 }  // namespace gdn
