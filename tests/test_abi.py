@@ -119,7 +119,13 @@ def test_bwd_workspace_and_argument_errors(lib):
     assert n.value >= rows * (2 * 64 * 64 * 4 + 4 * 64 * 4 + 2 * 128 * 128 * 4)
     d = desc()
     assert call_bwd(lib, desc(dk=256)) == 5                            # dk 256 not differentiated
-    assert call_bwd(lib, desc(flags=1)) == 5                           # q/k normalisation not differentiated
+    assert call_bwd(lib, desc(flags=4), ws_bytes=1 << 20) == 5         # unknown option
+    assert lib.gdn_chunk_bwd_workspace_size(ctypes.byref(desc(flags=4)), ctypes.byref(n)) == 5
+    # q/k normalisation: the normalised rows, v as fp32 and two factors per (token, head) on top
+    n1 = ctypes.c_size_t(0)
+    assert lib.gdn_chunk_bwd_workspace_size(ctypes.byref(desc(flags=1)), ctypes.byref(n1)) == 0
+    assert lib.gdn_chunk_bwd_workspace_size(ctypes.byref(desc()), ctypes.byref(n)) == 0
+    assert n1.value - n.value >= 2 * 100 * 3 * (2 * 128 + 128 + 2) * 4
     assert call_bwd(lib, d, do=None) == 1
     assert call_bwd(lib, d, dla=None) == 1
     assert call_bwd(lib, d, ws=None) == 6
@@ -149,7 +155,7 @@ def test_decode_argument_errors(lib):
     assert call(q=None) == 1
     assert call(v=FAKE + 2) == 4
     assert call(la=FAKE + 2) == 4                   # gates need 4-byte alignment
-    assert call(la=FAKE + 4, b=FAKE + 8) != 4        # ... and no more
+    assert call(la=FAKE + 4, b=FAKE + 8, o=FAKE2 + 64) == 8   # ... and no more (the later alias check fails)
     assert call(o=FAKE2 + 64) == 8                  # o inside the state
     assert call(N=0, state=None, q=None) == 0       # nothing to do
 
