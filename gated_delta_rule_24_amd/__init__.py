@@ -217,19 +217,20 @@ def chunk_fwd_noalloc(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None
     return o, final_state
 
 
-def chunk_bwd_workspace_size(B, T, H, dk, dv, num_seqs, in_dtype=torch.bfloat16, chunk=CHUNK) -> int:
-    d = _desc(B, T, H, dk, dv, num_seqs, _DT[in_dtype], GDN_FP32, chunk)
+def chunk_bwd_workspace_size(B, T, H, dk, dv, num_seqs, in_dtype=torch.bfloat16, chunk=CHUNK,
+                             qk_l2norm=False) -> int:
+    d = _desc(B, T, H, dk, dv, num_seqs, _DT[in_dtype], GDN_FP32, chunk, GDN_QK_L2NORM if qk_l2norm else 0)
     n = ctypes.c_size_t(0)
     _check(load().gdn_chunk_bwd_workspace_size(ctypes.byref(d), ctypes.byref(n)))
     return int(n.value)
 
 
 def chunk_bwd(q, k, v, log_alpha, beta, d_o, init_state=None, d_final=None, cu_seqlens=None, *,
-              d_init=True, workspace=None, chunk=CHUNK):
+              d_init=True, workspace=None, chunk=CHUNK, qk_l2norm=False):
     """Gradients of chunk_fwd's o and final state with respect to its inputs.
 
-    q, k, v, log_alpha, beta, init_state, cu_seqlens as for chunk_fwd;
-    d_o [B,T,H,dv] fp32; d_final [N,H,dv,dk] fp32 or None (zeros).
+    q, k, v, log_alpha, beta, init_state, cu_seqlens, qk_l2norm as for
+    chunk_fwd; d_o [B,T,H,dv] fp32; d_final [N,H,dv,dk] fp32 or None (zeros).
     d_init: True (allocate and return dL/d init_state) or False.
     Returns (dq, dk, dv, dlog_alpha, dbeta, d_init or None), all fp32.
     """
@@ -264,7 +265,7 @@ def chunk_bwd(q, k, v, log_alpha, beta, d_o, init_state=None, d_final=None, cu_s
     dq, dk_, dv_ = torch.empty((B, T, H, dk), **f32), torch.empty((B, T, H, dk), **f32), torch.empty((B, T, H, dv), **f32)
     dla, db = torch.empty((B, T, H), **f32), torch.empty((B, T, H), **f32)
     di = torch.empty((N, H, dv, dk), **f32) if d_init else None
-    desc = _desc(B, T, H, dk, dv, N, _DT[q.dtype], _DT[torch.float32], chunk)
+    desc = _desc(B, T, H, dk, dv, N, _DT[q.dtype], _DT[torch.float32], chunk, GDN_QK_L2NORM if qk_l2norm else 0)
     need = ctypes.c_size_t(0)
     _check(lib.gdn_chunk_bwd_workspace_size(ctypes.byref(desc), ctypes.byref(need)))
     if workspace is None:

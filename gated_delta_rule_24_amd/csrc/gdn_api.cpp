@@ -272,10 +272,11 @@ gdn_status gdn_chunk_bwd_workspace_size(const gdn_chunk_desc *desc, size_t *byte
     if (!bytes) return fail(GDN_ERR_NULL, "bytes is NULL");
     gdn_status s = check_chunk_desc(desc);
     if (s != GDN_OK) return s;
+    const bool qk_norm = (desc->flags & GDN_QK_L2NORM) != 0;
     const auto a = gdn::chunk_bwd_workspace_layout(desc->batch, desc->seqlen, desc->num_seqs, true, desc->heads,
-                                                   desc->dk, desc->dv);
+                                                   desc->dk, desc->dv, qk_norm);
     const auto b = gdn::chunk_bwd_workspace_layout(desc->batch, desc->seqlen, desc->num_seqs, false, desc->heads,
-                                                   desc->dk, desc->dv);
+                                                   desc->dk, desc->dv, qk_norm);
     *bytes = a.total > b.total ? a.total : b.total;
     return ok();
 }
@@ -289,7 +290,6 @@ gdn_status gdn_chunk_bwd(const gdn_chunk_desc *desc, const void *q, const void *
     if (s != GDN_OK) return s;
     const gdn_chunk_desc &d = *desc;
     if (d.dk > 128) return fail(GDN_ERR_UNSUPPORTED, "dk %d not built for the backward pass (at most 128)", d.dk);
-    if (d.flags != 0) return fail(GDN_ERR_UNSUPPORTED, "flags 0x%x not supported by the backward pass", d.flags);
     const bool packed = cu_seqlens != nullptr;
     if (packed && d.batch != 1) return fail(GDN_ERR_SHAPE, "cu_seqlens requires batch == 1 (got %d)", d.batch);
     if (!packed && d.num_seqs != d.batch)
@@ -298,7 +298,8 @@ gdn_status gdn_chunk_bwd(const gdn_chunk_desc *desc, const void *q, const void *
     if (toks > 0 && (!q || !k || !v || !log_alpha || !beta || !d_o || !dq || !dk || !dv || !dlog_alpha || !dbeta))
         return fail(GDN_ERR_NULL, "q, k, v, log_alpha, beta, d_o, dq, dk, dv, dlog_alpha and dbeta are required");
     if (!workspace) return fail(GDN_ERR_WORKSPACE, "workspace is NULL");
-    const auto w = gdn::chunk_bwd_workspace_layout(d.batch, d.seqlen, d.num_seqs, packed, d.heads, d.dk, d.dv);
+    const auto w = gdn::chunk_bwd_workspace_layout(d.batch, d.seqlen, d.num_seqs, packed, d.heads, d.dk, d.dv,
+                                                   (d.flags & GDN_QK_L2NORM) != 0);
     if (workspace_bytes < w.total)
         return fail(GDN_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, w.total);
     const void *ptrs[] = {q, k, v, init_state, d_o, d_final_state, dq, dk, dv, d_init_state, workspace};

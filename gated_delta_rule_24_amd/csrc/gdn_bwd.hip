@@ -1709,12 +1709,140 @@ hipError_t launch_bwd_typed(const ChunkArgs &a, const BwdArgs &g, const BwdWorks
     return hipErrorInvalidValue;
 }
 
+// ============================================================================
+// q/k L2 normalisation (GDN_QK_L2NORM).  The forward pass evaluates the rule
+// on q^ = q / ||q|| and k^ = k / ||k|| per (token, head), a zero row staying
+// zero (Gated Delta Networks paper, section 3.4: the token mixer block
+// normalises q and k).  The backward pass runs the kernels above on q^, k^
+// as fp32 rows (v widened to fp32 beside them: the kernels take one input
+// type) and then maps the gradients of q^ and k^ through the normalisation,
+//   dx = (dx^ - x^ (x^ . dx^)) / ||x||        (0 for a zero row),
+// the derivative of x / ||x||.  LPR = DK / 8 lanes share one (token, head)
+// row, 8 elements each; the row sums go by xor shuffles within those lanes.
+// ============================================================================
+template <typename in_t, int DK>
+__global__ __launch_bounds__(256) void bwd_norm_in_kernel(int64_t rows, int DV, const in_t *__restrict__ q,
+                                                          const in_t *__restrict__ k, const in_t *__restrict__ v,
+                                                          float *__restrict__ qh, float *__restrict__ kh,
+                                                          float *__restrict__ v32, float *__restrict__ rqk) {
+    constexpr int LPR = DK / 8, RPB = 256 / LPR;
+    const int sub = threadIdx.x % LPR;
+    const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
+    if (row >= rows) return;   // the lanes of a row leave together
+    const int64_t e0 = row * DK + 8 * sub;
+    Raw8<in_t> rq, rk;
+    rq.load(q + e0);
+    rk.load(k + e0);
+    float xq[8], xk[8];
+    rq.to_f32(xq);
+    rk.to_f32(xk);
+    float sq = 0.f, sk = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        sq = fmaf(xq[e], xq[e], sq);
+        sk = fmaf(xk[e], xk[e], sk);
+    }
+#pragma unroll
+    for (int m = LPR / 2; m >= 1; m >>= 1) {
+        sq += __shfl_xor(sq, m, 64);
+        sk += __shfl_xor(sk, m, 64);
+    }
+    const float fq = sq > 0.f ? rsqrtf(sq) : 0.f, fk = sk > 0.f ? rsqrtf(sk) : 0.f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        *reinterpret_cast<float4_t *>(qh + e0 + 4 * h) =
+            float4_t{fq * xq[4 * h], fq * xq[4 * h + 1], fq * xq[4 * h + 2], fq * xq[4 * h + 3]};
+        *reinterpret_cast<float4_t *>(kh + e0 + 4 * h) =
+            float4_t{fk * xk[4 * h], fk * xk[4 * h + 1], fk * xk[4 * h + 2], fk * xk[4 * h + 3]};
+    }
+    if (sub == 0) *reinterpret_cast<float2 *>(rqk + 2 * row) = make_float2(fq, fk);
+    for (int c = sub; c < DV; c += LPR) v32[row * DV + c] = to_f32(v[row * DV + c]);
+}
+
+template <int DK>
+__global__ __launch_bounds__(256) void bwd_norm_out_kernel(int64_t rows, int cpr, const int32_t *__restrict__ meta,
+                                                           const float *__restrict__ qh, const float *__restrict__ kh,
+                                                           const float *__restrict__ rqk, float *__restrict__ dq,
+                                                           float *__restrict__ dk) {
+    constexpr int LPR = DK / 8, RPB = 256 / LPR;
+    if (!cpr && meta[1] != 0) return;   // malformed cu_seqlens: no gradient was written
+    const int sub = threadIdx.x % LPR;
+    const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
+    if (row >= rows) return;
+    const int64_t e0 = row * DK + 8 * sub;
+    const float2 f = *reinterpret_cast<const float2 *>(rqk + 2 * row);
+    auto map = [&](const float *xh, float *d, float fx) {
+        float4_t x[2], g[2];
+        float dot = 0.f;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            x[h] = *reinterpret_cast<const float4_t *>(xh + e0 + 4 * h);
+            g[h] = *reinterpret_cast<const float4_t *>(d + e0 + 4 * h);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dot = fmaf(x[h][i], g[h][i], dot);
+        }
+#pragma unroll
+        for (int m = LPR / 2; m >= 1; m >>= 1) dot += __shfl_xor(dot, m, 64);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            float4_t r;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) r[i] = fx * fmaf(-x[h][i], dot, g[h][i]);
+            *reinterpret_cast<float4_t *>(d + e0 + 4 * h) = r;
+        }
+    };
+    map(qh, dq, f.x);
+    map(kh, dk, f.y);
+}
+
+template <typename in_t>
+hipError_t launch_bwd_norm_in(const ChunkArgs &a, const BwdWorkspace &w, hipStream_t st) {
+    char *ws = static_cast<char *>(a.workspace);
+    const int64_t rows = (int64_t)a.B * a.T * a.H;
+    auto go = [&](auto kern, int lpr) {
+        const int64_t rpb = 256 / lpr;
+        ProfScope prof("gdn_bwd_norm_in", st);
+        kern<<<dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256), 0, st>>>(
+            rows, a.dv, static_cast<const in_t *>(a.q), static_cast<const in_t *>(a.k),
+            static_cast<const in_t *>(a.v), reinterpret_cast<float *>(ws + w.off_qh),
+            reinterpret_cast<float *>(ws + w.off_kh), reinterpret_cast<float *>(ws + w.off_v32),
+            reinterpret_cast<float *>(ws + w.off_rqk));
+        return hipGetLastError();
+    };
+    switch (a.dk) {
+    case 32: return go(bwd_norm_in_kernel<in_t, 32>, 4);
+    case 64: return go(bwd_norm_in_kernel<in_t, 64>, 8);
+    case 128: return go(bwd_norm_in_kernel<in_t, 128>, 16);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_norm_out(const ChunkArgs &a, const BwdArgs &g, const BwdWorkspace &w, hipStream_t st) {
+    char *ws = static_cast<char *>(a.workspace);
+    const int64_t rows = (int64_t)a.B * a.T * a.H;
+    auto go = [&](auto kern, int lpr) {
+        const int64_t rpb = 256 / lpr;
+        ProfScope prof("gdn_bwd_norm_out", st);
+        kern<<<dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256), 0, st>>>(
+            rows, bwd_cpr(a), reinterpret_cast<const int32_t *>(ws + w.fwd.off_meta),
+            reinterpret_cast<const float *>(ws + w.off_qh), reinterpret_cast<const float *>(ws + w.off_kh),
+            reinterpret_cast<const float *>(ws + w.off_rqk), g.dq, g.dk);
+        return hipGetLastError();
+    };
+    switch (a.dk) {
+    case 32: return go(bwd_norm_out_kernel<32>, 4);
+    case 64: return go(bwd_norm_out_kernel<64>, 8);
+    case 128: return go(bwd_norm_out_kernel<128>, 16);
+    }
+    return hipErrorInvalidValue;
+}
+
 }  // namespace
 
 static size_t bwd_align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 BwdWorkspace chunk_bwd_workspace_layout(int32_t B, int32_t T, int32_t N, bool packed, int32_t H, int32_t dk,
-                                        int32_t dv) {
+                                        int32_t dv, bool qk_norm) {
     BwdWorkspace w{};
     w.fwd = chunk_workspace_layout(B, T, N, packed, H, DT_FP32, dk, dv);
     const size_t items = (size_t)w.fwd.max_rows * H;
@@ -1728,13 +1856,21 @@ BwdWorkspace chunk_bwd_workspace_layout(int32_t B, int32_t T, int32_t N, bool pa
     w.off_y = off;   off = bwd_align256(off + sizeof(float) * items * C * (size_t)dv);
     w.off_vp = off;  off = bwd_align256(off + sizeof(float) * items * C * (size_t)dv);
     w.off_dvp = off; off = bwd_align256(off + sizeof(float) * items * C * (size_t)dv);
+    if (qk_norm) {   // q^, k^ and v as fp32 rows, and the two normalisation factors per (token, head)
+        const size_t th = (size_t)B * T * H;
+        w.off_qh = off;  off = bwd_align256(off + sizeof(float) * th * dk);
+        w.off_kh = off;  off = bwd_align256(off + sizeof(float) * th * dk);
+        w.off_v32 = off; off = bwd_align256(off + sizeof(float) * th * dv);
+        w.off_rqk = off; off = bwd_align256(off + sizeof(float) * th * 2);
+    }
     w.total = off;
     return w;
 }
 
 hipError_t launch_chunk_bwd(const ChunkArgs &a, const BwdArgs &g, hipStream_t st) {
     const bool packed = a.cu_seqlens != nullptr;
-    const BwdWorkspace w = chunk_bwd_workspace_layout(a.B, a.T, a.N, packed, a.H, a.dk, a.dv);
+    const bool qk_norm = (a.flags & kFlagQkL2Norm) != 0;
+    const BwdWorkspace w = chunk_bwd_workspace_layout(a.B, a.T, a.N, packed, a.H, a.dk, a.dv, qk_norm);
     char *ws = static_cast<char *>(a.workspace);
     if (packed) {
         hipError_t e = launch_chunk_table(a.N, a.T, a.cu_seqlens, reinterpret_cast<int32_t *>(ws + w.fwd.off_meta),
@@ -1744,6 +1880,21 @@ hipError_t launch_chunk_bwd(const ChunkArgs &a, const BwdArgs &g, hipStream_t st
                                           reinterpret_cast<int32_t *>(ws + w.fwd.off_rowlen), 0, nullptr, nullptr,
                                           nullptr, st);
         if (e != hipSuccess) return e;
+    }
+    if (qk_norm) {
+        hipError_t e = a.in_dtype == DT_FP32   ? launch_bwd_norm_in<float>(a, w, st)
+                       : a.in_dtype == DT_BF16 ? launch_bwd_norm_in<bf16_t>(a, w, st)
+                                               : launch_bwd_norm_in<_Float16>(a, w, st);
+        if (e != hipSuccess) return e;
+        ChunkArgs an = a;
+        an.q = ws + w.off_qh;
+        an.k = ws + w.off_kh;
+        an.v = ws + w.off_v32;
+        an.in_dtype = DT_FP32;
+        an.flags = 0;
+        e = launch_bwd_typed<float>(an, g, w, st);
+        if (e != hipSuccess) return e;
+        return launch_bwd_norm_out(a, g, w, st);
     }
     switch (a.in_dtype) {
     case DT_FP32: return launch_bwd_typed<float>(a, g, w, st);

@@ -86,10 +86,12 @@ struct BwdArgs {
 // state and state-gradient checkpoints, and the chunk's Y, V' and dV'.
 struct BwdWorkspace {
     ChunkWorkspace fwd;
-    size_t off_t, off_p, off_gk, off_vec, off_ck, off_ds, off_y, off_vp, off_dvp, total;
+    size_t off_t, off_p, off_gk, off_vec, off_ck, off_ds, off_y, off_vp, off_dvp;
+    size_t off_qh, off_kh, off_v32, off_rqk;   // with q/k normalisation: q^, k^, v as fp32, 1/||q||, 1/||k||
+    size_t total;
 };
 BwdWorkspace chunk_bwd_workspace_layout(int32_t B, int32_t T, int32_t N, bool packed, int32_t H, int32_t dk,
-                                        int32_t dv);
+                                        int32_t dv, bool qk_norm);
 hipError_t launch_chunk_bwd(const ChunkArgs &a, const BwdArgs &g, hipStream_t stream);
 // G0 on its own (validates cu_seqlens and builds the chunk-row table).
 // With seg_chunks > 0 it also lays out the segment units: seg_first[n] and

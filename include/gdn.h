@@ -253,7 +253,9 @@ gdn_status gdn_chunk_fwd_noalloc(const gdn_chunk_desc *desc,
  * C = 64), the
  * state and the state's gradient at every chunk boundary (2 * dv * dk * 4
  * bytes) and three C x dv fp32 chunk intermediates.  Prefill with B = 4,
- * T = 4096, H = 16, dk = dv = 128 needs about 1 GiB.
+ * T = 4096, H = 16, dk = dv = 128 needs about 1 GiB.  With GDN_QK_L2NORM
+ * in desc->flags it also holds the normalised q and k and v as fp32 rows and
+ * the two normalisation factors, (2 dk + dv + 2) * 4 bytes per (token, head).
  * Errors: GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_DTYPE, GDN_ERR_UNSUPPORTED.
  */
 gdn_status gdn_chunk_bwd_workspace_size(const gdn_chunk_desc *desc, size_t *bytes);
@@ -278,8 +280,12 @@ gdn_status gdn_chunk_bwd_workspace_size(const gdn_chunk_desc *desc, size_t *byte
  *                  (with init_state NULL it is the gradient at a zero state)
  *   workspace      at least gdn_chunk_bwd_workspace_size bytes
  *
- * Supported: dk 32, 64 or 128; dv a multiple of 16 up to 1024; flags 0
- * (GDN_QK_L2NORM is not differentiated: GDN_ERR_UNSUPPORTED).  All
+ * Supported: dk 32, 64 or 128; dv a multiple of 16 up to 1024; flags 0 or
+ * GDN_QK_L2NORM.  With GDN_QK_L2NORM the gradients are those of the call
+ * that normalised q and k (paper section 3.4, token mixer block): the
+ * backward kernels run on q^ = q / ||q||, k^ = k / ||k|| (fp32 rows in the
+ * workspace) and dq, dk are carried back through the normalisation,
+ * dx = (dx^ - x^ (x^ . dx^)) / ||x||, zero for an all-zero row.  All
  * gradient arithmetic has fp32 precision for every input dtype (products
  * with a 16-bit q or k factor may run on the 16-bit matrix cores with the
  * other factor split exactly into three bf16 terms).  Tokens past a

@@ -20,7 +20,10 @@ Functions:
   recurrent_bwd(...)  gradients of recurrent() with respect to q, k, v,
                       log alpha, beta and the initial state, given the
                       gradients of o and of the final state (C, fp64, the
-                      chain rule through each token, newest first)
+                      chain rule through each token, newest first);
+                      qk_l2norm=True differentiates recurrent(...,
+                      qk_l2norm=True)
+  l2_normalise_bwd(x, g)  the gradient through l2_normalise (fp64)
 
 Parity pins (all in tests/test_oracle_pins.py): the tutorial's worked
 two-cell example (tests/golden/), the delta-vs-additive 1-D example, the
@@ -33,7 +36,9 @@ invariance of the result under positive per-token scaling of q and k, and
 zero vectors staying zero; for the gradients, central finite differences of
 recurrent() on every input element (packed sequences, initial and final
 state terms included), the closed form at alpha = 1, beta = 0 (a frozen
-state), and linearity in (d_o, d_final).  No function here is "parity
+state), and linearity in (d_o, d_final); for the normalisation's gradient,
+central finite differences of l2_normalise and of recurrent(...,
+qk_l2norm=True), orthogonality to x, the 1/c scaling and zero vectors.  No function here is "parity
 unpinned".
 """
 from __future__ import annotations
@@ -120,6 +125,20 @@ def l2_normalise(x):
     return np.divide(x, n, out=np.zeros_like(x), where=n > 0)
 
 
+def l2_normalise_bwd(x, d_xhat):
+    """Gradient through l2_normalise, in fp64: given g = dL/dx^ for
+    x^ = x / ||x|| (last axis), returns dL/dx.  The Jacobian of x / ||x|| is
+    (I - x^ x^T) / ||x|| (symmetric), so dL/dx = (g - x^ (x^ . g)) / ||x||.
+    The pages give no gradients; this is the derivative of the definition
+    above.  An all-zero x, which l2_normalise leaves at zero, gets a zero
+    gradient."""
+    x, g = _f64(x), _f64(d_xhat)
+    n = np.sqrt((x * x).sum(axis=-1, keepdims=True))
+    xh = np.divide(x, n, out=np.zeros_like(x), where=n > 0)
+    along = (xh * g).sum(axis=-1, keepdims=True)
+    return np.divide(g - xh * along, n, out=np.zeros_like(x), where=n > 0)
+
+
 def recurrent(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, threads=0,
               lib=None, qk_l2norm=False):
     """Token-by-token recurrence in fp64.
@@ -147,7 +166,7 @@ def recurrent(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, thread
 
 
 def recurrent_bwd(q, k, v, log_alpha, beta, d_o, init_state=None, d_final=None, cu_seqlens=None,
-                  threads=0, lib=None):
+                  threads=0, lib=None, qk_l2norm=False):
     """Gradients of recurrent(...) in fp64: the chain rule through each token
     of the recurrence, newest first (see oracle_gdn_recurrent_bwd in
     gdn_oracle.c for the step).  The pages give no gradient formulas.
@@ -156,8 +175,15 @@ def recurrent_bwd(q, k, v, log_alpha, beta, d_o, init_state=None, d_final=None, 
     [N,H,dv,dk] or None (zeros), its gradient with respect to the final state.
     Returns (dq, dk [B,T,H,dk], dv [B,T,H,dv], dlog_alpha, dbeta [B,T,H],
     d_init [N,H,dv,dk]), all fp64.  Memory per (sequence, head) chain is
-    (L + 1) dv dk doubles for a sequence of L tokens.
+    (L + 1) dv dk doubles for a sequence of L tokens.  qk_l2norm: the
+    gradients of recurrent(..., qk_l2norm=True), i.e. those of the rule on
+    the normalised q, k carried back through l2_normalise_bwd.
     """
+    if qk_l2norm:
+        qn, kn = l2_normalise(q), l2_normalise(k)
+        dq, dkk, *rest = recurrent_bwd(qn, kn, v, log_alpha, beta, d_o, init_state, d_final, cu_seqlens,
+                                       threads, lib)
+        return (l2_normalise_bwd(q, dq), l2_normalise_bwd(k, dkk), *rest)
     B, T, H, dk, dv, cu, qf, kf, vf, laf, bf = _flatten(q, k, v, log_alpha, beta, cu_seqlens)
     N = len(cu) - 1
     dof = _f64(d_o).reshape(B * T, H, dv)

@@ -9,6 +9,7 @@ import torch
 
 import gated_delta_rule_24_amd as gdn
 import oracle
+import workloads as W
 
 TORCH_DT = {"fp32": torch.float32, "bf16": torch.bfloat16, "fp16": torch.float16}
 
@@ -25,6 +26,18 @@ def log(msg):
 
 def dev(x, dtype=torch.float32):
     return torch.from_numpy(np.ascontiguousarray(x)).to(device="cuda", dtype=dtype)
+
+
+def rescale_qk(inp, seed, lo=0.3, hi=3.0, zero_tokens=()):
+    """Give every (token, head) of q and k its own length in [lo, hi]
+    (re-rounded to the input dtype); `zero_tokens` make q and k all zero."""
+    rng = np.random.default_rng(seed)
+    for name in ("q", "k"):
+        x = getattr(inp, name) * rng.uniform(lo, hi, size=inp.q.shape[:3] + (1,)).astype(np.float32)
+        for t in zero_tokens:
+            x[:, t] = 0.0
+        setattr(inp, name, W.cast(x.astype(np.float32), inp.in_dtype))
+    return inp
 
 
 def run_chunk(inp, out_dtype=torch.float32, init_override="default", final=True, **kw):

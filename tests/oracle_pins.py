@@ -290,7 +290,7 @@ def pin_contraction(lib):
 
 
 def pin_l2_normalise(lib):
-    """q/k normalisation (paper 3.3, token mixer block): unit norms, the same
+    """q/k normalisation (paper 3.4, token mixer block): unit norms, the same
     direction (x = ||x|| x_hat), and an all-zero vector stays zero."""
     rng = np.random.default_rng(23)
     x = rng.standard_normal((3, 7, 16)) * rng.uniform(0.1, 10.0, size=(3, 7, 1))
@@ -321,6 +321,63 @@ def pin_qk_l2norm_scale_invariance(lib):
     assert max(np.abs(o1 - o3).max(), np.abs(f1 - f3).max()) < 1e-12
     o4, _ = oracle.recurrent(cq * q, ck * k, v, la, b, init_state=S0, lib=lib)
     assert np.abs(o4 - o1).max() > 1e-3      # without the option the scalings matter
+
+
+def pin_l2_normalise_bwd(lib):
+    """The normalisation's gradient equals the central finite difference of
+    sum(g * l2_normalise(x)) on every element; it is orthogonal to x (the
+    normalisation ignores the length), scales as 1/c under x -> c x, and is
+    zero for an all-zero x."""
+    rng = np.random.default_rng(25)
+    x = rng.standard_normal((4, 3, 6)) * rng.uniform(0.2, 5.0, size=(4, 3, 1))
+    x[2, 1] = 0.0
+    g = rng.standard_normal(x.shape)
+    d = oracle.l2_normalise_bwd(x, g)
+    h = 1e-6
+    for pos in np.ndindex(*x.shape):
+        if pos[:2] == (2, 1):
+            continue
+        xp, xm = x.copy(), x.copy()
+        xp[pos] += h
+        xm[pos] -= h
+        fd = float((g * (oracle.l2_normalise(xp) - oracle.l2_normalise(xm))).sum()) / (2 * h)
+        assert abs(fd - d[pos]) <= 1e-7 * (1.0 + abs(fd)), (pos, fd, d[pos])
+    assert np.abs((x * d).sum(axis=-1)).max() < 1e-12
+    assert np.abs(d[2, 1]).max() == 0.0
+    assert np.abs(oracle.l2_normalise_bwd(3.5 * x, g) - d / 3.5).max() < 1e-12
+
+
+def pin_bwd_l2norm_finite_difference(lib):
+    """recurrent_bwd(..., qk_l2norm=True) equals the central finite difference
+    of the loss of recurrent(..., qk_l2norm=True) on every element of q and k
+    (raw vectors of different lengths), and its other gradients equal those
+    of the rule on the normalised q, k."""
+    rng = np.random.default_rng(26)
+    T, H, dk, dv = 5, 2, 4, 3
+    q, k, v, la, b = _rand_inputs(rng, 1, T, H, dk, dv, la_range=(-0.7, -0.05))
+    q = q * rng.uniform(0.3, 3.0, size=(1, T, H, 1))
+    k = k * rng.uniform(0.3, 3.0, size=(1, T, H, 1))
+    S0 = rng.standard_normal((1, H, dv, dk))
+    Wo = rng.standard_normal((1, T, H, dv))
+    WS = rng.standard_normal((1, H, dv, dk))
+
+    def loss(qq, kk):
+        o, fin = oracle.recurrent(qq, kk, v, la, b, init_state=S0, lib=lib, qk_l2norm=True)
+        return float((Wo * o).sum() + (WS * fin).sum())
+
+    grads = oracle.recurrent_bwd(q, k, v, la, b, Wo, init_state=S0, d_final=WS, lib=lib, qk_l2norm=True)
+    h = 1e-6
+    for idx, x in enumerate((q, k)):
+        for pos in np.ndindex(*x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[pos] += h
+            xm[pos] -= h
+            fd = (loss(xp, k) - loss(xm, k)) / (2 * h) if idx == 0 else (loss(q, xp) - loss(q, xm)) / (2 * h)
+            assert abs(fd - grads[idx][pos]) <= 1e-6 * (1.0 + abs(fd)), (idx, pos, fd, grads[idx][pos])
+    plain = oracle.recurrent_bwd(oracle.l2_normalise(q), oracle.l2_normalise(k), v, la, b, Wo, init_state=S0,
+                                 d_final=WS, lib=lib)
+    for x, y in zip(grads[2:], plain[2:]):
+        assert np.abs(x - y).max() < 1e-12
 
 
 # -- gradients ------------------------------------------------------------------
@@ -406,4 +463,5 @@ ALL_PINS = [pin_worked_example, pin_delta_vs_additive, pin_interpolation,
             pin_ssd_closed_form, pin_naive_product, pin_composition_order,
             pin_chunked_matches_recurrent, pin_resume, pin_packed_vs_separate, pin_linearity,
             pin_contraction, pin_l2_normalise, pin_qk_l2norm_scale_invariance,
-            pin_bwd_finite_difference, pin_bwd_frozen_state, pin_bwd_linearity]
+            pin_bwd_finite_difference, pin_bwd_frozen_state, pin_bwd_linearity,
+            pin_l2_normalise_bwd, pin_bwd_l2norm_finite_difference]

@@ -13,34 +13,34 @@ import gated_delta_rule_24_amd as gdn
 import oracle
 import workloads as W
 
-from .gpu_util import TORCH_DT, dev, log
+from .gpu_util import TORCH_DT, dev, log, rescale_qk
 
 pytestmark = pytest.mark.gpu
 GRAD_TOL = 1e-4
 NAMES = ("dq", "dk", "dv", "dlog_alpha", "dbeta", "d_init")
 
 
-def _run(inp, d_o, d_final):
+def _run(inp, d_o, d_final, qk_l2norm=False):
     dt = TORCH_DT[inp.in_dtype]
     q, k, v = dev(inp.q, dt), dev(inp.k, dt), dev(inp.v, dt)
     la, b = dev(inp.log_alpha), dev(inp.beta)
     S0 = None if inp.init_state is None else dev(inp.init_state)
     cu = None if inp.cu_seqlens is None else dev(inp.cu_seqlens, torch.int32)
     out = gdn.chunk_bwd(q, k, v, la, b, dev(d_o), init_state=S0, d_final=None if d_final is None else dev(d_final),
-                        cu_seqlens=cu)
+                        cu_seqlens=cu, qk_l2norm=qk_l2norm)
     torch.cuda.synchronize()
     return [x.cpu().numpy() for x in out]
 
 
-def _check(inp, d_o, d_final, label, heads=None, tol=GRAD_TOL):
-    got = _run(inp, d_o, d_final)
+def _check(inp, d_o, d_final, label, heads=None, tol=GRAD_TOL, qk_l2norm=False):
+    got = _run(inp, d_o, d_final, qk_l2norm)
     H = inp.H
     heads = list(range(H)) if heads is None else list(heads)
     sl = (slice(None), slice(None), heads)
     init = None if inp.init_state is None else inp.init_state[:, heads]
     ref = oracle.recurrent_bwd(inp.q[sl], inp.k[sl], inp.v[sl], inp.log_alpha[sl], inp.beta[sl], d_o[sl],
                                init_state=init, d_final=None if d_final is None else d_final[:, heads],
-                               cu_seqlens=inp.cu_seqlens)
+                               cu_seqlens=inp.cu_seqlens, qk_l2norm=qk_l2norm)
     errs = []
     for name, g, r in zip(NAMES, got, ref):
         g = g[:, heads] if name == "d_init" else g[:, :, heads]
@@ -71,6 +71,31 @@ def test_bwd_small(B, T, H, dk, dv, dt, init_std, dfin):
     inp = W.chunk_inputs(B, T, H, dk, dv, dt, seed=60 + T + dk, init_std=init_std)
     d_o, d_final = W.incoming_grads(inp, seed=61 + T, final=dfin)
     _check(inp, d_o, d_final, f"B{B} T{T} H{H} dk{dk} dv{dv} {dt}")
+
+
+@pytest.mark.parametrize("B,T,H,dk,dv,dt,seed", [
+    (2, 150, 2, 128, 128, "bf16", 64),
+    (1, 130, 2, 64, 48, "fp32", 65),
+    (1, 77, 3, 32, 32, "fp16", 66),
+])
+def test_bwd_l2norm(B, T, H, dk, dv, dt, seed):
+    """GDN_QK_L2NORM differentiated: q and k of per-token lengths in [0.3, 3]
+    against the oracle's gradients through the normalisation."""
+    inp = rescale_qk(W.chunk_inputs(B, T, H, dk, dv, dt, seed=seed, init_std=0.1), seed)
+    d_o, d_final = W.incoming_grads(inp, seed=seed + 1)
+    _check(inp, d_o, d_final, f"l2norm B{B} T{T} H{H} dk{dk} dv{dv} {dt}", qk_l2norm=True)
+
+
+def test_bwd_l2norm_packed_with_zero_vectors():
+    """Packed batch with all-zero q and k at some tokens: their gradients are
+    zero, the rest match the oracle."""
+    inp = W.packed_inputs([5, 0, 70, 129, 64], H=2, dk=128, dv=128, in_dtype="bf16", seed=67)
+    inp = rescale_qk(inp, 67, zero_tokens=(3, 80, 150))
+    d_o, d_final = W.incoming_grads(inp, seed=68)
+    _check(inp, d_o, d_final, "l2norm packed, zero vectors", qk_l2norm=True)
+    dq, dk = _run(inp, d_o, d_final, qk_l2norm=True)[:2]
+    for t in (3, 80, 150):
+        assert np.abs(dq[:, t]).max() == 0.0 and np.abs(dk[:, t]).max() == 0.0
 
 
 def test_bwd_packed():

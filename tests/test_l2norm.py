@@ -9,21 +9,9 @@ import gated_delta_rule_24_amd as gdn
 import oracle
 import workloads as W
 
-from .gpu_util import TOL, check_parity, dev, log, run_chunk
+from .gpu_util import TOL, check_parity, dev, log, rescale_qk, run_chunk
 
 pytestmark = pytest.mark.gpu
-
-
-def _rescale(inp, seed, lo=0.3, hi=3.0, zero_tokens=()):
-    """Give every (token, head) of q and k its own length in [lo, hi]
-    (re-rounded to the input dtype); `zero_tokens` make q and k all zero."""
-    rng = np.random.default_rng(seed)
-    for name in ("q", "k"):
-        x = getattr(inp, name) * rng.uniform(lo, hi, size=inp.q.shape[:3] + (1,)).astype(np.float32)
-        for t in zero_tokens:
-            x[:, t] = 0.0
-        setattr(inp, name, W.cast(x.astype(np.float32), inp.in_dtype))
-    return inp
 
 
 @pytest.mark.parametrize("B,T,H,dk,dv,dt,seed", [
@@ -32,7 +20,7 @@ def _rescale(inp, seed, lo=0.3, hi=3.0, zero_tokens=()):
     (1, 77, 2, 32, 32, "fp16", 53),
 ])
 def test_chunk_l2norm(B, T, H, dk, dv, dt, seed):
-    inp = _rescale(W.chunk_inputs(B, T, H, dk, dv, dt, seed=seed, init_std=0.1, name=f"l2norm {dt}"), seed)
+    inp = rescale_qk(W.chunk_inputs(B, T, H, dk, dv, dt, seed=seed, init_std=0.1, name=f"l2norm {dt}"), seed)
     o, S = run_chunk(inp, qk_l2norm=True)
     check_parity(inp, o, S, qk_l2norm=True)
 
@@ -40,7 +28,7 @@ def test_chunk_l2norm(B, T, H, dk, dv, dt, seed):
 def test_chunk_l2norm_packed_with_zero_vectors():
     lens = [5, 0, 70, 129, 64]
     inp = W.packed_inputs(lens, H=2, dk=128, dv=128, in_dtype="bf16", seed=54, name="l2norm packed")
-    inp = _rescale(inp, 54, zero_tokens=(3, 80, 150))
+    inp = rescale_qk(inp, 54, zero_tokens=(3, 80, 150))
     o, S = run_chunk(inp, qk_l2norm=True)
     assert torch.isfinite(o).all() and torch.isfinite(S).all()
     check_parity(inp, o, S, qk_l2norm=True)
