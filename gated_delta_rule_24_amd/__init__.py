@@ -90,7 +90,7 @@ def load():
     lib.gdn_profile_read.restype = ctypes.c_int
     lib.gdn_profile_read.argtypes = [i32, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_int64),
                                      ctypes.POINTER(ctypes.c_double)]
-    if lib.gdn_abi_version() != 4:
+    if lib.gdn_abi_version() != 5:
         raise RuntimeError(f"{p}: unexpected ABI version {lib.gdn_abi_version()}")
     _lib = lib
     return lib
