@@ -632,13 +632,7 @@ __global__ __launch_bounds__(256) void bwd_fwd_pass_kernel(int NH, int H, int DV
                 if constexpr (SPL) {
 #pragma unroll
                     for (int ks = 0; ks < C / 32; ++ks) {
-                        uint4 ka;
-                        uint32_t *kw = reinterpret_cast<uint32_t *>(&ka);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const int r2 = 32 * ks + 8 * jj + 2 * e;
-                            kw[e] = (uint32_t)skb[r2 * SBP + 16 * a + nn] | ((uint32_t)skb[(r2 + 1) * SBP + 16 * a + nn] << 16);
-                        }
+                        const uint4 ka = lds_col8_b16(skb, SBP, 32 * ks, 16 * a, nn, jj);   // K^T fragment
 #pragma unroll
                         for (int term = 0; term < 3; ++term)
                             mfma_bf16(acc, ka,
@@ -931,14 +925,8 @@ __global__ __launch_bounds__(512) void bwd_rev_pass_kernel(int NH, int H, int DV
                     if constexpr (SPL) {   // Q^T (diag(gamma) dO) + K^T (-diag(gamma) dY)
 #pragma unroll
                         for (int ks = 0; ks < C / 32; ++ks) {
-                            uint4 qa, ka;
-                            uint32_t *qw = reinterpret_cast<uint32_t *>(&qa), *kw = reinterpret_cast<uint32_t *>(&ka);
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) {
-                                const int r2 = 32 * ks + 8 * jj + 2 * e;
-                                qw[e] = (uint32_t)sqb[r2 * KB + 16 * a + nn] | ((uint32_t)sqb[(r2 + 1) * KB + 16 * a + nn] << 16);
-                                kw[e] = (uint32_t)skb[r2 * KB + 16 * a + nn] | ((uint32_t)skb[(r2 + 1) * KB + 16 * a + nn] << 16);
-                            }
+                            const uint4 qa = lds_col8_b16(sqb, KB, 32 * ks, 16 * a, nn, jj);   // Q^T fragment
+                            const uint4 ka = lds_col8_b16(skb, KB, 32 * ks, 16 * a, nn, jj);   // K^T fragment
 #pragma unroll
                             for (int term = 0; term < 3; ++term) {
                                 const int o = (16 * term + nn) * VB + 32 * ks + 8 * jj;
@@ -1510,14 +1498,8 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(int H, int DV, int T, int
 #pragma unroll
             for (int a = 0; a < NH; ++a) {
                 const int ka = 16 * (a0 + a);
-                uint32_t bk[4], bq[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int kx = 32 * ks + 8 * jj + 2 * e;
-                    bk[e] = (uint32_t)skb[kx * KB + ka + nn] | ((uint32_t)skb[(kx + 1) * KB + ka + nn] << 16);
-                    bq[e] = (uint32_t)sqb[kx * KB + ka + nn] | ((uint32_t)sqb[(kx + 1) * KB + ka + nn] << 16);
-                }
-                const uint4 kb = uint4{bk[0], bk[1], bk[2], bk[3]}, qb = uint4{bq[0], bq[1], bq[2], bq[3]};
+                const uint4 kb = lds_col8_b16(skb, KB, 32 * ks, ka, nn, jj);   // columns ka .. of K and Q
+                const uint4 qb = lds_col8_b16(sqb, KB, 32 * ks, ka, nn, jj);
 #pragma unroll
                 for (int term = 0; term < 3; ++term) {
                     mfma_bf16(acck[a], t3[term], kb);

@@ -116,6 +116,17 @@ __device__ __forceinline__ uint2 lds_read_tr16(const void *p) {
     return __builtin_bit_cast(uint2, v);
 }
 
+// Column fragment of a row-major 16-bit matrix in LDS (`pitch` elements per
+// row, a multiple of 4): lane (n, j) gets rows r0 + 8 j .. r0 + 8 j + 7 of
+// column c0 + n, packed two rows per word in increasing row order, which is
+// the operand of a 16x16x32 product with the matrix's transpose as a factor.
+// Two transposing reads replace sixteen 16-bit reads.
+__device__ __forceinline__ uint4 lds_col8_b16(const uint16_t *base, int pitch, int r0, int c0, int nn, int jj) {
+    const uint16_t *p = base + (r0 + 8 * jj + (nn >> 2)) * pitch + c0 + 4 * (nn & 3);
+    const uint2 lo = lds_read_tr16(p), hi = lds_read_tr16(p + 4 * pitch);
+    return uint4{lo.x, lo.y, hi.x, hi.y};
+}
+
 // Operand fragment of a pair of k-tiles (32 consecutive k indices in the
 // permuted order described at the top of this file): what one fp16 matrix
 // instruction consumes per lane, or eight fp32 instructions.
