@@ -617,12 +617,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PrepShape<in
 // chunk needs one barrier; otherwise a second barrier separates their
 // commit from the reads.
 // ============================================================================
-// Waves of a state-pass block that stage inputs (the others compute).
+// Waves of a state-pass block that stage inputs (the others compute): four,
+// and six in an output-pass block of two compute waves, which then has eight
+// waves (two per SIMD) and more loads in flight per compute unit (the
+// stagers' loads are what such a block waits for).
 constexpr int kStagers = 4;
 
 template <typename in_t, typename OP, int DK, int NW, bool OUT>
 struct StateSmem {
-    static constexpr int NLD = kStagers;                                // loading waves
+    static constexpr int NLD = (NW == 2 && OUT) ? 6 : kStagers;        // loading waves
     static constexpr int WAVES = NW + NLD;
     static constexpr int BV = 16 * NW;                                  // value columns per block
     static constexpr int QROW = DK * (int)sizeof(OP) + 32;              // bytes per Q / K row
@@ -801,7 +804,7 @@ __global__ __launch_bounds__((64 * StateSmem<in_t, OP, DK, NW, OUT>::WAVES)) voi
     const int chain = n * H + h;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, nn = l & 15, jj = l >> 4;
     // Waves 0..NW-1 compute: wave w holds 16 value columns (column group
-    // cg = w); the kStagers waves after them stage the next chunk's inputs
+    // cg = w); the L::NLD waves after them stage the next chunk's inputs
     // into LDS.
     const bool stager = w >= NW;
     const int sw = w - NW, stid = tid - 64 * NW;    // stager wave / thread index
@@ -930,7 +933,7 @@ __global__ __launch_bounds__((64 * StateSmem<in_t, OP, DK, NW, OUT>::WAVES)) voi
         }
     };
     // ---- direct global -> LDS copies of V, M, P and the decay factors ----
-    // Copy ii of a chunk (stager wave sw issues ii = sw, sw + kStagers, ...) fills LDS bytes
+    // Copy ii of a chunk (stager wave sw issues ii = sw, sw + NLD, ...) fills LDS bytes
     // [1024 ii, 1024 ii + 1024) of the chunk's buffer: V blocks first, then
     // M, P (output pass only) and the 4C decay factors.  Per-lane source
     // offsets do not depend on the chunk and are computed once.  Rows past the
@@ -1591,7 +1594,7 @@ ChunkWorkspace chunk_workspace_layout(int32_t B, int32_t T, int32_t N, bool pack
 }
 
 // Compute waves per state-pass block (16 value columns each; the block also
-// has kStagers staging waves).  A chunk's latency does not shrink with more
+// has StateSmem::NLD staging waves).  A chunk's latency does not shrink with more
 // compute waves per block, so the block count is what matters: the fewest
 // waves (at least 2) whose blocks still fit on the GPU in one round; 4 when
 // no choice does.  GDN_STATE_WAVES (1, 2 or 4) overrides, for experiments.
