@@ -5,8 +5,12 @@
 
 A step is one chunked prefill over the prefill workload (B=4, H=16, L=4096,
 dk=dv=128, C=64, bf16 q/k/v, fp32 gates, fp32 o and states), inputs resident
-in HBM.  `value` is prefill tokens/s (mean over K back-to-back steps; the
-median and minimum of K individually timed steps are reported beside it).
+in HBM.  `value` is prefill tokens/s (mean over K back-to-back steps after W
+untimed ones; the median and minimum of K individually timed steps are
+reported beside it).  The defaults, K = 50 and W = 400 (about 55 ms of
+prefill), let the GPU reach its steady clock before the timed steps: after
+the host has spent seconds drawing inputs, the first tens of milliseconds of
+GPU work run slower.  The other legs warm up for W steps and at least 50 ms.
 The same run times the long-context workload (B=1, H=16, L=32768, dk=128,
 dv=256, half the heads slow-forgetting) under "long", the packed batch (eight
 sequences of 512..8192 tokens with initial states) under "packed", 1000
@@ -120,15 +124,34 @@ def _to(x, dev, dt):
     return torch.from_numpy(np.ascontiguousarray(x)).to(dev, dt)
 
 
-def time_steps(step, steps, warmup):
+def warm_up(step, warmup, min_ms=0.0):
+    """`warmup` untimed steps, continued (for the legs after the headline one) until at least
+    `min_ms` of device time has passed: after the host has spent seconds drawing a leg's inputs,
+    the first tens of milliseconds of GPU work run slower (a long-context call: 0.59 ms per step
+    averaged over 20 steps after 5 warm-up steps, 0.50 ms after 50)."""
+    import torch
+    for _ in range(warmup):
+        step()
+    if min_ms <= 0:
+        return
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(10000):
+        step()
+        t1.record()
+        t1.synchronize()
+        if t0.elapsed_time(t1) >= min_ms:
+            break
+
+
+def time_steps(step, steps, warmup, min_warm_ms=0.0):
     """Mean step time over `steps` back-to-back steps bracketed by device synchronisation, then the
     median and minimum of the same number of individually timed steps (events on torch's current
     stream, the one every call here launches on)."""
     import statistics
 
     import torch
-    for _ in range(warmup):
-        step()
+    warm_up(step, warmup, min_warm_ms)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     ev0.record()
@@ -176,7 +199,9 @@ def run_chunk_workload(args, gdn, W, dev, name, out_dtype="fp32"):
         gdn.chunk_fwd(q, k, v, la, be, init_state=S0, cu_seqlens=cu, o=o, final_state=fin, workspace=ws,
                       out_dtype=odt)
 
-    ms_per_step, ms_med, ms_min = time_steps(step, args.steps, args.warmup)
+    # the headline prefill leg takes exactly args.warmup warm-up steps; the other legs also warm
+    # up for at least 50 ms of device time
+    ms_per_step, ms_med, ms_min = time_steps(step, args.steps, args.warmup, 0.0 if name == "prefill" else 50.0)
 
     # per-kernel durations (events recorded by the library around each launch)
     with gdn.profile() as prof:
@@ -270,8 +295,7 @@ def run_continuation(args, gdn, W, dev):
     def step():
         gdn.chunk_fwd(q, k, v, la, be, init_state=state, cu_seqlens=cu, o=o, final_state=state, workspace=ws)
 
-    for _ in range(args.warmup):
-        step()
+    warm_up(step, args.warmup, 50.0)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     ev0.record()
@@ -321,8 +345,7 @@ def run_backward(args, gdn, W, dev):
         gdn.chunk_bwd(q, k, v, la, be, d_o, d_final=d_fin, workspace=ws)
 
     steps = max(1, args.steps // 2)
-    for _ in range(max(1, args.warmup // 2)):
-        step()
+    warm_up(step, max(1, args.warmup // 2), 50.0)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     ev0.record()
@@ -408,8 +431,8 @@ def run_cpu_baseline(inp, seconds):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=400)
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
