@@ -762,7 +762,14 @@ __global__ __launch_bounds__((64 * StateSmem<in_t, OP, DK, NW, OUT>::WAVES)) voi
     constexpr int KT = DK / 16;                              // state tiles along dk
     constexpr int KP = DK / 32;                              // k-tile pairs along dk
     constexpr int QK_UNITS = C * (DK / 8);                   // 8-element pieces of Q (and K)
-    constexpr int QK_IT = (QK_UNITS + NT - 1) / NT;
+    // With six staging waves (waves 2..7; wave w runs on SIMD w mod 4) the
+    // four on the SIMDs without a compute wave stage Q and K, and the two
+    // that share a SIMD with one (waves 4, 5) issue only the direct copies,
+    // so the conversions' VALU work stays off the compute waves' SIMDs.
+    constexpr bool ROLES = NLD == 6 && L::QKB == 2 && OUT;   // (double-buffered Q/K: the order below)
+    constexpr int QNT = ROLES ? 256 : NT;                    // threads staging Q and K
+    constexpr int QK_IT = (QK_UNITS + QNT - 1) / QNT;
+    constexpr int NDW = ROLES ? 2 : NLD;                     // waves issuing the direct copies
     constexpr int OPB = (int)sizeof(OP);
     extern __shared__ __align__(16) unsigned char smem[];
     const uint32_t lds0 = (uint32_t)(uintptr_t)smem;       // LDS address of smem
@@ -807,7 +814,11 @@ __global__ __launch_bounds__((64 * StateSmem<in_t, OP, DK, NW, OUT>::WAVES)) voi
     // cg = w); the L::NLD waves after them stage the next chunk's inputs
     // into LDS.
     const bool stager = w >= NW;
-    const int sw = w - NW, stid = tid - 64 * NW;    // stager wave / thread index
+    const int sw = w - NW;                          // stager wave index
+    const bool qk_role = !ROLES || (sw & 2) == 0;   // stages Q and K (with ROLES: stager waves 0, 1, 4, 5)
+    // thread index among the Q/K stagers, and wave index among the copying waves
+    const int stid = ROLES ? ((sw >> 2) * 2 + (sw & 1)) * 64 + l : tid - 64 * NW;
+    const int dsw = ROLES ? (sw & 1) : sw;
     const int cg = w;
     const int v0 = vb + cg * 16;            // first value column of a compute wave
     const bool active = !stager && v0 < DVA;
@@ -887,7 +898,7 @@ __global__ __launch_bounds__((64 * StateSmem<in_t, OP, DK, NW, OUT>::WAVES)) voi
     int offq[QK_IT];
 #pragma unroll
     for (int it = 0; it < QK_IT; ++it) {
-        const int u = (stid + it * NT) % QK_UNITS;
+        const int u = (stid + it * QNT) % QK_UNITS;
         offq[it] = (u / (DK / 8)) * rowq + (u % (DK / 8)) * 8;
     }
     auto prefetch_qk = [&](int ci, QKRegs &R) {
@@ -904,7 +915,7 @@ __global__ __launch_bounds__((64 * StateSmem<in_t, OP, DK, NW, OUT>::WAVES)) voi
         } else {
 #pragma unroll
             for (int it = 0; it < QK_IT; ++it) {
-                const int u = (stid + it * NT) % QK_UNITS;
+                const int u = (stid + it * QNT) % QK_UNITS;
                 const int off = min(u / (DK / 8), last) * rowq + (u % (DK / 8)) * 8;
                 if constexpr (OUT) R.q[it].load(qc + off);
                 R.k[it].load(kc + off);
@@ -916,7 +927,7 @@ __global__ __launch_bounds__((64 * StateSmem<in_t, OP, DK, NW, OUT>::WAVES)) voi
         OP *Kb = reinterpret_cast<OP *>(smem + L::qk_off(b) + L::k_rel);
 #pragma unroll
         for (int it = 0; it < QK_IT; ++it) {
-            const int u = stid + it * NT;
+            const int u = stid + it * QNT;
             if (u >= QK_UNITS) continue;
             const int r = u / (DK / 8), c8 = (u % (DK / 8)) * 8;
             if (len < C && r >= len) {
@@ -941,11 +952,11 @@ __global__ __launch_bounds__((64 * StateSmem<in_t, OP, DK, NW, OUT>::WAVES)) voi
     // zero in those rows and columns, so they stay inert.  Columns past DV
     // (inactive waves, or the F columns of a transition pass, which use zero
     // values) read column 0 and are not used.
-    constexpr int KD = (L::NDMA + NLD - 1) / NLD;
+    constexpr int KD = (L::NDMA + NDW - 1) / NDW;
     int dsrc[KD];   // V: elements from the chunk's first row; M, P, g: bytes
 #pragma unroll
     for (int kx = 0; kx < KD; ++kx) {
-        const int ii = sw + NLD * kx;
+        const int ii = dsw + NDW * kx;
         if (ii < L::NV) {
             const int byte = ii * 1024 + 16 * l;
             const int row = byte / VROW, unit = (byte % VROW) / 16;
@@ -968,7 +979,7 @@ __global__ __launch_bounds__((64 * StateSmem<in_t, OP, DK, NW, OUT>::WAVES)) voi
         const unsigned char *gc = reinterpret_cast<const unsigned char *>(ws_g + rh * 4 * C);
 #pragma unroll
         for (int kx = 0; kx < KD; ++kx) {
-            const int ii = sw + NLD * kx;
+            const int ii = dsw + NDW * kx;
             if (ii >= L::NDMA) break;
             if (ii < L::NV) {
                 int off = dsrc[kx];
@@ -1352,6 +1363,37 @@ __global__ __launch_bounds__((64 * StateSmem<in_t, OP, DK, NW, OUT>::WAVES)) voi
         store_o(ci, len);
     };
 
+    if constexpr (ROLES) {
+        if (stager && qk_role) {
+            // Q/K staging: chunk ci+2's loads, then chunk ci+1 committed; the
+            // barrier leaves the newest chunk's loads outstanding.
+            if (nchunks > 0) {
+                prefetch_qk(0, RA);
+                commit_qk(0, min(C, len_seq), RA);
+                if (nchunks > 1) prefetch_qk(1, RB);
+            }
+            auto step_qk = [&](int ci, QKRegs &cur, QKRegs &nxt) {
+                asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * QK_IT) : "memory");
+                prefetch_qk(min(ci + 2, nchunks - 1), nxt);
+                if (ci + 1 < nchunks) commit_qk((ci + 1) & 1, min(C, len_seq - (ci + 1) * C), cur);
+            };
+            int ci = 0;
+            for (; ci + 1 < nchunks; ci += 2) {
+                step_qk(ci, RB, RA);
+                step_qk(ci + 1, RA, RB);
+            }
+            if (ci < nchunks) step_qk(ci, RB, RA);
+            return;
+        }
+        if (stager) {   // direct copies of V, M, P and the decay factors, one chunk ahead
+            if (nchunks > 0) dma(0, 0);
+            for (int ci = 0; ci < nchunks; ++ci) {
+                asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+                if (ci + 1 < nchunks) dma(ci + 1, (ci + 1) & 1);
+            }
+            return;
+        }
+    }
     if (stager) {
         if (nchunks > 0) {
             prefetch_qk(0, RA);
