@@ -1085,8 +1085,9 @@ __global__ __launch_bounds__((64 * StateSmem<in_t, OP, DK, NW, OUT>::WAVES)) voi
         }
     };
     // Rows of staged chunk cs (a whole chunk: only a sequence's last chunk
-    // can be partial, and that one is stored directly).
-    auto flush_o = [&](int cs) {
+    // can be partial, and that one is stored directly); flusher fi of NW
+    // stores its share.
+    auto flush_o = [&](int cs, int fi) {
         const unsigned char *ob = smem + L::ob_off + (size_t)(cs & 1) * L::ob_bytes;
         const uint64_t oc = o_blk + (uint64_t)(cs * o_chunk);
         if (odt == DT_FP32) {
@@ -1094,7 +1095,7 @@ __global__ __launch_bounds__((64 * StateSmem<in_t, OP, DK, NW, OUT>::WAVES)) voi
             const int tr = l / LPR, cb = 16 * (l % LPR);
 #pragma unroll
             for (int j = 0; j < PER; ++j) {
-                const int tok = (cg * PER + j) * TPI + tr;
+                const int tok = (fi * PER + j) * TPI + tr;
                 const float4_t d = *reinterpret_cast<const float4_t *>(ob + tok * L::OPITCH + cb);
                 __builtin_nontemporal_store(d, reinterpret_cast<__attribute__((address_space(1))) float4_t *>(
                                                    oc + (uint64_t)(tok * o_row + cb)));
@@ -1104,7 +1105,7 @@ __global__ __launch_bounds__((64 * StateSmem<in_t, OP, DK, NW, OUT>::WAVES)) voi
             const int tr = l / LPR, cb = 16 * (l % LPR);
 #pragma unroll
             for (int j = 0; j < PER; ++j) {
-                const int tok = (cg * PER + j) * TPI + tr;
+                const int tok = (fi * PER + j) * TPI + tr;
                 const float4_t d = *reinterpret_cast<const float4_t *>(ob + tok * L::OPITCH + cb);
                 __builtin_nontemporal_store(d, reinterpret_cast<__attribute__((address_space(1))) float4_t *>(
                                                    oc + (uint64_t)(tok * o_row + cb)));
@@ -1315,8 +1316,8 @@ __global__ __launch_bounds__((64 * StateSmem<in_t, OP, DK, NW, OUT>::WAVES)) voi
 
         // The previous chunk's rows (staged before this chunk's barrier) go
         // out here, after the stagers have issued this step's loads.
-        if constexpr (L::OBUF) {
-            if (obuf && ci > 0) flush_o(ci - 1);
+        if constexpr (L::OBUF && !ROLES) {   // (with the staging roles the copying waves flush)
+            if (obuf && ci > 0) flush_o(ci - 1, cg);
         }
         // -- phase 6: state update, K^T fragments read NT1 tiles ahead; the
         // two products of a tile are NT1 apart, not back to back --
@@ -1385,11 +1386,15 @@ __global__ __launch_bounds__((64 * StateSmem<in_t, OP, DK, NW, OUT>::WAVES)) voi
             if (ci < nchunks) step_qk(ci, RB, RA);
             return;
         }
-        if (stager) {   // direct copies of V, M, P and the decay factors, one chunk ahead
+        if (stager) {   // direct copies of V, M, P and the decay factors, one chunk ahead,
+                        // and the output rows the compute waves staged in the previous step
             if (nchunks > 0) dma(0, 0);
             for (int ci = 0; ci < nchunks; ++ci) {
                 asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
                 if (ci + 1 < nchunks) dma(ci + 1, (ci + 1) & 1);
+                if constexpr (L::OBUF) {
+                    if (obuf && ci > 0) flush_o(ci - 1, dsw);
+                }
             }
             return;
         }
